@@ -1,0 +1,187 @@
+// Device-side building blocks shared by the gfx950 attention kernels:
+// vector types, the bf16 MFMA, LDS transpose reads, register-staged tile
+// copies, the padded LDS tile layout and the work-item map.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define LDS_AS __attribute__((address_space(3)))
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+// Running-max start value: finite, so exp2(m_old - m_new) never sees
+// (-inf) - (-inf) when a row's first tiles are fully masked.
+constexpr float kMaxInit = -1.0e30f;
+
+// v_mfma_f32_32x32x16_bf16.  Operand layout (measured on gfx950):
+//   A: lane l holds A[row = l%32][k = 8*(l/32) + j], j = 0..7
+//   B: lane l holds B[k = 8*(l/32) + j][col = l%32]
+//   C: lane l, acc i holds C[row = 8*(i/4) + 4*(l/32) + i%4][col = l%32]
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Row index (within a 32-row MFMA output tile) held by accumulator i of a
+// lane in half g = lane/32.
+__device__ __forceinline__ int acc_row(int i, int g) {
+  return 8 * (i >> 2) + 4 * g + (i & 3);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) {
+  return __builtin_amdgcn_exp2f(x);
+}
+
+// max over lanes l and l^32.
+__device__ __forceinline__ float xor32_max(float x) {
+  return fmaxf(x, __shfl_xor(x, 32));
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+  return x + __shfl_xor(x, 32);
+}
+
+// ---------------------------------------------------------------- LDS tiles
+// A tile of ROWS x D bf16 lives in LDS row-major with a padded row stride
+// of D*2 + 48 bytes.  With 64 LDS banks (256 bytes per cycle) that stride
+// (48 mod 256) is conflict-free for both read patterns used here:
+//   * 16-byte row reads of 16 consecutive rows, same column (row operands):
+//     3r mod 16 hits 16 distinct 16-byte bank groups;
+//   * transpose reads, 4 consecutive rows x 32 contiguous bytes per 16
+//     lanes: [0,32), [48,80), [96,128), [144,176) do not overlap.
+// Padding (not an XOR swizzle) keeps every operand address a per-lane base
+// plus a compile-time immediate, so the unrolled loops need no extra
+// address registers.
+template <int D>
+struct Lay {
+  static constexpr int STRIDE = D * 2 + 48;
+  static constexpr int CPR = D / 8;  // 16-byte chunks per row
+  template <int ROWS>
+  static constexpr int bytes() { return ROWS * STRIDE; }
+  __device__ __forceinline__ static int off(int r, int col) { return r * STRIDE + col * 2; }
+};
+
+// Register-staged tile copy: global -> registers (issued early, so the
+// loads overlap compute) -> LDS (written once the buffer is free).
+// NTHREADS threads cooperate; thread tid owns chunks p = n*NTHREADS + tid.
+// Rows are clamped to nrows-1 so no access leaves the tensor (rows past
+// the end hold finite data that the causal mask removes).
+template <int D, int ROWS, int NTHREADS>
+struct TileStage {
+  static constexpr int CPR = D / 8;
+  static constexpr int CHUNKS = ROWS * CPR;
+  static_assert(CHUNKS % NTHREADS == 0, "tile not a multiple of the workgroup");
+  static constexpr int ROUNDS = CHUNKS / NTHREADS;
+  u32x4 r[ROUNDS];
+
+  __device__ __forceinline__ void load(const bf16* gbase, int row0, int nrows, int tid) {
+#pragma unroll
+    for (int n = 0; n < ROUNDS; ++n) {
+      const int p = n * NTHREADS + tid;
+      const int rr = p / CPR;
+      const int cc = p % CPR;
+      int grow = row0 + rr;
+      grow = grow < nrows ? grow : nrows - 1;
+      r[n] = *(const u32x4*)(gbase + (size_t)grow * D + cc * 8);
+    }
+  }
+  __device__ __forceinline__ void store(LDS_AS char* lds, int tid) const {
+#pragma unroll
+    for (int n = 0; n < ROUNDS; ++n) {
+      const int p = n * NTHREADS + tid;
+      *(LDS_AS u32x4*)(lds + Lay<D>::off(p / CPR, (p % CPR) * 8)) = r[n];
+    }
+  }
+};
+
+// A operand for a 32-row MFMA block read along d: lane l gets
+// tile[row0 + l%32][16*c + 8*(l/32) .. +7].
+template <int D>
+__device__ __forceinline__ bf16x8 lds_row_operand(const LDS_AS char* tile, int row0, int c,
+                                                  int lane) {
+  const int r = row0 + (lane & 31);
+  const int col = 16 * c + 8 * (lane >> 5);
+  return *(const LDS_AS bf16x8*)(tile + Lay<D>::off(r, col));
+}
+
+// Transposed operand for a contraction over tile rows: lane l gets
+//   tile[row0 + 16*c16 + 8*(j/4) + 4*(l/32) + j%4][col0 + l%32], j = 0..7
+// i.e. the A (or B) operand whose k index runs over rows in the order the
+// 32x32 MFMA accumulator layout holds them.  Two ds_read_b64_tr_b16: within
+// each 16-lane group, source lane r reads 4 elements of row (base + r/4) at
+// column (col0 + 16*((l/16)%2) + 4*(r%4)); the hardware transpose hands
+// lane i of the group element i of every source row.
+template <int D>
+__device__ __forceinline__ bf16x8 lds_tr_operand(const LDS_AS char* tile, int row0, int c16,
+                                                 int col0, int lane) {
+  const int r = lane & 15;
+  const int g = lane >> 5;
+  const int half = (lane >> 4) & 1;
+  const int row = row0 + 16 * c16 + 4 * g + (r >> 2);
+  const int col = col0 + 16 * half + 4 * (r & 3);
+  s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (LDS_AS s16x4*)(tile + Lay<D>::off(row, col)));
+  s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (LDS_AS s16x4*)(tile + Lay<D>::off(row + 8, col)));
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  s16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// Pack accumulators acc[8*h .. 8*h+7] of a 32x32 tile to 8 bf16 (RNE): the
+// B operand of a contraction over the tile's rows (16 rows per chunk h).
+__device__ __forceinline__ bf16x8 pack_bf16(const float* x) {
+  bf16x8 r;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) r[j] = (bf16)x[j];
+  return r;
+}
+
+// ---------------------------------------------------------------- work map
+// Workgroups are numbered heavy-first (the last query blocks of a causal
+// layer have the most key tiles) and, when the count allows, the G
+// workgroups that share one KV head (a GQA group) are placed on the same
+// XCD (dispatch assigns workgroup i to XCD i % 8) so K/V tiles are reused
+// from that XCD's L2.
+struct WorkItem {
+  int blk;   // query-block (or key-block) index
+  int b;
+  int hkv;
+  int r;     // head within the GQA group
+};
+
+__device__ __forceinline__ WorkItem decode_work(int id, int nblk, int B, int Hkv, int G,
+                                                bool reverse) {
+  const int units = nblk * B * Hkv;
+  int u, r;
+  if ((units & 7) == 0) {
+    const int x = id & 7;
+    const int j = id >> 3;
+    r = j % G;
+    u = (j / G) * 8 + x;
+  } else {
+    u = id / G;
+    r = id % G;
+  }
+  WorkItem w;
+  const int per = B * Hkv;
+  const int bi = u / per;
+  const int rest = u % per;
+  w.blk = reverse ? nblk - 1 - bi : bi;
+  w.b = rest / Hkv;
+  w.hkv = rest % Hkv;
+  w.r = r;
+  return w;
+}
+
+}  // namespace fa

@@ -1,0 +1,297 @@
+// C-ABI layer of libfa.so (declared in include/fa.h): argument validation,
+// error reporting, window resolution, kernel selection and stream-ordered
+// scratch.  Every check runs before any HIP call; no exception crosses the
+// interface.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+
+#include "fa.h"
+#include "internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+// Stage events armed by fa_set_stage_events (per thread).
+constexpr int kMaxStageEvents = 16;
+thread_local hipEvent_t g_stage_ev[kMaxStageEvents];
+thread_local int g_stage_n = 0;
+thread_local int g_stage_next = 0;
+
+void stage_begin(hipStream_t stream) {
+  if (g_stage_n <= 0) return;
+  hipEventRecord(g_stage_ev[0], stream);
+  g_stage_next = 1;
+}
+
+int fail(int code, const std::string& msg) {
+  g_last_error = msg;
+  return code;
+}
+
+bool debug_sync() {
+  static const bool on = [] {
+    const char* e = std::getenv("FA_DEBUG_SYNC");
+    return e && e[0] && e[0] != '0';
+  }();
+  return on;
+}
+
+int finish(hipError_t e, hipStream_t stream, const char* what) {
+  if (e == hipSuccess && debug_sync()) {
+    e = hipStreamSynchronize(stream);
+    if (e == hipSuccess) e = hipGetLastError();
+  }
+  if (e != hipSuccess)
+    return fail(FA_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+  return FA_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Range {
+  const char* name;
+  const void* p;
+  size_t bytes;
+};
+
+// Byte ranges must not overlap (outputs vs everything else).
+bool overlap(const Range& a, const Range& b) {
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+  return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
+}
+
+// Shared validation of the attention calls.  Returns FA_OK or an error.
+int check_attn(const char* fn, int B, int H, int Hkv, int T, int d, float scale, int window,
+               int global_every, float softcap) {
+  const std::string f(fn);
+  if (B <= 0 || H <= 0 || Hkv <= 0 || T <= 0)
+    return fail(FA_ERR_INVALID_ARG, f + ": B, H, Hkv and T must be positive");
+  if (H % Hkv != 0) return fail(FA_ERR_INVALID_ARG, f + ": H must be a multiple of Hkv");
+  if (d <= 0 || d % 2 != 0) return fail(FA_ERR_INVALID_ARG, f + ": head size d must be even and positive");
+  if (d != 64 && d != 128 && d != 256)
+    return fail(FA_ERR_UNSUPPORTED, f + ": head size d must be 64, 128 or 256");
+  if (!(scale > 0.f) || !std::isfinite(scale))
+    return fail(FA_ERR_INVALID_ARG, f + ": scale must be positive and finite");
+  if (window < 0) return fail(FA_ERR_INVALID_ARG, f + ": window must be >= 0");
+  if (global_every < 0) return fail(FA_ERR_INVALID_ARG, f + ": global_every must be >= 0");
+  if (!(softcap >= 0.f) || !std::isfinite(softcap))
+    return fail(FA_ERR_INVALID_ARG, f + ": softcap must be >= 0 and finite");
+  const double elems = (double)B * H * T * d;
+  if (elems > 4.0e12) return fail(FA_ERR_INVALID_ARG, f + ": tensor too large");
+  return FA_OK;
+}
+
+int check_ptrs(const char* fn, const Range* rs, int n, int first_out) {
+  for (int i = 0; i < n; ++i) {
+    if (!rs[i].p) return fail(FA_ERR_INVALID_ARG, std::string(fn) + ": null pointer " + rs[i].name);
+    if (!aligned16(rs[i].p))
+      return fail(FA_ERR_INVALID_ARG, std::string(fn) + ": " + rs[i].name + " not 16-byte aligned");
+  }
+  for (int i = first_out; i < n; ++i)
+    for (int j = 0; j < n; ++j)
+      if (j != i && overlap(rs[i], rs[j]))
+        return fail(FA_ERR_INVALID_ARG,
+                    std::string(fn) + ": output " + rs[i].name + " overlaps " + rs[j].name);
+  return FA_OK;
+}
+
+int resolve_window(int window, int T) { return window >= T ? 0 : window; }
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+int attn_fwd(bool f32, const void* q, const void* k, const void* v, void* o, float* lse, int B,
+             int H, int Hkv, int T, int d, float scale, int window, int global_every,
+             float softcap, hipStream_t stream) {
+  const char* fn = f32 ? "fa_fwd_f32" : "fa_fwd";
+  int rc = check_attn(fn, B, H, Hkv, T, d, scale, window, global_every, softcap);
+  if (rc) return rc;
+  const size_t es = f32 ? 4 : 2;
+  const size_t nq = (size_t)B * H * T * d * es, nk = (size_t)B * Hkv * T * d * es;
+  const Range rs[] = {{"q", q, nq}, {"k", k, nk}, {"v", v, nk},
+                      {"o", o, nq}, {"lse", lse, (size_t)B * H * T * 4}};
+  rc = check_ptrs(fn, rs, 5, 3);
+  if (rc) return rc;
+  const int W = resolve_window(window, T);
+  hipError_t e;
+  stage_begin(stream);
+  if (f32) {
+    fa::F32Args a{};
+    a.q = (const float*)q; a.k = (const float*)k; a.v = (const float*)v;
+    a.out = (float*)o; a.lse_out = lse;
+    a.B = B; a.H = H; a.Hkv = Hkv; a.T = T; a.d = d; a.window = W;
+    a.scale = scale; a.softcap = softcap;
+    e = fa::launch_fwd_f32(a, stream);
+  } else {
+    fa::FwdArgs a{};
+    a.q = (const fa::bf16*)q; a.k = (const fa::bf16*)k; a.v = (const fa::bf16*)v;
+    a.o = (fa::bf16*)o; a.lse = lse;
+    a.B = B; a.H = H; a.Hkv = Hkv; a.T = T; a.window = W;
+    a.scale_log2e = scale * kLog2e;
+    a.two_scale_over_cap_log2e = softcap > 0.f ? 2.f * scale * kLog2e / softcap : 0.f;
+    a.cap_log2e = softcap > 0.f ? softcap * kLog2e : 0.f;
+    e = fa::launch_fwd_bf16(a, d, stream);
+  }
+  return finish(e, stream, fn);
+}
+
+int attn_bwd(bool f32, const void* q, const void* k, const void* v, const void* o,
+             const float* lse, const void* dO, void* dq, void* dk, void* dv, int B, int H,
+             int Hkv, int T, int d, float scale, int window, int global_every, float softcap,
+             hipStream_t stream) {
+  const char* fn = f32 ? "fa_bwd_f32" : "fa_bwd";
+  int rc = check_attn(fn, B, H, Hkv, T, d, scale, window, global_every, softcap);
+  if (rc) return rc;
+  const size_t es = f32 ? 4 : 2;
+  const size_t nq = (size_t)B * H * T * d * es, nk = (size_t)B * Hkv * T * d * es;
+  const Range rs[] = {{"q", q, nq},   {"k", k, nk},   {"v", v, nk},
+                      {"o", o, nq},   {"lse", lse, (size_t)B * H * T * 4},
+                      {"dO", dO, nq}, {"dq", dq, nq}, {"dk", dk, nk},
+                      {"dv", dv, nk}};
+  rc = check_ptrs(fn, rs, 9, 6);
+  if (rc) return rc;
+  const int W = resolve_window(window, T);
+  float* Dst = nullptr;
+  hipError_t e = hipMallocAsync((void**)&Dst, (size_t)B * H * T * sizeof(float), stream);
+  if (e != hipSuccess) return finish(e, stream, "fa_bwd scratch");
+  stage_begin(stream);
+  if (f32) {
+    fa::F32Args a{};
+    a.q = (const float*)q; a.k = (const float*)k; a.v = (const float*)v;
+    a.o = (const float*)o; a.lse = lse; a.dO = (const float*)dO;
+    a.dq = (float*)dq; a.dk = (float*)dk; a.dv = (float*)dv; a.Dst = Dst;
+    a.B = B; a.H = H; a.Hkv = Hkv; a.T = T; a.d = d; a.window = W;
+    a.scale = scale; a.softcap = softcap;
+    e = fa::launch_bwd_f32(a, stream);
+  } else {
+    fa::BwdArgs a{};
+    a.q = (const fa::bf16*)q; a.k = (const fa::bf16*)k; a.v = (const fa::bf16*)v;
+    a.o = (const fa::bf16*)o; a.lse = lse; a.dO = (const fa::bf16*)dO;
+    a.dq = (fa::bf16*)dq; a.dk = (fa::bf16*)dk; a.dv = (fa::bf16*)dv; a.Dst = Dst;
+    a.B = B; a.H = H; a.Hkv = Hkv; a.T = T; a.window = W;
+    a.scale = scale;
+    a.scale_log2e = scale * kLog2e;
+    a.two_scale_over_cap_log2e = softcap > 0.f ? 2.f * scale * kLog2e / softcap : 0.f;
+    a.cap_log2e = softcap > 0.f ? softcap * kLog2e : 0.f;
+    a.inv_cap = softcap > 0.f ? 1.f / softcap : 0.f;
+    e = fa::launch_bwd_bf16(a, d, stream);
+  }
+  const hipError_t e2 = hipFreeAsync(Dst, stream);
+  if (e == hipSuccess) e = e2;
+  return finish(e, stream, fn);
+}
+
+int rope(bool f32, bool bwd, const void* x, void* y, const float* inv_freq, int B, int H, int T,
+         int d, hipStream_t stream) {
+  const char* fn = bwd ? (f32 ? "rope_apply_bwd_f32" : "rope_apply_bwd")
+                       : (f32 ? "rope_apply_f32" : "rope_apply");
+  const std::string f(fn);
+  if (B <= 0 || H <= 0 || T <= 0) return fail(FA_ERR_INVALID_ARG, f + ": B, H and T must be positive");
+  if (d <= 0 || d % 2 != 0) return fail(FA_ERR_INVALID_ARG, f + ": d must be even and positive");
+  if ((double)B * H * T * d > 4.0e12) return fail(FA_ERR_INVALID_ARG, f + ": tensor too large");
+  const size_t n = (size_t)B * H * T * d * (f32 ? 4 : 2);
+  if (!x || !y || !inv_freq) return fail(FA_ERR_INVALID_ARG, f + ": null pointer");
+  if (!aligned16(x) || !aligned16(y) || !aligned16(inv_freq))
+    return fail(FA_ERR_INVALID_ARG, f + ": pointers must be 16-byte aligned");
+  if (x != y && overlap({"y", y, n}, {"x", x, n}))
+    return fail(FA_ERR_INVALID_ARG, f + ": y partially overlaps x (only y == x is allowed)");
+  if (overlap({"inv_freq", inv_freq, (size_t)d / 2 * 4}, {"y", y, n}))
+    return fail(FA_ERR_INVALID_ARG, f + ": inv_freq overlaps y");
+  fa::RopeArgs a{x, y, inv_freq, B * H, T, d};
+  stage_begin(stream);
+  const hipError_t e = f32 ? fa::launch_rope_f32(a, bwd, stream) : fa::launch_rope_bf16(a, bwd, stream);
+  return finish(e, stream, fn);
+}
+
+}  // namespace
+
+namespace fa {
+void stage_mark(hipStream_t stream) {
+  if (g_stage_next > 0 && g_stage_next < g_stage_n) hipEventRecord(g_stage_ev[g_stage_next++], stream);
+}
+}  // namespace fa
+
+extern "C" {
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+           int Hkv, int T, int d, float scale, int window, int global_every, float softcap,
+           hipStream_t stream) {
+  return attn_fwd(false, q, k, v, o, lse, B, H, Hkv, T, d, scale, window, global_every, softcap,
+                  stream);
+}
+
+int fa_fwd_f32(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+               int Hkv, int T, int d, float scale, int window, int global_every, float softcap,
+               hipStream_t stream) {
+  return attn_fwd(true, q, k, v, o, lse, B, H, Hkv, T, d, scale, window, global_every, softcap,
+                  stream);
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+           const void* dO, void* dq, void* dk, void* dv, int B, int H, int Hkv, int T, int d,
+           float scale, int window, int global_every, float softcap, hipStream_t stream) {
+  return attn_bwd(false, q, k, v, o, lse, dO, dq, dk, dv, B, H, Hkv, T, d, scale, window,
+                  global_every, softcap, stream);
+}
+
+int fa_bwd_f32(const void* q, const void* k, const void* v, const void* o, const float* lse,
+               const void* dO, void* dq, void* dk, void* dv, int B, int H, int Hkv, int T,
+               int d, float scale, int window, int global_every, float softcap,
+               hipStream_t stream) {
+  return attn_bwd(true, q, k, v, o, lse, dO, dq, dk, dv, B, H, Hkv, T, d, scale, window,
+                  global_every, softcap, stream);
+}
+
+int rope_apply(const void* x, void* y, const float* inv_freq, int B, int H, int T, int d,
+               hipStream_t stream) {
+  return rope(false, false, x, y, inv_freq, B, H, T, d, stream);
+}
+int rope_apply_bwd(const void* dy, void* dx, const float* inv_freq, int B, int H, int T, int d,
+                   hipStream_t stream) {
+  return rope(false, true, dy, dx, inv_freq, B, H, T, d, stream);
+}
+int rope_apply_f32(const void* x, void* y, const float* inv_freq, int B, int H, int T, int d,
+                   hipStream_t stream) {
+  return rope(true, false, x, y, inv_freq, B, H, T, d, stream);
+}
+int rope_apply_bwd_f32(const void* dy, void* dx, const float* inv_freq, int B, int H, int T,
+                       int d, hipStream_t stream) {
+  return rope(true, true, dy, dx, inv_freq, B, H, T, d, stream);
+}
+
+int fa_layer_window(int layer, int window, int global_every) {
+  if (layer < 0 || window < 0 || global_every < 0)
+    return fail(FA_ERR_INVALID_ARG, "fa_layer_window: layer, window and global_every must be >= 0");
+  if (global_every > 0 && (layer + 1) % global_every == 0) return 0;
+  return window;
+}
+
+int fa_rope_inv_freq(float* host_out, int d, double theta) {
+  if (!host_out) return fail(FA_ERR_INVALID_ARG, "fa_rope_inv_freq: null pointer");
+  if (d <= 0 || d % 2 != 0) return fail(FA_ERR_INVALID_ARG, "fa_rope_inv_freq: d must be even and positive");
+  if (!(theta > 0.0) || !std::isfinite(theta))
+    return fail(FA_ERR_INVALID_ARG, "fa_rope_inv_freq: theta must be positive and finite");
+  for (int i = 0; i < d / 2; ++i) host_out[i] = (float)std::pow(theta, -2.0 * i / d);
+  return FA_OK;
+}
+
+int fa_set_stage_events(void* const* events, int count) {
+  if (count < 0 || count > kMaxStageEvents || (count > 0 && !events))
+    return fail(FA_ERR_INVALID_ARG, "fa_set_stage_events: count must be 0..16 with non-null events");
+  for (int i = 0; i < count; ++i) {
+    if (!events[i]) return fail(FA_ERR_INVALID_ARG, "fa_set_stage_events: null event");
+    g_stage_ev[i] = (hipEvent_t)events[i];
+  }
+  g_stage_n = count;
+  g_stage_next = 0;
+  return FA_OK;
+}
+
+const char* fa_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,434 @@
+// Fused causal flash-attention backward for gfx950 (bf16 in, fp32 accumulate).
+//
+// Gradients of L = sum(o * dO) by recomputation of the probabilities from
+// the forward's lse, with the exact softcap derivative 1 - tanh^2 (Forge
+// attention.h commit log, "Wave 2"; ARCHITECTURES.md plan wave 2, items 8-9).
+//
+//   dP = dO V^T,  D_i = <dO_i, o_i>,  dS' = P * (dP - D),
+//   dS = dS' * (1 - tanh^2) (softcap),  dq = scale dS K,
+//   dk = scale dS^T Q,  dv = P^T dO  (dk, dv summed over the GQA group).
+//
+// Two kernels, both deterministic (no atomics):
+//   1. fa_bwd_dq_kernel -- query-parallel, the forward's structure: each
+//      lane owns one query row; S^T = K Q^T and dP^T = V dO^T come out with
+//      the query along the lane, so lse, D and the softcap chain are
+//      per-lane scalars; dQ^T += K^T dS^T reads K^T through the LDS
+//      transpose read.  It also computes D_i for its rows (the backward
+//      prologue) and writes it to a [B, H, T] fp32 scratch for kernel 2.
+//   2. fa_bwd_dkdv_kernel -- key-parallel: a workgroup owns 128 key rows of
+//      one (b, kv head) and loops over the query heads of the GQA group and
+//      over the query tiles that can see its keys (the window bounds the
+//      loop).  Each lane owns one key row: K and V stay in registers as the
+//      B operands of S = Q K^T and dP = dO V^T, and dV^T += dO^T P,
+//      dK^T += Q^T dS take dO^T and Q^T from the natural tiles through the
+//      LDS transpose read.
+#include "device_common.h"
+#include "internal.h"
+
+namespace fa {
+
+// log2-domain capped score and (for the chain rule) tanh itself.
+template <bool CAP>
+__device__ __forceinline__ float score_log2(float x, const BwdArgs& a, float& th) {
+  if (CAP) {
+    const float e = fast_exp2(x * a.two_scale_over_cap_log2e);
+    th = 1.f - 2.f * __builtin_amdgcn_rcpf(e + 1.f);
+    return th * a.cap_log2e;
+  }
+  th = 0.f;
+  return x * a.scale_log2e;
+}
+
+// ------------------------------------------------------------------ dQ pass
+template <int D, int BKV, bool CAP>
+__global__ __launch_bounds__(256, (D >= 256 ? 1 : 2)) void fa_bwd_dq_kernel(BwdArgs a) {
+  constexpr int NW = 4;
+  constexpr int BQ = 32 * NW;
+  constexpr int TILE = Lay<D>::template bytes<BKV>();
+  constexpr int NDB = D / 32;
+  constexpr int NS = BKV / 32;
+  __shared__ __attribute__((aligned(1024))) char smem[4 * TILE];
+  LDS_AS char* lds = (LDS_AS char*)smem;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5;
+  const int l32 = lane & 31;
+  const int T = a.T;
+  const int W = a.window;
+  const int G = a.H / a.Hkv;
+  const int nqb = (T + BQ - 1) / BQ;
+  const WorkItem w = decode_work(blockIdx.x, nqb, a.B, a.Hkv, G, true);
+  const int h = w.hkv * G + w.r;
+  const int q0 = w.blk * BQ;
+  const int qw0 = q0 + 32 * wave;
+  const int qrow = qw0 + l32;
+  const int qr = qrow < T ? qrow : T - 1;
+  const size_t bh = (size_t)w.b * a.H + h;
+  const size_t bkv = (size_t)w.b * a.Hkv + w.hkv;
+  const bf16* Kp = a.k + bkv * T * D;
+  const bf16* Vp = a.v + bkv * T * D;
+
+  // Q and dO rows as B operands (lane = query row), D_i, lse in log2.
+  bf16x8 qreg[D / 16], doreg[D / 16];
+  float Di;
+  {
+    const size_t roff = (bh * T + qr) * D + 8 * g;
+    const bf16x8* qs = (const bf16x8*)(a.q + roff);
+    const bf16x8* ds = (const bf16x8*)(a.dO + roff);
+    const bf16x8* os = (const bf16x8*)(a.o + roff);
+    float part = 0.f;
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) {
+      qreg[c] = qs[2 * c];
+      doreg[c] = ds[2 * c];
+      const bf16x8 ov = os[2 * c];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) part += (float)doreg[c][j] * (float)ov[j];
+    }
+    Di = xor32_sum(part);
+    if (g == 0 && qrow < T) a.Dst[bh * T + qrow] = Di;
+  }
+  const float lse2 = a.lse[bh * T + qr] * kLog2e;
+
+  int kv_lo = 0;
+  if (W > 0) kv_lo = max(0, q0 - W + 1);
+  const int t_lo = kv_lo / BKV;
+  const int kv_hi = min(T, q0 + BQ);
+  const int ntiles = (kv_hi + BKV - 1) / BKV - t_lo;
+
+  f32x16 dqacc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) dqacc[db][i] = 0.f;
+
+  TileStage<D, BKV, 256> kst, vst;
+  kst.load(Kp, t_lo * BKV, T, tid);
+  vst.load(Vp, t_lo * BKV, T, tid);
+  kst.store(lds, tid);
+  vst.store(lds + 2 * TILE, tid);
+  __syncthreads();
+
+  const int qa = qw0, qb = qw0 + 31;
+  for (int j = 0; j < ntiles; ++j) {
+    const int cur = j & 1;
+    const LDS_AS char* Kt = lds + cur * TILE;
+    const LDS_AS char* Vt = lds + (2 + cur) * TILE;
+    const bool more = j + 1 < ntiles;
+    const int nrow = (t_lo + j + 1) * BKV;
+    if (more) kst.load(Kp, nrow, T, tid);
+    const int kv0 = (t_lo + j) * BKV;
+    const bool empty = qa >= T || kv0 > qb || (W > 0 && kv0 + BKV - 1 <= qa - W);
+    const bool full = kv0 + BKV - 1 <= qa && (W == 0 || kv0 > qb - W);
+    f32x16 s[NS], dp[NS];
+    if (!empty) {
+#pragma unroll
+      for (int t = 0; t < NS; ++t) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          s[t][i] = 0.f;
+          dp[t][i] = 0.f;
+        }
+#pragma unroll
+        for (int c = 0; c < D / 16; ++c) {
+          s[t] = mfma32(lds_row_operand<D>(Kt, 32 * t, c, lane), qreg[c], s[t]);
+          dp[t] = mfma32(lds_row_operand<D>(Vt, 32 * t, c, lane), doreg[c], dp[t]);
+        }
+      }
+    }
+    if (more) {
+      kst.store(lds + (cur ^ 1) * TILE, tid);
+      vst.load(Vp, nrow, T, tid);
+    }
+    if (!empty) {
+      // dS^T in s[] (fp32), then bf16 operands.
+#pragma unroll
+      for (int t = 0; t < NS; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float th;
+          const float s2 = score_log2<CAP>(s[t][i], a, th);
+          float p = fast_exp2(s2 - lse2);
+          if (!full) {
+            const int kv = kv0 + 32 * t + acc_row(i, g);
+            const bool vis = kv <= qrow && (W == 0 || kv > qrow - W);
+            p = vis ? p : 0.f;
+          }
+          float ds = p * (dp[t][i] - Di);
+          if (CAP) ds *= 1.f - th * th;
+          s[t][i] = ds;
+        }
+      bf16x8 dsb[BKV / 16];
+#pragma unroll
+      for (int c16 = 0; c16 < BKV / 16; ++c16) {
+        float tmp[8];
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) tmp[jj] = s[c16 >> 1][8 * (c16 & 1) + jj];
+        dsb[c16] = pack_bf16(tmp);
+      }
+#pragma unroll
+      for (int c16 = 0; c16 < BKV / 16; ++c16)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+          dqacc[db] = mfma32(lds_tr_operand<D>(Kt, 0, c16, 32 * db, lane), dsb[c16], dqacc[db]);
+    }
+    if (more) vst.store(lds + (2 + (cur ^ 1)) * TILE, tid);
+    __syncthreads();
+  }
+
+  if (qrow < T) {
+    bf16* Qd = a.dq + (bh * T + qrow) * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        bf16x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = (bf16)(dqacc[db][4 * i4 + e] * a.scale);
+        *(bf16x4*)(Qd + 32 * db + 8 * i4 + 4 * g) = v;
+      }
+  }
+}
+
+// ----------------------------------------------------------------- dK/dV pass
+// MODE 0 accumulates dK and dV together; for d = 256 the two accumulators
+// (2 x 128 registers per lane) do not fit beside K, V and the tiles, so the
+// pass runs twice: MODE 1 accumulates dV only (needs S, P), MODE 2 dK only
+// (needs S, dP, dS) -- one extra S = Q K^T product instead of spilling.
+template <int D, int BQB, bool CAP, int MODE>
+__global__ __launch_bounds__(256, 1) void fa_bwd_dkdv_kernel(BwdArgs a) {
+  constexpr bool DO_DV = MODE != 2;
+  constexpr bool DO_DK = MODE != 1;
+  constexpr int NW = 4;
+  constexpr int BKVB = 32 * NW;        // key rows per workgroup
+  constexpr int TILE = Lay<D>::template bytes<BQB>();  // one Q or dO tile
+  constexpr int NDB = D / 32;
+  constexpr int NS = BQB / 32;         // 32-query sub-tiles
+  constexpr int STAT = BQB * 4;        // bytes of one lse or D tile
+  __shared__ __attribute__((aligned(1024))) char smem[4 * TILE + 4 * STAT];
+  LDS_AS char* lds = (LDS_AS char*)smem;
+  LDS_AS char* stat = lds + 4 * TILE;  // [buf][lse2 | D][BQB] fp32
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5;
+  const int l32 = lane & 31;
+  const int T = a.T;
+  const int W = a.window;
+  const int G = a.H / a.Hkv;
+  const int nkb = (T + BKVB - 1) / BKVB;
+  const WorkItem w = decode_work(blockIdx.x, nkb, a.B, a.Hkv, 1, false);
+  const int k0 = w.blk * BKVB;
+  const int kw0 = k0 + 32 * wave;
+  const int krow = kw0 + l32;
+  const int kr = krow < T ? krow : T - 1;
+  const size_t bkv = (size_t)w.b * a.Hkv + w.hkv;
+
+  bf16x8 kreg[D / 16], vreg[D / 16];
+  {
+    const size_t roff = (bkv * T + kr) * D + 8 * g;
+    const bf16x8* ks = (const bf16x8*)(a.k + roff);
+    const bf16x8* vs = (const bf16x8*)(a.v + roff);
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) {
+      kreg[c] = ks[2 * c];
+      if (DO_DK) vreg[c] = vs[2 * c];
+    }
+  }
+
+  // Query tiles that can see keys [k0, k0 + BKVB).
+  const int qt_lo = k0 / BQB;
+  const int q_hi = W > 0 ? min(T, k0 + BKVB - 1 + W) : T;
+  const int nqt = (q_hi + BQB - 1) / BQB - qt_lo;
+  const int niter = G * nqt;
+
+  f32x16 dkacc[NDB], dvacc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      dkacc[db][i] = 0.f;
+      dvacc[db][i] = 0.f;
+    }
+
+  TileStage<D, BQB, 256> qst, dost;
+  float stv = 0.f;
+  auto stage_stats = [&](int it) {
+    const int hh = w.hkv * G + it / nqt;
+    const int q0 = (qt_lo + it % nqt) * BQB;
+    const size_t bhh = (size_t)w.b * a.H + hh;
+    if (tid < 2 * BQB) {
+      int qq = q0 + (tid % BQB);
+      qq = qq < T ? qq : T - 1;
+      stv = tid < BQB ? a.lse[bhh * T + qq] * kLog2e : a.Dst[bhh * T + qq];
+    }
+  };
+  auto tile_src = [&](int it, const bf16* base) {
+    const int hh = w.hkv * G + it / nqt;
+    return base + ((size_t)w.b * a.H + hh) * T * D;
+  };
+  auto tile_q0 = [&](int it) { return (qt_lo + it % nqt) * BQB; };
+
+  qst.load(tile_src(0, a.q), tile_q0(0), T, tid);
+  dost.load(tile_src(0, a.dO), tile_q0(0), T, tid);
+  stage_stats(0);
+  qst.store(lds, tid);
+  dost.store(lds + 2 * TILE, tid);
+  if (tid < 2 * BQB) *(LDS_AS float*)(stat + tid * 4) = stv;
+  __syncthreads();
+
+  const int ka = kw0, kb = kw0 + 31;
+  for (int it = 0; it < niter; ++it) {
+    const int cur = it & 1;
+    const LDS_AS char* Qt = lds + cur * TILE;
+    const LDS_AS char* dOt = lds + (2 + cur) * TILE;
+    const LDS_AS float* lse2t = (const LDS_AS float*)(stat + cur * 2 * STAT);
+    const LDS_AS float* Dt = lse2t + BQB;
+    const bool more = it + 1 < niter;
+    // Next Q tile loads now (stored once S is done), next dO tile and row
+    // statistics after that (stored at the end): one staging set live.
+    if (more) qst.load(tile_src(it + 1, a.q), tile_q0(it + 1), T, tid);
+    const int q0 = tile_q0(it);
+    const bool empty = ka >= T || q0 + BQB - 1 < ka || (W > 0 && q0 - kb >= W);
+    const bool full = q0 >= kb && q0 + BQB <= T && (W == 0 || q0 + BQB - 1 - ka < W);
+    f32x16 s[NS], dp[NS];
+    if (!empty) {
+#pragma unroll
+      for (int t = 0; t < NS; ++t) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          s[t][i] = 0.f;
+          dp[t][i] = 0.f;
+        }
+#pragma unroll
+        for (int c = 0; c < D / 16; ++c) {
+          s[t] = mfma32(lds_row_operand<D>(Qt, 32 * t, c, lane), kreg[c], s[t]);
+          if (DO_DK) dp[t] = mfma32(lds_row_operand<D>(dOt, 32 * t, c, lane), vreg[c], dp[t]);
+        }
+      }
+    }
+    if (more) {
+      qst.store(lds + (cur ^ 1) * TILE, tid);
+      dost.load(tile_src(it + 1, a.dO), tile_q0(it + 1), T, tid);
+      stage_stats(it + 1);
+    }
+    if (!empty) {
+      // S, dP: lane = key row, accumulator i = query row 32t + acc_row(i, g).
+      // P into s[], dS into dp[].
+#pragma unroll
+      for (int t = 0; t < NS; ++t)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const int qloc = 32 * t + 8 * i4 + 4 * g;
+          const f32x4 l4 = *(const LDS_AS f32x4*)(lse2t + qloc);
+          const f32x4 d4 = *(const LDS_AS f32x4*)(Dt + qloc);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int i = 4 * i4 + e;
+            float th;
+            const float s2 = score_log2<CAP>(s[t][i], a, th);
+            float p = fast_exp2(s2 - l4[e]);
+            if (!full) {
+              const int q = q0 + qloc + e;
+              const bool vis = q < T && krow <= q && (W == 0 || krow > q - W);
+              p = vis ? p : 0.f;
+            }
+            s[t][i] = p;
+            if (DO_DK) {
+              float ds = p * (dp[t][i] - d4[e]);
+              if (CAP) ds *= 1.f - th * th;
+              dp[t][i] = ds;
+            }
+          }
+        }
+      bf16x8 pb[BQB / 16], dsb[BQB / 16];
+#pragma unroll
+      for (int c16 = 0; c16 < BQB / 16; ++c16) {
+        float tp[8], td[8];
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+          tp[jj] = s[c16 >> 1][8 * (c16 & 1) + jj];
+          td[jj] = dp[c16 >> 1][8 * (c16 & 1) + jj];
+        }
+        if (DO_DV) pb[c16] = pack_bf16(tp);
+        if (DO_DK) dsb[c16] = pack_bf16(td);
+      }
+#pragma unroll
+      for (int c16 = 0; c16 < BQB / 16; ++c16)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          if (DO_DV)
+            dvacc[db] = mfma32(lds_tr_operand<D>(dOt, 0, c16, 32 * db, lane), pb[c16], dvacc[db]);
+          if (DO_DK)
+            dkacc[db] = mfma32(lds_tr_operand<D>(Qt, 0, c16, 32 * db, lane), dsb[c16], dkacc[db]);
+        }
+    }
+    if (more) {
+      dost.store(lds + (2 + (cur ^ 1)) * TILE, tid);
+      if (tid < 2 * BQB) *(LDS_AS float*)(stat + (cur ^ 1) * 2 * STAT + tid * 4) = stv;
+    }
+    __syncthreads();
+  }
+
+  if (krow < T) {
+    const size_t roff = (bkv * T + krow) * D;
+    bf16* Kd = a.dk + roff;
+    bf16* Vd = a.dv + roff;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        bf16x4 kv4, vv4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          kv4[e] = (bf16)(dkacc[db][4 * i4 + e] * a.scale);
+          vv4[e] = (bf16)dvacc[db][4 * i4 + e];
+        }
+        if (DO_DK) *(bf16x4*)(Kd + 32 * db + 8 * i4 + 4 * g) = kv4;
+        if (DO_DV) *(bf16x4*)(Vd + 32 * db + 8 * i4 + 4 * g) = vv4;
+      }
+  }
+}
+
+template <int D, int BKV, int BQB, bool CAP>
+static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
+  const int nqb = (a.T + 127) / 128;
+  hipLaunchKernelGGL((fa_bwd_dq_kernel<D, BKV, CAP>), dim3((unsigned)nqb * a.B * a.H),
+                     dim3(256), 0, stream, a);
+  stage_mark(stream);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const dim3 kgrid((unsigned)((a.T + 127) / 128) * a.B * a.Hkv);
+  if constexpr (D <= 128) {
+    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, BQB, CAP, 0>), kgrid, dim3(256), 0, stream, a);
+    stage_mark(stream);
+  } else {
+    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, BQB, CAP, 1>), kgrid, dim3(256), 0, stream, a);
+    stage_mark(stream);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, BQB, CAP, 2>), kgrid, dim3(256), 0, stream, a);
+    stage_mark(stream);
+  }
+  return hipGetLastError();
+}
+
+template <int D, int BKV, int BQB>
+static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
+  if (a.cap_log2e > 0.f) return launch_bwd_t<D, BKV, BQB, true>(a, stream);
+  return launch_bwd_t<D, BKV, BQB, false>(a, stream);
+}
+
+hipError_t launch_bwd_bf16(const BwdArgs& a, int d, hipStream_t stream) {
+  switch (d) {
+    case 64: return launch_bwd_d<64, 64, 64>(a, stream);
+    case 128: return launch_bwd_d<128, 32, 32>(a, stream);
+    case 256: return launch_bwd_d<256, 32, 32>(a, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace fa

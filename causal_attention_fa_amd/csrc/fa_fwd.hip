@@ -1,0 +1,221 @@
+// Fused causal flash-attention forward for gfx950 (bf16 in, fp32 accumulate).
+//
+// Computes o = softmax(mask(capped(scale * q k^T))) v and the natural-log
+// row log-sum-exp (lse), with GQA, a sliding window whose out-of-window key
+// tiles are never loaded, and the optional softcap cap*tanh(s/cap) on the
+// scaled scores (Forge ARCHITECTURES.md, implementation plan wave 2, items 8
+// and 9; Forge attention.h commit log, "Wave 2").
+//
+// Structure (one workgroup = 4 waves = 128 query rows of one (b, h)):
+//   * each wave owns 32 query rows; its Q rows stay in registers as the B
+//     operand of S^T = K Q^T, so every lane owns one query row (column of
+//     S^T) and the online-softmax max/sum are per-lane values combined with
+//     the partner lane l^32 -- no cross-lane row reductions inside a tile;
+//   * K and V tiles (BKV keys) stream through LDS, double-buffered: the next
+//     tile's global loads are issued into registers ahead of the MFMAs that
+//     hide them and written to the idle padded LDS buffer after;
+//   * P^T leaves the S^T accumulators as bf16 and is directly the B operand
+//     of O^T += V^T P^T; V^T comes from the natural V tile through the
+//     gfx950 LDS transpose read, so nothing is transposed in registers;
+//   * tiles entirely outside a wave's causal/window band are skipped, tiles
+//     entirely inside are not masked; only diagonal and window-edge tiles
+//     evaluate the mask.
+#include "device_common.h"
+#include "internal.h"
+
+namespace fa {
+
+template <int D, int BKV, bool CAP>
+__global__ __launch_bounds__(256, (D >= 256 ? 1 : 2)) void fa_fwd_kernel(FwdArgs a) {
+  constexpr int NW = 4;
+  constexpr int BQ = 32 * NW;
+  constexpr int TILE = Lay<D>::template bytes<BKV>();  // one K or V tile
+  constexpr int NDB = D / 32;        // 32-wide d blocks of the output
+  constexpr int NS = BKV / 32;       // 32-key sub-tiles
+  __shared__ __attribute__((aligned(1024))) char smem[4 * TILE];
+  LDS_AS char* lds = (LDS_AS char*)smem;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5;
+  const int l32 = lane & 31;
+  const int T = a.T;
+  const int W = a.window;
+  const int G = a.H / a.Hkv;
+  const int nqb = (T + BQ - 1) / BQ;
+  const WorkItem w = decode_work(blockIdx.x, nqb, a.B, a.Hkv, G, true);
+  const int h = w.hkv * G + w.r;
+  const int q0 = w.blk * BQ;
+  const int qw0 = q0 + 32 * wave;
+  const int qrow = qw0 + l32;
+  const size_t bh = (size_t)w.b * a.H + h;
+  const size_t bkv = (size_t)w.b * a.Hkv + w.hkv;
+  const bf16* Kp = a.k + bkv * T * D;
+  const bf16* Vp = a.v + bkv * T * D;
+
+  // Q as the B operand of S^T = K Q^T: lane holds Q[qrow][16c + 8g .. +7].
+  bf16x8 qreg[D / 16];
+  {
+    const int qr = qrow < T ? qrow : T - 1;
+    const bf16x8* src = (const bf16x8*)(a.q + (bh * T + qr) * D + 8 * g);
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) qreg[c] = src[2 * c];
+  }
+
+  int kv_lo = 0;
+  if (W > 0) kv_lo = max(0, q0 - W + 1);
+  const int t_lo = kv_lo / BKV;
+  const int kv_hi = min(T, q0 + BQ);
+  const int ntiles = (kv_hi + BKV - 1) / BKV - t_lo;
+
+  f32x16 oacc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
+  float m = kMaxInit;
+  float lsum = 0.f;
+
+  TileStage<D, BKV, 256> kst, vst;
+  kst.load(Kp, t_lo * BKV, T, tid);
+  vst.load(Vp, t_lo * BKV, T, tid);
+  kst.store(lds, tid);
+  vst.store(lds + 2 * TILE, tid);
+  __syncthreads();
+
+  const int qa = qw0, qb = qw0 + 31;
+  for (int j = 0; j < ntiles; ++j) {
+    const int cur = j & 1;
+    const LDS_AS char* Kt = lds + cur * TILE;
+    const LDS_AS char* Vt = lds + (2 + cur) * TILE;
+    const bool more = j + 1 < ntiles;
+    const int nrow = (t_lo + j + 1) * BKV;
+    // Next K tile: loads issued now, written to the idle buffer once this
+    // tile's scores are done; the V tile follows the same pattern around
+    // the P V product, so only one staging set is live at a time.
+    if (more) kst.load(Kp, nrow, T, tid);
+    const int kv0 = (t_lo + j) * BKV;
+    const bool empty = qa >= T || kv0 > qb || (W > 0 && kv0 + BKV - 1 <= qa - W);
+    const bool full = kv0 + BKV - 1 <= qa && (W == 0 || kv0 > qb - W);
+    f32x16 s[NS];
+    if (!empty) {
+#pragma unroll
+      for (int t = 0; t < NS; ++t) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[t][i] = 0.f;
+#pragma unroll
+        for (int c = 0; c < D / 16; ++c)
+          s[t] = mfma32(lds_row_operand<D>(Kt, 32 * t, c, lane), qreg[c], s[t]);
+      }
+    }
+    if (more) {
+      kst.store(lds + (cur ^ 1) * TILE, tid);
+      vst.load(Vp, nrow, T, tid);
+    }
+    if (!empty) {
+      float mt = -INFINITY;
+#pragma unroll
+      for (int t = 0; t < NS; ++t) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float x = s[t][i];
+          if (CAP) {
+            // cap * tanh(scale*x / cap), carried in the log2 domain
+            const float e = fast_exp2(x * a.two_scale_over_cap_log2e);
+            x = (1.f - 2.f * __builtin_amdgcn_rcpf(e + 1.f)) * a.cap_log2e;
+          } else {
+            x *= a.scale_log2e;
+          }
+          s[t][i] = x;
+        }
+      }
+      if (!full) {
+#pragma unroll
+        for (int t = 0; t < NS; ++t)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int kv = kv0 + 32 * t + acc_row(i, g);
+            const bool vis = kv <= qrow && (W == 0 || kv > qrow - W);
+            s[t][i] = vis ? s[t][i] : -INFINITY;
+          }
+      }
+#pragma unroll
+      for (int t = 0; t < NS; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[t][i]);
+      mt = xor32_max(mt);
+      const float mnew = fmaxf(m, mt);
+      const float alpha = fast_exp2(m - mnew);
+      m = mnew;
+      float ps = 0.f;
+#pragma unroll
+      for (int t = 0; t < NS; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float p = fast_exp2(s[t][i] - mnew);
+          s[t][i] = p;
+          ps += p;
+        }
+      lsum = lsum * alpha + ps;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+      bf16x8 pb[BKV / 16];
+#pragma unroll
+      for (int c16 = 0; c16 < BKV / 16; ++c16) {
+        float tmp[8];
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) tmp[jj] = s[c16 >> 1][8 * (c16 & 1) + jj];
+        pb[c16] = pack_bf16(tmp);
+      }
+#pragma unroll
+      for (int c16 = 0; c16 < BKV / 16; ++c16)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+          oacc[db] = mfma32(lds_tr_operand<D>(Vt, 0, c16, 32 * db, lane), pb[c16], oacc[db]);
+    }
+    if (more) vst.store(lds + (2 + (cur ^ 1)) * TILE, tid);
+    __syncthreads();
+  }
+
+  const float ltot = xor32_sum(lsum);
+  if (qrow < T) {
+    const float inv = 1.f / ltot;
+    bf16* Op = a.o + (bh * T + qrow) * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        bf16x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = (bf16)(oacc[db][4 * i4 + e] * inv);
+        *(bf16x4*)(Op + 32 * db + 8 * i4 + 4 * g) = v;
+      }
+    if (g == 0) a.lse[bh * T + qrow] = (m + __log2f(ltot)) * kLn2;
+  }
+}
+
+template <int D, int BKV>
+static hipError_t launch_fwd_d(const FwdArgs& a, hipStream_t stream) {
+  const int nqb = (a.T + 127) / 128;
+  const dim3 grid((unsigned)nqb * a.B * a.H);
+  if (a.cap_log2e > 0.f)
+    hipLaunchKernelGGL((fa_fwd_kernel<D, BKV, true>), grid, dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((fa_fwd_kernel<D, BKV, false>), grid, dim3(256), 0, stream, a);
+  stage_mark(stream);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_bf16(const FwdArgs& a, int d, hipStream_t stream) {
+  switch (d) {
+    case 64: return launch_fwd_d<64, 64>(a, stream);
+    case 128: return launch_fwd_d<128, 64>(a, stream);
+    case 256: return launch_fwd_d<256, 32>(a, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace fa

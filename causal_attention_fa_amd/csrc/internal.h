@@ -1,0 +1,86 @@
+// Host/device interface between the C-ABI layer (fa_api.cpp) and the
+// kernel launchers.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace fa {
+
+typedef __bf16 bf16;
+
+// Forward arguments.  `window` is already resolved (0 = full causal).
+// Score constants are folded for the log2-domain softmax:
+//   no cap:  s2 = x * scale * log2(e)
+//   cap:     s2 = cap * log2(e) * tanh(scale * x / cap), with tanh(y)
+//            = 1 - 2 / (exp2(2 y log2(e)) + 1)
+struct FwdArgs {
+  const bf16* q;
+  const bf16* k;
+  const bf16* v;
+  bf16* o;
+  float* lse;
+  int B, H, Hkv, T, window;
+  float scale_log2e;               // scale * log2(e)
+  float two_scale_over_cap_log2e;  // 2 * scale * log2(e) / cap   (cap > 0)
+  float cap_log2e;                 // cap * log2(e), 0 when no cap
+};
+
+// Backward arguments.  Dst holds the per-row D = <dO_i, o_i> scratch
+// ([B, H, T] fp32) written by the dq pass and read by the dk/dv pass.
+struct BwdArgs {
+  const bf16* q;
+  const bf16* k;
+  const bf16* v;
+  const bf16* o;
+  const float* lse;
+  const bf16* dO;
+  bf16* dq;
+  bf16* dk;
+  bf16* dv;
+  float* Dst;
+  int B, H, Hkv, T, window;
+  float scale;
+  float scale_log2e;
+  float two_scale_over_cap_log2e;
+  float cap_log2e;
+  float inv_cap;                   // 1 / cap, 0 when no cap
+};
+
+// float32 twins (plain pointers, same semantics).
+struct F32Args {
+  const float* q;
+  const float* k;
+  const float* v;
+  const float* o;
+  float* lse_out;      // forward output
+  const float* lse;    // backward input
+  const float* dO;
+  float* out;          // forward o
+  float* dq;
+  float* dk;
+  float* dv;
+  float* Dst;
+  int B, H, Hkv, T, d, window;
+  float scale;
+  float softcap;
+};
+
+struct RopeArgs {
+  const void* x;
+  void* y;
+  const float* inv_freq;
+  int BH, T, d;
+};
+
+// Called by the launchers right after each kernel launch; records the
+// caller's stage events when fa_set_stage_events() armed them.
+void stage_mark(hipStream_t stream);
+
+hipError_t launch_fwd_bf16(const FwdArgs& a, int d, hipStream_t stream);
+hipError_t launch_bwd_bf16(const BwdArgs& a, int d, hipStream_t stream);
+hipError_t launch_fwd_f32(const F32Args& a, hipStream_t stream);
+hipError_t launch_bwd_f32(const F32Args& a, hipStream_t stream);
+hipError_t launch_rope_bf16(const RopeArgs& a, bool bwd, hipStream_t stream);
+hipError_t launch_rope_f32(const RopeArgs& a, bool bwd, hipStream_t stream);
+
+}  // namespace fa

@@ -1,0 +1,129 @@
+// Rotary position embedding on interleaved pairs, bf16 and fp32 I/O.
+//
+// y[2i]   = x[2i] cos(t f_i) - x[2i+1] sin(t f_i)
+// y[2i+1] = x[2i] sin(t f_i) + x[2i+1] cos(t f_i)
+// with f the host-computed inverse-frequency table and the angle the fp32
+// product t * f_i (Forge README: interleaved pairs; Forge attention.h commit
+// log, "Wave 1": kernels read a host-precomputed inv-freq table).  The
+// backward is the transpose (rotation by -angle).
+//
+// HBM-bound elementwise work.  The angle depends only on (t, i), not on the
+// (b, h) row, so each thread fixes one 16-byte group of a [T, d] slice,
+// evaluates its cos/sin once (accurate sincosf: angles reach ~8e3 rad) and
+// then streams that group through BH_PER consecutive (b, h) slices:
+// coalesced 16-byte loads/stores, trigonometry amortised over the slices.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "internal.h"
+
+namespace fa {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kBhPer = 8;
+
+template <typename T>
+struct Vec;
+template <>
+struct Vec<__bf16> {
+  static constexpr int N = 8;  // elements per 16 bytes
+  typedef __bf16 V __attribute__((ext_vector_type(8)));
+};
+template <>
+struct Vec<float> {
+  static constexpr int N = 4;
+  typedef float V __attribute__((ext_vector_type(4)));
+};
+
+template <typename T, bool BWD>
+__global__ __launch_bounds__(kThreads) void rope_vec_kernel(RopeArgs a) {
+  constexpr int N = Vec<T>::N;
+  typedef typename Vec<T>::V V;
+  const long slice = (long)a.T * a.d;             // elements per (b, h)
+  const long e0 = ((long)blockIdx.x * kThreads + threadIdx.x) * N;
+  if (e0 >= slice) return;
+  const int t = (int)(e0 / a.d);
+  const int c0 = (int)(e0 % a.d);                 // even: N and d are even
+  float cs[N / 2], sn[N / 2];
+#pragma unroll
+  for (int p = 0; p < N / 2; ++p) {
+    const float ang = (float)t * a.inv_freq[c0 / 2 + p];
+    sincosf(ang, &sn[p], &cs[p]);
+    if (BWD) sn[p] = -sn[p];
+  }
+  const int bh0 = blockIdx.y * kBhPer;
+  const int bh1 = min(a.BH, bh0 + kBhPer);
+  const T* x = (const T*)a.x;
+  T* y = (T*)a.y;
+  for (int bh = bh0; bh < bh1; ++bh) {
+    const long off = (long)bh * slice + e0;
+    const V v = *(const V*)(x + off);
+    V r;
+#pragma unroll
+    for (int p = 0; p < N / 2; ++p) {
+      const float xe = (float)v[2 * p], xo = (float)v[2 * p + 1];
+      r[2 * p] = (T)(xe * cs[p] - xo * sn[p]);
+      r[2 * p + 1] = (T)(xe * sn[p] + xo * cs[p]);
+    }
+    *(V*)(y + off) = r;
+  }
+}
+
+// Any even d: one pair per thread.
+template <typename T, bool BWD>
+__global__ __launch_bounds__(kThreads) void rope_pair_kernel(RopeArgs a) {
+  const long slice = (long)a.T * a.d;
+  const long e0 = ((long)blockIdx.x * kThreads + threadIdx.x) * 2;
+  if (e0 >= slice) return;
+  const int t = (int)(e0 / a.d);
+  const int c0 = (int)(e0 % a.d);
+  float sn, cs;
+  sincosf((float)t * a.inv_freq[c0 / 2], &sn, &cs);
+  if (BWD) sn = -sn;
+  const int bh0 = blockIdx.y * kBhPer;
+  const int bh1 = min(a.BH, bh0 + kBhPer);
+  const T* x = (const T*)a.x;
+  T* y = (T*)a.y;
+  for (int bh = bh0; bh < bh1; ++bh) {
+    const long off = (long)bh * slice + e0;
+    const float xe = (float)x[off], xo = (float)x[off + 1];
+    y[off] = (T)(xe * cs - xo * sn);
+    y[off + 1] = (T)(xe * sn + xo * cs);
+  }
+}
+
+template <typename T>
+hipError_t launch_rope(const RopeArgs& a, bool bwd, hipStream_t stream) {
+  const long slice = (long)a.T * a.d;
+  const unsigned gy = (unsigned)((a.BH + kBhPer - 1) / kBhPer);
+  const int N = Vec<T>::N;
+  if (a.d % N == 0) {
+    const dim3 grid((unsigned)((slice / N + kThreads - 1) / kThreads), gy);
+    if (bwd)
+      hipLaunchKernelGGL((rope_vec_kernel<T, true>), grid, dim3(kThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL((rope_vec_kernel<T, false>), grid, dim3(kThreads), 0, stream, a);
+    stage_mark(stream);
+  } else {
+    const dim3 grid((unsigned)((slice / 2 + kThreads - 1) / kThreads), gy);
+    if (bwd)
+      hipLaunchKernelGGL((rope_pair_kernel<T, true>), grid, dim3(kThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL((rope_pair_kernel<T, false>), grid, dim3(kThreads), 0, stream, a);
+    stage_mark(stream);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_rope_bf16(const RopeArgs& a, bool bwd, hipStream_t stream) {
+  return launch_rope<__bf16>(a, bwd, stream);
+}
+hipError_t launch_rope_f32(const RopeArgs& a, bool bwd, hipStream_t stream) {
+  return launch_rope<float>(a, bwd, stream);
+}
+
+}  // namespace fa

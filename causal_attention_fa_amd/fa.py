@@ -1,0 +1,252 @@
+"""ctypes binding of libfa.so (include/fa.h), plus thin torch conveniences.
+
+The functions named like the C entry points (fa_fwd, fa_bwd, rope_apply,
+rope_apply_bwd and their _f32 twins, fa_layer_window, fa_rope_inv_freq,
+fa_last_error) only marshal arguments: a tensor argument is passed as its
+device pointer, sizes as C ints, the stream as the HIP stream handle (the
+current torch stream when omitted).  A negative return code raises FAError
+with the library's message.  Every step of the computation runs in the HIP
+kernels; there is no fallback: importing this module without the built
+library raises.
+
+The convenience wrappers (attention_forward, attention_backward, rope,
+FlashAttention) allocate outputs with torch and call the same entry points.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import numpy as np
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
+if not os.path.exists(_LIB_PATH):
+    raise ImportError(
+        f"{_LIB_PATH} is missing: build it with `python -m causal_attention_fa_amd.build` "
+        "(the HIP library is required; there is no CPU fallback)")
+_lib = ctypes.CDLL(_LIB_PATH)
+
+FA_OK = 0
+FA_ERR_INVALID_ARG = -1
+FA_ERR_UNSUPPORTED = -2
+FA_ERR_HIP = -3
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_F = ctypes.c_float
+
+_ATTN_FWD = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I, _F, _P]
+_ATTN_BWD = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I, _F, _P]
+_ROPE = [_P, _P, _P, _I, _I, _I, _I, _P]
+
+for _name, _args in [("fa_fwd", _ATTN_FWD), ("fa_fwd_f32", _ATTN_FWD),
+                     ("fa_bwd", _ATTN_BWD), ("fa_bwd_f32", _ATTN_BWD),
+                     ("rope_apply", _ROPE), ("rope_apply_bwd", _ROPE),
+                     ("rope_apply_f32", _ROPE), ("rope_apply_bwd_f32", _ROPE)]:
+    _fn = getattr(_lib, _name)
+    _fn.argtypes = _args
+    _fn.restype = _I
+_lib.fa_layer_window.argtypes = [_I, _I, _I]
+_lib.fa_layer_window.restype = _I
+_lib.fa_rope_inv_freq.argtypes = [ctypes.POINTER(ctypes.c_float), _I, ctypes.c_double]
+_lib.fa_rope_inv_freq.restype = _I
+_lib.fa_set_stage_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), _I]
+_lib.fa_set_stage_events.restype = _I
+_lib.fa_last_error.argtypes = []
+_lib.fa_last_error.restype = ctypes.c_char_p
+
+EXPORTS = ("fa_fwd", "fa_bwd", "rope_apply", "rope_apply_bwd", "fa_fwd_f32", "fa_bwd_f32",
+           "rope_apply_f32", "rope_apply_bwd_f32", "fa_layer_window", "fa_rope_inv_freq",
+           "fa_set_stage_events", "fa_last_error")
+
+
+class FAError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"[{code}] {msg}")
+        self.code = code
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def fa_last_error() -> str:
+    return _lib.fa_last_error().decode()
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if isinstance(x, torch.Tensor):
+        return x.data_ptr()
+    return int(x)
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _check(rc: int):
+    if rc != FA_OK:
+        raise FAError(rc, fa_last_error())
+    return rc
+
+
+def _call_fwd(fn, q, k, v, o, lse, B, H, Hkv, T, d, scale, window, global_every, softcap,
+              stream):
+    return _check(fn(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Hkv, T, d,
+                     float(scale), window, global_every, float(softcap), _stream(stream)))
+
+
+def _call_bwd(fn, q, k, v, o, lse, dO, dq, dk, dv, B, H, Hkv, T, d, scale, window,
+              global_every, softcap, stream):
+    return _check(fn(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dO), _ptr(dq),
+                     _ptr(dk), _ptr(dv), B, H, Hkv, T, d, float(scale), window, global_every,
+                     float(softcap), _stream(stream)))
+
+
+def fa_fwd(q, k, v, o, lse, B, H, Hkv, T, d, scale, window=0, global_every=0, softcap=0.0,
+           stream=None):
+    return _call_fwd(_lib.fa_fwd, q, k, v, o, lse, B, H, Hkv, T, d, scale, window,
+                     global_every, softcap, stream)
+
+
+def fa_fwd_f32(q, k, v, o, lse, B, H, Hkv, T, d, scale, window=0, global_every=0,
+               softcap=0.0, stream=None):
+    return _call_fwd(_lib.fa_fwd_f32, q, k, v, o, lse, B, H, Hkv, T, d, scale, window,
+                     global_every, softcap, stream)
+
+
+def fa_bwd(q, k, v, o, lse, dO, dq, dk, dv, B, H, Hkv, T, d, scale, window=0, global_every=0,
+           softcap=0.0, stream=None):
+    return _call_bwd(_lib.fa_bwd, q, k, v, o, lse, dO, dq, dk, dv, B, H, Hkv, T, d, scale,
+                     window, global_every, softcap, stream)
+
+
+def fa_bwd_f32(q, k, v, o, lse, dO, dq, dk, dv, B, H, Hkv, T, d, scale, window=0,
+               global_every=0, softcap=0.0, stream=None):
+    return _call_bwd(_lib.fa_bwd_f32, q, k, v, o, lse, dO, dq, dk, dv, B, H, Hkv, T, d, scale,
+                     window, global_every, softcap, stream)
+
+
+def _rope_call(fn, x, y, inv_freq, B, H, T, d, stream):
+    return _check(fn(_ptr(x), _ptr(y), _ptr(inv_freq), B, H, T, d, _stream(stream)))
+
+
+def rope_apply(x, y, inv_freq, B, H, T, d, stream=None):
+    return _rope_call(_lib.rope_apply, x, y, inv_freq, B, H, T, d, stream)
+
+
+def rope_apply_bwd(dy, dx, inv_freq, B, H, T, d, stream=None):
+    return _rope_call(_lib.rope_apply_bwd, dy, dx, inv_freq, B, H, T, d, stream)
+
+
+def rope_apply_f32(x, y, inv_freq, B, H, T, d, stream=None):
+    return _rope_call(_lib.rope_apply_f32, x, y, inv_freq, B, H, T, d, stream)
+
+
+def rope_apply_bwd_f32(dy, dx, inv_freq, B, H, T, d, stream=None):
+    return _rope_call(_lib.rope_apply_bwd_f32, dy, dx, inv_freq, B, H, T, d, stream)
+
+
+def fa_layer_window(layer: int, window: int, global_every: int) -> int:
+    r = _lib.fa_layer_window(layer, window, global_every)
+    if r < 0:
+        raise FAError(r, fa_last_error())
+    return r
+
+
+def fa_rope_inv_freq(d: int, theta: float) -> np.ndarray:
+    out = np.zeros(max(d // 2, 1), dtype=np.float32)
+    _check(_lib.fa_rope_inv_freq(out.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), d,
+                                 float(theta)))
+    return out[: d // 2]
+
+
+def fa_set_stage_events(events):
+    """Arm per-kernel stage events (a list of hipEvent_t handles as ints);
+    an empty list disarms."""
+    arr = (ctypes.c_void_p * max(len(events), 1))(*[int(e) for e in events])
+    return _check(_lib.fa_set_stage_events(arr, len(events)))
+
+
+# ------------------------------------------------------------ conveniences
+
+def _dims(q, k):
+    B, H, T, d = q.shape
+    Hkv = k.shape[1]
+    return B, H, Hkv, T, d
+
+
+def _need(t, dtype):
+    if not (t.is_cuda and t.is_contiguous() and t.dtype == dtype):
+        raise ValueError("expected contiguous device tensors of dtype " + str(dtype))
+
+
+def attention_forward(q, k, v, scale=None, window=0, global_every=0, softcap=0.0,
+                      stream=None):
+    """o, lse = attention(q [B,H,T,d], k/v [B,Hkv,T,d]) on the device."""
+    B, H, Hkv, T, d = _dims(q, k)
+    dt = q.dtype
+    for t in (q, k, v):
+        _need(t, dt)
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, T), dtype=torch.float32, device=q.device)
+    fn = fa_fwd_f32 if dt == torch.float32 else fa_fwd
+    fn(q, k, v, o, lse, B, H, Hkv, T, d, scale, window, global_every, softcap, stream)
+    return o, lse
+
+
+def attention_backward(q, k, v, o, lse, do, scale=None, window=0, global_every=0,
+                       softcap=0.0, stream=None):
+    B, H, Hkv, T, d = _dims(q, k)
+    dt = q.dtype
+    for t in (q, k, v, o, do):
+        _need(t, dt)
+    _need(lse, torch.float32)
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    fn = fa_bwd_f32 if dt == torch.float32 else fa_bwd
+    fn(q, k, v, o, lse, do, dq, dk, dv, B, H, Hkv, T, d, scale, window, global_every, softcap,
+       stream)
+    return dq, dk, dv
+
+
+def rope(x, inv_freq, out=None, backward=False, stream=None):
+    """RoPE of x [B,H,T,d] with a device fp32 table [d/2]; out may be x."""
+    B, H, T, d = x.shape
+    y = torch.empty_like(x) if out is None else out
+    if x.dtype == torch.float32:
+        fn = rope_apply_bwd_f32 if backward else rope_apply_f32
+    else:
+        fn = rope_apply_bwd if backward else rope_apply
+    fn(x, y, inv_freq, B, H, T, d, stream)
+    return y
+
+
+class FlashAttention(torch.autograd.Function):
+    """torch.autograd wrapper: forward = fa_fwd, backward = fa_bwd."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, scale, window, softcap):
+        o, lse = attention_forward(q, k, v, scale, window, 0, softcap)
+        ctx.save_for_backward(q, k, v, o, lse)
+        ctx.cfg = (scale, window, softcap)
+        return o
+
+    @staticmethod
+    def backward(ctx, do):
+        q, k, v, o, lse = ctx.saved_tensors
+        scale, window, softcap = ctx.cfg
+        dq, dk, dv = attention_backward(q, k, v, o, lse, do.contiguous(), scale, window, 0,
+                                        softcap)
+        return dq, dk, dv, None, None, None

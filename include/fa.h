@@ -1,0 +1,144 @@
+/*
+ * fa.h -- C ABI of the MI355X (gfx950) fused causal flash-attention library
+ * (libfa.so).  Plain pointers and sizes only; no C++ or torch types.
+ *
+ * What the calls compute (sources are web pages, cited by title/section):
+ *
+ *   For batch b, query head h, key/value head g = h / (H / Hkv):
+ *     S[i,j]  = scale * <q[b,h,i,:], k[b,g,j,:]>
+ *     S'[i,j] = softcap * tanh(S[i,j] / softcap)   (softcap > 0; else S)
+ *               -- Forge ARCHITECTURES.md, implementation plan wave 2,
+ *                  item 9: cap*tanh(s/cap) on the pre-softmax scores.
+ *     key j is visible to query i iff j <= i and, for 0 < W < T,
+ *               j > i - W       -- ARCHITECTURES.md, plan wave 2, item 8:
+ *                  the causal mask becomes q-W < k <= q; out-of-window KV
+ *                  tiles are skipped by the loop bound, not masked.
+ *     lse[i]  = log sum_{j visible} exp(S'[i,j])   (natural log)
+ *     o[i]    = sum_{j visible} exp(S'[i,j] - lse[i]) v[b,g,j,:]
+ *   fa_bwd returns the gradients of sum(o * dO); the softcap backward uses
+ *   the exact derivative 1 - tanh^2 (Forge attention.h commit log, "Wave 2").
+ *   GQA (n_kv_heads < n_heads, n_heads % n_kv_heads == 0): Forge README and
+ *   forge-studio RESEARCH.md section 2 (config validations).
+ *
+ * Layouts (all contiguous, row-major, device memory, caller-owned):
+ *   q, o, dO, dq : [B, H,   T, d]
+ *   k, v, dk, dv : [B, Hkv, T, d]
+ *   lse          : [B, H, T] float32
+ *   x, y, dy, dx : [B, H, T, d] for rope_* (call once with H query heads for
+ *                  Q and once with Hkv heads for K)
+ *   inv_freq     : [d/2] float32, device memory (fa_rope_inv_freq fills a
+ *                  host array the caller copies over)
+ * Element type: bfloat16 for the un-suffixed calls, float32 for the _f32
+ * twins (which never round through bf16).  Pointers must be 16-byte aligned.
+ * q, k, v, o, lse, dq, dk, dv, dO must not overlap one another; rope's y may
+ * equal x (in place), and dx may equal dy.
+ *
+ * Parameters:
+ *   B, H, Hkv, T > 0; H % Hkv == 0; d in {64, 128, 256} for attention,
+ *   d even and > 0 for rope (d % 8 == 0 takes the vector path).
+ *   scale > 0 (1/sqrt(d) for plain attention; any positive value, e.g. a
+ *   query_pre_attn_scalar, is accepted).
+ *   window: 0 = full causal; 0 < window < T = sliding window of `window`
+ *   keys including the query itself; window >= T = full causal.
+ *   global_every >= 0: the model's local:global pattern knob; validated
+ *   here, resolved per layer by the caller with fa_layer_window().
+ *   softcap: 0 = off, > 0 = cap.
+ *
+ * Ownership and streams: every call only enqueues work on `stream` (NULL =
+ * the default stream) and returns; device faults surface at the caller's
+ * next synchronisation.  fa_bwd allocates a small float32 scratch
+ * ([B, H, T] row statistics) stream-ordered (hipMallocAsync/hipFreeAsync on
+ * `stream`); nothing else is allocated and no state persists between calls.
+ *
+ * Errors: 0 on success, else a negative FA_ERR_* code; fa_last_error()
+ * returns a thread-local message describing the most recent failure.
+ * Argument checks run before any HIP call, so an invalid argument never
+ * touches the device.  No C++ exception crosses this interface.
+ */
+#ifndef CAUSAL_FA_H
+#define CAUSAL_FA_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* hipStream_t;
+
+#define FA_OK 0
+#define FA_ERR_INVALID_ARG (-1) /* null pointer, non-positive size, H % Hkv,
+                                   odd d, window < 0, bad scale/softcap,
+                                   global_every < 0 */
+#define FA_ERR_UNSUPPORTED (-2) /* attention head size not 64/128/256 */
+#define FA_ERR_HIP (-3)         /* HIP runtime or launch error */
+
+/* Forward: o and lse from q, k, v (bf16 tensors, fp32 lse). */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int H, int Hkv, int T, int d, float scale, int window,
+           int global_every, float softcap, hipStream_t stream);
+
+/* Backward: dq, dk, dv from q, k, v, the forward's o and lse, and dO.
+ * dk and dv sum over the query heads of each KV group; all three are fully
+ * overwritten (no accumulation into the caller's buffers). */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o,
+           const float* lse, const void* dO, void* dq, void* dk, void* dv,
+           int B, int H, int Hkv, int T, int d, float scale, int window,
+           int global_every, float softcap, hipStream_t stream);
+
+/* RoPE on interleaved pairs (x[2i], x[2i+1]) at positions t = 0..T-1 with
+ * angle fl32(t * inv_freq[i]) (Forge README: interleaved pairs; Forge
+ * attention.h commit log, "Wave 1": kernels read a host-precomputed
+ * inverse-frequency table).  rope_apply rotates by +angle, rope_apply_bwd
+ * (its transpose) by -angle. */
+int rope_apply(const void* x, void* y, const float* inv_freq, int B, int H,
+               int T, int d, hipStream_t stream);
+int rope_apply_bwd(const void* dy, void* dx, const float* inv_freq, int B,
+                   int H, int T, int d, hipStream_t stream);
+
+/* float32 twins: same parameters and semantics, float32 tensors. */
+int fa_fwd_f32(const void* q, const void* k, const void* v, void* o,
+               float* lse, int B, int H, int Hkv, int T, int d, float scale,
+               int window, int global_every, float softcap,
+               hipStream_t stream);
+int fa_bwd_f32(const void* q, const void* k, const void* v, const void* o,
+               const float* lse, const void* dO, void* dq, void* dk,
+               void* dv, int B, int H, int Hkv, int T, int d, float scale,
+               int window, int global_every, float softcap,
+               hipStream_t stream);
+int rope_apply_f32(const void* x, void* y, const float* inv_freq, int B,
+                   int H, int T, int d, hipStream_t stream);
+int rope_apply_bwd_f32(const void* dy, void* dx, const float* inv_freq,
+                       int B, int H, int T, int d, hipStream_t stream);
+
+/* Host helpers (no device work). */
+
+/* Effective window of layer `layer` (0-based) of a local:global stack
+ * (Forge attention.h commit log, "Wave 2": sliding_window with
+ * sliding_global_every; ARCHITECTURES.md family table: Gemma 3 is 5 local
+ * to 1 global): returns 0 (global, full causal) when global_every > 0 and
+ * (layer + 1) % global_every == 0, else `window`.  Returns FA_ERR_INVALID_ARG
+ * for layer < 0, window < 0 or global_every < 0. */
+int fa_layer_window(int layer, int window, int global_every);
+
+/* Fills host_out[i] = theta^(-2i/d) for i < d/2 (computed in double,
+ * stored as float).  Returns 0, or FA_ERR_INVALID_ARG for a null pointer,
+ * odd or non-positive d, or theta <= 0. */
+int fa_rope_inv_freq(float* host_out, int d, double theta);
+
+/* Per-kernel timing for callers that measure (benchmarks, profilers):
+ * `events` are `count` (<= 16) hipEvent_t handles created by the caller.
+ * While armed (count > 0), every later call on this thread records
+ * events[0] on its stream before its first kernel and events[i] right
+ * after its i-th kernel launch, for i < count (fa_bwd launches 2 kernels
+ * for d <= 128 and 3 for d = 256; fa_fwd and rope_* launch 1).  count = 0
+ * disarms.  Returns 0, or FA_ERR_INVALID_ARG for count outside 0..16 or a
+ * null handle.  Thread-local state; no device work. */
+int fa_set_stage_events(void* const* events, int count);
+
+/* Thread-local text of the last failure ("" if none yet). */
+const char* fa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CAUSAL_FA_H */

@@ -1,0 +1,111 @@
+"""C-ABI contract tests that need no GPU: the library loads, exports every
+entry point the header declares, validates arguments before touching the
+device (each invalid call returns its error code and message), and the host
+helpers agree with the oracle's table and layer pattern."""
+import ctypes
+import math
+import os
+import re
+
+import numpy as np
+import pytest
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+HEADER = os.path.join(os.path.dirname(HERE), "include", "fa.h")
+
+fa = pytest.importorskip("causal_attention_fa_amd.fa",
+                         reason="libfa.so not built (python -m causal_attention_fa_amd.build)")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\**(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_symbols_exported():
+    names = header_functions()
+    assert set(names) == set(fa.EXPORTS), names
+    lib = ctypes.CDLL(fa.library_path())
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+# A fake, aligned, non-null pointer: validation fails before it is used.
+P = 1 << 20
+
+
+def _fwd(**kw):
+    a = dict(q=P, k=2 * P, v=3 * P, o=4 * P, lse=5 * P, B=1, H=2, Hkv=1, T=8, d=64,
+             scale=0.125, window=0, global_every=0, softcap=0.0)
+    a.update(kw)
+    return fa._lib.fa_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Hkv"],
+                          a["T"], a["d"], a["scale"], a["window"], a["global_every"],
+                          a["softcap"], None)
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(q=0), -1, "null pointer q"),
+    (dict(lse=0), -1, "null pointer lse"),
+    (dict(B=0), -1, "positive"),
+    (dict(T=-3), -1, "positive"),
+    (dict(H=3, Hkv=2), -1, "multiple of Hkv"),
+    (dict(d=63), -1, "even"),
+    (dict(d=96), -2, "64, 128 or 256"),
+    (dict(window=-1), -1, "window"),
+    (dict(global_every=-2), -1, "global_every"),
+    (dict(softcap=-1.0), -1, "softcap"),
+    (dict(softcap=float("nan")), -1, "softcap"),
+    (dict(scale=0.0), -1, "scale"),
+    (dict(scale=float("inf")), -1, "scale"),
+    (dict(q=P + 8), -1, "aligned"),
+    (dict(o=P), -1, "overlaps"),
+])
+def test_fwd_validation(kw, code, msg):
+    assert _fwd(**kw) == code
+    assert msg in fa.fa_last_error()
+
+
+def test_bwd_validation_and_overlap():
+    lib = fa._lib
+    args = [P, 2 * P, 3 * P, 4 * P, 5 * P, 6 * P, 7 * P, 8 * P, 9 * P]
+    rc = lib.fa_bwd(*args, 1, 2, 2, 8, 64, 0.125, 0, 0, 0.0, None)
+    # all ranges are 1 MiB apart and small: valid up to the device call, so
+    # only check invalid variants here
+    bad = list(args)
+    bad[7] = bad[0]  # dk aliases q
+    assert lib.fa_bwd(*bad, 1, 2, 2, 8, 64, 0.125, 0, 0, 0.0, None) == -1
+    assert "overlaps" in fa.fa_last_error()
+    assert lib.fa_bwd(*args, 1, 2, 2, 8, 64, 0.125, -5, 0, 0.0, None) == -1
+    assert lib.fa_bwd_f32(*args, 1, 2, 2, 8, 32, 0.125, 0, 0, 0.0, None) == -2
+    del rc
+
+
+def test_rope_validation():
+    lib = fa._lib
+    assert lib.rope_apply(0, P, 2 * P, 1, 1, 4, 64, None) == -1
+    assert lib.rope_apply(P, 2 * P, 3 * P, 1, 1, 4, 7, None) == -1
+    assert lib.rope_apply(P, P + 16, 3 * P, 1, 1, 4, 64, None) == -1
+    assert "overlaps" in fa.fa_last_error()
+    assert lib.rope_apply_bwd_f32(P, 2 * P, 3 * P, 0, 1, 4, 64, None) == -1
+
+
+def test_layer_window_matches_oracle():
+    from oracle import attention as OA
+    for ge in (0, 1, 2, 6):
+        for w in (0, 1, 1024, 4096):
+            for layer in range(13):
+                assert fa.fa_layer_window(layer, w, ge) == OA.layer_window(layer, w, ge)
+    with pytest.raises(fa.FAError):
+        fa.fa_layer_window(0, -1, 0)
+
+
+@pytest.mark.parametrize("d,theta", [(64, 1e4), (128, 1e6), (256, 1e4), (2, 5.0)])
+def test_inv_freq_matches_oracle(d, theta):
+    from oracle import rope as OR
+    got = fa.fa_rope_inv_freq(d, theta)
+    want = OR.inv_freq(d, theta)
+    # both round theta^(-2i/d) from double; allow one float32 ulp
+    np.testing.assert_array_max_ulp(got, want, maxulp=1)
+    with pytest.raises(fa.FAError):
+        fa.fa_rope_inv_freq(5, theta)
