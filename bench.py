@@ -108,6 +108,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="mistral")
+    ap.add_argument("--calibrate-copy-mb", type=float, default=0.0,
+                    help="only run a plain device copy of this many MiB (5 times) and "
+                         "exit: the reference kernel for scaling HBM byte counters")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="CPU-baseline budget: oracle heads are timed until this many "
                          "seconds have passed (0: skip)")
@@ -120,6 +123,16 @@ def main():
 
     import torch
     from causal_attention_fa_amd import fa, synth
+
+    if args.calibrate_copy_mb > 0:
+        n = int(args.calibrate_copy_mb * (1 << 20)) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration_copy_bytes": n * 4, "launches": 5}))
+        return
 
     w = synth.WORKLOADS[args.workload]
     if w.dtype != "bf16":
@@ -146,8 +159,8 @@ def main():
         e.record(stream)
         return e
 
-    n_bwd = 2 if d <= 128 else 3
-    bwd_names = ["bwd_dq", "bwd_dkdv"] if d <= 128 else ["bwd_dq", "bwd_dv", "bwd_dk"]
+    bwd_names = ["bwd_dq", "bwd_dv", "bwd_dk"]   # the three launches of fa_bwd
+    n_bwd = len(bwd_names)
 
     def step(ev=None):
         if rope:

@@ -24,6 +24,9 @@ constexpr float kLn2 = 0.6931471805599453f;
 // Running-max start value: finite, so exp2(m_old - m_new) never sees
 // (-inf) - (-inf) when a row's first tiles are fully masked.
 constexpr float kMaxInit = -1.0e30f;
+// Headroom (log2 units) the online softmax allows before rescaling: p
+// values stay below 2^8, comfortably inside fp32 and bf16 range.
+constexpr float kRescaleSlack = 8.0f;
 
 // v_mfma_f32_32x32x16_bf16.  Operand layout (measured on gfx950):
 //   A: lane l holds A[row = l%32][k = 8*(l/32) + j], j = 0..7
@@ -136,6 +139,33 @@ __device__ __forceinline__ bf16x8 lds_tr_operand(const LDS_AS char* tile, int ro
   typedef short s16x8 __attribute__((ext_vector_type(8)));
   s16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   return __builtin_bit_cast(bf16x8, v);
+}
+
+// acc[t] = sum_c A_t(c) B(c) over the D/16 chunks of d, where A_t(c) is
+// the row operand of rows 32t.. of `tile` (read from LDS) and B(c) = breg[c]
+// lives in registers: NS independent 32x32 accumulators.  The LDS operands
+// of chunk c+1 are requested before the MFMAs of chunk c so their latency
+// overlaps the matrix work.
+template <int D, int NS>
+__device__ __forceinline__ void mma_rows(f32x16 (&acc)[NS], const LDS_AS char* tile,
+                                         const bf16x8 (&breg)[D / 16], int lane) {
+  constexpr int NC = D / 16;
+  bf16x8 op[2][NS];
+#pragma unroll
+  for (int t = 0; t < NS; ++t) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[t][i] = 0.f;
+    op[0][t] = lds_row_operand<D>(tile, 32 * t, 0, lane);
+  }
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    if (c + 1 < NC) {
+#pragma unroll
+      for (int t = 0; t < NS; ++t) op[(c + 1) & 1][t] = lds_row_operand<D>(tile, 32 * t, c + 1, lane);
+    }
+#pragma unroll
+    for (int t = 0; t < NS; ++t) acc[t] = mfma32(op[c & 1][t], breg[c], acc[t]);
+  }
 }
 
 // Pack accumulators acc[8*h .. 8*h+7] of a 32x32 tile to 8 bf16 (RNE): the

@@ -8,20 +8,20 @@
 //   dS = dS' * (1 - tanh^2) (softcap),  dq = scale dS K,
 //   dk = scale dS^T Q,  dv = P^T dO  (dk, dv summed over the GQA group).
 //
-// Two kernels, both deterministic (no atomics):
+// Three launches, all deterministic (no atomics):
 //   1. fa_bwd_dq_kernel -- query-parallel, the forward's structure: each
 //      lane owns one query row; S^T = K Q^T and dP^T = V dO^T come out with
 //      the query along the lane, so lse, D and the softcap chain are
 //      per-lane scalars; dQ^T += K^T dS^T reads K^T through the LDS
 //      transpose read.  It also computes D_i for its rows (the backward
 //      prologue) and writes it to a [B, H, T] fp32 scratch for kernel 2.
-//   2. fa_bwd_dkdv_kernel -- key-parallel: a workgroup owns 128 key rows of
-//      one (b, kv head) and loops over the query heads of the GQA group and
-//      over the query tiles that can see its keys (the window bounds the
-//      loop).  Each lane owns one key row: K and V stay in registers as the
-//      B operands of S = Q K^T and dP = dO V^T, and dV^T += dO^T P,
-//      dK^T += Q^T dS take dO^T and Q^T from the natural tiles through the
-//      LDS transpose read.
+//   2./3. fa_bwd_dkdv_kernel, once for dV and once for dK -- key-parallel:
+//      a workgroup owns 128 key rows of one (b, kv head) and loops over the
+//      query heads of the GQA group and over the query tiles that can see
+//      its keys (the window bounds the loop).  Each lane owns one key row:
+//      K and V stay in registers as the B operands of S = Q K^T and
+//      dP = dO V^T, and dV^T += dO^T P, dK^T += Q^T dS take dO^T and Q^T
+//      from the natural tiles through the LDS transpose read.
 #include "device_common.h"
 #include "internal.h"
 
@@ -118,29 +118,18 @@ __global__ __launch_bounds__(256, (D >= 256 ? 1 : 2)) void fa_bwd_dq_kernel(BwdA
     const LDS_AS char* Vt = lds + (2 + cur) * TILE;
     const bool more = j + 1 < ntiles;
     const int nrow = (t_lo + j + 1) * BKV;
-    if (more) kst.load(Kp, nrow, T, tid);
+    // next K, V tiles: loads now, LDS stores after this tile's MFMAs
+    if (more) {
+      kst.load(Kp, nrow, T, tid);
+      vst.load(Vp, nrow, T, tid);
+    }
     const int kv0 = (t_lo + j) * BKV;
     const bool empty = qa >= T || kv0 > qb || (W > 0 && kv0 + BKV - 1 <= qa - W);
     const bool full = kv0 + BKV - 1 <= qa && (W == 0 || kv0 > qb - W);
     f32x16 s[NS], dp[NS];
     if (!empty) {
-#pragma unroll
-      for (int t = 0; t < NS; ++t) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          s[t][i] = 0.f;
-          dp[t][i] = 0.f;
-        }
-#pragma unroll
-        for (int c = 0; c < D / 16; ++c) {
-          s[t] = mfma32(lds_row_operand<D>(Kt, 32 * t, c, lane), qreg[c], s[t]);
-          dp[t] = mfma32(lds_row_operand<D>(Vt, 32 * t, c, lane), doreg[c], dp[t]);
-        }
-      }
-    }
-    if (more) {
-      kst.store(lds + (cur ^ 1) * TILE, tid);
-      vst.load(Vp, nrow, T, tid);
+      mma_rows<D, NS>(s, Kt, qreg, lane);
+      mma_rows<D, NS>(dp, Vt, doreg, lane);
     }
     if (!empty) {
       // dS^T in s[] (fp32), then bf16 operands.
@@ -148,12 +137,16 @@ __global__ __launch_bounds__(256, (D >= 256 ? 1 : 2)) void fa_bwd_dq_kernel(BwdA
       for (int t = 0; t < NS; ++t)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          float th;
-          const float s2 = score_log2<CAP>(s[t][i], a, th);
-          float p = fast_exp2(s2 - lse2);
+          float th, p;
+          if (CAP) {
+            p = fast_exp2(score_log2<CAP>(s[t][i], a, th) - lse2);
+          } else {
+            th = 0.f;
+            p = fast_exp2(fmaf(s[t][i], a.scale_log2e, -lse2));
+          }
           if (!full) {
             const int kv = kv0 + 32 * t + acc_row(i, g);
-            const bool vis = kv <= qrow && (W == 0 || kv > qrow - W);
+            const bool vis = (kv <= qrow) & ((W == 0) | (kv > qrow - W));
             p = vis ? p : 0.f;
           }
           float ds = p * (dp[t][i] - Di);
@@ -174,7 +167,10 @@ __global__ __launch_bounds__(256, (D >= 256 ? 1 : 2)) void fa_bwd_dq_kernel(BwdA
         for (int db = 0; db < NDB; ++db)
           dqacc[db] = mfma32(lds_tr_operand<D>(Kt, 0, c16, 32 * db, lane), dsb[c16], dqacc[db]);
     }
-    if (more) vst.store(lds + (2 + (cur ^ 1)) * TILE, tid);
+    if (more) {
+      kst.store(lds + (cur ^ 1) * TILE, tid);
+      vst.store(lds + (2 + (cur ^ 1)) * TILE, tid);
+    }
     __syncthreads();
   }
 
@@ -193,12 +189,13 @@ __global__ __launch_bounds__(256, (D >= 256 ? 1 : 2)) void fa_bwd_dq_kernel(BwdA
 }
 
 // ----------------------------------------------------------------- dK/dV pass
-// MODE 0 accumulates dK and dV together; for d = 256 the two accumulators
-// (2 x 128 registers per lane) do not fit beside K, V and the tiles, so the
-// pass runs twice: MODE 1 accumulates dV only (needs S, P), MODE 2 dK only
-// (needs S, dP, dS) -- one extra S = Q K^T product instead of spilling.
+// MODE 0 accumulates dK and dV together.  Both accumulators (2 x D/2
+// registers per lane) beside K, V and the tiles exceed the 256 registers
+// that two waves per SIMD allow, so the pass runs as two launches instead:
+// MODE 1 accumulates dV only (needs S, P), MODE 2 dK only (needs S, dP,
+// dS) -- one extra S = Q K^T product buys twice the occupancy.
 template <int D, int BQB, bool CAP, int MODE>
-__global__ __launch_bounds__(256, 1) void fa_bwd_dkdv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256, (D >= 256 ? 1 : 2)) void fa_bwd_dkdv_kernel(BwdArgs a) {
   constexpr bool DO_DV = MODE != 2;
   constexpr bool DO_DK = MODE != 1;
   constexpr int NW = 4;
@@ -288,32 +285,19 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_dkdv_kernel(BwdArgs a) {
     const LDS_AS float* lse2t = (const LDS_AS float*)(stat + cur * 2 * STAT);
     const LDS_AS float* Dt = lse2t + BQB;
     const bool more = it + 1 < niter;
-    // Next Q tile loads now (stored once S is done), next dO tile and row
-    // statistics after that (stored at the end): one staging set live.
-    if (more) qst.load(tile_src(it + 1, a.q), tile_q0(it + 1), T, tid);
+    // next Q, dO tiles and row statistics: loads now, LDS stores at the end
+    if (more) {
+      qst.load(tile_src(it + 1, a.q), tile_q0(it + 1), T, tid);
+      dost.load(tile_src(it + 1, a.dO), tile_q0(it + 1), T, tid);
+      stage_stats(it + 1);
+    }
     const int q0 = tile_q0(it);
     const bool empty = ka >= T || q0 + BQB - 1 < ka || (W > 0 && q0 - kb >= W);
     const bool full = q0 >= kb && q0 + BQB <= T && (W == 0 || q0 + BQB - 1 - ka < W);
     f32x16 s[NS], dp[NS];
     if (!empty) {
-#pragma unroll
-      for (int t = 0; t < NS; ++t) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          s[t][i] = 0.f;
-          dp[t][i] = 0.f;
-        }
-#pragma unroll
-        for (int c = 0; c < D / 16; ++c) {
-          s[t] = mfma32(lds_row_operand<D>(Qt, 32 * t, c, lane), kreg[c], s[t]);
-          if (DO_DK) dp[t] = mfma32(lds_row_operand<D>(dOt, 32 * t, c, lane), vreg[c], dp[t]);
-        }
-      }
-    }
-    if (more) {
-      qst.store(lds + (cur ^ 1) * TILE, tid);
-      dost.load(tile_src(it + 1, a.dO), tile_q0(it + 1), T, tid);
-      stage_stats(it + 1);
+      mma_rows<D, NS>(s, Qt, kreg, lane);
+      if (DO_DK) mma_rows<D, NS>(dp, dOt, vreg, lane);
     }
     if (!empty) {
       // S, dP: lane = key row, accumulator i = query row 32t + acc_row(i, g).
@@ -328,12 +312,16 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int i = 4 * i4 + e;
-            float th;
-            const float s2 = score_log2<CAP>(s[t][i], a, th);
-            float p = fast_exp2(s2 - l4[e]);
+            float th, p;
+            if (CAP) {
+              p = fast_exp2(score_log2<CAP>(s[t][i], a, th) - l4[e]);
+            } else {
+              th = 0.f;
+              p = fast_exp2(fmaf(s[t][i], a.scale_log2e, -l4[e]));
+            }
             if (!full) {
               const int q = q0 + qloc + e;
-              const bool vis = q < T && krow <= q && (W == 0 || krow > q - W);
+              const bool vis = (q < T) & (krow <= q) & ((W == 0) | (krow > q - W));
               p = vis ? p : 0.f;
             }
             s[t][i] = p;
@@ -367,6 +355,7 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_dkdv_kernel(BwdArgs a) {
         }
     }
     if (more) {
+      qst.store(lds + (cur ^ 1) * TILE, tid);
       dost.store(lds + (2 + (cur ^ 1)) * TILE, tid);
       if (tid < 2 * BQB) *(LDS_AS float*)(stat + (cur ^ 1) * 2 * STAT + tid * 4) = stv;
     }
@@ -402,17 +391,12 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 kgrid((unsigned)((a.T + 127) / 128) * a.B * a.Hkv);
-  if constexpr (D <= 128) {
-    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, BQB, CAP, 0>), kgrid, dim3(256), 0, stream, a);
-    stage_mark(stream);
-  } else {
-    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, BQB, CAP, 1>), kgrid, dim3(256), 0, stream, a);
-    stage_mark(stream);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, BQB, CAP, 2>), kgrid, dim3(256), 0, stream, a);
-    stage_mark(stream);
-  }
+  hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, BQB, CAP, 1>), kgrid, dim3(256), 0, stream, a);
+  stage_mark(stream);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, BQB, CAP, 2>), kgrid, dim3(256), 0, stream, a);
+  stage_mark(stream);
   return hipGetLastError();
 }
 

@@ -12,8 +12,8 @@
 //     S^T) and the online-softmax max/sum are per-lane values combined with
 //     the partner lane l^32 -- no cross-lane row reductions inside a tile;
 //   * K and V tiles (BKV keys) stream through LDS, double-buffered: the next
-//     tile's global loads are issued into registers ahead of the MFMAs that
-//     hide them and written to the idle padded LDS buffer after;
+//     tile's global loads are issued into registers at the top of an
+//     iteration and written to the idle padded LDS buffers at its end;
 //   * P^T leaves the S^T accumulators as bf16 and is directly the B operand
 //     of O^T += V^T P^T; V^T comes from the natural V tile through the
 //     gfx950 LDS transpose read, so nothing is transposed in registers;
@@ -91,44 +91,30 @@ __global__ __launch_bounds__(256, (D >= 256 ? 1 : 2)) void fa_fwd_kernel(FwdArgs
     const LDS_AS char* Vt = lds + (2 + cur) * TILE;
     const bool more = j + 1 < ntiles;
     const int nrow = (t_lo + j + 1) * BKV;
-    // Next K tile: loads issued now, written to the idle buffer once this
-    // tile's scores are done; the V tile follows the same pattern around
-    // the P V product, so only one staging set is live at a time.
-    if (more) kst.load(Kp, nrow, T, tid);
+    // Next K and V tiles: global loads issued now, written to the idle
+    // buffers after this tile's MFMAs, so their latency hides behind a
+    // whole iteration.
+    if (more) {
+      kst.load(Kp, nrow, T, tid);
+      vst.load(Vp, nrow, T, tid);
+    }
     const int kv0 = (t_lo + j) * BKV;
     const bool empty = qa >= T || kv0 > qb || (W > 0 && kv0 + BKV - 1 <= qa - W);
     const bool full = kv0 + BKV - 1 <= qa && (W == 0 || kv0 > qb - W);
     f32x16 s[NS];
+    if (!empty) mma_rows<D, NS>(s, Kt, qreg, lane);
     if (!empty) {
+      // Scores in the log2 domain.  Without a cap the scale is folded into
+      // the exponent's FMA below (the max of raw scores scales with it).
+      if (CAP) {
 #pragma unroll
-      for (int t = 0; t < NS; ++t) {
+        for (int t = 0; t < NS; ++t)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) s[t][i] = 0.f;
-#pragma unroll
-        for (int c = 0; c < D / 16; ++c)
-          s[t] = mfma32(lds_row_operand<D>(Kt, 32 * t, c, lane), qreg[c], s[t]);
-      }
-    }
-    if (more) {
-      kst.store(lds + (cur ^ 1) * TILE, tid);
-      vst.load(Vp, nrow, T, tid);
-    }
-    if (!empty) {
-      float mt = -INFINITY;
-#pragma unroll
-      for (int t = 0; t < NS; ++t) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float x = s[t][i];
-          if (CAP) {
-            // cap * tanh(scale*x / cap), carried in the log2 domain
-            const float e = fast_exp2(x * a.two_scale_over_cap_log2e);
-            x = (1.f - 2.f * __builtin_amdgcn_rcpf(e + 1.f)) * a.cap_log2e;
-          } else {
-            x *= a.scale_log2e;
+          for (int i = 0; i < 16; ++i) {
+            // cap * tanh(scale*x / cap) * log2(e)
+            const float e = fast_exp2(s[t][i] * a.two_scale_over_cap_log2e);
+            s[t][i] = (1.f - 2.f * __builtin_amdgcn_rcpf(e + 1.f)) * a.cap_log2e;
           }
-          s[t][i] = x;
-        }
       }
       if (!full) {
 #pragma unroll
@@ -136,32 +122,40 @@ __global__ __launch_bounds__(256, (D >= 256 ? 1 : 2)) void fa_fwd_kernel(FwdArgs
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int kv = kv0 + 32 * t + acc_row(i, g);
-            const bool vis = kv <= qrow && (W == 0 || kv > qrow - W);
+            const bool vis = (kv <= qrow) & ((W == 0) | (kv > qrow - W));
             s[t][i] = vis ? s[t][i] : -INFINITY;
           }
       }
+      const float c = CAP ? 1.f : a.scale_log2e;
+      float mt = -INFINITY;
 #pragma unroll
       for (int t = 0; t < NS; ++t)
 #pragma unroll
         for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[t][i]);
-      mt = xor32_max(mt);
-      const float mnew = fmaxf(m, mt);
-      const float alpha = fast_exp2(m - mnew);
-      m = mnew;
+      mt = xor32_max(mt) * c;
+      // Lazy rescaling: the running max m only moves (and O, l are rescaled)
+      // when some row's tile max exceeds it by more than kRescaleSlack, so
+      // p = 2^(s - m) stays below 2^kRescaleSlack; the branch is uniform.
+      if (__any(mt > m + kRescaleSlack)) {
+        const float mnew = fmaxf(m, mt);
+        const float alpha = fast_exp2(m - mnew);
+        m = mnew;
+        lsum *= alpha;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+      }
       float ps = 0.f;
 #pragma unroll
       for (int t = 0; t < NS; ++t)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const float p = fast_exp2(s[t][i] - mnew);
+          const float p = fast_exp2(fmaf(s[t][i], c, -m));
           s[t][i] = p;
           ps += p;
         }
-      lsum = lsum * alpha + ps;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+      lsum += ps;
       bf16x8 pb[BKV / 16];
 #pragma unroll
       for (int c16 = 0; c16 < BKV / 16; ++c16) {
@@ -176,7 +170,10 @@ __global__ __launch_bounds__(256, (D >= 256 ? 1 : 2)) void fa_fwd_kernel(FwdArgs
         for (int db = 0; db < NDB; ++db)
           oacc[db] = mfma32(lds_tr_operand<D>(Vt, 0, c16, 32 * db, lane), pb[c16], oacc[db]);
     }
-    if (more) vst.store(lds + (2 + (cur ^ 1)) * TILE, tid);
+    if (more) {
+      kst.store(lds + (cur ^ 1) * TILE, tid);
+      vst.store(lds + (2 + (cur ^ 1)) * TILE, tid);
+    }
     __syncthreads();
   }
 

@@ -128,8 +128,8 @@ int fa_rope_inv_freq(float* host_out, int d, double theta);
  * `events` are `count` (<= 16) hipEvent_t handles created by the caller.
  * While armed (count > 0), every later call on this thread records
  * events[0] on its stream before its first kernel and events[i] right
- * after its i-th kernel launch, for i < count (fa_bwd launches 2 kernels
- * for d <= 128 and 3 for d = 256; fa_fwd and rope_* launch 1).  count = 0
+ * after its i-th kernel launch, for i < count (fa_bwd launches 3 kernels:
+ * dq, dv, dk; fa_fwd and rope_* launch 1).  count = 0
  * disarms.  Returns 0, or FA_ERR_INVALID_ARG for count outside 0..16 or a
  * null handle.  Thread-local state; no device work. */
 int fa_set_stage_events(void* const* events, int count);
