@@ -55,23 +55,30 @@ __device__ __forceinline__ float xor32_sum(float x) {
 }
 
 // ---------------------------------------------------------------- LDS tiles
-// A tile of ROWS x D bf16 lives in LDS row-major with a padded row stride
-// of D*2 + 48 bytes.  With 64 LDS banks (256 bytes per cycle) that stride
-// (48 mod 256) is conflict-free for both read patterns used here:
-//   * 16-byte row reads of 16 consecutive rows, same column (row operands):
-//     3r mod 16 hits 16 distinct 16-byte bank groups;
-//   * transpose reads, 4 consecutive rows x 32 contiguous bytes per 16
-//     lanes: [0,32), [48,80), [96,128), [144,176) do not overlap.
-// Padding (not an XOR swizzle) keeps every operand address a per-lane base
-// plus a compile-time immediate, so the unrolled loops need no extra
-// address registers.
+// A tile of ROWS x D bf16 lives in LDS in rows of D*2 + 64 bytes (stride
+// = 16 mod 64 dwords), with the 16-byte chunks of each aligned 64-byte
+// group permuted by XOR with (row >> 2) & 3.  Measured on gfx950 (64 banks,
+// 16 lanes per cycle for 16-byte reads, 32 lanes for the 8-byte transpose
+// reads), this is conflict-free for both read patterns used here:
+//   * 16-byte row reads of 16 consecutive rows, one column (row operands):
+//     rows 4a+b land on dword 16b + 4*(chunk ^ a): 16 distinct groups;
+//   * transpose reads, 4 consecutive rows x 64 contiguous bytes per 32
+//     lanes: the rows start 16 dwords apart and the XOR stays inside each
+//     row's 64-byte group.
+// The XOR touches only the two low chunk bits, so every operand address is
+// a per-lane base plus a compile-time immediate (no extra address
+// registers in the unrolled loops).
 template <int D>
 struct Lay {
-  static constexpr int STRIDE = D * 2 + 48;
+  static constexpr int STRIDE = D * 2 + 64;
   static constexpr int CPR = D / 8;  // 16-byte chunks per row
   template <int ROWS>
   static constexpr int bytes() { return ROWS * STRIDE; }
-  __device__ __forceinline__ static int off(int r, int col) { return r * STRIDE + col * 2; }
+  // byte offset of element (r, col); col a multiple of 4
+  __device__ __forceinline__ static int off(int r, int col) {
+    return r * STRIDE + ((((col >> 3) ^ (r >> 2)) & 3) | ((col >> 3) & ~3)) * 16 +
+           ((col & 7) << 1);
+  }
 };
 
 // Register-staged tile copy: global -> registers (issued early, so the
@@ -178,11 +185,15 @@ __device__ __forceinline__ bf16x8 pack_bf16(const float* x) {
 }
 
 // ---------------------------------------------------------------- work map
-// Workgroups are numbered heavy-first (the last query blocks of a causal
-// layer have the most key tiles) and, when the count allows, the G
-// workgroups that share one KV head (a GQA group) are placed on the same
-// XCD (dispatch assigns workgroup i to XCD i % 8) so K/V tiles are reused
-// from that XCD's L2.
+// A unit is one (batch, KV head, block); a unit runs as G workgroups, one
+// per query head of the GQA group (G = 1 for the key-parallel pass).  The
+// dispatcher hands workgroup i to XCD i % 8.  When the (batch, KV head)
+// pairs divide evenly over the 8 XCDs, XCD x is given a contiguous run of
+// units -- whole heads, block after block -- so the workgroups running
+// together on one XCD share their K/V (or Q/dO) windows in that XCD's
+// 4 MB L2 instead of streaming them from HBM; otherwise units are dealt
+// round-robin.  Within a head, blocks run heaviest first (`reverse` =
+// true counts query blocks down: the last ones see the most keys).
 struct WorkItem {
   int blk;   // query-block (or key-block) index
   int b;
@@ -192,24 +203,24 @@ struct WorkItem {
 
 __device__ __forceinline__ WorkItem decode_work(int id, int nblk, int B, int Hkv, int G,
                                                 bool reverse) {
-  const int units = nblk * B * Hkv;
+  const int heads = B * Hkv;
+  const int units = nblk * heads;
   int u, r;
-  if ((units & 7) == 0) {
+  if ((heads & 7) == 0) {
     const int x = id & 7;
     const int j = id >> 3;
     r = j % G;
-    u = (j / G) * 8 + x;
+    u = x * (units >> 3) + j / G;
   } else {
     u = id / G;
     r = id % G;
   }
   WorkItem w;
-  const int per = B * Hkv;
-  const int bi = u / per;
-  const int rest = u % per;
+  const int bhkv = u / nblk;
+  const int bi = u % nblk;
   w.blk = reverse ? nblk - 1 - bi : bi;
-  w.b = rest / Hkv;
-  w.hkv = rest % Hkv;
+  w.b = bhkv / Hkv;
+  w.hkv = bhkv % Hkv;
   w.r = r;
   return w;
 }

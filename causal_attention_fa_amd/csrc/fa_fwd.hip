@@ -25,10 +25,14 @@
 
 namespace fa {
 
-template <int D, int BKV, bool CAP>
-__global__ __launch_bounds__(256, (D >= 256 ? 1 : 2)) void fa_fwd_kernel(FwdArgs a) {
-  constexpr int NW = 4;
-  constexpr int BQ = 32 * NW;
+#ifndef FWD_NW
+#define FWD_NW 4
+#endif
+
+template <int D, int BKV, int NW, bool CAP>
+__global__ __launch_bounds__(64 * NW, (D >= 256 ? 1 : 8 / NW)) void fa_fwd_kernel(FwdArgs a) {
+  constexpr int NT = 64 * NW;        // threads per workgroup
+  constexpr int BQ = 32 * NW;        // query rows per workgroup
   constexpr int TILE = Lay<D>::template bytes<BKV>();  // one K or V tile
   constexpr int NDB = D / 32;        // 32-wide d blocks of the output
   constexpr int NS = BKV / 32;       // 32-key sub-tiles
@@ -77,7 +81,7 @@ __global__ __launch_bounds__(256, (D >= 256 ? 1 : 2)) void fa_fwd_kernel(FwdArgs
   float m = kMaxInit;
   float lsum = 0.f;
 
-  TileStage<D, BKV, 256> kst, vst;
+  TileStage<D, BKV, NT> kst, vst;
   kst.load(Kp, t_lo * BKV, T, tid);
   vst.load(Vp, t_lo * BKV, T, tid);
   kst.store(lds, tid);
@@ -194,23 +198,23 @@ __global__ __launch_bounds__(256, (D >= 256 ? 1 : 2)) void fa_fwd_kernel(FwdArgs
   }
 }
 
-template <int D, int BKV>
+template <int D, int BKV, int NW>
 static hipError_t launch_fwd_d(const FwdArgs& a, hipStream_t stream) {
-  const int nqb = (a.T + 127) / 128;
+  const int nqb = (a.T + 32 * NW - 1) / (32 * NW);
   const dim3 grid((unsigned)nqb * a.B * a.H);
   if (a.cap_log2e > 0.f)
-    hipLaunchKernelGGL((fa_fwd_kernel<D, BKV, true>), grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((fa_fwd_kernel<D, BKV, NW, true>), grid, dim3(64 * NW), 0, stream, a);
   else
-    hipLaunchKernelGGL((fa_fwd_kernel<D, BKV, false>), grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((fa_fwd_kernel<D, BKV, NW, false>), grid, dim3(64 * NW), 0, stream, a);
   stage_mark(stream);
   return hipGetLastError();
 }
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, int d, hipStream_t stream) {
   switch (d) {
-    case 64: return launch_fwd_d<64, 64>(a, stream);
-    case 128: return launch_fwd_d<128, 64>(a, stream);
-    case 256: return launch_fwd_d<256, 32>(a, stream);
+    case 64: return launch_fwd_d<64, 64, FWD_NW>(a, stream);
+    case 128: return launch_fwd_d<128, 64, FWD_NW>(a, stream);
+    case 256: return launch_fwd_d<256, 32, FWD_NW>(a, stream);
   }
   return hipErrorInvalidValue;
 }
