@@ -40,9 +40,9 @@ __device__ __forceinline__ float score_log2(float x, const BwdArgs& a, float& th
 }
 
 // ------------------------------------------------------------------ dQ pass
-template <int D, int BKV, bool CAP>
-__global__ __launch_bounds__(256, (D >= 256 ? 1 : 2)) void fa_bwd_dq_kernel(BwdArgs a) {
-  constexpr int NW = 4;
+template <int D, int BKV, int NW, bool CAP>
+__global__ __launch_bounds__(64 * NW, (D >= 256 ? 1 : 8 / NW)) void fa_bwd_dq_kernel(BwdArgs a) {
+  constexpr int NT = 64 * NW;
   constexpr int BQ = 32 * NW;
   constexpr int TILE = Lay<D>::template bytes<BKV>();
   constexpr int NDB = D / 32;
@@ -104,7 +104,7 @@ __global__ __launch_bounds__(256, (D >= 256 ? 1 : 2)) void fa_bwd_dq_kernel(BwdA
 #pragma unroll
     for (int i = 0; i < 16; ++i) dqacc[db][i] = 0.f;
 
-  TileStage<D, BKV, 256> kst, vst;
+  TileStage<D, BKV, NT> kst, vst;
   kst.load(Kp, t_lo * BKV, T, tid);
   vst.load(Vp, t_lo * BKV, T, tid);
   kst.store(lds, tid);
@@ -194,11 +194,11 @@ __global__ __launch_bounds__(256, (D >= 256 ? 1 : 2)) void fa_bwd_dq_kernel(BwdA
 // that two waves per SIMD allow, so the pass runs as two launches instead:
 // MODE 1 accumulates dV only (needs S, P), MODE 2 dK only (needs S, dP,
 // dS) -- one extra S = Q K^T product buys twice the occupancy.
-template <int D, int BQB, bool CAP, int MODE>
-__global__ __launch_bounds__(256, (D >= 256 ? 1 : 2)) void fa_bwd_dkdv_kernel(BwdArgs a) {
+template <int D, int BQB, int NW, bool CAP, int MODE>
+__global__ __launch_bounds__(64 * NW, (D >= 256 ? 1 : 8 / NW)) void fa_bwd_dkdv_kernel(BwdArgs a) {
   constexpr bool DO_DV = MODE != 2;
   constexpr bool DO_DK = MODE != 1;
-  constexpr int NW = 4;
+  constexpr int NT = 64 * NW;
   constexpr int BKVB = 32 * NW;        // key rows per workgroup
   constexpr int TILE = Lay<D>::template bytes<BQB>();  // one Q or dO tile
   constexpr int NDB = D / 32;
@@ -251,7 +251,7 @@ __global__ __launch_bounds__(256, (D >= 256 ? 1 : 2)) void fa_bwd_dkdv_kernel(Bw
       dvacc[db][i] = 0.f;
     }
 
-  TileStage<D, BQB, 256> qst, dost;
+  TileStage<D, BQB, NT> qst, dost;
   float stv = 0.f;
   auto stage_stats = [&](int it) {
     const int hh = w.hkv * G + it / nqt;
@@ -382,35 +382,53 @@ __global__ __launch_bounds__(256, (D >= 256 ? 1 : 2)) void fa_bwd_dkdv_kernel(Bw
   }
 }
 
-template <int D, int BKV, int BQB, bool CAP>
+// Tile shapes per head size: dq pass (BKV keys per tile, NW waves), dV pass
+// and dK pass (BQB queries per tile, NW waves).
+// Tile shapes per head size: dq pass (keys per tile, waves), dV pass and
+// dK pass (queries per tile, waves); chosen by measurement on MI355X.
+#ifndef BWD64_CFG
+#define BWD64_CFG 64, 4, 64, 4, 64, 4
+#endif
+#ifndef BWD256_CFG
+#define BWD256_CFG 32, 4, 64, 4, 32, 4
+#endif
+#ifndef BWD128_CFG
+#define BWD128_CFG 32, 8, 64, 8, 32, 8
+#endif
+
+template <int D, bool CAP, int DQ_BKV, int DQ_NW, int DV_BQB, int DV_NW, int DK_BQB, int DK_NW>
 static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
-  const int nqb = (a.T + 127) / 128;
-  hipLaunchKernelGGL((fa_bwd_dq_kernel<D, BKV, CAP>), dim3((unsigned)nqb * a.B * a.H),
-                     dim3(256), 0, stream, a);
+  const int nqb = (a.T + 32 * DQ_NW - 1) / (32 * DQ_NW);
+  hipLaunchKernelGGL((fa_bwd_dq_kernel<D, DQ_BKV, DQ_NW, CAP>), dim3((unsigned)nqb * a.B * a.H),
+                     dim3(64 * DQ_NW), 0, stream, a);
   stage_mark(stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const dim3 kgrid((unsigned)((a.T + 127) / 128) * a.B * a.Hkv);
-  hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, BQB, CAP, 1>), kgrid, dim3(256), 0, stream, a);
+  const dim3 vgrid((unsigned)((a.T + 32 * DV_NW - 1) / (32 * DV_NW)) * a.B * a.Hkv);
+  hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, DV_BQB, DV_NW, CAP, 1>), vgrid, dim3(64 * DV_NW), 0,
+                     stream, a);
   stage_mark(stream);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, BQB, CAP, 2>), kgrid, dim3(256), 0, stream, a);
+  const dim3 kgrid((unsigned)((a.T + 32 * DK_NW - 1) / (32 * DK_NW)) * a.B * a.Hkv);
+  hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, DK_BQB, DK_NW, CAP, 2>), kgrid, dim3(64 * DK_NW), 0,
+                     stream, a);
   stage_mark(stream);
   return hipGetLastError();
 }
 
-template <int D, int BKV, int BQB>
+template <int D, int DQ_BKV, int DQ_NW, int DV_BQB, int DV_NW, int DK_BQB, int DK_NW>
 static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
-  if (a.cap_log2e > 0.f) return launch_bwd_t<D, BKV, BQB, true>(a, stream);
-  return launch_bwd_t<D, BKV, BQB, false>(a, stream);
+  if (a.cap_log2e > 0.f)
+    return launch_bwd_t<D, true, DQ_BKV, DQ_NW, DV_BQB, DV_NW, DK_BQB, DK_NW>(a, stream);
+  return launch_bwd_t<D, false, DQ_BKV, DQ_NW, DV_BQB, DV_NW, DK_BQB, DK_NW>(a, stream);
 }
 
 hipError_t launch_bwd_bf16(const BwdArgs& a, int d, hipStream_t stream) {
   switch (d) {
-    case 64: return launch_bwd_d<64, 64, 64>(a, stream);
-    case 128: return launch_bwd_d<128, 32, 32>(a, stream);
-    case 256: return launch_bwd_d<256, 32, 32>(a, stream);
+    case 64: return launch_bwd_d<64, BWD64_CFG>(a, stream);
+    case 128: return launch_bwd_d<128, BWD128_CFG>(a, stream);
+    case 256: return launch_bwd_d<256, BWD256_CFG>(a, stream);
   }
   return hipErrorInvalidValue;
 }

@@ -25,17 +25,18 @@
 
 namespace fa {
 
-#ifndef FWD_NW
-#define FWD_NW 4
-#endif
-
-template <int D, int BKV, int NW, bool CAP>
-__global__ __launch_bounds__(64 * NW, (D >= 256 ? 1 : 8 / NW)) void fa_fwd_kernel(FwdArgs a) {
-  constexpr int NT = 64 * NW;        // threads per workgroup
-  constexpr int BQ = 32 * NW;        // query rows per workgroup
+// QW query blocks of 32 rows per wave: each K or V operand read from LDS
+// feeds QW MFMAs, dividing the LDS traffic per flop by QW.
+template <int D, int BKV, int NW, int QW, bool CAP>
+__global__ __launch_bounds__(64 * NW, (D >= 256 || QW > 1 ? 1 : 8 / NW)) void fa_fwd_kernel(
+    FwdArgs a) {
+  constexpr int NT = 64 * NW;         // threads per workgroup
+  constexpr int RW = 32 * QW;         // query rows per wave
+  constexpr int BQ = RW * NW;         // query rows per workgroup
   constexpr int TILE = Lay<D>::template bytes<BKV>();  // one K or V tile
-  constexpr int NDB = D / 32;        // 32-wide d blocks of the output
-  constexpr int NS = BKV / 32;       // 32-key sub-tiles
+  constexpr int NDB = D / 32;         // 32-wide d blocks of the output
+  constexpr int NS = BKV / 32;        // 32-key sub-tiles
+  constexpr int NC = D / 16;          // 16-wide d chunks (MFMA k steps)
   __shared__ __attribute__((aligned(1024))) char smem[4 * TILE];
   LDS_AS char* lds = (LDS_AS char*)smem;
 
@@ -51,20 +52,21 @@ __global__ __launch_bounds__(64 * NW, (D >= 256 ? 1 : 8 / NW)) void fa_fwd_kerne
   const WorkItem w = decode_work(blockIdx.x, nqb, a.B, a.Hkv, G, true);
   const int h = w.hkv * G + w.r;
   const int q0 = w.blk * BQ;
-  const int qw0 = q0 + 32 * wave;
-  const int qrow = qw0 + l32;
+  const int qw0 = q0 + RW * wave;
   const size_t bh = (size_t)w.b * a.H + h;
   const size_t bkv = (size_t)w.b * a.Hkv + w.hkv;
   const bf16* Kp = a.k + bkv * T * D;
   const bf16* Vp = a.v + bkv * T * D;
 
-  // Q as the B operand of S^T = K Q^T: lane holds Q[qrow][16c + 8g .. +7].
-  bf16x8 qreg[D / 16];
-  {
-    const int qr = qrow < T ? qrow : T - 1;
+  // Q as the B operand of S^T = K Q^T: lane holds Q[qrow][16c + 8g .. +7]
+  // of its row in each of the wave's QW blocks.
+  bf16x8 qreg[QW][NC];
+#pragma unroll
+  for (int u = 0; u < QW; ++u) {
+    const int qr = min(qw0 + 32 * u + l32, T - 1);
     const bf16x8* src = (const bf16x8*)(a.q + (bh * T + qr) * D + 8 * g);
 #pragma unroll
-    for (int c = 0; c < D / 16; ++c) qreg[c] = src[2 * c];
+    for (int c = 0; c < NC; ++c) qreg[u][c] = src[2 * c];
   }
 
   int kv_lo = 0;
@@ -73,13 +75,17 @@ __global__ __launch_bounds__(64 * NW, (D >= 256 ? 1 : 8 / NW)) void fa_fwd_kerne
   const int kv_hi = min(T, q0 + BQ);
   const int ntiles = (kv_hi + BKV - 1) / BKV - t_lo;
 
-  f32x16 oacc[NDB];
+  f32x16 oacc[QW][NDB];
+  float m[QW], lsum[QW];
 #pragma unroll
-  for (int db = 0; db < NDB; ++db)
+  for (int u = 0; u < QW; ++u) {
+    m[u] = kMaxInit;
+    lsum[u] = 0.f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
-  float m = kMaxInit;
-  float lsum = 0.f;
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) oacc[u][db][i] = 0.f;
+  }
 
   TileStage<D, BKV, NT> kst, vst;
   kst.load(Kp, t_lo * BKV, T, tid);
@@ -88,7 +94,7 @@ __global__ __launch_bounds__(64 * NW, (D >= 256 ? 1 : 8 / NW)) void fa_fwd_kerne
   vst.store(lds + 2 * TILE, tid);
   __syncthreads();
 
-  const int qa = qw0, qb = qw0 + 31;
+  const int qa = qw0, qb = qw0 + RW - 1;
   for (int j = 0; j < ntiles; ++j) {
     const int cur = j & 1;
     const LDS_AS char* Kt = lds + cur * TILE;
@@ -105,74 +111,105 @@ __global__ __launch_bounds__(64 * NW, (D >= 256 ? 1 : 8 / NW)) void fa_fwd_kerne
     const int kv0 = (t_lo + j) * BKV;
     const bool empty = qa >= T || kv0 > qb || (W > 0 && kv0 + BKV - 1 <= qa - W);
     const bool full = kv0 + BKV - 1 <= qa && (W == 0 || kv0 > qb - W);
-    f32x16 s[NS];
-    if (!empty) mma_rows<D, NS>(s, Kt, qreg, lane);
     if (!empty) {
+      // S^T = K Q^T for every query block; each K operand feeds QW MFMAs and
+      // the next chunk's operands are requested before this chunk's MFMAs.
+      f32x16 s[QW][NS];
+      {
+        bf16x8 op[2][NS];
+#pragma unroll
+        for (int t = 0; t < NS; ++t) {
+          op[0][t] = lds_row_operand<D>(Kt, 32 * t, 0, lane);
+#pragma unroll
+          for (int u = 0; u < QW; ++u)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) s[u][t][i] = 0.f;
+        }
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          if (c + 1 < NC) {
+#pragma unroll
+            for (int t = 0; t < NS; ++t) op[(c + 1) & 1][t] = lds_row_operand<D>(Kt, 32 * t, c + 1, lane);
+          }
+#pragma unroll
+          for (int t = 0; t < NS; ++t)
+#pragma unroll
+            for (int u = 0; u < QW; ++u) s[u][t] = mfma32(op[c & 1][t], qreg[u][c], s[u][t]);
+        }
+      }
       // Scores in the log2 domain.  Without a cap the scale is folded into
       // the exponent's FMA below (the max of raw scores scales with it).
-      if (CAP) {
+      const float cexp = CAP ? 1.f : a.scale_log2e;
+      bf16x8 pb[QW][BKV / 16];
 #pragma unroll
-        for (int t = 0; t < NS; ++t)
+      for (int u = 0; u < QW; ++u) {
+        const int qrow = qw0 + 32 * u + l32;
+        if (CAP) {
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            // cap * tanh(scale*x / cap) * log2(e)
-            const float e = fast_exp2(s[t][i] * a.two_scale_over_cap_log2e);
-            s[t][i] = (1.f - 2.f * __builtin_amdgcn_rcpf(e + 1.f)) * a.cap_log2e;
-          }
-      }
-      if (!full) {
+          for (int t = 0; t < NS; ++t)
 #pragma unroll
-        for (int t = 0; t < NS; ++t)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int kv = kv0 + 32 * t + acc_row(i, g);
-            const bool vis = (kv <= qrow) & ((W == 0) | (kv > qrow - W));
-            s[t][i] = vis ? s[t][i] : -INFINITY;
-          }
-      }
-      const float c = CAP ? 1.f : a.scale_log2e;
-      float mt = -INFINITY;
-#pragma unroll
-      for (int t = 0; t < NS; ++t)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[t][i]);
-      mt = xor32_max(mt) * c;
-      // Lazy rescaling: the running max m only moves (and O, l are rescaled)
-      // when some row's tile max exceeds it by more than kRescaleSlack, so
-      // p = 2^(s - m) stays below 2^kRescaleSlack; the branch is uniform.
-      if (__any(mt > m + kRescaleSlack)) {
-        const float mnew = fmaxf(m, mt);
-        const float alpha = fast_exp2(m - mnew);
-        m = mnew;
-        lsum *= alpha;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
-      }
-      float ps = 0.f;
-#pragma unroll
-      for (int t = 0; t < NS; ++t)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float p = fast_exp2(fmaf(s[t][i], c, -m));
-          s[t][i] = p;
-          ps += p;
+            for (int i = 0; i < 16; ++i) {
+              // cap * tanh(scale*x / cap) * log2(e)
+              const float e = fast_exp2(s[u][t][i] * a.two_scale_over_cap_log2e);
+              s[u][t][i] = (1.f - 2.f * __builtin_amdgcn_rcpf(e + 1.f)) * a.cap_log2e;
+            }
         }
-      lsum += ps;
-      bf16x8 pb[BKV / 16];
+        if (!full) {
 #pragma unroll
-      for (int c16 = 0; c16 < BKV / 16; ++c16) {
-        float tmp[8];
+          for (int t = 0; t < NS; ++t)
 #pragma unroll
-        for (int jj = 0; jj < 8; ++jj) tmp[jj] = s[c16 >> 1][8 * (c16 & 1) + jj];
-        pb[c16] = pack_bf16(tmp);
+            for (int i = 0; i < 16; ++i) {
+              const int kv = kv0 + 32 * t + acc_row(i, g);
+              const bool vis = (kv <= qrow) & ((W == 0) | (kv > qrow - W));
+              s[u][t][i] = vis ? s[u][t][i] : -INFINITY;
+            }
+        }
+        float mt = -INFINITY;
+#pragma unroll
+        for (int t = 0; t < NS; ++t)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[u][t][i]);
+        mt = xor32_max(mt) * cexp;
+        // Lazy rescaling: the running max only moves (and O, l are rescaled)
+        // when some row's tile max exceeds it by more than kRescaleSlack, so
+        // p = 2^(s - m) stays below 2^kRescaleSlack; the branch is uniform.
+        if (__any(mt > m[u] + kRescaleSlack)) {
+          const float mnew = fmaxf(m[u], mt);
+          const float alpha = fast_exp2(m[u] - mnew);
+          m[u] = mnew;
+          lsum[u] *= alpha;
+#pragma unroll
+          for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) oacc[u][db][i] *= alpha;
+        }
+        float ps = 0.f;
+#pragma unroll
+        for (int t = 0; t < NS; ++t)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const float p = fast_exp2(fmaf(s[u][t][i], cexp, -m[u]));
+            s[u][t][i] = p;
+            ps += p;
+          }
+        lsum[u] += ps;
+#pragma unroll
+        for (int c16 = 0; c16 < BKV / 16; ++c16) {
+          float tmp[8];
+#pragma unroll
+          for (int jj = 0; jj < 8; ++jj) tmp[jj] = s[u][c16 >> 1][8 * (c16 & 1) + jj];
+          pb[u][c16] = pack_bf16(tmp);
+        }
       }
+      // O^T += V^T P^T: each transposed V operand feeds QW MFMAs.
 #pragma unroll
       for (int c16 = 0; c16 < BKV / 16; ++c16)
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
-          oacc[db] = mfma32(lds_tr_operand<D>(Vt, 0, c16, 32 * db, lane), pb[c16], oacc[db]);
+        for (int db = 0; db < NDB; ++db) {
+          const bf16x8 vop = lds_tr_operand<D>(Vt, 0, c16, 32 * db, lane);
+#pragma unroll
+          for (int u = 0; u < QW; ++u) oacc[u][db] = mfma32(vop, pb[u][c16], oacc[u][db]);
+        }
     }
     if (more) {
       kst.store(lds + (cur ^ 1) * TILE, tid);
@@ -181,40 +218,50 @@ __global__ __launch_bounds__(64 * NW, (D >= 256 ? 1 : 8 / NW)) void fa_fwd_kerne
     __syncthreads();
   }
 
-  const float ltot = xor32_sum(lsum);
-  if (qrow < T) {
-    const float inv = 1.f / ltot;
-    bf16* Op = a.o + (bh * T + qrow) * D;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+  for (int u = 0; u < QW; ++u) {
+    const int qrow = qw0 + 32 * u + l32;
+    const float ltot = xor32_sum(lsum[u]);
+    if (qrow < T) {
+      const float inv = 1.f / ltot;
+      bf16* Op = a.o + (bh * T + qrow) * D;
 #pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        bf16x4 v;
+      for (int db = 0; db < NDB; ++db)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = (bf16)(oacc[db][4 * i4 + e] * inv);
-        *(bf16x4*)(Op + 32 * db + 8 * i4 + 4 * g) = v;
-      }
-    if (g == 0) a.lse[bh * T + qrow] = (m + __log2f(ltot)) * kLn2;
+        for (int i4 = 0; i4 < 4; ++i4) {
+          bf16x4 v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = (bf16)(oacc[u][db][4 * i4 + e] * inv);
+          *(bf16x4*)(Op + 32 * db + 8 * i4 + 4 * g) = v;
+        }
+      if (g == 0) a.lse[bh * T + qrow] = (m[u] + __log2f(ltot)) * kLn2;
+    }
   }
 }
 
-template <int D, int BKV, int NW>
+// Tile shapes per head size (keys per tile, waves, query blocks per wave),
+// chosen by measurement on MI355X.
+#ifndef FWD128_CFG
+#define FWD128_CFG 64, 4, 1
+#endif
+
+template <int D, int BKV, int NW, int QW>
 static hipError_t launch_fwd_d(const FwdArgs& a, hipStream_t stream) {
-  const int nqb = (a.T + 32 * NW - 1) / (32 * NW);
+  const int nqb = (a.T + 32 * NW * QW - 1) / (32 * NW * QW);
   const dim3 grid((unsigned)nqb * a.B * a.H);
   if (a.cap_log2e > 0.f)
-    hipLaunchKernelGGL((fa_fwd_kernel<D, BKV, NW, true>), grid, dim3(64 * NW), 0, stream, a);
+    hipLaunchKernelGGL((fa_fwd_kernel<D, BKV, NW, QW, true>), grid, dim3(64 * NW), 0, stream, a);
   else
-    hipLaunchKernelGGL((fa_fwd_kernel<D, BKV, NW, false>), grid, dim3(64 * NW), 0, stream, a);
+    hipLaunchKernelGGL((fa_fwd_kernel<D, BKV, NW, QW, false>), grid, dim3(64 * NW), 0, stream, a);
   stage_mark(stream);
   return hipGetLastError();
 }
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, int d, hipStream_t stream) {
   switch (d) {
-    case 64: return launch_fwd_d<64, 64, FWD_NW>(a, stream);
-    case 128: return launch_fwd_d<128, 64, FWD_NW>(a, stream);
-    case 256: return launch_fwd_d<256, 32, FWD_NW>(a, stream);
+    case 64: return launch_fwd_d<64, 64, 4, 1>(a, stream);
+    case 128: return launch_fwd_d<128, FWD128_CFG>(a, stream);
+    case 256: return launch_fwd_d<256, 32, 4, 1>(a, stream);
   }
   return hipErrorInvalidValue;
 }
