@@ -280,6 +280,42 @@ int fa_rope_inv_freq(float* host_out, int d, double theta) {
   return FA_OK;
 }
 
+int fa_rope_inv_freq_llama3(float* host_out, int d, double theta, double factor,
+                            double low_freq_factor, double high_freq_factor, double orig_ctx) {
+  const int rc = fa_rope_inv_freq(host_out, d, theta);
+  if (rc != FA_OK || factor <= 0.0) return rc;
+  if (!(high_freq_factor > low_freq_factor) || !(low_freq_factor > 0.0) || !(orig_ctx > 0.0) ||
+      !std::isfinite(factor) || !std::isfinite(high_freq_factor) || !std::isfinite(orig_ctx))
+    return fail(FA_ERR_INVALID_ARG,
+                "fa_rope_inv_freq_llama3: need high_freq_factor > low_freq_factor > 0, orig_ctx > 0");
+  const double two_pi = 6.283185307179586;
+  const double lo_wave = orig_ctx / low_freq_factor, hi_wave = orig_ctx / high_freq_factor;
+  for (int i = 0; i < d / 2; ++i) {
+    const double f = std::pow(theta, -2.0 * i / d);
+    const double wave = two_pi / f;
+    double g;
+    if (wave < hi_wave) {
+      g = f;
+    } else if (wave > lo_wave) {
+      g = f / factor;
+    } else {
+      const double smooth = (orig_ctx / wave - low_freq_factor) / (high_freq_factor - low_freq_factor);
+      g = (1.0 - smooth) * f / factor + smooth * f;
+    }
+    host_out[i] = (float)g;
+  }
+  return FA_OK;
+}
+
+int fa_layer_rope_theta(int layer, double theta, double theta_global, int global_every,
+                        double* out) {
+  if (!out || layer < 0 || global_every < 0 || !(theta > 0.0))
+    return fail(FA_ERR_INVALID_ARG, "fa_layer_rope_theta: bad argument");
+  const bool global = global_every > 0 && (layer + 1) % global_every == 0;
+  *out = (global && theta_global > 0.0) ? theta_global : theta;
+  return FA_OK;
+}
+
 int fa_set_stage_events(void* const* events, int count) {
   if (count < 0 || count > kMaxStageEvents || (count > 0 && !events))
     return fail(FA_ERR_INVALID_ARG, "fa_set_stage_events: count must be 0..16 with non-null events");

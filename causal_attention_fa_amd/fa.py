@@ -52,6 +52,13 @@ _lib.fa_layer_window.argtypes = [_I, _I, _I]
 _lib.fa_layer_window.restype = _I
 _lib.fa_rope_inv_freq.argtypes = [ctypes.POINTER(ctypes.c_float), _I, ctypes.c_double]
 _lib.fa_rope_inv_freq.restype = _I
+_lib.fa_rope_inv_freq_llama3.argtypes = [ctypes.POINTER(ctypes.c_float), _I, ctypes.c_double,
+                                         ctypes.c_double, ctypes.c_double, ctypes.c_double,
+                                         ctypes.c_double]
+_lib.fa_rope_inv_freq_llama3.restype = _I
+_lib.fa_layer_rope_theta.argtypes = [_I, ctypes.c_double, ctypes.c_double, _I,
+                                     ctypes.POINTER(ctypes.c_double)]
+_lib.fa_layer_rope_theta.restype = _I
 _lib.fa_set_stage_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), _I]
 _lib.fa_set_stage_events.restype = _I
 _lib.fa_last_error.argtypes = []
@@ -59,7 +66,8 @@ _lib.fa_last_error.restype = ctypes.c_char_p
 
 EXPORTS = ("fa_fwd", "fa_bwd", "rope_apply", "rope_apply_bwd", "fa_fwd_f32", "fa_bwd_f32",
            "rope_apply_f32", "rope_apply_bwd_f32", "fa_layer_window", "fa_rope_inv_freq",
-           "fa_set_stage_events", "fa_last_error")
+           "fa_rope_inv_freq_llama3", "fa_layer_rope_theta", "fa_set_stage_events",
+           "fa_last_error")
 
 
 class FAError(RuntimeError):
@@ -167,6 +175,22 @@ def fa_rope_inv_freq(d: int, theta: float) -> np.ndarray:
     _check(_lib.fa_rope_inv_freq(out.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), d,
                                  float(theta)))
     return out[: d // 2]
+
+
+def fa_rope_inv_freq_llama3(d: int, theta: float, factor: float, low_freq_factor: float = 1.0,
+                            high_freq_factor: float = 4.0, orig_ctx: float = 8192.0) -> np.ndarray:
+    out = np.zeros(max(d // 2, 1), dtype=np.float32)
+    _check(_lib.fa_rope_inv_freq_llama3(out.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), d,
+                                        float(theta), float(factor), float(low_freq_factor),
+                                        float(high_freq_factor), float(orig_ctx)))
+    return out[: d // 2]
+
+
+def fa_layer_rope_theta(layer: int, theta: float, theta_global: float, global_every: int) -> float:
+    out = ctypes.c_double(0.0)
+    _check(_lib.fa_layer_rope_theta(layer, float(theta), float(theta_global), global_every,
+                                    ctypes.byref(out)))
+    return out.value
 
 
 def fa_set_stage_events(events):

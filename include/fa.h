@@ -124,6 +124,25 @@ int fa_layer_window(int layer, int window, int global_every);
  * odd or non-positive d, or theta <= 0. */
 int fa_rope_inv_freq(float* host_out, int d, double theta);
 
+/* Inverse frequencies with the "llama3" context-extension rescaling
+ * (Forge ARCHITECTURES.md, "Formules clés"): starting from theta^(-2i/d),
+ * a component of wavelength 2*pi/f shorter than orig_ctx/high_freq_factor is
+ * kept, one longer than orig_ctx/low_freq_factor is divided by `factor`, and
+ * in between s = (orig_ctx/wavelength - low)/(high - low) blends the two:
+ * (1-s)*f/factor + s*f.  factor <= 0 means off (plain table; config default
+ * rope_scale_factor(0)).  Computed in double, stored as float.  Returns 0 or
+ * FA_ERR_INVALID_ARG (bad d/theta, or not high > low > 0, orig_ctx > 0). */
+int fa_rope_inv_freq_llama3(float* host_out, int d, double theta, double factor,
+                            double low_freq_factor, double high_freq_factor,
+                            double orig_ctx);
+
+/* RoPE base of layer `layer`: theta_global for the global layers of a
+ * local:global stack (same rule as fa_layer_window) when theta_global > 0,
+ * else theta (Forge attention.h commit log, "Wave 2": rope_theta_global).
+ * Writes *out; returns 0 or FA_ERR_INVALID_ARG. */
+int fa_layer_rope_theta(int layer, double theta, double theta_global,
+                        int global_every, double* out);
+
 /* Per-kernel timing for callers that measure (benchmarks, profilers):
  * `events` are `count` (<= 16) hipEvent_t handles created by the caller.
  * While armed (count > 0), every later call on this thread records

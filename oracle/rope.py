@@ -24,7 +24,7 @@ from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["inv_freq", "angles", "rope", "rope_bwd"]
+__all__ = ["inv_freq", "inv_freq_llama3", "layer_rope_theta", "angles", "rope", "rope_bwd"]
 
 
 def inv_freq(d: int, theta: float) -> np.ndarray:
@@ -37,6 +37,61 @@ def inv_freq(d: int, theta: float) -> np.ndarray:
         raise ValueError("d must be even and positive")
     i = np.arange(d // 2, dtype=np.float64)
     return (float(theta) ** (-2.0 * i / d)).astype(np.float32)
+
+
+def inv_freq_llama3(d: int, theta: float, factor: float, low: float = 1.0,
+                    high: float = 4.0, orig_ctx: float = 8192.0) -> np.ndarray:
+    """Inverse frequencies with the "llama3" context-extension rescaling.
+
+    Forge ARCHITECTURES.md, "Formules clés" (llama3 RoPE scaling, applied
+    per component): with wavelen = 2*pi/inv_freq, components whose
+    wavelength is shorter than orig_ctx/high keep their frequency, those
+    longer than orig_ctx/low are divided by `factor`, and in between the
+    two are blended with s = (orig_ctx/wavelen - low)/(high - low):
+    (1-s)*inv_freq/factor + s*inv_freq.  Config defaults (forge-studio
+    RESEARCH.md section 2): low 1, high 4, orig_ctx 8192; factor 0 = off.
+    Evaluated in float64, stored as float32.
+
+    Pinned: factor 1 and factor 0 give the plain table; components in the
+    high-frequency band are unchanged and those in the low band are exactly
+    inv_freq/factor; the blend meets both bands continuously at the two
+    thresholds; the scaled table stays strictly decreasing.
+    """
+    if d <= 0 or d % 2:
+        raise ValueError("d must be even and positive")
+    base = (float(theta) ** (-2.0 * np.arange(d // 2, dtype=np.float64) / d))
+    if factor <= 0:
+        return base.astype(np.float32)
+    if not (high > low > 0) or orig_ctx <= 0:
+        raise ValueError("need high > low > 0 and orig_ctx > 0")
+    return _llama3_scale(base, factor, low, high, orig_ctx).astype(np.float32)
+
+
+def _llama3_scale(inv, factor, low, high, orig_ctx):
+    inv = np.asarray(inv, dtype=np.float64)
+    wavelen = 2.0 * np.pi / inv
+    s = (orig_ctx / wavelen - low) / (high - low)
+    blended = (1.0 - s) * inv / factor + s * inv
+    out = np.where(wavelen > orig_ctx / low, inv / factor, blended)
+    return np.where(wavelen < orig_ctx / high, inv, out)
+
+
+def layer_rope_theta(layer: int, theta: float, theta_global: float,
+                     global_every: int) -> float:
+    """RoPE base of one layer of a local:global stack: global layers (every
+    global_every-th layer, as for the attention window) use theta_global
+    when it is set (> 0), every other layer uses theta.  Forge attention.h
+    commit log, "Wave 2": rope_theta_global gives Gemma 3 its dual base
+    (ARCHITECTURES.md family table: 10k local / 1M global).
+
+    Pinned: the Gemma 3 pattern with global_every 6; theta_global 0 leaves
+    every layer at theta.
+    """
+    if layer < 0 or global_every < 0:
+        raise ValueError("layer and global_every must be >= 0")
+    if theta_global > 0 and global_every > 0 and (layer + 1) % global_every == 0:
+        return float(theta_global)
+    return float(theta)
 
 
 def angles(T: int, table_f32: np.ndarray) -> np.ndarray:

@@ -109,3 +109,22 @@ def test_inv_freq_matches_oracle(d, theta):
     np.testing.assert_array_max_ulp(got, want, maxulp=1)
     with pytest.raises(fa.FAError):
         fa.fa_rope_inv_freq(5, theta)
+
+
+@pytest.mark.parametrize("d,theta,factor", [(128, 5e5, 32.0), (64, 1e4, 8.0), (128, 5e5, 0.0),
+                                            (256, 1e6, 1.0)])
+def test_llama3_table_matches_oracle(d, theta, factor):
+    from oracle import rope as OR
+    got = fa.fa_rope_inv_freq_llama3(d, theta, factor, 1.0, 4.0, 8192.0)
+    want = OR.inv_freq_llama3(d, theta, factor, 1.0, 4.0, 8192.0)
+    np.testing.assert_array_max_ulp(got, want, maxulp=1)
+    with pytest.raises(fa.FAError):
+        fa.fa_rope_inv_freq_llama3(d, theta, 8.0, 4.0, 1.0, 8192.0)
+
+
+def test_layer_rope_theta_matches_oracle():
+    from oracle import rope as OR
+    for ge in (0, 2, 6):
+        for tg in (0.0, 1e6):
+            for layer in range(13):
+                assert fa.fa_layer_rope_theta(layer, 1e4, tg, ge) == OR.layer_rope_theta(layer, 1e4, tg, ge)

@@ -52,3 +52,22 @@ def test_rope_parity(dtype, B, H, T, d, theta):
     fa.rope(xin, tab, out=xin)
     torch.cuda.synchronize()
     assert torch.equal(xin.cpu(), y.cpu())
+
+
+@pytest.mark.parametrize("theta,factor", [(5e5, 32.0), (1e4, 8.0)])
+def test_rope_llama3_table(theta, factor):
+    """RoPE with the llama3-rescaled table (host helper) against the oracle's
+    own rescaled table and rotation, T = 8192 (angles ~ 8e3 rad)."""
+    from causal_attention_fa_amd import fa
+    B, H, T, d = 1, 2, 8192, 128
+    say(f"[rope llama3] theta{theta:g} factor{factor:g}")
+    w = synth.Workload("rope3", "bf16", B, H, H, T, d)
+    x, _, _, _ = synth.draw(w, need_do=False)
+    tab = torch.from_numpy(fa.fa_rope_inv_freq_llama3(d, theta, factor)).to(dev())
+    y = poison(x.shape, x.dtype)
+    fa.rope(x.to(dev()), tab, out=y)
+    torch.cuda.synchronize()
+    xf = synth.to_f64(x)
+    ref = OR.rope(xf, OR.inv_freq_llama3(d, theta, factor))
+    err = np.abs(y.double().cpu().numpy() - ref) / np.maximum(_pair_norm(xf), 1e-30)
+    assert err.max() <= 2.0 ** -8, err.max()

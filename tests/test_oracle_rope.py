@@ -84,3 +84,43 @@ def test_relative_position_property():
     K = R.rope(np.broadcast_to(k, (T, d)).copy(), table)
     for m, n in [(3, 10), (0, 39), (17, 20), (25, 25)]:
         assert abs(Q[m] @ K[n] - q @ K[n - m]) < 1e-12
+
+
+def test_llama3_identity_cases():
+    """factor 1 blends a frequency with itself; factor 0 is "off"."""
+    plain = R.inv_freq(128, 5e5)
+    np.testing.assert_array_equal(R.inv_freq_llama3(128, 5e5, 1.0), plain)
+    np.testing.assert_array_equal(R.inv_freq_llama3(128, 5e5, 0.0), plain)
+
+
+def test_llama3_bands():
+    """High-frequency band unchanged, low-frequency band divided by factor,
+    blend in between strictly between the two."""
+    d, theta, factor, low, high, old = 128, 5e5, 32.0, 1.0, 4.0, 8192.0
+    base = theta ** (-2.0 * np.arange(d // 2) / d)
+    got = R.inv_freq_llama3(d, theta, factor, low, high, old).astype(np.float64)
+    wavelen = 2 * np.pi / base
+    hi = wavelen < old / high
+    lo = wavelen > old / low
+    mid = ~hi & ~lo
+    assert hi.any() and lo.any() and mid.any()
+    np.testing.assert_allclose(got[hi], base[hi], rtol=1e-7)
+    np.testing.assert_allclose(got[lo], base[lo] / factor, rtol=1e-7)
+    assert np.all(got[mid] < base[mid]) and np.all(got[mid] > base[mid] / factor)
+    assert np.all(np.diff(got) < 0)
+
+
+def test_llama3_blend_is_continuous_at_thresholds():
+    """At wavelen = old/high the blend equals the unchanged frequency; at
+    wavelen = old/low it equals inv/factor."""
+    old, low, high, factor = 8192.0, 1.0, 4.0, 8.0
+    for wl, want_div in ((old / high * (1 + 1e-12), 1.0), (old / low * (1 - 1e-12), factor)):
+        inv = np.array([2 * np.pi / wl])
+        got = R._llama3_scale(inv, factor, low, high, old)[0]
+        assert abs(got - inv[0] / want_div) / inv[0] < 1e-9
+
+
+def test_layer_rope_theta_gemma3():
+    thetas = [R.layer_rope_theta(l, 1e4, 1e6, 6) for l in range(12)]
+    assert thetas == [1e4] * 5 + [1e6] + [1e4] * 5 + [1e6]
+    assert [R.layer_rope_theta(l, 1e4, 0.0, 6) for l in range(6)] == [1e4] * 6
