@@ -42,7 +42,7 @@ import numpy as np
 __all__ = [
     "layer_window", "visibility", "capped_scores", "head_forward",
     "head_backward", "attn_fwd", "attn_bwd", "head_forward_rows",
-    "head_grads_sampled",
+    "head_grads_sampled", "max_logit",
 ]
 
 
@@ -95,13 +95,19 @@ def capped_scores(s: np.ndarray, softcap: float) -> np.ndarray:
     return s
 
 
-def head_forward_rows(q, k, v, scale, window, softcap, rows=None):
+def head_forward_rows(q, k, v, scale, window, softcap, rows=None, sink=None):
     """Forward of one (b, h) pair restricted to query positions ``rows``.
 
-    q: [T, d] (this head's queries), k, v: [T, d] (its KV head).  Returns
+    q: [T, d] (this head's queries), k, v: [T, d_v] (its KV head).  Returns
     (o[rows], lse[rows], P[rows, :]) in float64.  Each output row depends
     only on its own row of S, so evaluating a subset of rows is the same
     definition, not a reordering.
+
+    ``sink`` (a scalar logit, or None): the attention sink of GPT-OSS
+    (ARCHITECTURES.md family table, and plan wave 2 item 10: a learned
+    per-head logit in the softmax denominator that the online softmax
+    starts its (max, sum) from).  It joins every row's normaliser but
+    carries no value: lse = log(sum_j exp(S'_ij) + exp(sink)).
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -113,18 +119,23 @@ def head_forward_rows(q, k, v, scale, window, softcap, rows=None):
     vis = visibility(rows, np.arange(T), window)
     sm = np.where(vis, sc, -np.inf)
     m = sm.max(axis=1)
-    lse = m + np.log(np.exp(sm - m[:, None]).sum(axis=1))
+    if sink is not None:
+        m = np.maximum(m, sink)
+    tot = np.exp(sm - m[:, None]).sum(axis=1)
+    if sink is not None:
+        tot = tot + np.exp(sink - m)
+    lse = m + np.log(tot)
     p = np.exp(sm - lse[:, None])
     o = p @ v
     return o, lse, p
 
 
-def head_forward(q, k, v, scale, window, softcap):
+def head_forward(q, k, v, scale, window, softcap, sink=None):
     """Forward of one (b, h): (o [T, d], lse [T], P [T, T])."""
-    return head_forward_rows(q, k, v, scale, window, softcap)
+    return head_forward_rows(q, k, v, scale, window, softcap, sink=sink)
 
 
-def head_backward(q, k, v, do, scale, window, softcap):
+def head_backward(q, k, v, do, scale, window, softcap, sink=None):
     """Gradients of L = sum(o * dO) for one (b, h), all in float64.
 
     Returns (dq, dk, dv), each [T, d]; dk and dv are this query head's
@@ -132,15 +143,19 @@ def head_backward(q, k, v, do, scale, window, softcap):
     1 - tanh(S/cap)^2, the exact derivative (Forge attention.h commit log,
     "Wave 2").
 
-    Pinned: central finite differences of head_forward; closed forms for
-    window = 1 and q = 0; all keys equal => dq = 0; torch.autograd of the
-    library SDPA in the plain causal case.
+    With a sink, P is normalised including exp(sink) and the same formulas
+    hold; the sink's own gradient is d sink = -sum_i exp(sink - lse_i) D_i
+    (returned as a fourth value when ``sink`` is given).
+
+    Pinned: central finite differences of head_forward (also w.r.t. the
+    sink); closed forms for window = 1 and q = 0; all keys equal => dq = 0;
+    torch.autograd of the library SDPA in the plain causal case.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
     do = np.asarray(do, dtype=np.float64)
-    o, _, p = head_forward(q, k, v, scale, window, softcap)
+    o, lse, p = head_forward(q, k, v, scale, window, softcap, sink=sink)
     dp = do @ v.T
     D = (do * o).sum(axis=1)
     dsc = p * (dp - D[:, None])
@@ -152,55 +167,92 @@ def head_backward(q, k, v, do, scale, window, softcap):
     dq = scale * (ds @ k)
     dk = scale * (ds.T @ q)
     dv = p.T @ do
+    if sink is not None:
+        dsink = -float((np.exp(sink - lse) * D).sum())
+        return dq, dk, dv, dsink
     return dq, dk, dv
+
+
+def max_logit(q, k, scale, window=0, softcap=0.0):
+    """Largest logit entering the softmax, per (b, h): max over visible
+    (i, j) of S'_ij (= scale * <q_i, k_j> without a cap).  The per-head
+    quantity QK-Clip monitors (ARCHITECTURES.md family table, Kimi K2
+    MuonClip; plan wave 3 item 12: the flash kernel already keeps the row
+    max, expose it).  Returns [B, H].
+
+    Pinned: brute force over pairs on a tiny case; window = 1 closed form.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    B, H, T, _ = q.shape
+    Hkv = k.shape[1]
+    grp = H // Hkv
+    out = np.empty((B, H))
+    vis = visibility(np.arange(T), np.arange(T), window)
+    for b in range(B):
+        for h in range(H):
+            sc = capped_scores(scale * (q[b, h] @ k[b, h // grp].T), softcap)
+            out[b, h] = np.where(vis, sc, -np.inf).max()
+    return out
 
 
 def _check_shapes(q, k, v):
     B, H, T, d = q.shape
     Bk, Hkv, Tk, dk_ = k.shape
-    if (Bk, Tk, dk_) != (B, T, d) or v.shape != k.shape:
-        raise ValueError("q [B,H,T,d], k/v [B,Hkv,T,d] expected")
+    if (Bk, Tk, dk_) != (B, T, d) or v.shape[:3] != k.shape[:3]:
+        raise ValueError("q [B,H,T,d], k [B,Hkv,T,d], v [B,Hkv,T,dv] expected")
     if Hkv <= 0 or H % Hkv != 0:
         raise ValueError("H must be a multiple of Hkv")
     return B, H, Hkv, T, d
 
 
-def attn_fwd(q, k, v, scale, window=0, softcap=0.0):
-    """Batched forward.  q [B,H,T,d]; k, v [B,Hkv,T,d].  Returns
-    (o [B,H,T,d], lse [B,H,T]) in float64."""
+def attn_fwd(q, k, v, scale, window=0, softcap=0.0, sinks=None):
+    """Batched forward.  q [B,H,T,d]; k [B,Hkv,T,d]; v [B,Hkv,T,dv] (d_v may
+    differ from d, as in MLA: ARCHITECTURES.md plan wave 3 item 13).
+    ``sinks``: optional [H] per-head sink logits.  Returns
+    (o [B,H,T,dv], lse [B,H,T]) in float64."""
     B, H, Hkv, T, d = _check_shapes(q, k, v)
     grp = H // Hkv
-    o = np.empty((B, H, T, d))
+    o = np.empty((B, H, T, v.shape[-1]))
     lse = np.empty((B, H, T))
     for b in range(B):
         for h in range(H):
             g = h // grp
+            sk = None if sinks is None else float(sinks[h])
             o[b, h], lse[b, h], _ = head_forward(q[b, h], k[b, g], v[b, g],
-                                                 scale, window, softcap)
+                                                 scale, window, softcap, sink=sk)
     return o, lse
 
 
-def attn_bwd(q, k, v, do, scale, window=0, softcap=0.0):
-    """Batched backward.  Returns (dq [B,H,T,d], dk, dv [B,Hkv,T,d]); the
-    KV gradients sum over the query heads of each group."""
+def attn_bwd(q, k, v, do, scale, window=0, softcap=0.0, sinks=None):
+    """Batched backward.  Returns (dq [B,H,T,d], dk [B,Hkv,T,d],
+    dv [B,Hkv,T,dv]); the KV gradients sum over the query heads of each
+    group.  With ``sinks`` ([H]) a fourth value dsinks [H] (summed over the
+    batch) is returned."""
     B, H, Hkv, T, d = _check_shapes(q, k, v)
     grp = H // Hkv
     dq = np.empty((B, H, T, d))
     dk = np.zeros((B, Hkv, T, d))
-    dv = np.zeros((B, Hkv, T, d))
+    dv = np.zeros((B, Hkv, T, v.shape[-1]))
+    dsinks = np.zeros(H)
     for b in range(B):
         for h in range(H):
             g = h // grp
-            a, bk, bv = head_backward(q[b, h], k[b, g], v[b, g], do[b, h],
-                                      scale, window, softcap)
-            dq[b, h] = a
-            dk[b, g] += bk
-            dv[b, g] += bv
+            sk = None if sinks is None else float(sinks[h])
+            res = head_backward(q[b, h], k[b, g], v[b, g], do[b, h],
+                                scale, window, softcap, sink=sk)
+            dq[b, h] = res[0]
+            dk[b, g] += res[1]
+            dv[b, g] += res[2]
+            if sinks is not None:
+                dsinks[h] += res[3]
+    if sinks is not None:
+        return dq, dk, dv, dsinks
     return dq, dk, dv
 
 
 def head_grads_sampled(q, k, v, do, scale, window, softcap, q_rows, kv_rows,
-                       row_block=1024):
+                       row_block=1024, sink=None):
     """The backward definition evaluated only where a sampled check needs it.
 
     For one (b, h): dq at query positions ``q_rows`` and this head's
@@ -217,11 +269,11 @@ def head_grads_sampled(q, k, v, do, scale, window, softcap, q_rows, kv_rows,
     do = np.asarray(do, dtype=np.float64)
     T = k.shape[0]
     lse = np.empty(T)
-    o = np.empty_like(q)
+    o = np.empty((q.shape[0], v.shape[1]))
     for r0 in range(0, T, row_block):
         rows = np.arange(r0, min(T, r0 + row_block))
         o[rows], lse[rows], _ = head_forward_rows(q, k, v, scale, window,
-                                                  softcap, rows)
+                                                  softcap, rows, sink=sink)
     D = (do * o).sum(axis=1)
     q_rows = np.asarray(q_rows)
     kv_rows = np.asarray(kv_rows)

@@ -320,3 +320,95 @@ def test_sampled_grads_match_full(W, cap):
     np.testing.assert_allclose(sv, dv[kr], atol=1e-13)
     np.testing.assert_allclose(so, o, atol=1e-13)
     np.testing.assert_allclose(sl, lse, atol=1e-13)
+
+
+# ------------------------------------------------ sinks, max logit, d_v != d_k
+
+@pytest.mark.parametrize("W,sink", [(0, 0.7), (3, -1.2), (0, 4.0)])
+def test_sink_closed_form_zero_query(W, sink):
+    """q = 0: every visible logit is 0, so P_ij = 1/(n_i + e^s) and
+    lse_i = ln(n_i + e^s); o_i = n_i/(n_i + e^s) * mean of the visible v."""
+    T, d = 9, 4
+    q = np.zeros((1, 2, T, d))
+    k, v = _rand(1, 1, T, d), _rand(1, 1, T, d)
+    o, lse = A.attn_fwd(q, k, v, 0.5, W, 0.0, sinks=np.array([sink, sink]))
+    for i in range(T):
+        n = _n_visible(i, W)
+        z = n + math.exp(sink)
+        np.testing.assert_allclose(o[0, 0, i], v[0, 0, i - n + 1:i + 1].sum(0) / z, atol=1e-13)
+        assert abs(lse[0, 1, i] - math.log(z)) < 1e-13
+
+
+def test_very_negative_sink_is_no_sink():
+    T, d = 8, 4
+    q, k, v, do = _rand(1, 2, T, d), _rand(1, 1, T, d), _rand(1, 1, T, d), _rand(1, 2, T, d)
+    o0, l0 = A.attn_fwd(q, k, v, 0.5, 3, 2.0)
+    o1, l1 = A.attn_fwd(q, k, v, 0.5, 3, 2.0, sinks=np.array([-1e4, -1e4]))
+    np.testing.assert_allclose(o0, o1, atol=1e-14)
+    np.testing.assert_allclose(l0, l1, atol=1e-14)
+    g0 = A.attn_bwd(q, k, v, do, 0.5, 3, 2.0)
+    g1 = A.attn_bwd(q, k, v, do, 0.5, 3, 2.0, sinks=np.array([-1e4, -1e4]))
+    for a, b in zip(g0, g1[:3]):
+        np.testing.assert_allclose(a, b, atol=1e-13)
+    assert np.abs(g1[3]).max() < 1e-12
+
+
+@pytest.mark.parametrize("W,cap,dv", [(0, 0.0, 4), (3, 2.0, 4), (0, 0.0, 3)])
+def test_sink_and_dv_gradcheck(W, cap, dv):
+    """Central differences w.r.t. q, k, v and the sinks, including a value
+    head size different from the query/key head size (d_v = 3, d = 4)."""
+    H, T, d, scale, h = 2, 6, 4, 0.6, 1e-6
+    q, k = _rand(1, H, T, d, sigma=1.5), _rand(1, 1, T, d, sigma=1.5)
+    v = _rand(1, 1, T, dv)
+    r = _rand(1, H, T, dv)
+    sinks = np.array([0.3, -0.8])
+
+    def loss():
+        o, _ = A.attn_fwd(q, k, v, scale, W, cap, sinks=sinks)
+        return float((o * r).sum())
+
+    dq, dk, dvv, ds = A.attn_bwd(q, k, v, r, scale, W, cap, sinks=sinks)
+    for x, g in ((q, dq), (k, dk), (v, dvv), (sinks, ds)):
+        num = np.empty_like(x)
+        it = np.nditer(x, flags=["multi_index"])
+        for _ in it:
+            idx = it.multi_index
+            old = x[idx]
+            x[idx] = old + h
+            lp = loss()
+            x[idx] = old - h
+            lm = loss()
+            x[idx] = old
+            num[idx] = (lp - lm) / (2 * h)
+        err = np.abs(num - g).max() / max(1e-3, np.abs(num).max())
+        assert err < 1e-6, err
+
+
+def test_dv_differs_from_dk_closed_form():
+    """q = 0 with d_v != d: o_i is the mean of the visible v rows."""
+    T = 7
+    q = np.zeros((1, 1, T, 5))
+    k, v = _rand(1, 1, T, 5), _rand(1, 1, T, 3)
+    o, lse = A.attn_fwd(q, k, v, 0.3, 0, 0.0)
+    assert o.shape == (1, 1, T, 3)
+    for i in range(T):
+        np.testing.assert_allclose(o[0, 0, i], v[0, 0, :i + 1].mean(0), atol=1e-14)
+
+
+def test_max_logit_bruteforce_and_window_one():
+    B, H, Hkv, T, d, scale = 1, 4, 2, 6, 3, 0.7
+    q, k = _rand(B, H, T, d, sigma=2), _rand(B, Hkv, T, d, sigma=2)
+    for W, cap in ((0, 0.0), (2, 0.0), (0, 1.5)):
+        got = A.max_logit(q, k, scale, W, cap)
+        for h in range(H):
+            best = -math.inf
+            for i in range(T):
+                for j in range(T):
+                    if j <= i and (W == 0 or j > i - W):
+                        s = scale * sum(q[0, h, i, c] * k[0, h // 2, j, c] for c in range(d))
+                        best = max(best, cap * math.tanh(s / cap) if cap else s)
+            assert abs(got[0, h] - best) < 1e-12
+    got = A.max_logit(q, k, scale, 1, 0.0)
+    for h in range(H):
+        diag = scale * np.einsum("td,td->t", q[0, h], k[0, h // 2])
+        assert abs(got[0, h] - diag.max()) < 1e-12
