@@ -54,6 +54,17 @@ __device__ __forceinline__ float xor32_sum(float x) {
   return x + __shfl_xor(x, 32);
 }
 
+// Float atomic max through the integer order of IEEE-754 bit patterns
+// (non-negative values order as signed ints, negative ones reversed as
+// unsigned ints); the target must start at -inf or a real value.
+__device__ __forceinline__ void atomic_max_f32(float* addr, float v) {
+  // sign bit clear: larger float = larger int; set (incl. -0): smaller uint
+  if (__float_as_int(v) >= 0)
+    atomicMax((int*)addr, __float_as_int(v));
+  else
+    atomicMin((unsigned int*)addr, __float_as_uint(v));
+}
+
 // ---------------------------------------------------------------- LDS tiles
 // A tile of ROWS x D bf16 lives in LDS in rows of D*2 + 64 bytes (stride
 // = 16 mod 64 dwords), with the 16-byte chunks of each aligned 64-byte

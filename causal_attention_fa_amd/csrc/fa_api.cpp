@@ -107,8 +107,9 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 int attn_fwd(bool f32, const void* q, const void* k, const void* v, void* o, float* lse, int B,
              int H, int Hkv, int T, int d, float scale, int window, int global_every,
-             float softcap, hipStream_t stream) {
-  const char* fn = f32 ? "fa_fwd_f32" : "fa_fwd";
+             float softcap, hipStream_t stream, const char* fn = nullptr,
+             const float* sinks = nullptr, float* max_logit = nullptr) {
+  if (!fn) fn = f32 ? "fa_fwd_f32" : "fa_fwd";
   int rc = check_attn(fn, B, H, Hkv, T, d, scale, window, global_every, softcap);
   if (rc) return rc;
   const size_t es = f32 ? 4 : 2;
@@ -117,8 +118,18 @@ int attn_fwd(bool f32, const void* q, const void* k, const void* v, void* o, flo
                       {"o", o, nq}, {"lse", lse, (size_t)B * H * T * 4}};
   rc = check_ptrs(fn, rs, 5, 3);
   if (rc) return rc;
+  if (max_logit) {
+    const Range ml{"max_logit", max_logit, (size_t)B * H * 4};
+    if (!aligned16(max_logit)) return fail(FA_ERR_INVALID_ARG, std::string(fn) + ": max_logit not 16-byte aligned");
+    for (const Range& r : rs)
+      if (overlap(ml, r)) return fail(FA_ERR_INVALID_ARG, std::string(fn) + ": max_logit overlaps " + r.name);
+  }
   const int W = resolve_window(window, T);
   hipError_t e;
+  if (max_logit) {
+    e = fa::launch_fill_f32(max_logit, B * H, -INFINITY, stream);
+    if (e != hipSuccess) return finish(e, stream, fn);
+  }
   stage_begin(stream);
   if (f32) {
     fa::F32Args a{};
@@ -135,6 +146,8 @@ int attn_fwd(bool f32, const void* q, const void* k, const void* v, void* o, flo
     a.scale_log2e = scale * kLog2e;
     a.two_scale_over_cap_log2e = softcap > 0.f ? 2.f * scale * kLog2e / softcap : 0.f;
     a.cap_log2e = softcap > 0.f ? softcap * kLog2e : 0.f;
+    a.sinks = sinks;
+    a.max_logit = max_logit;
     e = fa::launch_fwd_bf16(a, d, stream);
   }
   return finish(e, stream, fn);
@@ -143,8 +156,9 @@ int attn_fwd(bool f32, const void* q, const void* k, const void* v, void* o, flo
 int attn_bwd(bool f32, const void* q, const void* k, const void* v, const void* o,
              const float* lse, const void* dO, void* dq, void* dk, void* dv, int B, int H,
              int Hkv, int T, int d, float scale, int window, int global_every, float softcap,
-             hipStream_t stream) {
-  const char* fn = f32 ? "fa_bwd_f32" : "fa_bwd";
+             hipStream_t stream, const char* fn = nullptr, const float* sinks = nullptr,
+             float* dsinks = nullptr) {
+  if (!fn) fn = f32 ? "fa_bwd_f32" : "fa_bwd";
   int rc = check_attn(fn, B, H, Hkv, T, d, scale, window, global_every, softcap);
   if (rc) return rc;
   const size_t es = f32 ? 4 : 2;
@@ -155,10 +169,28 @@ int attn_bwd(bool f32, const void* q, const void* k, const void* v, const void* 
                       {"dv", dv, nk}};
   rc = check_ptrs(fn, rs, 9, 6);
   if (rc) return rc;
+  if ((sinks == nullptr) != (dsinks == nullptr))
+    return fail(FA_ERR_INVALID_ARG, std::string(fn) + ": sinks and dsinks must both be given");
+  if (dsinks) {
+    const Range ds{"dsinks", dsinks, (size_t)H * 4};
+    if (!aligned16(dsinks) || !aligned16(sinks))
+      return fail(FA_ERR_INVALID_ARG, std::string(fn) + ": sinks/dsinks not 16-byte aligned");
+    for (const Range& r : rs)
+      if (overlap(ds, r)) return fail(FA_ERR_INVALID_ARG, std::string(fn) + ": dsinks overlaps " + r.name);
+    if (overlap(ds, {"sinks", sinks, (size_t)H * 4}))
+      return fail(FA_ERR_INVALID_ARG, std::string(fn) + ": dsinks overlaps sinks");
+  }
   const int W = resolve_window(window, T);
   float* Dst = nullptr;
   hipError_t e = hipMallocAsync((void**)&Dst, (size_t)B * H * T * sizeof(float), stream);
   if (e != hipSuccess) return finish(e, stream, "fa_bwd scratch");
+  if (dsinks) {
+    e = fa::launch_fill_f32(dsinks, H, 0.f, stream);
+    if (e != hipSuccess) {
+      (void)hipFreeAsync(Dst, stream);
+      return finish(e, stream, fn);
+    }
+  }
   stage_begin(stream);
   if (f32) {
     fa::F32Args a{};
@@ -179,6 +211,8 @@ int attn_bwd(bool f32, const void* q, const void* k, const void* v, const void* 
     a.two_scale_over_cap_log2e = softcap > 0.f ? 2.f * scale * kLog2e / softcap : 0.f;
     a.cap_log2e = softcap > 0.f ? softcap * kLog2e : 0.f;
     a.inv_cap = softcap > 0.f ? 1.f / softcap : 0.f;
+    a.sinks = sinks;
+    a.dsinks = dsinks;
     e = fa::launch_bwd_bf16(a, d, stream);
   }
   const hipError_t e2 = hipFreeAsync(Dst, stream);
@@ -245,6 +279,22 @@ int fa_bwd_f32(const void* q, const void* k, const void* v, const void* o, const
                hipStream_t stream) {
   return attn_bwd(true, q, k, v, o, lse, dO, dq, dk, dv, B, H, Hkv, T, d, scale, window,
                   global_every, softcap, stream);
+}
+
+int fa_fwd_sink(const void* q, const void* k, const void* v, void* o, float* lse,
+                const float* sinks, float* max_logit, int B, int H, int Hkv, int T, int d,
+                float scale, int window, int global_every, float softcap, hipStream_t stream) {
+  if (sinks && !aligned16(sinks)) return fail(FA_ERR_INVALID_ARG, "fa_fwd_sink: sinks not 16-byte aligned");
+  return attn_fwd(false, q, k, v, o, lse, B, H, Hkv, T, d, scale, window, global_every, softcap,
+                  stream, "fa_fwd_sink", sinks, max_logit);
+}
+
+int fa_bwd_sink(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                const void* dO, const float* sinks, void* dq, void* dk, void* dv, float* dsinks,
+                int B, int H, int Hkv, int T, int d, float scale, int window, int global_every,
+                float softcap, hipStream_t stream) {
+  return attn_bwd(false, q, k, v, o, lse, dO, dq, dk, dv, B, H, Hkv, T, d, scale, window,
+                  global_every, softcap, stream, "fa_bwd_sink", sinks, dsinks);
 }
 
 int rope_apply(const void* x, void* y, const float* inv_freq, int B, int H, int T, int d,

@@ -91,6 +91,14 @@ __global__ __launch_bounds__(64 * NW, (D >= 256 ? 1 : 8 / NW)) void fa_bwd_dq_ke
     if (g == 0 && qrow < T) a.Dst[bh * T + qrow] = Di;
   }
   const float lse2 = a.lse[bh * T + qr] * kLog2e;
+  if (a.sinks) {
+    // d sink_h = -sum_i exp(sink_h - lse_i) D_i over this head's rows (all
+    // batches accumulate into the same [H] entry).
+    float c = (g == 0 && qrow < T) ? fast_exp2(a.sinks[h] * kLog2e - lse2) * Di : 0.f;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) c += __shfl_xor(c, off);
+    if (lane == 0) atomicAdd(a.dsinks + h, -c);
+  }
 
   int kv_lo = 0;
   if (W > 0) kv_lo = max(0, q0 - W + 1);

@@ -75,12 +75,18 @@ __global__ __launch_bounds__(64 * NW, (D >= 256 || QW > 1 ? 1 : 8 / NW)) void fa
   const int kv_hi = min(T, q0 + BQ);
   const int ntiles = (kv_hi + BKV - 1) / BKV - t_lo;
 
+  // Attention sink (ARCHITECTURES.md plan wave 2 item 10): the online
+  // softmax starts from the sink logit, whose exp(0) = 1 enters the sum once
+  // (lane half 0) and whose value contribution is zero.
+  const bool has_sink = a.sinks != nullptr;
+  const float sink2 = has_sink ? a.sinks[h] * kLog2e : 0.f;
   f32x16 oacc[QW][NDB];
-  float m[QW], lsum[QW];
+  float m[QW], lsum[QW], mxl[QW];
 #pragma unroll
   for (int u = 0; u < QW; ++u) {
-    m[u] = kMaxInit;
-    lsum[u] = 0.f;
+    m[u] = has_sink ? sink2 : kMaxInit;
+    lsum[u] = (has_sink && g == 0) ? 1.f : 0.f;
+    mxl[u] = -INFINITY;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -170,6 +176,7 @@ __global__ __launch_bounds__(64 * NW, (D >= 256 || QW > 1 ? 1 : 8 / NW)) void fa
 #pragma unroll
           for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[u][t][i]);
         mt = xor32_max(mt) * cexp;
+        if (a.max_logit) mxl[u] = fmaxf(mxl[u], qrow < T ? mt : -INFINITY);
         // Lazy rescaling: the running max only moves (and O, l are rescaled)
         // when some row's tile max exceeds it by more than kRescaleSlack, so
         // p = 2^(s - m) stays below 2^kRescaleSlack; the branch is uniform.
@@ -218,6 +225,15 @@ __global__ __launch_bounds__(64 * NW, (D >= 256 || QW > 1 ? 1 : 8 / NW)) void fa
     __syncthreads();
   }
 
+  if (a.max_logit) {
+    // largest logit of the wave's rows (natural log units), one atomic per wave
+    float v = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < QW; ++u) v = fmaxf(v, mxl[u]);
+#pragma unroll
+    for (int off = 1; off < 32; off <<= 1) v = fmaxf(v, __shfl_xor(v, off));
+    if (lane == 0 && v > -INFINITY) atomic_max_f32(a.max_logit + bh, v * kLn2);
+  }
 #pragma unroll
   for (int u = 0; u < QW; ++u) {
     const int qrow = qw0 + 32 * u + l32;
@@ -254,6 +270,16 @@ static hipError_t launch_fwd_d(const FwdArgs& a, hipStream_t stream) {
   else
     hipLaunchKernelGGL((fa_fwd_kernel<D, BKV, NW, QW, false>), grid, dim3(64 * NW), 0, stream, a);
   stage_mark(stream);
+  return hipGetLastError();
+}
+
+__global__ void fill_f32_kernel(float* p, int n, float v) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+hipError_t launch_fill_f32(float* p, int n, float v, hipStream_t stream) {
+  hipLaunchKernelGGL(fill_f32_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, p, n, v);
   return hipGetLastError();
 }
 

@@ -23,6 +23,8 @@ struct FwdArgs {
   float scale_log2e;               // scale * log2(e)
   float two_scale_over_cap_log2e;  // 2 * scale * log2(e) / cap   (cap > 0)
   float cap_log2e;                 // cap * log2(e), 0 when no cap
+  const float* sinks;              // [H] sink logits (natural log) or null
+  float* max_logit;                // [B, H] largest softmax logit, or null
 };
 
 // Backward arguments.  Dst holds the per-row D = <dO_i, o_i> scratch
@@ -44,6 +46,8 @@ struct BwdArgs {
   float two_scale_over_cap_log2e;
   float cap_log2e;
   float inv_cap;                   // 1 / cap, 0 when no cap
+  const float* sinks;              // [H] sink logits or null
+  float* dsinks;                   // [H] gradient of the sinks (accumulated), or null
 };
 
 // float32 twins (plain pointers, same semantics).
@@ -75,6 +79,9 @@ struct RopeArgs {
 // Called by the launchers right after each kernel launch; records the
 // caller's stage events when fa_set_stage_events() armed them.
 void stage_mark(hipStream_t stream);
+
+// Fills n floats with v (initialises accumulated outputs inside a call).
+hipError_t launch_fill_f32(float* p, int n, float v, hipStream_t stream);
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, int d, hipStream_t stream);
 hipError_t launch_bwd_bf16(const BwdArgs& a, int d, hipStream_t stream);

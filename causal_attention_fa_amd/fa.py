@@ -48,6 +48,11 @@ for _name, _args in [("fa_fwd", _ATTN_FWD), ("fa_fwd_f32", _ATTN_FWD),
     _fn = getattr(_lib, _name)
     _fn.argtypes = _args
     _fn.restype = _I
+_lib.fa_fwd_sink.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I, _F, _P]
+_lib.fa_fwd_sink.restype = _I
+_lib.fa_bwd_sink.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F,
+                             _I, _I, _F, _P]
+_lib.fa_bwd_sink.restype = _I
 _lib.fa_layer_window.argtypes = [_I, _I, _I]
 _lib.fa_layer_window.restype = _I
 _lib.fa_rope_inv_freq.argtypes = [ctypes.POINTER(ctypes.c_float), _I, ctypes.c_double]
@@ -64,7 +69,7 @@ _lib.fa_set_stage_events.restype = _I
 _lib.fa_last_error.argtypes = []
 _lib.fa_last_error.restype = ctypes.c_char_p
 
-EXPORTS = ("fa_fwd", "fa_bwd", "rope_apply", "rope_apply_bwd", "fa_fwd_f32", "fa_bwd_f32",
+EXPORTS = ("fa_fwd", "fa_bwd", "fa_fwd_sink", "fa_bwd_sink", "rope_apply", "rope_apply_bwd", "fa_fwd_f32", "fa_bwd_f32",
            "rope_apply_f32", "rope_apply_bwd_f32", "fa_layer_window", "fa_rope_inv_freq",
            "fa_rope_inv_freq_llama3", "fa_layer_rope_theta", "fa_set_stage_events",
            "fa_last_error")
@@ -141,6 +146,21 @@ def fa_bwd_f32(q, k, v, o, lse, dO, dq, dk, dv, B, H, Hkv, T, d, scale, window=0
                global_every=0, softcap=0.0, stream=None):
     return _call_bwd(_lib.fa_bwd_f32, q, k, v, o, lse, dO, dq, dk, dv, B, H, Hkv, T, d, scale,
                      window, global_every, softcap, stream)
+
+
+def fa_fwd_sink(q, k, v, o, lse, sinks, max_logit, B, H, Hkv, T, d, scale, window=0,
+                global_every=0, softcap=0.0, stream=None):
+    return _check(_lib.fa_fwd_sink(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(sinks),
+                                   _ptr(max_logit), B, H, Hkv, T, d, float(scale), window,
+                                   global_every, float(softcap), _stream(stream)))
+
+
+def fa_bwd_sink(q, k, v, o, lse, dO, sinks, dq, dk, dv, dsinks, B, H, Hkv, T, d, scale,
+                window=0, global_every=0, softcap=0.0, stream=None):
+    return _check(_lib.fa_bwd_sink(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dO),
+                                   _ptr(sinks), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dsinks), B, H,
+                                   Hkv, T, d, float(scale), window, global_every, float(softcap),
+                                   _stream(stream)))
 
 
 def _rope_call(fn, x, y, inv_freq, B, H, T, d, stream):

@@ -84,6 +84,29 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o,
            int B, int H, int Hkv, int T, int d, float scale, int window,
            int global_every, float softcap, hipStream_t stream);
 
+/* Attention sinks and the per-head max logit (bf16 tensors).
+ * sinks: [H] float32 device array (natural-log logits) or NULL.  A sink is a
+ * learned per-head logit in every row's softmax denominator that carries no
+ * value (Forge ARCHITECTURES.md family table, GPT-OSS; plan wave 2 item 10:
+ * the online softmax starts its (max, sum) from it): lse includes it.
+ * max_logit: [B, H] float32 device output or NULL: the largest visible
+ * query-key logit (after the cap, if any; = scale*<q,k> without one; the
+ * sink is not a query-key logit and is not counted) --
+ * the quantity QK-Clip monitors (ARCHITECTURES.md, Kimi K2 MuonClip; plan
+ * wave 3 item 12).  fa_fwd_sink with both NULL equals fa_fwd.
+ * fa_bwd_sink: sinks and dsinks both NULL (= fa_bwd) or both given; dsinks
+ * [H] is overwritten with d sum(o*dO) / d sink summed over the batch
+ * (accumulated with float atomics: the last bits may vary run to run). */
+int fa_fwd_sink(const void* q, const void* k, const void* v, void* o,
+                float* lse, const float* sinks, float* max_logit, int B, int H,
+                int Hkv, int T, int d, float scale, int window,
+                int global_every, float softcap, hipStream_t stream);
+int fa_bwd_sink(const void* q, const void* k, const void* v, const void* o,
+                const float* lse, const void* dO, const float* sinks,
+                void* dq, void* dk, void* dv, float* dsinks, int B, int H,
+                int Hkv, int T, int d, float scale, int window,
+                int global_every, float softcap, hipStream_t stream);
+
 /* RoPE on interleaved pairs (x[2i], x[2i+1]) at positions t = 0..T-1 with
  * angle fl32(t * inv_freq[i]) (Forge README: interleaved pairs; Forge
  * attention.h commit log, "Wave 1": kernels read a host-precomputed

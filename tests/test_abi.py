@@ -81,6 +81,28 @@ def test_bwd_validation_and_overlap():
     del rc
 
 
+def test_sink_validation():
+    lib = fa._lib
+    fwd = [P, 2 * P, 3 * P, 4 * P, 5 * P]
+    assert lib.fa_fwd_sink(*fwd, 6 * P, 4 * P + 64, 1, 2, 2, 8, 64, 0.125, 0, 0, 0.0, None) == -1
+    assert "max_logit overlaps o" in fa.fa_last_error()
+    assert lib.fa_fwd_sink(*fwd, 6 * P, 7 * P + 4, 1, 2, 2, 8, 64, 0.125, 0, 0, 0.0, None) == -1
+    assert "aligned" in fa.fa_last_error()
+    assert lib.fa_fwd_sink(*fwd, 6 * P + 4, None, 1, 2, 2, 8, 64, 0.125, 0, 0, 0.0, None) == -1
+    assert "sinks not 16-byte aligned" in fa.fa_last_error()
+    bwd = [P, 2 * P, 3 * P, 4 * P, 5 * P, 6 * P]
+    outs = [8 * P, 9 * P, 10 * P]
+    assert lib.fa_bwd_sink(*bwd, 7 * P, *outs, None, 1, 2, 2, 8, 64, 0.125, 0, 0, 0.0,
+                           None) == -1
+    assert "both" in fa.fa_last_error()
+    assert lib.fa_bwd_sink(*bwd, 7 * P, *outs, 8 * P, 1, 2, 2, 8, 64, 0.125, 0, 0, 0.0,
+                           None) == -1
+    assert "dsinks overlaps" in fa.fa_last_error()
+    assert lib.fa_bwd_sink(*bwd, 7 * P, *outs, 7 * P, 1, 2, 2, 8, 64, 0.125, 0, 0, 0.0,
+                           None) == -1
+    assert "dsinks overlaps sinks" in fa.fa_last_error()
+
+
 def test_rope_validation():
     lib = fa._lib
     assert lib.rope_apply(0, P, 2 * P, 1, 1, 4, 64, None) == -1
