@@ -23,15 +23,21 @@ Sources (web pages; cited by title and section throughout):
   sliding_window(0), sliding_global_every(0), attn_softcap(0),
   n_kv_heads(=n_heads), rope_theta(10000); validations n_heads % n_kv_heads
   == 0 and even head_dim.
+* Same commit, INFERENCE_RESEARCH.md, section 2 ("KV cache"): a cache
+  preallocated at maximum length, [layer][head][seq][d], read by a
+  dedicated single-query kernel split along the cache.
 
 Modules:
     attention  -- attn_fwd / attn_bwd definitions (full score matrix, fp64),
                   row/column-restricted evaluators for sampled checks at
                   large T, layer_window.
-    rope       -- inv_freq table, rope / rope_bwd.
+    rope       -- inv_freq table (plain and llama3-rescaled), per-layer
+                  RoPE base, rope / rope_bwd.
+    decode     -- single-query decode over a KV cache, and the exact merge
+                  of partial results over disjoint key sets.
 
 Every function is pinned by tests in tests/test_oracle_*.py to closed
 forms, invariants, library routines or brute force; see each function's
 docstring for its pins.
 """
-from . import attention, rope  # noqa: F401
+from . import attention, decode, rope  # noqa: F401
