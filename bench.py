@@ -102,6 +102,50 @@ def traffic_for(workload, kernel, src_hash):
     return t.get("kernels", {}).get(kernel, {}).get("hbm_bytes_per_launch")
 
 
+def decode_leg(name, iters, dev):
+    """fa_decode on a decode workload: per-call time from HIP events on the
+    launch stream (split and combine kernels separately) and the HBM rate of
+    its algorithmic bytes (visible K and V rows once, q, o, lse, lens)."""
+    import torch
+    from causal_attention_fa_amd import fa, synth
+    w = synth.DECODE_WORKLOADS[name]
+    q, kc, vc, lens = synth.draw_decode(w, device=dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    for _ in range(3):
+        fa.fa_decode(q, kc, vc, lens, o, lse, None, w.B, w.H, w.Hkv, w.S, w.d, w.scale,
+                     w.window, w.softcap, sh)
+    torch.cuda.synchronize()
+    evs = []
+    for _ in range(iters):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        for x in e:          # creates the underlying HIP event
+            x.record(stream)
+        fa.fa_set_stage_events([x.cuda_event for x in e])
+        fa.fa_decode(q, kc, vc, lens, o, lse, None, w.B, w.H, w.Hkv, w.S, w.d, w.scale,
+                     w.window, w.softcap, sh)
+        evs.append(e)
+    fa.fa_set_stage_events([])
+    torch.cuda.synchronize()
+    split = sum(e[0].elapsed_time(e[1]) for e in evs) / iters
+    comb = sum(e[1].elapsed_time(e[2]) for e in evs) / iters
+    L = lens.cpu().long()
+    vis = L.clamp(max=w.window) if w.window > 0 else L
+    kv_bytes = int(vis.sum()) * w.Hkv * w.d * 2 * 2
+    io_bytes = q.numel() * 2 * 2 + lse.numel() * 4 + lens.numel() * 4
+    ms = split + comb
+    gbs = (kv_bytes + io_bytes) / (ms * 1e-3) / 1e9
+    ns, ch = fa.fa_decode_splits(w.B, w.Hkv, w.S, w.window)
+    return {"workload": w.name, "B": w.B, "H": w.H, "Hkv": w.Hkv, "S": w.S, "d": w.d,
+            "window": w.window, "softcap": w.softcap, "chunks": [ns, ch],
+            "ms": round(ms, 4), "split_ms": round(split, 4), "combine_ms": round(comb, 4),
+            "algorithmic_bytes": kv_bytes + io_bytes, "gbs": round(gbs, 1),
+            "split_gbs": round(kv_bytes / (split * 1e-3) / 1e9, 1),
+            "frac_hbm": round(gbs / PEAK_HBM_GBS, 4), "iters": iters}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -111,6 +155,9 @@ def main():
     ap.add_argument("--calibrate-copy-mb", type=float, default=0.0,
                     help="only run a plain device copy of this many MiB (5 times) and "
                          "exit: the reference kernel for scaling HBM byte counters")
+    ap.add_argument("--decode-workload", default="qwen25-decode",
+                    help="decode workload timed after the main step ('none' to skip)")
+    ap.add_argument("--decode-iters", type=int, default=20)
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="CPU-baseline budget: oracle heads are timed until this many "
                          "seconds have passed (0: skip)")
@@ -236,6 +283,14 @@ def main():
     if rope:
         nbytes_q = 2 * q.numel() * 2 + d // 2 * 4
         extra["rope_q_gbs"] = round(nbytes_q / (kern["rope_q"] * 1e-3) / 1e9, 1)
+
+    if args.decode_workload != "none":
+        del q, k, v, do, o, lse, dq, dk, dv
+        if rope:
+            del qr, kr, dqi, dki
+        torch.cuda.empty_cache()
+        log(f"[bench] decode leg: {args.decode_workload}")
+        extra["decode"] = decode_leg(args.decode_workload, args.decode_iters, dev)
 
     cpu = None
     if args.cpu_seconds > 0:

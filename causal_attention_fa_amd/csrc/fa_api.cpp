@@ -4,6 +4,7 @@
 // interface.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstdlib>
@@ -220,6 +221,20 @@ int attn_bwd(bool f32, const void* q, const void* k, const void* v, const void* 
   return finish(e, stream, fn);
 }
 
+// Chunking of the decode: enough (batch, KV head, chunk) units to fill the
+// chip several times over, at least 8 tiles of 32 keys per chunk, at most
+// kDecMaxSplits chunks.  max_keys bounds the visible keys of any sequence.
+void decode_split(int units, int max_keys, int* nsplit, int* chunk) {
+  constexpr int kTargetUnits = 4096, kMinChunk = 256, kTile = 32;
+  int ns = (kTargetUnits + units - 1) / units;
+  ns = std::min(ns, (max_keys + kMinChunk - 1) / kMinChunk);
+  ns = std::max(1, std::min(ns, fa::kDecMaxSplits));
+  int c = (max_keys + ns - 1) / ns;
+  c = (c + kTile - 1) / kTile * kTile;
+  *chunk = c;
+  *nsplit = (max_keys + c - 1) / c;
+}
+
 int rope(bool f32, bool bwd, const void* x, void* y, const float* inv_freq, int B, int H, int T,
          int d, hipStream_t stream) {
   const char* fn = bwd ? (f32 ? "rope_apply_bwd_f32" : "rope_apply_bwd")
@@ -295,6 +310,57 @@ int fa_bwd_sink(const void* q, const void* k, const void* v, const void* o, cons
                 float softcap, hipStream_t stream) {
   return attn_bwd(false, q, k, v, o, lse, dO, dq, dk, dv, B, H, Hkv, T, d, scale, window,
                   global_every, softcap, stream, "fa_bwd_sink", sinks, dsinks);
+}
+
+int fa_decode(const void* q, const void* k_cache, const void* v_cache, const int* lens, void* o,
+              float* lse, const float* sinks, int B, int H, int Hkv, int S, int d, float scale,
+              int window, float softcap, hipStream_t stream) {
+  const char* fn = "fa_decode";
+  int rc = check_attn(fn, B, H, Hkv, S, d, scale, window, 0, softcap);
+  if (rc) return rc;
+  if (H / Hkv > 32) return fail(FA_ERR_UNSUPPORTED, "fa_decode: at most 32 query heads per KV head");
+  const size_t nq = (size_t)B * H * d * 2, nc = (size_t)B * Hkv * S * d * 2;
+  const Range rs[] = {{"q", q, nq}, {"k_cache", k_cache, nc}, {"v_cache", v_cache, nc},
+                      {"lens", lens, (size_t)B * 4}, {"o", o, nq}};
+  rc = check_ptrs(fn, rs, 5, 4);
+  if (rc) return rc;
+  if (lse) {
+    const Range lr{"lse", lse, (size_t)B * H * 4};
+    if (!aligned16(lse)) return fail(FA_ERR_INVALID_ARG, "fa_decode: lse not 16-byte aligned");
+    for (const Range& r : rs)
+      if (overlap(lr, r)) return fail(FA_ERR_INVALID_ARG, std::string("fa_decode: lse overlaps ") + r.name);
+  }
+  if (sinks && !aligned16(sinks)) return fail(FA_ERR_INVALID_ARG, "fa_decode: sinks not 16-byte aligned");
+  const int max_keys = window > 0 ? std::min(window, S) : S;
+  int nsplit = 1, chunk = 32;
+  decode_split(B * Hkv, max_keys, &nsplit, &chunk);
+  if ((double)B * Hkv * nsplit > 2.0e9) return fail(FA_ERR_INVALID_ARG, "fa_decode: too many work units");
+  const size_t units = (size_t)B * Hkv * nsplit;
+  const size_t part_bytes = units * (H / Hkv) * (size_t)(d + 2) * sizeof(float);
+  float* part = nullptr;
+  hipError_t e = hipMallocAsync((void**)&part, part_bytes, stream);
+  if (e != hipSuccess) return finish(e, stream, "fa_decode scratch");
+  fa::DecodeArgs a{};
+  a.q = (const fa::bf16*)q; a.kc = (const fa::bf16*)k_cache; a.vc = (const fa::bf16*)v_cache;
+  a.lens = lens; a.o = (fa::bf16*)o; a.lse = lse; a.sinks = sinks;
+  a.part_o = part;
+  a.part_ml = part + units * (H / Hkv) * d;
+  a.B = B; a.H = H; a.Hkv = Hkv; a.S = S; a.window = window; a.nsplit = nsplit; a.chunk = chunk;
+  a.scale_log2e = scale * kLog2e;
+  a.two_scale_over_cap_log2e = softcap > 0.f ? 2.f * scale * kLog2e / softcap : 0.f;
+  a.cap_log2e = softcap > 0.f ? softcap * kLog2e : 0.f;
+  stage_begin(stream);
+  e = fa::launch_decode_bf16(a, d, softcap > 0.f, stream);
+  const hipError_t e2 = hipFreeAsync(part, stream);
+  if (e == hipSuccess) e = e2;
+  return finish(e, stream, fn);
+}
+
+int fa_decode_splits(int B, int Hkv, int S, int window, int* nsplit, int* chunk) {
+  if (B <= 0 || Hkv <= 0 || S <= 0 || window < 0 || !nsplit || !chunk)
+    return fail(FA_ERR_INVALID_ARG, "fa_decode_splits: invalid arguments");
+  decode_split(B * Hkv, window > 0 ? std::min(window, S) : S, nsplit, chunk);
+  return FA_OK;
 }
 
 int rope_apply(const void* x, void* y, const float* inv_freq, int B, int H, int T, int d,

@@ -1,0 +1,268 @@
+// Single-query decode attention over a preallocated KV cache, split along
+// the cache (Forge commit "Add HF streaming data pipeline and three research
+// reports", INFERENCE_RESEARCH.md, section 2: cache [layer][head][seq][d],
+// a dedicated one-query kernel split-K along the cache; GQA is the largest
+// saving in KV bandwidth).
+//
+// The work is bound by HBM: every visible K and V byte is read once and
+// used by all G query heads of its KV group.  Two kernels:
+//   * split: one wave per (batch, KV head, chunk of the cache).  K and V
+//     tiles of 32 keys stream global -> registers (one tile ahead) -> LDS;
+//     the G query heads of the group are the columns of S^T = K Q^T, so the
+//     contraction over d and P V run on the bf16 MFMA exactly as in the
+//     prefill forward (columns past G are idle), and the VALU only does the
+//     online softmax.  The chunk's unnormalised output O, running max m
+//     (log2 units) and sum l go to a float32 scratch;
+//   * combine: one wave per (batch, head) merges the chunks exactly by
+//     their maxima and sums (o = sum_c 2^(m_c - M) O_c / L), adds the sink
+//     to the normaliser, and writes o (bf16) and lse.
+// Cache rows at or past the sequence's length are never read (the tile
+// loads clamp to the last valid row and the mask removes the duplicates).
+#include "device_common.h"
+#include "internal.h"
+
+namespace fa {
+
+constexpr int kDecBKV = 32;  // keys per tile
+
+// NW waves per workgroup share the K/V tiles; each computes the (cheap,
+// identical) scores and owns D/NW of the output columns, so the d = 256
+// case keeps two waves per SIMD without spilling.
+template <int D, int NW, bool CAP>
+__global__ __launch_bounds__(64 * NW, 2) void fa_decode_split_kernel(DecodeArgs a) {
+  constexpr int NT = 64 * NW;
+  constexpr int TILE = Lay<D>::template bytes<kDecBKV>();
+  constexpr int NDB = D / 32 / NW;  // 32-wide output blocks per wave
+  constexpr int NC = D / 16;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * TILE];
+  LDS_AS char* Kt = (LDS_AS char*)smem;
+  LDS_AS char* Vt = Kt + TILE;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int d0 = wave * (D / NW);
+  const int lane = tid & 63;
+  const int g = lane >> 5;
+  const int l32 = lane & 31;
+  const int G = a.H / a.Hkv;
+  const int unit = blockIdx.x;  // (batch, KV head, chunk), chunk fastest
+  const int sp = unit % a.nsplit;
+  const int bhkv = unit / a.nsplit;
+  const int b = bhkv / a.Hkv;
+  const int hkv = bhkv % a.Hkv;
+  const int len = min(max(a.lens[b], 0), a.S);
+  const int lo = a.window > 0 ? max(0, len - a.window) : 0;
+  const int start = lo + sp * a.chunk;
+  const int end = min(start + a.chunk, len);
+  float* po = a.part_o + (size_t)unit * G * D;
+  float* pml = a.part_ml + (size_t)unit * G * 2;
+  if (start >= end) {
+    // empty chunk: m = -inf marks it; the combine never reads its O
+    for (int i = tid; i < G; i += NT) {
+      pml[2 * i] = -INFINITY;
+      pml[2 * i + 1] = 0.f;
+    }
+    return;
+  }
+
+  // The group's query heads as the B operand: lane column l32 = head
+  // hkv*G + l32 (columns past G repeat the last head and are not written).
+  bf16x8 qreg[NC];
+  {
+    const int r = min(l32, G - 1);
+    const bf16x8* src = (const bf16x8*)(a.q + ((size_t)b * a.H + hkv * G + r) * D + 8 * g);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) qreg[c] = src[2 * c];
+  }
+
+  const size_t base = (size_t)bhkv * a.S * D;
+  const bf16* Kp = a.kc + base;
+  const bf16* Vp = a.vc + base;
+  const int ntiles = (end - start + kDecBKV - 1) / kDecBKV;
+  const float cexp = CAP ? 1.f : a.scale_log2e;
+
+  f32x16 oacc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
+  float m = kMaxInit, l = 0.f;
+
+  TileStage<D, kDecBKV, NT> kst, vst;
+  kst.load(Kp, start, end, tid);
+  vst.load(Vp, start, end, tid);
+  for (int j = 0; j < ntiles; ++j) {
+    const int kv0 = start + j * kDecBKV;
+    kst.store(Kt, tid);
+    vst.store(Vt, tid);
+    __syncthreads();
+    if (j + 1 < ntiles) {
+      kst.load(Kp, kv0 + kDecBKV, end, tid);
+      vst.load(Vp, kv0 + kDecBKV, end, tid);
+    }
+    f32x16 sacc[1];
+    mma_rows<D, 1>(sacc, Kt, qreg, lane);
+    f32x16 s = sacc[0];
+    if (CAP) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float e = fast_exp2(s[i] * a.two_scale_over_cap_log2e);
+        s[i] = (1.f - 2.f * __builtin_amdgcn_rcpf(e + 1.f)) * a.cap_log2e;
+      }
+    }
+    if (kv0 + kDecBKV > end) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[i] = kv0 + acc_row(i, g) < end ? s[i] : -INFINITY;
+    }
+    float mt = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[i]);
+    mt = xor32_max(mt) * cexp;
+    if (__any(mt > m + kRescaleSlack)) {
+      const float mnew = fmaxf(m, mt);
+      const float alpha = fast_exp2(m - mnew);
+      m = mnew;
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+    }
+    float ps = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float p = fast_exp2(fmaf(s[i], cexp, -m));
+      s[i] = p;
+      ps += p;
+    }
+    l += ps;
+    bf16x8 pb[2];
+#pragma unroll
+    for (int c16 = 0; c16 < 2; ++c16) {
+      float tmp[8];
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) tmp[jj] = s[8 * c16 + jj];
+      pb[c16] = pack_bf16(tmp);
+    }
+#pragma unroll
+    for (int c16 = 0; c16 < 2; ++c16)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+        oacc[db] = mfma32(lds_tr_operand<D>(Vt, 0, c16, d0 + 32 * db, lane), pb[c16], oacc[db]);
+    __syncthreads();
+  }
+
+  const float lt = xor32_sum(l);
+  if (l32 < G) {
+    // O^T accumulator: acc i of block db holds d = d0 + 32 db + acc_row(i, g)
+    float* orow = po + (size_t)l32 * D + d0;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        f32x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = oacc[db][4 * i4 + e];
+        *(f32x4*)(orow + 32 * db + 8 * i4 + 4 * g) = v;
+      }
+    if (g == 0 && wave == 0) {
+      pml[2 * l32] = m;
+      pml[2 * l32 + 1] = lt;
+    }
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(64) void fa_decode_combine_kernel(DecodeArgs a) {
+  constexpr int PER = D / 64;  // output elements per lane
+  __shared__ float wsh[kDecMaxSplits];
+  const int lane = threadIdx.x;
+  const int G = a.H / a.Hkv;
+  const int bh = blockIdx.x;
+  const int b = bh / a.H;
+  const int h = bh % a.H;
+  const int hkv = h / G;
+  const int r = h % G;
+  const size_t unit0 = ((size_t)b * a.Hkv + hkv) * a.nsplit;
+  const int ns = a.nsplit;
+
+  float M = -INFINITY;
+  for (int s = lane; s < ns; s += 64) {
+    const float ms = a.part_ml[((unit0 + s) * G + r) * 2];
+    M = fmaxf(M, ms);
+  }
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) M = fmaxf(M, __shfl_xor(M, off));
+  const bool has_sink = a.sinks != nullptr;
+  const float sink2 = has_sink ? a.sinks[h] * kLog2e : -INFINITY;
+  M = fmaxf(M, sink2);
+
+  bf16* out = a.o + (size_t)bh * D + lane * PER;
+  if (M == -INFINITY) {
+    // no visible key and no sink: empty softmax
+#pragma unroll
+    for (int e = 0; e < PER; ++e) out[e] = (bf16)0.f;
+    if (lane == 0 && a.lse) a.lse[bh] = -INFINITY;
+    return;
+  }
+  float L = 0.f;
+  for (int s = lane; s < ns; s += 64) {
+    const float* e = a.part_ml + ((unit0 + s) * G + r) * 2;
+    const float w = e[0] == -INFINITY ? 0.f : fast_exp2(e[0] - M);
+    wsh[s] = w;
+    L += w * e[1];
+  }
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) L += __shfl_xor(L, off);
+  if (has_sink) L += fast_exp2(sink2 - M);
+  __syncthreads();
+
+  float acc[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) acc[e] = 0.f;
+  for (int s = 0; s < ns; ++s) {
+    const float w = wsh[s];
+    if (w != 0.f) {  // uniform; skips empty chunks, whose O is never written
+      const float* src = a.part_o + ((unit0 + s) * G + r) * D + lane * PER;
+#pragma unroll
+      for (int e = 0; e < PER; ++e) acc[e] = fmaf(w, src[e], acc[e]);
+    }
+  }
+  const float inv = 1.f / L;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) out[e] = (bf16)(acc[e] * inv);
+  if (lane == 0 && a.lse) a.lse[bh] = (M + __log2f(L)) * kLn2;
+}
+
+// Waves per split workgroup, by head size.
+#ifndef DEC_NW64
+#define DEC_NW64 1
+#endif
+#ifndef DEC_NW128
+#define DEC_NW128 2
+#endif
+#ifndef DEC_NW256
+#define DEC_NW256 4
+#endif
+
+template <int D, bool CAP>
+static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
+  constexpr int NW = D == 64 ? DEC_NW64 : D == 128 ? DEC_NW128 : DEC_NW256;
+  const unsigned units = (unsigned)a.B * a.Hkv * a.nsplit;
+  fa_decode_split_kernel<D, NW, CAP><<<units, 64 * NW, 0, stream>>>(a);
+  stage_mark(stream);
+  fa_decode_combine_kernel<D><<<(unsigned)a.B * a.H, 64, 0, stream>>>(a);
+  stage_mark(stream);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_bf16(const DecodeArgs& a, int d, bool cap, hipStream_t stream) {
+  switch (d) {
+    case 64: return cap ? launch_decode_t<64, true>(a, stream) : launch_decode_t<64, false>(a, stream);
+    case 128: return cap ? launch_decode_t<128, true>(a, stream) : launch_decode_t<128, false>(a, stream);
+    case 256: return cap ? launch_decode_t<256, true>(a, stream) : launch_decode_t<256, false>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace fa

@@ -69,6 +69,26 @@ struct F32Args {
   float softcap;
 };
 
+// Decode over a KV cache.  part_o / part_ml: per (batch, KV head, chunk)
+// float32 scratch of the split pass -- unnormalised O [G, d] and the
+// running (max in log2 units, sum) per query head of the group.
+constexpr int kDecMaxSplits = 256;
+struct DecodeArgs {
+  const bf16* q;      // [B, H, d]
+  const bf16* kc;     // [B, Hkv, S, d]
+  const bf16* vc;     // [B, Hkv, S, d]
+  const int* lens;    // [B] tokens held by each sequence (query at lens-1)
+  bf16* o;            // [B, H, d]
+  float* lse;         // [B, H] or null
+  const float* sinks; // [H] or null
+  float* part_o;
+  float* part_ml;
+  int B, H, Hkv, S, window, nsplit, chunk;
+  float scale_log2e;
+  float two_scale_over_cap_log2e;
+  float cap_log2e;
+};
+
 struct RopeArgs {
   const void* x;
   void* y;
@@ -87,6 +107,7 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, int d, hipStream_t stream);
 hipError_t launch_bwd_bf16(const BwdArgs& a, int d, hipStream_t stream);
 hipError_t launch_fwd_f32(const F32Args& a, hipStream_t stream);
 hipError_t launch_bwd_f32(const F32Args& a, hipStream_t stream);
+hipError_t launch_decode_bf16(const DecodeArgs& a, int d, bool cap, hipStream_t stream);
 hipError_t launch_rope_bf16(const RopeArgs& a, bool bwd, hipStream_t stream);
 hipError_t launch_rope_f32(const RopeArgs& a, bool bwd, hipStream_t stream);
 

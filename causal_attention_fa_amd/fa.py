@@ -53,6 +53,10 @@ _lib.fa_fwd_sink.restype = _I
 _lib.fa_bwd_sink.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F,
                              _I, _I, _F, _P]
 _lib.fa_bwd_sink.restype = _I
+_lib.fa_decode.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _F, _P]
+_lib.fa_decode.restype = _I
+_lib.fa_decode_splits.argtypes = [_I, _I, _I, _I, ctypes.POINTER(_I), ctypes.POINTER(_I)]
+_lib.fa_decode_splits.restype = _I
 _lib.fa_layer_window.argtypes = [_I, _I, _I]
 _lib.fa_layer_window.restype = _I
 _lib.fa_rope_inv_freq.argtypes = [ctypes.POINTER(ctypes.c_float), _I, ctypes.c_double]
@@ -69,7 +73,7 @@ _lib.fa_set_stage_events.restype = _I
 _lib.fa_last_error.argtypes = []
 _lib.fa_last_error.restype = ctypes.c_char_p
 
-EXPORTS = ("fa_fwd", "fa_bwd", "fa_fwd_sink", "fa_bwd_sink", "rope_apply", "rope_apply_bwd", "fa_fwd_f32", "fa_bwd_f32",
+EXPORTS = ("fa_fwd", "fa_bwd", "fa_fwd_sink", "fa_bwd_sink", "fa_decode", "fa_decode_splits", "rope_apply", "rope_apply_bwd", "fa_fwd_f32", "fa_bwd_f32",
            "rope_apply_f32", "rope_apply_bwd_f32", "fa_layer_window", "fa_rope_inv_freq",
            "fa_rope_inv_freq_llama3", "fa_layer_rope_theta", "fa_set_stage_events",
            "fa_last_error")
@@ -161,6 +165,20 @@ def fa_bwd_sink(q, k, v, o, lse, dO, sinks, dq, dk, dv, dsinks, B, H, Hkv, T, d,
                                    _ptr(sinks), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dsinks), B, H,
                                    Hkv, T, d, float(scale), window, global_every, float(softcap),
                                    _stream(stream)))
+
+
+def fa_decode(q, k_cache, v_cache, lens, o, lse, sinks, B, H, Hkv, S, d, scale, window=0,
+              softcap=0.0, stream=None):
+    return _check(_lib.fa_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(lens), _ptr(o),
+                                 _ptr(lse), _ptr(sinks), B, H, Hkv, S, d, float(scale), window,
+                                 float(softcap), _stream(stream)))
+
+
+def fa_decode_splits(B, Hkv, S, window=0):
+    """(nsplit, chunk) fa_decode uses for these sizes."""
+    ns, ch = _I(), _I()
+    _check(_lib.fa_decode_splits(B, Hkv, S, window, ctypes.byref(ns), ctypes.byref(ch)))
+    return ns.value, ch.value
 
 
 def _rope_call(fn, x, y, inv_freq, B, H, T, d, stream):

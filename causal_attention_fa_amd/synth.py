@@ -21,6 +21,12 @@ Workloads (shapes of the models the pages describe; no dataset is used):
   gemma-global  same, full causal, cap 50
   gemma3-local  same, window 1024, cap 50 (Gemma 3 row: 5 local : 1 global,
                 window 1024; the global layer is gemma-global)
+
+Decode workloads (one new token per sequence, preallocated 32k bf16 cache,
+ragged lengths uniform in [16384, 32768]):
+  qwen25-decode        B32 H28/4 S32768 d128, V ~ N(0, 0.5^2)
+  mistral-decode       B32 H32/8 S32768 d128, window 4096
+  gemma-global-decode  B16 H8/4 S32768 d256, cap 50, Q, K ~ N(0, 2^2)
 """
 from __future__ import annotations
 
@@ -29,7 +35,8 @@ import math
 
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "draw", "to_f64"]
+__all__ = ["Workload", "WORKLOADS", "draw", "to_f64", "DecodeWorkload", "DECODE_WORKLOADS",
+           "draw_decode"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -113,6 +120,68 @@ def draw(w: Workload, seed: int | None = None, need_do: bool = True):
     dt = w.torch_dtype
     out = [t.to(dt) if t is not None else None for t in (q, k, v, do)]
     return tuple(out)
+
+
+@dataclasses.dataclass(frozen=True)
+class DecodeWorkload:
+    """One new token per sequence against a preallocated bf16 KV cache of
+    S positions; sequence b holds lens[b] tokens, drawn uniformly from
+    [lens_lo, S] (ragged batch)."""
+    name: str
+    B: int
+    H: int
+    Hkv: int
+    S: int
+    d: int
+    window: int = 0
+    softcap: float = 0.0
+    lens_lo: int = 1
+    sigma_qk: float = 1.0
+    sigma_v: float = 1.0
+    seed: int = 0
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+    def replace(self, **kw) -> "DecodeWorkload":
+        return dataclasses.replace(self, **kw)
+
+
+# Decode counterparts of the training workloads, at a serving batch and a
+# 32k cache, so that the cache (>= 0.5 GB read per call) streams from HBM
+# rather than the 256 MB last-level cache.
+DECODE_WORKLOADS = {
+    w.name: w for w in [
+        DecodeWorkload("qwen25-decode", 32, 28, 4, 32768, 128, lens_lo=16384,
+                       sigma_v=0.5),
+        DecodeWorkload("mistral-decode", 32, 32, 8, 32768, 128, window=4096,
+                       lens_lo=16384),
+        DecodeWorkload("gemma-global-decode", 16, 8, 4, 32768, 256, softcap=50.0,
+                       lens_lo=16384, sigma_qk=2.0),
+    ]
+}
+
+
+def draw_decode(w: DecodeWorkload, device="cpu", seed: int | None = None):
+    """Seeded (q [B,H,d], k_cache, v_cache [B,Hkv,S,d] bf16, lens [B] int32)
+    on ``device``.  lens first (CPU generator), then q, K, V as float32
+    randn * sigma rounded to bf16, drawn by a generator on ``device`` (the
+    caches of the full-size workloads are several GB)."""
+    s = w.seed if seed is None else seed
+    gc = torch.Generator("cpu")
+    gc.manual_seed(s)
+    lens = torch.randint(w.lens_lo, w.S + 1, (w.B,), generator=gc, dtype=torch.int32)
+    g = torch.Generator(device)
+    g.manual_seed(s + 1)
+    q = (torch.randn((w.B, w.H, w.d), generator=g, device=device) * w.sigma_qk).to(torch.bfloat16)
+    shp = (w.B, w.Hkv, w.S, w.d)
+    k = torch.empty(shp, dtype=torch.bfloat16, device=device)
+    v = torch.empty(shp, dtype=torch.bfloat16, device=device)
+    for b in range(w.B):   # per sequence: bounded float32 temporaries
+        k[b] = (torch.randn(shp[1:], generator=g, device=device) * w.sigma_qk).to(torch.bfloat16)
+        v[b] = (torch.randn(shp[1:], generator=g, device=device) * w.sigma_v).to(torch.bfloat16)
+    return q, k, v, lens.to(device)
 
 
 def to_f64(t):

@@ -107,6 +107,36 @@ int fa_bwd_sink(const void* q, const void* k, const void* v, const void* o,
                 int Hkv, int T, int d, float scale, int window,
                 int global_every, float softcap, hipStream_t stream);
 
+/* Single-query decode over a preallocated KV cache (Forge commit "Add HF
+ * streaming data pipeline and three research reports", INFERENCE_RESEARCH.md
+ * section 2: cache [layer][head][seq][d] preallocated at the maximum length;
+ * one query per sequence; split along the cache for long contexts).
+ *   q        [B, H, d]        bf16, the new token's query (RoPE applied)
+ *   k_cache  [B, Hkv, S, d]   bf16, one layer's cache, S = allocated length
+ *   v_cache  [B, Hkv, S, d]   bf16
+ *   lens     [B]              int32 device array: tokens held by sequence b,
+ *                             the new one included (its query is at position
+ *                             lens[b]-1); values are clamped to [0, S]
+ *   o        [B, H, d]        bf16 output
+ *   lse      [B, H]           float32 output (natural log), or NULL
+ *   sinks    [H]              float32 sink logits, or NULL
+ * Head h reads KV head h / (H/Hkv) (H/Hkv <= 32); keys j < lens[b] with
+ * j > lens[b]-1-window are visible (window 0 = all); softcap as in fa_fwd.
+ * Cache rows at or past lens[b] are never read.  lens[b] = 0 gives o = 0
+ * and lse = -inf (= the sink with a sink).  The call allocates its float32
+ * chunk scratch with hipMallocAsync on `stream` and frees it there.
+ * Returns FA_OK, FA_ERR_INVALID_ARG or FA_ERR_UNSUPPORTED (d not 64, 128,
+ * 256; more than 32 heads per KV head), FA_ERR_HIP. */
+int fa_decode(const void* q, const void* k_cache, const void* v_cache,
+              const int* lens, void* o, float* lse, const float* sinks, int B,
+              int H, int Hkv, int S, int d, float scale, int window,
+              float softcap, hipStream_t stream);
+
+/* The chunking fa_decode uses for these sizes (host only): nsplit chunks of
+ * `chunk` keys (a multiple of 32) over the visible range of each sequence. */
+int fa_decode_splits(int B, int Hkv, int S, int window, int* nsplit,
+                     int* chunk);
+
 /* RoPE on interleaved pairs (x[2i], x[2i+1]) at positions t = 0..T-1 with
  * angle fl32(t * inv_freq[i]) (Forge README: interleaved pairs; Forge
  * attention.h commit log, "Wave 1": kernels read a host-precomputed
