@@ -79,13 +79,15 @@ def cpu_baseline(w, budget_s, seed=0):
                       f"host affinity {len(os.sched_getaffinity(0))} cpus"}
 
 
-def kernel_flops_per_pair(kind, d):
-    """Algorithmic MFMA flops per visible (q, k) pair of one kernel launch."""
-    return {"fwd": 4 * d,            # S = QK^T, O += PV
-            "bwd_dq": 6 * d,         # S, dP = dO V^T, dQ += dS K
-            "bwd_dkdv": 8 * d,       # S, dP, dV += P^T dO, dK += dS^T Q
-            "bwd_dv": 4 * d,         # S, dV
-            "bwd_dk": 6 * d}[kind]   # S, dP, dK
+def kernel_flops_per_pair(kind, d, dv=None):
+    """Algorithmic MFMA flops per visible (q, k) pair of one kernel launch
+    (d: query/key head size, dv: value head size)."""
+    dv = d if dv is None else dv
+    return {"fwd": 2 * d + 2 * dv,              # S = QK^T, O += PV
+            "bwd_dq": 4 * d + 2 * dv,           # S, dP = dO V^T, dQ += dS K
+            "bwd_dkdv": 4 * d + 4 * dv,         # S, dP, dV += P^T dO, dK += dS^T Q
+            "bwd_dv": 2 * d + 2 * dv,           # S, dV
+            "bwd_dk": 4 * d + 2 * dv}[kind]     # S, dP, dK
 
 
 def traffic_for(workload, kernel, src_hash):
@@ -188,7 +190,8 @@ def main():
     B, H, Hkv, T, d = w.B, w.H, w.Hkv, w.T, w.d
     log(f"[bench] workload {w.name}: B{B} H{H}/{Hkv} T{T} d{d} W{w.window} cap{w.softcap}")
     q, k, v, do = (t.to(dev) for t in synth.draw(w))
-    o = torch.empty_like(q)
+    o = torch.empty_like(do)
+    dvh = w.dv
     lse = torch.empty((B, H, T), dtype=torch.float32, device=dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     rope = bool(w.rope_theta)
@@ -216,11 +219,19 @@ def main():
             if ev: fa.fa_set_stage_events([ev["rk"][0].cuda_event, ev["rk"][1].cuda_event])
             fa.rope_apply(k, kr, tab, B, Hkv, T, d, sh)
         if ev: fa.fa_set_stage_events([e.cuda_event for e in ev["fwd"]])
-        fa.fa_fwd(qr, kr, v, o, lse, B, H, Hkv, T, d, w.scale, w.window, w.global_every,
-                  w.softcap, sh)
+        if dvh == d:
+            fa.fa_fwd(qr, kr, v, o, lse, B, H, Hkv, T, d, w.scale, w.window, w.global_every,
+                      w.softcap, sh)
+        else:
+            fa.fa_fwd_vdim(qr, kr, v, o, lse, B, H, Hkv, T, d, dvh, w.scale, w.window,
+                           w.global_every, w.softcap, sh)
         if ev: fa.fa_set_stage_events([e.cuda_event for e in ev["bwd"]])
-        fa.fa_bwd(qr, kr, v, o, lse, do, dq, dk, dv, B, H, Hkv, T, d, w.scale, w.window,
-                  w.global_every, w.softcap, sh)
+        if dvh == d:
+            fa.fa_bwd(qr, kr, v, o, lse, do, dq, dk, dv, B, H, Hkv, T, d, w.scale, w.window,
+                      w.global_every, w.softcap, sh)
+        else:
+            fa.fa_bwd_vdim(qr, kr, v, o, lse, do, dq, dk, dv, B, H, Hkv, T, d, dvh, w.scale,
+                           w.window, w.global_every, w.softcap, sh)
         if ev: fa.fa_set_stage_events([])
         if rope:
             fa.rope_apply_bwd(dq, dqi, tab, B, H, T, d, sh)
@@ -264,7 +275,7 @@ def main():
 
     # dominant kernel by time, priced at its own algorithmic flops
     dom = max(["fwd"] + bwd_names, key=lambda n: kern[n])
-    dom_flops = kernel_flops_per_pair(dom, d) * pairs_total
+    dom_flops = kernel_flops_per_pair(dom, d, dvh) * pairs_total
     achieved = dom_flops / (kern[dom] * 1e-3) / 1e12
     src_hash = kernel_sources_hash()
     roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1),
@@ -301,7 +312,7 @@ def main():
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
            "dtype": "bf16", "data": "synthetic",
-           "config": {"workload": w.name, "B": B, "H": H, "Hkv": Hkv, "T": T, "d": d,
+           "config": {"workload": w.name, "B": B, "H": H, "Hkv": Hkv, "T": T, "d": d, "d_v": dvh,
                       "window": w.window, "softcap": w.softcap,
                       "global_every": w.global_every, "rope_theta": w.rope_theta,
                       "visible_pairs_per_head": w.visible_pairs(),

@@ -67,7 +67,9 @@ __device__ __forceinline__ void atomic_max_f32(float* addr, float v) {
 
 // ---------------------------------------------------------------- LDS tiles
 // A tile of ROWS x D bf16 lives in LDS in rows of D*2 + 64 bytes (stride
-// = 16 mod 64 dwords), with the 16-byte chunks of each aligned 64-byte
+// = 16 mod 64 dwords for d = 128, 256; 48 = -16 mod 64 for d = 64, 192:
+// four consecutive rows start at the same four 16-dword bank offsets, in
+// another order), with the 16-byte chunks of each aligned 64-byte
 // group permuted by XOR with (row >> 2) & 3.  Measured on gfx950 (64 banks,
 // 16 lanes per cycle for 16-byte reads, 32 lanes for the 8-byte transpose
 // reads), this is conflict-free for both read patterns used here:
@@ -101,14 +103,19 @@ template <int D, int ROWS, int NTHREADS>
 struct TileStage {
   static constexpr int CPR = D / 8;
   static constexpr int CHUNKS = ROWS * CPR;
-  static_assert(CHUNKS % NTHREADS == 0, "tile not a multiple of the workgroup");
-  static constexpr int ROUNDS = CHUNKS / NTHREADS;
+  static constexpr int ROUNDS = (CHUNKS + NTHREADS - 1) / NTHREADS;
+  // true when the last round has threads without a chunk
+  static constexpr bool RAGGED = CHUNKS % NTHREADS != 0;
   u32x4 r[ROUNDS];
 
+  __device__ __forceinline__ static bool has(int n, int tid) {
+    return !RAGGED || n + 1 < ROUNDS || (n * NTHREADS + tid) < CHUNKS;
+  }
   __device__ __forceinline__ void load(const bf16* gbase, int row0, int nrows, int tid) {
 #pragma unroll
     for (int n = 0; n < ROUNDS; ++n) {
       const int p = n * NTHREADS + tid;
+      if (!has(n, tid)) continue;
       const int rr = p / CPR;
       const int cc = p % CPR;
       int grow = row0 + rr;
@@ -120,6 +127,7 @@ struct TileStage {
 #pragma unroll
     for (int n = 0; n < ROUNDS; ++n) {
       const int p = n * NTHREADS + tid;
+      if (!has(n, tid)) continue;
       *(LDS_AS u32x4*)(lds + Lay<D>::off(p / CPR, (p % CPR) * 8)) = r[n];
     }
   }

@@ -69,14 +69,19 @@ bool overlap(const Range& a, const Range& b) {
 
 // Shared validation of the attention calls.  Returns FA_OK or an error.
 int check_attn(const char* fn, int B, int H, int Hkv, int T, int d, float scale, int window,
-               int global_every, float softcap) {
+               int global_every, float softcap, int d_v = -1) {
+  if (d_v < 0) d_v = d;
   const std::string f(fn);
   if (B <= 0 || H <= 0 || Hkv <= 0 || T <= 0)
     return fail(FA_ERR_INVALID_ARG, f + ": B, H, Hkv and T must be positive");
   if (H % Hkv != 0) return fail(FA_ERR_INVALID_ARG, f + ": H must be a multiple of Hkv");
   if (d <= 0 || d % 2 != 0) return fail(FA_ERR_INVALID_ARG, f + ": head size d must be even and positive");
-  if (d != 64 && d != 128 && d != 256)
+  if (d_v <= 0 || d_v % 2 != 0)
+    return fail(FA_ERR_INVALID_ARG, f + ": value head size d_v must be even and positive");
+  if (d_v == d && d != 64 && d != 128 && d != 256)
     return fail(FA_ERR_UNSUPPORTED, f + ": head size d must be 64, 128 or 256");
+  if (d_v != d && !(d == 192 && d_v == 128))
+    return fail(FA_ERR_UNSUPPORTED, f + ": (d, d_v) must be equal or (192, 128)");
   if (!(scale > 0.f) || !std::isfinite(scale))
     return fail(FA_ERR_INVALID_ARG, f + ": scale must be positive and finite");
   if (window < 0) return fail(FA_ERR_INVALID_ARG, f + ": window must be >= 0");
@@ -109,14 +114,16 @@ constexpr float kLog2e = 1.4426950408889634f;
 int attn_fwd(bool f32, const void* q, const void* k, const void* v, void* o, float* lse, int B,
              int H, int Hkv, int T, int d, float scale, int window, int global_every,
              float softcap, hipStream_t stream, const char* fn = nullptr,
-             const float* sinks = nullptr, float* max_logit = nullptr) {
+             const float* sinks = nullptr, float* max_logit = nullptr, int d_v = -1) {
   if (!fn) fn = f32 ? "fa_fwd_f32" : "fa_fwd";
-  int rc = check_attn(fn, B, H, Hkv, T, d, scale, window, global_every, softcap);
+  if (d_v < 0) d_v = d;
+  int rc = check_attn(fn, B, H, Hkv, T, d, scale, window, global_every, softcap, d_v);
   if (rc) return rc;
   const size_t es = f32 ? 4 : 2;
   const size_t nq = (size_t)B * H * T * d * es, nk = (size_t)B * Hkv * T * d * es;
-  const Range rs[] = {{"q", q, nq}, {"k", k, nk}, {"v", v, nk},
-                      {"o", o, nq}, {"lse", lse, (size_t)B * H * T * 4}};
+  const size_t nv = (size_t)B * Hkv * T * d_v * es, no = (size_t)B * H * T * d_v * es;
+  const Range rs[] = {{"q", q, nq}, {"k", k, nk}, {"v", v, nv},
+                      {"o", o, no}, {"lse", lse, (size_t)B * H * T * 4}};
   rc = check_ptrs(fn, rs, 5, 3);
   if (rc) return rc;
   if (max_logit) {
@@ -149,7 +156,7 @@ int attn_fwd(bool f32, const void* q, const void* k, const void* v, void* o, flo
     a.cap_log2e = softcap > 0.f ? softcap * kLog2e : 0.f;
     a.sinks = sinks;
     a.max_logit = max_logit;
-    e = fa::launch_fwd_bf16(a, d, stream);
+    e = fa::launch_fwd_bf16(a, d, d_v, stream);
   }
   return finish(e, stream, fn);
 }
@@ -158,16 +165,18 @@ int attn_bwd(bool f32, const void* q, const void* k, const void* v, const void* 
              const float* lse, const void* dO, void* dq, void* dk, void* dv, int B, int H,
              int Hkv, int T, int d, float scale, int window, int global_every, float softcap,
              hipStream_t stream, const char* fn = nullptr, const float* sinks = nullptr,
-             float* dsinks = nullptr) {
+             float* dsinks = nullptr, int d_v = -1) {
   if (!fn) fn = f32 ? "fa_bwd_f32" : "fa_bwd";
-  int rc = check_attn(fn, B, H, Hkv, T, d, scale, window, global_every, softcap);
+  if (d_v < 0) d_v = d;
+  int rc = check_attn(fn, B, H, Hkv, T, d, scale, window, global_every, softcap, d_v);
   if (rc) return rc;
   const size_t es = f32 ? 4 : 2;
   const size_t nq = (size_t)B * H * T * d * es, nk = (size_t)B * Hkv * T * d * es;
-  const Range rs[] = {{"q", q, nq},   {"k", k, nk},   {"v", v, nk},
-                      {"o", o, nq},   {"lse", lse, (size_t)B * H * T * 4},
-                      {"dO", dO, nq}, {"dq", dq, nq}, {"dk", dk, nk},
-                      {"dv", dv, nk}};
+  const size_t nv = (size_t)B * Hkv * T * d_v * es, no = (size_t)B * H * T * d_v * es;
+  const Range rs[] = {{"q", q, nq},   {"k", k, nk},   {"v", v, nv},
+                      {"o", o, no},   {"lse", lse, (size_t)B * H * T * 4},
+                      {"dO", dO, no}, {"dq", dq, nq}, {"dk", dk, nk},
+                      {"dv", dv, nv}};
   rc = check_ptrs(fn, rs, 9, 6);
   if (rc) return rc;
   if ((sinks == nullptr) != (dsinks == nullptr))
@@ -214,7 +223,7 @@ int attn_bwd(bool f32, const void* q, const void* k, const void* v, const void* 
     a.inv_cap = softcap > 0.f ? 1.f / softcap : 0.f;
     a.sinks = sinks;
     a.dsinks = dsinks;
-    e = fa::launch_bwd_bf16(a, d, stream);
+    e = fa::launch_bwd_bf16(a, d, d_v, stream);
   }
   const hipError_t e2 = hipFreeAsync(Dst, stream);
   if (e == hipSuccess) e = e2;
@@ -361,6 +370,21 @@ int fa_decode_splits(int B, int Hkv, int S, int window, int* nsplit, int* chunk)
     return fail(FA_ERR_INVALID_ARG, "fa_decode_splits: invalid arguments");
   decode_split(B * Hkv, window > 0 ? std::min(window, S) : S, nsplit, chunk);
   return FA_OK;
+}
+
+int fa_fwd_vdim(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                int Hkv, int T, int d, int d_v, float scale, int window, int global_every,
+                float softcap, hipStream_t stream) {
+  return attn_fwd(false, q, k, v, o, lse, B, H, Hkv, T, d, scale, window, global_every, softcap,
+                  stream, "fa_fwd_vdim", nullptr, nullptr, d_v);
+}
+
+int fa_bwd_vdim(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                const void* dO, void* dq, void* dk, void* dv, int B, int H, int Hkv, int T, int d,
+                int d_v, float scale, int window, int global_every, float softcap,
+                hipStream_t stream) {
+  return attn_bwd(false, q, k, v, o, lse, dO, dq, dk, dv, B, H, Hkv, T, d, scale, window,
+                  global_every, softcap, stream, "fa_bwd_vdim", nullptr, nullptr, d_v);
 }
 
 int rope_apply(const void* x, void* y, const float* inv_freq, int B, int H, int T, int d,

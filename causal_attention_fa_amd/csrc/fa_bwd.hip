@@ -40,14 +40,15 @@ __device__ __forceinline__ float score_log2(float x, const BwdArgs& a, float& th
 }
 
 // ------------------------------------------------------------------ dQ pass
-template <int D, int BKV, int NW, bool CAP>
-__global__ __launch_bounds__(64 * NW, (D >= 256 ? 1 : 8 / NW)) void fa_bwd_dq_kernel(BwdArgs a) {
+template <int DK, int DV, int BKV, int NW, bool CAP>
+__global__ __launch_bounds__(64 * NW, (DK >= 192 ? 1 : 8 / NW)) void fa_bwd_dq_kernel(BwdArgs a) {
   constexpr int NT = 64 * NW;
   constexpr int BQ = 32 * NW;
-  constexpr int TILE = Lay<D>::template bytes<BKV>();
-  constexpr int NDB = D / 32;
+  constexpr int TILE_K = Lay<DK>::template bytes<BKV>();
+  constexpr int TILE_V = Lay<DV>::template bytes<BKV>();
+  constexpr int NDB = DK / 32;   // 32-wide blocks of dq
   constexpr int NS = BKV / 32;
-  __shared__ __attribute__((aligned(1024))) char smem[4 * TILE];
+  __shared__ __attribute__((aligned(1024))) char smem[2 * TILE_K + 2 * TILE_V];
   LDS_AS char* lds = (LDS_AS char*)smem;
 
   const int tid = threadIdx.x;
@@ -67,21 +68,22 @@ __global__ __launch_bounds__(64 * NW, (D >= 256 ? 1 : 8 / NW)) void fa_bwd_dq_ke
   const int qr = qrow < T ? qrow : T - 1;
   const size_t bh = (size_t)w.b * a.H + h;
   const size_t bkv = (size_t)w.b * a.Hkv + w.hkv;
-  const bf16* Kp = a.k + bkv * T * D;
-  const bf16* Vp = a.v + bkv * T * D;
+  const bf16* Kp = a.k + bkv * T * DK;
+  const bf16* Vp = a.v + bkv * T * DV;
 
   // Q and dO rows as B operands (lane = query row), D_i, lse in log2.
-  bf16x8 qreg[D / 16], doreg[D / 16];
+  bf16x8 qreg[DK / 16], doreg[DV / 16];
   float Di;
   {
-    const size_t roff = (bh * T + qr) * D + 8 * g;
-    const bf16x8* qs = (const bf16x8*)(a.q + roff);
-    const bf16x8* ds = (const bf16x8*)(a.dO + roff);
-    const bf16x8* os = (const bf16x8*)(a.o + roff);
+    const bf16x8* qs = (const bf16x8*)(a.q + (bh * T + qr) * DK + 8 * g);
+    const size_t voff = (bh * T + qr) * DV + 8 * g;
+    const bf16x8* ds = (const bf16x8*)(a.dO + voff);
+    const bf16x8* os = (const bf16x8*)(a.o + voff);
     float part = 0.f;
 #pragma unroll
-    for (int c = 0; c < D / 16; ++c) {
-      qreg[c] = qs[2 * c];
+    for (int c = 0; c < DK / 16; ++c) qreg[c] = qs[2 * c];
+#pragma unroll
+    for (int c = 0; c < DV / 16; ++c) {
       doreg[c] = ds[2 * c];
       const bf16x8 ov = os[2 * c];
 #pragma unroll
@@ -112,18 +114,20 @@ __global__ __launch_bounds__(64 * NW, (D >= 256 ? 1 : 8 / NW)) void fa_bwd_dq_ke
 #pragma unroll
     for (int i = 0; i < 16; ++i) dqacc[db][i] = 0.f;
 
-  TileStage<D, BKV, NT> kst, vst;
+  TileStage<DK, BKV, NT> kst;
+  TileStage<DV, BKV, NT> vst;
+  LDS_AS char* const vlds = lds + 2 * TILE_K;
   kst.load(Kp, t_lo * BKV, T, tid);
   vst.load(Vp, t_lo * BKV, T, tid);
   kst.store(lds, tid);
-  vst.store(lds + 2 * TILE, tid);
+  vst.store(vlds, tid);
   __syncthreads();
 
   const int qa = qw0, qb = qw0 + 31;
   for (int j = 0; j < ntiles; ++j) {
     const int cur = j & 1;
-    const LDS_AS char* Kt = lds + cur * TILE;
-    const LDS_AS char* Vt = lds + (2 + cur) * TILE;
+    const LDS_AS char* Kt = lds + cur * TILE_K;
+    const LDS_AS char* Vt = vlds + cur * TILE_V;
     const bool more = j + 1 < ntiles;
     const int nrow = (t_lo + j + 1) * BKV;
     // next K, V tiles: loads now, LDS stores after this tile's MFMAs
@@ -136,8 +140,8 @@ __global__ __launch_bounds__(64 * NW, (D >= 256 ? 1 : 8 / NW)) void fa_bwd_dq_ke
     const bool full = kv0 + BKV - 1 <= qa && (W == 0 || kv0 > qb - W);
     f32x16 s[NS], dp[NS];
     if (!empty) {
-      mma_rows<D, NS>(s, Kt, qreg, lane);
-      mma_rows<D, NS>(dp, Vt, doreg, lane);
+      mma_rows<DK, NS>(s, Kt, qreg, lane);
+      mma_rows<DV, NS>(dp, Vt, doreg, lane);
     }
     if (!empty) {
       // dS^T in s[] (fp32), then bf16 operands.
@@ -173,17 +177,17 @@ __global__ __launch_bounds__(64 * NW, (D >= 256 ? 1 : 8 / NW)) void fa_bwd_dq_ke
       for (int c16 = 0; c16 < BKV / 16; ++c16)
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
-          dqacc[db] = mfma32(lds_tr_operand<D>(Kt, 0, c16, 32 * db, lane), dsb[c16], dqacc[db]);
+          dqacc[db] = mfma32(lds_tr_operand<DK>(Kt, 0, c16, 32 * db, lane), dsb[c16], dqacc[db]);
     }
     if (more) {
-      kst.store(lds + (cur ^ 1) * TILE, tid);
-      vst.store(lds + (2 + (cur ^ 1)) * TILE, tid);
+      kst.store(lds + (cur ^ 1) * TILE_K, tid);
+      vst.store(vlds + (cur ^ 1) * TILE_V, tid);
     }
     __syncthreads();
   }
 
   if (qrow < T) {
-    bf16* Qd = a.dq + (bh * T + qrow) * D;
+    bf16* Qd = a.dq + (bh * T + qrow) * DK;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -202,19 +206,22 @@ __global__ __launch_bounds__(64 * NW, (D >= 256 ? 1 : 8 / NW)) void fa_bwd_dq_ke
 // that two waves per SIMD allow, so the pass runs as two launches instead:
 // MODE 1 accumulates dV only (needs S, P), MODE 2 dK only (needs S, dP,
 // dS) -- one extra S = Q K^T product buys twice the occupancy.
-template <int D, int BQB, int NW, bool CAP, int MODE>
-__global__ __launch_bounds__(64 * NW, (D >= 256 ? 1 : 8 / NW)) void fa_bwd_dkdv_kernel(BwdArgs a) {
+template <int DK, int DV, int BQB, int NW, bool CAP, int MODE>
+__global__ __launch_bounds__(64 * NW, (DK >= 192 ? 1 : 8 / NW)) void fa_bwd_dkdv_kernel(BwdArgs a) {
   constexpr bool DO_DV = MODE != 2;
   constexpr bool DO_DK = MODE != 1;
   constexpr int NT = 64 * NW;
   constexpr int BKVB = 32 * NW;        // key rows per workgroup
-  constexpr int TILE = Lay<D>::template bytes<BQB>();  // one Q or dO tile
-  constexpr int NDB = D / 32;
+  constexpr int TILE_Q = Lay<DK>::template bytes<BQB>();  // one Q tile
+  constexpr int TILE_O = Lay<DV>::template bytes<BQB>();  // one dO tile
+  constexpr int NDBK = DK / 32;        // 32-wide blocks of dk
+  constexpr int NDBV = DV / 32;        // 32-wide blocks of dv
   constexpr int NS = BQB / 32;         // 32-query sub-tiles
   constexpr int STAT = BQB * 4;        // bytes of one lse or D tile
-  __shared__ __attribute__((aligned(1024))) char smem[4 * TILE + 4 * STAT];
+  __shared__ __attribute__((aligned(1024))) char smem[2 * TILE_Q + 2 * TILE_O + 4 * STAT];
   LDS_AS char* lds = (LDS_AS char*)smem;
-  LDS_AS char* stat = lds + 4 * TILE;  // [buf][lse2 | D][BQB] fp32
+  LDS_AS char* const olds = lds + 2 * TILE_Q;
+  LDS_AS char* stat = olds + 2 * TILE_O;  // [buf][lse2 | D][BQB] fp32
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -232,15 +239,15 @@ __global__ __launch_bounds__(64 * NW, (D >= 256 ? 1 : 8 / NW)) void fa_bwd_dkdv_
   const int kr = krow < T ? krow : T - 1;
   const size_t bkv = (size_t)w.b * a.Hkv + w.hkv;
 
-  bf16x8 kreg[D / 16], vreg[D / 16];
+  bf16x8 kreg[DK / 16], vreg[DV / 16];
   {
-    const size_t roff = (bkv * T + kr) * D + 8 * g;
-    const bf16x8* ks = (const bf16x8*)(a.k + roff);
-    const bf16x8* vs = (const bf16x8*)(a.v + roff);
+    const bf16x8* ks = (const bf16x8*)(a.k + (bkv * T + kr) * DK + 8 * g);
+    const bf16x8* vs = (const bf16x8*)(a.v + (bkv * T + kr) * DV + 8 * g);
 #pragma unroll
-    for (int c = 0; c < D / 16; ++c) {
-      kreg[c] = ks[2 * c];
-      if (DO_DK) vreg[c] = vs[2 * c];
+    for (int c = 0; c < DK / 16; ++c) kreg[c] = ks[2 * c];
+    if (DO_DK) {
+#pragma unroll
+      for (int c = 0; c < DV / 16; ++c) vreg[c] = vs[2 * c];
     }
   }
 
@@ -250,16 +257,17 @@ __global__ __launch_bounds__(64 * NW, (D >= 256 ? 1 : 8 / NW)) void fa_bwd_dkdv_
   const int nqt = (q_hi + BQB - 1) / BQB - qt_lo;
   const int niter = G * nqt;
 
-  f32x16 dkacc[NDB], dvacc[NDB];
+  f32x16 dkacc[DO_DK ? NDBK : 1], dvacc[DO_DV ? NDBV : 1];
 #pragma unroll
-  for (int db = 0; db < NDB; ++db)
+  for (int i = 0; i < 16; ++i) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      dkacc[db][i] = 0.f;
-      dvacc[db][i] = 0.f;
-    }
+    for (int db = 0; db < (DO_DK ? NDBK : 1); ++db) dkacc[db][i] = 0.f;
+#pragma unroll
+    for (int db = 0; db < (DO_DV ? NDBV : 1); ++db) dvacc[db][i] = 0.f;
+  }
 
-  TileStage<D, BQB, NT> qst, dost;
+  TileStage<DK, BQB, NT> qst;
+  TileStage<DV, BQB, NT> dost;
   float stv = 0.f;
   auto stage_stats = [&](int it) {
     const int hh = w.hkv * G + it / nqt;
@@ -271,32 +279,32 @@ __global__ __launch_bounds__(64 * NW, (D >= 256 ? 1 : 8 / NW)) void fa_bwd_dkdv_
       stv = tid < BQB ? a.lse[bhh * T + qq] * kLog2e : a.Dst[bhh * T + qq];
     }
   };
-  auto tile_src = [&](int it, const bf16* base) {
+  auto tile_src = [&](int it, const bf16* base, int dd) {
     const int hh = w.hkv * G + it / nqt;
-    return base + ((size_t)w.b * a.H + hh) * T * D;
+    return base + ((size_t)w.b * a.H + hh) * T * dd;
   };
   auto tile_q0 = [&](int it) { return (qt_lo + it % nqt) * BQB; };
 
-  qst.load(tile_src(0, a.q), tile_q0(0), T, tid);
-  dost.load(tile_src(0, a.dO), tile_q0(0), T, tid);
+  qst.load(tile_src(0, a.q, DK), tile_q0(0), T, tid);
+  dost.load(tile_src(0, a.dO, DV), tile_q0(0), T, tid);
   stage_stats(0);
   qst.store(lds, tid);
-  dost.store(lds + 2 * TILE, tid);
+  dost.store(olds, tid);
   if (tid < 2 * BQB) *(LDS_AS float*)(stat + tid * 4) = stv;
   __syncthreads();
 
   const int ka = kw0, kb = kw0 + 31;
   for (int it = 0; it < niter; ++it) {
     const int cur = it & 1;
-    const LDS_AS char* Qt = lds + cur * TILE;
-    const LDS_AS char* dOt = lds + (2 + cur) * TILE;
+    const LDS_AS char* Qt = lds + cur * TILE_Q;
+    const LDS_AS char* dOt = olds + cur * TILE_O;
     const LDS_AS float* lse2t = (const LDS_AS float*)(stat + cur * 2 * STAT);
     const LDS_AS float* Dt = lse2t + BQB;
     const bool more = it + 1 < niter;
     // next Q, dO tiles and row statistics: loads now, LDS stores at the end
     if (more) {
-      qst.load(tile_src(it + 1, a.q), tile_q0(it + 1), T, tid);
-      dost.load(tile_src(it + 1, a.dO), tile_q0(it + 1), T, tid);
+      qst.load(tile_src(it + 1, a.q, DK), tile_q0(it + 1), T, tid);
+      dost.load(tile_src(it + 1, a.dO, DV), tile_q0(it + 1), T, tid);
       stage_stats(it + 1);
     }
     const int q0 = tile_q0(it);
@@ -304,8 +312,8 @@ __global__ __launch_bounds__(64 * NW, (D >= 256 ? 1 : 8 / NW)) void fa_bwd_dkdv_
     const bool full = q0 >= kb && q0 + BQB <= T && (W == 0 || q0 + BQB - 1 - ka < W);
     f32x16 s[NS], dp[NS];
     if (!empty) {
-      mma_rows<D, NS>(s, Qt, kreg, lane);
-      if (DO_DK) mma_rows<D, NS>(dp, dOt, vreg, lane);
+      mma_rows<DK, NS>(s, Qt, kreg, lane);
+      if (DO_DK) mma_rows<DV, NS>(dp, dOt, vreg, lane);
     }
     if (!empty) {
       // S, dP: lane = key row, accumulator i = query row 32t + acc_row(i, g).
@@ -353,40 +361,52 @@ __global__ __launch_bounds__(64 * NW, (D >= 256 ? 1 : 8 / NW)) void fa_bwd_dkdv_
         if (DO_DK) dsb[c16] = pack_bf16(td);
       }
 #pragma unroll
-      for (int c16 = 0; c16 < BQB / 16; ++c16)
+      for (int c16 = 0; c16 < BQB / 16; ++c16) {
+        if (DO_DV) {
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          if (DO_DV)
-            dvacc[db] = mfma32(lds_tr_operand<D>(dOt, 0, c16, 32 * db, lane), pb[c16], dvacc[db]);
-          if (DO_DK)
-            dkacc[db] = mfma32(lds_tr_operand<D>(Qt, 0, c16, 32 * db, lane), dsb[c16], dkacc[db]);
+          for (int db = 0; db < NDBV; ++db)
+            dvacc[db] = mfma32(lds_tr_operand<DV>(dOt, 0, c16, 32 * db, lane), pb[c16], dvacc[db]);
         }
+        if (DO_DK) {
+#pragma unroll
+          for (int db = 0; db < NDBK; ++db)
+            dkacc[db] = mfma32(lds_tr_operand<DK>(Qt, 0, c16, 32 * db, lane), dsb[c16], dkacc[db]);
+        }
+      }
     }
     if (more) {
-      qst.store(lds + (cur ^ 1) * TILE, tid);
-      dost.store(lds + (2 + (cur ^ 1)) * TILE, tid);
+      qst.store(lds + (cur ^ 1) * TILE_Q, tid);
+      dost.store(olds + (cur ^ 1) * TILE_O, tid);
       if (tid < 2 * BQB) *(LDS_AS float*)(stat + (cur ^ 1) * 2 * STAT + tid * 4) = stv;
     }
     __syncthreads();
   }
 
   if (krow < T) {
-    const size_t roff = (bkv * T + krow) * D;
-    bf16* Kd = a.dk + roff;
-    bf16* Vd = a.dv + roff;
+    if (DO_DK) {
+      bf16* Kd = a.dk + (bkv * T + krow) * DK;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+      for (int db = 0; db < NDBK; ++db)
 #pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        bf16x4 kv4, vv4;
+        for (int i4 = 0; i4 < 4; ++i4) {
+          bf16x4 kv4;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          kv4[e] = (bf16)(dkacc[db][4 * i4 + e] * a.scale);
-          vv4[e] = (bf16)dvacc[db][4 * i4 + e];
+          for (int e = 0; e < 4; ++e) kv4[e] = (bf16)(dkacc[db][4 * i4 + e] * a.scale);
+          *(bf16x4*)(Kd + 32 * db + 8 * i4 + 4 * g) = kv4;
         }
-        if (DO_DK) *(bf16x4*)(Kd + 32 * db + 8 * i4 + 4 * g) = kv4;
-        if (DO_DV) *(bf16x4*)(Vd + 32 * db + 8 * i4 + 4 * g) = vv4;
-      }
+    }
+    if (DO_DV) {
+      bf16* Vd = a.dv + (bkv * T + krow) * DV;
+#pragma unroll
+      for (int db = 0; db < NDBV; ++db)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          bf16x4 vv4;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) vv4[e] = (bf16)dvacc[db][4 * i4 + e];
+          *(bf16x4*)(Vd + 32 * db + 8 * i4 + 4 * g) = vv4;
+        }
+    }
   }
 }
 
@@ -403,40 +423,48 @@ __global__ __launch_bounds__(64 * NW, (D >= 256 ? 1 : 8 / NW)) void fa_bwd_dkdv_
 #ifndef BWD128_CFG
 #define BWD128_CFG 32, 8, 64, 8, 32, 8
 #endif
+#ifndef BWD192_CFG
+#define BWD192_CFG 32, 4, 64, 8, 32, 4
+#endif
 
-template <int D, bool CAP, int DQ_BKV, int DQ_NW, int DV_BQB, int DV_NW, int DK_BQB, int DK_NW>
+template <int DK, int DV, bool CAP, int DQ_BKV, int DQ_NW, int DV_BQB, int DV_NW, int DK_BQB,
+          int DK_NW>
 static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   const int nqb = (a.T + 32 * DQ_NW - 1) / (32 * DQ_NW);
-  hipLaunchKernelGGL((fa_bwd_dq_kernel<D, DQ_BKV, DQ_NW, CAP>), dim3((unsigned)nqb * a.B * a.H),
+  hipLaunchKernelGGL((fa_bwd_dq_kernel<DK, DV, DQ_BKV, DQ_NW, CAP>), dim3((unsigned)nqb * a.B * a.H),
                      dim3(64 * DQ_NW), 0, stream, a);
   stage_mark(stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 vgrid((unsigned)((a.T + 32 * DV_NW - 1) / (32 * DV_NW)) * a.B * a.Hkv);
-  hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, DV_BQB, DV_NW, CAP, 1>), vgrid, dim3(64 * DV_NW), 0,
+  hipLaunchKernelGGL((fa_bwd_dkdv_kernel<DK, DV, DV_BQB, DV_NW, CAP, 1>), vgrid, dim3(64 * DV_NW), 0,
                      stream, a);
   stage_mark(stream);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 kgrid((unsigned)((a.T + 32 * DK_NW - 1) / (32 * DK_NW)) * a.B * a.Hkv);
-  hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, DK_BQB, DK_NW, CAP, 2>), kgrid, dim3(64 * DK_NW), 0,
+  hipLaunchKernelGGL((fa_bwd_dkdv_kernel<DK, DV, DK_BQB, DK_NW, CAP, 2>), kgrid, dim3(64 * DK_NW), 0,
                      stream, a);
   stage_mark(stream);
   return hipGetLastError();
 }
 
-template <int D, int DQ_BKV, int DQ_NW, int DV_BQB, int DV_NW, int DK_BQB, int DK_NW>
+template <int DK, int DV, int DQ_BKV, int DQ_NW, int DV_BQB, int DV_NW, int DK_BQB, int DK_NW>
 static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
   if (a.cap_log2e > 0.f)
-    return launch_bwd_t<D, true, DQ_BKV, DQ_NW, DV_BQB, DV_NW, DK_BQB, DK_NW>(a, stream);
-  return launch_bwd_t<D, false, DQ_BKV, DQ_NW, DV_BQB, DV_NW, DK_BQB, DK_NW>(a, stream);
+    return launch_bwd_t<DK, DV, true, DQ_BKV, DQ_NW, DV_BQB, DV_NW, DK_BQB, DK_NW>(a, stream);
+  return launch_bwd_t<DK, DV, false, DQ_BKV, DQ_NW, DV_BQB, DV_NW, DK_BQB, DK_NW>(a, stream);
 }
 
-hipError_t launch_bwd_bf16(const BwdArgs& a, int d, hipStream_t stream) {
-  switch (d) {
-    case 64: return launch_bwd_d<64, BWD64_CFG>(a, stream);
-    case 128: return launch_bwd_d<128, BWD128_CFG>(a, stream);
-    case 256: return launch_bwd_d<256, BWD256_CFG>(a, stream);
+hipError_t launch_bwd_bf16(const BwdArgs& a, int d, int d_v, hipStream_t stream) {
+  if (d == d_v) {
+    switch (d) {
+      case 64: return launch_bwd_d<64, 64, BWD64_CFG>(a, stream);
+      case 128: return launch_bwd_d<128, 128, BWD128_CFG>(a, stream);
+      case 256: return launch_bwd_d<256, 256, BWD256_CFG>(a, stream);
+    }
+  } else if (d == 192 && d_v == 128) {
+    return launch_bwd_d<192, 128, BWD192_CFG>(a, stream);
   }
   return hipErrorInvalidValue;
 }

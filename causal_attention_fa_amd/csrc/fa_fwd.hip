@@ -26,18 +26,20 @@
 namespace fa {
 
 // QW query blocks of 32 rows per wave: each K or V operand read from LDS
-// feeds QW MFMAs, dividing the LDS traffic per flop by QW.
-template <int D, int BKV, int NW, int QW, bool CAP>
-__global__ __launch_bounds__(64 * NW, (D >= 256 || QW > 1 ? 1 : 8 / NW)) void fa_fwd_kernel(
+// feeds QW MFMAs, dividing the LDS traffic per flop by QW.  DK is the head
+// size of q and k, DV that of v and o (equal except for MLA-style heads).
+template <int DK, int DV, int BKV, int NW, int QW, bool CAP>
+__global__ __launch_bounds__(64 * NW, (DK >= 256 || QW > 1 ? 1 : 8 / NW)) void fa_fwd_kernel(
     FwdArgs a) {
   constexpr int NT = 64 * NW;         // threads per workgroup
   constexpr int RW = 32 * QW;         // query rows per wave
   constexpr int BQ = RW * NW;         // query rows per workgroup
-  constexpr int TILE = Lay<D>::template bytes<BKV>();  // one K or V tile
-  constexpr int NDB = D / 32;         // 32-wide d blocks of the output
+  constexpr int TILE_K = Lay<DK>::template bytes<BKV>();  // one K tile
+  constexpr int TILE_V = Lay<DV>::template bytes<BKV>();  // one V tile
+  constexpr int NDB = DV / 32;        // 32-wide blocks of the output
   constexpr int NS = BKV / 32;        // 32-key sub-tiles
-  constexpr int NC = D / 16;          // 16-wide d chunks (MFMA k steps)
-  __shared__ __attribute__((aligned(1024))) char smem[4 * TILE];
+  constexpr int NC = DK / 16;         // 16-wide chunks of the q.k contraction
+  __shared__ __attribute__((aligned(1024))) char smem[2 * TILE_K + 2 * TILE_V];
   LDS_AS char* lds = (LDS_AS char*)smem;
 
   const int tid = threadIdx.x;
@@ -55,8 +57,8 @@ __global__ __launch_bounds__(64 * NW, (D >= 256 || QW > 1 ? 1 : 8 / NW)) void fa
   const int qw0 = q0 + RW * wave;
   const size_t bh = (size_t)w.b * a.H + h;
   const size_t bkv = (size_t)w.b * a.Hkv + w.hkv;
-  const bf16* Kp = a.k + bkv * T * D;
-  const bf16* Vp = a.v + bkv * T * D;
+  const bf16* Kp = a.k + bkv * T * DK;
+  const bf16* Vp = a.v + bkv * T * DV;
 
   // Q as the B operand of S^T = K Q^T: lane holds Q[qrow][16c + 8g .. +7]
   // of its row in each of the wave's QW blocks.
@@ -64,7 +66,7 @@ __global__ __launch_bounds__(64 * NW, (D >= 256 || QW > 1 ? 1 : 8 / NW)) void fa
 #pragma unroll
   for (int u = 0; u < QW; ++u) {
     const int qr = min(qw0 + 32 * u + l32, T - 1);
-    const bf16x8* src = (const bf16x8*)(a.q + (bh * T + qr) * D + 8 * g);
+    const bf16x8* src = (const bf16x8*)(a.q + (bh * T + qr) * DK + 8 * g);
 #pragma unroll
     for (int c = 0; c < NC; ++c) qreg[u][c] = src[2 * c];
   }
@@ -93,18 +95,20 @@ __global__ __launch_bounds__(64 * NW, (D >= 256 || QW > 1 ? 1 : 8 / NW)) void fa
       for (int i = 0; i < 16; ++i) oacc[u][db][i] = 0.f;
   }
 
-  TileStage<D, BKV, NT> kst, vst;
+  TileStage<DK, BKV, NT> kst;
+  TileStage<DV, BKV, NT> vst;
+  LDS_AS char* const vlds = lds + 2 * TILE_K;
   kst.load(Kp, t_lo * BKV, T, tid);
   vst.load(Vp, t_lo * BKV, T, tid);
   kst.store(lds, tid);
-  vst.store(lds + 2 * TILE, tid);
+  vst.store(vlds, tid);
   __syncthreads();
 
   const int qa = qw0, qb = qw0 + RW - 1;
   for (int j = 0; j < ntiles; ++j) {
     const int cur = j & 1;
-    const LDS_AS char* Kt = lds + cur * TILE;
-    const LDS_AS char* Vt = lds + (2 + cur) * TILE;
+    const LDS_AS char* Kt = lds + cur * TILE_K;
+    const LDS_AS char* Vt = vlds + cur * TILE_V;
     const bool more = j + 1 < ntiles;
     const int nrow = (t_lo + j + 1) * BKV;
     // Next K and V tiles: global loads issued now, written to the idle
@@ -125,7 +129,7 @@ __global__ __launch_bounds__(64 * NW, (D >= 256 || QW > 1 ? 1 : 8 / NW)) void fa
         bf16x8 op[2][NS];
 #pragma unroll
         for (int t = 0; t < NS; ++t) {
-          op[0][t] = lds_row_operand<D>(Kt, 32 * t, 0, lane);
+          op[0][t] = lds_row_operand<DK>(Kt, 32 * t, 0, lane);
 #pragma unroll
           for (int u = 0; u < QW; ++u)
 #pragma unroll
@@ -135,7 +139,7 @@ __global__ __launch_bounds__(64 * NW, (D >= 256 || QW > 1 ? 1 : 8 / NW)) void fa
         for (int c = 0; c < NC; ++c) {
           if (c + 1 < NC) {
 #pragma unroll
-            for (int t = 0; t < NS; ++t) op[(c + 1) & 1][t] = lds_row_operand<D>(Kt, 32 * t, c + 1, lane);
+            for (int t = 0; t < NS; ++t) op[(c + 1) & 1][t] = lds_row_operand<DK>(Kt, 32 * t, c + 1, lane);
           }
 #pragma unroll
           for (int t = 0; t < NS; ++t)
@@ -213,14 +217,14 @@ __global__ __launch_bounds__(64 * NW, (D >= 256 || QW > 1 ? 1 : 8 / NW)) void fa
       for (int c16 = 0; c16 < BKV / 16; ++c16)
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-          const bf16x8 vop = lds_tr_operand<D>(Vt, 0, c16, 32 * db, lane);
+          const bf16x8 vop = lds_tr_operand<DV>(Vt, 0, c16, 32 * db, lane);
 #pragma unroll
           for (int u = 0; u < QW; ++u) oacc[u][db] = mfma32(vop, pb[u][c16], oacc[u][db]);
         }
     }
     if (more) {
-      kst.store(lds + (cur ^ 1) * TILE, tid);
-      vst.store(lds + (2 + (cur ^ 1)) * TILE, tid);
+      kst.store(lds + (cur ^ 1) * TILE_K, tid);
+      vst.store(vlds + (cur ^ 1) * TILE_V, tid);
     }
     __syncthreads();
   }
@@ -240,7 +244,7 @@ __global__ __launch_bounds__(64 * NW, (D >= 256 || QW > 1 ? 1 : 8 / NW)) void fa
     const float ltot = xor32_sum(lsum[u]);
     if (qrow < T) {
       const float inv = 1.f / ltot;
-      bf16* Op = a.o + (bh * T + qrow) * D;
+      bf16* Op = a.o + (bh * T + qrow) * DV;
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -261,14 +265,18 @@ __global__ __launch_bounds__(64 * NW, (D >= 256 || QW > 1 ? 1 : 8 / NW)) void fa
 #define FWD128_CFG 64, 4, 1
 #endif
 
-template <int D, int BKV, int NW, int QW>
+#ifndef FWD192_CFG
+#define FWD192_CFG 32, 4, 1
+#endif
+
+template <int DK, int DV, int BKV, int NW, int QW>
 static hipError_t launch_fwd_d(const FwdArgs& a, hipStream_t stream) {
   const int nqb = (a.T + 32 * NW * QW - 1) / (32 * NW * QW);
   const dim3 grid((unsigned)nqb * a.B * a.H);
   if (a.cap_log2e > 0.f)
-    hipLaunchKernelGGL((fa_fwd_kernel<D, BKV, NW, QW, true>), grid, dim3(64 * NW), 0, stream, a);
+    hipLaunchKernelGGL((fa_fwd_kernel<DK, DV, BKV, NW, QW, true>), grid, dim3(64 * NW), 0, stream, a);
   else
-    hipLaunchKernelGGL((fa_fwd_kernel<D, BKV, NW, QW, false>), grid, dim3(64 * NW), 0, stream, a);
+    hipLaunchKernelGGL((fa_fwd_kernel<DK, DV, BKV, NW, QW, false>), grid, dim3(64 * NW), 0, stream, a);
   stage_mark(stream);
   return hipGetLastError();
 }
@@ -283,11 +291,15 @@ hipError_t launch_fill_f32(float* p, int n, float v, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_fwd_bf16(const FwdArgs& a, int d, hipStream_t stream) {
-  switch (d) {
-    case 64: return launch_fwd_d<64, 64, 4, 1>(a, stream);
-    case 128: return launch_fwd_d<128, FWD128_CFG>(a, stream);
-    case 256: return launch_fwd_d<256, 32, 4, 1>(a, stream);
+hipError_t launch_fwd_bf16(const FwdArgs& a, int d, int d_v, hipStream_t stream) {
+  if (d == d_v) {
+    switch (d) {
+      case 64: return launch_fwd_d<64, 64, 64, 4, 1>(a, stream);
+      case 128: return launch_fwd_d<128, 128, FWD128_CFG>(a, stream);
+      case 256: return launch_fwd_d<256, 256, 32, 4, 1>(a, stream);
+    }
+  } else if (d == 192 && d_v == 128) {
+    return launch_fwd_d<192, 128, FWD192_CFG>(a, stream);
   }
   return hipErrorInvalidValue;
 }

@@ -103,8 +103,10 @@ void stage_mark(hipStream_t stream);
 // Fills n floats with v (initialises accumulated outputs inside a call).
 hipError_t launch_fill_f32(float* p, int n, float v, hipStream_t stream);
 
-hipError_t launch_fwd_bf16(const FwdArgs& a, int d, hipStream_t stream);
-hipError_t launch_bwd_bf16(const BwdArgs& a, int d, hipStream_t stream);
+// d: head size of q and k; d_v: head size of v and o (pairs (x, x) for
+// x in {64, 128, 256} and (192, 128)).
+hipError_t launch_fwd_bf16(const FwdArgs& a, int d, int d_v, hipStream_t stream);
+hipError_t launch_bwd_bf16(const BwdArgs& a, int d, int d_v, hipStream_t stream);
 hipError_t launch_fwd_f32(const F32Args& a, hipStream_t stream);
 hipError_t launch_bwd_f32(const F32Args& a, hipStream_t stream);
 hipError_t launch_decode_bf16(const DecodeArgs& a, int d, bool cap, hipStream_t stream);

@@ -53,6 +53,11 @@ _lib.fa_fwd_sink.restype = _I
 _lib.fa_bwd_sink.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F,
                              _I, _I, _F, _P]
 _lib.fa_bwd_sink.restype = _I
+_lib.fa_fwd_vdim.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I, _F, _P]
+_lib.fa_fwd_vdim.restype = _I
+_lib.fa_bwd_vdim.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I,
+                             _I, _F, _P]
+_lib.fa_bwd_vdim.restype = _I
 _lib.fa_decode.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _F, _P]
 _lib.fa_decode.restype = _I
 _lib.fa_decode_splits.argtypes = [_I, _I, _I, _I, ctypes.POINTER(_I), ctypes.POINTER(_I)]
@@ -73,8 +78,9 @@ _lib.fa_set_stage_events.restype = _I
 _lib.fa_last_error.argtypes = []
 _lib.fa_last_error.restype = ctypes.c_char_p
 
-EXPORTS = ("fa_fwd", "fa_bwd", "fa_fwd_sink", "fa_bwd_sink", "fa_decode", "fa_decode_splits", "rope_apply", "rope_apply_bwd", "fa_fwd_f32", "fa_bwd_f32",
-           "rope_apply_f32", "rope_apply_bwd_f32", "fa_layer_window", "fa_rope_inv_freq",
+EXPORTS = ("fa_fwd", "fa_bwd", "fa_fwd_sink", "fa_bwd_sink", "fa_fwd_vdim", "fa_bwd_vdim",
+           "fa_decode", "fa_decode_splits", "rope_apply", "rope_apply_bwd", "fa_fwd_f32",
+           "fa_bwd_f32", "rope_apply_f32", "rope_apply_bwd_f32", "fa_layer_window", "fa_rope_inv_freq",
            "fa_rope_inv_freq_llama3", "fa_layer_rope_theta", "fa_set_stage_events",
            "fa_last_error")
 
@@ -164,6 +170,21 @@ def fa_bwd_sink(q, k, v, o, lse, dO, sinks, dq, dk, dv, dsinks, B, H, Hkv, T, d,
     return _check(_lib.fa_bwd_sink(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dO),
                                    _ptr(sinks), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dsinks), B, H,
                                    Hkv, T, d, float(scale), window, global_every, float(softcap),
+                                   _stream(stream)))
+
+
+def fa_fwd_vdim(q, k, v, o, lse, B, H, Hkv, T, d, d_v, scale, window=0, global_every=0,
+                softcap=0.0, stream=None):
+    return _check(_lib.fa_fwd_vdim(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Hkv, T,
+                                   d, d_v, float(scale), window, global_every, float(softcap),
+                                   _stream(stream)))
+
+
+def fa_bwd_vdim(q, k, v, o, lse, dO, dq, dk, dv, B, H, Hkv, T, d, d_v, scale, window=0,
+                global_every=0, softcap=0.0, stream=None):
+    return _check(_lib.fa_bwd_vdim(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dO),
+                                   _ptr(dq), _ptr(dk), _ptr(dv), B, H, Hkv, T, d, d_v,
+                                   float(scale), window, global_every, float(softcap),
                                    _stream(stream)))
 
 

@@ -21,6 +21,10 @@ Workloads (shapes of the models the pages describe; no dataset is used):
   gemma-global  same, full causal, cap 50
   gemma3-local  same, window 1024, cap 50 (Gemma 3 row: 5 local : 1 global,
                 window 1024; the global layer is gemma-global)
+  mla           B2 H16/16 T8192 d192 d_v128 bf16, causal, scale 1/sqrt(192)
+                (DeepSeek-V3 / Kimi K2 MLA with the latent decompressed:
+                q, k 128 + 64 rotary dims, v 128; 16 heads = one GPU's
+                share of Kimi K2's 64 under 4-way head parallelism)
 
 Decode workloads (one new token per sequence, preallocated 32k bf16 cache,
 ragged lengths uniform in [16384, 32768]):
@@ -55,6 +59,11 @@ class Workload:
     sigma_qk: float = 1.0
     sigma_vdo: float = 1.0
     seed: int = 0
+    d_v: int = 0              # value head size; 0: same as d
+
+    @property
+    def dv(self) -> int:
+        return self.d_v or self.d
 
     @property
     def scale(self) -> float:
@@ -72,13 +81,15 @@ class Workload:
         return W * (W + 1) // 2 + (T - W) * W
 
     def fwd_flops(self) -> float:
-        """Effective forward FLOPs: 4*d per visible pair (QK^T and PV)."""
-        return 4.0 * self.d * self.visible_pairs() * self.B * self.H
+        """Effective forward FLOPs: 2*(d + d_v) per visible pair (QK^T and
+        PV; 4*d when d_v = d)."""
+        return 2.0 * (self.d + self.dv) * self.visible_pairs() * self.B * self.H
 
     def bwd_flops(self) -> float:
-        """Effective backward FLOPs: 2.5x forward (five d-long products per
-        visible pair: QK^T recompute, dO V^T, P^T dO, dS K, dS^T Q)."""
-        return 2.5 * self.fwd_flops()
+        """Effective backward FLOPs: five products per visible pair -- QK^T
+        recompute, dS K, dS^T Q (length d) and dO V^T, P^T dO (length d_v):
+        2*(3d + 2d_v), i.e. 2.5x forward when d_v = d."""
+        return 2.0 * (3 * self.d + 2 * self.dv) * self.visible_pairs() * self.B * self.H
 
     def replace(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
@@ -97,6 +108,7 @@ WORKLOADS = {
                  softcap=50.0, sigma_qk=2.0),
         Workload("gemma3-local", "bf16", 2, 8, 4, 8192, 256, window=1024,
                  softcap=50.0, global_every=6, sigma_qk=2.0),
+        Workload("mla", "bf16", 2, 16, 16, 8192, 192, d_v=128),
     ]
 }
 
@@ -104,7 +116,8 @@ WORKLOADS = {
 def draw(w: Workload, seed: int | None = None, need_do: bool = True):
     """Seeded CPU tensors (q, k, v, do) of workload ``w``.
 
-    q, do: [B, H, T, d]; k, v: [B, Hkv, T, d]; dtype float32 or bfloat16 as
+    q: [B, H, T, d]; k: [B, Hkv, T, d]; v: [B, Hkv, T, d_v]; do: [B, H, T, d_v]
+    (d_v = d unless the workload sets it); dtype float32 or bfloat16 as
     the workload says.  ``do`` is None when ``need_do`` is False.
     """
     g = torch.Generator("cpu")
@@ -113,10 +126,10 @@ def draw(w: Workload, seed: int | None = None, need_do: bool = True):
     shp_k = (w.B, w.Hkv, w.T, w.d)
     q = torch.randn(shp_q, generator=g, dtype=torch.float32) * w.sigma_qk
     k = torch.randn(shp_k, generator=g, dtype=torch.float32) * w.sigma_qk
-    v = torch.randn(shp_k, generator=g, dtype=torch.float32) * w.sigma_vdo
+    v = torch.randn(shp_k[:3] + (w.dv,), generator=g, dtype=torch.float32) * w.sigma_vdo
     do = None
     if need_do:
-        do = torch.randn(shp_q, generator=g, dtype=torch.float32) * w.sigma_vdo
+        do = torch.randn(shp_q[:3] + (w.dv,), generator=g, dtype=torch.float32) * w.sigma_vdo
     dt = w.torch_dtype
     out = [t.to(dt) if t is not None else None for t in (q, k, v, do)]
     return tuple(out)

@@ -84,6 +84,25 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o,
            int B, int H, int Hkv, int T, int d, float scale, int window,
            int global_every, float softcap, hipStream_t stream);
 
+/* Value head size different from the query/key head size (bf16 tensors):
+ * MLA-style heads with the latent decompressed, d = 192 for q and k (128
+ * "nope" + 64 rotary dims) and d_v = 128 for v, o, dO, dv, with the caller's
+ * scale 1/sqrt(192) (Forge ARCHITECTURES.md family table, DeepSeek-V3 row,
+ * and the "Formules clés" note on MLA; plan wave 3 item 13).
+ *   q, dq [B,H,T,d]; k, dk [B,Hkv,T,d]; v, dv [B,Hkv,T,d_v];
+ *   o, dO [B,H,T,d_v]; lse [B,H,T].
+ * Supported (d, d_v): (192, 128), and d == d_v in {64, 128, 256} (then
+ * identical to fa_fwd / fa_bwd).  Everything else as fa_fwd / fa_bwd. */
+int fa_fwd_vdim(const void* q, const void* k, const void* v, void* o,
+                float* lse, int B, int H, int Hkv, int T, int d, int d_v,
+                float scale, int window, int global_every, float softcap,
+                hipStream_t stream);
+int fa_bwd_vdim(const void* q, const void* k, const void* v, const void* o,
+                const float* lse, const void* dO, void* dq, void* dk, void* dv,
+                int B, int H, int Hkv, int T, int d, int d_v, float scale,
+                int window, int global_every, float softcap,
+                hipStream_t stream);
+
 /* Attention sinks and the per-head max logit (bf16 tensors).
  * sinks: [H] float32 device array (natural-log logits) or NULL.  A sink is a
  * learned per-head logit in every row's softmax denominator that carries no
