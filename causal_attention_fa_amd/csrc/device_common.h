@@ -65,6 +65,23 @@ __device__ __forceinline__ void atomic_max_f32(float* addr, float v) {
     atomicMin((unsigned int*)addr, __float_as_uint(v));
 }
 
+// ---------------------------------------------------------------- RoPE
+// Rotation of the interleaved pair (xe, xo) at position t by the angle
+// fl32(t * f) (f from the host inverse-frequency table; accurate sincosf,
+// angles reach ~1e4 rad); the backward rotates by -angle.  Every kernel that
+// rotates uses these two definitions, so fused and standalone RoPE round
+// identically.
+__device__ __forceinline__ void rope_sincos(float t, float f, bool bwd, float& cs, float& sn) {
+  sincosf(t * f, &sn, &cs);
+  if (bwd) sn = -sn;
+}
+__device__ __forceinline__ void rope_pair(float cs, float sn, float& xe, float& xo) {
+  const float ye = fmaf(xe, cs, -(xo * sn));
+  const float yo = fmaf(xe, sn, xo * cs);
+  xe = ye;
+  xo = yo;
+}
+
 // ---------------------------------------------------------------- LDS tiles
 // A tile of ROWS x D bf16 lives in LDS in rows of D*2 + 64 bytes (stride
 // = 16 mod 64 dwords for d = 128, 256; 48 = -16 mod 64 for d = 64, 192:

@@ -114,7 +114,8 @@ constexpr float kLog2e = 1.4426950408889634f;
 int attn_fwd(bool f32, const void* q, const void* k, const void* v, void* o, float* lse, int B,
              int H, int Hkv, int T, int d, float scale, int window, int global_every,
              float softcap, hipStream_t stream, const char* fn = nullptr,
-             const float* sinks = nullptr, float* max_logit = nullptr, int d_v = -1) {
+             const float* sinks = nullptr, float* max_logit = nullptr, int d_v = -1,
+             const float* rope = nullptr, void* q_rot = nullptr) {
   if (!fn) fn = f32 ? "fa_fwd_f32" : "fa_fwd";
   if (d_v < 0) d_v = d;
   int rc = check_attn(fn, B, H, Hkv, T, d, scale, window, global_every, softcap, d_v);
@@ -131,6 +132,12 @@ int attn_fwd(bool f32, const void* q, const void* k, const void* v, void* o, flo
     if (!aligned16(max_logit)) return fail(FA_ERR_INVALID_ARG, std::string(fn) + ": max_logit not 16-byte aligned");
     for (const Range& r : rs)
       if (overlap(ml, r)) return fail(FA_ERR_INVALID_ARG, std::string(fn) + ": max_logit overlaps " + r.name);
+  }
+  if (q_rot) {
+    const Range qr{"q_rot", q_rot, nq};
+    if (!aligned16(q_rot)) return fail(FA_ERR_INVALID_ARG, std::string(fn) + ": q_rot not 16-byte aligned");
+    for (const Range& r : rs)
+      if (overlap(qr, r)) return fail(FA_ERR_INVALID_ARG, std::string(fn) + ": q_rot overlaps " + r.name);
   }
   const int W = resolve_window(window, T);
   hipError_t e;
@@ -156,6 +163,8 @@ int attn_fwd(bool f32, const void* q, const void* k, const void* v, void* o, flo
     a.cap_log2e = softcap > 0.f ? softcap * kLog2e : 0.f;
     a.sinks = sinks;
     a.max_logit = max_logit;
+    a.rope_inv_freq = rope;
+    a.q_rot = (fa::bf16*)q_rot;
     e = fa::launch_fwd_bf16(a, d, d_v, stream);
   }
   return finish(e, stream, fn);
@@ -165,7 +174,7 @@ int attn_bwd(bool f32, const void* q, const void* k, const void* v, const void* 
              const float* lse, const void* dO, void* dq, void* dk, void* dv, int B, int H,
              int Hkv, int T, int d, float scale, int window, int global_every, float softcap,
              hipStream_t stream, const char* fn = nullptr, const float* sinks = nullptr,
-             float* dsinks = nullptr, int d_v = -1) {
+             float* dsinks = nullptr, int d_v = -1, const float* rope = nullptr) {
   if (!fn) fn = f32 ? "fa_bwd_f32" : "fa_bwd";
   if (d_v < 0) d_v = d;
   int rc = check_attn(fn, B, H, Hkv, T, d, scale, window, global_every, softcap, d_v);
@@ -223,6 +232,7 @@ int attn_bwd(bool f32, const void* q, const void* k, const void* v, const void* 
     a.inv_cap = softcap > 0.f ? 1.f / softcap : 0.f;
     a.sinks = sinks;
     a.dsinks = dsinks;
+    a.rope_inv_freq = rope;
     e = fa::launch_bwd_bf16(a, d, d_v, stream);
   }
   const hipError_t e2 = hipFreeAsync(Dst, stream);
@@ -370,6 +380,29 @@ int fa_decode_splits(int B, int Hkv, int S, int window, int* nsplit, int* chunk)
     return fail(FA_ERR_INVALID_ARG, "fa_decode_splits: invalid arguments");
   decode_split(B * Hkv, window > 0 ? std::min(window, S) : S, nsplit, chunk);
   return FA_OK;
+}
+
+int fa_fwd_rope(const void* q, const void* k, const void* v, void* o, float* lse,
+                const float* inv_freq, void* q_rot, int B, int H, int Hkv, int T, int d,
+                float scale, int window, int global_every, float softcap, hipStream_t stream) {
+  if (!inv_freq) return fail(FA_ERR_INVALID_ARG, "fa_fwd_rope: null pointer inv_freq");
+  if (!aligned16(inv_freq)) return fail(FA_ERR_INVALID_ARG, "fa_fwd_rope: inv_freq not 16-byte aligned");
+  if (d == 256)
+    return fail(FA_ERR_UNSUPPORTED, "fa_fwd_rope: fused RoPE supports d = 64 or 128");
+  return attn_fwd(false, q, k, v, o, lse, B, H, Hkv, T, d, scale, window, global_every, softcap,
+                  stream, "fa_fwd_rope", nullptr, nullptr, -1, inv_freq, q_rot);
+}
+
+int fa_bwd_rope(const void* q_rot, const void* k, const void* v, const void* o, const float* lse,
+                const void* dO, const float* inv_freq, void* dq, void* dk, void* dv, int B,
+                int H, int Hkv, int T, int d, float scale, int window, int global_every,
+                float softcap, hipStream_t stream) {
+  if (!inv_freq) return fail(FA_ERR_INVALID_ARG, "fa_bwd_rope: null pointer inv_freq");
+  if (!aligned16(inv_freq)) return fail(FA_ERR_INVALID_ARG, "fa_bwd_rope: inv_freq not 16-byte aligned");
+  if (d == 256)
+    return fail(FA_ERR_UNSUPPORTED, "fa_bwd_rope: fused RoPE supports d = 64 or 128");
+  return attn_bwd(false, q_rot, k, v, o, lse, dO, dq, dk, dv, B, H, Hkv, T, d, scale, window,
+                  global_every, softcap, stream, "fa_bwd_rope", nullptr, nullptr, -1, inv_freq);
 }
 
 int fa_fwd_vdim(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,

@@ -192,9 +192,22 @@ __global__ __launch_bounds__(64 * NW, (DK >= 192 ? 1 : 8 / NW)) void fa_bwd_dq_k
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
+        float x[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = dqacc[db][4 * i4 + e] * a.scale;
+        if constexpr (DK <= 128) if (a.rope_inv_freq) {
+          // RoPE backward fused into the store: elements d = 32 db + 8 i4
+          // + 4 g + e hold the pairs 16 db + 4 i4 + 2 g + {0, 1}
+#pragma unroll
+          for (int p = 0; p < 2; ++p) {
+            float cs, sn;
+            rope_sincos((float)qrow, a.rope_inv_freq[16 * db + 4 * i4 + 2 * g + p], true, cs, sn);
+            rope_pair(cs, sn, x[2 * p], x[2 * p + 1]);
+          }
+        }
         bf16x4 v;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = (bf16)(dqacc[db][4 * i4 + e] * a.scale);
+        for (int e = 0; e < 4; ++e) v[e] = (bf16)x[e];
         *(bf16x4*)(Qd + 32 * db + 8 * i4 + 4 * g) = v;
       }
   }

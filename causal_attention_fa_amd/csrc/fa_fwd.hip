@@ -70,6 +70,35 @@ __global__ __launch_bounds__(64 * NW, (DK >= 256 || QW > 1 ? 1 : 8 / NW)) void f
 #pragma unroll
     for (int c = 0; c < NC; ++c) qreg[u][c] = src[2 * c];
   }
+  // RoPE fused into the Q load (head sizes up to 128: the inlined sincosf
+  // would push the larger kernels into spills): this lane's 8-element
+  // chunks hold the pairs 8c + 4g + p of its row (position = row index);
+  // the rotated row is optionally written out once for the backward.
+  if constexpr (DK <= 128) if (a.rope_inv_freq) {
+#pragma unroll
+    for (int u = 0; u < QW; ++u) {
+      const int qrow = qw0 + 32 * u + l32;
+      const float t = (float)min(qrow, T - 1);
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        bf16x8 x = qreg[u][c];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          float cs, sn, xe = (float)x[2 * p], xo = (float)x[2 * p + 1];
+          rope_sincos(t, a.rope_inv_freq[8 * c + 4 * g + p], false, cs, sn);
+          rope_pair(cs, sn, xe, xo);
+          x[2 * p] = (bf16)xe;
+          x[2 * p + 1] = (bf16)xo;
+        }
+        qreg[u][c] = x;
+      }
+      if (a.q_rot && qrow < T) {
+        bf16x8* dst = (bf16x8*)(a.q_rot + (bh * T + qrow) * DK + 8 * g);
+#pragma unroll
+        for (int c = 0; c < NC; ++c) dst[2 * c] = qreg[u][c];
+      }
+    }
+  }
 
   int kv_lo = 0;
   if (W > 0) kv_lo = max(0, q0 - W + 1);

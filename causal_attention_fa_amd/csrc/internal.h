@@ -25,6 +25,8 @@ struct FwdArgs {
   float cap_log2e;                 // cap * log2(e), 0 when no cap
   const float* sinks;              // [H] sink logits (natural log) or null
   float* max_logit;                // [B, H] largest softmax logit, or null
+  const float* rope_inv_freq;      // [d/2]: rotate q at load (q is un-rotated), or null
+  bf16* q_rot;                     // [B, H, T, d] rotated q output, or null
 };
 
 // Backward arguments.  Dst holds the per-row D = <dO_i, o_i> scratch
@@ -48,6 +50,8 @@ struct BwdArgs {
   float inv_cap;                   // 1 / cap, 0 when no cap
   const float* sinks;              // [H] sink logits or null
   float* dsinks;                   // [H] gradient of the sinks (accumulated), or null
+  const float* rope_inv_freq;      // [d/2]: dq is rotated back (gradient w.r.t. the
+                                   // un-rotated q), or null
 };
 
 // float32 twins (plain pointers, same semantics).

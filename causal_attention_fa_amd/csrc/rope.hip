@@ -15,6 +15,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "device_common.h"
 #include "internal.h"
 
 namespace fa {
@@ -48,11 +49,7 @@ __global__ __launch_bounds__(kThreads) void rope_vec_kernel(RopeArgs a) {
   const int c0 = (int)(e0 % a.d);                 // even: N and d are even
   float cs[N / 2], sn[N / 2];
 #pragma unroll
-  for (int p = 0; p < N / 2; ++p) {
-    const float ang = (float)t * a.inv_freq[c0 / 2 + p];
-    sincosf(ang, &sn[p], &cs[p]);
-    if (BWD) sn[p] = -sn[p];
-  }
+  for (int p = 0; p < N / 2; ++p) rope_sincos((float)t, a.inv_freq[c0 / 2 + p], BWD, cs[p], sn[p]);
   const int bh0 = blockIdx.y * kBhPer;
   const int bh1 = min(a.BH, bh0 + kBhPer);
   const T* x = (const T*)a.x;
@@ -63,9 +60,10 @@ __global__ __launch_bounds__(kThreads) void rope_vec_kernel(RopeArgs a) {
     V r;
 #pragma unroll
     for (int p = 0; p < N / 2; ++p) {
-      const float xe = (float)v[2 * p], xo = (float)v[2 * p + 1];
-      r[2 * p] = (T)(xe * cs[p] - xo * sn[p]);
-      r[2 * p + 1] = (T)(xe * sn[p] + xo * cs[p]);
+      float xe = (float)v[2 * p], xo = (float)v[2 * p + 1];
+      rope_pair(cs[p], sn[p], xe, xo);
+      r[2 * p] = (T)xe;
+      r[2 * p + 1] = (T)xo;
     }
     *(V*)(y + off) = r;
   }
@@ -80,17 +78,17 @@ __global__ __launch_bounds__(kThreads) void rope_pair_kernel(RopeArgs a) {
   const int t = (int)(e0 / a.d);
   const int c0 = (int)(e0 % a.d);
   float sn, cs;
-  sincosf((float)t * a.inv_freq[c0 / 2], &sn, &cs);
-  if (BWD) sn = -sn;
+  rope_sincos((float)t, a.inv_freq[c0 / 2], BWD, cs, sn);
   const int bh0 = blockIdx.y * kBhPer;
   const int bh1 = min(a.BH, bh0 + kBhPer);
   const T* x = (const T*)a.x;
   T* y = (T*)a.y;
   for (int bh = bh0; bh < bh1; ++bh) {
     const long off = (long)bh * slice + e0;
-    const float xe = (float)x[off], xo = (float)x[off + 1];
-    y[off] = (T)(xe * cs - xo * sn);
-    y[off + 1] = (T)(xe * sn + xo * cs);
+    float xe = (float)x[off], xo = (float)x[off + 1];
+    rope_pair(cs, sn, xe, xo);
+    y[off] = (T)xe;
+    y[off + 1] = (T)xo;
   }
 }
 

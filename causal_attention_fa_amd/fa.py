@@ -53,6 +53,11 @@ _lib.fa_fwd_sink.restype = _I
 _lib.fa_bwd_sink.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F,
                              _I, _I, _F, _P]
 _lib.fa_bwd_sink.restype = _I
+_lib.fa_fwd_rope.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I, _F, _P]
+_lib.fa_fwd_rope.restype = _I
+_lib.fa_bwd_rope.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I,
+                             _I, _F, _P]
+_lib.fa_bwd_rope.restype = _I
 _lib.fa_fwd_vdim.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I, _F, _P]
 _lib.fa_fwd_vdim.restype = _I
 _lib.fa_bwd_vdim.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I,
@@ -79,6 +84,7 @@ _lib.fa_last_error.argtypes = []
 _lib.fa_last_error.restype = ctypes.c_char_p
 
 EXPORTS = ("fa_fwd", "fa_bwd", "fa_fwd_sink", "fa_bwd_sink", "fa_fwd_vdim", "fa_bwd_vdim",
+           "fa_fwd_rope", "fa_bwd_rope",
            "fa_decode", "fa_decode_splits", "rope_apply", "rope_apply_bwd", "fa_fwd_f32",
            "fa_bwd_f32", "rope_apply_f32", "rope_apply_bwd_f32", "fa_layer_window", "fa_rope_inv_freq",
            "fa_rope_inv_freq_llama3", "fa_layer_rope_theta", "fa_set_stage_events",
@@ -170,6 +176,21 @@ def fa_bwd_sink(q, k, v, o, lse, dO, sinks, dq, dk, dv, dsinks, B, H, Hkv, T, d,
     return _check(_lib.fa_bwd_sink(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dO),
                                    _ptr(sinks), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dsinks), B, H,
                                    Hkv, T, d, float(scale), window, global_every, float(softcap),
+                                   _stream(stream)))
+
+
+def fa_fwd_rope(q, k, v, o, lse, inv_freq, q_rot, B, H, Hkv, T, d, scale, window=0,
+                global_every=0, softcap=0.0, stream=None):
+    return _check(_lib.fa_fwd_rope(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(inv_freq),
+                                   _ptr(q_rot), B, H, Hkv, T, d, float(scale), window,
+                                   global_every, float(softcap), _stream(stream)))
+
+
+def fa_bwd_rope(q_rot, k, v, o, lse, dO, inv_freq, dq, dk, dv, B, H, Hkv, T, d, scale,
+                window=0, global_every=0, softcap=0.0, stream=None):
+    return _check(_lib.fa_bwd_rope(_ptr(q_rot), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dO),
+                                   _ptr(inv_freq), _ptr(dq), _ptr(dk), _ptr(dv), B, H, Hkv, T, d,
+                                   float(scale), window, global_every, float(softcap),
                                    _stream(stream)))
 
 
