@@ -4,8 +4,11 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
 One step is one pass of the whole path over one batch of synthetic input
-already resident in HBM: RoPE on Q and K (workloads that have it), fa_fwd,
-fa_bwd, RoPE backward on dQ and dK.  The default workload is "mistral"
+already resident in HBM: RoPE (workloads that have it), the attention
+forward and backward, RoPE backward.  With --rope fused (default) K is
+rotated by rope_apply, q is rotated inside fa_fwd_rope and dq rotated back
+inside fa_bwd_rope, dK by rope_apply_bwd; --rope separate runs rope_apply on
+Q and K around fa_fwd / fa_bwd.  The default workload is "mistral"
 (B4 H32/8 T8192 d128, window 4096): the largest T = 8192 workload, the
 sequence length the throughput bars are set at.  Prints ONE JSON line:
 effective fwd+bwd TFLOPS (only mask-visible (q, k) pairs count; bwd = 2.5x
@@ -157,6 +160,10 @@ def main():
     ap.add_argument("--calibrate-copy-mb", type=float, default=0.0,
                     help="only run a plain device copy of this many MiB (5 times) and "
                          "exit: the reference kernel for scaling HBM byte counters")
+    ap.add_argument("--rope", choices=["fused", "separate"], default="fused",
+                    help="RoPE workloads: fused into the attention (fa_fwd_rope / "
+                         "fa_bwd_rope; K rotated by rope_apply) or rope_apply on Q and K "
+                         "around fa_fwd / fa_bwd")
     ap.add_argument("--decode-workload", default="qwen25-decode",
                     help="decode workload timed after the main step ('none' to skip)")
     ap.add_argument("--decode-iters", type=int, default=20)
@@ -195,6 +202,7 @@ def main():
     lse = torch.empty((B, H, T), dtype=torch.float32, device=dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     rope = bool(w.rope_theta)
+    fused = rope and args.rope == "fused" and d in (64, 128) and dvh == d
     if rope:
         tab = torch.from_numpy(fa.fa_rope_inv_freq(d, w.rope_theta)).to(dev)
         qr, kr = torch.empty_like(q), torch.empty_like(k)
@@ -212,7 +220,23 @@ def main():
     bwd_names = ["bwd_dq", "bwd_dv", "bwd_dk"]   # the three launches of fa_bwd
     n_bwd = len(bwd_names)
 
+    def step_fused(ev=None):
+        # K rotated once; q rotated at the attention's load (rotated q kept
+        # for the backward); dq comes back un-rotated; dk rotated back.
+        if ev: fa.fa_set_stage_events([ev["rk"][0].cuda_event, ev["rk"][1].cuda_event])
+        fa.rope_apply(k, kr, tab, B, Hkv, T, d, sh)
+        if ev: fa.fa_set_stage_events([e.cuda_event for e in ev["fwd"]])
+        fa.fa_fwd_rope(q, kr, v, o, lse, tab, qr, B, H, Hkv, T, d, w.scale, w.window,
+                       w.global_every, w.softcap, sh)
+        if ev: fa.fa_set_stage_events([e.cuda_event for e in ev["bwd"]])
+        fa.fa_bwd_rope(qr, kr, v, o, lse, do, tab, dqi, dk, dv, B, H, Hkv, T, d, w.scale,
+                       w.window, w.global_every, w.softcap, sh)
+        if ev: fa.fa_set_stage_events([])
+        fa.rope_apply_bwd(dk, dki, tab, B, Hkv, T, d, sh)
+
     def step(ev=None):
+        if fused:
+            return step_fused(ev)
         if rope:
             if ev: fa.fa_set_stage_events([ev["rq"][0].cuda_event, ev["rq"][1].cuda_event])
             fa.rope_apply(q, qr, tab, B, H, T, d, sh)
@@ -262,7 +286,8 @@ def main():
     for j, nm in enumerate(bwd_names):
         kern[nm] = avg([(e["bwd"][j], e["bwd"][j + 1]) for e in evs])
     if rope:
-        kern["rope_q"] = avg([(e["rq"][0], e["rq"][1]) for e in evs])
+        if not fused:
+            kern["rope_q"] = avg([(e["rq"][0], e["rq"][1]) for e in evs])
         kern["rope_k"] = avg([(e["rk"][0], e["rk"][1]) for e in evs])
 
     pairs_total = w.visible_pairs() * B * H
@@ -292,8 +317,12 @@ def main():
              "kernel_ms": {n: round(t, 4) for n, t in kern.items()},
              "wall_s": round(wall, 3), "kernel_sources_sha": src_hash}
     if rope:
-        nbytes_q = 2 * q.numel() * 2 + d // 2 * 4
-        extra["rope_q_gbs"] = round(nbytes_q / (kern["rope_q"] * 1e-3) / 1e9, 1)
+        extra["rope_mode"] = "fused" if fused else "separate"
+        nbytes_k = 2 * k.numel() * 2 + d // 2 * 4
+        extra["rope_k_gbs"] = round(nbytes_k / (kern["rope_k"] * 1e-3) / 1e9, 1)
+        if not fused:
+            nbytes_q = 2 * q.numel() * 2 + d // 2 * 4
+            extra["rope_q_gbs"] = round(nbytes_q / (kern["rope_q"] * 1e-3) / 1e9, 1)
 
     if args.decode_workload != "none":
         del q, k, v, do, o, lse, dq, dk, dv

@@ -47,11 +47,20 @@ __device__ __forceinline__ float fast_exp2(float x) {
 }
 
 // max over lanes l and l^32.
+// Combine a value with the one in lane l ^ 32 through the gfx950 VGPR
+// half-swap (v_permlane32_swap: lanes 32..63 of the first operand trade
+// places with lanes 0..31 of the second), which stays in the VALU instead of
+// a round trip through the LDS crossbar.  With both operands = x, the two
+// results hold, in every lane, x[l] and x[l ^ 32] (in some order).
 __device__ __forceinline__ float xor32_max(float x) {
-  return fmaxf(x, __shfl_xor(x, 32));
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float xor32_sum(float x) {
-  return x + __shfl_xor(x, 32);
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // Float atomic max through the integer order of IEEE-754 bit patterns

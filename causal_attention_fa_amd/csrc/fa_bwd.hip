@@ -282,9 +282,12 @@ __global__ __launch_bounds__(64 * NW, (DK >= 192 ? 1 : 8 / NW)) void fa_bwd_dkdv
   TileStage<DK, BQB, NT> qst;
   TileStage<DV, BQB, NT> dost;
   float stv = 0.f;
-  auto stage_stats = [&](int it) {
-    const int hh = w.hkv * G + it / nqt;
-    const int q0 = (qt_lo + it % nqt) * BQB;
+  // Iteration it visits query head (hkv*G + hi) and query tile ti, with
+  // it = hi * nqt + ti; (hi, ti) advance incrementally (no integer division
+  // in the loop).
+  auto stage_stats = [&](int hi, int ti) {
+    const int hh = w.hkv * G + hi;
+    const int q0 = (qt_lo + ti) * BQB;
     const size_t bhh = (size_t)w.b * a.H + hh;
     if (tid < 2 * BQB) {
       int qq = q0 + (tid % BQB);
@@ -292,22 +295,27 @@ __global__ __launch_bounds__(64 * NW, (DK >= 192 ? 1 : 8 / NW)) void fa_bwd_dkdv
       stv = tid < BQB ? a.lse[bhh * T + qq] * kLog2e : a.Dst[bhh * T + qq];
     }
   };
-  auto tile_src = [&](int it, const bf16* base, int dd) {
-    const int hh = w.hkv * G + it / nqt;
-    return base + ((size_t)w.b * a.H + hh) * T * dd;
+  auto tile_src = [&](int hi, const bf16* base, int dd) {
+    return base + ((size_t)w.b * a.H + w.hkv * G + hi) * T * dd;
   };
-  auto tile_q0 = [&](int it) { return (qt_lo + it % nqt) * BQB; };
+  auto tile_q0 = [&](int ti) { return (qt_lo + ti) * BQB; };
 
   qst.load(tile_src(0, a.q, DK), tile_q0(0), T, tid);
   dost.load(tile_src(0, a.dO, DV), tile_q0(0), T, tid);
-  stage_stats(0);
+  stage_stats(0, 0);
   qst.store(lds, tid);
   dost.store(olds, tid);
   if (tid < 2 * BQB) *(LDS_AS float*)(stat + tid * 4) = stv;
   __syncthreads();
 
   const int ka = kw0, kb = kw0 + 31;
+  int hi_cur = 0, ti_cur = 0;
   for (int it = 0; it < niter; ++it) {
+    int hi_nx = hi_cur, ti_nx = ti_cur + 1;
+    if (ti_nx == nqt) {
+      ti_nx = 0;
+      ++hi_nx;
+    }
     const int cur = it & 1;
     const LDS_AS char* Qt = lds + cur * TILE_Q;
     const LDS_AS char* dOt = olds + cur * TILE_O;
@@ -316,11 +324,11 @@ __global__ __launch_bounds__(64 * NW, (DK >= 192 ? 1 : 8 / NW)) void fa_bwd_dkdv
     const bool more = it + 1 < niter;
     // next Q, dO tiles and row statistics: loads now, LDS stores at the end
     if (more) {
-      qst.load(tile_src(it + 1, a.q, DK), tile_q0(it + 1), T, tid);
-      dost.load(tile_src(it + 1, a.dO, DV), tile_q0(it + 1), T, tid);
-      stage_stats(it + 1);
+      qst.load(tile_src(hi_nx, a.q, DK), tile_q0(ti_nx), T, tid);
+      dost.load(tile_src(hi_nx, a.dO, DV), tile_q0(ti_nx), T, tid);
+      stage_stats(hi_nx, ti_nx);
     }
-    const int q0 = tile_q0(it);
+    const int q0 = tile_q0(ti_cur);
     const bool empty = ka >= T || q0 + BQB - 1 < ka || (W > 0 && q0 - kb >= W);
     const bool full = q0 >= kb && q0 + BQB <= T && (W == 0 || q0 + BQB - 1 - ka < W);
     f32x16 s[NS], dp[NS];
@@ -393,6 +401,8 @@ __global__ __launch_bounds__(64 * NW, (DK >= 192 ? 1 : 8 / NW)) void fa_bwd_dkdv
       if (tid < 2 * BQB) *(LDS_AS float*)(stat + (cur ^ 1) * 2 * STAT + tid * 4) = stv;
     }
     __syncthreads();
+    hi_cur = hi_nx;
+    ti_cur = ti_nx;
   }
 
   if (krow < T) {
