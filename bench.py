@@ -202,7 +202,7 @@ def main():
     lse = torch.empty((B, H, T), dtype=torch.float32, device=dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     rope = bool(w.rope_theta)
-    fused = rope and args.rope == "fused" and d in (64, 128) and dvh == d
+    fused = rope and args.rope == "fused" and dvh == d
     if rope:
         tab = torch.from_numpy(fa.fa_rope_inv_freq(d, w.rope_theta)).to(dev)
         qr, kr = torch.empty_like(q), torch.empty_like(k)

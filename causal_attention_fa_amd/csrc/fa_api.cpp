@@ -145,6 +145,16 @@ int attn_fwd(bool f32, const void* q, const void* k, const void* v, void* o, flo
     e = fa::launch_fill_f32(max_logit, B * H, -INFINITY, stream);
     if (e != hipSuccess) return finish(e, stream, fn);
   }
+  float* rope_cs = nullptr;   // [T, d/2, 2] (cos, sin) for the fused RoPE
+  if (rope) {
+    e = hipMallocAsync((void**)&rope_cs, (size_t)T * d * sizeof(float), stream);
+    if (e != hipSuccess) return finish(e, stream, "fa_fwd_rope table");
+    e = fa::launch_rope_table(rope, rope_cs, T, d / 2, stream);
+    if (e != hipSuccess) {
+      (void)hipFreeAsync(rope_cs, stream);
+      return finish(e, stream, fn);
+    }
+  }
   stage_begin(stream);
   if (f32) {
     fa::F32Args a{};
@@ -163,9 +173,13 @@ int attn_fwd(bool f32, const void* q, const void* k, const void* v, void* o, flo
     a.cap_log2e = softcap > 0.f ? softcap * kLog2e : 0.f;
     a.sinks = sinks;
     a.max_logit = max_logit;
-    a.rope_inv_freq = rope;
+    a.rope_cs = rope_cs;
     a.q_rot = (fa::bf16*)q_rot;
     e = fa::launch_fwd_bf16(a, d, d_v, stream);
+  }
+  if (rope_cs) {
+    const hipError_t e2 = hipFreeAsync(rope_cs, stream);
+    if (e == hipSuccess) e = e2;
   }
   return finish(e, stream, fn);
 }
@@ -210,6 +224,16 @@ int attn_bwd(bool f32, const void* q, const void* k, const void* v, const void* 
       return finish(e, stream, fn);
     }
   }
+  float* rope_cs = nullptr;   // [T, d/2, 2] (cos, sin) for the fused RoPE backward
+  if (rope) {
+    e = hipMallocAsync((void**)&rope_cs, (size_t)T * d * sizeof(float), stream);
+    if (e == hipSuccess) e = fa::launch_rope_table(rope, rope_cs, T, d / 2, stream);
+    if (e != hipSuccess) {
+      if (rope_cs) (void)hipFreeAsync(rope_cs, stream);
+      (void)hipFreeAsync(Dst, stream);
+      return finish(e, stream, fn);
+    }
+  }
   stage_begin(stream);
   if (f32) {
     fa::F32Args a{};
@@ -232,11 +256,15 @@ int attn_bwd(bool f32, const void* q, const void* k, const void* v, const void* 
     a.inv_cap = softcap > 0.f ? 1.f / softcap : 0.f;
     a.sinks = sinks;
     a.dsinks = dsinks;
-    a.rope_inv_freq = rope;
+    a.rope_cs = rope_cs;
     e = fa::launch_bwd_bf16(a, d, d_v, stream);
   }
-  const hipError_t e2 = hipFreeAsync(Dst, stream);
+  hipError_t e2 = hipFreeAsync(Dst, stream);
   if (e == hipSuccess) e = e2;
+  if (rope_cs) {
+    e2 = hipFreeAsync(rope_cs, stream);
+    if (e == hipSuccess) e = e2;
+  }
   return finish(e, stream, fn);
 }
 
@@ -387,8 +415,6 @@ int fa_fwd_rope(const void* q, const void* k, const void* v, void* o, float* lse
                 float scale, int window, int global_every, float softcap, hipStream_t stream) {
   if (!inv_freq) return fail(FA_ERR_INVALID_ARG, "fa_fwd_rope: null pointer inv_freq");
   if (!aligned16(inv_freq)) return fail(FA_ERR_INVALID_ARG, "fa_fwd_rope: inv_freq not 16-byte aligned");
-  if (d == 256)
-    return fail(FA_ERR_UNSUPPORTED, "fa_fwd_rope: fused RoPE supports d = 64 or 128");
   return attn_fwd(false, q, k, v, o, lse, B, H, Hkv, T, d, scale, window, global_every, softcap,
                   stream, "fa_fwd_rope", nullptr, nullptr, -1, inv_freq, q_rot);
 }
@@ -399,8 +425,6 @@ int fa_bwd_rope(const void* q_rot, const void* k, const void* v, const void* o, 
                 float softcap, hipStream_t stream) {
   if (!inv_freq) return fail(FA_ERR_INVALID_ARG, "fa_bwd_rope: null pointer inv_freq");
   if (!aligned16(inv_freq)) return fail(FA_ERR_INVALID_ARG, "fa_bwd_rope: inv_freq not 16-byte aligned");
-  if (d == 256)
-    return fail(FA_ERR_UNSUPPORTED, "fa_bwd_rope: fused RoPE supports d = 64 or 128");
   return attn_bwd(false, q_rot, k, v, o, lse, dO, dq, dk, dv, B, H, Hkv, T, d, scale, window,
                   global_every, softcap, stream, "fa_bwd_rope", nullptr, nullptr, -1, inv_freq);
 }

@@ -195,15 +195,14 @@ __global__ __launch_bounds__(64 * NW, (DK >= 192 ? 1 : 8 / NW)) void fa_bwd_dq_k
         float x[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) x[e] = dqacc[db][4 * i4 + e] * a.scale;
-        if constexpr (DK <= 128) if (a.rope_inv_freq) {
+        if (a.rope_cs) {
           // RoPE backward fused into the store: elements d = 32 db + 8 i4
-          // + 4 g + e hold the pairs 16 db + 4 i4 + 2 g + {0, 1}
-#pragma unroll
-          for (int p = 0; p < 2; ++p) {
-            float cs, sn;
-            rope_sincos((float)qrow, a.rope_inv_freq[16 * db + 4 * i4 + 2 * g + p], true, cs, sn);
-            rope_pair(cs, sn, x[2 * p], x[2 * p + 1]);
-          }
+          // + 4 g + e hold the pairs 16 db + 4 i4 + 2 g + {0, 1}; rotate by
+          // the negative angle
+          const float4 r = *(const float4*)(a.rope_cs + (size_t)qrow * DK +
+                                            2 * (16 * db + 4 * i4 + 2 * g));
+          rope_pair(r.x, -r.y, x[0], x[1]);
+          rope_pair(r.z, -r.w, x[2], x[3]);
         }
         bf16x4 v;
 #pragma unroll

@@ -70,23 +70,25 @@ __global__ __launch_bounds__(64 * NW, (DK >= 256 || QW > 1 ? 1 : 8 / NW)) void f
 #pragma unroll
     for (int c = 0; c < NC; ++c) qreg[u][c] = src[2 * c];
   }
-  // RoPE fused into the Q load (head sizes up to 128: the inlined sincosf
-  // would push the larger kernels into spills): this lane's 8-element
-  // chunks hold the pairs 8c + 4g + p of its row (position = row index);
-  // the rotated row is optionally written out once for the backward.
-  if constexpr (DK <= 128) if (a.rope_inv_freq) {
+  // RoPE fused into the Q load: this lane's 8-element chunks hold the pairs
+  // 8c + 4g + p of its row (position = row index), whose (cos, sin) come from
+  // the call's table; the rotated row is optionally written out once for the
+  // backward.
+  if (a.rope_cs) {
 #pragma unroll
     for (int u = 0; u < QW; ++u) {
       const int qrow = qw0 + 32 * u + l32;
-      const float t = (float)min(qrow, T - 1);
+      const float4* cs4 = (const float4*)(a.rope_cs + (size_t)min(qrow, T - 1) * DK);
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
         bf16x8 x = qreg[u][c];
+        // pairs 8c + 4g .. +3: 4 (cos, sin) = two float4
+        const float4 r0 = cs4[(8 * c + 4 * g) / 2], r1 = cs4[(8 * c + 4 * g) / 2 + 1];
+        const float cv[4] = {r0.x, r0.z, r1.x, r1.z}, sv[4] = {r0.y, r0.w, r1.y, r1.w};
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-          float cs, sn, xe = (float)x[2 * p], xo = (float)x[2 * p + 1];
-          rope_sincos(t, a.rope_inv_freq[8 * c + 4 * g + p], false, cs, sn);
-          rope_pair(cs, sn, xe, xo);
+          float xe = (float)x[2 * p], xo = (float)x[2 * p + 1];
+          rope_pair(cv[p], sv[p], xe, xo);
           x[2 * p] = (bf16)xe;
           x[2 * p + 1] = (bf16)xo;
         }

@@ -25,7 +25,8 @@ struct FwdArgs {
   float cap_log2e;                 // cap * log2(e), 0 when no cap
   const float* sinks;              // [H] sink logits (natural log) or null
   float* max_logit;                // [B, H] largest softmax logit, or null
-  const float* rope_inv_freq;      // [d/2]: rotate q at load (q is un-rotated), or null
+  const float* rope_cs;            // [T, d/2, 2] (cos, sin) of the RoPE angles: rotate q
+                                   // at load (q is un-rotated), or null
   bf16* q_rot;                     // [B, H, T, d] rotated q output, or null
 };
 
@@ -50,8 +51,8 @@ struct BwdArgs {
   float inv_cap;                   // 1 / cap, 0 when no cap
   const float* sinks;              // [H] sink logits or null
   float* dsinks;                   // [H] gradient of the sinks (accumulated), or null
-  const float* rope_inv_freq;      // [d/2]: dq is rotated back (gradient w.r.t. the
-                                   // un-rotated q), or null
+  const float* rope_cs;            // [T, d/2, 2] RoPE (cos, sin): dq is rotated back
+                                   // (gradient w.r.t. the un-rotated q), or null
 };
 
 // float32 twins (plain pointers, same semantics).
@@ -114,6 +115,9 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, int d, int d_v, hipStream_t stream)
 hipError_t launch_fwd_f32(const F32Args& a, hipStream_t stream);
 hipError_t launch_bwd_f32(const F32Args& a, hipStream_t stream);
 hipError_t launch_decode_bf16(const DecodeArgs& a, int d, bool cap, hipStream_t stream);
+// (cos, sin) of the RoPE angle fl32(t * inv_freq[i]) for t < T, i < half,
+// into cs [T, half, 2] -- the same values the RoPE kernels compute.
+hipError_t launch_rope_table(const float* inv_freq, float* cs, int T, int half, hipStream_t stream);
 hipError_t launch_rope_bf16(const RopeArgs& a, bool bwd, hipStream_t stream);
 hipError_t launch_rope_f32(const RopeArgs& a, bool bwd, hipStream_t stream);
 

@@ -124,4 +124,22 @@ hipError_t launch_rope_f32(const RopeArgs& a, bool bwd, hipStream_t stream) {
   return launch_rope<float>(a, bwd, stream);
 }
 
+__global__ __launch_bounds__(256) void rope_table_kernel(const float* inv_freq, float2* cs, int T,
+                                                        int half) {
+  const long e = (long)blockIdx.x * 256 + threadIdx.x;
+  if (e >= (long)T * half) return;
+  const int t = (int)(e / half);
+  const int i = (int)(e % half);
+  float c, sn;
+  rope_sincos((float)t, inv_freq[i], false, c, sn);
+  cs[e] = make_float2(c, sn);
+}
+
+hipError_t launch_rope_table(const float* inv_freq, float* cs, int T, int half, hipStream_t stream) {
+  const long n = (long)T * half;
+  hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
+                     inv_freq, (float2*)cs, T, half);
+  return hipGetLastError();
+}
+
 }  // namespace fa

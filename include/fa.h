@@ -84,20 +84,21 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o,
            int B, int H, int Hkv, int T, int d, float scale, int window,
            int global_every, float softcap, hipStream_t stream);
 
-/* RoPE fused into the attention (bf16 tensors, d = 64 or 128).  The query
- * rows are loaded once per workgroup into registers, so their rotation (and
- * the inverse rotation of dq at its store) costs no extra pass over HBM;
+/* RoPE fused into the attention (bf16 tensors, d = 64, 128, 256).  The
+ * query rows are loaded once per workgroup into registers, so their rotation
+ * (and the inverse rotation of dq at its store) costs no extra pass over HBM;
  * key tiles are re-read by every query block, so K is rotated beforehand by
  * rope_apply (Forge attention.h commit log, "Wave 1": RoPE reads the host
- * inverse-frequency table; README: interleaved pairs).
+ * inverse-frequency table; README: interleaved pairs).  Each call builds a
+ * [T, d/2] (cos, sin) table of the angles (stream-ordered hipMallocAsync
+ * scratch, freed on the stream) with the same arithmetic as rope_apply.
  * fa_fwd_rope: q un-rotated [B,H,T,d]; k already rotated; inv_freq [d/2]
  *   float32 device table; q_rot [B,H,T,d] receives rope_apply(q) bit for bit
  *   (for the backward), or NULL.  o, lse as fa_fwd.
  * fa_bwd_rope: q_rot = rotated q (fa_fwd_rope's q_rot); dq is written as the
  *   gradient with respect to the UN-rotated q (rope_apply_bwd fused, without
  *   the intermediate bf16 rounding); dk and dv as fa_bwd (dk is with respect
- *   to the rotated k: apply rope_apply_bwd to it).
- * d = 256 returns FA_ERR_UNSUPPORTED (use rope_apply + fa_fwd). */
+ *   to the rotated k: apply rope_apply_bwd to it). */
 int fa_fwd_rope(const void* q, const void* k, const void* v, void* o,
                 float* lse, const float* inv_freq, void* q_rot, int B, int H,
                 int Hkv, int T, int d, float scale, int window,

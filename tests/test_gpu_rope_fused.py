@@ -27,6 +27,7 @@ CASES = [
     (1, 7, 1, 333, 128, 0, 0.0, 1e6),
     (1, 4, 2, 515, 128, 100, 30.0, 1e4),
     (1, 8, 4, 1024, 128, 1, 0.0, 5e5),
+    (1, 4, 2, 700, 256, 300, 50.0, 1e4),
 ]
 
 
