@@ -144,7 +144,9 @@ __global__ __launch_bounds__(64 * NW, (DK >= 192 ? 1 : 8 / NW)) void fa_bwd_dq_k
       mma_rows<DV, NS>(dp, Vt, doreg, lane);
     }
     if (!empty) {
-      // dS^T in s[] (fp32), then bf16 operands.
+      // dS^T in s[] (fp32), then bf16 operands.  Every element is computed
+      // branch-free; partial tiles then zero the invisible ones in one block
+      // (ds = 0 exactly where p = 0).
 #pragma unroll
       for (int t = 0; t < NS; ++t)
 #pragma unroll
@@ -156,15 +158,20 @@ __global__ __launch_bounds__(64 * NW, (DK >= 192 ? 1 : 8 / NW)) void fa_bwd_dq_k
             th = 0.f;
             p = fast_exp2(fmaf(s[t][i], a.scale_log2e, -lse2));
           }
-          if (!full) {
-            const int kv = kv0 + 32 * t + acc_row(i, g);
-            const bool vis = (kv <= qrow) & ((W == 0) | (kv > qrow - W));
-            p = vis ? p : 0.f;
-          }
           float ds = p * (dp[t][i] - Di);
           if (CAP) ds *= 1.f - th * th;
           s[t][i] = ds;
         }
+      if (!full) {
+#pragma unroll
+        for (int t = 0; t < NS; ++t)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int kv = kv0 + 32 * t + acc_row(i, g);
+            const bool vis = (kv <= qrow) & ((W == 0) | (kv > qrow - W));
+            s[t][i] = vis ? s[t][i] : 0.f;
+          }
+      }
       bf16x8 dsb[BKV / 16];
 #pragma unroll
       for (int c16 = 0; c16 < BKV / 16; ++c16) {
@@ -355,11 +362,6 @@ __global__ __launch_bounds__(64 * NW, (DK >= 192 ? 1 : 8 / NW)) void fa_bwd_dkdv
               th = 0.f;
               p = fast_exp2(fmaf(s[t][i], a.scale_log2e, -l4[e]));
             }
-            if (!full) {
-              const int q = q0 + qloc + e;
-              const bool vis = (q < T) & (krow <= q) & ((W == 0) | (krow > q - W));
-              p = vis ? p : 0.f;
-            }
             s[t][i] = p;
             if (DO_DK) {
               float ds = p * (dp[t][i] - d4[e]);
@@ -368,6 +370,19 @@ __global__ __launch_bounds__(64 * NW, (DK >= 192 ? 1 : 8 / NW)) void fa_bwd_dkdv
             }
           }
         }
+      // Partial tiles: zero P and dS of invisible pairs in one block (every
+      // element above is computed branch-free).
+      if (!full) {
+#pragma unroll
+        for (int t = 0; t < NS; ++t)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int q = q0 + 32 * t + acc_row(i, g);
+            const bool vis = (q < T) & (krow <= q) & ((W == 0) | (krow > q - W));
+            if (DO_DV) s[t][i] = vis ? s[t][i] : 0.f;
+            if (DO_DK) dp[t][i] = vis ? dp[t][i] : 0.f;
+          }
+      }
       bf16x8 pb[BQB / 16], dsb[BQB / 16];
 #pragma unroll
       for (int c16 = 0; c16 < BQB / 16; ++c16) {
