@@ -272,7 +272,13 @@ int attn_bwd(bool f32, const void* q, const void* k, const void* v, const void* 
 // chip several times over, at least 8 tiles of 32 keys per chunk, at most
 // kDecMaxSplits chunks.  max_keys bounds the visible keys of any sequence.
 void decode_split(int units, int max_keys, int* nsplit, int* chunk) {
-  constexpr int kTargetUnits = 4096, kMinChunk = 256, kTile = 32;
+#ifndef DEC_TARGET_UNITS
+#define DEC_TARGET_UNITS 4096
+#endif
+#ifndef DEC_MIN_CHUNK
+#define DEC_MIN_CHUNK 256
+#endif
+  constexpr int kTargetUnits = DEC_TARGET_UNITS, kMinChunk = DEC_MIN_CHUNK, kTile = 32;
   int ns = (kTargetUnits + units - 1) / units;
   ns = std::min(ns, (max_keys + kMinChunk - 1) / kMinChunk);
   ns = std::max(1, std::min(ns, fa::kDecMaxSplits));

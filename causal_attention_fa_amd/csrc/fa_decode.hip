@@ -57,11 +57,13 @@ __global__ __launch_bounds__(64 * NW, 2) void fa_decode_split_kernel(DecodeArgs 
   float* po = a.part_o + (size_t)unit * G * D;
   float* pml = a.part_ml + (size_t)unit * G * 2;
   if (start >= end) {
-    // empty chunk: m = -inf marks it; the combine never reads its O
+    // empty chunk: m = -inf, l = 0 and O = 0, so the combine can read every
+    // chunk unconditionally (its weight is 0)
     for (int i = tid; i < G; i += NT) {
       pml[2 * i] = -INFINITY;
       pml[2 * i + 1] = 0.f;
     }
+    for (int i = tid; i < G * D / 4; i += NT) ((f32x4*)po)[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     return;
   }
 
@@ -217,16 +219,27 @@ __global__ __launch_bounds__(64) void fa_decode_combine_kernel(DecodeArgs a) {
   if (has_sink) L += fast_exp2(sink2 - M);
   __syncthreads();
 
+  // O rows of 8 chunks in flight at a time (every chunk's O is written, empty
+  // ones as zeros with weight 0)
+  constexpr int U = 8;
   float acc[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) acc[e] = 0.f;
-  for (int s = 0; s < ns; ++s) {
-    const float w = wsh[s];
-    if (w != 0.f) {  // uniform; skips empty chunks, whose O is never written
-      const float* src = a.part_o + ((unit0 + s) * G + r) * D + lane * PER;
+  const float* base = a.part_o + (unit0 * G + r) * D + lane * PER;
+  for (int s0 = 0; s0 < ns; s0 += U) {
+    float wv[U], xv[U][PER];
 #pragma unroll
-      for (int e = 0; e < PER; ++e) acc[e] = fmaf(w, src[e], acc[e]);
+    for (int u = 0; u < U; ++u) {
+      const int s = min(s0 + u, ns - 1);
+      wv[u] = s0 + u < ns ? wsh[s] : 0.f;
+      const float* src = base + (size_t)s * G * D;
+#pragma unroll
+      for (int e = 0; e < PER; ++e) xv[u][e] = src[e];
     }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int e = 0; e < PER; ++e) acc[e] = fmaf(wv[u], xv[u][e], acc[e]);
   }
   const float inv = 1.f / L;
 #pragma unroll
