@@ -461,7 +461,7 @@ __global__ __launch_bounds__(64 * NW, (DK >= 192 ? 1 : 8 / NW)) void fa_bwd_dkdv
 #define BWD128_CFG 32, 8, 64, 8, 32, 8
 #endif
 #ifndef BWD192_CFG
-#define BWD192_CFG 32, 4, 64, 8, 32, 4
+#define BWD192_CFG 32, 8, 64, 8, 32, 8
 #endif
 
 template <int DK, int DV, bool CAP, int DQ_BKV, int DQ_NW, int DV_BQB, int DV_NW, int DK_BQB,
