@@ -290,6 +290,249 @@ __global__ __launch_bounds__(64 * NW, (DK >= 256 || QW > 1 ? 1 : 8 / NW)) void f
   }
 }
 
+// Head size 256: one wave cannot hold q, the 256-wide O accumulator and
+// the staging registers at two waves per SIMD, and one wave per SIMD leaves
+// the matrix pipe idle.  So waves work in pairs on the same 32 query rows:
+// wave half hf holds q[:, 128 hf .. +127], computes the partial scores over
+// its half of d, and owns output columns 128 hf .. +127.  The pair swaps
+// partial scores through LDS (one extra barrier per tile); both then add
+// them in the same order, so their scores, softmax state and P are
+// identical, and each accumulates its half of O^T += V^T P^T.
+template <int D, int BKV, bool CAP>
+__global__ __launch_bounds__(512, 1) void fa_fwd_pair_kernel(FwdArgs a) {
+  constexpr int NW = 8, NT = 64 * NW;
+  constexpr int HD = D / 2;             // columns per wave
+  constexpr int BQ = 32 * NW / 2;       // query rows per workgroup
+  constexpr int TILE = Lay<D>::template bytes<BKV>();
+  constexpr int NDB = HD / 32;          // output blocks per wave
+  constexpr int NS = BKV / 32;
+  constexpr int NC = HD / 16;           // chunks of the half contraction
+  constexpr int XS = NS * 16 * 64 * 4;  // one wave's partial scores (bytes)
+  __shared__ __attribute__((aligned(1024))) char smem[4 * TILE + NW * XS];
+  LDS_AS char* lds = (LDS_AS char*)smem;
+  LDS_AS float* xsb = (LDS_AS float*)(lds + 4 * TILE);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int pair = wave >> 1;
+  const int hf = wave & 1;
+  const int g = lane >> 5;
+  const int l32 = lane & 31;
+  const int T = a.T;
+  const int W = a.window;
+  const int G = a.H / a.Hkv;
+  const int nqb = (T + BQ - 1) / BQ;
+  const WorkItem w = decode_work(blockIdx.x, nqb, a.B, a.Hkv, G, true);
+  const int h = w.hkv * G + w.r;
+  const int q0 = w.blk * BQ;
+  const int qw0 = q0 + 32 * pair;
+  const int qrow = qw0 + l32;
+  const size_t bh = (size_t)w.b * a.H + h;
+  const size_t bkv = (size_t)w.b * a.Hkv + w.hkv;
+  const bf16* Kp = a.k + bkv * T * D;
+  const bf16* Vp = a.v + bkv * T * D;
+
+  // this wave's half of the q row: chunk c holds columns HD hf + 16c + 8g ..
+  bf16x8 qreg[NC];
+  {
+    const int qr = min(qrow, T - 1);
+    const bf16x8* src = (const bf16x8*)(a.q + (bh * T + qr) * D + HD * hf + 8 * g);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) qreg[c] = src[2 * c];
+    if (a.rope_cs) {
+      // fused RoPE on this half: chunk c holds pairs HD/2 hf + 8c + 4g + p
+      const float4* cs4 = (const float4*)(a.rope_cs + (size_t)qr * D);
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        bf16x8 x = qreg[c];
+        const int p0 = HD / 2 * hf + 8 * c + 4 * g;
+        const float4 r0 = cs4[p0 / 2], r1 = cs4[p0 / 2 + 1];
+        const float cv[4] = {r0.x, r0.z, r1.x, r1.z}, sv[4] = {r0.y, r0.w, r1.y, r1.w};
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          float xe = (float)x[2 * p], xo = (float)x[2 * p + 1];
+          rope_pair(cv[p], sv[p], xe, xo);
+          x[2 * p] = (bf16)xe;
+          x[2 * p + 1] = (bf16)xo;
+        }
+        qreg[c] = x;
+      }
+      if (a.q_rot && qrow < T) {
+        bf16x8* dst = (bf16x8*)(a.q_rot + (bh * T + qrow) * D + HD * hf + 8 * g);
+#pragma unroll
+        for (int c = 0; c < NC; ++c) dst[2 * c] = qreg[c];
+      }
+    }
+  }
+
+  int kv_lo = 0;
+  if (W > 0) kv_lo = max(0, q0 - W + 1);
+  const int t_lo = kv_lo / BKV;
+  const int kv_hi = min(T, q0 + BQ);
+  const int ntiles = (kv_hi + BKV - 1) / BKV - t_lo;
+
+  const bool has_sink = a.sinks != nullptr;
+  const float sink2 = has_sink ? a.sinks[h] * kLog2e : 0.f;
+  f32x16 oacc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
+  float m = has_sink ? sink2 : kMaxInit;
+  float lsum = (has_sink && g == 0) ? 1.f : 0.f;
+  float mxl = -INFINITY;
+  const float cexp = CAP ? 1.f : a.scale_log2e;
+
+  TileStage<D, BKV, NT> kst, vst;
+  kst.load(Kp, t_lo * BKV, T, tid);
+  vst.load(Vp, t_lo * BKV, T, tid);
+  kst.store(lds, tid);
+  vst.store(lds + 2 * TILE, tid);
+  __syncthreads();
+
+  LDS_AS float* const xs_mine = xsb + wave * (XS / 4);
+  const LDS_AS float* const xs_peer = xsb + (wave ^ 1) * (XS / 4);
+  const int qa = qw0, qb = qw0 + 31;
+  for (int j = 0; j < ntiles; ++j) {
+    const int cur = j & 1;
+    const LDS_AS char* Kt = lds + cur * TILE;
+    const LDS_AS char* Vt = lds + (2 + cur) * TILE;
+    const bool more = j + 1 < ntiles;
+    if (more) {
+      kst.load(Kp, (t_lo + j + 1) * BKV, T, tid);
+      vst.load(Vp, (t_lo + j + 1) * BKV, T, tid);
+    }
+    const int kv0 = (t_lo + j) * BKV;
+    // the same for both waves of a pair (same rows)
+    const bool empty = qa >= T || kv0 > qb || (W > 0 && kv0 + BKV - 1 <= qa - W);
+    const bool full = kv0 + BKV - 1 <= qa && (W == 0 || kv0 > qb - W);
+    f32x16 s[NS];
+    if (!empty) {
+      // partial S^T over this wave's half of d (chunks NC*hf .. of the row)
+      bf16x8 op[2][NS];
+#pragma unroll
+      for (int t = 0; t < NS; ++t) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[t][i] = 0.f;
+        op[0][t] = lds_row_operand<D>(Kt, 32 * t, NC * hf, lane);
+      }
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        if (c + 1 < NC) {
+#pragma unroll
+          for (int t = 0; t < NS; ++t)
+            op[(c + 1) & 1][t] = lds_row_operand<D>(Kt, 32 * t, NC * hf + c + 1, lane);
+        }
+#pragma unroll
+        for (int t = 0; t < NS; ++t) s[t] = mfma32(op[c & 1][t], qreg[c], s[t]);
+      }
+#pragma unroll
+      for (int t = 0; t < NS; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) xs_mine[(t * 16 + i) * 64 + lane] = s[t][i];
+    }
+    __syncthreads();
+    if (!empty) {
+      // full scores: lower half + upper half, the same order in both waves
+#pragma unroll
+      for (int t = 0; t < NS; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float peer = xs_peer[(t * 16 + i) * 64 + lane];
+          s[t][i] = hf == 0 ? s[t][i] + peer : peer + s[t][i];
+        }
+      if (CAP) {
+#pragma unroll
+        for (int t = 0; t < NS; ++t)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const float e = fast_exp2(s[t][i] * a.two_scale_over_cap_log2e);
+            s[t][i] = (1.f - 2.f * __builtin_amdgcn_rcpf(e + 1.f)) * a.cap_log2e;
+          }
+      }
+      if (!full) {
+#pragma unroll
+        for (int t = 0; t < NS; ++t)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int kv = kv0 + 32 * t + acc_row(i, g);
+            const bool vis = (kv <= qrow) & ((W == 0) | (kv > qrow - W));
+            s[t][i] = vis ? s[t][i] : -INFINITY;
+          }
+      }
+      float mt = -INFINITY;
+#pragma unroll
+      for (int t = 0; t < NS; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[t][i]);
+      mt = xor32_max(mt) * cexp;
+      if (a.max_logit) mxl = fmaxf(mxl, qrow < T ? mt : -INFINITY);
+      if (__any(mt > m + kRescaleSlack)) {
+        const float mnew = fmaxf(m, mt);
+        const float alpha = fast_exp2(m - mnew);
+        m = mnew;
+        lsum *= alpha;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+      }
+      float ps = 0.f;
+#pragma unroll
+      for (int t = 0; t < NS; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float p = fast_exp2(fmaf(s[t][i], cexp, -m));
+          s[t][i] = p;
+          ps += p;
+        }
+      lsum += ps;
+      bf16x8 pb[BKV / 16];
+#pragma unroll
+      for (int c16 = 0; c16 < BKV / 16; ++c16) {
+        float tmp[8];
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) tmp[jj] = s[c16 >> 1][8 * (c16 & 1) + jj];
+        pb[c16] = pack_bf16(tmp);
+      }
+#pragma unroll
+      for (int c16 = 0; c16 < BKV / 16; ++c16)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+          oacc[db] = mfma32(lds_tr_operand<D>(Vt, 0, c16, HD * hf + 32 * db, lane), pb[c16],
+                            oacc[db]);
+    }
+    if (more) {
+      kst.store(lds + (cur ^ 1) * TILE, tid);
+      vst.store(lds + (2 + (cur ^ 1)) * TILE, tid);
+    }
+    __syncthreads();
+  }
+
+  if (a.max_logit && hf == 0) {
+    float v = mxl;
+#pragma unroll
+    for (int off = 1; off < 32; off <<= 1) v = fmaxf(v, __shfl_xor(v, off));
+    if (lane == 0 && v > -INFINITY) atomic_max_f32(a.max_logit + bh, v * kLn2);
+  }
+  const float ltot = xor32_sum(lsum);
+  if (qrow < T) {
+    const float inv = 1.f / ltot;
+    bf16* Op = a.o + (bh * T + qrow) * D + HD * hf;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        bf16x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = (bf16)(oacc[db][4 * i4 + e] * inv);
+        *(bf16x4*)(Op + 32 * db + 8 * i4 + 4 * g) = v;
+      }
+    if (g == 0 && hf == 0) a.lse[bh * T + qrow] = (m + __log2f(ltot)) * kLn2;
+  }
+}
+
 // Tile shapes per head size (keys per tile, waves, query blocks per wave),
 // chosen by measurement on MI355X.
 #ifndef FWD128_CFG
@@ -312,6 +555,23 @@ static hipError_t launch_fwd_d(const FwdArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+#ifndef FWD256_BKV
+#define FWD256_BKV 32
+#endif
+
+template <int D, int BKV>
+static hipError_t launch_fwd_pair(const FwdArgs& a, hipStream_t stream) {
+  constexpr int BQ = 128;   // 4 pairs x 32 query rows
+  const int nqb = (a.T + BQ - 1) / BQ;
+  const dim3 grid((unsigned)nqb * a.B * a.H);
+  if (a.cap_log2e > 0.f)
+    hipLaunchKernelGGL((fa_fwd_pair_kernel<D, BKV, true>), grid, dim3(512), 0, stream, a);
+  else
+    hipLaunchKernelGGL((fa_fwd_pair_kernel<D, BKV, false>), grid, dim3(512), 0, stream, a);
+  stage_mark(stream);
+  return hipGetLastError();
+}
+
 __global__ void fill_f32_kernel(float* p, int n, float v) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = v;
@@ -327,7 +587,7 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, int d, int d_v, hipStream_t stream)
     switch (d) {
       case 64: return launch_fwd_d<64, 64, 64, 4, 1>(a, stream);
       case 128: return launch_fwd_d<128, 128, FWD128_CFG>(a, stream);
-      case 256: return launch_fwd_d<256, 256, 32, 4, 1>(a, stream);
+      case 256: return launch_fwd_pair<256, FWD256_BKV>(a, stream);
     }
   } else if (d == 192 && d_v == 128) {
     return launch_fwd_d<192, 128, FWD192_CFG>(a, stream);
