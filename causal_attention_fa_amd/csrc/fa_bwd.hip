@@ -27,16 +27,19 @@
 
 namespace fa {
 
-// log2-domain capped score and (for the chain rule) tanh itself.
+// exp2 argument of P: capped score in the log2 domain minus the row's lse
+// (log2), with the constant folded into one FMA -- cap*log2(e)*tanh(scale*x/
+// cap) with a cap (th = the tanh, for the chain rule), scale*log2(e)*x
+// without.
 template <bool CAP>
-__device__ __forceinline__ float score_log2(float x, const BwdArgs& a, float& th) {
+__device__ __forceinline__ float p_arg(float x, const BwdArgs& a, float lse2, float& th) {
   if (CAP) {
     const float e = fast_exp2(x * a.two_scale_over_cap_log2e);
     th = 1.f - 2.f * __builtin_amdgcn_rcpf(e + 1.f);
-    return th * a.cap_log2e;
+    return fmaf(th, a.cap_log2e, -lse2);
   }
   th = 0.f;
-  return x * a.scale_log2e;
+  return fmaf(x, a.scale_log2e, -lse2);
 }
 
 // ------------------------------------------------------------------ dQ pass
@@ -151,13 +154,8 @@ __global__ __launch_bounds__(64 * NW, (DK >= 192 ? 1 : 8 / NW)) void fa_bwd_dq_k
       for (int t = 0; t < NS; ++t)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          float th, p;
-          if (CAP) {
-            p = fast_exp2(score_log2<CAP>(s[t][i], a, th) - lse2);
-          } else {
-            th = 0.f;
-            p = fast_exp2(fmaf(s[t][i], a.scale_log2e, -lse2));
-          }
+          float th;
+          const float p = fast_exp2(p_arg<CAP>(s[t][i], a, lse2, th));
           float ds = p * (dp[t][i] - Di);
           if (CAP) ds *= 1.f - th * th;
           s[t][i] = ds;
@@ -355,13 +353,8 @@ __global__ __launch_bounds__(64 * NW, (DK >= 192 ? 1 : 8 / NW)) void fa_bwd_dkdv
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int i = 4 * i4 + e;
-            float th, p;
-            if (CAP) {
-              p = fast_exp2(score_log2<CAP>(s[t][i], a, th) - l4[e]);
-            } else {
-              th = 0.f;
-              p = fast_exp2(fmaf(s[t][i], a.scale_log2e, -l4[e]));
-            }
+            float th;
+            const float p = fast_exp2(p_arg<CAP>(s[t][i], a, l4[e], th));
             s[t][i] = p;
             if (DO_DK) {
               float ds = p * (dp[t][i] - d4[e]);

@@ -81,7 +81,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fa_decode_split_kernel(DecodeArgs 
   const bf16* Kp = a.kc + base;
   const bf16* Vp = a.vc + base;
   const int ntiles = (end - start + kDecBKV - 1) / kDecBKV;
-  const float cexp = CAP ? 1.f : a.scale_log2e;
+  const float cexp = CAP ? a.cap_log2e : a.scale_log2e;
 
   f32x16 oacc[NDB];
 #pragma unroll
@@ -109,7 +109,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fa_decode_split_kernel(DecodeArgs 
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const float e = fast_exp2(s[i] * a.two_scale_over_cap_log2e);
-        s[i] = (1.f - 2.f * __builtin_amdgcn_rcpf(e + 1.f)) * a.cap_log2e;
+        s[i] = 1.f - 2.f * __builtin_amdgcn_rcpf(e + 1.f);  // tanh
       }
     }
     if (kv0 + kDecBKV > end) {

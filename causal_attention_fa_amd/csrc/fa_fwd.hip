@@ -178,9 +178,10 @@ __global__ __launch_bounds__(64 * NW, (DK >= 256 || QW > 1 ? 1 : 8 / NW)) void f
             for (int u = 0; u < QW; ++u) s[u][t] = mfma32(op[c & 1][t], qreg[u][c], s[u][t]);
         }
       }
-      // Scores in the log2 domain.  Without a cap the scale is folded into
-      // the exponent's FMA below (the max of raw scores scales with it).
-      const float cexp = CAP ? 1.f : a.scale_log2e;
+      // The exponent's FMA carries the constant: scale*log2(e) on raw scores
+      // without a cap, cap*log2(e) on tanh(scale*x/cap) with one (the max
+      // scales with it either way).
+      const float cexp = CAP ? a.cap_log2e : a.scale_log2e;
       bf16x8 pb[QW][BKV / 16];
 #pragma unroll
       for (int u = 0; u < QW; ++u) {
@@ -192,7 +193,7 @@ __global__ __launch_bounds__(64 * NW, (DK >= 256 || QW > 1 ? 1 : 8 / NW)) void f
             for (int i = 0; i < 16; ++i) {
               // cap * tanh(scale*x / cap) * log2(e)
               const float e = fast_exp2(s[u][t][i] * a.two_scale_over_cap_log2e);
-              s[u][t][i] = (1.f - 2.f * __builtin_amdgcn_rcpf(e + 1.f)) * a.cap_log2e;
+              s[u][t][i] = 1.f - 2.f * __builtin_amdgcn_rcpf(e + 1.f);  // tanh
             }
         }
         if (!full) {
@@ -382,7 +383,7 @@ __global__ __launch_bounds__(512, 1) void fa_fwd_pair_kernel(FwdArgs a) {
   float m = has_sink ? sink2 : kMaxInit;
   float lsum = (has_sink && g == 0) ? 1.f : 0.f;
   float mxl = -INFINITY;
-  const float cexp = CAP ? 1.f : a.scale_log2e;
+  const float cexp = CAP ? a.cap_log2e : a.scale_log2e;
 
   TileStage<D, BKV, NT> kst, vst;
   kst.load(Kp, t_lo * BKV, T, tid);
@@ -448,7 +449,7 @@ __global__ __launch_bounds__(512, 1) void fa_fwd_pair_kernel(FwdArgs a) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const float e = fast_exp2(s[t][i] * a.two_scale_over_cap_log2e);
-            s[t][i] = (1.f - 2.f * __builtin_amdgcn_rcpf(e + 1.f)) * a.cap_log2e;
+            s[t][i] = 1.f - 2.f * __builtin_amdgcn_rcpf(e + 1.f);  // tanh
           }
       }
       if (!full) {
