@@ -22,6 +22,8 @@
 //      K and V stay in registers as the B operands of S = Q K^T and
 //      dP = dO V^T, and dV^T += dO^T P, dK^T += Q^T dS take dO^T and Q^T
 //      from the natural tiles through the LDS transpose read.
+#include <type_traits>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -223,7 +225,7 @@ __global__ __launch_bounds__(64 * NW, (DK >= 192 ? 1 : 8 / NW)) void fa_bwd_dq_k
 // that two waves per SIMD allow, so the pass runs as two launches instead:
 // MODE 1 accumulates dV only (needs S, P), MODE 2 dK only (needs S, dP,
 // dS) -- one extra S = Q K^T product buys twice the occupancy.
-template <int DK, int DV, int BQB, int NW, bool CAP, int MODE>
+template <int DK, int DV, int BQB, int NW, bool CAP, int MODE, int PF>
 __global__ __launch_bounds__(64 * NW, (DK >= 192 ? 1 : 8 / NW)) void fa_bwd_dkdv_kernel(BwdArgs a) {
   constexpr bool DO_DV = MODE != 2;
   constexpr bool DO_DK = MODE != 1;
@@ -283,133 +285,182 @@ __global__ __launch_bounds__(64 * NW, (DK >= 192 ? 1 : 8 / NW)) void fa_bwd_dkdv
     for (int db = 0; db < (DO_DV ? NDBV : 1); ++db) dvacc[db][i] = 0.f;
   }
 
-  TileStage<DK, BQB, NT> qst;
-  TileStage<DV, BQB, NT> dost;
-  float stv = 0.f;
+  // Q, dO tiles and their row statistics run PF (1 or 2) iterations ahead:
+  // tile t is loaded into register set t % 2 at the top of iteration t - PF
+  // and written to LDS buffer t % 2 at the end of iteration t - 1 (the loop
+  // is unrolled by two so both indices are compile-time constants).  Two
+  // ahead hides more load latency but holds a second register set.
+  TileStage<DK, BQB, NT> qst[2];
+  TileStage<DV, BQB, NT> dost[2];
+  float stv[2] = {0.f, 0.f};
   // Iteration it visits query head (hkv*G + hi) and query tile ti, with
   // it = hi * nqt + ti; (hi, ti) advance incrementally (no integer division
   // in the loop).
-  auto stage_stats = [&](int hi, int ti) {
+  auto stage_stats = [&](int hi, int ti) -> float {
     const int hh = w.hkv * G + hi;
     const int q0 = (qt_lo + ti) * BQB;
     const size_t bhh = (size_t)w.b * a.H + hh;
+    float v = 0.f;
     if (tid < 2 * BQB) {
       int qq = q0 + (tid % BQB);
       qq = qq < T ? qq : T - 1;
-      stv = tid < BQB ? a.lse[bhh * T + qq] * kLog2e : a.Dst[bhh * T + qq];
+      v = tid < BQB ? a.lse[bhh * T + qq] * kLog2e : a.Dst[bhh * T + qq];
     }
+    return v;
   };
   auto tile_src = [&](int hi, const bf16* base, int dd) {
     return base + ((size_t)w.b * a.H + w.hkv * G + hi) * T * dd;
   };
   auto tile_q0 = [&](int ti) { return (qt_lo + ti) * BQB; };
+  auto advance = [&](int& hi, int& ti) {
+    if (++ti == nqt) {
+      ti = 0;
+      ++hi;
+    }
+  };
+  auto load_into = [&](auto r_c, int hi, int ti) __attribute__((always_inline)) {
+    constexpr int r = decltype(r_c)::value;
+    qst[r].load(tile_src(hi, a.q, DK), tile_q0(ti), T, tid);
+    dost[r].load(tile_src(hi, a.dO, DV), tile_q0(ti), T, tid);
+    stv[r] = stage_stats(hi, ti);
+  };
+  auto store_from = [&](auto r_c) __attribute__((always_inline)) {
+    constexpr int r = decltype(r_c)::value;
+    qst[r].store(lds + r * TILE_Q, tid);
+    dost[r].store(olds + r * TILE_O, tid);
+    if (tid < 2 * BQB) *(LDS_AS float*)(stat + r * 2 * STAT + tid * 4) = stv[r];
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
 
-  qst.load(tile_src(0, a.q, DK), tile_q0(0), T, tid);
-  dost.load(tile_src(0, a.dO, DV), tile_q0(0), T, tid);
-  stage_stats(0, 0);
-  qst.store(lds, tid);
-  dost.store(olds, tid);
-  if (tid < 2 * BQB) *(LDS_AS float*)(stat + tid * 4) = stv;
+  load_into(I0{}, 0, 0);
+  store_from(I0{});
+  int h1 = 0, t1 = 0;
+  advance(h1, t1);   // tile 1
+  int h2 = h1, t2 = t1;
+  advance(h2, t2);   // tile 2
+  if (PF == 2 && niter > 1) load_into(I1{}, h1, t1);
   __syncthreads();
 
   const int ka = kw0, kb = kw0 + 31;
-  int hi_cur = 0, ti_cur = 0;
-  for (int it = 0; it < niter; ++it) {
-    int hi_nx = hi_cur, ti_nx = ti_cur + 1;
-    if (ti_nx == nqt) {
-      ti_nx = 0;
-      ++hi_nx;
-    }
-    const int cur = it & 1;
-    const LDS_AS char* Qt = lds + cur * TILE_Q;
-    const LDS_AS char* dOt = olds + cur * TILE_O;
-    const LDS_AS float* lse2t = (const LDS_AS float*)(stat + cur * 2 * STAT);
-    const LDS_AS float* Dt = lse2t + BQB;
-    const bool more = it + 1 < niter;
-    // next Q, dO tiles and row statistics: loads now, LDS stores at the end
-    if (more) {
-      qst.load(tile_src(hi_nx, a.q, DK), tile_q0(ti_nx), T, tid);
-      dost.load(tile_src(hi_nx, a.dO, DV), tile_q0(ti_nx), T, tid);
-      stage_stats(hi_nx, ti_nx);
-    }
-    const int q0 = tile_q0(ti_cur);
-    const bool empty = ka >= T || q0 + BQB - 1 < ka || (W > 0 && q0 - kb >= W);
-    const bool full = q0 >= kb && q0 + BQB <= T && (W == 0 || q0 + BQB - 1 - ka < W);
-    f32x16 s[NS], dp[NS];
-    if (!empty) {
-      mma_rows<DK, NS>(s, Qt, kreg, lane);
-      if (DO_DK) mma_rows<DV, NS>(dp, dOt, vreg, lane);
-    }
-    if (!empty) {
-      // S, dP: lane = key row, accumulator i = query row 32t + acc_row(i, g).
-      // P into s[], dS into dp[].
-#pragma unroll
-      for (int t = 0; t < NS; ++t)
-#pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          const int qloc = 32 * t + 8 * i4 + 4 * g;
-          const f32x4 l4 = *(const LDS_AS f32x4*)(lse2t + qloc);
-          const f32x4 d4 = *(const LDS_AS f32x4*)(Dt + qloc);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int i = 4 * i4 + e;
-            float th;
-            const float p = fast_exp2(p_arg<CAP>(s[t][i], a, l4[e], th));
-            s[t][i] = p;
-            if (DO_DK) {
-              float ds = p * (dp[t][i] - d4[e]);
-              if (CAP) ds *= 1.f - th * th;
-              dp[t][i] = ds;
+  int hc = 0, tc = 0;   // tile of the current iteration
+  // one query tile: S (and dP) against this workgroup's keys, P (and dS),
+  // then dV (or dK) accumulation
+  auto compute = [&](const LDS_AS char* Qt, const LDS_AS char* dOt, const LDS_AS float* lse2t,
+                     const LDS_AS float* Dt, const int q0) __attribute__((always_inline)) {
+        const bool empty = ka >= T || q0 + BQB - 1 < ka || (W > 0 && q0 - kb >= W);
+      const bool full = q0 >= kb && q0 + BQB <= T && (W == 0 || q0 + BQB - 1 - ka < W);
+      f32x16 s[NS], dp[NS];
+      if (!empty) {
+        mma_rows<DK, NS>(s, Qt, kreg, lane);
+        if (DO_DK) mma_rows<DV, NS>(dp, dOt, vreg, lane);
+      }
+      if (!empty) {
+        // S, dP: lane = key row, accumulator i = query row 32t + acc_row(i, g).
+        // P into s[], dS into dp[].
+  #pragma unroll
+        for (int t = 0; t < NS; ++t)
+  #pragma unroll
+          for (int i4 = 0; i4 < 4; ++i4) {
+            const int qloc = 32 * t + 8 * i4 + 4 * g;
+            const f32x4 l4 = *(const LDS_AS f32x4*)(lse2t + qloc);
+            const f32x4 d4 = *(const LDS_AS f32x4*)(Dt + qloc);
+  #pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int i = 4 * i4 + e;
+              float th;
+              const float p = fast_exp2(p_arg<CAP>(s[t][i], a, l4[e], th));
+              s[t][i] = p;
+              if (DO_DK) {
+                float ds = p * (dp[t][i] - d4[e]);
+                if (CAP) ds *= 1.f - th * th;
+                dp[t][i] = ds;
+              }
             }
           }
+        // Partial tiles: zero P and dS of invisible pairs in one block (every
+        // element above is computed branch-free).
+        if (!full) {
+  #pragma unroll
+          for (int t = 0; t < NS; ++t)
+  #pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int q = q0 + 32 * t + acc_row(i, g);
+              const bool vis = (q < T) & (krow <= q) & ((W == 0) | (krow > q - W));
+              if (DO_DV) s[t][i] = vis ? s[t][i] : 0.f;
+              if (DO_DK) dp[t][i] = vis ? dp[t][i] : 0.f;
+            }
         }
-      // Partial tiles: zero P and dS of invisible pairs in one block (every
-      // element above is computed branch-free).
-      if (!full) {
-#pragma unroll
-        for (int t = 0; t < NS; ++t)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int q = q0 + 32 * t + acc_row(i, g);
-            const bool vis = (q < T) & (krow <= q) & ((W == 0) | (krow > q - W));
-            if (DO_DV) s[t][i] = vis ? s[t][i] : 0.f;
-            if (DO_DK) dp[t][i] = vis ? dp[t][i] : 0.f;
+        bf16x8 pb[BQB / 16], dsb[BQB / 16];
+  #pragma unroll
+        for (int c16 = 0; c16 < BQB / 16; ++c16) {
+          float tp[8], td[8];
+  #pragma unroll
+          for (int jj = 0; jj < 8; ++jj) {
+            tp[jj] = s[c16 >> 1][8 * (c16 & 1) + jj];
+            td[jj] = dp[c16 >> 1][8 * (c16 & 1) + jj];
           }
-      }
-      bf16x8 pb[BQB / 16], dsb[BQB / 16];
-#pragma unroll
-      for (int c16 = 0; c16 < BQB / 16; ++c16) {
-        float tp[8], td[8];
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
-          tp[jj] = s[c16 >> 1][8 * (c16 & 1) + jj];
-          td[jj] = dp[c16 >> 1][8 * (c16 & 1) + jj];
+          if (DO_DV) pb[c16] = pack_bf16(tp);
+          if (DO_DK) dsb[c16] = pack_bf16(td);
         }
-        if (DO_DV) pb[c16] = pack_bf16(tp);
-        if (DO_DK) dsb[c16] = pack_bf16(td);
-      }
-#pragma unroll
-      for (int c16 = 0; c16 < BQB / 16; ++c16) {
-        if (DO_DV) {
-#pragma unroll
-          for (int db = 0; db < NDBV; ++db)
-            dvacc[db] = mfma32(lds_tr_operand<DV>(dOt, 0, c16, 32 * db, lane), pb[c16], dvacc[db]);
-        }
-        if (DO_DK) {
-#pragma unroll
-          for (int db = 0; db < NDBK; ++db)
-            dkacc[db] = mfma32(lds_tr_operand<DK>(Qt, 0, c16, 32 * db, lane), dsb[c16], dkacc[db]);
+  #pragma unroll
+        for (int c16 = 0; c16 < BQB / 16; ++c16) {
+          if (DO_DV) {
+  #pragma unroll
+            for (int db = 0; db < NDBV; ++db)
+              dvacc[db] = mfma32(lds_tr_operand<DV>(dOt, 0, c16, 32 * db, lane), pb[c16], dvacc[db]);
+          }
+          if (DO_DK) {
+  #pragma unroll
+            for (int db = 0; db < NDBK; ++db)
+              dkacc[db] = mfma32(lds_tr_operand<DK>(Qt, 0, c16, 32 * db, lane), dsb[c16], dkacc[db]);
+          }
         }
       }
+  };
+
+  if constexpr (PF == 2) {
+    auto step = [&](auto p_c, const int it) __attribute__((always_inline)) {
+      constexpr int P = decltype(p_c)::value;
+      if (it + 2 < niter) load_into(p_c, h2, t2);
+      const LDS_AS float* lse2t = (const LDS_AS float*)(stat + P * 2 * STAT);
+      compute(lds + P * TILE_Q, olds + P * TILE_O, lse2t, lse2t + BQB, tile_q0(tc));
+      if (it + 1 < niter) store_from(std::integral_constant<int, 1 - P>{});
+      __syncthreads();
+      hc = h1;
+      tc = t1;
+      h1 = h2;
+      t1 = t2;
+      advance(h2, t2);
+    };
+    int it = 0;
+    for (; it + 1 < niter; it += 2) {
+      step(I0{}, it);
+      step(I1{}, it + 1);
     }
-    if (more) {
-      qst.store(lds + (cur ^ 1) * TILE_Q, tid);
-      dost.store(olds + (cur ^ 1) * TILE_O, tid);
-      if (tid < 2 * BQB) *(LDS_AS float*)(stat + (cur ^ 1) * 2 * STAT + tid * 4) = stv;
+    if (it < niter) step(I0{}, it);
+  } else {
+    // one tile ahead, one register set, LDS buffer chosen at run time
+    for (int it = 0; it < niter; ++it) {
+      const int cur = it & 1;
+      const bool more = it + 1 < niter;
+      if (more) {
+        qst[0].load(tile_src(h1, a.q, DK), tile_q0(t1), T, tid);
+        dost[0].load(tile_src(h1, a.dO, DV), tile_q0(t1), T, tid);
+        stv[0] = stage_stats(h1, t1);
+      }
+      const LDS_AS float* lse2t = (const LDS_AS float*)(stat + cur * 2 * STAT);
+      compute(lds + cur * TILE_Q, olds + cur * TILE_O, lse2t, lse2t + BQB, tile_q0(tc));
+      if (more) {
+        qst[0].store(lds + (cur ^ 1) * TILE_Q, tid);
+        dost[0].store(olds + (cur ^ 1) * TILE_O, tid);
+        if (tid < 2 * BQB) *(LDS_AS float*)(stat + (cur ^ 1) * 2 * STAT + tid * 4) = stv[0];
+      }
+      __syncthreads();
+      hc = h1;
+      tc = t1;
+      advance(h1, t1);
     }
-    __syncthreads();
-    hi_cur = hi_nx;
-    ti_cur = ti_nx;
   }
 
   if (krow < T) {
@@ -457,6 +508,15 @@ __global__ __launch_bounds__(64 * NW, (DK >= 192 ? 1 : 8 / NW)) void fa_bwd_dkdv
 #define BWD192_CFG 32, 8, 64, 8, 32, 8
 #endif
 
+// Prefetch depth of the dV / dK passes, chosen by measurement: two tiles
+// ahead where the second register set fits without spilling.
+#ifndef BWD_PF_DV
+#define BWD_PF_DV(DK) ((DK) <= 128 ? 2 : 1)
+#endif
+#ifndef BWD_PF_DK
+#define BWD_PF_DK(DK) ((DK) == 192 ? 1 : 2)
+#endif
+
 template <int DK, int DV, bool CAP, int DQ_BKV, int DQ_NW, int DV_BQB, int DV_NW, int DK_BQB,
           int DK_NW>
 static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
@@ -467,13 +527,15 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 vgrid((unsigned)((a.T + 32 * DV_NW - 1) / (32 * DV_NW)) * a.B * a.Hkv);
-  hipLaunchKernelGGL((fa_bwd_dkdv_kernel<DK, DV, DV_BQB, DV_NW, CAP, 1>), vgrid, dim3(64 * DV_NW), 0,
+  hipLaunchKernelGGL((fa_bwd_dkdv_kernel<DK, DV, DV_BQB, DV_NW, CAP, 1, BWD_PF_DV(DK)>), vgrid,
+                     dim3(64 * DV_NW), 0,
                      stream, a);
   stage_mark(stream);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 kgrid((unsigned)((a.T + 32 * DK_NW - 1) / (32 * DK_NW)) * a.B * a.Hkv);
-  hipLaunchKernelGGL((fa_bwd_dkdv_kernel<DK, DV, DK_BQB, DK_NW, CAP, 2>), kgrid, dim3(64 * DK_NW), 0,
+  hipLaunchKernelGGL((fa_bwd_dkdv_kernel<DK, DV, DK_BQB, DK_NW, CAP, 2, BWD_PF_DK(DK)>), kgrid,
+                     dim3(64 * DK_NW), 0,
                      stream, a);
   stage_mark(stream);
   return hipGetLastError();
