@@ -45,7 +45,7 @@ __device__ __forceinline__ float p_arg(float x, const BwdArgs& a, float lse2, fl
 }
 
 // ------------------------------------------------------------------ dQ pass
-template <int DK, int DV, int BKV, int NW, bool CAP>
+template <int DK, int DV, int BKV, int NW, bool CAP, int PF>
 __global__ __launch_bounds__(64 * NW, (DK >= 192 ? 1 : 8 / NW)) void fa_bwd_dq_kernel(BwdArgs a) {
   constexpr int NT = 64 * NW;
   constexpr int BQ = 32 * NW;
@@ -119,78 +119,107 @@ __global__ __launch_bounds__(64 * NW, (DK >= 192 ? 1 : 8 / NW)) void fa_bwd_dq_k
 #pragma unroll
     for (int i = 0; i < 16; ++i) dqacc[db][i] = 0.f;
 
-  TileStage<DK, BKV, NT> kst;
-  TileStage<DV, BKV, NT> vst;
+  // K, V tiles run PF (1 or 2) iterations ahead: tile j is loaded into
+  // register set j % 2 at the top of iteration j - PF and written to LDS
+  // buffer j % 2 at the end of iteration j - 1 (two ahead: loop unrolled by
+  // two so both indices are compile-time constants).
+  TileStage<DK, BKV, NT> kst[PF];
+  TileStage<DV, BKV, NT> vst[PF];
   LDS_AS char* const vlds = lds + 2 * TILE_K;
-  kst.load(Kp, t_lo * BKV, T, tid);
-  vst.load(Vp, t_lo * BKV, T, tid);
-  kst.store(lds, tid);
-  vst.store(vlds, tid);
+  auto load_into = [&](auto r_c, int tile) __attribute__((always_inline)) {
+    constexpr int r = decltype(r_c)::value;
+    kst[r].load(Kp, tile * BKV, T, tid);
+    vst[r].load(Vp, tile * BKV, T, tid);
+  };
+  auto store_from = [&](auto r_c, int buf) __attribute__((always_inline)) {
+    constexpr int r = decltype(r_c)::value;
+    kst[r].store(lds + buf * TILE_K, tid);
+    vst[r].store(vlds + buf * TILE_V, tid);
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  load_into(I0{}, t_lo);
+  store_from(I0{}, 0);
+  if constexpr (PF == 2) {
+    if (ntiles > 1) load_into(I1{}, t_lo + 1);
+  }
   __syncthreads();
 
   const int qa = qw0, qb = qw0 + 31;
-  for (int j = 0; j < ntiles; ++j) {
-    const int cur = j & 1;
-    const LDS_AS char* Kt = lds + cur * TILE_K;
-    const LDS_AS char* Vt = vlds + cur * TILE_V;
-    const bool more = j + 1 < ntiles;
-    const int nrow = (t_lo + j + 1) * BKV;
-    // next K, V tiles: loads now, LDS stores after this tile's MFMAs
-    if (more) {
-      kst.load(Kp, nrow, T, tid);
-      vst.load(Vp, nrow, T, tid);
-    }
-    const int kv0 = (t_lo + j) * BKV;
-    const bool empty = qa >= T || kv0 > qb || (W > 0 && kv0 + BKV - 1 <= qa - W);
-    const bool full = kv0 + BKV - 1 <= qa && (W == 0 || kv0 > qb - W);
-    f32x16 s[NS], dp[NS];
-    if (!empty) {
-      mma_rows<DK, NS>(s, Kt, qreg, lane);
-      mma_rows<DV, NS>(dp, Vt, doreg, lane);
-    }
-    if (!empty) {
-      // dS^T in s[] (fp32), then bf16 operands.  Every element is computed
-      // branch-free; partial tiles then zero the invisible ones in one block
-      // (ds = 0 exactly where p = 0).
-#pragma unroll
-      for (int t = 0; t < NS; ++t)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float th;
-          const float p = fast_exp2(p_arg<CAP>(s[t][i], a, lse2, th));
-          float ds = p * (dp[t][i] - Di);
-          if (CAP) ds *= 1.f - th * th;
-          s[t][i] = ds;
-        }
-      if (!full) {
-#pragma unroll
+  // one key tile: S, dP, dS, then dQ^T += K^T dS^T
+  auto compute = [&](const LDS_AS char* Kt, const LDS_AS char* Vt, const int kv0)
+                     __attribute__((always_inline)) {
+      const bool empty = qa >= T || kv0 > qb || (W > 0 && kv0 + BKV - 1 <= qa - W);
+      const bool full = kv0 + BKV - 1 <= qa && (W == 0 || kv0 > qb - W);
+      f32x16 s[NS], dp[NS];
+      if (!empty) {
+        mma_rows<DK, NS>(s, Kt, qreg, lane);
+        mma_rows<DV, NS>(dp, Vt, doreg, lane);
+      }
+      if (!empty) {
+        // dS^T in s[] (fp32), then bf16 operands.  Every element is computed
+        // branch-free; partial tiles then zero the invisible ones in one block
+        // (ds = 0 exactly where p = 0).
+  #pragma unroll
         for (int t = 0; t < NS; ++t)
-#pragma unroll
+  #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            const int kv = kv0 + 32 * t + acc_row(i, g);
-            const bool vis = (kv <= qrow) & ((W == 0) | (kv > qrow - W));
-            s[t][i] = vis ? s[t][i] : 0.f;
+            float th;
+            const float p = fast_exp2(p_arg<CAP>(s[t][i], a, lse2, th));
+            float ds = p * (dp[t][i] - Di);
+            if (CAP) ds *= 1.f - th * th;
+            s[t][i] = ds;
           }
+        if (!full) {
+  #pragma unroll
+          for (int t = 0; t < NS; ++t)
+  #pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int kv = kv0 + 32 * t + acc_row(i, g);
+              const bool vis = (kv <= qrow) & ((W == 0) | (kv > qrow - W));
+              s[t][i] = vis ? s[t][i] : 0.f;
+            }
+        }
+        bf16x8 dsb[BKV / 16];
+  #pragma unroll
+        for (int c16 = 0; c16 < BKV / 16; ++c16) {
+          float tmp[8];
+  #pragma unroll
+          for (int jj = 0; jj < 8; ++jj) tmp[jj] = s[c16 >> 1][8 * (c16 & 1) + jj];
+          dsb[c16] = pack_bf16(tmp);
+        }
+  #pragma unroll
+        for (int c16 = 0; c16 < BKV / 16; ++c16)
+  #pragma unroll
+          for (int db = 0; db < NDB; ++db)
+            dqacc[db] = mfma32(lds_tr_operand<DK>(Kt, 0, c16, 32 * db, lane), dsb[c16], dqacc[db]);
       }
-      bf16x8 dsb[BKV / 16];
-#pragma unroll
-      for (int c16 = 0; c16 < BKV / 16; ++c16) {
-        float tmp[8];
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) tmp[jj] = s[c16 >> 1][8 * (c16 & 1) + jj];
-        dsb[c16] = pack_bf16(tmp);
-      }
-#pragma unroll
-      for (int c16 = 0; c16 < BKV / 16; ++c16)
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-          dqacc[db] = mfma32(lds_tr_operand<DK>(Kt, 0, c16, 32 * db, lane), dsb[c16], dqacc[db]);
+  };
+
+  if constexpr (PF == 2) {
+    auto step = [&](auto p_c, const int j) __attribute__((always_inline)) {
+      constexpr int P = decltype(p_c)::value;
+      if (j + 2 < ntiles) load_into(p_c, t_lo + j + 2);
+      compute(lds + P * TILE_K, vlds + P * TILE_V, (t_lo + j) * BKV);
+      if (j + 1 < ntiles) store_from(std::integral_constant<int, 1 - P>{}, 1 - P);
+      __syncthreads();
+    };
+    int j = 0;
+    for (; j + 1 < ntiles; j += 2) {
+      step(I0{}, j);
+      step(I1{}, j + 1);
     }
-    if (more) {
-      kst.store(lds + (cur ^ 1) * TILE_K, tid);
-      vst.store(vlds + (cur ^ 1) * TILE_V, tid);
+    if (j < ntiles) step(I0{}, j);
+  } else {
+    for (int j = 0; j < ntiles; ++j) {
+      const int cur = j & 1;
+      const bool more = j + 1 < ntiles;
+      // next K, V tiles: loads now, LDS stores after this tile's MFMAs
+      if (more) load_into(I0{}, t_lo + j + 1);
+      compute(lds + cur * TILE_K, vlds + cur * TILE_V, (t_lo + j) * BKV);
+      if (more) store_from(I0{}, cur ^ 1);
+      __syncthreads();
     }
-    __syncthreads();
   }
 
   if (qrow < T) {
@@ -290,9 +319,9 @@ __global__ __launch_bounds__(64 * NW, (DK >= 192 ? 1 : 8 / NW)) void fa_bwd_dkdv
   // and written to LDS buffer t % 2 at the end of iteration t - 1 (the loop
   // is unrolled by two so both indices are compile-time constants).  Two
   // ahead hides more load latency but holds a second register set.
-  TileStage<DK, BQB, NT> qst[2];
-  TileStage<DV, BQB, NT> dost[2];
-  float stv[2] = {0.f, 0.f};
+  TileStage<DK, BQB, NT> qst[PF];
+  TileStage<DV, BQB, NT> dost[PF];
+  float stv[PF] = {};
   // Iteration it visits query head (hkv*G + hi) and query tile ti, with
   // it = hi * nqt + ti; (hi, ti) advance incrementally (no integer division
   // in the loop).
@@ -339,7 +368,9 @@ __global__ __launch_bounds__(64 * NW, (DK >= 192 ? 1 : 8 / NW)) void fa_bwd_dkdv
   advance(h1, t1);   // tile 1
   int h2 = h1, t2 = t1;
   advance(h2, t2);   // tile 2
-  if (PF == 2 && niter > 1) load_into(I1{}, h1, t1);
+  if constexpr (PF == 2) {
+    if (niter > 1) load_into(I1{}, h1, t1);
+  }
   __syncthreads();
 
   const int ka = kw0, kb = kw0 + 31;
@@ -516,12 +547,16 @@ __global__ __launch_bounds__(64 * NW, (DK >= 192 ? 1 : 8 / NW)) void fa_bwd_dkdv
 #ifndef BWD_PF_DK
 #define BWD_PF_DK(DK) ((DK) == 192 ? 1 : 2)
 #endif
+#ifndef BWD_PF_DQ
+#define BWD_PF_DQ(DK) ((DK) <= 128 ? 2 : 1)
+#endif
 
 template <int DK, int DV, bool CAP, int DQ_BKV, int DQ_NW, int DV_BQB, int DV_NW, int DK_BQB,
           int DK_NW>
 static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   const int nqb = (a.T + 32 * DQ_NW - 1) / (32 * DQ_NW);
-  hipLaunchKernelGGL((fa_bwd_dq_kernel<DK, DV, DQ_BKV, DQ_NW, CAP>), dim3((unsigned)nqb * a.B * a.H),
+  hipLaunchKernelGGL((fa_bwd_dq_kernel<DK, DV, DQ_BKV, DQ_NW, CAP, BWD_PF_DQ(DK)>),
+                     dim3((unsigned)nqb * a.B * a.H),
                      dim3(64 * DQ_NW), 0, stream, a);
   stage_mark(stream);
   hipError_t e = hipGetLastError();
