@@ -167,6 +167,8 @@ def main():
     ap.add_argument("--decode-workload", default="qwen25-decode",
                     help="decode workload timed after the main step ('none' to skip)")
     ap.add_argument("--decode-iters", type=int, default=20)
+    ap.add_argument("--decode-only", action="store_true",
+                    help="time only fa_decode on --decode-workload (one JSON line in GB/s)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="CPU-baseline budget: oracle heads are timed until this many "
                          "seconds have passed (0: skip)")
@@ -188,6 +190,20 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"calibration_copy_bytes": n * 4, "launches": 5}))
+        return
+
+    if args.decode_only:
+        r = decode_leg(args.decode_workload, args.decode_iters, torch.device("cuda:0"))
+        print(json.dumps({"metric": "decode attention HBM throughput (algorithmic bytes), 1xMI355X",
+                          "value": r["gbs"], "unit": "GB/s", "n_gpus": 1,
+                          "steps": args.decode_iters, "warmup": 3, "ms_per_step": r["ms"],
+                          "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+                          "dtype": "bf16", "data": "synthetic",
+                          "config": {"workload": r["workload"]},
+                          "roofline": {"bound": "hbm", "achieved": r["gbs"],
+                                       "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                       "frac": r["frac_hbm"], "traffic": None},
+                          "decode": r}), flush=True)
         return
 
     w = synth.WORKLOADS[args.workload]
