@@ -1,7 +1,7 @@
 """GPU parity of fa_fwd / fa_bwd (and the fp32 twins) against the float64
 oracle, element by element, at sizes that span several tiles and ragged
 tails, with the edge cases of the method: T = 1, windows 1, 2, T-1, T, 2T,
-window edges inside a tile, GQA ratios 1..8, H = 7, softcap on and off,
+window edges inside a tile, GQA ratios 1..16, H = 7, softcap on and off,
 d = 64, 128, 256.  Outputs are NaN-poisoned first so an unwritten element
 fails; each case also runs twice and must be bitwise identical (no atomics
 on this path)."""
@@ -36,6 +36,8 @@ BF16_CASES = [
     (1, 8, 8, 1000, 64, 300, 0.0, 1.0),
     (1, 8, 1, 384, 128, 128, 50.0, 2.0),
     (1, 4, 2, 640, 256, 257, 0.0, 1.0),
+    (1, 16, 1, 700, 64, 0, 0.0, 1.0),
+    (1, 32, 2, 333, 128, 100, 20.0, 2.0),
 ]
 
 F32_CASES = [

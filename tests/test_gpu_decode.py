@@ -4,7 +4,7 @@ split along the cache) against the float64 decode oracle.
 Small cases compare every output; the cache positions at or past each
 sequence's length are filled with NaN, so any read of them fails.  Lengths
 cover 0, 1, a tile edge +-1 and S; windows 1, inside a tile and past S;
-GQA ratios 1..8; d 64, 128, 256; cap on/off; sinks; several chunks.  The
+GQA ratios 1..32; d 64, 128, 256; cap on/off; sinks; several chunks.  The
 full-size qwen25-decode workload is checked on sampled sequences."""
 import math
 
@@ -30,6 +30,9 @@ CASES = [
     (1, 4, 2, 5000, 256, 4096, 50.0, True, [4999]),
     (1, 32, 8, 4100, 128, 0, 0.0, False, [4100]),
     (2, 2, 1, 3000, 64, 5000, 0.0, False, [3000, 2999]),
+    (1, 32, 1, 600, 128, 0, 0.0, False, [600]),
+    (2, 64, 2, 300, 64, 100, 20.0, True, [300, 150]),
+    (1, 32, 1, 2000, 256, 0, 50.0, False, [1999]),
 ]
 
 

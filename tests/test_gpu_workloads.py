@@ -145,6 +145,19 @@ def test_workload_sampled_parity(name, softcap):
         _compare_groups(w, got, q, k, v, do, softcap)
 
 
+def test_long_sequence_sampled_parity():
+    """T = 16384 (twice the longest workload), GQA 8:1, a window that is not
+    a multiple of any tile: the 64-bit offsets, the tile bounds of long
+    loops and the dK/dV head loop, against the oracle on sampled rows."""
+    w = synth.Workload("long", "bf16", 1, 8, 1, 16384, 128, window=5000, seed=77)
+    say(f"[long] B{w.B} H{w.H}/{w.Hkv} T{w.T} d{w.d} W{w.window}")
+    q, k, v, do = synth.draw(w)
+    got = _gpu_path(w, q, k, v, do, 0.0)
+    for n in ("o", "lse", "dq", "dk", "dv"):
+        assert torch.isfinite(got[n]).all(), f"{n} has unwritten/non-finite entries"
+    _compare_groups(w, got, q, k, v, do, 0.0)
+
+
 def test_forge_f32_every_element():
     w = synth.WORKLOADS["forge-f32"]
     say(f"[workload] forge-f32 B{w.B} H{w.H} T{w.T} d{w.d}")
