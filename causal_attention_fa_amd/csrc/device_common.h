@@ -220,6 +220,123 @@ __device__ __forceinline__ void mma_rows(f32x16 (&acc)[NS], const LDS_AS char* t
   }
 }
 
+// Two independent products in one pass, their MFMAs alternating:
+//   accA[t] = sum_c rows(tileA, 32t, c) bregA[c]   (DA/16 chunks)
+//   accB[t] = sum_c rows(tileB, 32t, c) bregB[c]   (DB/16 chunks)
+// LDS reads run PD chunks ahead through a ring of PD+1 operand sets: an LDS
+// read takes about two MFMA durations to return, so reading just one chunk
+// ahead stalls every MFMA.  The scheduling barrier after each chunk keeps
+// the compiler from sinking the reads back next to their MFMAs.  PD = 0
+// leaves the two products to the compiler's schedule (mma_rows each), which
+// needs fewer registers.
+template <int DA, int DB, int NS, int PD>
+__device__ __forceinline__ void mma_rows2(f32x16 (&accA)[NS], const LDS_AS char* tileA,
+                                          const bf16x8 (&bregA)[DA / 16], f32x16 (&accB)[NS],
+                                          const LDS_AS char* tileB,
+                                          const bf16x8 (&bregB)[DB / 16], int lane) {
+  if constexpr (PD == 0) {
+    // no pinned order: the compiler schedules (fewer live registers)
+    mma_rows<DA, NS>(accA, tileA, bregA, lane);
+    mma_rows<DB, NS>(accB, tileB, bregB, lane);
+    return;
+  }
+  constexpr int NA = DA / 16, NB = DB / 16, NC = NA > NB ? NA : NB, R = PD + 1;
+  bf16x8 opA[R][NS], opB[R][NS];
+  auto fetch = [&](int c) __attribute__((always_inline)) {
+#pragma unroll
+    for (int t = 0; t < NS; ++t) {
+      if (c < NA) opA[c % R][t] = lds_row_operand<DA>(tileA, 32 * t, c, lane);
+      if (c < NB) opB[c % R][t] = lds_row_operand<DB>(tileB, 32 * t, c, lane);
+    }
+  };
+#pragma unroll
+  for (int t = 0; t < NS; ++t)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      accA[t][i] = 0.f;
+      accB[t][i] = 0.f;
+    }
+#pragma unroll
+  for (int c = 0; c < PD; ++c) fetch(c);
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    if (c + PD < NC) fetch(c + PD);
+#pragma unroll
+    for (int t = 0; t < NS; ++t) {
+      if (c < NA) accA[t] = mfma32(opA[c % R][t], bregA[c], accA[t]);
+      if (c < NB) accB[t] = mfma32(opB[c % R][t], bregB[c], accB[t]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// One product acc[t] = sum_c rows(tile, 32t, c) breg[c], reads PD chunks
+// ahead as in mma_rows2 (PD = 0: mma_rows).
+template <int D, int NS, int PD>
+__device__ __forceinline__ void mma_rows_pd(f32x16 (&acc)[NS], const LDS_AS char* tile,
+                                            const bf16x8 (&breg)[D / 16], int lane) {
+  if constexpr (PD == 0) {
+    mma_rows<D, NS>(acc, tile, breg, lane);
+    return;
+  }
+  constexpr int NC = D / 16, R = PD + 1;
+  bf16x8 op[R][NS];
+#pragma unroll
+  for (int t = 0; t < NS; ++t)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[t][i] = 0.f;
+#pragma unroll
+  for (int c = 0; c < PD; ++c)
+#pragma unroll
+    for (int t = 0; t < NS; ++t) op[c % R][t] = lds_row_operand<D>(tile, 32 * t, c, lane);
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    if (c + PD < NC) {
+#pragma unroll
+      for (int t = 0; t < NS; ++t) op[(c + PD) % R][t] = lds_row_operand<D>(tile, 32 * t, c + PD, lane);
+    }
+#pragma unroll
+    for (int t = 0; t < NS; ++t) acc[t] = mfma32(op[c % R][t], breg[c], acc[t]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// acc[db] += tr(tile, c16, col0 + 32 db) breg[c16] over c16 < NC16, db < NDB:
+// a contraction over the tile's rows with the transposed LDS operand, its
+// reads PD MFMAs ahead (ring of PD+1 operands), order pinned as above
+// (PD = 0: plain loop, scheduled by the compiler).  start() issues the
+// first PD reads; it can go before the VALU work that
+// produces breg, so that their latency hides behind it.
+template <int D, int NDB, int NC16, int PD>
+struct TrPipe {
+  static constexpr int N = NC16 * NDB, R = PD + 1;
+  bf16x8 op[R];
+  __device__ __forceinline__ void start(const LDS_AS char* tile, int col0, int lane) {
+#pragma unroll
+    for (int k = 0; k < PD && k < N; ++k)
+      op[k % R] = lds_tr_operand<D>(tile, 0, k / NDB, col0 + 32 * (k % NDB), lane);
+    if constexpr (PD > 0) __builtin_amdgcn_sched_barrier(0);   // keep them here
+  }
+  __device__ __forceinline__ void run(f32x16 (&acc)[NDB], const LDS_AS char* tile, int col0,
+                                      const bf16x8 (&breg)[NC16], int lane) {
+    if constexpr (PD == 0) {
+#pragma unroll
+      for (int k = 0; k < N; ++k)
+        acc[k % NDB] = mfma32(lds_tr_operand<D>(tile, 0, k / NDB, col0 + 32 * (k % NDB), lane),
+                              breg[k / NDB], acc[k % NDB]);
+      return;
+    }
+#pragma unroll
+    for (int k = 0; k < N; ++k) {
+      if (k + PD < N)
+        op[(k + PD) % R] =
+            lds_tr_operand<D>(tile, 0, (k + PD) / NDB, col0 + 32 * ((k + PD) % NDB), lane);
+      acc[k % NDB] = mfma32(op[k % R], breg[k / NDB], acc[k % NDB]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+};
+
 // Pack accumulators acc[8*h .. 8*h+7] of a 32x32 tile to 8 bf16 (RNE): the
 // B operand of a contraction over the tile's rows (16 rows per chunk h).
 __device__ __forceinline__ bf16x8 pack_bf16(const float* x) {

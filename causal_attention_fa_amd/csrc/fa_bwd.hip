@@ -29,6 +29,13 @@
 
 namespace fa {
 
+// LDS operand reads run this many MFMAs ahead of their use, in a pinned
+// order; 0 leaves the order to the compiler (d = 192: two more operand sets
+// add spills that cost more than the stalls they remove).
+#ifndef BWD_LDS_PD
+#define BWD_LDS_PD(DK) ((DK) == 192 ? 0 : 2)
+#endif
+
 // exp2 argument of P: capped score in the log2 domain minus the row's lse
 // (log2), with the constant folded into one FMA -- cap*log2(e)*tanh(scale*x/
 // cap) with a cap (th = the tanh, for the chain rule), scale*log2(e)*x
@@ -152,9 +159,10 @@ __global__ __launch_bounds__(64 * NW, (DK >= 192 ? 1 : 8 / NW)) void fa_bwd_dq_k
       const bool empty = qa >= T || kv0 > qb || (W > 0 && kv0 + BKV - 1 <= qa - W);
       const bool full = kv0 + BKV - 1 <= qa && (W == 0 || kv0 > qb - W);
       f32x16 s[NS], dp[NS];
+      TrPipe<DK, NDB, BKV / 16, BWD_LDS_PD(DK)> ktp;
       if (!empty) {
-        mma_rows<DK, NS>(s, Kt, qreg, lane);
-        mma_rows<DV, NS>(dp, Vt, doreg, lane);
+        mma_rows2<DK, DV, NS, BWD_LDS_PD(DK)>(s, Kt, qreg, dp, Vt, doreg, lane);
+        ktp.start(Kt, 0, lane);   // first K^T operands of dQ, read during the softmax
       }
       if (!empty) {
         // dS^T in s[] (fp32), then bf16 operands.  Every element is computed
@@ -188,11 +196,7 @@ __global__ __launch_bounds__(64 * NW, (DK >= 192 ? 1 : 8 / NW)) void fa_bwd_dq_k
           for (int jj = 0; jj < 8; ++jj) tmp[jj] = s[c16 >> 1][8 * (c16 & 1) + jj];
           dsb[c16] = pack_bf16(tmp);
         }
-  #pragma unroll
-        for (int c16 = 0; c16 < BKV / 16; ++c16)
-  #pragma unroll
-          for (int db = 0; db < NDB; ++db)
-            dqacc[db] = mfma32(lds_tr_operand<DK>(Kt, 0, c16, 32 * db, lane), dsb[c16], dqacc[db]);
+        ktp.run(dqacc, Kt, 0, dsb, lane);
       }
   };
 
@@ -237,6 +241,212 @@ __global__ __launch_bounds__(64 * NW, (DK >= 192 ? 1 : 8 / NW)) void fa_bwd_dq_k
           // the negative angle
           const float4 r = *(const float4*)(a.rope_cs + (size_t)qrow * DK +
                                             2 * (16 * db + 4 * i4 + 2 * g));
+          rope_pair(r.x, -r.y, x[0], x[1]);
+          rope_pair(r.z, -r.w, x[2], x[3]);
+        }
+        bf16x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = (bf16)x[e];
+        *(bf16x4*)(Qd + 32 * db + 8 * i4 + 4 * g) = v;
+      }
+  }
+}
+
+// Head size 256, dQ pass: as the forward's paired kernel, waves work in
+// pairs on the same 32 query rows.  Wave half hf holds q and dO over columns
+// 128 hf .. +127, computes the partial S^T and dP^T over its half of d, and
+// owns dq columns 128 hf .. +127; the pair swaps its partial S^T and dP^T
+// (and once, its partial D_i) through LDS and both add them in the same
+// order, so dS is identical in both waves.  Two waves per SIMD without
+// spilling, where the single-wave kernel needs ~490 registers.
+template <int D, int BKV, bool CAP>
+__global__ __launch_bounds__(512, 1) void fa_bwd_dq_pair_kernel(BwdArgs a) {
+  constexpr int NW = 8, NT = 64 * NW;
+  constexpr int HD = D / 2;
+  constexpr int BQ = 32 * NW / 2;
+  constexpr int TILE = Lay<D>::template bytes<BKV>();
+  constexpr int NDB = HD / 32;
+  constexpr int NS = BKV / 32;
+  constexpr int NC = HD / 16;
+  constexpr int XS = 2 * NS * 16 * 64 * 4;   // one wave's partial S^T and dP^T
+  __shared__ __attribute__((aligned(1024))) char smem[4 * TILE + NW * XS];
+  LDS_AS char* lds = (LDS_AS char*)smem;
+  LDS_AS float* xsb = (LDS_AS float*)(lds + 4 * TILE);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int pair = wave >> 1;
+  const int hf = wave & 1;
+  const int g = lane >> 5;
+  const int l32 = lane & 31;
+  const int T = a.T;
+  const int W = a.window;
+  const int G = a.H / a.Hkv;
+  const int nqb = (T + BQ - 1) / BQ;
+  const WorkItem w = decode_work(blockIdx.x, nqb, a.B, a.Hkv, G, true);
+  const int h = w.hkv * G + w.r;
+  const int q0 = w.blk * BQ;
+  const int qw0 = q0 + 32 * pair;
+  const int qrow = qw0 + l32;
+  const int qr = qrow < T ? qrow : T - 1;
+  const size_t bh = (size_t)w.b * a.H + h;
+  const size_t bkv = (size_t)w.b * a.Hkv + w.hkv;
+  const bf16* Kp = a.k + bkv * T * D;
+  const bf16* Vp = a.v + bkv * T * D;
+  LDS_AS float* const xs_mine = xsb + wave * (XS / 4);
+  const LDS_AS float* const xs_peer = xsb + (wave ^ 1) * (XS / 4);
+
+  // this wave's half of the q and dO rows; partial D_i over that half
+  bf16x8 qreg[NC], doreg[NC];
+  float Di;
+  {
+    const size_t roff = (bh * T + qr) * D + HD * hf + 8 * g;
+    const bf16x8* qs = (const bf16x8*)(a.q + roff);
+    const bf16x8* ds = (const bf16x8*)(a.dO + roff);
+    const bf16x8* os = (const bf16x8*)(a.o + roff);
+    float part = 0.f;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      qreg[c] = qs[2 * c];
+      doreg[c] = ds[2 * c];
+      const bf16x8 ov = os[2 * c];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) part += (float)doreg[c][j] * (float)ov[j];
+    }
+    part = xor32_sum(part);
+    xs_mine[lane] = part;
+    __syncthreads();
+    const float peer = xs_peer[lane];
+    Di = hf == 0 ? part + peer : peer + part;
+    if (hf == 0 && g == 0 && qrow < T) a.Dst[bh * T + qrow] = Di;
+  }
+  const float lse2 = a.lse[bh * T + qr] * kLog2e;
+  if (a.sinks && hf == 0) {
+    float c = (g == 0 && qrow < T) ? fast_exp2(a.sinks[h] * kLog2e - lse2) * Di : 0.f;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) c += __shfl_xor(c, off);
+    if (lane == 0) atomicAdd(a.dsinks + h, -c);
+  }
+
+  int kv_lo = 0;
+  if (W > 0) kv_lo = max(0, q0 - W + 1);
+  const int t_lo = kv_lo / BKV;
+  const int kv_hi = min(T, q0 + BQ);
+  const int ntiles = (kv_hi + BKV - 1) / BKV - t_lo;
+
+  f32x16 dqacc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) dqacc[db][i] = 0.f;
+
+  TileStage<D, BKV, NT> kst, vst;
+  kst.load(Kp, t_lo * BKV, T, tid);
+  vst.load(Vp, t_lo * BKV, T, tid);
+  kst.store(lds, tid);
+  vst.store(lds + 2 * TILE, tid);
+  __syncthreads();
+
+  const int qa = qw0, qb = qw0 + 31;
+  for (int j = 0; j < ntiles; ++j) {
+    const int cur = j & 1;
+    const LDS_AS char* Kt = lds + cur * TILE;
+    const LDS_AS char* Vt = lds + (2 + cur) * TILE;
+    const bool more = j + 1 < ntiles;
+    if (more) {
+      kst.load(Kp, (t_lo + j + 1) * BKV, T, tid);
+      vst.load(Vp, (t_lo + j + 1) * BKV, T, tid);
+    }
+    const int kv0 = (t_lo + j) * BKV;
+    const bool empty = qa >= T || kv0 > qb || (W > 0 && kv0 + BKV - 1 <= qa - W);
+    const bool full = kv0 + BKV - 1 <= qa && (W == 0 || kv0 > qb - W);
+    f32x16 s[NS], dp[NS];
+    if (!empty) {
+      // partial S^T = K Q^T and dP^T = V dO^T over this wave's half of d
+#pragma unroll
+      for (int t = 0; t < NS; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          s[t][i] = 0.f;
+          dp[t][i] = 0.f;
+        }
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+#pragma unroll
+        for (int t = 0; t < NS; ++t) {
+          s[t] = mfma32(lds_row_operand<D>(Kt, 32 * t, NC * hf + c, lane), qreg[c], s[t]);
+          dp[t] = mfma32(lds_row_operand<D>(Vt, 32 * t, NC * hf + c, lane), doreg[c], dp[t]);
+        }
+#pragma unroll
+      for (int t = 0; t < NS; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          xs_mine[((2 * t) * 16 + i) * 64 + lane] = s[t][i];
+          xs_mine[((2 * t + 1) * 16 + i) * 64 + lane] = dp[t][i];
+        }
+    }
+    __syncthreads();
+    if (!empty) {
+#pragma unroll
+      for (int t = 0; t < NS; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float ps = xs_peer[((2 * t) * 16 + i) * 64 + lane];
+          const float pd = xs_peer[((2 * t + 1) * 16 + i) * 64 + lane];
+          const float sv = hf == 0 ? s[t][i] + ps : ps + s[t][i];
+          const float dv = hf == 0 ? dp[t][i] + pd : pd + dp[t][i];
+          float th;
+          const float p = fast_exp2(p_arg<CAP>(sv, a, lse2, th));
+          float ds = p * (dv - Di);
+          if (CAP) ds *= 1.f - th * th;
+          s[t][i] = ds;
+        }
+      if (!full) {
+#pragma unroll
+        for (int t = 0; t < NS; ++t)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int kv = kv0 + 32 * t + acc_row(i, g);
+            const bool vis = (kv <= qrow) & ((W == 0) | (kv > qrow - W));
+            s[t][i] = vis ? s[t][i] : 0.f;
+          }
+      }
+      bf16x8 dsb[BKV / 16];
+#pragma unroll
+      for (int c16 = 0; c16 < BKV / 16; ++c16) {
+        float tmp[8];
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) tmp[jj] = s[c16 >> 1][8 * (c16 & 1) + jj];
+        dsb[c16] = pack_bf16(tmp);
+      }
+#pragma unroll
+      for (int c16 = 0; c16 < BKV / 16; ++c16)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+          dqacc[db] = mfma32(lds_tr_operand<D>(Kt, 0, c16, HD * hf + 32 * db, lane), dsb[c16],
+                             dqacc[db]);
+    }
+    if (more) {
+      kst.store(lds + (cur ^ 1) * TILE, tid);
+      vst.store(lds + (2 + (cur ^ 1)) * TILE, tid);
+    }
+    __syncthreads();
+  }
+
+  if (qrow < T) {
+    bf16* Qd = a.dq + (bh * T + qrow) * D + HD * hf;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        float x[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = dqacc[db][4 * i4 + e] * a.scale;
+        if (a.rope_cs) {
+          // pairs 16 (NDB hf + db) + 4 i4 + 2 g + {0, 1} of the full row
+          const float4 r = *(const float4*)(a.rope_cs + (size_t)qrow * D +
+                                            2 * (16 * (NDB * hf + db) + 4 * i4 + 2 * g));
           rope_pair(r.x, -r.y, x[0], x[1]);
           rope_pair(r.z, -r.w, x[2], x[3]);
         }
@@ -382,9 +592,17 @@ __global__ __launch_bounds__(64 * NW, (DK >= 192 ? 1 : 8 / NW)) void fa_bwd_dkdv
         const bool empty = ka >= T || q0 + BQB - 1 < ka || (W > 0 && q0 - kb >= W);
       const bool full = q0 >= kb && q0 + BQB <= T && (W == 0 || q0 + BQB - 1 - ka < W);
       f32x16 s[NS], dp[NS];
+      // first transposed operands of the dV (dO^T) or dK (Q^T) product,
+      // issued before the softmax so their latency hides behind it
+      TrPipe<DV, NDBV, BQB / 16, BWD_LDS_PD(DK)> otp;
+      TrPipe<DK, NDBK, BQB / 16, BWD_LDS_PD(DK)> qtp;
       if (!empty) {
-        mma_rows<DK, NS>(s, Qt, kreg, lane);
-        if (DO_DK) mma_rows<DV, NS>(dp, dOt, vreg, lane);
+        if constexpr (DO_DK)
+          mma_rows2<DK, DV, NS, BWD_LDS_PD(DK)>(s, Qt, kreg, dp, dOt, vreg, lane);
+        else
+          mma_rows_pd<DK, NS, BWD_LDS_PD(DK)>(s, Qt, kreg, lane);
+        if constexpr (DO_DV) otp.start(dOt, 0, lane);
+        if constexpr (DO_DK) qtp.start(Qt, 0, lane);
       }
       if (!empty) {
         // S, dP: lane = key row, accumulator i = query row 32t + acc_row(i, g).
@@ -434,19 +652,8 @@ __global__ __launch_bounds__(64 * NW, (DK >= 192 ? 1 : 8 / NW)) void fa_bwd_dkdv
           if (DO_DV) pb[c16] = pack_bf16(tp);
           if (DO_DK) dsb[c16] = pack_bf16(td);
         }
-  #pragma unroll
-        for (int c16 = 0; c16 < BQB / 16; ++c16) {
-          if (DO_DV) {
-  #pragma unroll
-            for (int db = 0; db < NDBV; ++db)
-              dvacc[db] = mfma32(lds_tr_operand<DV>(dOt, 0, c16, 32 * db, lane), pb[c16], dvacc[db]);
-          }
-          if (DO_DK) {
-  #pragma unroll
-            for (int db = 0; db < NDBK; ++db)
-              dkacc[db] = mfma32(lds_tr_operand<DK>(Qt, 0, c16, 32 * db, lane), dsb[c16], dkacc[db]);
-          }
-        }
+        if constexpr (DO_DV) otp.run(dvacc, dOt, 0, pb, lane);
+        if constexpr (DO_DK) qtp.run(dkacc, Qt, 0, dsb, lane);
       }
   };
 
@@ -547,6 +754,9 @@ __global__ __launch_bounds__(64 * NW, (DK >= 192 ? 1 : 8 / NW)) void fa_bwd_dkdv
 #ifndef BWD_PF_DK
 #define BWD_PF_DK(DK) ((DK) == 192 ? 1 : 2)
 #endif
+#ifndef BWD_DQ_PAIR
+#define BWD_DQ_PAIR 1
+#endif
 #ifndef BWD_PF_DQ
 #define BWD_PF_DQ(DK) ((DK) <= 128 ? 2 : 1)
 #endif
@@ -554,10 +764,16 @@ __global__ __launch_bounds__(64 * NW, (DK >= 192 ? 1 : 8 / NW)) void fa_bwd_dkdv
 template <int DK, int DV, bool CAP, int DQ_BKV, int DQ_NW, int DV_BQB, int DV_NW, int DK_BQB,
           int DK_NW>
 static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
+  if constexpr (DK == 256 && DV == 256 && BWD_DQ_PAIR) {
+    const int nqb = (a.T + 127) / 128;
+    hipLaunchKernelGGL((fa_bwd_dq_pair_kernel<256, 32, CAP>), dim3((unsigned)nqb * a.B * a.H),
+                       dim3(512), 0, stream, a);
+  } else {
   const int nqb = (a.T + 32 * DQ_NW - 1) / (32 * DQ_NW);
   hipLaunchKernelGGL((fa_bwd_dq_kernel<DK, DV, DQ_BKV, DQ_NW, CAP, BWD_PF_DQ(DK)>),
                      dim3((unsigned)nqb * a.B * a.H),
                      dim3(64 * DQ_NW), 0, stream, a);
+  }
   stage_mark(stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
