@@ -5,7 +5,9 @@
 Every source under csrc/ is compiled with hipcc for gfx950 (in parallel)
 into _build/, then linked into causal_attention_fa_amd/libfa.so, which the
 ctypes binding in fa.py loads.  Packed-FP32 instructions are disabled for
-device code (-packed-fp32-ops).
+device code (-packed-fp32-ops).  The backward kernels are scheduled with
+LLVM's max-ILP machine scheduler (measured 1-2% faster there; the forward
+is not faster with it).
 """
 from __future__ import annotations
 
@@ -30,6 +32,16 @@ CFLAGS = [
 ]
 
 
+# extra flags per source file
+FILE_FLAGS = {
+    "fa_bwd.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
+}
+
+
+def flags_for(src: str) -> list:
+    return CFLAGS + FILE_FLAGS.get(os.path.basename(src), [])
+
+
 def _hipcc() -> str:
     for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if c and os.path.exists(c):
@@ -44,7 +56,7 @@ def sources():
 
 def _compile(hipcc, src, verbose):
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc, "-x", "hip", *CFLAGS, "-c", src, "-o", obj]
+    cmd = [hipcc, "-x", "hip", *flags_for(src), "-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -378,12 +378,15 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dq_pair_kernel(BwdArgs a) {
           s[t] = mfma32(lds_row_operand<D>(Kt, 32 * t, NC * hf + c, lane), qreg[c], s[t]);
           dp[t] = mfma32(lds_row_operand<D>(Vt, 32 * t, NC * hf + c, lane), doreg[c], dp[t]);
         }
+      // lane-major 16-byte groups: element i of array x at ((x*4 + i/4)*64 + lane)*4 + i%4
 #pragma unroll
       for (int t = 0; t < NS; ++t)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          xs_mine[((2 * t) * 16 + i) * 64 + lane] = s[t][i];
-          xs_mine[((2 * t + 1) * 16 + i) * 64 + lane] = dp[t][i];
+        for (int i4 = 0; i4 < 4; ++i4) {
+          *(LDS_AS f32x4*)(xs_mine + (((2 * t) * 4 + i4) * 64 + lane) * 4) =
+              f32x4{s[t][4 * i4], s[t][4 * i4 + 1], s[t][4 * i4 + 2], s[t][4 * i4 + 3]};
+          *(LDS_AS f32x4*)(xs_mine + (((2 * t + 1) * 4 + i4) * 64 + lane) * 4) =
+              f32x4{dp[t][4 * i4], dp[t][4 * i4 + 1], dp[t][4 * i4 + 2], dp[t][4 * i4 + 3]};
         }
     }
     __syncthreads();
@@ -392,8 +395,8 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dq_pair_kernel(BwdArgs a) {
       for (int t = 0; t < NS; ++t)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const float ps = xs_peer[((2 * t) * 16 + i) * 64 + lane];
-          const float pd = xs_peer[((2 * t + 1) * 16 + i) * 64 + lane];
+          const float ps = xs_peer[(((2 * t) * 4 + i / 4) * 64 + lane) * 4 + i % 4];
+          const float pd = xs_peer[(((2 * t + 1) * 4 + i / 4) * 64 + lane) * 4 + i % 4];
           const float sv = hf == 0 ? s[t][i] + ps : ps + s[t][i];
           const float dv = hf == 0 ? dp[t][i] + pd : pd + dp[t][i];
           float th;

@@ -431,7 +431,9 @@ __global__ __launch_bounds__(512, 1) void fa_fwd_pair_kernel(FwdArgs a) {
 #pragma unroll
       for (int t = 0; t < NS; ++t)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) xs_mine[(t * 16 + i) * 64 + lane] = s[t][i];
+        for (int i4 = 0; i4 < 4; ++i4)   // lane-major 16-byte groups
+          *(LDS_AS f32x4*)(xs_mine + ((t * 4 + i4) * 64 + lane) * 4) =
+              f32x4{s[t][4 * i4], s[t][4 * i4 + 1], s[t][4 * i4 + 2], s[t][4 * i4 + 3]};
     }
     __syncthreads();
     if (!empty) {
@@ -440,7 +442,7 @@ __global__ __launch_bounds__(512, 1) void fa_fwd_pair_kernel(FwdArgs a) {
       for (int t = 0; t < NS; ++t)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const float peer = xs_peer[(t * 16 + i) * 64 + lane];
+          const float peer = xs_peer[((t * 4 + i / 4) * 64 + lane) * 4 + i % 4];
           s[t][i] = hf == 0 ? s[t][i] + peer : peer + s[t][i];
         }
       if (CAP) {
