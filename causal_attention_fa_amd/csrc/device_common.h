@@ -137,6 +137,9 @@ struct TileStage {
   __device__ __forceinline__ static bool has(int n, int tid) {
     return !RAGGED || n + 1 < ROUNDS || (n * NTHREADS + tid) < CHUNKS;
   }
+  // NT: non-temporal loads (data read once, e.g. a KV cache streamed by
+  // decode; measured ~8 % more HBM read bandwidth on gfx950)
+  template <bool NT = false>
   __device__ __forceinline__ void load(const bf16* gbase, int row0, int nrows, int tid) {
 #pragma unroll
     for (int n = 0; n < ROUNDS; ++n) {
@@ -146,7 +149,8 @@ struct TileStage {
       const int cc = p % CPR;
       int grow = row0 + rr;
       grow = grow < nrows ? grow : nrows - 1;
-      r[n] = *(const u32x4*)(gbase + (size_t)grow * D + cc * 8);
+      const u32x4* src = (const u32x4*)(gbase + (size_t)grow * D + cc * 8);
+      r[n] = NT ? __builtin_nontemporal_load(src) : *src;
     }
   }
   __device__ __forceinline__ void store(LDS_AS char* lds, int tid) const {

@@ -23,6 +23,11 @@
 
 namespace fa {
 
+// the cache is streamed once per call: non-temporal loads
+#ifndef DEC_NT
+#define DEC_NT true
+#endif
+
 constexpr int kDecBKV = 32;  // keys per tile
 
 // NW waves per workgroup share the K/V tiles; each computes the (cheap,
@@ -91,16 +96,16 @@ __global__ __launch_bounds__(64 * NW, 2) void fa_decode_split_kernel(DecodeArgs 
   float m = kMaxInit, l = 0.f;
 
   TileStage<D, kDecBKV, NT> kst, vst;
-  kst.load(Kp, start, end, tid);
-  vst.load(Vp, start, end, tid);
+  kst.template load<DEC_NT>(Kp, start, end, tid);
+  vst.template load<DEC_NT>(Vp, start, end, tid);
   for (int j = 0; j < ntiles; ++j) {
     const int kv0 = start + j * kDecBKV;
     kst.store(Kt, tid);
     vst.store(Vt, tid);
     __syncthreads();
     if (j + 1 < ntiles) {
-      kst.load(Kp, kv0 + kDecBKV, end, tid);
-      vst.load(Vp, kv0 + kDecBKV, end, tid);
+      kst.template load<DEC_NT>(Kp, kv0 + kDecBKV, end, tid);
+      vst.template load<DEC_NT>(Vp, kv0 + kDecBKV, end, tid);
     }
     f32x16 sacc[1];
     mma_rows<D, 1>(sacc, Kt, qreg, lane);
