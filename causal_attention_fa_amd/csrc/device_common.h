@@ -163,6 +163,61 @@ struct TileStage {
   }
 };
 
+// Direct global -> LDS tile copy (gfx950 buffer_load ... lds, 16 bytes per
+// lane): each wave-level load writes 1 KB of LDS at consecutive addresses,
+// lane l at +16 l, so the loader walks the padded tile image (Lay<D>) in
+// 1 KB pieces and gives every lane the global chunk that belongs at its LDS
+// position; lanes on row padding get an offset past the buffer, which the
+// range check turns into a zero read with no memory traffic.  Rows past
+// the buffer's end read as zeros as well (the buffer covers rows
+// [0, nrows) of the slice), so no clamping is needed.  The data lands
+// asynchronously: s_waitcnt vmcnt(0) before the barrier that publishes it.
+// No staging registers: one offset per lane per 1 KB piece.
+
+template <int D, int ROWS, int NW>
+struct TileDma {
+  static constexpr int STRIDE = Lay<D>::STRIDE;
+  static constexpr int BYTES = ROWS * STRIDE;
+  static_assert(BYTES % 1024 == 0, "tile image must be whole 1 KB pieces");
+  static constexpr int NI = BYTES / 1024;          // pieces per tile
+  static constexpr int PER = (NI + NW - 1) / NW;   // pieces per wave (last round ragged)
+  static constexpr unsigned kOut = 0x7fffffffu;    // past any buffer: reads 0
+  unsigned voff[PER];
+
+  __device__ __forceinline__ void init(int wave, int lane) {
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int P = (wave + k * NW) * 1024 + lane * 16;
+      const int r = P / STRIDE;
+      const int o = P % STRIDE;
+      const int pc = o >> 4;
+      const int lc = ((pc ^ (r >> 2)) & 3) | (pc & ~3);   // Lay<D>'s XOR is its own inverse
+      voff[k] = (o < 2 * D && P < BYTES) ? (unsigned)(r * 2 * D + lc * 16) : kOut;
+    }
+  }
+  // rows row0 .. row0 + ROWS - 1 of the buffer [base, base + nbytes) into
+  // the tile image at lds
+  __device__ __forceinline__ void load(const void* base, int nbytes, LDS_AS char* lds, int row0,
+                                       int wave) const {
+#if defined(__HIP_DEVICE_COMPILE__)   // device-only builtins (the host pass only needs the stub)
+    // raw buffer, 32-bit data format, no swizzle (gfx9 word 3)
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, nbytes, 0x00020000);
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int ins = wave + k * NW;
+      if (ins < NI)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void*)(lds + ins * 1024), 16, voff[k],
+                                                 row0 * 2 * D, 0, 0);
+    }
+#endif
+  }
+};
+
+// Waits for this wave's outstanding vector-memory operations (direct LDS
+// loads among them) -- vmcnt(0), the other counters left alone.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0f70); }
+
 // A operand for a 32-row MFMA block read along d: lane l gets
 // tile[row0 + l%32][16*c + 8*(l/32) .. +7].
 template <int D>

@@ -90,6 +90,10 @@ int check_attn(const char* fn, int B, int H, int Hkv, int T, int d, float scale,
     return fail(FA_ERR_INVALID_ARG, f + ": softcap must be >= 0 and finite");
   const double elems = (double)B * H * T * d;
   if (elems > 4.0e12) return fail(FA_ERR_INVALID_ARG, f + ": tensor too large");
+  // the kernels address one head's [T, d] slice through a buffer resource
+  // with a 32-bit byte range
+  if ((double)T * std::max(d, d_v) * 2.0 > 2147483647.0)
+    return fail(FA_ERR_INVALID_ARG, f + ": one head's [T, d] slice exceeds 2 GiB");
   return FA_OK;
 }
 

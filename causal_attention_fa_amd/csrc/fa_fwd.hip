@@ -25,6 +25,10 @@
 
 namespace fa {
 
+#ifndef FWD_DMA
+#define FWD_DMA 1
+#endif
+
 // QW query blocks of 32 rows per wave: each K or V operand read from LDS
 // feeds QW MFMAs, dividing the LDS traffic per flop by QW.  DK is the head
 // size of q and k, DV that of v and o (equal except for MLA-style heads).
@@ -126,13 +130,26 @@ __global__ __launch_bounds__(64 * NW, (DK >= 256 || QW > 1 ? 1 : 8 / NW)) void f
       for (int i = 0; i < 16; ++i) oacc[u][db][i] = 0.f;
   }
 
+  LDS_AS char* const vlds = lds + 2 * TILE_K;
+#if FWD_DMA
+  // K, V tiles go straight from HBM to the idle LDS buffers (no staging
+  // registers): issued at the top of an iteration, waited for before its
+  // closing barrier
+  TileDma<DK, BKV, NW> kdm;
+  TileDma<DV, BKV, NW> vdm;
+  kdm.init(wave, lane);
+  vdm.init(wave, lane);
+  kdm.load(Kp, T * DK * 2, lds, t_lo * BKV, wave);
+  vdm.load(Vp, T * DV * 2, vlds, t_lo * BKV, wave);
+  wait_vmem();
+#else
   TileStage<DK, BKV, NT> kst;
   TileStage<DV, BKV, NT> vst;
-  LDS_AS char* const vlds = lds + 2 * TILE_K;
   kst.load(Kp, t_lo * BKV, T, tid);
   vst.load(Vp, t_lo * BKV, T, tid);
   kst.store(lds, tid);
   vst.store(vlds, tid);
+#endif
   __syncthreads();
 
   const int qa = qw0, qb = qw0 + RW - 1;
@@ -146,8 +163,13 @@ __global__ __launch_bounds__(64 * NW, (DK >= 256 || QW > 1 ? 1 : 8 / NW)) void f
     // buffers after this tile's MFMAs, so their latency hides behind a
     // whole iteration.
     if (more) {
+#if FWD_DMA
+      kdm.load(Kp, T * DK * 2, lds + (cur ^ 1) * TILE_K, nrow, wave);
+      vdm.load(Vp, T * DV * 2, vlds + (cur ^ 1) * TILE_V, nrow, wave);
+#else
       kst.load(Kp, nrow, T, tid);
       vst.load(Vp, nrow, T, tid);
+#endif
     }
     const int kv0 = (t_lo + j) * BKV;
     const bool empty = qa >= T || kv0 > qb || (W > 0 && kv0 + BKV - 1 <= qa - W);
@@ -254,10 +276,14 @@ __global__ __launch_bounds__(64 * NW, (DK >= 256 || QW > 1 ? 1 : 8 / NW)) void f
           for (int u = 0; u < QW; ++u) oacc[u][db] = mfma32(vop, pb[u][c16], oacc[u][db]);
         }
     }
+#if FWD_DMA
+    if (more) wait_vmem();
+#else
     if (more) {
       kst.store(lds + (cur ^ 1) * TILE_K, tid);
       vst.store(vlds + (cur ^ 1) * TILE_V, tid);
     }
+#endif
     __syncthreads();
   }
 
