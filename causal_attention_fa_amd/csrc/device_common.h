@@ -181,6 +181,7 @@ struct TileDma {
   static_assert(BYTES % 1024 == 0, "tile image must be whole 1 KB pieces");
   static constexpr int NI = BYTES / 1024;          // pieces per tile
   static constexpr int PER = (NI + NW - 1) / NW;   // pieces per wave (last round ragged)
+  static constexpr int MINPER = NI / NW;           // pieces every wave issues
   static constexpr unsigned kOut = 0x7fffffffu;    // past any buffer: reads 0
   unsigned voff[PER];
 
@@ -214,9 +215,15 @@ struct TileDma {
   }
 };
 
-// Waits for this wave's outstanding vector-memory operations (direct LDS
-// loads among them) -- vmcnt(0), the other counters left alone.
-__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0f70); }
+// Waits until at most N of this wave's vector-memory operations (direct
+// LDS loads among them) are outstanding -- vmcnt(N), the other counters left
+// alone.  They complete in issue order, so N = the size of the newest batch
+// waits for every older one.
+template <int N = 0>
+__device__ __forceinline__ void wait_vmem() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt(0x0f70 | (N & 15) | ((N >> 4) << 14));
+}
 
 // A operand for a 32-row MFMA block read along d: lane l gets
 // tile[row0 + l%32][16*c + 8*(l/32) .. +7].

@@ -29,6 +29,31 @@
 
 namespace fa {
 
+// backward tiles loaded straight into LDS (buffer_load ... lds)
+#ifndef BWD_DMA
+#define BWD_DMA 1
+#endif
+// direct-load depth per pass and head size (tiles in flight ahead)
+// one LDS object per tile buffer (else one array; see the dQ pass), per
+// pass (0 dQ, 1 dV, 2 dK) -- chosen by measurement
+#ifndef BWD_LDS_SEP
+#define BWD_LDS_SEP(DK, PASS) ((PASS) == 1 && (DK) != 192)
+#endif
+// loop unrolled by the buffer count (buffers chosen at compile time), or
+// the buffer picked at run time (one array only)
+#ifndef BWD_UNROLL
+#define BWD_UNROLL(DK) ((DK) != 192)
+#endif
+#ifndef BWD_DMA_DEPTH_DQ
+#define BWD_DMA_DEPTH_DQ(DK) 1
+#endif
+#ifndef BWD_DMA_DEPTH_DV
+#define BWD_DMA_DEPTH_DV(DK) 1
+#endif
+#ifndef BWD_DMA_DEPTH_DK
+#define BWD_DMA_DEPTH_DK(DK) 1
+#endif
+
 // LDS operand reads run this many MFMAs ahead of their use, in a pinned
 // order; 0 leaves the order to the compiler (d = 192: two more operand sets
 // add spills that cost more than the stalls they remove).
@@ -60,8 +85,28 @@ __global__ __launch_bounds__(64 * NW, (DK >= 192 ? 1 : 8 / NW)) void fa_bwd_dq_k
   constexpr int TILE_V = Lay<DV>::template bytes<BKV>();
   constexpr int NDB = DK / 32;   // 32-wide blocks of dq
   constexpr int NS = BKV / 32;
-  __shared__ __attribute__((aligned(1024))) char smem[2 * TILE_K + 2 * TILE_V];
+  // direct-load depth: tiles in flight ahead of the one being computed
+  constexpr int DEPTH = BWD_DMA ? BWD_DMA_DEPTH_DQ(DK) : 1;
+  constexpr int NBUF = BWD_DMA ? DEPTH + 1 : 2;
+#if BWD_DMA
+  // SEP: one LDS object per buffer, so that the compiler can tell the buffer
+  // being filled by direct loads from the ones being read; otherwise (one
+  // array) it makes the transposed reads wait for every outstanding load,
+  // which also bounds how far it moves work and so the registers it needs.
+  constexpr bool SEP = BWD_LDS_SEP(DK, 0);
+  constexpr bool UNROLL = BWD_UNROLL(DK);
+  static_assert(UNROLL || !SEP, "run-time buffer choice needs the one-array layout");
+  __shared__ __attribute__((aligned(1024))) char one[SEP ? 16 : NBUF * (TILE_K + TILE_V)];
+  __shared__ __attribute__((aligned(1024))) char kb0[SEP ? TILE_K : 16];
+  __shared__ __attribute__((aligned(1024))) char kb1[SEP ? TILE_K : 16];
+  __shared__ __attribute__((aligned(1024))) char kb2[SEP && NBUF > 2 ? TILE_K : 16];
+  __shared__ __attribute__((aligned(1024))) char vb0[SEP ? TILE_V : 16];
+  __shared__ __attribute__((aligned(1024))) char vb1[SEP ? TILE_V : 16];
+  __shared__ __attribute__((aligned(1024))) char vb2[SEP && NBUF > 2 ? TILE_V : 16];
+#else
+  __shared__ __attribute__((aligned(1024))) char smem[NBUF * (TILE_K + TILE_V)];
   LDS_AS char* lds = (LDS_AS char*)smem;
+#endif
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -130,9 +175,44 @@ __global__ __launch_bounds__(64 * NW, (DK >= 192 ? 1 : 8 / NW)) void fa_bwd_dq_k
   // register set j % 2 at the top of iteration j - PF and written to LDS
   // buffer j % 2 at the end of iteration j - 1 (two ahead: loop unrolled by
   // two so both indices are compile-time constants).
+#if BWD_DMA
+  // K, V tiles straight from HBM into LDS (no staging registers), DEPTH
+  // tiles ahead: tile t lives in buffer t % NBUF; the loads of tile j+DEPTH
+  // go out at the top of iteration j, and before its closing barrier the
+  // wave waits for all but that newest batch (tile j+1 has landed).
+  TileDma<DK, BKV, NW> kdm;
+  TileDma<DV, BKV, NW> vdm;
+  kdm.init(wave, lane);
+  vdm.init(wave, lane);
+  constexpr int BATCH = TileDma<DK, BKV, NW>::MINPER + TileDma<DV, BKV, NW>::MINPER;
+  auto kbuf = [&](auto b_c) -> LDS_AS char* {
+    constexpr int b = decltype(b_c)::value;
+    if constexpr (!SEP) return (LDS_AS char*)one + b * TILE_K;
+    return b == 0 ? (LDS_AS char*)kb0 : b == 1 ? (LDS_AS char*)kb1 : (LDS_AS char*)kb2;
+  };
+  auto vbuf = [&](auto b_c) -> LDS_AS char* {
+    constexpr int b = decltype(b_c)::value;
+    if constexpr (!SEP) return (LDS_AS char*)one + NBUF * TILE_K + b * TILE_V;
+    return b == 0 ? (LDS_AS char*)vb0 : b == 1 ? (LDS_AS char*)vb1 : (LDS_AS char*)vb2;
+  };
+  auto issue = [&](auto b_c, int tile) __attribute__((always_inline)) {
+    kdm.load(Kp, T * DK * 2, kbuf(b_c), tile * BKV, wave);
+    vdm.load(Vp, T * DV * 2, vbuf(b_c), tile * BKV, wave);
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  issue(I0{}, t_lo);
+  if (DEPTH > 1 && ntiles > 1) issue(I1{}, t_lo + 1);
+  if (DEPTH > 1 && ntiles > 1 && BATCH > 0)
+    wait_vmem<(DEPTH > 1 ? BATCH : 0)>();
+  else
+    wait_vmem();
+  __syncthreads();
+#else
+  LDS_AS char* const vlds = lds + NBUF * TILE_K;
   TileStage<DK, BKV, NT> kst[PF];
   TileStage<DV, BKV, NT> vst[PF];
-  LDS_AS char* const vlds = lds + 2 * TILE_K;
   auto load_into = [&](auto r_c, int tile) __attribute__((always_inline)) {
     constexpr int r = decltype(r_c)::value;
     kst[r].load(Kp, tile * BKV, T, tid);
@@ -151,6 +231,7 @@ __global__ __launch_bounds__(64 * NW, (DK >= 192 ? 1 : 8 / NW)) void fa_bwd_dq_k
     if (ntiles > 1) load_into(I1{}, t_lo + 1);
   }
   __syncthreads();
+#endif
 
   const int qa = qw0, qb = qw0 + 31;
   // one key tile: S, dP, dS, then dQ^T += K^T dS^T
@@ -200,6 +281,54 @@ __global__ __launch_bounds__(64 * NW, (DK >= 192 ? 1 : 8 / NW)) void fa_bwd_dq_k
       }
   };
 
+#if BWD_DMA
+  // one iteration on the tile in buffer B (loop unrolled by NBUF so that
+  // every buffer is a compile-time choice)
+  auto step = [&](auto b_c, const int j) __attribute__((always_inline)) {
+    constexpr int B = decltype(b_c)::value;
+    const bool issued = j + DEPTH < ntiles;
+    if (issued) issue(std::integral_constant<int, (B + DEPTH) % NBUF>{}, t_lo + j + DEPTH);
+    compute(kbuf(b_c), vbuf(b_c), (t_lo + j) * BKV);
+    if (j + 1 < ntiles) {
+      if (DEPTH > 1 && issued && BATCH > 0)
+        wait_vmem<(DEPTH > 1 ? BATCH : 0)>();
+      else
+        wait_vmem();
+    }
+    __syncthreads();
+  };
+  int j = 0;
+  if constexpr (!UNROLL) {
+    // buffers picked at run time in the one array (depth 1)
+    static_assert(DEPTH == 1, "run-time buffer choice runs one tile ahead");
+    for (; j < ntiles; ++j) {
+      const int cur = j & 1;
+      if (j + 1 < ntiles) {
+        kdm.load(Kp, T * DK * 2, (LDS_AS char*)one + (cur ^ 1) * TILE_K, (t_lo + j + 1) * BKV, wave);
+        vdm.load(Vp, T * DV * 2, (LDS_AS char*)one + NBUF * TILE_K + (cur ^ 1) * TILE_V,
+                 (t_lo + j + 1) * BKV, wave);
+      }
+      compute((LDS_AS char*)one + cur * TILE_K, (LDS_AS char*)one + NBUF * TILE_K + cur * TILE_V,
+              (t_lo + j) * BKV);
+      if (j + 1 < ntiles) wait_vmem();
+      __syncthreads();
+    }
+  } else if constexpr (NBUF == 2) {
+    for (; j + 1 < ntiles; j += 2) {
+      step(I0{}, j);
+      step(I1{}, j + 1);
+    }
+    if (j < ntiles) step(I0{}, j);
+  } else {
+    for (; j + 2 < ntiles; j += 3) {
+      step(I0{}, j);
+      step(I1{}, j + 1);
+      step(I2{}, j + 2);
+    }
+    if (j < ntiles) step(I0{}, j);
+    if (j + 1 < ntiles) step(I1{}, j + 1);
+  }
+#else
   if constexpr (PF == 2) {
     auto step = [&](auto p_c, const int j) __attribute__((always_inline)) {
       constexpr int P = decltype(p_c)::value;
@@ -225,6 +354,7 @@ __global__ __launch_bounds__(64 * NW, (DK >= 192 ? 1 : 8 / NW)) void fa_bwd_dq_k
       __syncthreads();
     }
   }
+#endif
 
   if (qrow < T) {
     bf16* Qd = a.dq + (bh * T + qrow) * DK;
@@ -479,10 +609,29 @@ __global__ __launch_bounds__(64 * NW, (DK >= 192 ? 1 : 8 / NW)) void fa_bwd_dkdv
   constexpr int NDBV = DV / 32;        // 32-wide blocks of dv
   constexpr int NS = BQB / 32;         // 32-query sub-tiles
   constexpr int STAT = BQB * 4;        // bytes of one lse or D tile
-  __shared__ __attribute__((aligned(1024))) char smem[2 * TILE_Q + 2 * TILE_O + 4 * STAT];
+  // direct-load depth: tiles in flight ahead of the one being computed
+  constexpr int DEPTH = BWD_DMA ? (MODE == 1 ? BWD_DMA_DEPTH_DV(DK) : BWD_DMA_DEPTH_DK(DK)) : 1;
+  constexpr int NBUF = BWD_DMA ? DEPTH + 1 : 2;
+#if BWD_DMA
+  // one LDS object per buffer or one array (see the dQ pass)
+  constexpr bool SEP = BWD_LDS_SEP(DK, MODE);
+  constexpr bool UNROLL = BWD_UNROLL(DK);
+  static_assert(UNROLL || !SEP, "run-time buffer choice needs the one-array layout");
+  __shared__ __attribute__((aligned(1024))) char one[SEP ? 16 : NBUF * (TILE_Q + TILE_O)];
+  __shared__ __attribute__((aligned(1024))) char qb0[SEP ? TILE_Q : 16];
+  __shared__ __attribute__((aligned(1024))) char qb1[SEP ? TILE_Q : 16];
+  __shared__ __attribute__((aligned(1024))) char qb2[SEP && NBUF > 2 ? TILE_Q : 16];
+  __shared__ __attribute__((aligned(1024))) char ob0[SEP ? TILE_O : 16];
+  __shared__ __attribute__((aligned(1024))) char ob1[SEP ? TILE_O : 16];
+  __shared__ __attribute__((aligned(1024))) char ob2[SEP && NBUF > 2 ? TILE_O : 16];
+  __shared__ __attribute__((aligned(16))) char sbuf[4 * STAT];
+  LDS_AS char* stat = (LDS_AS char*)sbuf;  // [buf][lse2 | D][BQB] fp32
+#else
+  __shared__ __attribute__((aligned(1024))) char smem[NBUF * (TILE_Q + TILE_O) + 4 * STAT];
   LDS_AS char* lds = (LDS_AS char*)smem;
-  LDS_AS char* const olds = lds + 2 * TILE_Q;
-  LDS_AS char* stat = olds + 2 * TILE_O;  // [buf][lse2 | D][BQB] fp32
+  LDS_AS char* const olds = lds + NBUF * TILE_Q;
+  LDS_AS char* stat = olds + NBUF * TILE_O;  // [buf][lse2 | D][BQB] fp32
+#endif
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -532,9 +681,11 @@ __global__ __launch_bounds__(64 * NW, (DK >= 192 ? 1 : 8 / NW)) void fa_bwd_dkdv
   // and written to LDS buffer t % 2 at the end of iteration t - 1 (the loop
   // is unrolled by two so both indices are compile-time constants).  Two
   // ahead hides more load latency but holds a second register set.
+#if !BWD_DMA
   TileStage<DK, BQB, NT> qst[PF];
   TileStage<DV, BQB, NT> dost[PF];
   float stv[PF] = {};
+#endif
   // Iteration it visits query head (hkv*G + hi) and query tile ti, with
   // it = hi * nqt + ti; (hi, ti) advance incrementally (no integer division
   // in the loop).
@@ -560,6 +711,51 @@ __global__ __launch_bounds__(64 * NW, (DK >= 192 ? 1 : 8 / NW)) void fa_bwd_dkdv
       ++hi;
     }
   };
+#if BWD_DMA
+  // Q and dO tiles straight from HBM into LDS (no staging registers), DEPTH
+  // tiles ahead (tile t in buffer t % NBUF); the row statistics one tile
+  // ahead through a register, loaded before the newest tile batch so that
+  // waiting for all but that batch also covers them.
+  TileDma<DK, BQB, NW> qdm;
+  TileDma<DV, BQB, NW> odm;
+  qdm.init(wave, lane);
+  odm.init(wave, lane);
+  constexpr int BATCH = TileDma<DK, BQB, NW>::MINPER + TileDma<DV, BQB, NW>::MINPER;
+  auto qbuf = [&](auto b_c) -> LDS_AS char* {
+    constexpr int b = decltype(b_c)::value;
+    if constexpr (!SEP) return (LDS_AS char*)one + b * TILE_Q;
+    return b == 0 ? (LDS_AS char*)qb0 : b == 1 ? (LDS_AS char*)qb1 : (LDS_AS char*)qb2;
+  };
+  auto obuf = [&](auto b_c) -> LDS_AS char* {
+    constexpr int b = decltype(b_c)::value;
+    if constexpr (!SEP) return (LDS_AS char*)one + NBUF * TILE_Q + b * TILE_O;
+    return b == 0 ? (LDS_AS char*)ob0 : b == 1 ? (LDS_AS char*)ob1 : (LDS_AS char*)ob2;
+  };
+  auto issue = [&](auto b_c, int hi, int ti) __attribute__((always_inline)) {
+    qdm.load(tile_src(hi, a.q, DK), T * DK * 2, qbuf(b_c), tile_q0(ti), wave);
+    odm.load(tile_src(hi, a.dO, DV), T * DV * 2, obuf(b_c), tile_q0(ti), wave);
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  // (ha, ta): the next tile to issue
+  int ha = 0, ta = 0;
+  const float sv0 = stage_stats(0, 0);
+  issue(I0{}, ha, ta);
+  advance(ha, ta);
+  if (DEPTH > 1 && niter > 1) {
+    issue(I1{}, ha, ta);
+    advance(ha, ta);
+  }
+  if (tid < 2 * BQB) *(LDS_AS float*)(stat + tid * 4) = sv0;
+  if (DEPTH > 1 && niter > 1 && BATCH > 0)
+    wait_vmem<(DEPTH > 1 ? BATCH : 0)>();
+  else
+    wait_vmem();
+  int h1 = 0, t1 = 0;
+  advance(h1, t1);   // tile 1
+  __syncthreads();
+#else
   auto load_into = [&](auto r_c, int hi, int ti) __attribute__((always_inline)) {
     constexpr int r = decltype(r_c)::value;
     qst[r].load(tile_src(hi, a.q, DK), tile_q0(ti), T, tid);
@@ -585,6 +781,7 @@ __global__ __launch_bounds__(64 * NW, (DK >= 192 ? 1 : 8 / NW)) void fa_bwd_dkdv
     if (niter > 1) load_into(I1{}, h1, t1);
   }
   __syncthreads();
+#endif
 
   const int ka = kw0, kb = kw0 + 31;
   int hc = 0, tc = 0;   // tile of the current iteration
@@ -660,6 +857,75 @@ __global__ __launch_bounds__(64 * NW, (DK >= 192 ? 1 : 8 / NW)) void fa_bwd_dkdv
       }
   };
 
+#if BWD_DMA
+  // one iteration on the tile in buffer B (loop unrolled by NBUF)
+  auto step = [&](auto b_c, const int it) __attribute__((always_inline)) {
+    constexpr int B = decltype(b_c)::value;
+    const bool more = it + 1 < niter;
+    float sv = 0.f;
+    if (more) sv = stage_stats(h1, t1);
+    const bool issued = it + DEPTH < niter;
+    if (issued) {
+      issue(std::integral_constant<int, (B + DEPTH) % NBUF>{}, ha, ta);
+      advance(ha, ta);
+    }
+    const LDS_AS float* lse2t = (const LDS_AS float*)(stat + (it & 1) * 2 * STAT);
+    compute(qbuf(b_c), obuf(b_c), lse2t, lse2t + BQB, tile_q0(tc));
+    if (more) {
+      if (tid < 2 * BQB) *(LDS_AS float*)(stat + ((it + 1) & 1) * 2 * STAT + tid * 4) = sv;
+      if (DEPTH > 1 && issued && BATCH > 0)
+        wait_vmem<(DEPTH > 1 ? BATCH : 0)>();
+      else
+        wait_vmem();
+    }
+    __syncthreads();
+    hc = h1;
+    tc = t1;
+    advance(h1, t1);
+  };
+  int it = 0;
+  if constexpr (!UNROLL) {
+    // buffers picked at run time in the one array (depth 1)
+    static_assert(DEPTH == 1, "run-time buffer choice runs one tile ahead");
+    for (; it < niter; ++it) {
+      const int cur = it & 1;
+      const bool more = it + 1 < niter;
+      float sv = 0.f;
+      if (more) {
+        sv = stage_stats(h1, t1);
+        qdm.load(tile_src(h1, a.q, DK), T * DK * 2, (LDS_AS char*)one + (cur ^ 1) * TILE_Q,
+                 tile_q0(t1), wave);
+        odm.load(tile_src(h1, a.dO, DV), T * DV * 2,
+                 (LDS_AS char*)one + NBUF * TILE_Q + (cur ^ 1) * TILE_O, tile_q0(t1), wave);
+      }
+      const LDS_AS float* lse2t = (const LDS_AS float*)(stat + cur * 2 * STAT);
+      compute((LDS_AS char*)one + cur * TILE_Q, (LDS_AS char*)one + NBUF * TILE_Q + cur * TILE_O,
+              lse2t, lse2t + BQB, tile_q0(tc));
+      if (more) {
+        if (tid < 2 * BQB) *(LDS_AS float*)(stat + (cur ^ 1) * 2 * STAT + tid * 4) = sv;
+        wait_vmem();
+      }
+      __syncthreads();
+      hc = h1;
+      tc = t1;
+      advance(h1, t1);
+    }
+  } else if constexpr (NBUF == 2) {
+    for (; it + 1 < niter; it += 2) {
+      step(I0{}, it);
+      step(I1{}, it + 1);
+    }
+    if (it < niter) step(I0{}, it);
+  } else {
+    for (; it + 2 < niter; it += 3) {
+      step(I0{}, it);
+      step(I1{}, it + 1);
+      step(I2{}, it + 2);
+    }
+    if (it < niter) step(I0{}, it);
+    if (it + 1 < niter) step(I1{}, it + 1);
+  }
+#else
   if constexpr (PF == 2) {
     auto step = [&](auto p_c, const int it) __attribute__((always_inline)) {
       constexpr int P = decltype(p_c)::value;
@@ -703,6 +969,7 @@ __global__ __launch_bounds__(64 * NW, (DK >= 192 ? 1 : 8 / NW)) void fa_bwd_dkdv
       advance(h1, t1);
     }
   }
+#endif
 
   if (krow < T) {
     if (DO_DK) {

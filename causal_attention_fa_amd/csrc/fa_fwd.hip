@@ -20,14 +20,13 @@
 //   * tiles entirely outside a wave's causal/window band are skipped, tiles
 //     entirely inside are not masked; only diagonal and window-edge tiles
 //     evaluate the mask.
+#include <type_traits>
+
 #include "device_common.h"
 #include "internal.h"
 
 namespace fa {
 
-#ifndef FWD_DMA
-#define FWD_DMA 1
-#endif
 
 // QW query blocks of 32 rows per wave: each K or V operand read from LDS
 // feeds QW MFMAs, dividing the LDS traffic per flop by QW.  DK is the head
@@ -43,8 +42,13 @@ __global__ __launch_bounds__(64 * NW, (DK >= 256 || QW > 1 ? 1 : 8 / NW)) void f
   constexpr int NDB = DV / 32;        // 32-wide blocks of the output
   constexpr int NS = BKV / 32;        // 32-key sub-tiles
   constexpr int NC = DK / 16;         // 16-wide chunks of the q.k contraction
-  __shared__ __attribute__((aligned(1024))) char smem[2 * TILE_K + 2 * TILE_V];
-  LDS_AS char* lds = (LDS_AS char*)smem;
+  // one LDS object per buffer: the compiler can then tell the buffer being
+  // filled by direct loads from the one being read, and does not make the
+  // reads wait for the loads
+  __shared__ __attribute__((aligned(1024))) char kb0[TILE_K];
+  __shared__ __attribute__((aligned(1024))) char kb1[TILE_K];
+  __shared__ __attribute__((aligned(1024))) char vb0[TILE_V];
+  __shared__ __attribute__((aligned(1024))) char vb1[TILE_V];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -130,8 +134,6 @@ __global__ __launch_bounds__(64 * NW, (DK >= 256 || QW > 1 ? 1 : 8 / NW)) void f
       for (int i = 0; i < 16; ++i) oacc[u][db][i] = 0.f;
   }
 
-  LDS_AS char* const vlds = lds + 2 * TILE_K;
-#if FWD_DMA
   // K, V tiles go straight from HBM to the idle LDS buffers (no staging
   // registers): issued at the top of an iteration, waited for before its
   // closing barrier
@@ -139,37 +141,33 @@ __global__ __launch_bounds__(64 * NW, (DK >= 256 || QW > 1 ? 1 : 8 / NW)) void f
   TileDma<DV, BKV, NW> vdm;
   kdm.init(wave, lane);
   vdm.init(wave, lane);
-  kdm.load(Kp, T * DK * 2, lds, t_lo * BKV, wave);
-  vdm.load(Vp, T * DV * 2, vlds, t_lo * BKV, wave);
+  auto kbuf = [&](auto p_c) -> LDS_AS char* {
+    return decltype(p_c)::value ? (LDS_AS char*)kb1 : (LDS_AS char*)kb0;
+  };
+  auto vbuf = [&](auto p_c) -> LDS_AS char* {
+    return decltype(p_c)::value ? (LDS_AS char*)vb1 : (LDS_AS char*)vb0;
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  kdm.load(Kp, T * DK * 2, kbuf(I0{}), t_lo * BKV, wave);
+  vdm.load(Vp, T * DV * 2, vbuf(I0{}), t_lo * BKV, wave);
   wait_vmem();
-#else
-  TileStage<DK, BKV, NT> kst;
-  TileStage<DV, BKV, NT> vst;
-  kst.load(Kp, t_lo * BKV, T, tid);
-  vst.load(Vp, t_lo * BKV, T, tid);
-  kst.store(lds, tid);
-  vst.store(vlds, tid);
-#endif
   __syncthreads();
 
   const int qa = qw0, qb = qw0 + RW - 1;
-  for (int j = 0; j < ntiles; ++j) {
-    const int cur = j & 1;
-    const LDS_AS char* Kt = lds + cur * TILE_K;
-    const LDS_AS char* Vt = vlds + cur * TILE_V;
+  // one iteration on the tile in buffer P (the loop is unrolled by two so
+  // that the buffers are compile-time choices)
+  auto step = [&](auto p_c, const int j) __attribute__((always_inline)) {
+    constexpr int P = decltype(p_c)::value;
+    using PN = std::integral_constant<int, 1 - P>;
+    const LDS_AS char* Kt = kbuf(p_c);
+    const LDS_AS char* Vt = vbuf(p_c);
     const bool more = j + 1 < ntiles;
-    const int nrow = (t_lo + j + 1) * BKV;
-    // Next K and V tiles: global loads issued now, written to the idle
-    // buffers after this tile's MFMAs, so their latency hides behind a
-    // whole iteration.
+    // next K and V tiles into the idle buffers: their latency hides behind
+    // this iteration
     if (more) {
-#if FWD_DMA
-      kdm.load(Kp, T * DK * 2, lds + (cur ^ 1) * TILE_K, nrow, wave);
-      vdm.load(Vp, T * DV * 2, vlds + (cur ^ 1) * TILE_V, nrow, wave);
-#else
-      kst.load(Kp, nrow, T, tid);
-      vst.load(Vp, nrow, T, tid);
-#endif
+      kdm.load(Kp, T * DK * 2, kbuf(PN{}), (t_lo + j + 1) * BKV, wave);
+      vdm.load(Vp, T * DV * 2, vbuf(PN{}), (t_lo + j + 1) * BKV, wave);
     }
     const int kv0 = (t_lo + j) * BKV;
     const bool empty = qa >= T || kv0 > qb || (W > 0 && kv0 + BKV - 1 <= qa - W);
@@ -276,16 +274,15 @@ __global__ __launch_bounds__(64 * NW, (DK >= 256 || QW > 1 ? 1 : 8 / NW)) void f
           for (int u = 0; u < QW; ++u) oacc[u][db] = mfma32(vop, pb[u][c16], oacc[u][db]);
         }
     }
-#if FWD_DMA
     if (more) wait_vmem();
-#else
-    if (more) {
-      kst.store(lds + (cur ^ 1) * TILE_K, tid);
-      vst.store(vlds + (cur ^ 1) * TILE_V, tid);
-    }
-#endif
     __syncthreads();
+  };
+  int j = 0;
+  for (; j + 1 < ntiles; j += 2) {
+    step(I0{}, j);
+    step(I1{}, j + 1);
   }
+  if (j < ntiles) step(I0{}, j);
 
   if (a.max_logit) {
     // largest logit of the wave's rows (natural log units), one atomic per wave
