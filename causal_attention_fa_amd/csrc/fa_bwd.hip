@@ -399,9 +399,14 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dq_pair_kernel(BwdArgs a) {
   constexpr int NS = BKV / 32;
   constexpr int NC = HD / 16;
   constexpr int XS = 2 * NS * 16 * 64 * 4;   // one wave's partial S^T and dP^T
-  __shared__ __attribute__((aligned(1024))) char smem[4 * TILE + NW * XS];
-  LDS_AS char* lds = (LDS_AS char*)smem;
-  LDS_AS float* xsb = (LDS_AS float*)(lds + 4 * TILE);
+  // K, V buffers as separate LDS objects (direct loads into one, reads from
+  // the other), the partial-product exchange area
+  __shared__ __attribute__((aligned(1024))) char kb0[TILE];
+  __shared__ __attribute__((aligned(1024))) char kb1[TILE];
+  __shared__ __attribute__((aligned(1024))) char vb0[TILE];
+  __shared__ __attribute__((aligned(1024))) char vb1[TILE];
+  __shared__ __attribute__((aligned(1024))) char xsm[NW * XS];
+  LDS_AS float* xsb = (LDS_AS float*)xsm;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -471,22 +476,33 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dq_pair_kernel(BwdArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) dqacc[db][i] = 0.f;
 
-  TileStage<D, BKV, NT> kst, vst;
-  kst.load(Kp, t_lo * BKV, T, tid);
-  vst.load(Vp, t_lo * BKV, T, tid);
-  kst.store(lds, tid);
-  vst.store(lds + 2 * TILE, tid);
+  TileDma<D, BKV, NW> kdm, vdm;
+  kdm.init(wave, lane);
+  vdm.init(wave, lane);
+  auto kbuf = [&](auto p_c) -> LDS_AS char* {
+    return decltype(p_c)::value ? (LDS_AS char*)kb1 : (LDS_AS char*)kb0;
+  };
+  auto vbuf = [&](auto p_c) -> LDS_AS char* {
+    return decltype(p_c)::value ? (LDS_AS char*)vb1 : (LDS_AS char*)vb0;
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  kdm.load(Kp, T * D * 2, kbuf(I0{}), t_lo * BKV, wave);
+  vdm.load(Vp, T * D * 2, vbuf(I0{}), t_lo * BKV, wave);
+  wait_vmem();
   __syncthreads();
 
   const int qa = qw0, qb = qw0 + 31;
-  for (int j = 0; j < ntiles; ++j) {
-    const int cur = j & 1;
-    const LDS_AS char* Kt = lds + cur * TILE;
-    const LDS_AS char* Vt = lds + (2 + cur) * TILE;
+  // one iteration on the tile in buffer P (unrolled by two)
+  auto step = [&](auto p_c, const int j) __attribute__((always_inline)) {
+    constexpr int P = decltype(p_c)::value;
+    using PN = std::integral_constant<int, 1 - P>;
+    const LDS_AS char* Kt = kbuf(p_c);
+    const LDS_AS char* Vt = vbuf(p_c);
     const bool more = j + 1 < ntiles;
     if (more) {
-      kst.load(Kp, (t_lo + j + 1) * BKV, T, tid);
-      vst.load(Vp, (t_lo + j + 1) * BKV, T, tid);
+      kdm.load(Kp, T * D * 2, kbuf(PN{}), (t_lo + j + 1) * BKV, wave);
+      vdm.load(Vp, T * D * 2, vbuf(PN{}), (t_lo + j + 1) * BKV, wave);
     }
     const int kv0 = (t_lo + j) * BKV;
     const bool empty = qa >= T || kv0 > qb || (W > 0 && kv0 + BKV - 1 <= qa - W);
@@ -560,12 +576,15 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dq_pair_kernel(BwdArgs a) {
           dqacc[db] = mfma32(lds_tr_operand<D>(Kt, 0, c16, HD * hf + 32 * db, lane), dsb[c16],
                              dqacc[db]);
     }
-    if (more) {
-      kst.store(lds + (cur ^ 1) * TILE, tid);
-      vst.store(lds + (2 + (cur ^ 1)) * TILE, tid);
-    }
+    if (more) wait_vmem();
     __syncthreads();
+  };
+  int j = 0;
+  for (; j + 1 < ntiles; j += 2) {
+    step(I0{}, j);
+    step(I1{}, j + 1);
   }
+  if (j < ntiles) step(I0{}, j);
 
   if (qrow < T) {
     bf16* Qd = a.dq + (bh * T + qrow) * D + HD * hf;
