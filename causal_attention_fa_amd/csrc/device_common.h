@@ -197,7 +197,9 @@ struct TileDma {
     }
   }
   // rows row0 .. row0 + ROWS - 1 of the buffer [base, base + nbytes) into
-  // the tile image at lds
+  // the tile image at lds; AUX: the loads' cache policy (2: non-temporal,
+  // for data read once)
+  template <int AUX = 0>
   __device__ __forceinline__ void load(const void* base, int nbytes, LDS_AS char* lds, int row0,
                                        int wave) const {
 #if defined(__HIP_DEVICE_COMPILE__)   // device-only builtins (the host pass only needs the stub)
@@ -209,7 +211,7 @@ struct TileDma {
       const int ins = wave + k * NW;
       if (ins < NI)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void*)(lds + ins * 1024), 16, voff[k],
-                                                 row0 * 2 * D, 0, 0);
+                                                 row0 * 2 * D, 0, AUX);
     }
 #endif
   }

@@ -18,14 +18,16 @@
 //     to the normaliser, and writes o (bf16) and lse.
 // Cache rows at or past the sequence's length are never read (the tile
 // loads clamp to the last valid row and the mask removes the duplicates).
+#include <type_traits>
+
 #include "device_common.h"
 #include "internal.h"
 
 namespace fa {
 
-// the cache is streamed once per call: non-temporal loads
-#ifndef DEC_NT
-#define DEC_NT true
+// the cache is streamed once per call: non-temporal loads (cache policy 2)
+#ifndef DEC_AUX
+#define DEC_AUX 2
 #endif
 
 constexpr int kDecBKV = 32;  // keys per tile
@@ -39,9 +41,13 @@ __global__ __launch_bounds__(64 * NW, 2) void fa_decode_split_kernel(DecodeArgs 
   constexpr int TILE = Lay<D>::template bytes<kDecBKV>();
   constexpr int NDB = D / 32 / NW;  // 32-wide output blocks per wave
   constexpr int NC = D / 16;
-  __shared__ __attribute__((aligned(1024))) char smem[2 * TILE];
-  LDS_AS char* Kt = (LDS_AS char*)smem;
-  LDS_AS char* Vt = Kt + TILE;
+  // K, V tiles double-buffered, one LDS object per buffer (direct loads
+  // into one while the other is read, without the compiler making the
+  // reads wait for the loads)
+  __shared__ __attribute__((aligned(1024))) char kb0[TILE];
+  __shared__ __attribute__((aligned(1024))) char kb1[TILE];
+  __shared__ __attribute__((aligned(1024))) char vb0[TILE];
+  __shared__ __attribute__((aligned(1024))) char vb1[TILE];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -95,17 +101,31 @@ __global__ __launch_bounds__(64 * NW, 2) void fa_decode_split_kernel(DecodeArgs 
     for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
   float m = kMaxInit, l = 0.f;
 
-  TileStage<D, kDecBKV, NT> kst, vst;
-  kst.template load<DEC_NT>(Kp, start, end, tid);
-  vst.template load<DEC_NT>(Vp, start, end, tid);
-  for (int j = 0; j < ntiles; ++j) {
+  // the cache streams straight into LDS with non-temporal loads (read once
+  // per call); rows at or past `end` read as zeros through the buffer range
+  TileDma<D, kDecBKV, NW> kdm, vdm;
+  kdm.init(wave, lane);
+  vdm.init(wave, lane);
+  auto kbuf = [&](auto p_c) -> LDS_AS char* {
+    return decltype(p_c)::value ? (LDS_AS char*)kb1 : (LDS_AS char*)kb0;
+  };
+  auto vbuf = [&](auto p_c) -> LDS_AS char* {
+    return decltype(p_c)::value ? (LDS_AS char*)vb1 : (LDS_AS char*)vb0;
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  kdm.template load<DEC_AUX>(Kp, end * D * 2, kbuf(I0{}), start, wave);
+  vdm.template load<DEC_AUX>(Vp, end * D * 2, vbuf(I0{}), start, wave);
+  wait_vmem();
+  __syncthreads();
+  auto step = [&](auto p_c, const int j) __attribute__((always_inline)) {
+    using PN = std::integral_constant<int, 1 - decltype(p_c)::value>;
+    const LDS_AS char* Kt = kbuf(p_c);
+    const LDS_AS char* Vt = vbuf(p_c);
     const int kv0 = start + j * kDecBKV;
-    kst.store(Kt, tid);
-    vst.store(Vt, tid);
-    __syncthreads();
     if (j + 1 < ntiles) {
-      kst.template load<DEC_NT>(Kp, kv0 + kDecBKV, end, tid);
-      vst.template load<DEC_NT>(Vp, kv0 + kDecBKV, end, tid);
+      kdm.template load<DEC_AUX>(Kp, end * D * 2, kbuf(PN{}), kv0 + kDecBKV, wave);
+      vdm.template load<DEC_AUX>(Vp, end * D * 2, vbuf(PN{}), kv0 + kDecBKV, wave);
     }
     f32x16 sacc[1];
     mma_rows<D, 1>(sacc, Kt, qreg, lane);
@@ -156,8 +176,15 @@ __global__ __launch_bounds__(64 * NW, 2) void fa_decode_split_kernel(DecodeArgs 
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
         oacc[db] = mfma32(lds_tr_operand<D>(Vt, 0, c16, d0 + 32 * db, lane), pb[c16], oacc[db]);
+    if (j + 1 < ntiles) wait_vmem();
     __syncthreads();
+  };
+  int j = 0;
+  for (; j + 1 < ntiles; j += 2) {
+    step(I0{}, j);
+    step(I1{}, j + 1);
   }
+  if (j < ntiles) step(I0{}, j);
 
   const float lt = xor32_sum(l);
   if (l32 < G) {
