@@ -1,5 +1,5 @@
 // Device-side building blocks shared by the gfx950 attention kernels:
-// vector types, the bf16 MFMA, LDS transpose reads, register-staged tile
+// vector types, the bf16 MFMA, LDS transpose reads, direct global -> LDS tile
 // copies, the padded LDS tile layout and the work-item map.
 #pragma once
 
@@ -120,49 +120,6 @@ struct Lay {
   }
 };
 
-// Register-staged tile copy: global -> registers (issued early, so the
-// loads overlap compute) -> LDS (written once the buffer is free).
-// NTHREADS threads cooperate; thread tid owns chunks p = n*NTHREADS + tid.
-// Rows are clamped to nrows-1 so no access leaves the tensor (rows past
-// the end hold finite data that the causal mask removes).
-template <int D, int ROWS, int NTHREADS>
-struct TileStage {
-  static constexpr int CPR = D / 8;
-  static constexpr int CHUNKS = ROWS * CPR;
-  static constexpr int ROUNDS = (CHUNKS + NTHREADS - 1) / NTHREADS;
-  // true when the last round has threads without a chunk
-  static constexpr bool RAGGED = CHUNKS % NTHREADS != 0;
-  u32x4 r[ROUNDS];
-
-  __device__ __forceinline__ static bool has(int n, int tid) {
-    return !RAGGED || n + 1 < ROUNDS || (n * NTHREADS + tid) < CHUNKS;
-  }
-  // NT: non-temporal loads (data read once, e.g. a KV cache streamed by
-  // decode; measured ~8 % more HBM read bandwidth on gfx950)
-  template <bool NT = false>
-  __device__ __forceinline__ void load(const bf16* gbase, int row0, int nrows, int tid) {
-#pragma unroll
-    for (int n = 0; n < ROUNDS; ++n) {
-      const int p = n * NTHREADS + tid;
-      if (!has(n, tid)) continue;
-      const int rr = p / CPR;
-      const int cc = p % CPR;
-      int grow = row0 + rr;
-      grow = grow < nrows ? grow : nrows - 1;
-      const u32x4* src = (const u32x4*)(gbase + (size_t)grow * D + cc * 8);
-      r[n] = NT ? __builtin_nontemporal_load(src) : *src;
-    }
-  }
-  __device__ __forceinline__ void store(LDS_AS char* lds, int tid) const {
-#pragma unroll
-    for (int n = 0; n < ROUNDS; ++n) {
-      const int p = n * NTHREADS + tid;
-      if (!has(n, tid)) continue;
-      *(LDS_AS u32x4*)(lds + Lay<D>::off(p / CPR, (p % CPR) * 8)) = r[n];
-    }
-  }
-};
-
 // Direct global -> LDS tile copy (gfx950 buffer_load ... lds, 16 bytes per
 // lane): each wave-level load writes 1 KB of LDS at consecutive addresses,
 // lane l at +16 l, so the loader walks the padded tile image (Lay<D>) in
@@ -181,7 +138,6 @@ struct TileDma {
   static_assert(BYTES % 1024 == 0, "tile image must be whole 1 KB pieces");
   static constexpr int NI = BYTES / 1024;          // pieces per tile
   static constexpr int PER = (NI + NW - 1) / NW;   // pieces per wave (last round ragged)
-  static constexpr int MINPER = NI / NW;           // pieces every wave issues
   static constexpr unsigned kOut = 0x7fffffffu;    // past any buffer: reads 0
   unsigned voff[PER];
 

@@ -8,7 +8,9 @@
 //   dS = dS' * (1 - tanh^2) (softcap),  dq = scale dS K,
 //   dk = scale dS^T Q,  dv = P^T dO  (dk, dv summed over the GQA group).
 //
-// Three launches, all deterministic (no atomics):
+// Three launches, deterministic (the only atomics accumulate the attention
+// sinks' gradient).  Every pass streams its tiles straight from HBM into
+// double-buffered LDS (direct buffer loads, one tile ahead):
 //   1. fa_bwd_dq_kernel -- query-parallel, the forward's structure: each
 //      lane owns one query row; S^T = K Q^T and dP^T = V dO^T come out with
 //      the query along the lane, so lse, D and the softcap chain are
@@ -29,34 +31,20 @@
 
 namespace fa {
 
-// backward tiles loaded straight into LDS (buffer_load ... lds)
-#ifndef BWD_DMA
-#define BWD_DMA 1
-#endif
-// direct-load depth per pass and head size (tiles in flight ahead)
-// one LDS object per tile buffer (else one array; see the dQ pass), per
-// pass (0 dQ, 1 dV, 2 dK) -- chosen by measurement
+// LDS layout of the tile buffers per pass (0 dQ, 1 dV, 2 dK): one LDS object
+// per buffer, or one array.  With one array the compiler makes the
+// transposed LDS reads wait for every outstanding direct load; that costs
+// overlap but also bounds how far it moves work, and so its register use.
+// Chosen by measurement.
 #ifndef BWD_LDS_SEP
 #define BWD_LDS_SEP(DK, PASS) ((PASS) == 1 && (DK) != 192)
 #endif
-// loop unrolled by the buffer count (buffers chosen at compile time), or
-// the buffer picked at run time (one array only)
+// loop unrolled by two (buffers chosen at compile time), or the buffer
+// picked at run time in the one array (fewer registers at d = 192)
 #ifndef BWD_UNROLL
 #define BWD_UNROLL(DK) ((DK) != 192)
 #endif
-#ifndef BWD_DMA_DEPTH_DQ
-#define BWD_DMA_DEPTH_DQ(DK) 1
-#endif
-#ifndef BWD_DMA_DEPTH_DV
-#define BWD_DMA_DEPTH_DV(DK) 1
-#endif
-#ifndef BWD_DMA_DEPTH_DK
-#define BWD_DMA_DEPTH_DK(DK) 1
-#endif
 
-// LDS operand reads run this many MFMAs ahead of their use, in a pinned
-// order; 0 leaves the order to the compiler (d = 192: two more operand sets
-// add spills that cost more than the stalls they remove).
 #ifndef BWD_LDS_PD
 #define BWD_LDS_PD(DK) ((DK) == 192 ? 0 : 2)
 #endif
@@ -77,7 +65,7 @@ __device__ __forceinline__ float p_arg(float x, const BwdArgs& a, float lse2, fl
 }
 
 // ------------------------------------------------------------------ dQ pass
-template <int DK, int DV, int BKV, int NW, bool CAP, int PF>
+template <int DK, int DV, int BKV, int NW, bool CAP>
 __global__ __launch_bounds__(64 * NW, (DK >= 192 ? 1 : 8 / NW)) void fa_bwd_dq_kernel(BwdArgs a) {
   constexpr int NT = 64 * NW;
   constexpr int BQ = 32 * NW;
@@ -85,28 +73,15 @@ __global__ __launch_bounds__(64 * NW, (DK >= 192 ? 1 : 8 / NW)) void fa_bwd_dq_k
   constexpr int TILE_V = Lay<DV>::template bytes<BKV>();
   constexpr int NDB = DK / 32;   // 32-wide blocks of dq
   constexpr int NS = BKV / 32;
-  // direct-load depth: tiles in flight ahead of the one being computed
-  constexpr int DEPTH = BWD_DMA ? BWD_DMA_DEPTH_DQ(DK) : 1;
-  constexpr int NBUF = BWD_DMA ? DEPTH + 1 : 2;
-#if BWD_DMA
-  // SEP: one LDS object per buffer, so that the compiler can tell the buffer
-  // being filled by direct loads from the ones being read; otherwise (one
-  // array) it makes the transposed reads wait for every outstanding load,
-  // which also bounds how far it moves work and so the registers it needs.
+  // K, V tiles double-buffered (see BWD_LDS_SEP / BWD_UNROLL)
   constexpr bool SEP = BWD_LDS_SEP(DK, 0);
   constexpr bool UNROLL = BWD_UNROLL(DK);
   static_assert(UNROLL || !SEP, "run-time buffer choice needs the one-array layout");
-  __shared__ __attribute__((aligned(1024))) char one[SEP ? 16 : NBUF * (TILE_K + TILE_V)];
+  __shared__ __attribute__((aligned(1024))) char one[SEP ? 16 : 2 * (TILE_K + TILE_V)];
   __shared__ __attribute__((aligned(1024))) char kb0[SEP ? TILE_K : 16];
   __shared__ __attribute__((aligned(1024))) char kb1[SEP ? TILE_K : 16];
-  __shared__ __attribute__((aligned(1024))) char kb2[SEP && NBUF > 2 ? TILE_K : 16];
   __shared__ __attribute__((aligned(1024))) char vb0[SEP ? TILE_V : 16];
   __shared__ __attribute__((aligned(1024))) char vb1[SEP ? TILE_V : 16];
-  __shared__ __attribute__((aligned(1024))) char vb2[SEP && NBUF > 2 ? TILE_V : 16];
-#else
-  __shared__ __attribute__((aligned(1024))) char smem[NBUF * (TILE_K + TILE_V)];
-  LDS_AS char* lds = (LDS_AS char*)smem;
-#endif
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -171,67 +146,29 @@ __global__ __launch_bounds__(64 * NW, (DK >= 192 ? 1 : 8 / NW)) void fa_bwd_dq_k
 #pragma unroll
     for (int i = 0; i < 16; ++i) dqacc[db][i] = 0.f;
 
-  // K, V tiles run PF (1 or 2) iterations ahead: tile j is loaded into
-  // register set j % 2 at the top of iteration j - PF and written to LDS
-  // buffer j % 2 at the end of iteration j - 1 (two ahead: loop unrolled by
-  // two so both indices are compile-time constants).
-#if BWD_DMA
-  // K, V tiles straight from HBM into LDS (no staging registers), DEPTH
-  // tiles ahead: tile t lives in buffer t % NBUF; the loads of tile j+DEPTH
-  // go out at the top of iteration j, and before its closing barrier the
-  // wave waits for all but that newest batch (tile j+1 has landed).
+  // K, V tiles go straight from HBM into the idle LDS buffer (no staging
+  // registers): issued at the top of an iteration, waited for before its
+  // closing barrier.
   TileDma<DK, BKV, NW> kdm;
   TileDma<DV, BKV, NW> vdm;
   kdm.init(wave, lane);
   vdm.init(wave, lane);
-  constexpr int BATCH = TileDma<DK, BKV, NW>::MINPER + TileDma<DV, BKV, NW>::MINPER;
   auto kbuf = [&](auto b_c) -> LDS_AS char* {
     constexpr int b = decltype(b_c)::value;
     if constexpr (!SEP) return (LDS_AS char*)one + b * TILE_K;
-    return b == 0 ? (LDS_AS char*)kb0 : b == 1 ? (LDS_AS char*)kb1 : (LDS_AS char*)kb2;
+    return b == 0 ? (LDS_AS char*)kb0 : (LDS_AS char*)kb1;
   };
   auto vbuf = [&](auto b_c) -> LDS_AS char* {
     constexpr int b = decltype(b_c)::value;
-    if constexpr (!SEP) return (LDS_AS char*)one + NBUF * TILE_K + b * TILE_V;
-    return b == 0 ? (LDS_AS char*)vb0 : b == 1 ? (LDS_AS char*)vb1 : (LDS_AS char*)vb2;
-  };
-  auto issue = [&](auto b_c, int tile) __attribute__((always_inline)) {
-    kdm.load(Kp, T * DK * 2, kbuf(b_c), tile * BKV, wave);
-    vdm.load(Vp, T * DV * 2, vbuf(b_c), tile * BKV, wave);
+    if constexpr (!SEP) return (LDS_AS char*)one + 2 * TILE_K + b * TILE_V;
+    return b == 0 ? (LDS_AS char*)vb0 : (LDS_AS char*)vb1;
   };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
-  using I2 = std::integral_constant<int, 2>;
-  issue(I0{}, t_lo);
-  if (DEPTH > 1 && ntiles > 1) issue(I1{}, t_lo + 1);
-  if (DEPTH > 1 && ntiles > 1 && BATCH > 0)
-    wait_vmem<(DEPTH > 1 ? BATCH : 0)>();
-  else
-    wait_vmem();
+  kdm.load(Kp, T * DK * 2, kbuf(I0{}), t_lo * BKV, wave);
+  vdm.load(Vp, T * DV * 2, vbuf(I0{}), t_lo * BKV, wave);
+  wait_vmem();
   __syncthreads();
-#else
-  LDS_AS char* const vlds = lds + NBUF * TILE_K;
-  TileStage<DK, BKV, NT> kst[PF];
-  TileStage<DV, BKV, NT> vst[PF];
-  auto load_into = [&](auto r_c, int tile) __attribute__((always_inline)) {
-    constexpr int r = decltype(r_c)::value;
-    kst[r].load(Kp, tile * BKV, T, tid);
-    vst[r].load(Vp, tile * BKV, T, tid);
-  };
-  auto store_from = [&](auto r_c, int buf) __attribute__((always_inline)) {
-    constexpr int r = decltype(r_c)::value;
-    kst[r].store(lds + buf * TILE_K, tid);
-    vst[r].store(vlds + buf * TILE_V, tid);
-  };
-  using I0 = std::integral_constant<int, 0>;
-  using I1 = std::integral_constant<int, 1>;
-  load_into(I0{}, t_lo);
-  store_from(I0{}, 0);
-  if constexpr (PF == 2) {
-    if (ntiles > 1) load_into(I1{}, t_lo + 1);
-  }
-  __syncthreads();
-#endif
 
   const int qa = qw0, qb = qw0 + 31;
   // one key tile: S, dP, dS, then dQ^T += K^T dS^T
@@ -281,62 +218,20 @@ __global__ __launch_bounds__(64 * NW, (DK >= 192 ? 1 : 8 / NW)) void fa_bwd_dq_k
       }
   };
 
-#if BWD_DMA
-  // one iteration on the tile in buffer B (loop unrolled by NBUF so that
-  // every buffer is a compile-time choice)
+  // one iteration on the tile in buffer B (loop unrolled by two so that the
+  // buffers are compile-time choices)
   auto step = [&](auto b_c, const int j) __attribute__((always_inline)) {
-    constexpr int B = decltype(b_c)::value;
-    const bool issued = j + DEPTH < ntiles;
-    if (issued) issue(std::integral_constant<int, (B + DEPTH) % NBUF>{}, t_lo + j + DEPTH);
-    compute(kbuf(b_c), vbuf(b_c), (t_lo + j) * BKV);
-    if (j + 1 < ntiles) {
-      if (DEPTH > 1 && issued && BATCH > 0)
-        wait_vmem<(DEPTH > 1 ? BATCH : 0)>();
-      else
-        wait_vmem();
+    using BN = std::integral_constant<int, 1 - decltype(b_c)::value>;
+    const bool more = j + 1 < ntiles;
+    if (more) {
+      kdm.load(Kp, T * DK * 2, kbuf(BN{}), (t_lo + j + 1) * BKV, wave);
+      vdm.load(Vp, T * DV * 2, vbuf(BN{}), (t_lo + j + 1) * BKV, wave);
     }
+    compute(kbuf(b_c), vbuf(b_c), (t_lo + j) * BKV);
+    if (more) wait_vmem();
     __syncthreads();
   };
-  int j = 0;
-  if constexpr (!UNROLL) {
-    // buffers picked at run time in the one array (depth 1)
-    static_assert(DEPTH == 1, "run-time buffer choice runs one tile ahead");
-    for (; j < ntiles; ++j) {
-      const int cur = j & 1;
-      if (j + 1 < ntiles) {
-        kdm.load(Kp, T * DK * 2, (LDS_AS char*)one + (cur ^ 1) * TILE_K, (t_lo + j + 1) * BKV, wave);
-        vdm.load(Vp, T * DV * 2, (LDS_AS char*)one + NBUF * TILE_K + (cur ^ 1) * TILE_V,
-                 (t_lo + j + 1) * BKV, wave);
-      }
-      compute((LDS_AS char*)one + cur * TILE_K, (LDS_AS char*)one + NBUF * TILE_K + cur * TILE_V,
-              (t_lo + j) * BKV);
-      if (j + 1 < ntiles) wait_vmem();
-      __syncthreads();
-    }
-  } else if constexpr (NBUF == 2) {
-    for (; j + 1 < ntiles; j += 2) {
-      step(I0{}, j);
-      step(I1{}, j + 1);
-    }
-    if (j < ntiles) step(I0{}, j);
-  } else {
-    for (; j + 2 < ntiles; j += 3) {
-      step(I0{}, j);
-      step(I1{}, j + 1);
-      step(I2{}, j + 2);
-    }
-    if (j < ntiles) step(I0{}, j);
-    if (j + 1 < ntiles) step(I1{}, j + 1);
-  }
-#else
-  if constexpr (PF == 2) {
-    auto step = [&](auto p_c, const int j) __attribute__((always_inline)) {
-      constexpr int P = decltype(p_c)::value;
-      if (j + 2 < ntiles) load_into(p_c, t_lo + j + 2);
-      compute(lds + P * TILE_K, vlds + P * TILE_V, (t_lo + j) * BKV);
-      if (j + 1 < ntiles) store_from(std::integral_constant<int, 1 - P>{}, 1 - P);
-      __syncthreads();
-    };
+  if constexpr (UNROLL) {
     int j = 0;
     for (; j + 1 < ntiles; j += 2) {
       step(I0{}, j);
@@ -344,17 +239,21 @@ __global__ __launch_bounds__(64 * NW, (DK >= 192 ? 1 : 8 / NW)) void fa_bwd_dq_k
     }
     if (j < ntiles) step(I0{}, j);
   } else {
+    // the buffer picked at run time in the one array
     for (int j = 0; j < ntiles; ++j) {
       const int cur = j & 1;
       const bool more = j + 1 < ntiles;
-      // next K, V tiles: loads now, LDS stores after this tile's MFMAs
-      if (more) load_into(I0{}, t_lo + j + 1);
-      compute(lds + cur * TILE_K, vlds + cur * TILE_V, (t_lo + j) * BKV);
-      if (more) store_from(I0{}, cur ^ 1);
+      if (more) {
+        kdm.load(Kp, T * DK * 2, (LDS_AS char*)one + (cur ^ 1) * TILE_K, (t_lo + j + 1) * BKV, wave);
+        vdm.load(Vp, T * DV * 2, (LDS_AS char*)one + 2 * TILE_K + (cur ^ 1) * TILE_V,
+                 (t_lo + j + 1) * BKV, wave);
+      }
+      compute((LDS_AS char*)one + cur * TILE_K, (LDS_AS char*)one + 2 * TILE_K + cur * TILE_V,
+              (t_lo + j) * BKV);
+      if (more) wait_vmem();
       __syncthreads();
     }
   }
-#endif
 
   if (qrow < T) {
     bf16* Qd = a.dq + (bh * T + qrow) * DK;
@@ -616,7 +515,7 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dq_pair_kernel(BwdArgs a) {
 // that two waves per SIMD allow, so the pass runs as two launches instead:
 // MODE 1 accumulates dV only (needs S, P), MODE 2 dK only (needs S, dP,
 // dS) -- one extra S = Q K^T product buys twice the occupancy.
-template <int DK, int DV, int BQB, int NW, bool CAP, int MODE, int PF>
+template <int DK, int DV, int BQB, int NW, bool CAP, int MODE>
 __global__ __launch_bounds__(64 * NW, (DK >= 192 ? 1 : 8 / NW)) void fa_bwd_dkdv_kernel(BwdArgs a) {
   constexpr bool DO_DV = MODE != 2;
   constexpr bool DO_DK = MODE != 1;
@@ -628,29 +527,18 @@ __global__ __launch_bounds__(64 * NW, (DK >= 192 ? 1 : 8 / NW)) void fa_bwd_dkdv
   constexpr int NDBV = DV / 32;        // 32-wide blocks of dv
   constexpr int NS = BQB / 32;         // 32-query sub-tiles
   constexpr int STAT = BQB * 4;        // bytes of one lse or D tile
-  // direct-load depth: tiles in flight ahead of the one being computed
-  constexpr int DEPTH = BWD_DMA ? (MODE == 1 ? BWD_DMA_DEPTH_DV(DK) : BWD_DMA_DEPTH_DK(DK)) : 1;
-  constexpr int NBUF = BWD_DMA ? DEPTH + 1 : 2;
-#if BWD_DMA
-  // one LDS object per buffer or one array (see the dQ pass)
+  // Q, dO tiles double-buffered (see BWD_LDS_SEP / BWD_UNROLL), row
+  // statistics double-buffered beside them
   constexpr bool SEP = BWD_LDS_SEP(DK, MODE);
   constexpr bool UNROLL = BWD_UNROLL(DK);
   static_assert(UNROLL || !SEP, "run-time buffer choice needs the one-array layout");
-  __shared__ __attribute__((aligned(1024))) char one[SEP ? 16 : NBUF * (TILE_Q + TILE_O)];
+  __shared__ __attribute__((aligned(1024))) char one[SEP ? 16 : 2 * (TILE_Q + TILE_O)];
   __shared__ __attribute__((aligned(1024))) char qb0[SEP ? TILE_Q : 16];
   __shared__ __attribute__((aligned(1024))) char qb1[SEP ? TILE_Q : 16];
-  __shared__ __attribute__((aligned(1024))) char qb2[SEP && NBUF > 2 ? TILE_Q : 16];
   __shared__ __attribute__((aligned(1024))) char ob0[SEP ? TILE_O : 16];
   __shared__ __attribute__((aligned(1024))) char ob1[SEP ? TILE_O : 16];
-  __shared__ __attribute__((aligned(1024))) char ob2[SEP && NBUF > 2 ? TILE_O : 16];
   __shared__ __attribute__((aligned(16))) char sbuf[4 * STAT];
   LDS_AS char* stat = (LDS_AS char*)sbuf;  // [buf][lse2 | D][BQB] fp32
-#else
-  __shared__ __attribute__((aligned(1024))) char smem[NBUF * (TILE_Q + TILE_O) + 4 * STAT];
-  LDS_AS char* lds = (LDS_AS char*)smem;
-  LDS_AS char* const olds = lds + NBUF * TILE_Q;
-  LDS_AS char* stat = olds + NBUF * TILE_O;  // [buf][lse2 | D][BQB] fp32
-#endif
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -695,16 +583,6 @@ __global__ __launch_bounds__(64 * NW, (DK >= 192 ? 1 : 8 / NW)) void fa_bwd_dkdv
     for (int db = 0; db < (DO_DV ? NDBV : 1); ++db) dvacc[db][i] = 0.f;
   }
 
-  // Q, dO tiles and their row statistics run PF (1 or 2) iterations ahead:
-  // tile t is loaded into register set t % 2 at the top of iteration t - PF
-  // and written to LDS buffer t % 2 at the end of iteration t - 1 (the loop
-  // is unrolled by two so both indices are compile-time constants).  Two
-  // ahead hides more load latency but holds a second register set.
-#if !BWD_DMA
-  TileStage<DK, BQB, NT> qst[PF];
-  TileStage<DV, BQB, NT> dost[PF];
-  float stv[PF] = {};
-#endif
   // Iteration it visits query head (hkv*G + hi) and query tile ti, with
   // it = hi * nqt + ti; (hi, ti) advance incrementally (no integer division
   // in the loop).
@@ -730,77 +608,40 @@ __global__ __launch_bounds__(64 * NW, (DK >= 192 ? 1 : 8 / NW)) void fa_bwd_dkdv
       ++hi;
     }
   };
-#if BWD_DMA
-  // Q and dO tiles straight from HBM into LDS (no staging registers), DEPTH
-  // tiles ahead (tile t in buffer t % NBUF); the row statistics one tile
-  // ahead through a register, loaded before the newest tile batch so that
-  // waiting for all but that batch also covers them.
+  // Q and dO tiles go straight from HBM into the idle LDS buffer (no
+  // staging registers), the row statistics through one register: issued at
+  // the top of an iteration, waited for before its closing barrier.
   TileDma<DK, BQB, NW> qdm;
   TileDma<DV, BQB, NW> odm;
   qdm.init(wave, lane);
   odm.init(wave, lane);
-  constexpr int BATCH = TileDma<DK, BQB, NW>::MINPER + TileDma<DV, BQB, NW>::MINPER;
   auto qbuf = [&](auto b_c) -> LDS_AS char* {
     constexpr int b = decltype(b_c)::value;
     if constexpr (!SEP) return (LDS_AS char*)one + b * TILE_Q;
-    return b == 0 ? (LDS_AS char*)qb0 : b == 1 ? (LDS_AS char*)qb1 : (LDS_AS char*)qb2;
+    return b == 0 ? (LDS_AS char*)qb0 : (LDS_AS char*)qb1;
   };
   auto obuf = [&](auto b_c) -> LDS_AS char* {
     constexpr int b = decltype(b_c)::value;
-    if constexpr (!SEP) return (LDS_AS char*)one + NBUF * TILE_Q + b * TILE_O;
-    return b == 0 ? (LDS_AS char*)ob0 : b == 1 ? (LDS_AS char*)ob1 : (LDS_AS char*)ob2;
+    if constexpr (!SEP) return (LDS_AS char*)one + 2 * TILE_Q + b * TILE_O;
+    return b == 0 ? (LDS_AS char*)ob0 : (LDS_AS char*)ob1;
   };
-  auto issue = [&](auto b_c, int hi, int ti) __attribute__((always_inline)) {
-    qdm.load(tile_src(hi, a.q, DK), T * DK * 2, qbuf(b_c), tile_q0(ti), wave);
-    odm.load(tile_src(hi, a.dO, DV), T * DV * 2, obuf(b_c), tile_q0(ti), wave);
+  auto issue = [&](LDS_AS char* qdst, LDS_AS char* odst, int hi, int ti)
+                   __attribute__((always_inline)) -> float {
+    const float v = stage_stats(hi, ti);
+    qdm.load(tile_src(hi, a.q, DK), T * DK * 2, qdst, tile_q0(ti), wave);
+    odm.load(tile_src(hi, a.dO, DV), T * DV * 2, odst, tile_q0(ti), wave);
+    return v;
   };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
-  using I2 = std::integral_constant<int, 2>;
-  // (ha, ta): the next tile to issue
-  int ha = 0, ta = 0;
-  const float sv0 = stage_stats(0, 0);
-  issue(I0{}, ha, ta);
-  advance(ha, ta);
-  if (DEPTH > 1 && niter > 1) {
-    issue(I1{}, ha, ta);
-    advance(ha, ta);
-  }
-  if (tid < 2 * BQB) *(LDS_AS float*)(stat + tid * 4) = sv0;
-  if (DEPTH > 1 && niter > 1 && BATCH > 0)
-    wait_vmem<(DEPTH > 1 ? BATCH : 0)>();
-  else
+  {
+    const float v = issue(qbuf(I0{}), obuf(I0{}), 0, 0);
+    if (tid < 2 * BQB) *(LDS_AS float*)(stat + tid * 4) = v;
     wait_vmem();
-  int h1 = 0, t1 = 0;
-  advance(h1, t1);   // tile 1
-  __syncthreads();
-#else
-  auto load_into = [&](auto r_c, int hi, int ti) __attribute__((always_inline)) {
-    constexpr int r = decltype(r_c)::value;
-    qst[r].load(tile_src(hi, a.q, DK), tile_q0(ti), T, tid);
-    dost[r].load(tile_src(hi, a.dO, DV), tile_q0(ti), T, tid);
-    stv[r] = stage_stats(hi, ti);
-  };
-  auto store_from = [&](auto r_c) __attribute__((always_inline)) {
-    constexpr int r = decltype(r_c)::value;
-    qst[r].store(lds + r * TILE_Q, tid);
-    dost[r].store(olds + r * TILE_O, tid);
-    if (tid < 2 * BQB) *(LDS_AS float*)(stat + r * 2 * STAT + tid * 4) = stv[r];
-  };
-  using I0 = std::integral_constant<int, 0>;
-  using I1 = std::integral_constant<int, 1>;
-
-  load_into(I0{}, 0, 0);
-  store_from(I0{});
-  int h1 = 0, t1 = 0;
-  advance(h1, t1);   // tile 1
-  int h2 = h1, t2 = t1;
-  advance(h2, t2);   // tile 2
-  if constexpr (PF == 2) {
-    if (niter > 1) load_into(I1{}, h1, t1);
   }
+  int h1 = 0, t1 = 0;
+  advance(h1, t1);   // tile 1
   __syncthreads();
-#endif
 
   const int ka = kw0, kb = kw0 + 31;
   int hc = 0, tc = 0;   // tile of the current iteration
@@ -876,119 +717,42 @@ __global__ __launch_bounds__(64 * NW, (DK >= 192 ? 1 : 8 / NW)) void fa_bwd_dkdv
       }
   };
 
-#if BWD_DMA
-  // one iteration on the tile in buffer B (loop unrolled by NBUF)
-  auto step = [&](auto b_c, const int it) __attribute__((always_inline)) {
-    constexpr int B = decltype(b_c)::value;
+  // one iteration on the tile in buffer cur (qt, ot: its Q and dO tiles;
+  // qn, on: the idle buffers)
+  auto step = [&](const int it, const int cur, const LDS_AS char* qt, const LDS_AS char* ot,
+                  LDS_AS char* qn, LDS_AS char* on) __attribute__((always_inline)) {
     const bool more = it + 1 < niter;
     float sv = 0.f;
-    if (more) sv = stage_stats(h1, t1);
-    const bool issued = it + DEPTH < niter;
-    if (issued) {
-      issue(std::integral_constant<int, (B + DEPTH) % NBUF>{}, ha, ta);
-      advance(ha, ta);
-    }
-    const LDS_AS float* lse2t = (const LDS_AS float*)(stat + (it & 1) * 2 * STAT);
-    compute(qbuf(b_c), obuf(b_c), lse2t, lse2t + BQB, tile_q0(tc));
+    if (more) sv = issue(qn, on, h1, t1);
+    const LDS_AS float* lse2t = (const LDS_AS float*)(stat + cur * 2 * STAT);
+    compute(qt, ot, lse2t, lse2t + BQB, tile_q0(tc));
     if (more) {
-      if (tid < 2 * BQB) *(LDS_AS float*)(stat + ((it + 1) & 1) * 2 * STAT + tid * 4) = sv;
-      if (DEPTH > 1 && issued && BATCH > 0)
-        wait_vmem<(DEPTH > 1 ? BATCH : 0)>();
-      else
-        wait_vmem();
+      if (tid < 2 * BQB) *(LDS_AS float*)(stat + (cur ^ 1) * 2 * STAT + tid * 4) = sv;
+      wait_vmem();
     }
     __syncthreads();
     hc = h1;
     tc = t1;
     advance(h1, t1);
   };
-  int it = 0;
-  if constexpr (!UNROLL) {
-    // buffers picked at run time in the one array (depth 1)
-    static_assert(DEPTH == 1, "run-time buffer choice runs one tile ahead");
-    for (; it < niter; ++it) {
-      const int cur = it & 1;
-      const bool more = it + 1 < niter;
-      float sv = 0.f;
-      if (more) {
-        sv = stage_stats(h1, t1);
-        qdm.load(tile_src(h1, a.q, DK), T * DK * 2, (LDS_AS char*)one + (cur ^ 1) * TILE_Q,
-                 tile_q0(t1), wave);
-        odm.load(tile_src(h1, a.dO, DV), T * DV * 2,
-                 (LDS_AS char*)one + NBUF * TILE_Q + (cur ^ 1) * TILE_O, tile_q0(t1), wave);
-      }
-      const LDS_AS float* lse2t = (const LDS_AS float*)(stat + cur * 2 * STAT);
-      compute((LDS_AS char*)one + cur * TILE_Q, (LDS_AS char*)one + NBUF * TILE_Q + cur * TILE_O,
-              lse2t, lse2t + BQB, tile_q0(tc));
-      if (more) {
-        if (tid < 2 * BQB) *(LDS_AS float*)(stat + (cur ^ 1) * 2 * STAT + tid * 4) = sv;
-        wait_vmem();
-      }
-      __syncthreads();
-      hc = h1;
-      tc = t1;
-      advance(h1, t1);
-    }
-  } else if constexpr (NBUF == 2) {
-    for (; it + 1 < niter; it += 2) {
-      step(I0{}, it);
-      step(I1{}, it + 1);
-    }
-    if (it < niter) step(I0{}, it);
-  } else {
-    for (; it + 2 < niter; it += 3) {
-      step(I0{}, it);
-      step(I1{}, it + 1);
-      step(I2{}, it + 2);
-    }
-    if (it < niter) step(I0{}, it);
-    if (it + 1 < niter) step(I1{}, it + 1);
-  }
-#else
-  if constexpr (PF == 2) {
-    auto step = [&](auto p_c, const int it) __attribute__((always_inline)) {
-      constexpr int P = decltype(p_c)::value;
-      if (it + 2 < niter) load_into(p_c, h2, t2);
-      const LDS_AS float* lse2t = (const LDS_AS float*)(stat + P * 2 * STAT);
-      compute(lds + P * TILE_Q, olds + P * TILE_O, lse2t, lse2t + BQB, tile_q0(tc));
-      if (it + 1 < niter) store_from(std::integral_constant<int, 1 - P>{});
-      __syncthreads();
-      hc = h1;
-      tc = t1;
-      h1 = h2;
-      t1 = t2;
-      advance(h2, t2);
-    };
+  if constexpr (UNROLL) {
+    // loop unrolled by two: the buffers are compile-time choices
     int it = 0;
     for (; it + 1 < niter; it += 2) {
-      step(I0{}, it);
-      step(I1{}, it + 1);
+      step(it, 0, qbuf(I0{}), obuf(I0{}), qbuf(I1{}), obuf(I1{}));
+      step(it + 1, 1, qbuf(I1{}), obuf(I1{}), qbuf(I0{}), obuf(I0{}));
     }
-    if (it < niter) step(I0{}, it);
+    if (it < niter) step(it, 0, qbuf(I0{}), obuf(I0{}), qbuf(I1{}), obuf(I1{}));
   } else {
-    // one tile ahead, one register set, LDS buffer chosen at run time
+    // the buffer picked at run time in the one array
     for (int it = 0; it < niter; ++it) {
       const int cur = it & 1;
-      const bool more = it + 1 < niter;
-      if (more) {
-        qst[0].load(tile_src(h1, a.q, DK), tile_q0(t1), T, tid);
-        dost[0].load(tile_src(h1, a.dO, DV), tile_q0(t1), T, tid);
-        stv[0] = stage_stats(h1, t1);
-      }
-      const LDS_AS float* lse2t = (const LDS_AS float*)(stat + cur * 2 * STAT);
-      compute(lds + cur * TILE_Q, olds + cur * TILE_O, lse2t, lse2t + BQB, tile_q0(tc));
-      if (more) {
-        qst[0].store(lds + (cur ^ 1) * TILE_Q, tid);
-        dost[0].store(olds + (cur ^ 1) * TILE_O, tid);
-        if (tid < 2 * BQB) *(LDS_AS float*)(stat + (cur ^ 1) * 2 * STAT + tid * 4) = stv[0];
-      }
-      __syncthreads();
-      hc = h1;
-      tc = t1;
-      advance(h1, t1);
+      LDS_AS char* const q0b = (LDS_AS char*)one;
+      LDS_AS char* const o0b = (LDS_AS char*)one + 2 * TILE_Q;
+      step(it, cur, q0b + cur * TILE_Q, o0b + cur * TILE_O, q0b + (cur ^ 1) * TILE_Q,
+           o0b + (cur ^ 1) * TILE_O);
     }
   }
-#endif
 
   if (krow < T) {
     if (DO_DK) {
@@ -1035,19 +799,8 @@ __global__ __launch_bounds__(64 * NW, (DK >= 192 ? 1 : 8 / NW)) void fa_bwd_dkdv
 #define BWD192_CFG 32, 8, 64, 8, 32, 8
 #endif
 
-// Prefetch depth of the dV / dK passes, chosen by measurement: two tiles
-// ahead where the second register set fits without spilling.
-#ifndef BWD_PF_DV
-#define BWD_PF_DV(DK) ((DK) <= 128 ? 2 : 1)
-#endif
-#ifndef BWD_PF_DK
-#define BWD_PF_DK(DK) ((DK) == 192 ? 1 : 2)
-#endif
 #ifndef BWD_DQ_PAIR
 #define BWD_DQ_PAIR 1
-#endif
-#ifndef BWD_PF_DQ
-#define BWD_PF_DQ(DK) ((DK) <= 128 ? 2 : 1)
 #endif
 
 template <int DK, int DV, bool CAP, int DQ_BKV, int DQ_NW, int DV_BQB, int DV_NW, int DK_BQB,
@@ -1058,23 +811,22 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL((fa_bwd_dq_pair_kernel<256, 32, CAP>), dim3((unsigned)nqb * a.B * a.H),
                        dim3(512), 0, stream, a);
   } else {
-  const int nqb = (a.T + 32 * DQ_NW - 1) / (32 * DQ_NW);
-  hipLaunchKernelGGL((fa_bwd_dq_kernel<DK, DV, DQ_BKV, DQ_NW, CAP, BWD_PF_DQ(DK)>),
-                     dim3((unsigned)nqb * a.B * a.H),
-                     dim3(64 * DQ_NW), 0, stream, a);
+    const int nqb = (a.T + 32 * DQ_NW - 1) / (32 * DQ_NW);
+    hipLaunchKernelGGL((fa_bwd_dq_kernel<DK, DV, DQ_BKV, DQ_NW, CAP>), dim3((unsigned)nqb * a.B * a.H),
+                       dim3(64 * DQ_NW), 0, stream, a);
   }
   stage_mark(stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 vgrid((unsigned)((a.T + 32 * DV_NW - 1) / (32 * DV_NW)) * a.B * a.Hkv);
-  hipLaunchKernelGGL((fa_bwd_dkdv_kernel<DK, DV, DV_BQB, DV_NW, CAP, 1, BWD_PF_DV(DK)>), vgrid,
+  hipLaunchKernelGGL((fa_bwd_dkdv_kernel<DK, DV, DV_BQB, DV_NW, CAP, 1>), vgrid,
                      dim3(64 * DV_NW), 0,
                      stream, a);
   stage_mark(stream);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 kgrid((unsigned)((a.T + 32 * DK_NW - 1) / (32 * DK_NW)) * a.B * a.Hkv);
-  hipLaunchKernelGGL((fa_bwd_dkdv_kernel<DK, DV, DK_BQB, DK_NW, CAP, 2, BWD_PF_DK(DK)>), kgrid,
+  hipLaunchKernelGGL((fa_bwd_dkdv_kernel<DK, DV, DK_BQB, DK_NW, CAP, 2>), kgrid,
                      dim3(64 * DK_NW), 0,
                      stream, a);
   stage_mark(stream);

@@ -12,8 +12,9 @@
 //     S^T) and the online-softmax max/sum are per-lane values combined with
 //     the partner lane l^32 -- no cross-lane row reductions inside a tile;
 //   * K and V tiles (BKV keys) stream through LDS, double-buffered: the next
-//     tile's global loads are issued into registers at the top of an
-//     iteration and written to the idle padded LDS buffers at its end;
+//     tile goes straight from HBM into the idle padded LDS buffer (direct
+//     buffer loads, no staging registers), issued at the top of an
+//     iteration and waited for before its closing barrier;
 //   * P^T leaves the S^T accumulators as bf16 and is directly the B operand
 //     of O^T += V^T P^T; V^T comes from the natural V tile through the
 //     gfx950 LDS transpose read, so nothing is transposed in registers;
@@ -314,8 +315,8 @@ __global__ __launch_bounds__(64 * NW, (DK >= 256 || QW > 1 ? 1 : 8 / NW)) void f
   }
 }
 
-// Head size 256: one wave cannot hold q, the 256-wide O accumulator and
-// the staging registers at two waves per SIMD, and one wave per SIMD leaves
+// Head size 256: one wave cannot hold q and the 256-wide O accumulator at
+// two waves per SIMD, and one wave per SIMD leaves
 // the matrix pipe idle.  So waves work in pairs on the same 32 query rows:
 // wave half hf holds q[:, 128 hf .. +127], computes the partial scores over
 // its half of d, and owns output columns 128 hf .. +127.  The pair swaps
