@@ -60,6 +60,8 @@ def _fwd(**kw):
     (dict(scale=float("inf")), -1, "scale"),
     (dict(q=P + 8), -1, "aligned"),
     (dict(o=P), -1, "overlaps"),
+    # one head's [T, d] slice is addressed through a 32-bit buffer range
+    (dict(B=1, H=1, Hkv=1, T=9_000_000, d=128), -1, "exceeds 2 GiB"),
 ])
 def test_fwd_validation(kw, code, msg):
     assert _fwd(**kw) == code
