@@ -273,8 +273,8 @@ int attn_bwd(bool f32, const void* q, const void* k, const void* v, const void* 
 }
 
 // Chunking of the decode: enough (batch, KV head, chunk) units to fill the
-// chip several times over, at least 16 tiles of 32 keys per chunk (shorter
-// chunks measured slower: 4.99 against 5.33 TB/s on a 4096-key window), at
+// chip several times over, at least 32 tiles of 32 keys per chunk (shorter
+// chunks measured slower: 5.25 against 5.74 TB/s on a 4096-key window), at
 // most kDecMaxSplits chunks.  max_keys bounds the visible keys of any
 // sequence.
 void decode_split(int units, int max_keys, int* nsplit, int* chunk) {
@@ -282,7 +282,7 @@ void decode_split(int units, int max_keys, int* nsplit, int* chunk) {
 #define DEC_TARGET_UNITS 4096
 #endif
 #ifndef DEC_MIN_CHUNK
-#define DEC_MIN_CHUNK 512
+#define DEC_MIN_CHUNK 1024
 #endif
   constexpr int kTargetUnits = DEC_TARGET_UNITS, kMinChunk = DEC_MIN_CHUNK, kTile = 32;
   int ns = (kTargetUnits + units - 1) / units;

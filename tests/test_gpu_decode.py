@@ -33,6 +33,8 @@ CASES = [
     (1, 32, 1, 600, 128, 0, 0.0, False, [600]),
     (2, 64, 2, 300, 64, 100, 20.0, True, [300, 150]),
     (1, 32, 1, 2000, 256, 0, 50.0, False, [1999]),
+    # chunks wholly past a short sequence's length (empty chunks) beside a sink
+    (2, 8, 2, 3000, 128, 0, 0.0, True, [3000, 100]),
 ]
 
 
