@@ -793,7 +793,7 @@ __global__ __launch_bounds__(64 * NW, (DK >= 192 ? 1 : 8 / NW)) void fa_bwd_dkdv
 #define BWD256_CFG 32, 4, 64, 4, 32, 4
 #endif
 #ifndef BWD128_CFG
-#define BWD128_CFG 32, 8, 64, 8, 32, 8
+#define BWD128_CFG 32, 4, 64, 8, 32, 8
 #endif
 #ifndef BWD192_CFG
 #define BWD192_CFG 32, 8, 64, 8, 32, 8
