@@ -233,7 +233,7 @@ def main():
         e.record(stream)
         return e
 
-    bwd_names = ["bwd_dq", "bwd_dv", "bwd_dk"]   # the three launches of fa_bwd
+    bwd_names = ["bwd_" + n for n in fa.fa_bwd_kernels(d, dvh)]   # the launches of fa_bwd
     n_bwd = len(bwd_names)
 
     def step_fused(ev=None):

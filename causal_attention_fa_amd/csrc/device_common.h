@@ -162,12 +162,16 @@ struct TileDma {
     // raw buffer, 32-bit data format, no swizzle (gfx9 word 3)
     const __amdgpu_buffer_rsrc_t rs =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, nbytes, 0x00020000);
+    // the row offset is the same in every lane; said explicitly, so that a
+    // value the compiler merged through divergent code cannot turn the
+    // scalar offset into a per-lane loop
+    const int soff = __builtin_amdgcn_readfirstlane(row0 * 2 * D);
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
       const int ins = wave + k * NW;
       if (ins < NI)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void*)(lds + ins * 1024), 16, voff[k],
-                                                 row0 * 2 * D, 0, AUX);
+                                                 soff, 0, AUX);
     }
 #endif
   }

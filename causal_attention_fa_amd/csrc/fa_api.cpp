@@ -415,6 +415,8 @@ int fa_decode(const void* q, const void* k_cache, const void* v_cache, const int
   return finish(e, stream, fn);
 }
 
+const char* fa_bwd_kernels(int d, int d_v) { return fa::bwd_kernel_plan(d, d_v); }
+
 int fa_decode_splits(int B, int Hkv, int S, int window, int* nsplit, int* chunk) {
   if (B <= 0 || Hkv <= 0 || S <= 0 || window < 0 || !nsplit || !chunk)
     return fail(FA_ERR_INVALID_ARG, "fa_decode_splits: invalid arguments");

@@ -782,8 +782,293 @@ __global__ __launch_bounds__(64 * NW, (DK >= 192 ? 1 : 8 / NW)) void fa_bwd_dkdv
   }
 }
 
-// Tile shapes per head size: dq pass (BKV keys per tile, NW waves), dV pass
-// and dK pass (BQB queries per tile, NW waves).
+// ------------------------------------------------------ fused dK/dV pass
+// One launch for dK and dV, with paired waves: waves p and p + 4 own the
+// same 32 key rows of the workgroup's 128.  Wave p (the P side) keeps K in
+// registers; per query tile it computes S = Q K^T and P, accumulates
+// dV^T += dO^T P, and leaves the factor that multiplies (dP - D) in dS --
+// P, or with the cap P (1 - tanh^2) -- to its partner in LDS as bf16.
+// Wave p + 4 (the dS side) keeps V in registers; per tile it computes
+// dP - D with dP = dO V^T, and one tile later, once the barrier has
+// published the P side's factor, dS and dK^T += Q^T dS.  S and the exp
+// chain are computed once per tile (the two-launch scheme computes them in
+// both passes), and each wave holds one gradient accumulator, so two waves
+// per SIMD still fit.  Because the dS side lags one tile, Q tiles are
+// triple-buffered: the one being loaded, the current one, and the previous
+// one the dS side still reads.  Each buffer is its own LDS object and the
+// loop is unrolled by six (three Q slots x two dO / exchange slots), so
+// every buffer is a compile-time choice.
+template <int D, int BQB, bool CAP>
+__global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_pair_kernel(BwdArgs a) {
+  constexpr int NW = 8;
+  constexpr int BKVB = 128;                 // key rows per workgroup
+  constexpr int TILE = Lay<D>::template bytes<BQB>();
+  constexpr int NDB = D / 32;               // 32-wide blocks of dk / dv
+  constexpr int NS = BQB / 32;              // 32-query sub-tiles
+  constexpr int NC16 = BQB / 16;            // 16-query chunks (operand k steps)
+  constexpr int STAT = BQB * 4;             // bytes of one lse or D tile
+  constexpr int XB = 4 * NC16 * 1024;       // exchange: 4 pairs x NC16 x 64 lanes x 16 B
+  constexpr int PD = BWD_LDS_PD(D);
+  __shared__ __attribute__((aligned(1024))) char qs0[TILE];
+  __shared__ __attribute__((aligned(1024))) char qs1[TILE];
+  __shared__ __attribute__((aligned(1024))) char qs2[TILE];
+  __shared__ __attribute__((aligned(1024))) char os0[TILE];
+  __shared__ __attribute__((aligned(1024))) char os1[TILE];
+  __shared__ __attribute__((aligned(1024))) char xs0[XB];
+  __shared__ __attribute__((aligned(1024))) char xs1[XB];
+  __shared__ __attribute__((aligned(16))) char sbuf[4 * STAT];
+  LDS_AS char* stat = (LDS_AS char*)sbuf;  // [slot][lse2 | D][BQB] fp32
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool pside = wave < 4;
+  const int pr = wave & 3;
+  const int g = lane >> 5;
+  const int l32 = lane & 31;
+  const int T = a.T;
+  const int W = a.window;
+  const int G = a.H / a.Hkv;
+  const int nkb = (T + BKVB - 1) / BKVB;
+  const WorkItem w = decode_work(blockIdx.x, nkb, a.B, a.Hkv, 1, false);
+  const int k0 = w.blk * BKVB;
+  const int kw0 = k0 + 32 * pr;
+  const int krow = kw0 + l32;
+  const int kr = krow < T ? krow : T - 1;
+  const size_t bkv = (size_t)w.b * a.Hkv + w.hkv;
+
+  // K (P side) or V (dS side) rows: the B operand of S = Q K^T or dP = dO V^T
+  bf16x8 kv[D / 16];
+  {
+    const bf16x8* src = (const bf16x8*)((pside ? a.k : a.v) + (bkv * T + kr) * D + 8 * g);
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) kv[c] = src[2 * c];
+  }
+  f32x16 acc[NDB];   // dV (P side) or dK (dS side)
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
+
+  // Query tiles that can see keys [k0, k0 + BKVB).
+  const int qt_lo = k0 / BQB;
+  const int q_hi = W > 0 ? min(T, k0 + BKVB - 1 + W) : T;
+  const int nqt = (q_hi + BQB - 1) / BQB - qt_lo;
+  const int niter = G * nqt;
+
+  // iteration it visits query head (hkv*G + hi) and tile ti, it = hi*nqt + ti
+  auto stage_stats = [&](int hi, int ti) -> float {
+    const int hh = w.hkv * G + hi;
+    const int q0 = (qt_lo + ti) * BQB;
+    const size_t bhh = (size_t)w.b * a.H + hh;
+    float v = 0.f;
+    if (tid < 2 * BQB) {
+      int qq = q0 + (tid % BQB);
+      qq = qq < T ? qq : T - 1;
+      v = tid < BQB ? a.lse[bhh * T + qq] * kLog2e : a.Dst[bhh * T + qq];
+    }
+    return v;
+  };
+  auto tile_src = [&](int hi, const bf16* base) {
+    return base + ((size_t)w.b * a.H + w.hkv * G + hi) * T * D;
+  };
+  auto tile_q0 = [&](int ti) { return (qt_lo + ti) * BQB; };
+  auto advance = [&](int& hi, int& ti) {
+    if (++ti == nqt) {
+      ti = 0;
+      ++hi;
+    }
+  };
+  TileDma<D, BQB, NW> qdm, odm;
+  qdm.init(wave, lane);
+  odm.init(wave, lane);
+  auto qbuf = [&](auto b_c) -> LDS_AS char* {
+    constexpr int b = decltype(b_c)::value;
+    return b == 0 ? (LDS_AS char*)qs0 : b == 1 ? (LDS_AS char*)qs1 : (LDS_AS char*)qs2;
+  };
+  auto obuf = [&](auto b_c) -> LDS_AS char* {
+    constexpr int b = decltype(b_c)::value;
+    return b == 0 ? (LDS_AS char*)os0 : (LDS_AS char*)os1;
+  };
+  auto xbuf = [&](auto b_c, int ln) -> LDS_AS char* {
+    constexpr int b = decltype(b_c)::value;
+    return (b == 0 ? (LDS_AS char*)xs0 : (LDS_AS char*)xs1) + pr * NC16 * 1024 + ln * 16;
+  };
+  auto issue = [&](LDS_AS char* qdst, LDS_AS char* odst, int hi, int ti)
+                   __attribute__((always_inline)) -> float {
+    const float v = stage_stats(hi, ti);
+    qdm.load(tile_src(hi, a.q), T * D * 2, qdst, tile_q0(ti), wave);
+    odm.load(tile_src(hi, a.dO), T * D * 2, odst, tile_q0(ti), wave);
+    return v;
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  {
+    const float v = issue(qbuf(I0{}), obuf(I0{}), 0, 0);
+    if (tid < 2 * BQB) *(LDS_AS float*)(stat + tid * 4) = v;
+    wait_vmem();
+  }
+  int h1 = 0, t1 = 0;
+  advance(h1, t1);   // tile 1
+  __syncthreads();
+
+  const int ka = kw0, kb = kw0 + 31;
+  auto empty_tile = [&](int q0) {
+    return ka >= T || q0 + BQB - 1 < ka || (W > 0 && q0 - kb >= W);
+  };
+
+  // P side, one query tile: S, P, the exchange factor, dV^T += dO^T P
+  auto p_tile = [&](const LDS_AS char* Qt, const LDS_AS char* dOt, LDS_AS char* X,
+                    const LDS_AS float* lse2t, const int q0, const int ln)
+                    __attribute__((always_inline)) {
+    if (empty_tile(q0)) return;
+    const bool full = q0 >= kb && q0 + BQB <= T && (W == 0 || q0 + BQB - 1 - ka < W);
+    f32x16 s[NS];
+    mma_rows_pd<D, NS, PD>(s, Qt, kv, ln);
+    TrPipe<D, NDB, NC16, PD> otp;   // first dO^T operands, issued before the softmax
+    otp.start(dOt, 0, ln);
+    f32x16 c[CAP ? NS : 1];
+#pragma unroll
+    for (int t = 0; t < NS; ++t)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const f32x4 l4 = *(const LDS_AS f32x4*)(lse2t + 32 * t + 8 * i4 + 4 * g);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 4 * i4 + e;
+          float th;
+          const float p = fast_exp2(p_arg<CAP>(s[t][i], a, l4[e], th));
+          s[t][i] = p;
+          if (CAP) c[t][i] = p * (1.f - th * th);
+        }
+      }
+    if (!full) {
+#pragma unroll
+      for (int t = 0; t < NS; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int q = q0 + 32 * t + acc_row(i, g);
+          const bool vis = (q < T) & (krow <= q) & ((W == 0) | (krow > q - W));
+          s[t][i] = vis ? s[t][i] : 0.f;
+          if (CAP) c[t][i] = vis ? c[t][i] : 0.f;
+        }
+    }
+    bf16x8 pb[NC16];
+#pragma unroll
+    for (int c16 = 0; c16 < NC16; ++c16) {
+      float tp[8], tc[8];
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        tp[jj] = s[c16 >> 1][8 * (c16 & 1) + jj];
+        if (CAP) tc[jj] = c[c16 >> 1][8 * (c16 & 1) + jj];
+      }
+      pb[c16] = pack_bf16(tp);
+      *(LDS_AS bf16x8*)(X + c16 * 1024) = CAP ? pack_bf16(tc) : pb[c16];
+    }
+    otp.run(acc, dOt, 0, pb, ln);
+  };
+  // dS side, the previous tile: dS = factor * (dP - D), dK^T += Q^T dS
+  auto ds_prev = [&](f32x16 (&dpm)[NS], const LDS_AS char* Qt, const LDS_AS char* X,
+                     const int q0, const int ln) __attribute__((always_inline)) {
+    if (empty_tile(q0)) return;
+    TrPipe<D, NDB, NC16, PD> qtp;
+    qtp.start(Qt, 0, ln);
+    bf16x8 dsb[NC16];
+#pragma unroll
+    for (int c16 = 0; c16 < NC16; ++c16) {
+      const bf16x8 f = *(const LDS_AS bf16x8*)(X + c16 * 1024);
+      float td[8];
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) td[jj] = (float)f[jj] * dpm[c16 >> 1][8 * (c16 & 1) + jj];
+      dsb[c16] = pack_bf16(td);
+    }
+    qtp.run(acc, Qt, 0, dsb, ln);
+  };
+  // dS side, the current tile: dP - D
+  auto dp_cur = [&](f32x16 (&dpm)[NS], const LDS_AS char* dOt, const LDS_AS float* Dt,
+                    const int q0, const int ln) __attribute__((always_inline)) {
+    if (empty_tile(q0)) return;
+    mma_rows_pd<D, NS, PD>(dpm, dOt, kv, ln);
+#pragma unroll
+    for (int t = 0; t < NS; ++t)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const f32x4 d4 = *(const LDS_AS f32x4*)(Dt + 32 * t + 8 * i4 + 4 * g);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dpm[t][4 * i4 + e] -= d4[e];
+      }
+  };
+
+  // Iteration it (0 .. niter; the last one only finishes the dS side's
+  // lag): load tile it+1, P side on tile it, dS side on tiles it-1 and it.
+  // The two sides run separate copies of the loop (the same loads and
+  // barriers), so that neither holds the other's registers.
+  int tc = 0, tp = 0;   // tile index (within the head) of tiles it and it-1
+  f32x16 dpm[NS];       // dS side: dP - D of the previous tile
+  auto step = [&](auto side_c, const int it, auto qc, auto qn, auto qp, auto oc, auto on,
+                  auto xc, auto xp) __attribute__((always_inline)) {
+    constexpr bool PS = decltype(side_c)::value;
+    constexpr int sc = decltype(oc)::value;   // stats slot = dO slot
+    const bool more = it + 1 < niter;
+    float sv = 0.f;
+    if (more) sv = issue(qbuf(qn), obuf(on), h1, t1);
+    const LDS_AS float* lse2t = (const LDS_AS float*)(stat + sc * 2 * STAT);
+    // the lane index laundered per step: the LDS addresses derived from it
+    // are recomputed here instead of hoisted out of the loop, where the
+    // per-lane bases of all seven buffers would stay live
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    if constexpr (PS) {
+      if (it < niter) p_tile(qbuf(qc), obuf(oc), xbuf(xc, ln), lse2t, tile_q0(tc), ln);
+    } else {
+      if (it > 0) ds_prev(dpm, qbuf(qp), xbuf(xp, ln), tile_q0(tp), ln);
+      if (it < niter) dp_cur(dpm, obuf(oc), lse2t + BQB, tile_q0(tc), ln);
+    }
+    if (more) {
+      if (tid < 2 * BQB) *(LDS_AS float*)(stat + (sc ^ 1) * 2 * STAT + tid * 4) = sv;
+      wait_vmem();
+    }
+    __syncthreads();
+    tp = tc;
+    tc = t1;
+    advance(h1, t1);
+  };
+  auto run = [&](auto side_c) __attribute__((always_inline)) {
+    for (int it = 0; it <= niter; it += 6) {
+      step(side_c, it, I0{}, I1{}, I2{}, I0{}, I1{}, I0{}, I1{});
+      if (it + 1 > niter) break;
+      step(side_c, it + 1, I1{}, I2{}, I0{}, I1{}, I0{}, I1{}, I0{});
+      if (it + 2 > niter) break;
+      step(side_c, it + 2, I2{}, I0{}, I1{}, I0{}, I1{}, I0{}, I1{});
+      if (it + 3 > niter) break;
+      step(side_c, it + 3, I0{}, I1{}, I2{}, I1{}, I0{}, I1{}, I0{});
+      if (it + 4 > niter) break;
+      step(side_c, it + 4, I1{}, I2{}, I0{}, I0{}, I1{}, I0{}, I1{});
+      if (it + 5 > niter) break;
+      step(side_c, it + 5, I2{}, I0{}, I1{}, I1{}, I0{}, I1{}, I0{});
+    }
+  };
+  if (pside)
+    run(std::true_type{});
+  else
+    run(std::false_type{});
+
+  if (krow < T) {
+    bf16* dst = (pside ? a.dv : a.dk) + (bkv * T + krow) * D;
+    const float f = pside ? 1.f : a.scale;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        bf16x4 v4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v4[e] = (bf16)(acc[db][4 * i4 + e] * f);
+        *(bf16x4*)(dst + 32 * db + 8 * i4 + 4 * g) = v4;
+      }
+  }
+}
+
 // Tile shapes per head size: dq pass (keys per tile, waves), dV pass and
 // dK pass (queries per tile, waves); chosen by measurement on MI355X.
 #ifndef BWD64_CFG
@@ -802,6 +1087,10 @@ __global__ __launch_bounds__(64 * NW, (DK >= 192 ? 1 : 8 / NW)) void fa_bwd_dkdv
 #ifndef BWD_DQ_PAIR
 #define BWD_DQ_PAIR 1
 #endif
+// dK and dV in one launch with paired waves (d = 64, 128)
+#ifndef BWD_KV_PAIR
+#define BWD_KV_PAIR 1
+#endif
 
 template <int DK, int DV, bool CAP, int DQ_BKV, int DQ_NW, int DV_BQB, int DV_NW, int DK_BQB,
           int DK_NW>
@@ -818,6 +1107,12 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   stage_mark(stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if constexpr (DK == DV && (DK == 64 || DK == 128) && BWD_KV_PAIR) {
+    const dim3 grid((unsigned)((a.T + 127) / 128) * a.B * a.Hkv);
+    hipLaunchKernelGGL((fa_bwd_dkdv_pair_kernel<DK, 64, CAP>), grid, dim3(512), 0, stream, a);
+    stage_mark(stream);
+    return hipGetLastError();
+  }
   const dim3 vgrid((unsigned)((a.T + 32 * DV_NW - 1) / (32 * DV_NW)) * a.B * a.Hkv);
   hipLaunchKernelGGL((fa_bwd_dkdv_kernel<DK, DV, DV_BQB, DV_NW, CAP, 1>), vgrid,
                      dim3(64 * DV_NW), 0,
@@ -838,6 +1133,12 @@ static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
   if (a.cap_log2e > 0.f)
     return launch_bwd_t<DK, DV, true, DQ_BKV, DQ_NW, DV_BQB, DV_NW, DK_BQB, DK_NW>(a, stream);
   return launch_bwd_t<DK, DV, false, DQ_BKV, DQ_NW, DV_BQB, DV_NW, DK_BQB, DK_NW>(a, stream);
+}
+
+const char* bwd_kernel_plan(int d, int d_v) {
+  if (d == d_v && (d == 64 || d == 128)) return BWD_KV_PAIR ? "dq,dkdv" : "dq,dv,dk";
+  if ((d == d_v && d == 256) || (d == 192 && d_v == 128)) return "dq,dv,dk";
+  return nullptr;
 }
 
 hipError_t launch_bwd_bf16(const BwdArgs& a, int d, int d_v, hipStream_t stream) {

@@ -112,6 +112,9 @@ hipError_t launch_fill_f32(float* p, int n, float v, hipStream_t stream);
 // x in {64, 128, 256} and (192, 128)).
 hipError_t launch_fwd_bf16(const FwdArgs& a, int d, int d_v, hipStream_t stream);
 hipError_t launch_bwd_bf16(const BwdArgs& a, int d, int d_v, hipStream_t stream);
+// kernels launch_bwd_bf16 runs for (d, d_v), in order ("dq,dkdv" or
+// "dq,dv,dk"); null for unsupported sizes
+const char* bwd_kernel_plan(int d, int d_v);
 hipError_t launch_fwd_f32(const F32Args& a, hipStream_t stream);
 hipError_t launch_bwd_f32(const F32Args& a, hipStream_t stream);
 hipError_t launch_decode_bf16(const DecodeArgs& a, int d, bool cap, hipStream_t stream);

@@ -80,6 +80,8 @@ _lib.fa_layer_rope_theta.argtypes = [_I, ctypes.c_double, ctypes.c_double, _I,
 _lib.fa_layer_rope_theta.restype = _I
 _lib.fa_set_stage_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), _I]
 _lib.fa_set_stage_events.restype = _I
+_lib.fa_bwd_kernels.argtypes = [_I, _I]
+_lib.fa_bwd_kernels.restype = ctypes.c_char_p
 _lib.fa_last_error.argtypes = []
 _lib.fa_last_error.restype = ctypes.c_char_p
 
@@ -88,7 +90,7 @@ EXPORTS = ("fa_fwd", "fa_bwd", "fa_fwd_sink", "fa_bwd_sink", "fa_fwd_vdim", "fa_
            "fa_decode", "fa_decode_splits", "rope_apply", "rope_apply_bwd", "fa_fwd_f32",
            "fa_bwd_f32", "rope_apply_f32", "rope_apply_bwd_f32", "fa_layer_window", "fa_rope_inv_freq",
            "fa_rope_inv_freq_llama3", "fa_layer_rope_theta", "fa_set_stage_events",
-           "fa_last_error")
+           "fa_bwd_kernels", "fa_last_error")
 
 
 class FAError(RuntimeError):
@@ -214,6 +216,14 @@ def fa_decode(q, k_cache, v_cache, lens, o, lse, sinks, B, H, Hkv, S, d, scale, 
     return _check(_lib.fa_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(lens), _ptr(o),
                                  _ptr(lse), _ptr(sinks), B, H, Hkv, S, d, float(scale), window,
                                  float(softcap), _stream(stream)))
+
+
+def fa_bwd_kernels(d, d_v=None):
+    """Names of the kernels the bf16 backward launches for (d, d_v), in order."""
+    r = _lib.fa_bwd_kernels(d, d if d_v is None else d_v)
+    if r is None:
+        raise FAError(FA_ERR_UNSUPPORTED, f"fa_bwd_kernels: unsupported head sizes ({d}, {d_v})")
+    return r.decode().split(",")
 
 
 def fa_decode_splits(B, Hkv, S, window=0):

@@ -244,11 +244,18 @@ int fa_layer_rope_theta(int layer, double theta, double theta_global,
  * `events` are `count` (<= 16) hipEvent_t handles created by the caller.
  * While armed (count > 0), every later call on this thread records
  * events[0] on its stream before its first kernel and events[i] right
- * after its i-th kernel launch, for i < count (fa_bwd launches 3 kernels:
- * dq, dv, dk; fa_fwd and rope_* launch 1).  count = 0
+ * after its i-th kernel launch, for i < count (fa_bwd launches the kernels
+ * fa_bwd_kernels names; fa_fwd and rope_* launch 1).  count = 0
  * disarms.  Returns 0, or FA_ERR_INVALID_ARG for count outside 0..16 or a
  * null handle.  Thread-local state; no device work. */
 int fa_set_stage_events(void* const* events, int count);
+
+/* The kernels the bf16 fa_bwd (and its _rope, _vdim, _sink variants)
+ * launches for head sizes (d, d_v), in launch order, comma-separated:
+ * "dq,dkdv" (dK and dV in one pass) or "dq,dv,dk"; null for sizes the
+ * backward does not support.  Static string owned by the library; host
+ * only, no device work. */
+const char* fa_bwd_kernels(int d, int d_v);
 
 /* Thread-local text of the last failure ("" if none yet). */
 const char* fa_last_error(void);

@@ -152,3 +152,15 @@ def test_layer_rope_theta_matches_oracle():
         for tg in (0.0, 1e6):
             for layer in range(13):
                 assert fa.fa_layer_rope_theta(layer, 1e4, tg, ge) == OR.layer_rope_theta(layer, 1e4, tg, ge)
+
+
+def test_bwd_kernel_plan():
+    """Every supported head-size pair names the dq pass first and covers dK
+    and dV exactly once; unsupported sizes raise."""
+    for d, dv in ((64, 64), (128, 128), (256, 256), (192, 128)):
+        plan = fa.fa_bwd_kernels(d, dv)
+        assert plan[0] == "dq"
+        assert plan[1:] in (["dkdv"], ["dv", "dk"]), plan
+    for d, dv in ((96, 96), (128, 64), (0, 0)):
+        with pytest.raises(fa.FAError):
+            fa.fa_bwd_kernels(d, dv)
