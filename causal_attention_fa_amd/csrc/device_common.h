@@ -221,6 +221,105 @@ __device__ __forceinline__ bf16x8 lds_tr_operand(const LDS_AS char* tile, int ro
   return __builtin_bit_cast(bf16x8, v);
 }
 
+// The same two read patterns with the per-lane part of the address
+// computed once.  In a Lay<D> tile, moving the row operand by a 32-row
+// block or by two 16-column chunks, and the transposed operand by a
+// 16-row chunk or a 32-column block, moves whole rows or whole 64-byte
+// groups and leaves the XOR alone, so every operand address is
+//   tile + (one of four per-lane offsets) + a compile-time constant:
+//   row operand (rows 32t.., chunk c):  row_e or row_o (c even / odd)
+//                                       + 32t * STRIDE + 64 (c >> 1)
+//   transposed (rows 16 c16.., cols 32 db..): tr_lo, tr_hi (its two
+//                                       8-row reads) + 16 c16 * STRIDE + 64 db
+// (the formulas are those of lds_row_operand / lds_tr_operand with the
+// constant parts split off; checked against Lay<D>::off for d = 64..256).
+template <int D>
+struct LaneOffs {
+  static constexpr int S = Lay<D>::STRIDE;
+  int row_e, row_o, tr_lo, tr_hi;
+  __device__ __forceinline__ void init(int lane) {
+    const int l32 = lane & 31, g = lane >> 5, x = (l32 >> 2) & 3;
+    const int r = lane & 15, half = (lane >> 4) & 1, b = (r & 3) >> 1;
+    row_e = l32 * S + 16 * (g ^ x);
+    row_o = l32 * S + 16 * ((2 + g) ^ x);
+    tr_lo = (4 * g + (r >> 2)) * S + 16 * ((2 * half + b) ^ g) + 8 * (r & 1);
+    tr_hi = (4 * g + (r >> 2) + 8) * S + 16 * ((2 * half + b) ^ (g + 2)) + 8 * (r & 1);
+  }
+  // hide the values from loop-invariant code motion: addresses derived
+  // after this are recomputed where they are used instead of being hoisted
+  // (one add per buffer) -- for loops that touch many LDS buffers
+  __device__ __forceinline__ void refresh() {
+    asm volatile("" : "+v"(row_e), "+v"(row_o), "+v"(tr_lo), "+v"(tr_hi));
+  }
+};
+
+template <int D>
+__device__ __forceinline__ bf16x8 lds_row_op(const LDS_AS char* tile, const LaneOffs<D>& o, int t,
+                                             int c) {
+  return *(const LDS_AS bf16x8*)(tile + ((c & 1) ? o.row_o : o.row_e) + 32 * t * Lay<D>::STRIDE +
+                                 64 * (c >> 1));
+}
+
+template <int D>
+__device__ __forceinline__ bf16x8 lds_tr_op(const LDS_AS char* tile, const LaneOffs<D>& o, int c16,
+                                            int db) {
+  const int imm = 16 * c16 * Lay<D>::STRIDE + 64 * db;
+  s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(tile + o.tr_lo + imm));
+  s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(tile + o.tr_hi + imm));
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  s16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// mma_rows_pd with the precomputed lane offsets (PD >= 1).
+template <int D, int NS, int PD>
+__device__ __forceinline__ void mma_rows_lo(f32x16 (&acc)[NS], const LDS_AS char* tile,
+                                            const LaneOffs<D>& o, const bf16x8 (&breg)[D / 16]) {
+  static_assert(PD >= 1, "reads run at least one chunk ahead");
+  constexpr int NC = D / 16, R = PD + 1;
+  bf16x8 op[R][NS];
+#pragma unroll
+  for (int t = 0; t < NS; ++t)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[t][i] = 0.f;
+#pragma unroll
+  for (int c = 0; c < PD && c < NC; ++c)
+#pragma unroll
+    for (int t = 0; t < NS; ++t) op[c % R][t] = lds_row_op<D>(tile, o, t, c);
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    if (c + PD < NC) {
+#pragma unroll
+      for (int t = 0; t < NS; ++t) op[(c + PD) % R][t] = lds_row_op<D>(tile, o, t, c + PD);
+    }
+#pragma unroll
+    for (int t = 0; t < NS; ++t) acc[t] = mfma32(op[c % R][t], breg[c], acc[t]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// TrPipe with the precomputed lane offsets (PD >= 1, col0 = 0).
+template <int D, int NDB, int NC16, int PD>
+struct TrPipeLo {
+  static_assert(PD >= 1, "reads run at least one MFMA ahead");
+  static constexpr int N = NC16 * NDB, R = PD + 1;
+  bf16x8 op[R];
+  __device__ __forceinline__ void start(const LDS_AS char* tile, const LaneOffs<D>& o) {
+#pragma unroll
+    for (int k = 0; k < PD && k < N; ++k) op[k % R] = lds_tr_op<D>(tile, o, k / NDB, k % NDB);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  __device__ __forceinline__ void run(f32x16 (&acc)[NDB], const LDS_AS char* tile,
+                                      const LaneOffs<D>& o, const bf16x8 (&breg)[NC16]) {
+#pragma unroll
+    for (int k = 0; k < N; ++k) {
+      if (k + PD < N) op[(k + PD) % R] = lds_tr_op<D>(tile, o, (k + PD) / NDB, (k + PD) % NDB);
+      acc[k % NDB] = mfma32(op[k % R], breg[k / NDB], acc[k % NDB]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+};
+
 // acc[t] = sum_c A_t(c) B(c) over the D/16 chunks of d, where A_t(c) is
 // the row operand of rows 32t.. of `tile` (read from LDS) and B(c) = breg[c]
 // lives in registers: NS independent 32x32 accumulators.  The LDS operands

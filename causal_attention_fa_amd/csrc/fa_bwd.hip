@@ -592,12 +592,16 @@ __global__ __launch_bounds__(64 * NW, (DK >= 192 ? 1 : 8 / NW)) void fa_bwd_dkdv
     const size_t bhh = (size_t)w.b * a.H + hh;
     float v = 0.f;
     if (tid < 2 * BQB) {
+      // one load, raw (the lse is scaled when it is stored to LDS): a use
+      // here would make these waves wait for the load at once
       int qq = q0 + (tid % BQB);
       qq = qq < T ? qq : T - 1;
-      v = tid < BQB ? a.lse[bhh * T + qq] * kLog2e : a.Dst[bhh * T + qq];
+      v = (tid < BQB ? a.lse : a.Dst)[bhh * T + qq];
     }
     return v;
   };
+  // lse (log2 units) or D, as stored in the LDS statistics tile
+  auto stat_val = [&](float v) { return tid < BQB ? v * kLog2e : v; };
   auto tile_src = [&](int hi, const bf16* base, int dd) {
     return base + ((size_t)w.b * a.H + w.hkv * G + hi) * T * dd;
   };
@@ -636,7 +640,7 @@ __global__ __launch_bounds__(64 * NW, (DK >= 192 ? 1 : 8 / NW)) void fa_bwd_dkdv
   using I1 = std::integral_constant<int, 1>;
   {
     const float v = issue(qbuf(I0{}), obuf(I0{}), 0, 0);
-    if (tid < 2 * BQB) *(LDS_AS float*)(stat + tid * 4) = v;
+    if (tid < 2 * BQB) *(LDS_AS float*)(stat + tid * 4) = stat_val(v);
     wait_vmem();
   }
   int h1 = 0, t1 = 0;
@@ -727,7 +731,7 @@ __global__ __launch_bounds__(64 * NW, (DK >= 192 ? 1 : 8 / NW)) void fa_bwd_dkdv
     const LDS_AS float* lse2t = (const LDS_AS float*)(stat + cur * 2 * STAT);
     compute(qt, ot, lse2t, lse2t + BQB, tile_q0(tc));
     if (more) {
-      if (tid < 2 * BQB) *(LDS_AS float*)(stat + (cur ^ 1) * 2 * STAT + tid * 4) = sv;
+      if (tid < 2 * BQB) *(LDS_AS float*)(stat + (cur ^ 1) * 2 * STAT + tid * 4) = stat_val(sv);
       wait_vmem();
     }
     __syncthreads();
@@ -783,6 +787,18 @@ __global__ __launch_bounds__(64 * NW, (DK >= 192 ? 1 : 8 / NW)) void fa_bwd_dkdv
 }
 
 // ------------------------------------------------------ fused dK/dV pass
+#ifndef PAIR_LAUNDER
+#define PAIR_LAUNDER 1
+#endif
+#ifndef PAIR_PD
+#define PAIR_PD(D) 3
+#endif
+#ifndef PAIR_BQB
+#define PAIR_BQB 64
+#endif
+#ifndef PAIR_OSLOTS
+#define PAIR_OSLOTS 3
+#endif
 // One launch for dK and dV, with paired waves: waves p and p + 4 own the
 // same 32 key rows of the workgroup's 128.  Wave p (the P side) keeps K in
 // registers; per query tile it computes S = Q K^T and P, accumulates
@@ -808,14 +824,15 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_pair_kernel(BwdArgs a) {
   constexpr int NC16 = BQB / 16;            // 16-query chunks (operand k steps)
   constexpr int STAT = BQB * 4;             // bytes of one lse or D tile
   constexpr int XB = 4 * NC16 * 1024;       // exchange: 4 pairs x NC16 x 64 lanes x 16 B
-  constexpr int PD = BWD_LDS_PD(D);
+  constexpr int PD = PAIR_PD(D);
+  constexpr int OSLOTS = PAIR_OSLOTS;   // dO slots: 2 (loop unrolled by 6) or 3 (by 3)
   __shared__ __attribute__((aligned(1024))) char qs0[TILE];
   __shared__ __attribute__((aligned(1024))) char qs1[TILE];
   __shared__ __attribute__((aligned(1024))) char qs2[TILE];
   __shared__ __attribute__((aligned(1024))) char os0[TILE];
   __shared__ __attribute__((aligned(1024))) char os1[TILE];
-  __shared__ __attribute__((aligned(1024))) char xs0[XB];
-  __shared__ __attribute__((aligned(1024))) char xs1[XB];
+  __shared__ __attribute__((aligned(1024))) char os2[OSLOTS == 3 ? TILE : 16];
+  __shared__ __attribute__((aligned(1024))) char xsa[2 * XB];
   __shared__ __attribute__((aligned(16))) char sbuf[4 * STAT];
   LDS_AS char* stat = (LDS_AS char*)sbuf;  // [slot][lse2 | D][BQB] fp32
 
@@ -863,12 +880,16 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_pair_kernel(BwdArgs a) {
     const size_t bhh = (size_t)w.b * a.H + hh;
     float v = 0.f;
     if (tid < 2 * BQB) {
+      // one load, raw (the lse is scaled when it is stored to LDS): a use
+      // here would make these waves wait for the load at once
       int qq = q0 + (tid % BQB);
       qq = qq < T ? qq : T - 1;
-      v = tid < BQB ? a.lse[bhh * T + qq] * kLog2e : a.Dst[bhh * T + qq];
+      v = (tid < BQB ? a.lse : a.Dst)[bhh * T + qq];
     }
     return v;
   };
+  // lse (log2 units) or D, as stored in the LDS statistics tile
+  auto stat_val = [&](float v) { return tid < BQB ? v * kLog2e : v; };
   auto tile_src = [&](int hi, const bf16* base) {
     return base + ((size_t)w.b * a.H + w.hkv * G + hi) * T * D;
   };
@@ -888,12 +909,10 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_pair_kernel(BwdArgs a) {
   };
   auto obuf = [&](auto b_c) -> LDS_AS char* {
     constexpr int b = decltype(b_c)::value;
-    return b == 0 ? (LDS_AS char*)os0 : (LDS_AS char*)os1;
+    return b == 0 ? (LDS_AS char*)os0 : b == 1 ? (LDS_AS char*)os1 : (LDS_AS char*)os2;
   };
-  auto xbuf = [&](auto b_c, int ln) -> LDS_AS char* {
-    constexpr int b = decltype(b_c)::value;
-    return (b == 0 ? (LDS_AS char*)xs0 : (LDS_AS char*)xs1) + pr * NC16 * 1024 + ln * 16;
-  };
+  // exchange slot b (written with ordinary LDS stores: a run-time choice)
+  auto xbuf = [&](int b, int xo) -> LDS_AS char* { return (LDS_AS char*)xsa + b * XB + xo; };
   auto issue = [&](LDS_AS char* qdst, LDS_AS char* odst, int hi, int ti)
                    __attribute__((always_inline)) -> float {
     const float v = stage_stats(hi, ti);
@@ -906,7 +925,7 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_pair_kernel(BwdArgs a) {
   using I2 = std::integral_constant<int, 2>;
   {
     const float v = issue(qbuf(I0{}), obuf(I0{}), 0, 0);
-    if (tid < 2 * BQB) *(LDS_AS float*)(stat + tid * 4) = v;
+    if (tid < 2 * BQB) *(LDS_AS float*)(stat + tid * 4) = stat_val(v);
     wait_vmem();
   }
   int h1 = 0, t1 = 0;
@@ -920,14 +939,14 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_pair_kernel(BwdArgs a) {
 
   // P side, one query tile: S, P, the exchange factor, dV^T += dO^T P
   auto p_tile = [&](const LDS_AS char* Qt, const LDS_AS char* dOt, LDS_AS char* X,
-                    const LDS_AS float* lse2t, const int q0, const int ln)
+                    const LDS_AS float* lse2t, const int q0, const LaneOffs<D>& lo)
                     __attribute__((always_inline)) {
     if (empty_tile(q0)) return;
     const bool full = q0 >= kb && q0 + BQB <= T && (W == 0 || q0 + BQB - 1 - ka < W);
     f32x16 s[NS];
-    mma_rows_pd<D, NS, PD>(s, Qt, kv, ln);
-    TrPipe<D, NDB, NC16, PD> otp;   // first dO^T operands, issued before the softmax
-    otp.start(dOt, 0, ln);
+    mma_rows_lo<D, NS, PD>(s, Qt, lo, kv);
+    TrPipeLo<D, NDB, NC16, PD> otp;   // first dO^T operands, issued before the softmax
+    otp.start(dOt, lo);
     f32x16 c[CAP ? NS : 1];
 #pragma unroll
     for (int t = 0; t < NS; ++t)
@@ -966,14 +985,14 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_pair_kernel(BwdArgs a) {
       pb[c16] = pack_bf16(tp);
       *(LDS_AS bf16x8*)(X + c16 * 1024) = CAP ? pack_bf16(tc) : pb[c16];
     }
-    otp.run(acc, dOt, 0, pb, ln);
+    otp.run(acc, dOt, lo, pb);
   };
   // dS side, the previous tile: dS = factor * (dP - D), dK^T += Q^T dS
   auto ds_prev = [&](f32x16 (&dpm)[NS], const LDS_AS char* Qt, const LDS_AS char* X,
-                     const int q0, const int ln) __attribute__((always_inline)) {
+                     const int q0, const LaneOffs<D>& lo) __attribute__((always_inline)) {
     if (empty_tile(q0)) return;
-    TrPipe<D, NDB, NC16, PD> qtp;
-    qtp.start(Qt, 0, ln);
+    TrPipeLo<D, NDB, NC16, PD> qtp;
+    qtp.start(Qt, lo);
     bf16x8 dsb[NC16];
 #pragma unroll
     for (int c16 = 0; c16 < NC16; ++c16) {
@@ -983,13 +1002,13 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_pair_kernel(BwdArgs a) {
       for (int jj = 0; jj < 8; ++jj) td[jj] = (float)f[jj] * dpm[c16 >> 1][8 * (c16 & 1) + jj];
       dsb[c16] = pack_bf16(td);
     }
-    qtp.run(acc, Qt, 0, dsb, ln);
+    qtp.run(acc, Qt, lo, dsb);
   };
   // dS side, the current tile: dP - D
   auto dp_cur = [&](f32x16 (&dpm)[NS], const LDS_AS char* dOt, const LDS_AS float* Dt,
-                    const int q0, const int ln) __attribute__((always_inline)) {
+                    const int q0, const LaneOffs<D>& lo) __attribute__((always_inline)) {
     if (empty_tile(q0)) return;
-    mma_rows_pd<D, NS, PD>(dpm, dOt, kv, ln);
+    mma_rows_lo<D, NS, PD>(dpm, dOt, lo, kv);
 #pragma unroll
     for (int t = 0; t < NS; ++t)
 #pragma unroll
@@ -1005,28 +1024,35 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_pair_kernel(BwdArgs a) {
   // The two sides run separate copies of the loop (the same loads and
   // barriers), so that neither holds the other's registers.
   int tc = 0, tp = 0;   // tile index (within the head) of tiles it and it-1
+  LaneOffs<D> lo0;
+  lo0.init(lane);
+  const int xo0 = pr * NC16 * 1024 + lane * 16;   // this lane's exchange slot
   f32x16 dpm[NS];       // dS side: dP - D of the previous tile
-  auto step = [&](auto side_c, const int it, auto qc, auto qn, auto qp, auto oc, auto on,
-                  auto xc, auto xp) __attribute__((always_inline)) {
+  auto step = [&](auto side_c, const int it, auto qc, auto qn, auto qp, auto oc, auto on)
+                  __attribute__((always_inline)) {
     constexpr bool PS = decltype(side_c)::value;
-    constexpr int sc = decltype(oc)::value;   // stats slot = dO slot
+    const int sc = it & 1;   // stats and exchange slot of tile it
     const bool more = it + 1 < niter;
     float sv = 0.f;
     if (more) sv = issue(qbuf(qn), obuf(on), h1, t1);
     const LDS_AS float* lse2t = (const LDS_AS float*)(stat + sc * 2 * STAT);
-    // the lane index laundered per step: the LDS addresses derived from it
-    // are recomputed here instead of hoisted out of the loop, where the
-    // per-lane bases of all seven buffers would stay live
-    int ln = lane;
-    asm volatile("" : "+v"(ln));
+    // lane offsets refreshed per step: the buffer addresses derived from
+    // them are formed here (one add per buffer) instead of hoisted out of
+    // the loop, where those of all the buffers would stay live
+    LaneOffs<D> lo = lo0;
+    int xo = xo0;
+#if PAIR_LAUNDER
+    lo.refresh();
+    asm volatile("" : "+v"(xo));
+#endif
     if constexpr (PS) {
-      if (it < niter) p_tile(qbuf(qc), obuf(oc), xbuf(xc, ln), lse2t, tile_q0(tc), ln);
+      if (it < niter) p_tile(qbuf(qc), obuf(oc), xbuf(sc, xo), lse2t, tile_q0(tc), lo);
     } else {
-      if (it > 0) ds_prev(dpm, qbuf(qp), xbuf(xp, ln), tile_q0(tp), ln);
-      if (it < niter) dp_cur(dpm, obuf(oc), lse2t + BQB, tile_q0(tc), ln);
+      if (it > 0) ds_prev(dpm, qbuf(qp), xbuf(sc ^ 1, xo), tile_q0(tp), lo);
+      if (it < niter) dp_cur(dpm, obuf(oc), lse2t + BQB, tile_q0(tc), lo);
     }
     if (more) {
-      if (tid < 2 * BQB) *(LDS_AS float*)(stat + (sc ^ 1) * 2 * STAT + tid * 4) = sv;
+      if (tid < 2 * BQB) *(LDS_AS float*)(stat + (sc ^ 1) * 2 * STAT + tid * 4) = stat_val(sv);
       wait_vmem();
     }
     __syncthreads();
@@ -1035,18 +1061,28 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_pair_kernel(BwdArgs a) {
     advance(h1, t1);
   };
   auto run = [&](auto side_c) __attribute__((always_inline)) {
-    for (int it = 0; it <= niter; it += 6) {
-      step(side_c, it, I0{}, I1{}, I2{}, I0{}, I1{}, I0{}, I1{});
-      if (it + 1 > niter) break;
-      step(side_c, it + 1, I1{}, I2{}, I0{}, I1{}, I0{}, I1{}, I0{});
-      if (it + 2 > niter) break;
-      step(side_c, it + 2, I2{}, I0{}, I1{}, I0{}, I1{}, I0{}, I1{});
-      if (it + 3 > niter) break;
-      step(side_c, it + 3, I0{}, I1{}, I2{}, I1{}, I0{}, I1{}, I0{});
-      if (it + 4 > niter) break;
-      step(side_c, it + 4, I1{}, I2{}, I0{}, I0{}, I1{}, I0{}, I1{});
-      if (it + 5 > niter) break;
-      step(side_c, it + 5, I2{}, I0{}, I1{}, I1{}, I0{}, I1{}, I0{});
+    if constexpr (OSLOTS == 3) {
+      for (int it = 0; it <= niter; it += 3) {
+        step(side_c, it, I0{}, I1{}, I2{}, I0{}, I1{});
+        if (it + 1 > niter) break;
+        step(side_c, it + 1, I1{}, I2{}, I0{}, I1{}, I2{});
+        if (it + 2 > niter) break;
+        step(side_c, it + 2, I2{}, I0{}, I1{}, I2{}, I0{});
+      }
+    } else {
+      for (int it = 0; it <= niter; it += 6) {
+        step(side_c, it, I0{}, I1{}, I2{}, I0{}, I1{});
+        if (it + 1 > niter) break;
+        step(side_c, it + 1, I1{}, I2{}, I0{}, I1{}, I0{});
+        if (it + 2 > niter) break;
+        step(side_c, it + 2, I2{}, I0{}, I1{}, I0{}, I1{});
+        if (it + 3 > niter) break;
+        step(side_c, it + 3, I0{}, I1{}, I2{}, I1{}, I0{});
+        if (it + 4 > niter) break;
+        step(side_c, it + 4, I1{}, I2{}, I0{}, I0{}, I1{});
+        if (it + 5 > niter) break;
+        step(side_c, it + 5, I2{}, I0{}, I1{}, I1{}, I0{});
+      }
     }
   };
   if (pside)
@@ -1109,7 +1145,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   if (e != hipSuccess) return e;
   if constexpr (DK == DV && (DK == 64 || DK == 128) && BWD_KV_PAIR) {
     const dim3 grid((unsigned)((a.T + 127) / 128) * a.B * a.Hkv);
-    hipLaunchKernelGGL((fa_bwd_dkdv_pair_kernel<DK, 64, CAP>), grid, dim3(512), 0, stream, a);
+    hipLaunchKernelGGL((fa_bwd_dkdv_pair_kernel<DK, PAIR_BQB, CAP>), grid, dim3(512), 0, stream, a);
     stage_mark(stream);
     return hipGetLastError();
   }
