@@ -320,6 +320,36 @@ struct TrPipeLo {
   }
 };
 
+// A pinned sequence of N MFMAs acc(k) += A(k) B(k): A(k) from LDS through
+// fetch(k), issued PD MFMAs ahead of its use (ring of PD + 1 operands), B(k)
+// from registers; after MFMA k, hook(k) runs VALU work that does not wait for
+// the MFMAs in flight, so the wave's own VALU fills the matrix unit's busy
+// cycles.  start() issues the first PD fetches and may be called early (for
+// instance from another sequence's hook) to hide their latency.
+template <int N, int PD>
+struct MfmaSeq {
+  static_assert(PD >= 1, "reads run at least one MFMA ahead");
+  static constexpr int R = PD + 1;
+  bf16x8 op[R];
+  template <class Fetch>
+  __device__ __forceinline__ void start(Fetch&& fetch) {
+#pragma unroll
+    for (int k = 0; k < PD && k < N; ++k) op[k % R] = fetch(k);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  template <class Fetch, class BOp, class Acc, class Hook>
+  __device__ __forceinline__ void run(Fetch&& fetch, BOp&& bop, Acc&& acc, Hook&& hook) {
+#pragma unroll
+    for (int k = 0; k < N; ++k) {
+      if (k + PD < N) op[(k + PD) % R] = fetch(k + PD);
+      f32x16& c = acc(k);
+      c = mfma32(op[k % R], bop(k), c);
+      hook(k);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+};
+
 // acc[t] = sum_c A_t(c) B(c) over the D/16 chunks of d, where A_t(c) is
 // the row operand of rows 32t.. of `tile` (read from LDS) and B(c) = breg[c]
 // lives in registers: NS independent 32x32 accumulators.  The LDS operands

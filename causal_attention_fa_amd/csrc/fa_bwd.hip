@@ -787,17 +787,11 @@ __global__ __launch_bounds__(64 * NW, (DK >= 192 ? 1 : 8 / NW)) void fa_bwd_dkdv
 }
 
 // ------------------------------------------------------ fused dK/dV pass
-#ifndef PAIR_LAUNDER
-#define PAIR_LAUNDER 1
-#endif
 #ifndef PAIR_PD
 #define PAIR_PD(D) 3
 #endif
 #ifndef PAIR_BQB
 #define PAIR_BQB 64
-#endif
-#ifndef PAIR_OSLOTS
-#define PAIR_OSLOTS 3
 #endif
 // One launch for dK and dV, with paired waves: waves p and p + 4 own the
 // same 32 key rows of the workgroup's 128.  Wave p (the P side) keeps K in
@@ -820,20 +814,21 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_pair_kernel(BwdArgs a) {
   constexpr int BKVB = 128;                 // key rows per workgroup
   constexpr int TILE = Lay<D>::template bytes<BQB>();
   constexpr int NDB = D / 32;               // 32-wide blocks of dk / dv
-  constexpr int NS = BQB / 32;              // 32-query sub-tiles
-  constexpr int NC16 = BQB / 16;            // 16-query chunks (operand k steps)
+  constexpr int NC = D / 16;                // 16-wide chunks of d (k steps of S, dP)
+  constexpr int NS = BQB / 32;              // 32-query halves
+  constexpr int NC16 = BQB / 16;            // 16-query chunks (k steps of dV, dK)
   constexpr int STAT = BQB * 4;             // bytes of one lse or D tile
   constexpr int XB = 4 * NC16 * 1024;       // exchange: 4 pairs x NC16 x 64 lanes x 16 B
   constexpr int PD = PAIR_PD(D);
-  constexpr int OSLOTS = PAIR_OSLOTS;   // dO slots: 2 (loop unrolled by 6) or 3 (by 3)
+  static_assert(NS == 2, "the pipelined tile body handles two 32-query halves");
   __shared__ __attribute__((aligned(1024))) char qs0[TILE];
   __shared__ __attribute__((aligned(1024))) char qs1[TILE];
   __shared__ __attribute__((aligned(1024))) char qs2[TILE];
   __shared__ __attribute__((aligned(1024))) char os0[TILE];
   __shared__ __attribute__((aligned(1024))) char os1[TILE];
-  __shared__ __attribute__((aligned(1024))) char os2[OSLOTS == 3 ? TILE : 16];
+  __shared__ __attribute__((aligned(1024))) char os2[TILE];
   __shared__ __attribute__((aligned(1024))) char xsa[2 * XB];
-  __shared__ __attribute__((aligned(16))) char sbuf[4 * STAT];
+  __shared__ __attribute__((aligned(16))) char sbuf[3 * 2 * STAT];
   LDS_AS char* stat = (LDS_AS char*)sbuf;  // [slot][lse2 | D][BQB] fp32
 
   const int tid = threadIdx.x;
@@ -855,11 +850,11 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_pair_kernel(BwdArgs a) {
   const size_t bkv = (size_t)w.b * a.Hkv + w.hkv;
 
   // K (P side) or V (dS side) rows: the B operand of S = Q K^T or dP = dO V^T
-  bf16x8 kv[D / 16];
+  bf16x8 kv[NC];
   {
     const bf16x8* src = (const bf16x8*)((pside ? a.k : a.v) + (bkv * T + kr) * D + 8 * g);
 #pragma unroll
-    for (int c = 0; c < D / 16; ++c) kv[c] = src[2 * c];
+    for (int c = 0; c < NC; ++c) kv[c] = src[2 * c];
   }
   f32x16 acc[NDB];   // dV (P side) or dK (dS side)
 #pragma unroll
@@ -872,6 +867,8 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_pair_kernel(BwdArgs a) {
   const int q_hi = W > 0 ? min(T, k0 + BKVB - 1 + W) : T;
   const int nqt = (q_hi + BQB - 1) / BQB - qt_lo;
   const int niter = G * nqt;
+  // query q sees this lane's key iff 0 <= q - krow < span
+  const unsigned span = (unsigned)max(0, min(T, W > 0 ? krow + W : T) - krow);
 
   // iteration it visits query head (hkv*G + hi) and tile ti, it = hi*nqt + ti
   auto stage_stats = [&](int hi, int ti) -> float {
@@ -903,6 +900,7 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_pair_kernel(BwdArgs a) {
   TileDma<D, BQB, NW> qdm, odm;
   qdm.init(wave, lane);
   odm.init(wave, lane);
+  // tile it uses Q, dO and statistics slot it % 3
   auto qbuf = [&](auto b_c) -> LDS_AS char* {
     constexpr int b = decltype(b_c)::value;
     return b == 0 ? (LDS_AS char*)qs0 : b == 1 ? (LDS_AS char*)qs1 : (LDS_AS char*)qs2;
@@ -910,6 +908,10 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_pair_kernel(BwdArgs a) {
   auto obuf = [&](auto b_c) -> LDS_AS char* {
     constexpr int b = decltype(b_c)::value;
     return b == 0 ? (LDS_AS char*)os0 : b == 1 ? (LDS_AS char*)os1 : (LDS_AS char*)os2;
+  };
+  auto sbufp = [&](auto b_c) -> LDS_AS float* {
+    constexpr int b = decltype(b_c)::value;
+    return (LDS_AS float*)(stat + b * 2 * STAT);
   };
   // exchange slot b (written with ordinary LDS stores: a run-time choice)
   auto xbuf = [&](int b, int xo) -> LDS_AS char* { return (LDS_AS char*)xsa + b * XB + xo; };
@@ -925,7 +927,7 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_pair_kernel(BwdArgs a) {
   using I2 = std::integral_constant<int, 2>;
   {
     const float v = issue(qbuf(I0{}), obuf(I0{}), 0, 0);
-    if (tid < 2 * BQB) *(LDS_AS float*)(stat + tid * 4) = stat_val(v);
+    if (tid < 2 * BQB) sbufp(I0{})[tid] = stat_val(v);
     wait_vmem();
   }
   int h1 = 0, t1 = 0;
@@ -937,86 +939,132 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_pair_kernel(BwdArgs a) {
     return ka >= T || q0 + BQB - 1 < ka || (W > 0 && q0 - kb >= W);
   };
 
-  // P side, one query tile: S, P, the exchange factor, dV^T += dO^T P
+  // Element (t, i) of a 32x32 accumulator pair held by this lane: query
+  // 32t + 8(i/4) + 4g + i%4 of the tile; chunk c16 = 2t + i/8 of the
+  // 16-query k steps holds elements i%8 of that half.
+  constexpr int EPH_S = 16 / NC;            // P side: exp elements per S MFMA (half 0)
+  constexpr int EPH_V = 16 / (2 * NDB);     // P side: exp elements per dV MFMA (half 1)
+  constexpr int EPH_K = 8 / NDB;            // dS side: dS elements per dK MFMA
+
+  // P side, one query tile: S of the two halves in turn (exp of half 0 under
+  // the MFMAs of half 1), then dV^T += dO^T P over the 16-query chunks (exp of
+  // half 1 under the MFMAs of chunks 0-1); P and the exchange factor are
+  // packed per chunk as soon as its eight elements exist.
   auto p_tile = [&](const LDS_AS char* Qt, const LDS_AS char* dOt, LDS_AS char* X,
                     const LDS_AS float* lse2t, const int q0, const LaneOffs<D>& lo)
                     __attribute__((always_inline)) {
     if (empty_tile(q0)) return;
-    const bool full = q0 >= kb && q0 + BQB <= T && (W == 0 || q0 + BQB - 1 - ka < W);
+    const int vb = q0 + 4 * g - krow;   // q - krow = vb + 32t + 8(i/4) + i%4
     f32x16 s[NS];
-    mma_rows_lo<D, NS, PD>(s, Qt, lo, kv);
-    TrPipeLo<D, NDB, NC16, PD> otp;   // first dO^T operands, issued before the softmax
-    otp.start(dOt, lo);
-    f32x16 c[CAP ? NS : 1];
+    f32x16 cx[CAP ? NS : 1];
 #pragma unroll
     for (int t = 0; t < NS; ++t)
 #pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const f32x4 l4 = *(const LDS_AS f32x4*)(lse2t + 32 * t + 8 * i4 + 4 * g);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = 4 * i4 + e;
-          float th;
-          const float p = fast_exp2(p_arg<CAP>(s[t][i], a, l4[e], th));
-          s[t][i] = p;
-          if (CAP) c[t][i] = p * (1.f - th * th);
-        }
-      }
-    if (!full) {
-#pragma unroll
-      for (int t = 0; t < NS; ++t)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int q = q0 + 32 * t + acc_row(i, g);
-          const bool vis = (q < T) & (krow <= q) & ((W == 0) | (krow > q - W));
-          s[t][i] = vis ? s[t][i] : 0.f;
-          if (CAP) c[t][i] = vis ? c[t][i] : 0.f;
-        }
-    }
+      for (int i = 0; i < 16; ++i) s[t][i] = 0.f;
     bf16x8 pb[NC16];
+    f32x4 lv[NS][4];   // lse (log2) of the lane's rows
+    auto fS = [&](int k) { return lds_row_op<D>(Qt, lo, k / NC, k % NC); };
+    auto fV = [&](int k) { return lds_tr_op<D>(dOt, lo, k / NDB, k % NDB); };
+    MfmaSeq<NS * NC, PD> sq;
+    MfmaSeq<NC16 * NDB, PD> vq;
+    sq.start(fS);
 #pragma unroll
-    for (int c16 = 0; c16 < NC16; ++c16) {
+    for (int i4 = 0; i4 < 4; ++i4) lv[0][i4] = *(const LDS_AS f32x4*)(lse2t + 8 * i4 + 4 * g);
+    auto elem = [&](int t, int i) __attribute__((always_inline)) {
+      float th;
+      float p = fast_exp2(p_arg<CAP>(s[t][i], a, lv[t][i >> 2][i & 3], th));
+      const bool vis = (unsigned)(vb + 32 * t + 8 * (i >> 2) + (i & 3)) < span;
+      p = vis ? p : 0.f;
+      s[t][i] = p;
+      if (CAP) cx[t][i] = p * (1.f - th * th);
+    };
+    auto pack_chunk = [&](int c16) __attribute__((always_inline)) {
       float tp[8], tc[8];
 #pragma unroll
       for (int jj = 0; jj < 8; ++jj) {
         tp[jj] = s[c16 >> 1][8 * (c16 & 1) + jj];
-        if (CAP) tc[jj] = c[c16 >> 1][8 * (c16 & 1) + jj];
+        if (CAP) tc[jj] = cx[c16 >> 1][8 * (c16 & 1) + jj];
       }
       pb[c16] = pack_bf16(tp);
       *(LDS_AS bf16x8*)(X + c16 * 1024) = CAP ? pack_bf16(tc) : pb[c16];
-    }
-    otp.run(acc, dOt, lo, pb);
+    };
+    sq.run(fS, [&](int k) { return kv[k % NC]; }, [&](int k) -> f32x16& { return s[k / NC]; },
+           [&](int k) __attribute__((always_inline)) {
+             if (k == 0) {
+#pragma unroll
+               for (int i4 = 0; i4 < 4; ++i4)
+                 lv[1][i4] = *(const LDS_AS f32x4*)(lse2t + 32 + 8 * i4 + 4 * g);
+             }
+             if (k >= NC) {
+               const int e0 = EPH_S * (k - NC);
+#pragma unroll
+               for (int e = 0; e < EPH_S; ++e) elem(0, e0 + e);
+               if (e0 + EPH_S == 8) pack_chunk(0);
+               if (e0 + EPH_S == 16) pack_chunk(1);
+             }
+             if (k == NS * NC - PD) vq.start(fV);
+           });
+    vq.run(fV, [&](int k) { return pb[k / NDB]; }, [&](int k) -> f32x16& { return acc[k % NDB]; },
+           [&](int k) __attribute__((always_inline)) {
+             if (k < 2 * NDB) {
+               const int e0 = EPH_V * k;
+#pragma unroll
+               for (int e = 0; e < EPH_V; ++e) elem(1, e0 + e);
+               if (e0 + EPH_V == 8) pack_chunk(2);
+               if (e0 + EPH_V == 16) pack_chunk(3);
+             }
+           });
   };
-  // dS side, the previous tile: dS = factor * (dP - D), dK^T += Q^T dS
-  auto ds_prev = [&](f32x16 (&dpm)[NS], const LDS_AS char* Qt, const LDS_AS char* X,
-                     const int q0, const LaneOffs<D>& lo) __attribute__((always_inline)) {
-    if (empty_tile(q0)) return;
-    TrPipeLo<D, NDB, NC16, PD> qtp;
-    qtp.start(Qt, lo);
+
+  // dS side, the previous tile: dS = factor * (dP - D) per chunk, each
+  // chunk computed under the MFMAs of the one before, dK^T += Q^T dS
+  auto ds_prev = [&](f32x16 (&dp)[NS], const LDS_AS char* Qt, const LDS_AS char* X,
+                     const LDS_AS float* Dt, const LaneOffs<D>& lo, auto&& tail)
+                     __attribute__((always_inline)) {
+    bf16x8 xf[NC16];
+#pragma unroll
+    for (int c16 = 0; c16 < NC16; ++c16) xf[c16] = *(const LDS_AS bf16x8*)(X + c16 * 1024);
+    auto fK = [&](int k) { return lds_tr_op<D>(Qt, lo, k / NDB, k % NDB); };
+    MfmaSeq<NC16 * NDB, PD> kq;
+    kq.start(fK);
+    f32x4 dv[NC16][2];   // D of the rows of each chunk
+#pragma unroll
+    for (int c16 = 0; c16 < NC16; ++c16)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        dv[c16][h] = *(const LDS_AS f32x4*)(Dt + 32 * (c16 >> 1) + 8 * (2 * (c16 & 1) + h) + 4 * g);
+    float td[NC16][8];
     bf16x8 dsb[NC16];
+    auto dsel = [&](int c16, int jj) __attribute__((always_inline)) {
+      const int t = c16 >> 1, i = 8 * (c16 & 1) + jj;
+      td[c16][jj] = (float)xf[c16][jj] * (dp[t][i] - dv[c16][jj >> 2][jj & 3]);
+    };
 #pragma unroll
-    for (int c16 = 0; c16 < NC16; ++c16) {
-      const bf16x8 f = *(const LDS_AS bf16x8*)(X + c16 * 1024);
-      float td[8];
+    for (int jj = 0; jj < 8; ++jj) dsel(0, jj);
+    dsb[0] = pack_bf16(td[0]);
+    kq.run(fK, [&](int k) { return dsb[k / NDB]; }, [&](int k) -> f32x16& { return acc[k % NDB]; },
+           [&](int k) __attribute__((always_inline)) {
+             const int c = k / NDB + 1;
+             if (c < NC16) {
+               const int j0 = EPH_K * (k % NDB);
 #pragma unroll
-      for (int jj = 0; jj < 8; ++jj) td[jj] = (float)f[jj] * dpm[c16 >> 1][8 * (c16 & 1) + jj];
-      dsb[c16] = pack_bf16(td);
-    }
-    qtp.run(acc, Qt, lo, dsb);
+               for (int e = 0; e < EPH_K; ++e) dsel(c, j0 + e);
+               if (j0 + EPH_K == 8) dsb[c] = pack_bf16(td[c]);
+             }
+             if (k == NC16 * NDB - PD) tail();
+           });
   };
-  // dS side, the current tile: dP - D
-  auto dp_cur = [&](f32x16 (&dpm)[NS], const LDS_AS char* dOt, const LDS_AS float* Dt,
-                    const int q0, const LaneOffs<D>& lo) __attribute__((always_inline)) {
-    if (empty_tile(q0)) return;
-    mma_rows_lo<D, NS, PD>(dpm, dOt, lo, kv);
+  // dS side, the current tile: dP (D is subtracted one tile later); the two
+  // halves' accumulations alternate (independent MFMAs back to back)
+  auto dp_cur = [&](f32x16 (&dp)[NS], MfmaSeq<NS * NC, PD>& pq, auto&& fP, const bool started)
+                    __attribute__((always_inline)) {
 #pragma unroll
     for (int t = 0; t < NS; ++t)
 #pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const f32x4 d4 = *(const LDS_AS f32x4*)(Dt + 32 * t + 8 * i4 + 4 * g);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) dpm[t][4 * i4 + e] -= d4[e];
-      }
+      for (int i = 0; i < 16; ++i) dp[t][i] = 0.f;
+    if (!started) pq.start(fP);
+    pq.run(fP, [&](int k) { return kv[k / NS]; }, [&](int k) -> f32x16& { return dp[k % NS]; },
+           [&](int) {});
   };
 
   // Iteration it (0 .. niter; the last one only finishes the dS side's
@@ -1027,32 +1075,38 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_pair_kernel(BwdArgs a) {
   LaneOffs<D> lo0;
   lo0.init(lane);
   const int xo0 = pr * NC16 * 1024 + lane * 16;   // this lane's exchange slot
-  f32x16 dpm[NS];       // dS side: dP - D of the previous tile
-  auto step = [&](auto side_c, const int it, auto qc, auto qn, auto qp, auto oc, auto on)
+  f32x16 dp[NS];        // dS side: dP of the previous tile
+  auto step = [&](auto side_c, const int it, auto qc, auto qn, auto qp)
                   __attribute__((always_inline)) {
     constexpr bool PS = decltype(side_c)::value;
-    const int sc = it & 1;   // stats and exchange slot of tile it
+    const int xs = it & 1;   // exchange slot of tile it
     const bool more = it + 1 < niter;
     float sv = 0.f;
-    if (more) sv = issue(qbuf(qn), obuf(on), h1, t1);
-    const LDS_AS float* lse2t = (const LDS_AS float*)(stat + sc * 2 * STAT);
+    if (more) sv = issue(qbuf(qn), obuf(qn), h1, t1);
     // lane offsets refreshed per step: the buffer addresses derived from
     // them are formed here (one add per buffer) instead of hoisted out of
     // the loop, where those of all the buffers would stay live
     LaneOffs<D> lo = lo0;
     int xo = xo0;
-#if PAIR_LAUNDER
     lo.refresh();
     asm volatile("" : "+v"(xo));
-#endif
     if constexpr (PS) {
-      if (it < niter) p_tile(qbuf(qc), obuf(oc), xbuf(sc, xo), lse2t, tile_q0(tc), lo);
+      if (it < niter) p_tile(qbuf(qc), obuf(qc), xbuf(xs, xo), sbufp(qc), tile_q0(tc), lo);
     } else {
-      if (it > 0) ds_prev(dpm, qbuf(qp), xbuf(sc ^ 1, xo), tile_q0(tp), lo);
-      if (it < niter) dp_cur(dpm, obuf(oc), lse2t + BQB, tile_q0(tc), lo);
+      const bool cur = it < niter && !empty_tile(tile_q0(tc));
+      auto fP = [&](int k) { return lds_row_op<D>(obuf(qc), lo, k % NS, k / NS); };
+      MfmaSeq<NS * NC, PD> pq;   // dP of the current tile, its first reads issued early
+      bool started = false;
+      if (it > 0 && !empty_tile(tile_q0(tp))) {
+        ds_prev(dp, qbuf(qp), xbuf(xs ^ 1, xo), sbufp(qp) + BQB, lo, [&]() {
+          if (cur) pq.start(fP);
+        });
+        started = true;
+      }
+      if (cur) dp_cur(dp, pq, fP, started);
     }
     if (more) {
-      if (tid < 2 * BQB) *(LDS_AS float*)(stat + (sc ^ 1) * 2 * STAT + tid * 4) = stat_val(sv);
+      if (tid < 2 * BQB) sbufp(qn)[tid] = stat_val(sv);
       wait_vmem();
     }
     __syncthreads();
@@ -1061,28 +1115,12 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_pair_kernel(BwdArgs a) {
     advance(h1, t1);
   };
   auto run = [&](auto side_c) __attribute__((always_inline)) {
-    if constexpr (OSLOTS == 3) {
-      for (int it = 0; it <= niter; it += 3) {
-        step(side_c, it, I0{}, I1{}, I2{}, I0{}, I1{});
-        if (it + 1 > niter) break;
-        step(side_c, it + 1, I1{}, I2{}, I0{}, I1{}, I2{});
-        if (it + 2 > niter) break;
-        step(side_c, it + 2, I2{}, I0{}, I1{}, I2{}, I0{});
-      }
-    } else {
-      for (int it = 0; it <= niter; it += 6) {
-        step(side_c, it, I0{}, I1{}, I2{}, I0{}, I1{});
-        if (it + 1 > niter) break;
-        step(side_c, it + 1, I1{}, I2{}, I0{}, I1{}, I0{});
-        if (it + 2 > niter) break;
-        step(side_c, it + 2, I2{}, I0{}, I1{}, I0{}, I1{});
-        if (it + 3 > niter) break;
-        step(side_c, it + 3, I0{}, I1{}, I2{}, I1{}, I0{});
-        if (it + 4 > niter) break;
-        step(side_c, it + 4, I1{}, I2{}, I0{}, I0{}, I1{});
-        if (it + 5 > niter) break;
-        step(side_c, it + 5, I2{}, I0{}, I1{}, I1{}, I0{});
-      }
+    for (int it = 0; it <= niter; it += 3) {
+      step(side_c, it, I0{}, I1{}, I2{});
+      if (it + 1 > niter) break;
+      step(side_c, it + 1, I1{}, I2{}, I0{});
+      if (it + 2 > niter) break;
+      step(side_c, it + 2, I2{}, I0{}, I1{});
     }
   };
   if (pside)
