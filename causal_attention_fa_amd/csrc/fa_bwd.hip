@@ -799,34 +799,51 @@ __global__ __launch_bounds__(64 * NW, (DK >= 192 ? 1 : 8 / NW)) void fa_bwd_dkdv
 // dV^T += dO^T P, and leaves the factor that multiplies (dP - D) in dS --
 // P, or with the cap P (1 - tanh^2) -- to its partner in LDS as bf16.
 // Wave p + 4 (the dS side) keeps V in registers; per tile it computes
-// dP - D with dP = dO V^T, and one tile later, once the barrier has
-// published the P side's factor, dS and dK^T += Q^T dS.  S and the exp
+// dP = dO V^T, and one tile later, once the barrier has published the P
+// side's factor, dS = factor (dP - D) and dK^T += Q^T dS.  S and the exp
 // chain are computed once per tile (the two-launch scheme computes them in
 // both passes), and each wave holds one gradient accumulator, so two waves
-// per SIMD still fit.  Because the dS side lags one tile, Q tiles are
-// triple-buffered: the one being loaded, the current one, and the previous
-// one the dS side still reads.  Each buffer is its own LDS object and the
-// loop is unrolled by six (three Q slots x two dO / exchange slots), so
-// every buffer is a compile-time choice.
-template <int D, int BQB, bool CAP>
+// per SIMD still fit.  Because the dS side lags one tile, Q tiles and the
+// row statistics are triple-buffered (the tile being loaded, the current
+// one, and the previous one the dS side still reads); dO tiles are triple-
+// or, where LDS is short (d_k = 192), double-buffered.  Each buffer is its
+// own LDS object and the loop is unrolled by three (or six), so every
+// buffer is a compile-time choice.  Within a tile, each side's VALU work
+// runs under the MFMAs of its next product (MfmaSeq hooks).
+template <int DK, int DV, int BQB>
+struct PairShape {
+  static constexpr int TILE_Q = Lay<DK>::template bytes<BQB>();
+  static constexpr int TILE_O = Lay<DV>::template bytes<BQB>();
+  static constexpr int XB = 4 * (BQB / 16) * 1024;   // exchange: 4 pairs x chunks x 64 lanes x 16 B
+  static constexpr int STAT = BQB * 4;
+  static constexpr int LDS_MAX = 160 * 1024;
+  static constexpr int fixed = 3 * TILE_Q + 2 * XB + 3 * 2 * STAT;
+  static constexpr int OSL = fixed + 3 * TILE_O <= LDS_MAX ? 3 : 2;   // dO slots
+  static_assert(fixed + OSL * TILE_O <= LDS_MAX, "tiles exceed the LDS");
+};
+
+template <int DK, int DV, int BQB, bool CAP>
 __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_pair_kernel(BwdArgs a) {
+  using SH = PairShape<DK, DV, BQB>;
   constexpr int NW = 8;
   constexpr int BKVB = 128;                 // key rows per workgroup
-  constexpr int TILE = Lay<D>::template bytes<BQB>();
-  constexpr int NDB = D / 32;               // 32-wide blocks of dk / dv
-  constexpr int NC = D / 16;                // 16-wide chunks of d (k steps of S, dP)
+  constexpr int TILE_Q = SH::TILE_Q, TILE_O = SH::TILE_O, OSL = SH::OSL;
+  constexpr int NDBK = DK / 32, NDBV = DV / 32;   // 32-wide blocks of dk, dv
+  constexpr int NCK = DK / 16, NCV = DV / 16;     // 16-wide chunks (k steps of S, dP)
   constexpr int NS = BQB / 32;              // 32-query halves
   constexpr int NC16 = BQB / 16;            // 16-query chunks (k steps of dV, dK)
-  constexpr int STAT = BQB * 4;             // bytes of one lse or D tile
-  constexpr int XB = 4 * NC16 * 1024;       // exchange: 4 pairs x NC16 x 64 lanes x 16 B
-  constexpr int PD = PAIR_PD(D);
+  constexpr int STAT = SH::STAT;            // bytes of one lse or D tile
+  constexpr int XB = SH::XB;
+  constexpr int PD = PAIR_PD(DK);
+  constexpr int NKV = NCK > NCV ? NCK : NCV;
+  constexpr int NACC = NDBK > NDBV ? NDBK : NDBV;
   static_assert(NS == 2, "the pipelined tile body handles two 32-query halves");
-  __shared__ __attribute__((aligned(1024))) char qs0[TILE];
-  __shared__ __attribute__((aligned(1024))) char qs1[TILE];
-  __shared__ __attribute__((aligned(1024))) char qs2[TILE];
-  __shared__ __attribute__((aligned(1024))) char os0[TILE];
-  __shared__ __attribute__((aligned(1024))) char os1[TILE];
-  __shared__ __attribute__((aligned(1024))) char os2[TILE];
+  __shared__ __attribute__((aligned(1024))) char qs0[TILE_Q];
+  __shared__ __attribute__((aligned(1024))) char qs1[TILE_Q];
+  __shared__ __attribute__((aligned(1024))) char qs2[TILE_Q];
+  __shared__ __attribute__((aligned(1024))) char os0[TILE_O];
+  __shared__ __attribute__((aligned(1024))) char os1[TILE_O];
+  __shared__ __attribute__((aligned(1024))) char os2[OSL == 3 ? TILE_O : 16];
   __shared__ __attribute__((aligned(1024))) char xsa[2 * XB];
   __shared__ __attribute__((aligned(16))) char sbuf[3 * 2 * STAT];
   LDS_AS char* stat = (LDS_AS char*)sbuf;  // [slot][lse2 | D][BQB] fp32
@@ -850,17 +867,17 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_pair_kernel(BwdArgs a) {
   const size_t bkv = (size_t)w.b * a.Hkv + w.hkv;
 
   // K (P side) or V (dS side) rows: the B operand of S = Q K^T or dP = dO V^T
-  bf16x8 kv[NC];
-  {
-    const bf16x8* src = (const bf16x8*)((pside ? a.k : a.v) + (bkv * T + kr) * D + 8 * g);
+  bf16x8 kv[NKV];
+  if (pside) {
+    const bf16x8* src = (const bf16x8*)(a.k + (bkv * T + kr) * DK + 8 * g);
 #pragma unroll
-    for (int c = 0; c < NC; ++c) kv[c] = src[2 * c];
+    for (int c = 0; c < NCK; ++c) kv[c] = src[2 * c];
+  } else {
+    const bf16x8* src = (const bf16x8*)(a.v + (bkv * T + kr) * DV + 8 * g);
+#pragma unroll
+    for (int c = 0; c < NCV; ++c) kv[c] = src[2 * c];
   }
-  f32x16 acc[NDB];   // dV (P side) or dK (dS side)
-#pragma unroll
-  for (int db = 0; db < NDB; ++db)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
+  f32x16 acc[NACC];   // dV (P side, NDBV blocks) or dK (dS side, NDBK blocks)
 
   // Query tiles that can see keys [k0, k0 + BKVB).
   const int qt_lo = k0 / BQB;
@@ -887,8 +904,8 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_pair_kernel(BwdArgs a) {
   };
   // lse (log2 units) or D, as stored in the LDS statistics tile
   auto stat_val = [&](float v) { return tid < BQB ? v * kLog2e : v; };
-  auto tile_src = [&](int hi, const bf16* base) {
-    return base + ((size_t)w.b * a.H + w.hkv * G + hi) * T * D;
+  auto tile_src = [&](int hi, const bf16* base, int dd) {
+    return base + ((size_t)w.b * a.H + w.hkv * G + hi) * T * dd;
   };
   auto tile_q0 = [&](int ti) { return (qt_lo + ti) * BQB; };
   auto advance = [&](int& hi, int& ti) {
@@ -897,10 +914,11 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_pair_kernel(BwdArgs a) {
       ++hi;
     }
   };
-  TileDma<D, BQB, NW> qdm, odm;
+  TileDma<DK, BQB, NW> qdm;
+  TileDma<DV, BQB, NW> odm;
   qdm.init(wave, lane);
   odm.init(wave, lane);
-  // tile it uses Q, dO and statistics slot it % 3
+  // tile it uses Q and statistics slot it % 3 and dO slot it % OSL
   auto qbuf = [&](auto b_c) -> LDS_AS char* {
     constexpr int b = decltype(b_c)::value;
     return b == 0 ? (LDS_AS char*)qs0 : b == 1 ? (LDS_AS char*)qs1 : (LDS_AS char*)qs2;
@@ -918,8 +936,8 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_pair_kernel(BwdArgs a) {
   auto issue = [&](LDS_AS char* qdst, LDS_AS char* odst, int hi, int ti)
                    __attribute__((always_inline)) -> float {
     const float v = stage_stats(hi, ti);
-    qdm.load(tile_src(hi, a.q), T * D * 2, qdst, tile_q0(ti), wave);
-    odm.load(tile_src(hi, a.dO), T * D * 2, odst, tile_q0(ti), wave);
+    qdm.load(tile_src(hi, a.q, DK), T * DK * 2, qdst, tile_q0(ti), wave);
+    odm.load(tile_src(hi, a.dO, DV), T * DV * 2, odst, tile_q0(ti), wave);
     return v;
   };
   using I0 = std::integral_constant<int, 0>;
@@ -941,18 +959,21 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_pair_kernel(BwdArgs a) {
 
   // Element (t, i) of a 32x32 accumulator pair held by this lane: query
   // 32t + 8(i/4) + 4g + i%4 of the tile; chunk c16 = 2t + i/8 of the
-  // 16-query k steps holds elements i%8 of that half.
-  constexpr int EPH_S = 16 / NC;            // P side: exp elements per S MFMA (half 0)
-  constexpr int EPH_V = 16 / (2 * NDB);     // P side: exp elements per dV MFMA (half 1)
-  constexpr int EPH_K = 8 / NDB;            // dS side: dS elements per dK MFMA
+  // 16-query k steps holds elements i%8 of that half.  VALU work of M
+  // elements spread over the N MFMAs of a sequence: hook k takes elements
+  // [M k / N, M (k + 1) / N).
+  auto span_of = [](int M, int N, int k, int& e0, int& e1) {
+    e0 = M * k / N;
+    e1 = M * (k + 1) / N;
+  };
 
   // P side, one query tile: S of the two halves in turn (exp of half 0 under
   // the MFMAs of half 1), then dV^T += dO^T P over the 16-query chunks (exp of
   // half 1 under the MFMAs of chunks 0-1); P and the exchange factor are
   // packed per chunk as soon as its eight elements exist.
   auto p_tile = [&](const LDS_AS char* Qt, const LDS_AS char* dOt, LDS_AS char* X,
-                    const LDS_AS float* lse2t, const int q0, const LaneOffs<D>& lo)
-                    __attribute__((always_inline)) {
+                    const LDS_AS float* lse2t, const int q0, const LaneOffs<DK>& lq,
+                    const LaneOffs<DV>& lv_) __attribute__((always_inline)) {
     if (empty_tile(q0)) return;
     const int vb = q0 + 4 * g - krow;   // q - krow = vb + 32t + 8(i/4) + i%4
     f32x16 s[NS];
@@ -963,10 +984,11 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_pair_kernel(BwdArgs a) {
       for (int i = 0; i < 16; ++i) s[t][i] = 0.f;
     bf16x8 pb[NC16];
     f32x4 lv[NS][4];   // lse (log2) of the lane's rows
-    auto fS = [&](int k) { return lds_row_op<D>(Qt, lo, k / NC, k % NC); };
-    auto fV = [&](int k) { return lds_tr_op<D>(dOt, lo, k / NDB, k % NDB); };
-    MfmaSeq<NS * NC, PD> sq;
-    MfmaSeq<NC16 * NDB, PD> vq;
+    auto fS = [&](int k) { return lds_row_op<DK>(Qt, lq, k / NCK, k % NCK); };
+    auto fV = [&](int k) { return lds_tr_op<DV>(dOt, lv_, k / NDBV, k % NDBV); };
+    constexpr int NSQ = NS * NCK, NVQ = NC16 * NDBV;
+    MfmaSeq<NSQ, PD> sq;
+    MfmaSeq<NVQ, PD> vq;
     sq.start(fS);
 #pragma unroll
     for (int i4 = 0; i4 < 4; ++i4) lv[0][i4] = *(const LDS_AS f32x4*)(lse2t + 8 * i4 + 4 * g);
@@ -988,75 +1010,85 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_pair_kernel(BwdArgs a) {
       pb[c16] = pack_bf16(tp);
       *(LDS_AS bf16x8*)(X + c16 * 1024) = CAP ? pack_bf16(tc) : pb[c16];
     };
-    sq.run(fS, [&](int k) { return kv[k % NC]; }, [&](int k) -> f32x16& { return s[k / NC]; },
+    // half t's 16 elements [e0, e1), packing each chunk when it completes
+    auto elems = [&](int t, int e0, int e1) __attribute__((always_inline)) {
+#pragma unroll
+      for (int e = e0; e < e1; ++e) {
+        elem(t, e);
+        if (e == 7) pack_chunk(2 * t);
+        if (e == 15) pack_chunk(2 * t + 1);
+      }
+    };
+    sq.run(fS, [&](int k) { return kv[k % NCK]; }, [&](int k) -> f32x16& { return s[k / NCK]; },
            [&](int k) __attribute__((always_inline)) {
              if (k == 0) {
 #pragma unroll
                for (int i4 = 0; i4 < 4; ++i4)
                  lv[1][i4] = *(const LDS_AS f32x4*)(lse2t + 32 + 8 * i4 + 4 * g);
              }
-             if (k >= NC) {
-               const int e0 = EPH_S * (k - NC);
-#pragma unroll
-               for (int e = 0; e < EPH_S; ++e) elem(0, e0 + e);
-               if (e0 + EPH_S == 8) pack_chunk(0);
-               if (e0 + EPH_S == 16) pack_chunk(1);
+             if (k >= NCK) {
+               int e0, e1;
+               span_of(16, NCK, k - NCK, e0, e1);
+               elems(0, e0, e1);
              }
-             if (k == NS * NC - PD) vq.start(fV);
+             if (k == NSQ - PD) vq.start(fV);
            });
-    vq.run(fV, [&](int k) { return pb[k / NDB]; }, [&](int k) -> f32x16& { return acc[k % NDB]; },
+    vq.run(fV, [&](int k) { return pb[k / NDBV]; }, [&](int k) -> f32x16& { return acc[k % NDBV]; },
            [&](int k) __attribute__((always_inline)) {
-             if (k < 2 * NDB) {
-               const int e0 = EPH_V * k;
-#pragma unroll
-               for (int e = 0; e < EPH_V; ++e) elem(1, e0 + e);
-               if (e0 + EPH_V == 8) pack_chunk(2);
-               if (e0 + EPH_V == 16) pack_chunk(3);
+             if (k < 2 * NDBV) {
+               int e0, e1;
+               span_of(16, 2 * NDBV, k, e0, e1);
+               elems(1, e0, e1);
              }
            });
   };
 
   // dS side, the previous tile: dS = factor * (dP - D) per chunk, each
-  // chunk computed under the MFMAs of the one before, dK^T += Q^T dS
+  // chunk computed under the MFMAs of the one before, dK^T += Q^T dS;
+  // tail() runs a few MFMAs before the end (it starts the next product)
   auto ds_prev = [&](f32x16 (&dp)[NS], const LDS_AS char* Qt, const LDS_AS char* X,
-                     const LDS_AS float* Dt, const LaneOffs<D>& lo, auto&& tail)
+                     const LDS_AS float* Dt, const LaneOffs<DK>& lq, auto&& tail)
                      __attribute__((always_inline)) {
     bf16x8 xf[NC16];
-#pragma unroll
-    for (int c16 = 0; c16 < NC16; ++c16) xf[c16] = *(const LDS_AS bf16x8*)(X + c16 * 1024);
-    auto fK = [&](int k) { return lds_tr_op<D>(Qt, lo, k / NDB, k % NDB); };
-    MfmaSeq<NC16 * NDB, PD> kq;
-    kq.start(fK);
     f32x4 dv[NC16][2];   // D of the rows of each chunk
-#pragma unroll
-    for (int c16 = 0; c16 < NC16; ++c16)
+    // the exchange factor and D of chunk c16, read a chunk before their use
+    auto load_chunk = [&](int c16) __attribute__((always_inline)) {
+      xf[c16] = *(const LDS_AS bf16x8*)(X + c16 * 1024);
 #pragma unroll
       for (int h = 0; h < 2; ++h)
         dv[c16][h] = *(const LDS_AS f32x4*)(Dt + 32 * (c16 >> 1) + 8 * (2 * (c16 & 1) + h) + 4 * g);
+    };
+    load_chunk(0);
+    load_chunk(1);
+    auto fK = [&](int k) { return lds_tr_op<DK>(Qt, lq, k / NDBK, k % NDBK); };
+    constexpr int NKQ = NC16 * NDBK;
+    MfmaSeq<NKQ, PD> kq;
+    kq.start(fK);
     float td[NC16][8];
     bf16x8 dsb[NC16];
     auto dsel = [&](int c16, int jj) __attribute__((always_inline)) {
       const int t = c16 >> 1, i = 8 * (c16 & 1) + jj;
       td[c16][jj] = (float)xf[c16][jj] * (dp[t][i] - dv[c16][jj >> 2][jj & 3]);
+      if (jj == 7) dsb[c16] = pack_bf16(td[c16]);
     };
 #pragma unroll
     for (int jj = 0; jj < 8; ++jj) dsel(0, jj);
-    dsb[0] = pack_bf16(td[0]);
-    kq.run(fK, [&](int k) { return dsb[k / NDB]; }, [&](int k) -> f32x16& { return acc[k % NDB]; },
+    kq.run(fK, [&](int k) { return dsb[k / NDBK]; }, [&](int k) -> f32x16& { return acc[k % NDBK]; },
            [&](int k) __attribute__((always_inline)) {
-             const int c = k / NDB + 1;
+             const int c = k / NDBK + 1;   // the chunk after this MFMA's
+             if (k % NDBK == 0 && c + 1 < NC16) load_chunk(c + 1);
              if (c < NC16) {
-               const int j0 = EPH_K * (k % NDB);
+               int j0, j1;
+               span_of(8, NDBK, k % NDBK, j0, j1);
 #pragma unroll
-               for (int e = 0; e < EPH_K; ++e) dsel(c, j0 + e);
-               if (j0 + EPH_K == 8) dsb[c] = pack_bf16(td[c]);
+               for (int jj = j0; jj < j1; ++jj) dsel(c, jj);
              }
-             if (k == NC16 * NDB - PD) tail();
+             if (k == NKQ - PD) tail();
            });
   };
   // dS side, the current tile: dP (D is subtracted one tile later); the two
   // halves' accumulations alternate (independent MFMAs back to back)
-  auto dp_cur = [&](f32x16 (&dp)[NS], MfmaSeq<NS * NC, PD>& pq, auto&& fP, const bool started)
+  auto dp_cur = [&](f32x16 (&dp)[NS], MfmaSeq<NS * NCV, PD>& pq, auto&& fP, const bool started)
                     __attribute__((always_inline)) {
 #pragma unroll
     for (int t = 0; t < NS; ++t)
@@ -1072,33 +1104,39 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_pair_kernel(BwdArgs a) {
   // The two sides run separate copies of the loop (the same loads and
   // barriers), so that neither holds the other's registers.
   int tc = 0, tp = 0;   // tile index (within the head) of tiles it and it-1
-  LaneOffs<D> lo0;
-  lo0.init(lane);
+  LaneOffs<DK> lq0;
+  LaneOffs<DV> lv0;
+  lq0.init(lane);
+  lv0.init(lane);
   const int xo0 = pr * NC16 * 1024 + lane * 16;   // this lane's exchange slot
   f32x16 dp[NS];        // dS side: dP of the previous tile
-  auto step = [&](auto side_c, const int it, auto qc, auto qn, auto qp)
+  // qc, qn, qp: Q / statistics slots of tiles it, it+1, it-1; oc, on: dO
+  // slots of tiles it, it+1
+  auto step = [&](auto side_c, const int it, auto qc, auto qn, auto qp, auto oc, auto on)
                   __attribute__((always_inline)) {
     constexpr bool PS = decltype(side_c)::value;
     const int xs = it & 1;   // exchange slot of tile it
     const bool more = it + 1 < niter;
     float sv = 0.f;
-    if (more) sv = issue(qbuf(qn), obuf(qn), h1, t1);
+    if (more) sv = issue(qbuf(qn), obuf(on), h1, t1);
     // lane offsets refreshed per step: the buffer addresses derived from
     // them are formed here (one add per buffer) instead of hoisted out of
     // the loop, where those of all the buffers would stay live
-    LaneOffs<D> lo = lo0;
+    LaneOffs<DK> lq = lq0;
+    LaneOffs<DV> lv = lv0;
     int xo = xo0;
-    lo.refresh();
+    lq.refresh();
+    lv.refresh();
     asm volatile("" : "+v"(xo));
     if constexpr (PS) {
-      if (it < niter) p_tile(qbuf(qc), obuf(qc), xbuf(xs, xo), sbufp(qc), tile_q0(tc), lo);
+      if (it < niter) p_tile(qbuf(qc), obuf(oc), xbuf(xs, xo), sbufp(qc), tile_q0(tc), lq, lv);
     } else {
       const bool cur = it < niter && !empty_tile(tile_q0(tc));
-      auto fP = [&](int k) { return lds_row_op<D>(obuf(qc), lo, k % NS, k / NS); };
-      MfmaSeq<NS * NC, PD> pq;   // dP of the current tile, its first reads issued early
+      auto fP = [&](int k) { return lds_row_op<DV>(obuf(oc), lv, k % NS, k / NS); };
+      MfmaSeq<NS * NCV, PD> pq;   // dP of the current tile, its first reads issued early
       bool started = false;
       if (it > 0 && !empty_tile(tile_q0(tp))) {
-        ds_prev(dp, qbuf(qp), xbuf(xs ^ 1, xo), sbufp(qp) + BQB, lo, [&]() {
+        ds_prev(dp, qbuf(qp), xbuf(xs ^ 1, xo), sbufp(qp) + BQB, lq, [&]() {
           if (cur) pq.start(fP);
         });
         started = true;
@@ -1115,32 +1153,55 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_pair_kernel(BwdArgs a) {
     advance(h1, t1);
   };
   auto run = [&](auto side_c) __attribute__((always_inline)) {
-    for (int it = 0; it <= niter; it += 3) {
-      step(side_c, it, I0{}, I1{}, I2{});
-      if (it + 1 > niter) break;
-      step(side_c, it + 1, I1{}, I2{}, I0{});
-      if (it + 2 > niter) break;
-      step(side_c, it + 2, I2{}, I0{}, I1{});
+    constexpr int NDB_ = decltype(side_c)::value ? NDBV : NDBK;
+#pragma unroll
+    for (int db = 0; db < NDB_; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
+    if constexpr (OSL == 3) {
+      for (int it = 0; it <= niter; it += 3) {
+        step(side_c, it, I0{}, I1{}, I2{}, I0{}, I1{});
+        if (it + 1 > niter) break;
+        step(side_c, it + 1, I1{}, I2{}, I0{}, I1{}, I2{});
+        if (it + 2 > niter) break;
+        step(side_c, it + 2, I2{}, I0{}, I1{}, I2{}, I0{});
+      }
+    } else {
+      for (int it = 0; it <= niter; it += 6) {
+        step(side_c, it, I0{}, I1{}, I2{}, I0{}, I1{});
+        if (it + 1 > niter) break;
+        step(side_c, it + 1, I1{}, I2{}, I0{}, I1{}, I0{});
+        if (it + 2 > niter) break;
+        step(side_c, it + 2, I2{}, I0{}, I1{}, I0{}, I1{});
+        if (it + 3 > niter) break;
+        step(side_c, it + 3, I0{}, I1{}, I2{}, I1{}, I0{});
+        if (it + 4 > niter) break;
+        step(side_c, it + 4, I1{}, I2{}, I0{}, I0{}, I1{});
+        if (it + 5 > niter) break;
+        step(side_c, it + 5, I2{}, I0{}, I1{}, I1{}, I0{});
+      }
+    }
+    // this side's gradient rows: dV (P side) or scale * dK (dS side)
+    if (krow < T) {
+      constexpr bool PS = decltype(side_c)::value;
+      constexpr int DD = PS ? DV : DK;
+      bf16* dst = (PS ? a.dv : a.dk) + (bkv * T + krow) * DD;
+      const float f = PS ? 1.f : a.scale;
+#pragma unroll
+      for (int db = 0; db < NDB_; ++db)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          bf16x4 v4;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v4[e] = (bf16)(acc[db][4 * i4 + e] * f);
+          *(bf16x4*)(dst + 32 * db + 8 * i4 + 4 * g) = v4;
+        }
     }
   };
   if (pside)
     run(std::true_type{});
   else
     run(std::false_type{});
-
-  if (krow < T) {
-    bf16* dst = (pside ? a.dv : a.dk) + (bkv * T + krow) * D;
-    const float f = pside ? 1.f : a.scale;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        bf16x4 v4;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v4[e] = (bf16)(acc[db][4 * i4 + e] * f);
-        *(bf16x4*)(dst + 32 * db + 8 * i4 + 4 * g) = v4;
-      }
-  }
 }
 
 // Tile shapes per head size: dq pass (keys per tile, waves), dV pass and
@@ -1161,10 +1222,17 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_pair_kernel(BwdArgs a) {
 #ifndef BWD_DQ_PAIR
 #define BWD_DQ_PAIR 1
 #endif
-// dK and dV in one launch with paired waves (d = 64, 128)
+// dK and dV in one launch with paired waves (d = 64, 128 and d_k = 192 /
+// d_v = 128; at d = 256 one wave's K and gradient rows exceed its registers)
 #ifndef BWD_KV_PAIR
 #define BWD_KV_PAIR 1
 #endif
+#ifndef BWD_KV_PAIR_192
+#define BWD_KV_PAIR_192 1
+#endif
+#define BWD_KV_PAIR_FOR(DK, DV)                                                    \
+  (BWD_KV_PAIR && (((DK) == (DV) && ((DK) == 64 || (DK) == 128)) ||              \
+                   ((DK) == 192 && (DV) == 128 && BWD_KV_PAIR_192)))
 
 template <int DK, int DV, bool CAP, int DQ_BKV, int DQ_NW, int DV_BQB, int DV_NW, int DK_BQB,
           int DK_NW>
@@ -1181,9 +1249,10 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   stage_mark(stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if constexpr (DK == DV && (DK == 64 || DK == 128) && BWD_KV_PAIR) {
+  if constexpr (BWD_KV_PAIR_FOR(DK, DV)) {
     const dim3 grid((unsigned)((a.T + 127) / 128) * a.B * a.Hkv);
-    hipLaunchKernelGGL((fa_bwd_dkdv_pair_kernel<DK, PAIR_BQB, CAP>), grid, dim3(512), 0, stream, a);
+    hipLaunchKernelGGL((fa_bwd_dkdv_pair_kernel<DK, DV, PAIR_BQB, CAP>), grid, dim3(512), 0, stream,
+                       a);
     stage_mark(stream);
     return hipGetLastError();
   }
@@ -1210,8 +1279,9 @@ static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
 }
 
 const char* bwd_kernel_plan(int d, int d_v) {
-  if (d == d_v && (d == 64 || d == 128)) return BWD_KV_PAIR ? "dq,dkdv" : "dq,dv,dk";
-  if ((d == d_v && d == 256) || (d == 192 && d_v == 128)) return "dq,dv,dk";
+  if (d == d_v && (d == 64 || d == 128)) return BWD_KV_PAIR_FOR(64, 64) ? "dq,dkdv" : "dq,dv,dk";
+  if (d == 192 && d_v == 128) return BWD_KV_PAIR_FOR(192, 128) ? "dq,dkdv" : "dq,dv,dk";
+  if (d == d_v && d == 256) return "dq,dv,dk";
   return nullptr;
 }
 
