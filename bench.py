@@ -82,6 +82,56 @@ def cpu_baseline(w, budget_s, seed=0):
                       f"host affinity {len(os.sched_getaffinity(0))} cpus"}
 
 
+class SclkSampler:
+    """Shader clock observed while the timed steps run: a background thread
+    reads the driver's current-level line of pp_dpm_sclk (the one marked '*')
+    every few milliseconds.  Best effort: null when the file is not exposed."""
+
+    def __init__(self, period_s=0.004):
+        import glob
+        paths = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+        self.path = paths[0] if paths else None
+        self.period = period_s
+        self.samples = []
+        self._stop = False
+        self._thread = None
+
+    def _read(self):
+        try:
+            with open(self.path) as fh:
+                for line in fh:
+                    if line.rstrip().endswith("*"):
+                        return int(line.split(":")[1].strip().split("Mhz")[0].split("MHz")[0])
+        except (OSError, ValueError, IndexError):
+            return None
+        return None
+
+    def _run(self):
+        while not self._stop:
+            v = self._read()
+            if v is not None:
+                self.samples.append(v)
+            time.sleep(self.period)
+
+    def start(self):
+        if self.path:
+            import threading
+            self._thread = threading.Thread(target=self._run, daemon=True)
+            self._thread.start()
+
+    def stop(self):
+        self._stop = True
+        if self._thread:
+            self._thread.join()
+
+    def summary(self):
+        if not self.samples:
+            return None
+        v = sorted(self.samples)
+        return {"median": v[len(v) // 2], "min": v[0], "max": v[-1], "samples": len(v),
+                "source": self.path}
+
+
 def kernel_flops_per_pair(kind, d, dv=None):
     """Algorithmic MFMA flops per visible (q, k) pair of one kernel launch
     (d: query/key head size, dv: value head size)."""
@@ -284,16 +334,24 @@ def main():
     evs = [dict(fwd=[new_event(), new_event()], bwd=[new_event() for _ in range(n_bwd + 1)],
                 rq=[new_event(), new_event()], rk=[new_event(), new_event()])
            for _ in range(args.steps)]
+    # step boundaries: one event between consecutive steps
+    bounds = [new_event() for _ in range(args.steps + 1)]
     t_start, t_end = new_event(), new_event()
     torch.cuda.synchronize()
+    sclk = SclkSampler()
+    sclk.start()
     wall0 = time.perf_counter()
     t_start.record(stream)
+    bounds[0].record(stream)
     for i in range(args.steps):
         step(evs[i])
+        bounds[i + 1].record(stream)
     t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
+    sclk.stop()
     ms = t_start.elapsed_time(t_end) / args.steps
+    step_ms = sorted(bounds[i].elapsed_time(bounds[i + 1]) for i in range(args.steps))
 
     def avg(pairs):
         return sum(a.elapsed_time(b) for a, b in pairs) / len(pairs)
@@ -326,11 +384,19 @@ def main():
                 "algorithmic_flops_per_launch": dom_flops,
                 "avg_launch_ms": round(kern[dom], 4)}
 
+    sc = sclk.summary()
+    if sc:
+        # the same fraction against the peak at the observed median shader
+        # clock (the published peak assumes 2400 MHz)
+        roofline["frac_at_observed_sclk"] = round(achieved / (PEAK_BF16_TFLOPS * sc["median"] / 2400.0), 4)
     extra = {"fwd_tflops": round(fwd_tf, 1), "fwd_pct_peak": round(100 * fwd_tf / PEAK_BF16_TFLOPS, 2),
              "bwd_tflops": round(bwd_tf, 1),
              "attn_fwd_bwd_tflops": round((fwd_f + bwd_f) / (attn_ms * 1e-3) / 1e12, 1),
              "pct_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
              "kernel_ms": {n: round(t, 4) for n, t in kern.items()},
+             "step_ms_median": round(step_ms[len(step_ms) // 2], 4),
+             "step_ms_min": round(step_ms[0], 4),
+             "sclk_mhz": sc,
              "wall_s": round(wall, 3), "kernel_sources_sha": src_hash}
     if rope:
         extra["rope_mode"] = "fused" if fused else "separate"
