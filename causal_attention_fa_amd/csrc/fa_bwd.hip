@@ -8,22 +8,30 @@
 //   dS = dS' * (1 - tanh^2) (softcap),  dq = scale dS K,
 //   dk = scale dS^T Q,  dv = P^T dO  (dk, dv summed over the GQA group).
 //
-// Three launches, deterministic (the only atomics accumulate the attention
-// sinks' gradient).  Every pass streams its tiles straight from HBM into
-// double-buffered LDS (direct buffer loads, one tile ahead):
+// Two launches (three at d = 256), deterministic (the only atomics
+// accumulate the attention sinks' gradient).  Every pass streams its tiles
+// straight from HBM into multi-buffered LDS (direct buffer loads, one tile
+// ahead):
 //   1. fa_bwd_dq_kernel -- query-parallel, the forward's structure: each
 //      lane owns one query row; S^T = K Q^T and dP^T = V dO^T come out with
 //      the query along the lane, so lse, D and the softcap chain are
 //      per-lane scalars; dQ^T += K^T dS^T reads K^T through the LDS
 //      transpose read.  It also computes D_i for its rows (the backward
-//      prologue) and writes it to a [B, H, T] fp32 scratch for kernel 2.
-//   2./3. fa_bwd_dkdv_kernel, once for dV and once for dK -- key-parallel:
-//      a workgroup owns 128 key rows of one (b, kv head) and loops over the
-//      query heads of the GQA group and over the query tiles that can see
-//      its keys (the window bounds the loop).  Each lane owns one key row:
-//      K and V stay in registers as the B operands of S = Q K^T and
-//      dP = dO V^T, and dV^T += dO^T P, dK^T += Q^T dS take dO^T and Q^T
-//      from the natural tiles through the LDS transpose read.
+//      prologue) and writes it to a [B, H, T] fp32 scratch for the dK/dV
+//      pass.  At d = 256 fa_bwd_dq_pair_kernel splits each row over two
+//      waves.
+//   2. fa_bwd_dkdv_pair_kernel -- key-parallel: a workgroup owns 128 key
+//      rows of one (b, kv head) and loops over the query heads of the GQA
+//      group and over the query tiles that can see its keys (the window
+//      bounds the loop).  Each lane owns one key row, and two waves share
+//      each 32 rows: one keeps K in registers and computes S, P and dV, the
+//      other keeps V and computes dP, dS and dK one tile later from the
+//      factor the first leaves in LDS.  dV^T += dO^T P and dK^T += Q^T dS
+//      take dO^T and Q^T from the natural tiles through the LDS transpose
+//      read.
+//   At d = 256 a wave cannot hold K and a 32 x 256 accumulator beside the
+//   tiles, so fa_bwd_dkdv_kernel runs once for dV and once for dK (each
+//   recomputing S) instead of the paired pass.
 #include <type_traits>
 
 #include "device_common.h"
