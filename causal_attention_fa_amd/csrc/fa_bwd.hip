@@ -820,9 +820,14 @@ __global__ __launch_bounds__(64 * NW, (DK >= 192 ? 1 : 8 / NW)) void fa_bwd_dkdv
 // runs under the MFMAs of its next product (MfmaSeq hooks).
 template <int DK, int DV, int BQB>
 struct PairShape {
+  // 64-query tiles: 8 waves (4 pairs, 128 keys), two waves per SIMD;
+  // 32-query tiles (d = 256): 4 waves (2 pairs, 64 keys), one wave per SIMD
+  // (a wave's K rows and 32 x 256 accumulator need more than 256 registers)
+  static constexpr int NW = BQB == 32 ? 4 : 8;
+  static constexpr int NP = NW / 2;
   static constexpr int TILE_Q = Lay<DK>::template bytes<BQB>();
   static constexpr int TILE_O = Lay<DV>::template bytes<BQB>();
-  static constexpr int XB = 4 * (BQB / 16) * 1024;   // exchange: 4 pairs x chunks x 64 lanes x 16 B
+  static constexpr int XB = NP * (BQB / 16) * 1024;   // exchange: pairs x chunks x 64 lanes x 16 B
   static constexpr int STAT = BQB * 4;
   static constexpr int LDS_MAX = 160 * 1024;
   static constexpr int fixed = 3 * TILE_Q + 2 * XB + 3 * 2 * STAT;
@@ -831,10 +836,11 @@ struct PairShape {
 };
 
 template <int DK, int DV, int BQB, bool CAP>
-__global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_pair_kernel(BwdArgs a) {
+__global__ __launch_bounds__(BQB == 32 ? 256 : 512, 1) void fa_bwd_dkdv_pair_kernel(BwdArgs a) {
   using SH = PairShape<DK, DV, BQB>;
-  constexpr int NW = 8;
-  constexpr int BKVB = 128;                 // key rows per workgroup
+  constexpr int NW = SH::NW;
+  constexpr int NP = SH::NP;                // wave pairs
+  constexpr int BKVB = 32 * NP;             // key rows per workgroup
   constexpr int TILE_Q = SH::TILE_Q, TILE_O = SH::TILE_O, OSL = SH::OSL;
   constexpr int NDBK = DK / 32, NDBV = DV / 32;   // 32-wide blocks of dk, dv
   constexpr int NCK = DK / 16, NCV = DV / 16;     // 16-wide chunks (k steps of S, dP)
@@ -845,7 +851,7 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_pair_kernel(BwdArgs a) {
   constexpr int PD = PAIR_PD(DK);
   constexpr int NKV = NCK > NCV ? NCK : NCV;
   constexpr int NACC = NDBK > NDBV ? NDBK : NDBV;
-  static_assert(NS == 2, "the pipelined tile body handles two 32-query halves");
+  static_assert(NS == 1 || NS == 2, "32 or 64 queries per tile");
   __shared__ __attribute__((aligned(1024))) char qs0[TILE_Q];
   __shared__ __attribute__((aligned(1024))) char qs1[TILE_Q];
   __shared__ __attribute__((aligned(1024))) char qs2[TILE_Q];
@@ -859,8 +865,8 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_pair_kernel(BwdArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const bool pside = wave < 4;
-  const int pr = wave & 3;
+  const bool pside = wave < NP;
+  const int pr = wave & (NP - 1);
   const int g = lane >> 5;
   const int l32 = lane & 31;
   const int T = a.T;
@@ -1027,26 +1033,44 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_pair_kernel(BwdArgs a) {
         if (e == 15) pack_chunk(2 * t + 1);
       }
     };
-    sq.run(fS, [&](int k) { return kv[k % NCK]; }, [&](int k) -> f32x16& { return s[k / NCK]; },
+    // with one half, S accumulates in two partial sums (even and odd d
+    // chunks) so that consecutive MFMAs do not depend on each other
+    f32x16 s2[NS == 1 ? 2 : 1];
+    if constexpr (NS == 1) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s2[0][i] = s2[1][i] = 0.f;
+    }
+    sq.run(fS, [&](int k) { return kv[k % NCK]; },
+           [&](int k) -> f32x16& { return NS == 1 ? s2[k & 1] : s[k / NCK]; },
            [&](int k) __attribute__((always_inline)) {
-             if (k == 0) {
+             if (NS == 2 && k == 0) {
 #pragma unroll
                for (int i4 = 0; i4 < 4; ++i4)
-                 lv[1][i4] = *(const LDS_AS f32x4*)(lse2t + 32 + 8 * i4 + 4 * g);
+                 lv[NS - 1][i4] = *(const LDS_AS f32x4*)(lse2t + 32 + 8 * i4 + 4 * g);
              }
-             if (k >= NCK) {
+             if (NS == 2 && k >= NCK) {
                int e0, e1;
                span_of(16, NCK, k - NCK, e0, e1);
                elems(0, e0, e1);
              }
              if (k == NSQ - PD) vq.start(fV);
            });
+    // the last half: with one half, its first chunk before the dV product
+    // and the second under the MFMAs of the first
+    constexpr int TL = NS - 1;
+    constexpr int NH = NS == 2 ? 2 * NDBV : NDBV;   // dV MFMAs that carry exp work
+    constexpr int EH = NS == 2 ? 16 : 8;            // elements placed in them
+    if constexpr (NS == 1) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[0][i] = s2[0][i] + s2[1][i];
+      elems(0, 0, 8);
+    }
     vq.run(fV, [&](int k) { return pb[k / NDBV]; }, [&](int k) -> f32x16& { return acc[k % NDBV]; },
            [&](int k) __attribute__((always_inline)) {
-             if (k < 2 * NDBV) {
+             if (k < NH) {
                int e0, e1;
-               span_of(16, 2 * NDBV, k, e0, e1);
-               elems(1, e0, e1);
+               span_of(EH, NH, k, e0, e1);
+               elems(TL, 16 - EH + e0, 16 - EH + e1);
              }
            });
   };
@@ -1103,8 +1127,19 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_pair_kernel(BwdArgs a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) dp[t][i] = 0.f;
     if (!started) pq.start(fP);
-    pq.run(fP, [&](int k) { return kv[k / NS]; }, [&](int k) -> f32x16& { return dp[k % NS]; },
-           [&](int) {});
+    if constexpr (NS == 1) {
+      // two partial sums (even and odd d chunks), added at the end
+      f32x16 dp2;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) dp2[i] = 0.f;
+      pq.run(fP, [&](int k) { return kv[k]; },
+             [&](int k) -> f32x16& { return (k & 1) ? dp2 : dp[0]; }, [&](int) {});
+#pragma unroll
+      for (int i = 0; i < 16; ++i) dp[0][i] += dp2[i];
+    } else {
+      pq.run(fP, [&](int k) { return kv[k / NS]; }, [&](int k) -> f32x16& { return dp[k % NS]; },
+             [&](int) {});
+    }
   };
 
   // Iteration it (0 .. niter; the last one only finishes the dS side's
@@ -1238,9 +1273,13 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_pair_kernel(BwdArgs a) {
 #ifndef BWD_KV_PAIR_192
 #define BWD_KV_PAIR_192 1
 #endif
+#ifndef BWD_KV_PAIR_256
+#define BWD_KV_PAIR_256 1
+#endif
 #define BWD_KV_PAIR_FOR(DK, DV)                                                    \
   (BWD_KV_PAIR && (((DK) == (DV) && ((DK) == 64 || (DK) == 128)) ||              \
-                   ((DK) == 192 && (DV) == 128 && BWD_KV_PAIR_192)))
+                   ((DK) == 192 && (DV) == 128 && BWD_KV_PAIR_192) ||            \
+                   ((DK) == 256 && (DV) == 256 && BWD_KV_PAIR_256)))
 
 template <int DK, int DV, bool CAP, int DQ_BKV, int DQ_NW, int DV_BQB, int DV_NW, int DK_BQB,
           int DK_NW>
@@ -1258,9 +1297,12 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if constexpr (BWD_KV_PAIR_FOR(DK, DV)) {
-    const dim3 grid((unsigned)((a.T + 127) / 128) * a.B * a.Hkv);
-    hipLaunchKernelGGL((fa_bwd_dkdv_pair_kernel<DK, DV, PAIR_BQB, CAP>), grid, dim3(512), 0, stream,
-                       a);
+    constexpr int BQB = DK == 256 ? 32 : PAIR_BQB;
+    using SH = PairShape<DK, DV, BQB>;
+    constexpr int BKVB = 32 * SH::NP;
+    const dim3 grid((unsigned)((a.T + BKVB - 1) / BKVB) * a.B * a.Hkv);
+    hipLaunchKernelGGL((fa_bwd_dkdv_pair_kernel<DK, DV, BQB, CAP>), grid, dim3(64 * SH::NW), 0,
+                       stream, a);
     stage_mark(stream);
     return hipGetLastError();
   }
@@ -1289,7 +1331,7 @@ static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
 const char* bwd_kernel_plan(int d, int d_v) {
   if (d == d_v && (d == 64 || d == 128)) return BWD_KV_PAIR_FOR(64, 64) ? "dq,dkdv" : "dq,dv,dk";
   if (d == 192 && d_v == 128) return BWD_KV_PAIR_FOR(192, 128) ? "dq,dkdv" : "dq,dv,dk";
-  if (d == d_v && d == 256) return "dq,dv,dk";
+  if (d == d_v && d == 256) return BWD_KV_PAIR_FOR(256, 256) ? "dq,dkdv" : "dq,dv,dk";
   return nullptr;
 }
 
