@@ -8,10 +8,9 @@
 //   dS = dS' * (1 - tanh^2) (softcap),  dq = scale dS K,
 //   dk = scale dS^T Q,  dv = P^T dO  (dk, dv summed over the GQA group).
 //
-// Two launches (three at d = 256), deterministic (the only atomics
-// accumulate the attention sinks' gradient).  Every pass streams its tiles
-// straight from HBM into multi-buffered LDS (direct buffer loads, one tile
-// ahead):
+// Two launches, deterministic (the only atomics accumulate the attention
+// sinks' gradient).  Every pass streams its tiles straight from HBM into
+// multi-buffered LDS (direct buffer loads, one tile ahead):
 //   1. fa_bwd_dq_kernel -- query-parallel, the forward's structure: each
 //      lane owns one query row; S^T = K Q^T and dP^T = V dO^T come out with
 //      the query along the lane, so lse, D and the softcap chain are
@@ -21,17 +20,14 @@
 //      pass.  At d = 256 fa_bwd_dq_pair_kernel splits each row over two
 //      waves.
 //   2. fa_bwd_dkdv_pair_kernel -- key-parallel: a workgroup owns 128 key
-//      rows of one (b, kv head) and loops over the query heads of the GQA
-//      group and over the query tiles that can see its keys (the window
-//      bounds the loop).  Each lane owns one key row, and two waves share
-//      each 32 rows: one keeps K in registers and computes S, P and dV, the
-//      other keeps V and computes dP, dS and dK one tile later from the
-//      factor the first leaves in LDS.  dV^T += dO^T P and dK^T += Q^T dS
-//      take dO^T and Q^T from the natural tiles through the LDS transpose
-//      read.
-//   At d = 256 a wave cannot hold K and a 32 x 256 accumulator beside the
-//   tiles, so fa_bwd_dkdv_kernel runs once for dV and once for dK (each
-//   recomputing S) instead of the paired pass.
+//      rows (64 at d = 256) of one (b, kv head) and loops over the query
+//      heads of the GQA group and over the query tiles that can see its
+//      keys (the window bounds the loop).  Each lane owns one key row, and
+//      two waves share each 32 rows: one keeps K in registers and computes
+//      S, P and dV, the other keeps V and computes dP, dS and dK one tile
+//      later from the factor the first leaves in LDS.  dV^T += dO^T P and
+//      dK^T += Q^T dS take dO^T and Q^T from the natural tiles through the
+//      LDS transpose read.
 #include <type_traits>
 
 #include "device_common.h"
@@ -518,11 +514,13 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dq_pair_kernel(BwdArgs a) {
 }
 
 // ----------------------------------------------------------------- dK/dV pass
-// MODE 0 accumulates dK and dV together.  Both accumulators (2 x D/2
-// registers per lane) beside K, V and the tiles exceed the 256 registers
-// that two waves per SIMD allow, so the pass runs as two launches instead:
-// MODE 1 accumulates dV only (needs S, P), MODE 2 dK only (needs S, dP,
-// dS) -- one extra S = Q K^T product buys twice the occupancy.
+// The two-launch alternative to the fused pass below (built when
+// BWD_KV_PAIR or its per-size switches are 0, for comparison).  MODE 0
+// accumulates dK and dV together; both accumulators (2 x D/2 registers per
+// lane) beside K, V and the tiles exceed the 256 registers that two waves
+// per SIMD allow, so the pass runs as two launches instead: MODE 1
+// accumulates dV only (needs S, P), MODE 2 dK only (needs S, dP, dS) --
+// one extra S = Q K^T product buys twice the occupancy.
 template <int DK, int DV, int BQB, int NW, bool CAP, int MODE>
 __global__ __launch_bounds__(64 * NW, (DK >= 192 ? 1 : 8 / NW)) void fa_bwd_dkdv_kernel(BwdArgs a) {
   constexpr bool DO_DV = MODE != 2;
@@ -801,20 +799,21 @@ __global__ __launch_bounds__(64 * NW, (DK >= 192 ? 1 : 8 / NW)) void fa_bwd_dkdv
 #ifndef PAIR_BQB
 #define PAIR_BQB 64
 #endif
-// One launch for dK and dV, with paired waves: waves p and p + 4 own the
-// same 32 key rows of the workgroup's 128.  Wave p (the P side) keeps K in
+// One launch for dK and dV, with paired waves: waves p and p + NP own the
+// same 32 key rows (NP = 4 pairs, 128 keys per workgroup; at d = 256 NP = 2
+// and one wave per SIMD, see PairShape).  Wave p (the P side) keeps K in
 // registers; per query tile it computes S = Q K^T and P, accumulates
 // dV^T += dO^T P, and leaves the factor that multiplies (dP - D) in dS --
 // P, or with the cap P (1 - tanh^2) -- to its partner in LDS as bf16.
-// Wave p + 4 (the dS side) keeps V in registers; per tile it computes
+// Wave p + NP (the dS side) keeps V in registers; per tile it computes
 // dP = dO V^T, and one tile later, once the barrier has published the P
 // side's factor, dS = factor (dP - D) and dK^T += Q^T dS.  S and the exp
 // chain are computed once per tile (the two-launch scheme computes them in
 // both passes), and each wave holds one gradient accumulator, so two waves
-// per SIMD still fit.  Because the dS side lags one tile, Q tiles and the
-// row statistics are triple-buffered (the tile being loaded, the current
-// one, and the previous one the dS side still reads); dO tiles are triple-
-// or, where LDS is short (d_k = 192), double-buffered.  Each buffer is its
+// per SIMD still fit below d = 256.  Because the dS side lags one tile, Q
+// tiles and the row statistics are triple-buffered (the tile being loaded,
+// the current one, and the previous one the dS side still reads); dO tiles
+// are triple- or, where LDS is short (d_k = 192), double-buffered.  Each buffer is its
 // own LDS object and the loop is unrolled by three (or six), so every
 // buffer is a compile-time choice.  Within a tile, each side's VALU work
 // runs under the MFMAs of its next product (MfmaSeq hooks).
@@ -1265,8 +1264,8 @@ __global__ __launch_bounds__(BQB == 32 ? 256 : 512, 1) void fa_bwd_dkdv_pair_ker
 #ifndef BWD_DQ_PAIR
 #define BWD_DQ_PAIR 1
 #endif
-// dK and dV in one launch with paired waves (d = 64, 128 and d_k = 192 /
-// d_v = 128; at d = 256 one wave's K and gradient rows exceed its registers)
+// dK and dV in one launch with paired waves (every supported head size; 0
+// selects the two-launch fa_bwd_dkdv_kernel scheme)
 #ifndef BWD_KV_PAIR
 #define BWD_KV_PAIR 1
 #endif
