@@ -605,6 +605,14 @@ static hipError_t launch_fwd_d(const FwdArgs& a, hipStream_t stream) {
 #ifndef FWD256_BKV
 #define FWD256_BKV 32
 #endif
+// d = 256 forward: paired waves (two per SIMD, each holding half of d), or
+// the one-wave-per-row kernel at one wave per SIMD (FWD256_CFG shape)
+#ifndef FWD256_PAIR
+#define FWD256_PAIR 1
+#endif
+#ifndef FWD256_CFG
+#define FWD256_CFG 64, 4, 1
+#endif
 
 template <int D, int BKV>
 static hipError_t launch_fwd_pair(const FwdArgs& a, hipStream_t stream) {
@@ -634,7 +642,12 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, int d, int d_v, hipStream_t stream)
     switch (d) {
       case 64: return launch_fwd_d<64, 64, 64, 4, 1>(a, stream);
       case 128: return launch_fwd_d<128, 128, FWD128_CFG>(a, stream);
-      case 256: return launch_fwd_pair<256, FWD256_BKV>(a, stream);
+      case 256:
+#if FWD256_PAIR
+        return launch_fwd_pair<256, FWD256_BKV>(a, stream);
+#else
+        return launch_fwd_d<256, 256, FWD256_CFG>(a, stream);
+#endif
     }
   } else if (d == 192 && d_v == 128) {
     return launch_fwd_d<192, 128, FWD192_CFG>(a, stream);
