@@ -271,55 +271,6 @@ __device__ __forceinline__ bf16x8 lds_tr_op(const LDS_AS char* tile, const LaneO
   return __builtin_bit_cast(bf16x8, v);
 }
 
-// mma_rows_pd with the precomputed lane offsets (PD >= 1).
-template <int D, int NS, int PD>
-__device__ __forceinline__ void mma_rows_lo(f32x16 (&acc)[NS], const LDS_AS char* tile,
-                                            const LaneOffs<D>& o, const bf16x8 (&breg)[D / 16]) {
-  static_assert(PD >= 1, "reads run at least one chunk ahead");
-  constexpr int NC = D / 16, R = PD + 1;
-  bf16x8 op[R][NS];
-#pragma unroll
-  for (int t = 0; t < NS; ++t)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) acc[t][i] = 0.f;
-#pragma unroll
-  for (int c = 0; c < PD && c < NC; ++c)
-#pragma unroll
-    for (int t = 0; t < NS; ++t) op[c % R][t] = lds_row_op<D>(tile, o, t, c);
-#pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    if (c + PD < NC) {
-#pragma unroll
-      for (int t = 0; t < NS; ++t) op[(c + PD) % R][t] = lds_row_op<D>(tile, o, t, c + PD);
-    }
-#pragma unroll
-    for (int t = 0; t < NS; ++t) acc[t] = mfma32(op[c % R][t], breg[c], acc[t]);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-}
-
-// TrPipe with the precomputed lane offsets (PD >= 1, col0 = 0).
-template <int D, int NDB, int NC16, int PD>
-struct TrPipeLo {
-  static_assert(PD >= 1, "reads run at least one MFMA ahead");
-  static constexpr int N = NC16 * NDB, R = PD + 1;
-  bf16x8 op[R];
-  __device__ __forceinline__ void start(const LDS_AS char* tile, const LaneOffs<D>& o) {
-#pragma unroll
-    for (int k = 0; k < PD && k < N; ++k) op[k % R] = lds_tr_op<D>(tile, o, k / NDB, k % NDB);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  __device__ __forceinline__ void run(f32x16 (&acc)[NDB], const LDS_AS char* tile,
-                                      const LaneOffs<D>& o, const bf16x8 (&breg)[NC16]) {
-#pragma unroll
-    for (int k = 0; k < N; ++k) {
-      if (k + PD < N) op[(k + PD) % R] = lds_tr_op<D>(tile, o, (k + PD) / NDB, (k + PD) % NDB);
-      acc[k % NDB] = mfma32(op[k % R], breg[k / NDB], acc[k % NDB]);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  }
-};
-
 // A pinned sequence of N MFMAs acc(k) += A(k) B(k): A(k) from LDS through
 // fetch(k), issued PD MFMAs ahead of its use (ring of PD + 1 operands), B(k)
 // from registers; after MFMA k, hook(k) runs VALU work that does not wait for
