@@ -290,11 +290,23 @@ __global__ __launch_bounds__(64) void fa_decode_combine_kernel(DecodeArgs a) {
 #define DEC_NW256 4
 #endif
 
+// At d = 128 with at least this many (b, KV head, chunk) units, one wave per
+// workgroup: enough workgroups to keep the loads in flight, and no score
+// recomputation per wave (qwen25-decode 5.56 -> 5.76 TB/s); with fewer
+// units the two-wave split keeps more waves per CU (mistral-decode, 1024
+// units, is 3 % faster with two).
+#ifndef DEC_NW128_ONE_UNITS
+#define DEC_NW128_ONE_UNITS 2048
+#endif
+
 template <int D, bool CAP>
 static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
   constexpr int NW = D == 64 ? DEC_NW64 : D == 128 ? DEC_NW128 : DEC_NW256;
   const unsigned units = (unsigned)a.B * a.Hkv * a.nsplit;
-  fa_decode_split_kernel<D, NW, CAP><<<units, 64 * NW, 0, stream>>>(a);
+  if (D == 128 && NW != 1 && units >= DEC_NW128_ONE_UNITS)
+    fa_decode_split_kernel<D, 1, CAP><<<units, 64, 0, stream>>>(a);
+  else
+    fa_decode_split_kernel<D, NW, CAP><<<units, 64 * NW, 0, stream>>>(a);
   stage_mark(stream);
   fa_decode_combine_kernel<D><<<(unsigned)a.B * a.H, 64, 0, stream>>>(a);
   stage_mark(stream);

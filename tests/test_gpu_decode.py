@@ -4,8 +4,10 @@ split along the cache) against the float64 decode oracle.
 Small cases compare every output; the cache positions at or past each
 sequence's length are filled with NaN, so any read of them fails.  Lengths
 cover 0, 1, a tile edge +-1 and S; windows 1, inside a tile and past S;
-GQA ratios 1..32; d 64, 128, 256; cap on/off; sinks; several chunks.  The
-full-size qwen25-decode workload is checked on sampled sequences."""
+GQA ratios 1..32; d 64, 128, 256; cap on/off; sinks; several chunks; both
+split-kernel shapes at d = 128 (two waves per workgroup, and one wave when
+there are many (b, KV head, chunk) units).  The full-size qwen25-decode
+workload is checked on sampled sequences."""
 import math
 
 import numpy as np
@@ -35,6 +37,9 @@ CASES = [
     (1, 32, 1, 2000, 256, 0, 50.0, False, [1999]),
     # chunks wholly past a short sequence's length (empty chunks) beside a sink
     (2, 8, 2, 3000, 128, 0, 0.0, True, [3000, 100]),
+    # enough (b, KV head, chunk) units (12 x 64 x 3) for the one-wave split at d = 128
+    (12, 64, 64, 3000, 128, 0, 0.0, False,
+     [3000, 1, 1500, 2999, 1025, 1023, 0, 2048, 3000, 17, 2500, 1999]),
 ]
 
 
