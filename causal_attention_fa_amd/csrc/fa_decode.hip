@@ -287,7 +287,7 @@ __global__ __launch_bounds__(64) void fa_decode_combine_kernel(DecodeArgs a) {
 #define DEC_NW128 2
 #endif
 #ifndef DEC_NW256
-#define DEC_NW256 4
+#define DEC_NW256 2
 #endif
 
 // At d = 128 with at least this many (b, KV head, chunk) units, one wave per
