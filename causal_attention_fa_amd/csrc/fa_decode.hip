@@ -33,8 +33,8 @@ namespace fa {
 constexpr int kDecBKV = 32;  // keys per tile
 
 // NW waves per workgroup share the K/V tiles; each computes the (cheap,
-// identical) scores and owns D/NW of the output columns, so the d = 256
-// case keeps two waves per SIMD without spilling.
+// identical) scores and owns D/NW of the output columns (fewer accumulator
+// registers per wave; at d = 256 one wave would spill).
 template <int D, int NW, bool CAP>
 __global__ __launch_bounds__(64 * NW, 2) void fa_decode_split_kernel(DecodeArgs a) {
   constexpr int NT = 64 * NW;
@@ -303,10 +303,12 @@ template <int D, bool CAP>
 static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
   constexpr int NW = D == 64 ? DEC_NW64 : D == 128 ? DEC_NW128 : DEC_NW256;
   const unsigned units = (unsigned)a.B * a.Hkv * a.nsplit;
-  if (D == 128 && NW != 1 && units >= DEC_NW128_ONE_UNITS)
-    fa_decode_split_kernel<D, 1, CAP><<<units, 64, 0, stream>>>(a);
-  else
-    fa_decode_split_kernel<D, NW, CAP><<<units, 64 * NW, 0, stream>>>(a);
+  bool one = false;
+  if constexpr (D == 128 && NW != 1) {
+    one = units >= DEC_NW128_ONE_UNITS;
+    if (one) fa_decode_split_kernel<D, 1, CAP><<<units, 64, 0, stream>>>(a);
+  }
+  if (!one) fa_decode_split_kernel<D, NW, CAP><<<units, 64 * NW, 0, stream>>>(a);
   stage_mark(stream);
   fa_decode_combine_kernel<D><<<(unsigned)a.B * a.H, 64, 0, stream>>>(a);
   stage_mark(stream);
