@@ -1304,20 +1304,20 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
                        stream, a);
     stage_mark(stream);
     return hipGetLastError();
+  } else {
+    // the two-launch alternative (only built when selected)
+    const dim3 vgrid((unsigned)((a.T + 32 * DV_NW - 1) / (32 * DV_NW)) * a.B * a.Hkv);
+    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<DK, DV, DV_BQB, DV_NW, CAP, 1>), vgrid, dim3(64 * DV_NW),
+                       0, stream, a);
+    stage_mark(stream);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const dim3 kgrid((unsigned)((a.T + 32 * DK_NW - 1) / (32 * DK_NW)) * a.B * a.Hkv);
+    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<DK, DV, DK_BQB, DK_NW, CAP, 2>), kgrid, dim3(64 * DK_NW),
+                       0, stream, a);
+    stage_mark(stream);
+    return hipGetLastError();
   }
-  const dim3 vgrid((unsigned)((a.T + 32 * DV_NW - 1) / (32 * DV_NW)) * a.B * a.Hkv);
-  hipLaunchKernelGGL((fa_bwd_dkdv_kernel<DK, DV, DV_BQB, DV_NW, CAP, 1>), vgrid,
-                     dim3(64 * DV_NW), 0,
-                     stream, a);
-  stage_mark(stream);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const dim3 kgrid((unsigned)((a.T + 32 * DK_NW - 1) / (32 * DK_NW)) * a.B * a.Hkv);
-  hipLaunchKernelGGL((fa_bwd_dkdv_kernel<DK, DV, DK_BQB, DK_NW, CAP, 2>), kgrid,
-                     dim3(64 * DK_NW), 0,
-                     stream, a);
-  stage_mark(stream);
-  return hipGetLastError();
 }
 
 template <int DK, int DV, int DQ_BKV, int DQ_NW, int DV_BQB, int DV_NW, int DK_BQB, int DK_NW>
