@@ -915,8 +915,9 @@ __global__ __launch_bounds__(BQB == 32 ? 256 : 512, 1) void fa_bwd_dkdv_pair_ker
     }
     return v;
   };
-  // lse (log2 units) or D, as stored in the LDS statistics tile
-  auto stat_val = [&](float v) { return tid < BQB ? v * kLog2e : v; };
+  // lse (log2 units) or -D, as stored in the LDS statistics tile (the dS
+  // side starts its dP accumulators from -D, so they finish as dP - D)
+  auto stat_val = [&](float v) { return tid < BQB ? v * kLog2e : -v; };
   auto tile_src = [&](int hi, const bf16* base, int dd) {
     return base + ((size_t)w.b * a.H + w.hkv * G + hi) * T * dd;
   };
@@ -1080,14 +1081,11 @@ __global__ __launch_bounds__(BQB == 32 ? 256 : 512, 1) void fa_bwd_dkdv_pair_ker
   auto ds_prev = [&](f32x16 (&dp)[NS], const LDS_AS char* Qt, const LDS_AS char* X,
                      const LDS_AS float* Dt, const LaneOffs<DK>& lq, auto&& tail)
                      __attribute__((always_inline)) {
+    (void)Dt;
     bf16x8 xf[NC16];
-    f32x4 dv[NC16][2];   // D of the rows of each chunk
-    // the exchange factor and D of chunk c16, read a chunk before their use
+    // the exchange factor of chunk c16, read a chunk before its use
     auto load_chunk = [&](int c16) __attribute__((always_inline)) {
       xf[c16] = *(const LDS_AS bf16x8*)(X + c16 * 1024);
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-        dv[c16][h] = *(const LDS_AS f32x4*)(Dt + 32 * (c16 >> 1) + 8 * (2 * (c16 & 1) + h) + 4 * g);
     };
     load_chunk(0);
     load_chunk(1);
@@ -1099,7 +1097,7 @@ __global__ __launch_bounds__(BQB == 32 ? 256 : 512, 1) void fa_bwd_dkdv_pair_ker
     bf16x8 dsb[NC16];
     auto dsel = [&](int c16, int jj) __attribute__((always_inline)) {
       const int t = c16 >> 1, i = 8 * (c16 & 1) + jj;
-      td[c16][jj] = (float)xf[c16][jj] * (dp[t][i] - dv[c16][jj >> 2][jj & 3]);
+      td[c16][jj] = (float)xf[c16][jj] * dp[t][i];   // dp holds dP - D
       if (jj == 7) dsb[c16] = pack_bf16(td[c16]);
     };
 #pragma unroll
@@ -1117,14 +1115,19 @@ __global__ __launch_bounds__(BQB == 32 ? 256 : 512, 1) void fa_bwd_dkdv_pair_ker
              if (k == NKQ - PD) tail();
            });
   };
-  // dS side, the current tile: dP (D is subtracted one tile later); the two
-  // halves' accumulations alternate (independent MFMAs back to back)
-  auto dp_cur = [&](f32x16 (&dp)[NS], MfmaSeq<NS * NCV, PD>& pq, auto&& fP, const bool started)
-                    __attribute__((always_inline)) {
+  // dS side, the current tile: dP - D, the accumulators starting from -D
+  // (the statistics tile holds -D); the two halves' accumulations alternate
+  // (independent MFMAs back to back)
+  auto dp_cur = [&](f32x16 (&dp)[NS], MfmaSeq<NS * NCV, PD>& pq, auto&& fP, const bool started,
+                    const LDS_AS float* Dn) __attribute__((always_inline)) {
 #pragma unroll
     for (int t = 0; t < NS; ++t)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) dp[t][i] = 0.f;
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const f32x4 d4 = *(const LDS_AS f32x4*)(Dn + 32 * t + 8 * i4 + 4 * g);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dp[t][4 * i4 + e] = d4[e];
+      }
     if (!started) pq.start(fP);
     if constexpr (NS == 1) {
       // two partial sums (even and odd d chunks), added at the end
@@ -1183,7 +1186,7 @@ __global__ __launch_bounds__(BQB == 32 ? 256 : 512, 1) void fa_bwd_dkdv_pair_ker
         });
         started = true;
       }
-      if (cur) dp_cur(dp, pq, fP, started);
+      if (cur) dp_cur(dp, pq, fP, started, sbufp(qc) + BQB);
     }
     if (more) {
       if (tid < 2 * BQB) sbufp(qn)[tid] = stat_val(sv);
