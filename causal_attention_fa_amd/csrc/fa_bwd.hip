@@ -799,6 +799,10 @@ __global__ __launch_bounds__(64 * NW, (DK >= 192 ? 1 : 8 / NW)) void fa_bwd_dkdv
 #ifndef PAIR_BQB
 #define PAIR_BQB 64
 #endif
+// mask every tile (1) or only the tiles that cross the band's edges (0)
+#ifndef PAIR_MASK_FULL
+#define PAIR_MASK_FULL 0
+#endif
 // One launch for dK and dV, with paired waves: waves p and p + NP own the
 // same 32 key rows (NP = 4 pairs, 128 keys per workgroup; at d = 256 NP = 2
 // and one wave per SIMD, see PairShape).  Wave p (the P side) keeps K in
@@ -990,6 +994,8 @@ __global__ __launch_bounds__(BQB == 32 ? 256 : 512, 1) void fa_bwd_dkdv_pair_ker
                     const LaneOffs<DV>& lv_) __attribute__((always_inline)) {
     if (empty_tile(q0)) return;
     const int vb = q0 + 4 * g - krow;   // q - krow = vb + 32t + 8(i/4) + i%4
+    // every pair of the tile visible to every key of the wave: no mask
+    const bool full = q0 >= kb && q0 + BQB <= T && (W == 0 || q0 + BQB - 1 - ka < W);
     f32x16 s[NS];
     f32x16 cx[CAP ? NS : 1];
 #pragma unroll
@@ -1009,8 +1015,15 @@ __global__ __launch_bounds__(BQB == 32 ? 256 : 512, 1) void fa_bwd_dkdv_pair_ker
     auto elem = [&](int t, int i) __attribute__((always_inline)) {
       float th;
       float p = fast_exp2(p_arg<CAP>(s[t][i], a, lv[t][i >> 2][i & 3], th));
+#if PAIR_MASK_FULL
       const bool vis = (unsigned)(vb + 32 * t + 8 * (i >> 2) + (i & 3)) < span;
       p = vis ? p : 0.f;
+#else
+      if (!full) {
+        const bool vis = (unsigned)(vb + 32 * t + 8 * (i >> 2) + (i & 3)) < span;
+        p = vis ? p : 0.f;
+      }
+#endif
       s[t][i] = p;
       if (CAP) cx[t][i] = p * (1.f - th * th);
     };
