@@ -910,7 +910,7 @@ __global__ __launch_bounds__(BQB == 32 ? 256 : 512, 1) void fa_bwd_dkdv_pair_ker
     const int q0 = (qt_lo + ti) * BQB;
     const size_t bhh = (size_t)w.b * a.H + hh;
     float v = 0.f;
-    if (tid < 2 * BQB) {
+    if (wave < 2 * BQB / 64) {   // the waves holding threads 0 .. 2 BQB - 1 (wave-uniform)
       // one load, raw (the lse is scaled when it is stored to LDS): a use
       // here would make these waves wait for the load at once
       int qq = q0 + (tid % BQB);
@@ -963,7 +963,7 @@ __global__ __launch_bounds__(BQB == 32 ? 256 : 512, 1) void fa_bwd_dkdv_pair_ker
   using I2 = std::integral_constant<int, 2>;
   {
     const float v = issue(qbuf(I0{}), obuf(I0{}), 0, 0);
-    if (tid < 2 * BQB) sbufp(I0{})[tid] = stat_val(v);
+    if (wave < 2 * BQB / 64) sbufp(I0{})[tid] = stat_val(v);
     wait_vmem();
   }
   int h1 = 0, t1 = 0;
@@ -1166,7 +1166,7 @@ __global__ __launch_bounds__(BQB == 32 ? 256 : 512, 1) void fa_bwd_dkdv_pair_ker
   LaneOffs<DV> lv0;
   lq0.init(lane);
   lv0.init(lane);
-  const int xo0 = pr * NC16 * 1024 + lane * 16;   // this lane's exchange slot
+  int xo0 = pr * NC16 * 1024 + lane * 16;   // this lane's exchange slot
   f32x16 dp[NS];        // dS side: dP of the previous tile
   // qc, qn, qp: Q / statistics slots of tiles it, it+1, it-1; oc, on: dO
   // slots of tiles it, it+1
@@ -1177,15 +1177,15 @@ __global__ __launch_bounds__(BQB == 32 ? 256 : 512, 1) void fa_bwd_dkdv_pair_ker
     const bool more = it + 1 < niter;
     float sv = 0.f;
     if (more) sv = issue(qbuf(qn), obuf(on), h1, t1);
-    // lane offsets refreshed per step: the buffer addresses derived from
-    // them are formed here (one add per buffer) instead of hoisted out of
-    // the loop, where those of all the buffers would stay live
-    LaneOffs<DK> lq = lq0;
-    LaneOffs<DV> lv = lv0;
-    int xo = xo0;
-    lq.refresh();
-    lv.refresh();
-    asm volatile("" : "+v"(xo));
+    // lane offsets refreshed per step (in place): the buffer addresses
+    // derived from them are formed here (one add per buffer) instead of
+    // hoisted out of the loop, where those of all the buffers would stay live
+    lq0.refresh();
+    lv0.refresh();
+    asm volatile("" : "+v"(xo0));
+    const LaneOffs<DK>& lq = lq0;
+    const LaneOffs<DV>& lv = lv0;
+    const int xo = xo0;
     if constexpr (PS) {
       if (it < niter) p_tile(qbuf(qc), obuf(oc), xbuf(xs, xo), sbufp(qc), tile_q0(tc), lq, lv);
     } else {
@@ -1202,7 +1202,7 @@ __global__ __launch_bounds__(BQB == 32 ? 256 : 512, 1) void fa_bwd_dkdv_pair_ker
       if (cur) dp_cur(dp, pq, fP, started, sbufp(qc) + BQB);
     }
     if (more) {
-      if (tid < 2 * BQB) sbufp(qn)[tid] = stat_val(sv);
+      if (wave < 2 * BQB / 64) sbufp(qn)[tid] = stat_val(sv);
       wait_vmem();
     }
     __syncthreads();
