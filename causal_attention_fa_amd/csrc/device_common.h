@@ -443,6 +443,23 @@ struct TrPipe {
       __builtin_amdgcn_sched_barrier(0);
     }
   }
+  // as run(), with hook(k) after MFMA k: VALU work for the wave to issue
+  // while the matrix unit is busy; it may fill breg[c16] for chunks whose
+  // MFMAs come later (c16 > k / NDB).
+  template <class Hook>
+  __device__ __forceinline__ void run(f32x16 (&acc)[NDB], const LDS_AS char* tile, int col0,
+                                      const bf16x8 (&breg)[NC16], int lane, Hook&& hook) {
+    static_assert(PD > 0, "the hooked order is pinned");
+#pragma unroll
+    for (int k = 0; k < N; ++k) {
+      if (k + PD < N)
+        op[(k + PD) % R] =
+            lds_tr_operand<D>(tile, 0, (k + PD) / NDB, col0 + 32 * ((k + PD) % NDB), lane);
+      acc[k % NDB] = mfma32(op[k % R], breg[k / NDB], acc[k % NDB]);
+      hook(k);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
 };
 
 // Pack accumulators acc[8*h .. 8*h+7] of a 32x32 tile to 8 bf16 (RNE): the

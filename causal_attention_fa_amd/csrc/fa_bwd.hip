@@ -49,6 +49,13 @@ namespace fa {
 #define BWD_UNROLL(DK) ((DK) != 192)
 #endif
 
+// 1: on tiles without a mask the dQ pass computes dS chunk by chunk
+// between the MFMAs of dQ^T += K^T dS^T (the VALU of chunk c + 1 under
+// the MFMAs of chunk c); 0: all of dS first, then the product.
+#ifndef DQ_SPLIT
+#define DQ_SPLIT 1
+#endif
+
 #ifndef BWD_LDS_PD
 #define BWD_LDS_PD(DK) ((DK) == 192 ? 0 : 2)
 #endif
@@ -186,6 +193,56 @@ __global__ __launch_bounds__(64 * NW, (DK >= 192 ? 1 : 8 / NW)) void fa_bwd_dq_k
         mma_rows2<DK, DV, NS, BWD_LDS_PD(DK)>(s, Kt, qreg, dp, Vt, doreg, lane);
         ktp.start(Kt, 0, lane);   // first K^T operands of dQ, read during the softmax
       }
+      auto elem = [&](int t, int i) __attribute__((always_inline)) {
+        float th;
+        const float p = fast_exp2(p_arg<CAP>(s[t][i], a, lse2, th));
+        float ds = p * (dp[t][i] - Di);
+        if (CAP) ds *= 1.f - th * th;
+        s[t][i] = ds;
+      };
+      auto pack_chunk = [&](int c16) __attribute__((always_inline)) {
+        float tmp[8];
+  #pragma unroll
+        for (int jj = 0; jj < 8; ++jj) tmp[jj] = s[c16 >> 1][8 * (c16 & 1) + jj];
+        return pack_bf16(tmp);
+      };
+      constexpr int NC16 = BKV / 16;
+      if constexpr (DQ_SPLIT && BWD_LDS_PD(DK) > 0 && 8 % NDB == 0) {
+        if (!empty) {
+          if (!full) {
+            // invisible pairs: S = -inf gives p = 0 without a cap; with one,
+            // p <= 1 stays finite and dP = D_i makes dS exactly 0
+  #pragma unroll
+            for (int t = 0; t < NS; ++t)
+  #pragma unroll
+              for (int i = 0; i < 16; ++i) {
+                const int kv = kv0 + 32 * t + acc_row(i, g);
+                const bool vis = (kv <= qrow) & ((W == 0) | (kv > qrow - W));
+                s[t][i] = vis ? s[t][i] : -INFINITY;
+                if (CAP) dp[t][i] = vis ? dp[t][i] : Di;
+              }
+          }
+          // chunk 0's dS first, then the dQ MFMAs of chunk c carry the dS
+          // VALU of chunk c + 1 (8 / NDB elements after each MFMA)
+          bf16x8 dsb[NC16];
+  #pragma unroll
+          for (int jj = 0; jj < 8; ++jj) elem(0, jj);
+          dsb[0] = pack_chunk(0);
+          ktp.run(dqacc, Kt, 0, dsb, lane, [&](int k) __attribute__((always_inline)) {
+            constexpr int EPH = 8 / NDB;
+            const int c = k / NDB, r = k % NDB;
+            if (c + 1 < NC16) {
+  #pragma unroll
+              for (int e = 0; e < EPH; ++e) {
+                const int jj = r * EPH + e;
+                elem((c + 1) >> 1, 8 * ((c + 1) & 1) + jj);
+              }
+              if (r == NDB - 1) dsb[c + 1] = pack_chunk(c + 1);
+            }
+          });
+          return;
+        }
+      }
       if (!empty) {
         // dS^T in s[] (fp32), then bf16 operands.  Every element is computed
         // branch-free; partial tiles then zero the invisible ones in one block
@@ -193,13 +250,7 @@ __global__ __launch_bounds__(64 * NW, (DK >= 192 ? 1 : 8 / NW)) void fa_bwd_dq_k
   #pragma unroll
         for (int t = 0; t < NS; ++t)
   #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            float th;
-            const float p = fast_exp2(p_arg<CAP>(s[t][i], a, lse2, th));
-            float ds = p * (dp[t][i] - Di);
-            if (CAP) ds *= 1.f - th * th;
-            s[t][i] = ds;
-          }
+          for (int i = 0; i < 16; ++i) elem(t, i);
         if (!full) {
   #pragma unroll
           for (int t = 0; t < NS; ++t)
@@ -210,14 +261,9 @@ __global__ __launch_bounds__(64 * NW, (DK >= 192 ? 1 : 8 / NW)) void fa_bwd_dq_k
               s[t][i] = vis ? s[t][i] : 0.f;
             }
         }
-        bf16x8 dsb[BKV / 16];
+        bf16x8 dsb[NC16];
   #pragma unroll
-        for (int c16 = 0; c16 < BKV / 16; ++c16) {
-          float tmp[8];
-  #pragma unroll
-          for (int jj = 0; jj < 8; ++jj) tmp[jj] = s[c16 >> 1][8 * (c16 & 1) + jj];
-          dsb[c16] = pack_bf16(tmp);
-        }
+        for (int c16 = 0; c16 < NC16; ++c16) dsb[c16] = pack_chunk(c16);
         ktp.run(dqacc, Kt, 0, dsb, lane);
       }
   };
