@@ -49,11 +49,13 @@ namespace fa {
 #define BWD_UNROLL(DK) ((DK) != 192)
 #endif
 
-// 1: on tiles without a mask the dQ pass computes dS chunk by chunk
-// between the MFMAs of dQ^T += K^T dS^T (the VALU of chunk c + 1 under
-// the MFMAs of chunk c); 0: all of dS first, then the product.
+// 1: the dQ pass computes dS chunk by chunk between the MFMAs of
+// dQ^T += K^T dS^T (the VALU of chunk c + 1 under the MFMAs of chunk c);
+// 2 (32-key tiles): in addition S is computed before dP, and P under the
+// MFMAs of dP, so that only P (dP - D) is left for the product's MFMAs;
+// 0: all of dS first, then the product.
 #ifndef DQ_SPLIT
-#define DQ_SPLIT 1
+#define DQ_SPLIT 2
 #endif
 
 #ifndef BWD_LDS_PD
@@ -189,6 +191,74 @@ __global__ __launch_bounds__(64 * NW, (DK >= 192 ? 1 : 8 / NW)) void fa_bwd_dq_k
       const bool full = kv0 + BKV - 1 <= qa && (W == 0 || kv0 > qb - W);
       f32x16 s[NS], dp[NS];
       TrPipe<DK, NDB, BKV / 16, BWD_LDS_PD(DK)> ktp;
+      constexpr int NC16 = BKV / 16;
+      auto pack_chunk = [&](int c16) __attribute__((always_inline)) {
+        float tmp[8];
+  #pragma unroll
+        for (int jj = 0; jj < 8; ++jj) tmp[jj] = s[c16 >> 1][8 * (c16 & 1) + jj];
+        return pack_bf16(tmp);
+      };
+      if constexpr (DQ_SPLIT == 2 && NS == 1 && BWD_LDS_PD(DK) > 0 && 8 % NDB == 0 &&
+                    16 % (DV / 16) == 0) {
+        // S first, then dP with P = 2^(...) computed under its MFMAs; dS =
+        // P (dP - D) chunk by chunk under the dQ product's MFMAs.
+        if (empty) return;
+        constexpr int PD = BWD_LDS_PD(DK), NK = DK / 16, NV = DV / 16, EP = 16 / NV;
+  #pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          s[0][i] = 0.f;
+          dp[0][i] = 0.f;
+        }
+        auto fS = [&](int k) { return lds_row_operand<DK>(Kt, 0, k, lane); };
+        auto fV = [&](int k) { return lds_row_operand<DV>(Vt, 0, k, lane); };
+        MfmaSeq<NK, PD> sq;
+        MfmaSeq<NV, PD> vq;
+        sq.start(fS);
+        sq.run(fS, [&](int k) { return qreg[k]; }, [&](int) -> f32x16& { return s[0]; },
+               [&](int) {});
+        vq.start(fV);
+        if (!full) {
+          // invisible pairs: S = -inf gives P = 0, and under a cap
+          // tanh = -1, so that the factor 1 - tanh^2 is 0
+  #pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int kv = kv0 + acc_row(i, g);
+            const bool vis = (kv <= qrow) & ((W == 0) | (kv > qrow - W));
+            s[0][i] = vis ? s[0][i] : -INFINITY;
+          }
+        }
+        float thv[CAP ? 16 : 1];
+        vq.run(fV, [&](int k) { return doreg[k]; }, [&](int) -> f32x16& { return dp[0]; },
+               [&](int k) __attribute__((always_inline)) {
+  #pragma unroll
+                 for (int e = 0; e < EP; ++e) {
+                   const int i = k * EP + e;
+                   float th;
+                   s[0][i] = fast_exp2(p_arg<CAP>(s[0][i], a, lse2, th));
+                   if (CAP) thv[i] = th;
+                 }
+               });
+        ktp.start(Kt, 0, lane);
+        auto fin = [&](int i) __attribute__((always_inline)) {
+          float ds = s[0][i] * (dp[0][i] - Di);
+          if (CAP) ds *= 1.f - thv[i] * thv[i];
+          s[0][i] = ds;
+        };
+        bf16x8 dsb[NC16];
+  #pragma unroll
+        for (int jj = 0; jj < 8; ++jj) fin(jj);
+        dsb[0] = pack_chunk(0);
+        ktp.run(dqacc, Kt, 0, dsb, lane, [&](int k) __attribute__((always_inline)) {
+          constexpr int EPH = 8 / NDB;
+          const int c = k / NDB, r = k % NDB;
+          if (c + 1 < NC16) {
+  #pragma unroll
+            for (int e = 0; e < EPH; ++e) fin(8 * (c + 1) + r * EPH + e);
+            if (r == NDB - 1) dsb[c + 1] = pack_chunk(c + 1);
+          }
+        });
+        return;
+      }
       if (!empty) {
         mma_rows2<DK, DV, NS, BWD_LDS_PD(DK)>(s, Kt, qreg, dp, Vt, doreg, lane);
         ktp.start(Kt, 0, lane);   // first K^T operands of dQ, read during the softmax
@@ -200,13 +270,6 @@ __global__ __launch_bounds__(64 * NW, (DK >= 192 ? 1 : 8 / NW)) void fa_bwd_dq_k
         if (CAP) ds *= 1.f - th * th;
         s[t][i] = ds;
       };
-      auto pack_chunk = [&](int c16) __attribute__((always_inline)) {
-        float tmp[8];
-  #pragma unroll
-        for (int jj = 0; jj < 8; ++jj) tmp[jj] = s[c16 >> 1][8 * (c16 & 1) + jj];
-        return pack_bf16(tmp);
-      };
-      constexpr int NC16 = BKV / 16;
       if constexpr (DQ_SPLIT && BWD_LDS_PD(DK) > 0 && 8 % NDB == 0) {
         if (!empty) {
           if (!full) {
