@@ -198,8 +198,7 @@ __global__ __launch_bounds__(64 * NW, (DK >= 192 ? 1 : 8 / NW)) void fa_bwd_dq_k
         for (int jj = 0; jj < 8; ++jj) tmp[jj] = s[c16 >> 1][8 * (c16 & 1) + jj];
         return pack_bf16(tmp);
       };
-      if constexpr (DQ_SPLIT == 2 && NS == 1 && BWD_LDS_PD(DK) > 0 && 8 % NDB == 0 &&
-                    16 % (DV / 16) == 0) {
+      if constexpr (DQ_SPLIT == 2 && NS == 1 && BWD_LDS_PD(DK) > 0 && 16 % (DV / 16) == 0) {
         // S first, then dP with P = 2^(...) computed under its MFMAs; dS =
         // P (dP - D) chunk by chunk under the dQ product's MFMAs.
         if (empty) return;
@@ -249,11 +248,10 @@ __global__ __launch_bounds__(64 * NW, (DK >= 192 ? 1 : 8 / NW)) void fa_bwd_dq_k
         for (int jj = 0; jj < 8; ++jj) fin(jj);
         dsb[0] = pack_chunk(0);
         ktp.run(dqacc, Kt, 0, dsb, lane, [&](int k) __attribute__((always_inline)) {
-          constexpr int EPH = 8 / NDB;
           const int c = k / NDB, r = k % NDB;
           if (c + 1 < NC16) {
   #pragma unroll
-            for (int e = 0; e < EPH; ++e) fin(8 * (c + 1) + r * EPH + e);
+            for (int e = r * 8 / NDB; e < (r + 1) * 8 / NDB; ++e) fin(8 * (c + 1) + e);
             if (r == NDB - 1) dsb[c + 1] = pack_chunk(c + 1);
           }
         });
