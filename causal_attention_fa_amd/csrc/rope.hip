@@ -10,8 +10,11 @@
 // HBM-bound elementwise work.  The angle depends only on (t, i), not on the
 // (b, h) row, so each thread fixes one 16-byte group of a [T, d] slice,
 // evaluates its cos/sin once (accurate sincosf: angles reach ~8e3 rad) and
-// then streams that group through BH_PER consecutive (b, h) slices:
-// coalesced 16-byte loads/stores, trigonometry amortised over the slices.
+// then handles that group in BH_PER (b, h) slices: all BH_PER 16-byte loads
+// are issued before the first store (each thread touches only its own
+// addresses, so this order is safe in place), trigonometry amortised over
+// the slices.  The launcher picks BH_PER (1, 2, 4 or 8) as the largest
+// value that still gives the grid at least 8 workgroups per CU.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -38,7 +41,7 @@ struct Vec<float> {
   typedef float V __attribute__((ext_vector_type(4)));
 };
 
-template <typename T, bool BWD>
+template <typename T, bool BWD, int BH_PER>
 __global__ __launch_bounds__(kThreads) void rope_vec_kernel(RopeArgs a) {
   constexpr int N = Vec<T>::N;
   typedef typename Vec<T>::V V;
@@ -47,25 +50,30 @@ __global__ __launch_bounds__(kThreads) void rope_vec_kernel(RopeArgs a) {
   if (e0 >= slice) return;
   const int t = (int)(e0 / a.d);
   const int c0 = (int)(e0 % a.d);                 // even: N and d are even
+  const int bh0 = blockIdx.y * BH_PER;
+  const int nb = min(a.BH - bh0, BH_PER);        // ragged last row of the grid
+  const T* x = (const T*)a.x;
+  T* y = (T*)a.y;
+  V v[BH_PER];
+#pragma unroll
+  for (int j = 0; j < BH_PER; ++j)
+    if (j < nb) v[j] = *(const V*)(x + (long)(bh0 + j) * slice + e0);
   float cs[N / 2], sn[N / 2];
 #pragma unroll
   for (int p = 0; p < N / 2; ++p) rope_sincos((float)t, a.inv_freq[c0 / 2 + p], BWD, cs[p], sn[p]);
-  const int bh0 = blockIdx.y * kBhPer;
-  const int bh1 = min(a.BH, bh0 + kBhPer);
-  const T* x = (const T*)a.x;
-  T* y = (T*)a.y;
-  for (int bh = bh0; bh < bh1; ++bh) {
-    const long off = (long)bh * slice + e0;
-    const V v = *(const V*)(x + off);
-    V r;
 #pragma unroll
-    for (int p = 0; p < N / 2; ++p) {
-      float xe = (float)v[2 * p], xo = (float)v[2 * p + 1];
-      rope_pair(cs[p], sn[p], xe, xo);
-      r[2 * p] = (T)xe;
-      r[2 * p + 1] = (T)xo;
+  for (int j = 0; j < BH_PER; ++j) {
+    if (j < nb) {
+      V r;
+#pragma unroll
+      for (int p = 0; p < N / 2; ++p) {
+        float xe = (float)v[j][2 * p], xo = (float)v[j][2 * p + 1];
+        rope_pair(cs[p], sn[p], xe, xo);
+        r[2 * p] = (T)xe;
+        r[2 * p + 1] = (T)xo;
+      }
+      *(V*)(y + (long)(bh0 + j) * slice + e0) = r;
     }
-    *(V*)(y + off) = r;
   }
 }
 
@@ -92,19 +100,40 @@ __global__ __launch_bounds__(kThreads) void rope_pair_kernel(RopeArgs a) {
   }
 }
 
+template <typename T, bool BWD, int BH_PER>
+void launch_vec(const RopeArgs& a, unsigned gx, hipStream_t stream) {
+  const dim3 grid(gx, (unsigned)((a.BH + BH_PER - 1) / BH_PER));
+  hipLaunchKernelGGL((rope_vec_kernel<T, BWD, BH_PER>), grid, dim3(kThreads), 0, stream, a);
+}
+
+template <typename T, bool BWD>
+void launch_vec_bh(const RopeArgs& a, unsigned gx, hipStream_t stream) {
+  // largest slices-per-thread count that keeps >= 8 workgroups per CU
+  constexpr long kMinGroups = 8 * 256;
+  const long per1 = (long)gx * a.BH;               // workgroups at one slice per thread
+  if (per1 >= 8 * kMinGroups)
+    launch_vec<T, BWD, 8>(a, gx, stream);
+  else if (per1 >= 4 * kMinGroups)
+    launch_vec<T, BWD, 4>(a, gx, stream);
+  else if (per1 >= 2 * kMinGroups)
+    launch_vec<T, BWD, 2>(a, gx, stream);
+  else
+    launch_vec<T, BWD, 1>(a, gx, stream);
+}
+
 template <typename T>
 hipError_t launch_rope(const RopeArgs& a, bool bwd, hipStream_t stream) {
   const long slice = (long)a.T * a.d;
-  const unsigned gy = (unsigned)((a.BH + kBhPer - 1) / kBhPer);
   const int N = Vec<T>::N;
   if (a.d % N == 0) {
-    const dim3 grid((unsigned)((slice / N + kThreads - 1) / kThreads), gy);
+    const unsigned gx = (unsigned)((slice / N + kThreads - 1) / kThreads);
     if (bwd)
-      hipLaunchKernelGGL((rope_vec_kernel<T, true>), grid, dim3(kThreads), 0, stream, a);
+      launch_vec_bh<T, true>(a, gx, stream);
     else
-      hipLaunchKernelGGL((rope_vec_kernel<T, false>), grid, dim3(kThreads), 0, stream, a);
+      launch_vec_bh<T, false>(a, gx, stream);
     stage_mark(stream);
   } else {
+    const unsigned gy = (unsigned)((a.BH + kBhPer - 1) / kBhPer);
     const dim3 grid((unsigned)((slice / 2 + kThreads - 1) / kThreads), gy);
     if (bwd)
       hipLaunchKernelGGL((rope_pair_kernel<T, true>), grid, dim3(kThreads), 0, stream, a);
