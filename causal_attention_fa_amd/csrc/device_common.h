@@ -36,6 +36,32 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// The same product with the accumulator held in the accumulation registers
+// (AGPRs), for kernels whose long-lived accumulator does not fit beside
+// their working set in the VGPRs.  Written as the instruction itself so that
+// the accumulator's register class is fixed; the compiler's hazard tracking
+// does not see it, so before any VALU access of such an accumulator (a
+// rescale, the epilogue) the caller waits with agpr_acc_fence() -- the
+// matrix core's write-back latency of a 32x32 product (at most 19 wait
+// states for a 16-pass XDL op) -- and operands written by the VALU are
+// never the instruction right before it.
+__device__ __forceinline__ void mfma32_agpr(f32x16& acc, bf16x8 a, bf16x8 b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+// The accumulators are operands of the wait, so no read of them can be
+// scheduled ahead of it.
+template <int N>
+__device__ __forceinline__ void agpr_acc_fence(f32x16 (&acc)[N]) {
+  static_assert(N == 4 || N == 8, "accumulator count");
+  if constexpr (N == 8)
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+                 : "+a"(acc[0]), "+a"(acc[1]), "+a"(acc[2]), "+a"(acc[3]), "+a"(acc[4]),
+                   "+a"(acc[5]), "+a"(acc[6]), "+a"(acc[7]));
+  else
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+                 : "+a"(acc[0]), "+a"(acc[1]), "+a"(acc[2]), "+a"(acc[3]));
+}
+
 // Row index (within a 32-row MFMA output tile) held by accumulator i of a
 // lane in half g = lane/32.
 __device__ __forceinline__ int acc_row(int i, int g) {

@@ -580,6 +580,312 @@ __global__ __launch_bounds__(512, 1) void fa_fwd_pair_kernel(FwdArgs a) {
   }
 }
 
+// Software-pipelined forward (one wave per 32 query rows holding the whole
+// head, the key range walked in 32-key units).  Per unit i the wave issues
+// two MFMA blocks and puts the softmax VALU of the *other* unit under each:
+//   S(i+1) = K(i+1) Q^T  (D/16 MFMAs)  carrying  exp2, row sum, bf16 pack of P(i)
+//   O^T += V(i)^T P(i)^T (2 D/32 MFMAs) carrying  cap tanh, mask, row max of S(i+1)
+// so the matrix core always has the next product while the VALU works on a
+// unit that no MFMA in flight touches.  The online-softmax rescale of O
+// that unit i+1's max may require is applied after the O^T block (O is not
+// being accumulated then); the running sum is rescaled with it.  Unit i+1's
+// K tile and unit i's V tile are read in iteration i, so K(i+2) and V(i+1)
+// are loaded during it into the buffers that K(i) and V(i-1) left: both are
+// double-buffered, one barrier per unit.  Head size 256 runs one wave per
+// SIMD (the 32 x 256 accumulator lives in the accumulation registers, q in
+// 64 VGPRs); head size 128 fits two.
+template <int D, bool CAP>
+__global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void fa_fwd_pipe_kernel(FwdArgs a) {
+  constexpr int NW = 4, BQ = 32 * NW, BKV = 32;
+  constexpr int TILE = Lay<D>::template bytes<BKV>();
+  constexpr int NC = D / 16;     // 16-wide chunks of the q.k contraction
+  constexpr int NDB = D / 32;    // 32-wide blocks of the output
+  constexpr int NO = 2 * NDB;    // MFMAs of the O^T block
+  constexpr int PD = 2;          // LDS operands issued this many MFMAs ahead
+  // head size 256: O (32 x 256 fp32 = 128 registers per lane) stays in the
+  // AGPRs, beside q (64 VGPRs) and the working set in the VGPRs
+  constexpr bool AGPR_O = D >= 256;
+  __shared__ __attribute__((aligned(1024))) char kb0[TILE];
+  __shared__ __attribute__((aligned(1024))) char kb1[TILE];
+  __shared__ __attribute__((aligned(1024))) char vb0[TILE];
+  __shared__ __attribute__((aligned(1024))) char vb1[TILE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5;
+  const int l32 = lane & 31;
+  const int T = a.T;
+  const int W = a.window;
+  const int G = a.H / a.Hkv;
+  const int nqb = (T + BQ - 1) / BQ;
+  const WorkItem w = decode_work(blockIdx.x, nqb, a.B, a.Hkv, G, true);
+  const int h = w.hkv * G + w.r;
+  const int q0 = w.blk * BQ;
+  const int qw0 = q0 + 32 * wave;
+  const int qrow = qw0 + l32;
+  const size_t bh = (size_t)w.b * a.H + h;
+  const size_t bkv = (size_t)w.b * a.Hkv + w.hkv;
+  const bf16* Kp = a.k + bkv * T * D;
+  const bf16* Vp = a.v + bkv * T * D;
+
+  // q as the B operand of S^T = K Q^T: lane holds q[qrow][16c + 8g .. +7]
+  bf16x8 qreg[NC];
+  {
+    const int qr = min(qrow, T - 1);
+    const bf16x8* src = (const bf16x8*)(a.q + (bh * T + qr) * D + 8 * g);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) qreg[c] = src[2 * c];
+    if (a.rope_cs) {
+      // RoPE fused into the load: chunk c holds the pairs 8c + 4g + p
+      const float4* cs4 = (const float4*)(a.rope_cs + (size_t)qr * D);
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        bf16x8 x = qreg[c];
+        const float4 r0 = cs4[(8 * c + 4 * g) / 2], r1 = cs4[(8 * c + 4 * g) / 2 + 1];
+        const float cv[4] = {r0.x, r0.z, r1.x, r1.z}, sv[4] = {r0.y, r0.w, r1.y, r1.w};
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          float xe = (float)x[2 * p], xo = (float)x[2 * p + 1];
+          rope_pair(cv[p], sv[p], xe, xo);
+          x[2 * p] = (bf16)xe;
+          x[2 * p + 1] = (bf16)xo;
+        }
+        qreg[c] = x;
+      }
+      if (a.q_rot && qrow < T) {
+        bf16x8* dst = (bf16x8*)(a.q_rot + (bh * T + qrow) * D + 8 * g);
+#pragma unroll
+        for (int c = 0; c < NC; ++c) dst[2 * c] = qreg[c];
+      }
+    }
+  }
+
+  int kv_lo = 0;
+  if (W > 0) kv_lo = max(0, q0 - W + 1);
+  const int t_lo = kv_lo / BKV;
+  const int kv_hi = min(T, q0 + BQ);
+  const int nu = (kv_hi + BKV - 1) / BKV - t_lo;   // units of the workgroup
+
+  const bool has_sink = a.sinks != nullptr;
+  const float sink2 = has_sink ? a.sinks[h] * kLog2e : 0.f;
+  f32x16 oacc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
+  float m = has_sink ? sink2 : kMaxInit;
+  float lsum = (has_sink && g == 0) ? 1.f : 0.f;
+  float mxl = -INFINITY;
+  const float cexp = CAP ? a.cap_log2e : a.scale_log2e;
+
+  TileDma<D, BKV, NW> dm;
+  dm.init(wave, lane);
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  auto kbuf = [&](auto p_c) -> LDS_AS char* {
+    return decltype(p_c)::value ? (LDS_AS char*)kb1 : (LDS_AS char*)kb0;
+  };
+  auto vbuf = [&](auto p_c) -> LDS_AS char* {
+    return decltype(p_c)::value ? (LDS_AS char*)vb1 : (LDS_AS char*)vb0;
+  };
+  // per-lane parts of the LDS operand addresses (the rest are immediates)
+  LaneOffs<D> lo;
+  lo.init(lane);
+  // keys visible to this lane's row: qrow - span < key <= qrow.  Units of
+  // the workgroup's range that hold none of a wave's keys (at most a few
+  // per wave: near the diagonal, at the window's start) are computed
+  // anyway, fully masked: they add exact zeros, and every wave runs the
+  // same straight-line schedule.
+  const unsigned span = W > 0 ? (unsigned)W : 0x7fffffffu;
+
+  // the two score tiles (unit parity)
+  f32x16 sa[2];
+  float mt = -INFINITY;        // running max of the unit being prepared
+  float ps = 0.f;              // row sum of the unit being exponentiated
+  bf16x8 pb[2];                // P of the current unit, bf16, per 16-key chunk
+
+  // S(u) into sa[X] (+ sb[X]), hook(k) after MFMA k
+  auto s_block = [&](auto x_c, const LDS_AS char* Kt, auto&& hook) __attribute__((always_inline)) {
+    constexpr int X = decltype(x_c)::value;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sa[X][i] = 0.f;
+    auto fS = [&](int k) { return lds_row_op<D>(Kt, lo, 0, k); };
+    MfmaSeq<NC, PD> sq;
+    sq.start(fS);
+    sq.run(fS, [&](int k) { return qreg[k]; }, [&](int) -> f32x16& { return sa[X]; }, hook);
+  };
+  // softmax part A of the unit in tile X: score elements [e0, e1) -- the
+  // partial sums added, cap, mask -- and their running max
+  // softmax part A of the unit in tile X: score elements [e0, e1) -- cap,
+  // visibility mask (branch-free, every unit) -- and their running max.
+  // Element i of the tile is key kv0 + acc_row(i, g); it is visible iff
+  // 0 <= qrow - key < span (span = W, or everything for a causal layer)
+  auto part_a = [&](auto x_c, int u, int e0, int e1) __attribute__((always_inline)) {
+    constexpr int X = decltype(x_c)::value;
+    const int base = qrow - (t_lo + u) * BKV - 4 * g;   // qrow - key for acc_row(i, g) = 4g
+#pragma unroll
+    for (int i = e0; i < e1; ++i) {
+      float x = sa[X][i];
+      if (CAP) {
+        const float e = fast_exp2(x * a.two_scale_over_cap_log2e);
+        x = 1.f - 2.f * __builtin_amdgcn_rcpf(e + 1.f);   // tanh
+      }
+      const bool vis = (unsigned)(base - (8 * (i >> 2) + (i & 3))) < span;
+      x = vis ? x : -INFINITY;
+      sa[X][i] = x;
+      mt = fmaxf(mt, x);
+    }
+  };
+  // the unit's max across the lane pair, then (after the O^T block that
+  // precedes it) the lazy rescale of O and l
+  auto a_tail = [&]() __attribute__((always_inline)) {
+    mt = xor32_max(mt) * cexp;
+    if (a.max_logit) mxl = fmaxf(mxl, qrow < T ? mt : -INFINITY);
+  };
+  auto rescale = [&]() __attribute__((always_inline)) {
+    if (__any(mt > m + kRescaleSlack)) {
+      if constexpr (AGPR_O) agpr_acc_fence(oacc);
+      const float mnew = fmaxf(m, mt);
+      const float alpha = fast_exp2(m - mnew);
+      m = mnew;
+      lsum *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+    }
+    mt = -INFINITY;
+  };
+  // softmax part B of the unit in tile X: p = 2^(s c - m) for elements
+  // [e0, e1), row sum, bf16 packs of the 16-key chunks as they complete
+  auto part_b = [&](auto x_c, int e0, int e1) __attribute__((always_inline)) {
+    constexpr int X = decltype(x_c)::value;
+#pragma unroll
+    for (int i = e0; i < e1; ++i) {
+      const float p = fast_exp2(fmaf(sa[X][i], cexp, -m));
+      sa[X][i] = p;
+      ps += p;
+      if (i == 7 || i == 15) {
+        float tmp[8];
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) tmp[jj] = sa[X][i - 7 + jj];
+        pb[i >> 3] = pack_bf16(tmp);
+      }
+    }
+  };
+  auto b_tail = [&]() __attribute__((always_inline)) {
+    lsum += ps;
+    ps = 0.f;
+  };
+  // O^T += V^T P^T for the unit whose P is in pb, hook(k) after MFMA k
+  auto o_block = [&](const LDS_AS char* Vt, auto&& hook) __attribute__((always_inline)) {
+    auto fV = [&](int k) { return lds_tr_op<D>(Vt, lo, k / NDB, k % NDB); };
+    if constexpr (AGPR_O) {
+      // the ring of MfmaSeq, with the accumulator pinned to the AGPRs
+      constexpr int R = PD + 1;
+      bf16x8 op[R];
+#pragma unroll
+      for (int k = 0; k < PD; ++k) op[k] = fV(k);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int k = 0; k < NO; ++k) {
+        if (k + PD < NO) op[(k + PD) % R] = fV(k + PD);
+        mfma32_agpr(oacc[k % NDB], op[k % R], pb[k / NDB]);
+        hook(k);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+      MfmaSeq<NO, PD> vq;
+      vq.start(fV);
+      vq.run(fV, [&](int k) { return pb[k / NDB]; },
+             [&](int k) -> f32x16& { return oacc[k % NDB]; }, hook);
+    }
+  };
+
+  // prologue: K(0), V(0), K(1) resident; S(0) and its part A
+  dm.load(Kp, T * D * 2, kbuf(I0{}), t_lo * BKV, wave);
+  dm.load(Vp, T * D * 2, vbuf(I0{}), t_lo * BKV, wave);
+  if (nu > 1) dm.load(Kp, T * D * 2, kbuf(I1{}), (t_lo + 1) * BKV, wave);
+  wait_vmem();
+  __syncthreads();
+  s_block(I0{}, kbuf(I0{}), [&](int) {});
+  part_a(I0{}, 0, 0, 16);
+  a_tail();
+  rescale();
+  __syncthreads();   // every wave is done with K(0) before K(2) replaces it
+
+  // iteration i: tiles K(i+1) in kbuf[(i+1)&1], V(i) in vbuf[i&1]; score
+  // tile of unit i in sa[i&1], of unit i+1 in sa[(i+1)&1]
+  auto step = [&](auto p_c, auto more_c, const int i) __attribute__((always_inline)) {
+    constexpr int P = decltype(p_c)::value;
+    constexpr bool more = decltype(more_c)::value;   // a unit i + 1 exists
+    using PN = std::integral_constant<int, 1 - P>;
+    lo.refresh();   // addresses formed per step, not hoisted for every buffer
+    if (i + 2 < nu) dm.load(Kp, T * D * 2, kbuf(p_c), (t_lo + i + 2) * BKV, wave);
+    if (more) dm.load(Vp, T * D * 2, vbuf(PN{}), (t_lo + i + 1) * BKV, wave);
+    constexpr int EP = 16 / NC > 0 ? 16 / NC : 1;   // elements per S MFMA
+    constexpr int EA = 16 / NO > 0 ? 16 / NO : 1;   // elements per O MFMA
+    if constexpr (more) {
+      // S(i+1) with P(i)'s exponentials under its MFMAs
+      s_block(PN{}, kbuf(PN{}), [&](int k) __attribute__((always_inline)) {
+        if (k * EP < 16) part_b(p_c, k * EP, k * EP + EP);
+      });
+      if (16 / NC == 0) part_b(p_c, 0, 16);
+      b_tail();
+      // O^T += V(i)^T P(i)^T with S(i+1)'s cap, mask and max under its MFMAs
+      o_block(vbuf(p_c), [&](int k) __attribute__((always_inline)) {
+        if (k * EA < 16) part_a(PN{}, i + 1, k * EA, k * EA + EA);
+      });
+      if (16 / NO == 0) part_a(PN{}, i + 1, 0, 16);
+      a_tail();
+      rescale();
+      wait_vmem();
+      __syncthreads();
+    } else {
+      part_b(p_c, 0, 16);
+      b_tail();
+      o_block(vbuf(p_c), [&](int) {});
+    }
+  };
+  using T1 = std::true_type;
+  using F1 = std::false_type;
+  int i = 0;
+  for (; i + 2 < nu; i += 2) {
+    step(I0{}, T1{}, i);
+    step(I1{}, T1{}, i + 1);
+  }
+  if (i + 2 == nu) {
+    step(I0{}, T1{}, i);
+    step(I1{}, F1{}, i + 1);
+  } else {
+    step(I0{}, F1{}, i);
+  }
+
+  if (a.max_logit) {
+    float v = mxl;
+#pragma unroll
+    for (int off = 1; off < 32; off <<= 1) v = fmaxf(v, __shfl_xor(v, off));
+    if (lane == 0 && v > -INFINITY) atomic_max_f32(a.max_logit + bh, v * kLn2);
+  }
+  const float ltot = xor32_sum(lsum);
+  if constexpr (AGPR_O) agpr_acc_fence(oacc);
+  if (qrow < T) {
+    const float inv = 1.f / ltot;
+    bf16* Op = a.o + (bh * T + qrow) * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        bf16x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = (bf16)(oacc[db][4 * i4 + e] * inv);
+        *(bf16x4*)(Op + 32 * db + 8 * i4 + 4 * g) = v;
+      }
+    if (g == 0) a.lse[bh * T + qrow] = (m + __log2f(ltot)) * kLn2;
+  }
+}
+
 // Tile shapes per head size (keys per tile, waves, query blocks per wave),
 // chosen by measurement on MI355X.
 #ifndef FWD128_CFG
@@ -627,6 +933,27 @@ static hipError_t launch_fwd_pair(const FwdArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int D>
+static hipError_t launch_fwd_pipe(const FwdArgs& a, hipStream_t stream) {
+  const int nqb = (a.T + 127) / 128;
+  const dim3 grid((unsigned)nqb * a.B * a.H);
+  if (a.cap_log2e > 0.f)
+    hipLaunchKernelGGL((fa_fwd_pipe_kernel<D, true>), grid, dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((fa_fwd_pipe_kernel<D, false>), grid, dim3(256), 0, stream, a);
+  stage_mark(stream);
+  return hipGetLastError();
+}
+
+// forward kernel per head size: 0 the one-tile kernel (fa_fwd_kernel, or the
+// paired kernel at d = 256), 1 the software-pipelined kernel
+#ifndef FWD128_PIPE
+#define FWD128_PIPE 0
+#endif
+#ifndef FWD256_PIPE
+#define FWD256_PIPE 1
+#endif
+
 __global__ void fill_f32_kernel(float* p, int n, float v) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = v;
@@ -641,9 +968,16 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, int d, int d_v, hipStream_t stream)
   if (d == d_v) {
     switch (d) {
       case 64: return launch_fwd_d<64, 64, 64, 4, 1>(a, stream);
-      case 128: return launch_fwd_d<128, 128, FWD128_CFG>(a, stream);
+      case 128:
+#if FWD128_PIPE
+        return launch_fwd_pipe<128>(a, stream);
+#else
+        return launch_fwd_d<128, 128, FWD128_CFG>(a, stream);
+#endif
       case 256:
-#if FWD256_PAIR
+#if FWD256_PIPE
+        return launch_fwd_pipe<256>(a, stream);
+#elif FWD256_PAIR
         return launch_fwd_pair<256, FWD256_BKV>(a, stream);
 #else
         return launch_fwd_d<256, 256, FWD256_CFG>(a, stream);
