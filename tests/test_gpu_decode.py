@@ -16,6 +16,7 @@ import torch
 
 from causal_attention_fa_amd import synth
 from oracle import decode as OD
+from tests import envelope as EV
 from tests.gpu_util import check, dev, poison, say
 
 pytestmark = pytest.mark.gpu
@@ -91,7 +92,10 @@ def test_decode_parity_vs_oracle(case):
                 np.testing.assert_allclose(lse[b], sinks, rtol=1e-6)
             else:
                 assert np.all(np.isneginf(lse[b]))
-    errs = dict(o=check("o", o[live], ro[live], False), lse=check("lse", lse[live], rl[live], False))
+    Eo, El = EV.decode_envelopes(synth.to_f64(q), np.nan_to_num(kf), np.nan_to_num(vf), lens,
+                                 scale, W, cap, None if sinks is None else sinks.astype(np.float64))
+    errs = dict(o=check("o", o[live], ro[live], env=Eo[live]),
+                lse=check("lse", lse[live], rl[live], env=El[live]))
     say(f"  errors {errs}")
     o2, l2 = run_decode(q, k, v, lens, sinks, scale, W, cap)
     assert np.array_equal(o, o2) and np.array_equal(lse, l2, equal_nan=True), "not deterministic"
@@ -116,7 +120,9 @@ def test_decode_full_size_sampled():
         n = int(lens_h[b])
         kb = synth.to_f64(k[b:b + 1, :, :n].cpu())
         vb = synth.to_f64(v[b:b + 1, :, :n].cpu())
-        ro, rl = OD.decode(synth.to_f64(q[b:b + 1].cpu()), kb, vb, [n], w.scale, w.window, w.softcap)
-        e1 = check("o", o_h[b:b + 1], ro, False)
-        e2 = check("lse", l_h[b:b + 1], rl, False)
+        qb = synth.to_f64(q[b:b + 1].cpu())
+        ro, rl = OD.decode(qb, kb, vb, [n], w.scale, w.window, w.softcap)
+        Eo, El = EV.decode_envelopes(qb, kb, vb, [n], w.scale, w.window, w.softcap)
+        e1 = check("o", o_h[b:b + 1], ro, env=Eo)
+        e2 = check("lse", l_h[b:b + 1], rl, env=El)
         say(f"  b={b} len={n} errors o {e1:.2e} lse {e2:.2e}")

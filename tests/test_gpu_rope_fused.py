@@ -16,6 +16,7 @@ import torch
 from causal_attention_fa_amd import synth
 from oracle import attention as OA
 from oracle import rope as OR
+from tests import envelope as EV
 from tests.gpu_util import check, dev, poison, say
 
 pytestmark = pytest.mark.gpu
@@ -81,14 +82,18 @@ def test_fused_rope(case):
     # stage-isolated dq: oracle backward on the GPU's rotated q and k, rotated back
     qr64, kr64 = synth.to_f64(r["qr_f_t"]), synth.to_f64(r["kr"])
     vf, dof = synth.to_f64(v), synth.to_f64(do)
-    dq_rot, _, _ = OA.attn_bwd(qr64, kr64, vf, dof, scale, W, cap)
-    dq_ref = OR.rope_bwd(dq_rot, table)
-    e1 = check("dq (stage)", r["dq_f"], dq_ref, False)
-    # end to end from the un-rotated inputs
+    st = EV.full_envelopes(qr64, kr64, vf, dof, scale, W, cap)
+    e1 = check("dq (stage)", r["dq_f"], OR.rope_bwd(st["dq"], table), env=EV.rotate_env(st["E_dq"]),
+               qty="dq")
+    # end to end from the un-rotated inputs: the envelope on the oracle's own
+    # rotation rounded to bf16, plus what that rounding moves the result
     q64, k64 = synth.to_f64(q), synth.to_f64(k)
     qe, ke = OR.rope(q64, table), OR.rope(k64, table)
-    dq_e, _, _ = OA.attn_bwd(qe, ke, vf, dof, scale, W, cap)
-    e2 = check("dq (e2e)", r["dq_f"], OR.rope_bwd(dq_e, table), False, elem_guard=False)
-    o_e, _ = OA.attn_fwd(qe, ke, vf, scale, W, cap)
-    e3 = check("o (e2e)", r["o_f"], o_e, False, elem_guard=False)
+    rnd = lambda x: torch.from_numpy(x).to(torch.bfloat16).double().numpy()
+    ex = EV.full_envelopes(qe, ke, vf, dof, scale, W, cap)
+    rb = EV.full_envelopes(rnd(qe), rnd(ke), vf, dof, scale, W, cap)
+    dq_ref, dq_rb = OR.rope_bwd(ex["dq"], table), OR.rope_bwd(rb["dq"], table)
+    e2 = check("dq (e2e)", r["dq_f"], dq_ref,
+               env=EV.rotate_env(rb["E_dq"]) + np.abs(dq_ref - dq_rb), qty="dq")
+    e3 = check("o (e2e)", r["o_f"], ex["o"], env=rb["E_o"] + np.abs(ex["o"] - rb["o"]), qty="o")
     say(f"  dq stage {e1:.2e} dq e2e {e2:.2e} o e2e {e3:.2e}")

@@ -17,6 +17,7 @@ import torch
 
 from causal_attention_fa_amd import synth
 from oracle import attention as OA
+from tests import envelope as EV
 from tests.gpu_util import check, dev, poison, run_gpu, say
 
 pytestmark = pytest.mark.gpu
@@ -72,10 +73,10 @@ def test_sink_parity_vs_oracle(case):
     got = run_gpu_sink(q, k, v, do, sinks, scale, W, cap)
     qf, kf, vf, dof = (synth.to_f64(t) for t in (q, k, v, do))
     s64 = sinks.astype(np.float64)
-    o, lse = OA.attn_fwd(qf, kf, vf, scale, W, cap, sinks=s64)
-    dq, dk, dv, dsk = OA.attn_bwd(qf, kf, vf, dof, scale, W, cap, sinks=s64)
-    errs = {n: check(n, got[n], r, False) for n, r in
-            dict(o=o, lse=lse, dq=dq, dk=dk, dv=dv).items()}
+    ref = EV.full_envelopes(qf, kf, vf, dof, scale, W, cap, sinks=s64)
+    o, lse = ref["o"], ref["lse"]
+    _, _, _, dsk = OA.attn_bwd(qf, kf, vf, dof, scale, W, cap, sinks=s64)
+    errs = {n: check(n, got[n], ref[n], env=ref["E_" + n]) for n in ("o", "lse", "dq", "dk", "dv")}
     # sink gradient: bound by the magnitude sum of its terms
     G = H // Hkv
     Dm = np.sum(dof * o, axis=-1)                              # [B, H, T]

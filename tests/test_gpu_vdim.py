@@ -12,6 +12,7 @@ import torch
 
 from causal_attention_fa_amd import synth
 from oracle import attention as OA
+from tests import envelope as EV
 from tests.gpu_util import check, dev, oracle_full, poison, run_gpu, say
 
 pytestmark = pytest.mark.gpu
@@ -59,7 +60,7 @@ def test_vdim_parity_vs_oracle(case):
     say(f"[vdim] B{B} H{H}/{Hkv} T{T} d{DK}/{DV} W{W} cap{cap}")
     got = run_vdim(q, k, v, do, scale, W, cap)
     ref = oracle_full(q, k, v, do, scale, W, cap)
-    errs = {n: check(n, got[n], ref[n], False) for n in ("o", "lse", "dq", "dk", "dv")}
+    errs = {n: check(n, got[n], ref[n], env=ref["E_" + n]) for n in ("o", "lse", "dq", "dk", "dv")}
     say(f"  errors {errs}")
     again = run_vdim(q, k, v, do, scale, W, cap)
     for n in got:
@@ -86,26 +87,36 @@ def test_unsupported_pair_is_rejected():
     assert e.value.code == fa.FA_ERR_UNSUPPORTED
 
 
-def test_mla_full_size_sampled():
-    """mla workload (B2 H16 T8192 d192/128) at full size: o and lse on
-    sampled query rows of every head, gradients for a sampled (b, h)."""
+def test_mla_full_size():
+    """mla workload (B2 H16 T8192 d192/128) at full size: o and lse on every
+    row of every (b, h); dq, dk, dv on sampled rows of four heads."""
+    from concurrent.futures import ThreadPoolExecutor
+    from threadpoolctl import threadpool_limits
     w = synth.WORKLOADS["mla"]
     q, k, v, do = synth.draw(w)
     say(f"[mla full] {w}")
     got = run_vdim(q, k, v, do, w.scale, w.window, w.softcap)
-    rows = np.array([0, 1, 31, 32, 4095, 4096, 8000, 8191])
-    for b, h in [(0, 0), (1, 15), (0, 7)]:
-        qf, kf, vf = (synth.to_f64(t) for t in (q[b, h], k[b, h], v[b, h]))
-        o, lse, _ = OA.head_forward_rows(qf, kf, vf, w.scale, 0, 0.0, rows=rows)
-        e1 = check("o", got["o"][b, h][rows], o, False)
-        e2 = check("lse", got["lse"][b, h][rows], lse, False)
-        say(f"  (b,h)=({b},{h}) o {e1:.2e} lse {e2:.2e}")
-    b, h = 1, 3
-    qf, kf, vf, dof = (synth.to_f64(t) for t in (q[b, h], k[b, h], v[b, h], do[b, h]))
-    q_rows = np.array([5, 2047, 6000, 8191])
-    kv_rows = np.array([0, 100, 4096, 8191])
-    dq, dk, dv, _, _ = OA.head_grads_sampled(qf, kf, vf, dof, w.scale, 0, 0.0, q_rows, kv_rows)
-    e = [check("dq", got["dq"][b, h][q_rows], dq, False),
-         check("dk", got["dk"][b, h][kv_rows], dk, False),
-         check("dv", got["dv"][b, h][kv_rows], dv, False)]
-    say(f"  grads (b,h)=({b},{h}) {e}")
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    grad_heads = {(0, 0), (1, 15), (0, 7), (1, 3)}
+    q_rows = np.array([0, 5, 31, 32, 2047, 4096, 6000, 8191])
+    kv_rows = np.array([0, 1, 100, 4095, 4096, 8191])
+
+    def one(bh):
+        b, h = bh
+        qf, kf, vf, dof = (synth.to_f64(t) for t in (q[b, h], k[b, h], v[b, h], do[b, h]))
+        if bh in grad_heads:
+            return bh, EV.head_envelopes(qf, kf, vf, dof, w.scale, 0, 0.0, q_rows=q_rows,
+                                         kv_rows=kv_rows)
+        return bh, EV.head_envelopes(qf, kf, vf, None, w.scale, 0, 0.0)
+
+    with threadpool_limits(1), ThreadPoolExecutor(16) as ex:
+        res = dict(ex.map(one, heads))
+    for (b, h), r in res.items():
+        check(f"o[{b},{h}]", got["o"][b, h], r["o"], env=r["E_o"], qty="o")
+        check(f"lse[{b},{h}]", got["lse"][b, h], r["lse"], env=r["E_lse"], qty="lse")
+        if (b, h) in grad_heads:
+            kvc = EV.combine_kv([r])     # H = Hkv: one query head per KV head
+            check(f"dq[{b},{h}]", got["dq"][b, h][q_rows], r["dq"], env=r["E_dq"], qty="dq")
+            check(f"dk[{b},{h}]", got["dk"][b, h][kv_rows], kvc["dk"], env=kvc["E_dk"], qty="dk")
+            check(f"dv[{b},{h}]", got["dv"][b, h][kv_rows], kvc["dv"], env=kvc["E_dv"], qty="dv")
+    say(f"  {len(heads)} heads: o, lse every row; grads on {sorted(grad_heads)}")
