@@ -6,9 +6,10 @@
 //
 // The work is bound by HBM: every visible K and V byte is read once and
 // used by all G query heads of its KV group.  Two kernels:
-//   * split: one wave per (batch, KV head, chunk of the cache).  K and V
-//     tiles of 32 keys stream global -> registers (one tile ahead) -> LDS;
-//     the G query heads of the group are the columns of S^T = K Q^T, so the
+//   * split: one or two waves per (batch, KV head, chunk of the cache).  K
+//     and V tiles of 32 keys go straight from HBM into double-buffered LDS
+//     (direct buffer loads, one tile ahead, non-temporal: the cache is read
+//     once); the G query heads of the group are the columns of S^T = K Q^T, so the
 //     contraction over d and P V run on the bf16 MFMA exactly as in the
 //     prefill forward (columns past G are idle), and the VALU only does the
 //     online softmax.  The chunk's unnormalised output O, running max m
@@ -16,8 +17,10 @@
 //   * combine: one wave per (batch, head) merges the chunks exactly by
 //     their maxima and sums (o = sum_c 2^(m_c - M) O_c / L), adds the sink
 //     to the normaliser, and writes o (bf16) and lse.
-// Cache rows at or past the sequence's length are never read (the tile
-// loads clamp to the last valid row and the mask removes the duplicates).
+// Cache rows at or past the sequence's length are never read: the loads go
+// through a buffer resource whose range ends at the sequence's last row, so
+// rows past it read as zeros with no memory access, and the mask removes
+// them from the softmax.
 #include <type_traits>
 
 #include "device_common.h"
