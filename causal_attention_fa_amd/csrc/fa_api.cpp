@@ -9,6 +9,7 @@
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "fa.h"
@@ -111,6 +112,48 @@ int check_ptrs(const char* fn, const Range* rs, int n, int first_out) {
   return FA_OK;
 }
 
+// fa_bwd_noalloc: the backward's [B, H, T] row statistics in a fixed
+// device array instead of an allocation.  Each GPU holds its own copy; its
+// address on a device comes from hipGetSymbolAddress with that device
+// current (the array's name in host code is only a host-side stand-in),
+// looked up on the first call that runs on the device and kept.
+constexpr size_t kNoAllocRows = size_t(1) << 22;   // B * H * T at most (16 MiB of float)
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch_dev[kMaxDevices] = {};
+
+}  // namespace
+
+static __device__ __align__(256) float scratch[kNoAllocRows];
+
+namespace {
+
+// scratch's address on the device that runs `stream` (which must be the
+// current device) into *out; FA_OK or the error (recorded)
+int scratch_on_stream_device(hipStream_t stream, const char* fn, float** out) {
+  int cur = -1;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return finish(e, stream, fn);
+  int sdev = cur;
+  if (stream) {
+    e = hipStreamGetDevice(stream, &sdev);
+    if (e != hipSuccess) return finish(e, stream, fn);
+  }
+  if (sdev != cur || cur < 0 || cur >= kMaxDevices)
+    return fail(FA_ERR_INVALID_ARG,
+                std::string(fn) + ": the stream's device must be the current device (< 64)");
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_dev[cur]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return finish(e, stream, fn);
+    if (!ptr) return fail(FA_ERR_HIP, std::string(fn) + ": no device address for the scratch");
+    g_scratch_dev[cur] = (float*)ptr;
+  }
+  *out = g_scratch_dev[cur];
+  return FA_OK;
+}
+
 int resolve_window(int window, int T) { return window >= T ? 0 : window; }
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -192,7 +235,8 @@ int attn_bwd(bool f32, const void* q, const void* k, const void* v, const void* 
              const float* lse, const void* dO, void* dq, void* dk, void* dv, int B, int H,
              int Hkv, int T, int d, float scale, int window, int global_every, float softcap,
              hipStream_t stream, const char* fn = nullptr, const float* sinks = nullptr,
-             float* dsinks = nullptr, int d_v = -1, const float* rope = nullptr) {
+             float* dsinks = nullptr, int d_v = -1, const float* rope = nullptr,
+             bool static_rows = false) {
   if (!fn) fn = f32 ? "fa_bwd_f32" : "fa_bwd";
   if (d_v < 0) d_v = d;
   int rc = check_attn(fn, B, H, Hkv, T, d, scale, window, global_every, softcap, d_v);
@@ -218,13 +262,24 @@ int attn_bwd(bool f32, const void* q, const void* k, const void* v, const void* 
       return fail(FA_ERR_INVALID_ARG, std::string(fn) + ": dsinks overlaps sinks");
   }
   const int W = resolve_window(window, T);
+  // the [B, H, T] row statistics D: the library's fixed array
+  // (fa_bwd_noalloc), else stream-ordered scratch
   float* Dst = nullptr;
-  hipError_t e = hipMallocAsync((void**)&Dst, (size_t)B * H * T * sizeof(float), stream);
-  if (e != hipSuccess) return finish(e, stream, "fa_bwd scratch");
+  hipError_t e = hipSuccess;
+  if (static_rows) {
+    rc = scratch_on_stream_device(stream, fn, &Dst);
+    if (rc) return rc;
+  } else {
+    e = hipMallocAsync((void**)&Dst, (size_t)B * H * T * sizeof(float), stream);
+    if (e != hipSuccess) return finish(e, stream, "fa_bwd scratch");
+  }
+  auto free_d = [&]() {
+    if (!static_rows) (void)hipFreeAsync(Dst, stream);
+  };
   if (dsinks) {
     e = fa::launch_fill_f32(dsinks, H, 0.f, stream);
     if (e != hipSuccess) {
-      (void)hipFreeAsync(Dst, stream);
+      free_d();
       return finish(e, stream, fn);
     }
   }
@@ -234,7 +289,7 @@ int attn_bwd(bool f32, const void* q, const void* k, const void* v, const void* 
     if (e == hipSuccess) e = fa::launch_rope_table(rope, rope_cs, T, d / 2, stream);
     if (e != hipSuccess) {
       if (rope_cs) (void)hipFreeAsync(rope_cs, stream);
-      (void)hipFreeAsync(Dst, stream);
+      free_d();
       return finish(e, stream, fn);
     }
   }
@@ -263,7 +318,7 @@ int attn_bwd(bool f32, const void* q, const void* k, const void* v, const void* 
     a.rope_cs = rope_cs;
     e = fa::launch_bwd_bf16(a, d, d_v, stream);
   }
-  hipError_t e2 = hipFreeAsync(Dst, stream);
+  hipError_t e2 = static_rows ? hipSuccess : hipFreeAsync(Dst, stream);
   if (e == hipSuccess) e = e2;
   if (rope_cs) {
     e2 = hipFreeAsync(rope_cs, stream);
@@ -353,6 +408,22 @@ int fa_bwd_f32(const void* q, const void* k, const void* v, const void* o, const
                hipStream_t stream) {
   return attn_bwd(true, q, k, v, o, lse, dO, dq, dk, dv, B, H, Hkv, T, d, scale, window,
                   global_every, softcap, stream);
+}
+
+int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                   const void* dO, void* dq, void* dk, void* dv, int B, int H, int Hkv, int T,
+                   int d, float scale, int window, int global_every, float softcap,
+                   hipStream_t stream) {
+  const char* fn = "fa_bwd_noalloc";
+  const int rc = check_attn(fn, B, H, Hkv, T, d, scale, window, global_every, softcap);
+  if (rc) return rc;
+  if ((double)B * H * T > (double)kNoAllocRows)
+    return fail(FA_ERR_INVALID_ARG, std::string(fn) + ": B*H*T = " +
+                                        std::to_string((long long)B * H * T) +
+                                        " exceeds its fixed scratch of " +
+                                        std::to_string(kNoAllocRows) + " rows");
+  return attn_bwd(false, q, k, v, o, lse, dO, dq, dk, dv, B, H, Hkv, T, d, scale, window,
+                  global_every, softcap, stream, fn, nullptr, nullptr, -1, nullptr, true);
 }
 
 int fa_fwd_sink(const void* q, const void* k, const void* v, void* o, float* lse,

@@ -43,6 +43,7 @@ _ROPE = [_P, _P, _P, _I, _I, _I, _I, _P]
 
 for _name, _args in [("fa_fwd", _ATTN_FWD), ("fa_fwd_f32", _ATTN_FWD),
                      ("fa_bwd", _ATTN_BWD), ("fa_bwd_f32", _ATTN_BWD),
+                     ("fa_bwd_noalloc", _ATTN_BWD),
                      ("rope_apply", _ROPE), ("rope_apply_bwd", _ROPE),
                      ("rope_apply_f32", _ROPE), ("rope_apply_bwd_f32", _ROPE)]:
     _fn = getattr(_lib, _name)
@@ -85,7 +86,7 @@ _lib.fa_bwd_kernels.restype = ctypes.c_char_p
 _lib.fa_last_error.argtypes = []
 _lib.fa_last_error.restype = ctypes.c_char_p
 
-EXPORTS = ("fa_fwd", "fa_bwd", "fa_fwd_sink", "fa_bwd_sink", "fa_fwd_vdim", "fa_bwd_vdim",
+EXPORTS = ("fa_fwd", "fa_bwd", "fa_bwd_noalloc", "fa_fwd_sink", "fa_bwd_sink", "fa_fwd_vdim", "fa_bwd_vdim",
            "fa_fwd_rope", "fa_bwd_rope",
            "fa_decode", "fa_decode_splits", "rope_apply", "rope_apply_bwd", "fa_fwd_f32",
            "fa_bwd_f32", "rope_apply_f32", "rope_apply_bwd_f32", "fa_layer_window", "fa_rope_inv_freq",
@@ -164,6 +165,12 @@ def fa_bwd_f32(q, k, v, o, lse, dO, dq, dk, dv, B, H, Hkv, T, d, scale, window=0
                global_every=0, softcap=0.0, stream=None):
     return _call_bwd(_lib.fa_bwd_f32, q, k, v, o, lse, dO, dq, dk, dv, B, H, Hkv, T, d, scale,
                      window, global_every, softcap, stream)
+
+
+def fa_bwd_noalloc(q, k, v, o, lse, dO, dq, dk, dv, B, H, Hkv, T, d, scale, window=0,
+                   global_every=0, softcap=0.0, stream=None):
+    return _call_bwd(_lib.fa_bwd_noalloc, q, k, v, o, lse, dO, dq, dk, dv, B, H, Hkv, T, d,
+                     scale, window, global_every, softcap, stream)
 
 
 def fa_fwd_sink(q, k, v, o, lse, sinks, max_logit, B, H, Hkv, T, d, scale, window=0,

@@ -46,9 +46,12 @@
  *
  * Ownership and streams: every call only enqueues work on `stream` (NULL =
  * the default stream) and returns; device faults surface at the caller's
- * next synchronisation.  fa_bwd allocates a small float32 scratch
- * ([B, H, T] row statistics) stream-ordered (hipMallocAsync/hipFreeAsync on
- * `stream`); nothing else is allocated and no state persists between calls.
+ * next synchronisation.  Calls that need scratch allocate it stream-ordered
+ * (hipMallocAsync/hipFreeAsync on `stream`): fa_bwd and its _sink, _vdim
+ * and _rope variants (the [B, H, T] float32 row statistics), fa_fwd_rope
+ * and fa_bwd_rope (a [T, d/2] float32 (cos, sin) table), fa_decode (the
+ * per-chunk partial results).  fa_bwd_noalloc allocates nothing.  No state
+ * persists between calls.
  *
  * Errors: 0 on success, else a negative FA_ERR_* code; fa_last_error()
  * returns a thread-local message describing the most recent failure.
@@ -83,6 +86,22 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o,
            const float* lse, const void* dO, void* dq, void* dk, void* dv,
            int B, int H, int Hkv, int T, int d, float scale, int window,
            int global_every, float softcap, hipStream_t stream);
+
+/* fa_bwd without any allocation, for callers that cannot allocate (code
+ * under HIP graph capture, allocation-free serving loops, harnesses that
+ * forbid hipMalloc): same parameters, semantics and results as fa_bwd
+ * (bit for bit), with the [B, H, T] float32 row statistics in a fixed array
+ * in device memory that the library holds for the life of the process on
+ * each GPU it runs on (16 MiB).  B * H * T must not exceed 4,194,304
+ * (FA_ERR_INVALID_ARG otherwise, before any device work); `stream` must
+ * belong to the current device.  The array is fully rewritten by each call
+ * before it is read (nothing has to start at zero); calls that overlap on
+ * one GPU share it and race -- order them on one stream. */
+int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                   const float* lse, const void* dO, void* dq, void* dk,
+                   void* dv, int B, int H, int Hkv, int T, int d, float scale,
+                   int window, int global_every, float softcap,
+                   hipStream_t stream);
 
 /* RoPE fused into the attention (bf16 tensors, d = 64, 128, 256).  The
  * query rows are loaded once per workgroup into registers, so their rotation

@@ -164,3 +164,18 @@ def test_bwd_kernel_plan():
     for d, dv in ((96, 96), (128, 64), (0, 0)):
         with pytest.raises(fa.FAError):
             fa.fa_bwd_kernels(d, dv)
+
+
+def test_bwd_noalloc_rejects_oversize_before_device_work():
+    """fa_bwd_noalloc's fixed scratch holds B*H*T <= 4,194,304 rows; a larger
+    call is rejected with its own message before any HIP call."""
+    lib = fa._lib
+    args = [P, 2 * P, 3 * P, 4 * P, 5 * P, 6 * P, 7 * P, 8 * P, 9 * P]
+    # 1 * 2 * 2,097,153 rows: one past the limit (tiny fake buffers: the size
+    # check comes first)
+    assert lib.fa_bwd_noalloc(*args, 1, 2, 2, 2_097_153, 64, 0.125, 0, 0, 0.0, None) == -1
+    assert "exceeds its fixed scratch" in fa.fa_last_error()
+    bad = list(args)
+    bad[6] = bad[0]  # dq aliases q: the shared validation still applies
+    assert lib.fa_bwd_noalloc(*bad, 1, 2, 2, 8, 64, 0.125, 0, 0, 0.0, None) == -1
+    assert "overlaps" in fa.fa_last_error()
