@@ -425,6 +425,8 @@ def main():
                          "around fa_fwd / fa_bwd")
     ap.add_argument("--rope-workloads", default="forge-default,qwen25",
                     help="workloads whose standalone RoPE is timed in GB/s ('none' to skip)")
+    ap.add_argument("--dq-strategy", type=int, default=1,
+                    help="1: time the dQ-atomics traffic beside the separate dQ pass")
     ap.add_argument("--decode-workload", default="qwen25-decode",
                     help="decode workload timed after the main step ('none' to skip)")
     ap.add_argument("--decode-iters", type=int, default=20)
@@ -478,6 +480,7 @@ def main():
                           "decode": r}), flush=True)
         return
 
+    from causal_attention_fa_amd import fa
     src_hash = kernel_sources_hash()
     log(f"[bench] headline workload {args.workload}")
     layers, desc = build_layers(args.workload, dev, args.rope)
@@ -525,6 +528,23 @@ def main():
         del ls
     if configs:
         out["configs"] = configs
+
+    # the dQ strategy, chosen by measurement: the separate query-parallel
+    # pass's time against only the float atomics that accumulating dQ in the
+    # dK/dV pass would issue (a lower bound on that variant's extra cost)
+    if args.dq_strategy:
+        dqs = {}
+        timed = {args.workload: out.get("kernel_ms", {})}
+        timed.update({n: c.get("kernel_ms", {}) for n, c in configs.items()})
+        for name, km in timed.items():
+            w = synth.WORKLOADS.get(name)
+            if w is None or "bwd_dq" not in km or w.dv != w.d:
+                continue
+            torch.cuda.empty_cache()
+            ms = fa.fa_measure_dq_atomics(w.B, w.H, w.Hkv, w.T, w.d, w.window)
+            dqs[name] = {"dq_pass_ms": km["bwd_dq"], "atomics_only_ms": round(ms, 4),
+                         "choice": "separate pass" if km["bwd_dq"] < ms else "atomics"}
+        out["dq_strategy"] = dqs
 
     rope = {}
     for name in [c for c in args.rope_workloads.split(",") if c and c != "none"]:

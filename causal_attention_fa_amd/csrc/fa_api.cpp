@@ -488,6 +488,39 @@ int fa_decode(const void* q, const void* k_cache, const void* v_cache, const int
 
 const char* fa_bwd_kernels(int d, int d_v) { return fa::bwd_kernel_plan(d, d_v); }
 
+int fa_measure_dq_atomics(int B, int H, int Hkv, int T, int d, int window, float* ms) {
+  const char* fn = "fa_measure_dq_atomics";
+  int rc = check_attn(fn, B, H, Hkv, T, d, 1.f, window, 0, 0.f);
+  if (rc) return rc;
+  if (!ms) return fail(FA_ERR_INVALID_ARG, std::string(fn) + ": null pointer ms");
+  // the dK/dV pass's key block and query tile for this head size
+  const int bkvb = d == 256 ? 64 : 128, bqb = d == 256 ? 32 : 64;
+  const int W = resolve_window(window, T);
+  const size_t bytes = (size_t)B * H * T * d * sizeof(float);
+  float* acc = nullptr;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  hipError_t e = hipMalloc((void**)&acc, bytes);
+  if (e == hipSuccess) e = hipMemset(acc, 0, bytes);
+  if (e == hipSuccess) e = hipEventCreate(&e0);
+  if (e == hipSuccess) e = hipEventCreate(&e1);
+  float best = 0.f;
+  for (int rep = 0; rep < 3 && e == hipSuccess; ++rep) {   // best of three
+    e = hipEventRecord(e0, nullptr);
+    if (e == hipSuccess) e = fa::launch_dq_atomic_probe(acc, B, H, Hkv, T, d, W, bkvb, bqb, nullptr);
+    if (e == hipSuccess) e = hipEventRecord(e1, nullptr);
+    if (e == hipSuccess) e = hipEventSynchronize(e1);
+    float t = 0.f;
+    if (e == hipSuccess) e = hipEventElapsedTime(&t, e0, e1);
+    if (e == hipSuccess && (rep == 0 || t < best)) best = t;
+  }
+  if (e0) (void)hipEventDestroy(e0);
+  if (e1) (void)hipEventDestroy(e1);
+  if (acc) (void)hipFree(acc);
+  if (e != hipSuccess) return fail(FA_ERR_HIP, std::string(fn) + ": " + hipGetErrorString(e));
+  *ms = best;
+  return FA_OK;
+}
+
 int fa_decode_splits(int B, int Hkv, int S, int window, int* nsplit, int* chunk) {
   if (B <= 0 || Hkv <= 0 || S <= 0 || window < 0 || !nsplit || !chunk)
     return fail(FA_ERR_INVALID_ARG, "fa_decode_splits: invalid arguments");

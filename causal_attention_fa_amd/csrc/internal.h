@@ -122,6 +122,10 @@ hipError_t launch_decode_bf16(const DecodeArgs& a, int d, bool cap, hipStream_t 
 // into cs [T, half, 2] -- the same values the RoPE kernels compute.
 hipError_t launch_rope_table(const float* inv_freq, float* cs, int T, int half, hipStream_t stream);
 hipError_t launch_rope_bf16(const RopeArgs& a, bool bwd, hipStream_t stream);
+// the dQ-atomics traffic probe (fa_probe.hip): bkvb keys per workgroup,
+// bqb-row query tiles, into acc [B, H, T, d] fp32
+hipError_t launch_dq_atomic_probe(float* acc, int B, int H, int Hkv, int T, int d, int W,
+                                  int bkvb, int bqb, hipStream_t stream);
 hipError_t launch_rope_f32(const RopeArgs& a, bool bwd, hipStream_t stream);
 
 }  // namespace fa

@@ -83,6 +83,8 @@ _lib.fa_set_stage_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), _I]
 _lib.fa_set_stage_events.restype = _I
 _lib.fa_bwd_kernels.argtypes = [_I, _I]
 _lib.fa_bwd_kernels.restype = ctypes.c_char_p
+_lib.fa_measure_dq_atomics.argtypes = [_I, _I, _I, _I, _I, _I, ctypes.POINTER(ctypes.c_float)]
+_lib.fa_measure_dq_atomics.restype = _I
 _lib.fa_last_error.argtypes = []
 _lib.fa_last_error.restype = ctypes.c_char_p
 
@@ -91,7 +93,7 @@ EXPORTS = ("fa_fwd", "fa_bwd", "fa_bwd_noalloc", "fa_fwd_sink", "fa_bwd_sink", "
            "fa_decode", "fa_decode_splits", "rope_apply", "rope_apply_bwd", "fa_fwd_f32",
            "fa_bwd_f32", "rope_apply_f32", "rope_apply_bwd_f32", "fa_layer_window", "fa_rope_inv_freq",
            "fa_rope_inv_freq_llama3", "fa_layer_rope_theta", "fa_set_stage_events",
-           "fa_bwd_kernels", "fa_last_error")
+           "fa_bwd_kernels", "fa_measure_dq_atomics", "fa_last_error")
 
 
 class FAError(RuntimeError):
@@ -231,6 +233,14 @@ def fa_bwd_kernels(d, d_v=None):
     if r is None:
         raise FAError(FA_ERR_UNSUPPORTED, f"fa_bwd_kernels: unsupported head sizes ({d}, {d_v})")
     return r.decode().split(",")
+
+
+def fa_measure_dq_atomics(B, H, Hkv, T, d, window=0):
+    """ms of only the float atomics that accumulating dQ inside the dK/dV
+    pass would issue for this shape (best of three; synchronous)."""
+    ms = ctypes.c_float(0.0)
+    _check(_lib.fa_measure_dq_atomics(B, H, Hkv, T, d, window, ctypes.byref(ms)))
+    return ms.value
 
 
 def fa_decode_splits(B, Hkv, S, window=0):

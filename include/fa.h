@@ -276,6 +276,18 @@ int fa_set_stage_events(void* const* events, int count);
  * only, no device work. */
 const char* fa_bwd_kernels(int d, int d_v);
 
+/* Measurement behind the choice of the dQ strategy (host call, synchronous;
+ * allocates and frees its own buffer): the time in ms (best of three) of
+ * only the global float atomics that accumulating dQ inside the key-parallel
+ * dK/dV pass would issue for this shape -- one add per element of each
+ * query tile's [rows x d] block per key block that sees it, into a
+ * [B, H, T, d] float32 accumulator, in that pass's key blocks and order.  A
+ * lower bound on that variant's extra cost, to set beside the time of the
+ * separate dQ pass.  Returns 0, FA_ERR_INVALID_ARG/UNSUPPORTED (as fa_fwd's
+ * sizes) or FA_ERR_HIP. */
+int fa_measure_dq_atomics(int B, int H, int Hkv, int T, int d, int window,
+                          float* ms);
+
 /* Thread-local text of the last failure ("" if none yet). */
 const char* fa_last_error(void);
 
