@@ -25,8 +25,13 @@ constexpr float kLn2 = 0.6931471805599453f;
 // (-inf) - (-inf) when a row's first tiles are fully masked.
 constexpr float kMaxInit = -1.0e30f;
 // Headroom (log2 units) the online softmax allows before rescaling: p
-// values stay below 2^8, comfortably inside fp32 and bf16 range.
-constexpr float kRescaleSlack = 8.0f;
+// values stay below 2^20.  bf16 shares fp32's exponent range and every
+// rounding is relative, so the headroom costs no precision; the fp32 sums
+// of p v over up to 2^20 keys keep more than 2^80 of range.  A wide slack
+// makes rescales rare: with logits of standard deviation 4 a row's max
+// climbs about 10 log2 units past its first tile, and a rescale of a
+// 32 x 256 accumulator costs as much VALU work as a whole tile.
+constexpr float kRescaleSlack = 20.0f;
 
 // v_mfma_f32_32x32x16_bf16.  Operand layout (measured on gfx950):
 //   A: lane l holds A[row = l%32][k = 8*(l/32) + j], j = 0..7
@@ -82,6 +87,11 @@ __device__ __forceinline__ float xor32_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
                                                   false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_min(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fminf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float xor32_sum(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
@@ -178,6 +188,22 @@ struct TileDma {
       voff[k] = (o < 2 * D && P < BYTES) ? (unsigned)(r * 2 * D + lc * 16) : kOut;
     }
   }
+  // The descriptor of rows row0.. of the buffer [base, base + nbytes): its
+  // base is the tile's first row and its size what is left of the buffer
+  // (at least 0), so that the hardware range check -- which covers the
+  // per-lane offset -- turns every byte past the buffer's end into a zero
+  // read that touches no memory, whatever the tile's position.  The row
+  // offset is the same in every lane; said explicitly, so that a value the
+  // compiler merged through divergent code cannot turn it into a per-lane
+  // loop.
+  __device__ __forceinline__ static __amdgpu_buffer_rsrc_t rsrc(const void* base, int nbytes,
+                                                                int row0) {
+    const int off = __builtin_amdgcn_readfirstlane(row0 * 2 * D);
+    const int left = nbytes - off;
+    // raw buffer, 32-bit data format, no swizzle (gfx9 word 3)
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>((const char*)base + off), 0,
+                                             left > 0 ? left : 0, 0x00020000);
+  }
   // rows row0 .. row0 + ROWS - 1 of the buffer [base, base + nbytes) into
   // the tile image at lds; AUX: the loads' cache policy (2: non-temporal,
   // for data read once)
@@ -185,20 +211,30 @@ struct TileDma {
   __device__ __forceinline__ void load(const void* base, int nbytes, LDS_AS char* lds, int row0,
                                        int wave) const {
 #if defined(__HIP_DEVICE_COMPILE__)   // device-only builtins (the host pass only needs the stub)
-    // raw buffer, 32-bit data format, no swizzle (gfx9 word 3)
-    const __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, nbytes, 0x00020000);
-    // the row offset is the same in every lane; said explicitly, so that a
-    // value the compiler merged through divergent code cannot turn the
-    // scalar offset into a per-lane loop
-    const int soff = __builtin_amdgcn_readfirstlane(row0 * 2 * D);
+    const __amdgpu_buffer_rsrc_t rs = rsrc(base, nbytes, row0);
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
       const int ins = wave + k * NW;
       if (ins < NI)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void*)(lds + ins * 1024), 16, voff[k],
-                                                 soff, 0, AUX);
+                                                 0, 0, AUX);
     }
+#endif
+  }
+  // Load k (0 .. PER-1) of this wave's share of load(), alone: a caller
+  // spreads the loads over its instruction stream, since a burst of them
+  // stalls the wave until the memory pipeline has taken them.  Branch-free
+  // (a branch per load would split the caller's instruction schedule): a
+  // wave with no piece k left loads zeros (its offsets are out of range)
+  // into the image's last, partial round, so the LDS buffer must hold IMG
+  // bytes.
+  static constexpr int IMG = PER * NW * 1024;
+  __device__ __forceinline__ void load_piece(int k, const void* base, int nbytes, LDS_AS char* lds,
+                                             int row0, int wave) const {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc(base, nbytes, row0),
+                                             (LDS_AS void*)(lds + (wave + k * NW) * 1024), 16,
+                                             voff[k], 0, 0, 0);
 #endif
   }
 };
@@ -211,6 +247,17 @@ template <int N = 0>
 __device__ __forceinline__ void wait_vmem() {
   static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
   __builtin_amdgcn_s_waitcnt(0x0f70 | (N & 15) | ((N >> 4) << 14));
+}
+
+// Workgroup barrier between LDS tile phases.  __syncthreads() carries a
+// workgroup release fence, which makes the compiler wait for every
+// outstanding vector-memory operation -- every direct HBM->LDS load still in
+// flight for later tiles -- before the barrier.  This barrier only finishes
+// the wave's own LDS reads and writes (lgkmcnt(0)); the caller has already
+// waited (wait_vmem) for the loads of the tile the barrier publishes.  The
+// memory clobber keeps the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 // A operand for a 32-row MFMA block read along d: lane l gets

@@ -29,31 +29,48 @@
 namespace fa {
 
 
-// QW query blocks of 32 rows per wave: each K or V operand read from LDS
-// feeds QW MFMAs, dividing the LDS traffic per flop by QW.  DK is the head
-// size of q and k, DV that of v and o (equal except for MLA-style heads).
-template <int DK, int DV, int BKV, int NW, int QW, bool CAP>
-__global__ __launch_bounds__(64 * NW, (DK >= 256 || QW > 1 ? 1 : 8 / NW)) void fa_fwd_kernel(
+// LDS operand reads run this many MFMAs ahead of their use (the one-tile
+// kernel, the software-pipelined kernel).
+#ifndef FWD_PD
+#define FWD_PD 3
+#endif
+#ifndef FWD_PIPE_PD
+#define FWD_PIPE_PD 2
+#endif
+
+// One wave owns 32 query rows.  DK is the head size of q and k, DV that of
+// v and o (equal except for MLA-style heads).  NSTG (2..4) K/V tiles are in
+// LDS or in flight at once: the load of tile j + NSTG - 1 is issued when
+// tile j's compute starts, so an HBM load has NSTG - 1 tiles of compute to
+// arrive in.  MINWG > 0 asks for that many resident workgroups per CU (the
+// compiler then caps the registers to fit them); 0 keeps two waves per SIMD.
+template <int DK, int DV, int BKV, int NW, bool CAP, int NSTG = 2, int MINWG = 0>
+__global__ __launch_bounds__(64 * NW, (MINWG > 0 ? MINWG : DK >= 256 ? 1 : 8 / NW)) void fa_fwd_kernel(
     FwdArgs a) {
-  constexpr int NT = 64 * NW;         // threads per workgroup
-  constexpr int RW = 32 * QW;         // query rows per wave
-  constexpr int BQ = RW * NW;         // query rows per workgroup
+  static_assert(NSTG >= 2 && NSTG <= 4, "2 to 4 tile buffers");
+  constexpr int BQ = 32 * NW;         // query rows per workgroup
   constexpr int TILE_K = Lay<DK>::template bytes<BKV>();  // one K tile
   constexpr int TILE_V = Lay<DV>::template bytes<BKV>();  // one V tile
   constexpr int NDB = DV / 32;        // 32-wide blocks of the output
   constexpr int NS = BKV / 32;        // 32-key sub-tiles
   constexpr int NC = DK / 16;         // 16-wide chunks of the q.k contraction
+  constexpr int NP = BKV / 16;        // 16-key chunks of P (B operands of O^T += V^T P^T)
   // one LDS object per buffer: the compiler can then tell the buffer being
   // filled by direct loads from the one being read, and does not make the
   // reads wait for the loads
   __shared__ __attribute__((aligned(1024))) char kb0[TILE_K];
   __shared__ __attribute__((aligned(1024))) char kb1[TILE_K];
+  __shared__ __attribute__((aligned(1024))) char kb2[NSTG > 2 ? TILE_K : 4];
+  __shared__ __attribute__((aligned(1024))) char kb3[NSTG > 3 ? TILE_K : 4];
   __shared__ __attribute__((aligned(1024))) char vb0[TILE_V];
   __shared__ __attribute__((aligned(1024))) char vb1[TILE_V];
+  __shared__ __attribute__((aligned(1024))) char vb2[NSTG > 2 ? TILE_V : 4];
+  __shared__ __attribute__((aligned(1024))) char vb3[NSTG > 3 ? TILE_V : 4];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  __builtin_assume(wave < NW);
   const int g = lane >> 5;
   const int l32 = lane & 31;
   const int T = a.T;
@@ -63,51 +80,45 @@ __global__ __launch_bounds__(64 * NW, (DK >= 256 || QW > 1 ? 1 : 8 / NW)) void f
   const WorkItem w = decode_work(blockIdx.x, nqb, a.B, a.Hkv, G, true);
   const int h = w.hkv * G + w.r;
   const int q0 = w.blk * BQ;
-  const int qw0 = q0 + RW * wave;
+  const int qw0 = q0 + 32 * wave;
+  const int qrow = qw0 + l32;
   const size_t bh = (size_t)w.b * a.H + h;
   const size_t bkv = (size_t)w.b * a.Hkv + w.hkv;
   const bf16* Kp = a.k + bkv * T * DK;
   const bf16* Vp = a.v + bkv * T * DV;
 
-  // Q as the B operand of S^T = K Q^T: lane holds Q[qrow][16c + 8g .. +7]
-  // of its row in each of the wave's QW blocks.
-  bf16x8 qreg[QW][NC];
+  // Q as the B operand of S^T = K Q^T: lane holds Q[qrow][16c + 8g .. +7].
+  bf16x8 qreg[NC];
+  {
+    const bf16x8* src = (const bf16x8*)(a.q + (bh * T + min(qrow, T - 1)) * DK + 8 * g);
 #pragma unroll
-  for (int u = 0; u < QW; ++u) {
-    const int qr = min(qw0 + 32 * u + l32, T - 1);
-    const bf16x8* src = (const bf16x8*)(a.q + (bh * T + qr) * DK + 8 * g);
-#pragma unroll
-    for (int c = 0; c < NC; ++c) qreg[u][c] = src[2 * c];
+    for (int c = 0; c < NC; ++c) qreg[c] = src[2 * c];
   }
   // RoPE fused into the Q load: this lane's 8-element chunks hold the pairs
   // 8c + 4g + p of its row (position = row index), whose (cos, sin) come from
   // the call's table; the rotated row is optionally written out once for the
   // backward.
   if (a.rope_cs) {
+    const float4* cs4 = (const float4*)(a.rope_cs + (size_t)min(qrow, T - 1) * DK);
 #pragma unroll
-    for (int u = 0; u < QW; ++u) {
-      const int qrow = qw0 + 32 * u + l32;
-      const float4* cs4 = (const float4*)(a.rope_cs + (size_t)min(qrow, T - 1) * DK);
+    for (int c = 0; c < NC; ++c) {
+      bf16x8 x = qreg[c];
+      // pairs 8c + 4g .. +3: 4 (cos, sin) = two float4
+      const float4 r0 = cs4[(8 * c + 4 * g) / 2], r1 = cs4[(8 * c + 4 * g) / 2 + 1];
+      const float cv[4] = {r0.x, r0.z, r1.x, r1.z}, sv[4] = {r0.y, r0.w, r1.y, r1.w};
 #pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        bf16x8 x = qreg[u][c];
-        // pairs 8c + 4g .. +3: 4 (cos, sin) = two float4
-        const float4 r0 = cs4[(8 * c + 4 * g) / 2], r1 = cs4[(8 * c + 4 * g) / 2 + 1];
-        const float cv[4] = {r0.x, r0.z, r1.x, r1.z}, sv[4] = {r0.y, r0.w, r1.y, r1.w};
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          float xe = (float)x[2 * p], xo = (float)x[2 * p + 1];
-          rope_pair(cv[p], sv[p], xe, xo);
-          x[2 * p] = (bf16)xe;
-          x[2 * p + 1] = (bf16)xo;
-        }
-        qreg[u][c] = x;
+      for (int p = 0; p < 4; ++p) {
+        float xe = (float)x[2 * p], xo = (float)x[2 * p + 1];
+        rope_pair(cv[p], sv[p], xe, xo);
+        x[2 * p] = (bf16)xe;
+        x[2 * p + 1] = (bf16)xo;
       }
-      if (a.q_rot && qrow < T) {
-        bf16x8* dst = (bf16x8*)(a.q_rot + (bh * T + qrow) * DK + 8 * g);
+      qreg[c] = x;
+    }
+    if (a.q_rot && qrow < T) {
+      bf16x8* dst = (bf16x8*)(a.q_rot + (bh * T + qrow) * DK + 8 * g);
 #pragma unroll
-        for (int c = 0; c < NC; ++c) dst[2 * c] = qreg[u][c];
-      }
+      for (int c = 0; c < NC; ++c) dst[2 * c] = qreg[c];
     }
   }
 
@@ -122,375 +133,121 @@ __global__ __launch_bounds__(64 * NW, (DK >= 256 || QW > 1 ? 1 : 8 / NW)) void f
   // (lane half 0) and whose value contribution is zero.
   const bool has_sink = a.sinks != nullptr;
   const float sink2 = has_sink ? a.sinks[h] * kLog2e : 0.f;
-  f32x16 oacc[QW][NDB];
-  float m[QW], lsum[QW], mxl[QW];
-#pragma unroll
-  for (int u = 0; u < QW; ++u) {
-    m[u] = has_sink ? sink2 : kMaxInit;
-    lsum[u] = (has_sink && g == 0) ? 1.f : 0.f;
-    mxl[u] = -INFINITY;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) oacc[u][db][i] = 0.f;
-  }
-
-  // K, V tiles go straight from HBM to the idle LDS buffers (no staging
-  // registers): issued at the top of an iteration, waited for before its
-  // closing barrier
-  TileDma<DK, BKV, NW> kdm;
-  TileDma<DV, BKV, NW> vdm;
-  kdm.init(wave, lane);
-  vdm.init(wave, lane);
-  auto kbuf = [&](auto p_c) -> LDS_AS char* {
-    return decltype(p_c)::value ? (LDS_AS char*)kb1 : (LDS_AS char*)kb0;
-  };
-  auto vbuf = [&](auto p_c) -> LDS_AS char* {
-    return decltype(p_c)::value ? (LDS_AS char*)vb1 : (LDS_AS char*)vb0;
-  };
-  using I0 = std::integral_constant<int, 0>;
-  using I1 = std::integral_constant<int, 1>;
-  kdm.load(Kp, T * DK * 2, kbuf(I0{}), t_lo * BKV, wave);
-  vdm.load(Vp, T * DV * 2, vbuf(I0{}), t_lo * BKV, wave);
-  wait_vmem();
-  __syncthreads();
-
-  const int qa = qw0, qb = qw0 + RW - 1;
-  // one iteration on the tile in buffer P (the loop is unrolled by two so
-  // that the buffers are compile-time choices)
-  auto step = [&](auto p_c, const int j) __attribute__((always_inline)) {
-    constexpr int P = decltype(p_c)::value;
-    using PN = std::integral_constant<int, 1 - P>;
-    const LDS_AS char* Kt = kbuf(p_c);
-    const LDS_AS char* Vt = vbuf(p_c);
-    const bool more = j + 1 < ntiles;
-    // next K and V tiles into the idle buffers: their latency hides behind
-    // this iteration
-    if (more) {
-      kdm.load(Kp, T * DK * 2, kbuf(PN{}), (t_lo + j + 1) * BKV, wave);
-      vdm.load(Vp, T * DV * 2, vbuf(PN{}), (t_lo + j + 1) * BKV, wave);
-    }
-    const int kv0 = (t_lo + j) * BKV;
-    const bool empty = qa >= T || kv0 > qb || (W > 0 && kv0 + BKV - 1 <= qa - W);
-    const bool full = kv0 + BKV - 1 <= qa && (W == 0 || kv0 > qb - W);
-    if (!empty) {
-      // S^T = K Q^T for every query block; each K operand feeds QW MFMAs and
-      // the next chunk's operands are requested before this chunk's MFMAs.
-      f32x16 s[QW][NS];
-      {
-        bf16x8 op[2][NS];
-#pragma unroll
-        for (int t = 0; t < NS; ++t) {
-          op[0][t] = lds_row_operand<DK>(Kt, 32 * t, 0, lane);
-#pragma unroll
-          for (int u = 0; u < QW; ++u)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) s[u][t][i] = 0.f;
-        }
-#pragma unroll
-        for (int c = 0; c < NC; ++c) {
-          if (c + 1 < NC) {
-#pragma unroll
-            for (int t = 0; t < NS; ++t) op[(c + 1) & 1][t] = lds_row_operand<DK>(Kt, 32 * t, c + 1, lane);
-          }
-#pragma unroll
-          for (int t = 0; t < NS; ++t)
-#pragma unroll
-            for (int u = 0; u < QW; ++u) s[u][t] = mfma32(op[c & 1][t], qreg[u][c], s[u][t]);
-        }
-      }
-      // The exponent's FMA carries the constant: scale*log2(e) on raw scores
-      // without a cap, cap*log2(e) on tanh(scale*x/cap) with one (the max
-      // scales with it either way).
-      const float cexp = CAP ? a.cap_log2e : a.scale_log2e;
-      bf16x8 pb[QW][BKV / 16];
-#pragma unroll
-      for (int u = 0; u < QW; ++u) {
-        const int qrow = qw0 + 32 * u + l32;
-        if (CAP) {
-#pragma unroll
-          for (int t = 0; t < NS; ++t)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              // cap * tanh(scale*x / cap) * log2(e)
-              const float e = fast_exp2(s[u][t][i] * a.two_scale_over_cap_log2e);
-              s[u][t][i] = 1.f - 2.f * __builtin_amdgcn_rcpf(e + 1.f);  // tanh
-            }
-        }
-        if (!full) {
-#pragma unroll
-          for (int t = 0; t < NS; ++t)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int kv = kv0 + 32 * t + acc_row(i, g);
-              const bool vis = (kv <= qrow) & ((W == 0) | (kv > qrow - W));
-              s[u][t][i] = vis ? s[u][t][i] : -INFINITY;
-            }
-        }
-        float mt = -INFINITY;
-#pragma unroll
-        for (int t = 0; t < NS; ++t)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[u][t][i]);
-        mt = xor32_max(mt) * cexp;
-        if (a.max_logit) mxl[u] = fmaxf(mxl[u], qrow < T ? mt : -INFINITY);
-        // Lazy rescaling: the running max only moves (and O, l are rescaled)
-        // when some row's tile max exceeds it by more than kRescaleSlack, so
-        // p = 2^(s - m) stays below 2^kRescaleSlack; the branch is uniform.
-        if (__any(mt > m[u] + kRescaleSlack)) {
-          const float mnew = fmaxf(m[u], mt);
-          const float alpha = fast_exp2(m[u] - mnew);
-          m[u] = mnew;
-          lsum[u] *= alpha;
-#pragma unroll
-          for (int db = 0; db < NDB; ++db)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) oacc[u][db][i] *= alpha;
-        }
-        float ps = 0.f;
-#pragma unroll
-        for (int t = 0; t < NS; ++t)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const float p = fast_exp2(fmaf(s[u][t][i], cexp, -m[u]));
-            s[u][t][i] = p;
-            ps += p;
-          }
-        lsum[u] += ps;
-#pragma unroll
-        for (int c16 = 0; c16 < BKV / 16; ++c16) {
-          float tmp[8];
-#pragma unroll
-          for (int jj = 0; jj < 8; ++jj) tmp[jj] = s[u][c16 >> 1][8 * (c16 & 1) + jj];
-          pb[u][c16] = pack_bf16(tmp);
-        }
-      }
-      // O^T += V^T P^T: each transposed V operand feeds QW MFMAs.
-#pragma unroll
-      for (int c16 = 0; c16 < BKV / 16; ++c16)
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const bf16x8 vop = lds_tr_operand<DV>(Vt, 0, c16, 32 * db, lane);
-#pragma unroll
-          for (int u = 0; u < QW; ++u) oacc[u][db] = mfma32(vop, pb[u][c16], oacc[u][db]);
-        }
-    }
-    if (more) wait_vmem();
-    __syncthreads();
-  };
-  int j = 0;
-  for (; j + 1 < ntiles; j += 2) {
-    step(I0{}, j);
-    step(I1{}, j + 1);
-  }
-  if (j < ntiles) step(I0{}, j);
-
-  if (a.max_logit) {
-    // largest logit of the wave's rows (natural log units), one atomic per wave
-    float v = -INFINITY;
-#pragma unroll
-    for (int u = 0; u < QW; ++u) v = fmaxf(v, mxl[u]);
-#pragma unroll
-    for (int off = 1; off < 32; off <<= 1) v = fmaxf(v, __shfl_xor(v, off));
-    if (lane == 0 && v > -INFINITY) atomic_max_f32(a.max_logit + bh, v * kLn2);
-  }
-#pragma unroll
-  for (int u = 0; u < QW; ++u) {
-    const int qrow = qw0 + 32 * u + l32;
-    const float ltot = xor32_sum(lsum[u]);
-    if (qrow < T) {
-      const float inv = 1.f / ltot;
-      bf16* Op = a.o + (bh * T + qrow) * DV;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          bf16x4 v;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = (bf16)(oacc[u][db][4 * i4 + e] * inv);
-          *(bf16x4*)(Op + 32 * db + 8 * i4 + 4 * g) = v;
-        }
-      if (g == 0) a.lse[bh * T + qrow] = (m[u] + __log2f(ltot)) * kLn2;
-    }
-  }
-}
-
-// Head size 256: one wave cannot hold q and the 256-wide O accumulator at
-// two waves per SIMD, and one wave per SIMD leaves
-// the matrix pipe idle.  So waves work in pairs on the same 32 query rows:
-// wave half hf holds q[:, 128 hf .. +127], computes the partial scores over
-// its half of d, and owns output columns 128 hf .. +127.  The pair swaps
-// partial scores through LDS (one extra barrier per tile); both then add
-// them in the same order, so their scores, softmax state and P are
-// identical, and each accumulates its half of O^T += V^T P^T.
-template <int D, int BKV, bool CAP>
-__global__ __launch_bounds__(512, 1) void fa_fwd_pair_kernel(FwdArgs a) {
-  constexpr int NW = 8, NT = 64 * NW;
-  constexpr int HD = D / 2;             // columns per wave
-  constexpr int BQ = 32 * NW / 2;       // query rows per workgroup
-  constexpr int TILE = Lay<D>::template bytes<BKV>();
-  constexpr int NDB = HD / 32;          // output blocks per wave
-  constexpr int NS = BKV / 32;
-  constexpr int NC = HD / 16;           // chunks of the half contraction
-  constexpr int XS = NS * 16 * 64 * 4;  // one wave's partial scores (bytes)
-  // K, V buffers as separate LDS objects (direct loads into one, reads from
-  // the other, without the compiler making the reads wait), the partial
-  // score exchange area
-  __shared__ __attribute__((aligned(1024))) char kb0[TILE];
-  __shared__ __attribute__((aligned(1024))) char kb1[TILE];
-  __shared__ __attribute__((aligned(1024))) char vb0[TILE];
-  __shared__ __attribute__((aligned(1024))) char vb1[TILE];
-  __shared__ __attribute__((aligned(1024))) char xsm[NW * XS];
-  LDS_AS float* xsb = (LDS_AS float*)xsm;
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int pair = wave >> 1;
-  const int hf = wave & 1;
-  const int g = lane >> 5;
-  const int l32 = lane & 31;
-  const int T = a.T;
-  const int W = a.window;
-  const int G = a.H / a.Hkv;
-  const int nqb = (T + BQ - 1) / BQ;
-  const WorkItem w = decode_work(blockIdx.x, nqb, a.B, a.Hkv, G, true);
-  const int h = w.hkv * G + w.r;
-  const int q0 = w.blk * BQ;
-  const int qw0 = q0 + 32 * pair;
-  const int qrow = qw0 + l32;
-  const size_t bh = (size_t)w.b * a.H + h;
-  const size_t bkv = (size_t)w.b * a.Hkv + w.hkv;
-  const bf16* Kp = a.k + bkv * T * D;
-  const bf16* Vp = a.v + bkv * T * D;
-
-  // this wave's half of the q row: chunk c holds columns HD hf + 16c + 8g ..
-  bf16x8 qreg[NC];
-  {
-    const int qr = min(qrow, T - 1);
-    const bf16x8* src = (const bf16x8*)(a.q + (bh * T + qr) * D + HD * hf + 8 * g);
-#pragma unroll
-    for (int c = 0; c < NC; ++c) qreg[c] = src[2 * c];
-    if (a.rope_cs) {
-      // fused RoPE on this half: chunk c holds pairs HD/2 hf + 8c + 4g + p
-      const float4* cs4 = (const float4*)(a.rope_cs + (size_t)qr * D);
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        bf16x8 x = qreg[c];
-        const int p0 = HD / 2 * hf + 8 * c + 4 * g;
-        const float4 r0 = cs4[p0 / 2], r1 = cs4[p0 / 2 + 1];
-        const float cv[4] = {r0.x, r0.z, r1.x, r1.z}, sv[4] = {r0.y, r0.w, r1.y, r1.w};
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          float xe = (float)x[2 * p], xo = (float)x[2 * p + 1];
-          rope_pair(cv[p], sv[p], xe, xo);
-          x[2 * p] = (bf16)xe;
-          x[2 * p + 1] = (bf16)xo;
-        }
-        qreg[c] = x;
-      }
-      if (a.q_rot && qrow < T) {
-        bf16x8* dst = (bf16x8*)(a.q_rot + (bh * T + qrow) * D + HD * hf + 8 * g);
-#pragma unroll
-        for (int c = 0; c < NC; ++c) dst[2 * c] = qreg[c];
-      }
-    }
-  }
-
-  int kv_lo = 0;
-  if (W > 0) kv_lo = max(0, q0 - W + 1);
-  const int t_lo = kv_lo / BKV;
-  const int kv_hi = min(T, q0 + BQ);
-  const int ntiles = (kv_hi + BKV - 1) / BKV - t_lo;
-
-  const bool has_sink = a.sinks != nullptr;
-  const float sink2 = has_sink ? a.sinks[h] * kLog2e : 0.f;
   f32x16 oacc[NDB];
+  float m = has_sink ? sink2 : kMaxInit;
+  float lsum = (has_sink && g == 0) ? 1.f : 0.f;
+  float mxl = -INFINITY;
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
-  float m = has_sink ? sink2 : kMaxInit;
-  float lsum = (has_sink && g == 0) ? 1.f : 0.f;
-  float mxl = -INFINITY;
-  const float cexp = CAP ? a.cap_log2e : a.scale_log2e;
 
-  TileDma<D, BKV, NW> kdm, vdm;
+  // K, V tiles go straight from HBM to the idle LDS buffers (no staging
+  // registers)
+  using KDma = TileDma<DK, BKV, NW>;
+  using VDma = TileDma<DV, BKV, NW>;
+  KDma kdm;
+  VDma vdm;
   kdm.init(wave, lane);
   vdm.init(wave, lane);
   auto kbuf = [&](auto p_c) -> LDS_AS char* {
-    return decltype(p_c)::value ? (LDS_AS char*)kb1 : (LDS_AS char*)kb0;
+    constexpr int P = decltype(p_c)::value;
+    return P == 0 ? (LDS_AS char*)kb0 : P == 1 ? (LDS_AS char*)kb1 : P == 2 ? (LDS_AS char*)kb2 : (LDS_AS char*)kb3;
   };
   auto vbuf = [&](auto p_c) -> LDS_AS char* {
-    return decltype(p_c)::value ? (LDS_AS char*)vb1 : (LDS_AS char*)vb0;
+    constexpr int P = decltype(p_c)::value;
+    return P == 0 ? (LDS_AS char*)vb0 : P == 1 ? (LDS_AS char*)vb1 : P == 2 ? (LDS_AS char*)vb2 : (LDS_AS char*)vb3;
   };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
-  kdm.load(Kp, T * D * 2, kbuf(I0{}), t_lo * BKV, wave);
-  vdm.load(Vp, T * D * 2, vbuf(I0{}), t_lo * BKV, wave);
-  wait_vmem();
-  __syncthreads();
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  // tile j (counted from t_lo) into buffer P
+  auto issue = [&](auto p_c, int j) __attribute__((always_inline)) {
+    kdm.load(Kp, T * DK * 2, kbuf(p_c), (t_lo + j) * BKV, wave);
+    vdm.load(Vp, T * DV * 2, vbuf(p_c), (t_lo + j) * BKV, wave);
+  };
+  // Waits until this wave's share of the oldest tile in flight is in LDS,
+  // while the `newer` tiles issued after it (0 .. NSTG - 2) may stay in
+  // flight.  Loads finish in issue order, and a wave issues at least LMIN
+  // loads per tile (when a tile's 1 KB pieces do not divide evenly among the
+  // waves, some issue one more), so allowing newer * LMIN outstanding never
+  // lets part of the oldest tile through.
+  constexpr int LMIN = KDma::NI / NW + VDma::NI / NW;
+  auto wait_tile = [&](int newer) __attribute__((always_inline)) {
+    if constexpr (NSTG >= 4) {
+      if (newer >= 2) {
+        wait_vmem<2 * LMIN>();
+        return;
+      }
+    }
+    if constexpr (NSTG >= 3) {
+      if (newer >= 1) {
+        wait_vmem<LMIN>();
+        return;
+      }
+    }
+    wait_vmem<0>();
+  };
+  issue(I0{}, 0);
+  if constexpr (NSTG >= 3)
+    if (1 < ntiles) issue(I1{}, 1);
+  if constexpr (NSTG >= 4)
+    if (2 < ntiles) issue(I2{}, 2);
+  wait_tile(min(NSTG - 2, ntiles - 1));
+  lds_barrier();
 
-  LDS_AS float* const xs_mine = xsb + wave * (XS / 4);
-  const LDS_AS float* const xs_peer = xsb + (wave ^ 1) * (XS / 4);
+  // The exponent's FMA carries the constant: scale*log2(e) on raw scores
+  // without a cap, cap*log2(e) on tanh(scale*x/cap) with one (the max
+  // scales with it either way).
+  const float cexp = CAP ? a.cap_log2e : a.scale_log2e;
   const int qa = qw0, qb = qw0 + 31;
-  // one iteration on the tile in buffer P (unrolled by two)
+  // one iteration on the tile in buffer P (the loop is unrolled by NSTG so
+  // that the buffers are compile-time choices)
   auto step = [&](auto p_c, const int j) __attribute__((always_inline)) {
     constexpr int P = decltype(p_c)::value;
-    using PN = std::integral_constant<int, 1 - P>;
+    using PN = std::integral_constant<int, (P + NSTG - 1) % NSTG>;
     const LDS_AS char* Kt = kbuf(p_c);
     const LDS_AS char* Vt = vbuf(p_c);
-    const bool more = j + 1 < ntiles;
-    if (more) {
-      kdm.load(Kp, T * D * 2, kbuf(PN{}), (t_lo + j + 1) * BKV, wave);
-      vdm.load(Vp, T * D * 2, vbuf(PN{}), (t_lo + j + 1) * BKV, wave);
-    }
+    // tile j + NSTG - 1 into the buffer that tile j - 1 used (every wave has
+    // passed the barrier that ended tile j - 1): its latency hides behind
+    // NSTG - 1 tiles of compute
+    if (j + NSTG - 1 < ntiles) issue(PN{}, j + NSTG - 1);
     const int kv0 = (t_lo + j) * BKV;
-    // the same for both waves of a pair (same rows)
     const bool empty = qa >= T || kv0 > qb || (W > 0 && kv0 + BKV - 1 <= qa - W);
     const bool full = kv0 + BKV - 1 <= qa && (W == 0 || kv0 > qb - W);
-    f32x16 s[NS];
     if (!empty) {
-      // partial S^T over this wave's half of d (chunks NC*hf .. of the row)
-      bf16x8 op[2][NS];
+      // S^T = K Q^T as a pinned MFMA sequence whose K operands are read
+      // FWD_PD MFMAs ahead: left to itself the compiler sinks each read down
+      // to its MFMA, and the LDS latency stalls the matrix unit.
+      f32x16 s[NS];
 #pragma unroll
-      for (int t = 0; t < NS; ++t) {
+      for (int t = 0; t < NS; ++t)
 #pragma unroll
         for (int i = 0; i < 16; ++i) s[t][i] = 0.f;
-        op[0][t] = lds_row_operand<D>(Kt, 32 * t, NC * hf, lane);
+      {
+        MfmaSeq<NC * NS, FWD_PD> sq;
+        auto fK = [&](int k) __attribute__((always_inline)) {
+          return lds_row_operand<DK>(Kt, 32 * (k % NS), k / NS, lane);
+        };
+        sq.start(fK);
+        sq.run(fK, [&](int k) __attribute__((always_inline)) { return qreg[k / NS]; },
+               [&](int k) __attribute__((always_inline)) -> f32x16& { return s[k % NS]; },
+               [](int) {});
       }
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        if (c + 1 < NC) {
-#pragma unroll
-          for (int t = 0; t < NS; ++t)
-            op[(c + 1) & 1][t] = lds_row_operand<D>(Kt, 32 * t, NC * hf + c + 1, lane);
-        }
-#pragma unroll
-        for (int t = 0; t < NS; ++t) s[t] = mfma32(op[c & 1][t], qreg[c], s[t]);
-      }
-#pragma unroll
-      for (int t = 0; t < NS; ++t)
-#pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4)   // lane-major 16-byte groups
-          *(LDS_AS f32x4*)(xs_mine + ((t * 4 + i4) * 64 + lane) * 4) =
-              f32x4{s[t][4 * i4], s[t][4 * i4 + 1], s[t][4 * i4 + 2], s[t][4 * i4 + 3]};
-    }
-    __syncthreads();
-    if (!empty) {
-      // full scores: lower half + upper half, the same order in both waves
-#pragma unroll
-      for (int t = 0; t < NS; ++t)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float peer = xs_peer[((t * 4 + i / 4) * 64 + lane) * 4 + i % 4];
-          s[t][i] = hf == 0 ? s[t][i] + peer : peer + s[t][i];
-        }
+      // the transposed V operands of O^T += V^T P^T are requested now, their
+      // latency hidden behind the softmax
+      MfmaSeq<NP * NDB, FWD_PD> vq;
+      auto fV = [&](int k) __attribute__((always_inline)) {
+        return lds_tr_operand<DV>(Vt, 0, k / NDB, 32 * (k % NDB), lane);
+      };
+      vq.start(fV);
       if (CAP) {
 #pragma unroll
         for (int t = 0; t < NS; ++t)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
+            // cap * tanh(scale*x / cap) * log2(e)
             const float e = fast_exp2(s[t][i] * a.two_scale_over_cap_log2e);
             s[t][i] = 1.f - 2.f * __builtin_amdgcn_rcpf(e + 1.f);  // tanh
           }
@@ -512,6 +269,9 @@ __global__ __launch_bounds__(512, 1) void fa_fwd_pair_kernel(FwdArgs a) {
         for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[t][i]);
       mt = xor32_max(mt) * cexp;
       if (a.max_logit) mxl = fmaxf(mxl, qrow < T ? mt : -INFINITY);
+      // Lazy rescaling: the running max only moves (and O, l are rescaled)
+      // when some row's tile max exceeds it by more than kRescaleSlack, so
+      // p = 2^(s - m) stays below 2^kRescaleSlack; the branch is uniform.
       if (__any(mt > m + kRescaleSlack)) {
         const float mnew = fmaxf(m, mt);
         const float alpha = fast_exp2(m - mnew);
@@ -522,42 +282,56 @@ __global__ __launch_bounds__(512, 1) void fa_fwd_pair_kernel(FwdArgs a) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
       }
+      // P^T in bf16, 16 keys (one B operand) at a time: chunk c + 1 is
+      // computed under the MFMAs that consume chunk c.
+      bf16x8 pb[NP];
       float ps = 0.f;
+      auto pchunk = [&](int c, int e0, int e1) __attribute__((always_inline)) {
 #pragma unroll
-      for (int t = 0; t < NS; ++t)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float p = fast_exp2(fmaf(s[t][i], cexp, -m));
-          s[t][i] = p;
+        for (int e = e0; e < e1; ++e) {
+          const float p = fast_exp2(fmaf(s[c >> 1][8 * (c & 1) + e], cexp, -m));
+          s[c >> 1][8 * (c & 1) + e] = p;
           ps += p;
         }
+        if (e1 == 8) {
+          float tmp[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) tmp[e] = s[c >> 1][8 * (c & 1) + e];
+          pb[c] = pack_bf16(tmp);
+        }
+      };
+      pchunk(0, 0, 8);
+      constexpr int EPM = 8 / NDB > 0 ? 8 / NDB : 1;   // exponentials per MFMA
+      vq.run(fV, [&](int k) __attribute__((always_inline)) { return pb[k / NDB]; },
+             [&](int k) __attribute__((always_inline)) -> f32x16& { return oacc[k % NDB]; },
+             [&](int k) __attribute__((always_inline)) {
+               const int c = k / NDB + 1, part = k % NDB;
+               if (c < NP && part * EPM < 8) pchunk(c, part * EPM, min(8, part * EPM + EPM));
+             });
       lsum += ps;
-      bf16x8 pb[BKV / 16];
-#pragma unroll
-      for (int c16 = 0; c16 < BKV / 16; ++c16) {
-        float tmp[8];
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) tmp[jj] = s[c16 >> 1][8 * (c16 & 1) + jj];
-        pb[c16] = pack_bf16(tmp);
-      }
-#pragma unroll
-      for (int c16 = 0; c16 < BKV / 16; ++c16)
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-          oacc[db] = mfma32(lds_tr_operand<D>(Vt, 0, c16, HD * hf + 32 * db, lane), pb[c16],
-                            oacc[db]);
     }
-    if (more) wait_vmem();
-    __syncthreads();
+    // tile j + 1 complete before the barrier that publishes it.  The wait
+    // is unconditional (a no-op when nothing is in flight): behind a branch
+    // the compiler sees a path with a load still pending into the buffer
+    // the next step reads, and stalls that step's first read on it.
+    wait_tile(min(NSTG - 2, ntiles - j - 2));
+    lds_barrier();
   };
   int j = 0;
-  for (; j + 1 < ntiles; j += 2) {
+  for (; j + NSTG <= ntiles; j += NSTG) {
     step(I0{}, j);
     step(I1{}, j + 1);
+    if constexpr (NSTG >= 3) step(I2{}, j + 2);
+    if constexpr (NSTG >= 4) step(I3{}, j + 3);
   }
   if (j < ntiles) step(I0{}, j);
+  if constexpr (NSTG >= 3)
+    if (j + 1 < ntiles) step(I1{}, j + 1);
+  if constexpr (NSTG >= 4)
+    if (j + 2 < ntiles) step(I2{}, j + 2);
 
-  if (a.max_logit && hf == 0) {
+  if (a.max_logit) {
+    // largest logit of the wave's rows (natural log units), one atomic per wave
     float v = mxl;
 #pragma unroll
     for (int off = 1; off < 32; off <<= 1) v = fmaxf(v, __shfl_xor(v, off));
@@ -566,7 +340,7 @@ __global__ __launch_bounds__(512, 1) void fa_fwd_pair_kernel(FwdArgs a) {
   const float ltot = xor32_sum(lsum);
   if (qrow < T) {
     const float inv = 1.f / ltot;
-    bf16* Op = a.o + (bh * T + qrow) * D + HD * hf;
+    bf16* Op = a.o + (bh * T + qrow) * DV;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -576,7 +350,7 @@ __global__ __launch_bounds__(512, 1) void fa_fwd_pair_kernel(FwdArgs a) {
         for (int e = 0; e < 4; ++e) v[e] = (bf16)(oacc[db][4 * i4 + e] * inv);
         *(bf16x4*)(Op + 32 * db + 8 * i4 + 4 * g) = v;
       }
-    if (g == 0 && hf == 0) a.lse[bh * T + qrow] = (m + __log2f(ltot)) * kLn2;
+    if (g == 0) a.lse[bh * T + qrow] = (m + __log2f(ltot)) * kLn2;
   }
 }
 
@@ -597,11 +371,12 @@ __global__ __launch_bounds__(512, 1) void fa_fwd_pair_kernel(FwdArgs a) {
 template <int D, bool CAP>
 __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void fa_fwd_pipe_kernel(FwdArgs a) {
   constexpr int NW = 4, BQ = 32 * NW, BKV = 32;
-  constexpr int TILE = Lay<D>::template bytes<BKV>();
+  // a tile image, rounded up to whole rounds of the loaders' 1 KB pieces
+  constexpr int TILE = TileDma<D, BKV, NW>::IMG;
   constexpr int NC = D / 16;     // 16-wide chunks of the q.k contraction
   constexpr int NDB = D / 32;    // 32-wide blocks of the output
   constexpr int NO = 2 * NDB;    // MFMAs of the O^T block
-  constexpr int PD = 2;          // LDS operands issued this many MFMAs ahead
+  constexpr int PD = FWD_PIPE_PD; // LDS operands issued this many MFMAs ahead
   // head size 256: O (32 x 256 fp32 = 128 registers per lane) stays in the
   // AGPRs, beside q (64 VGPRs) and the working set in the VGPRs
   constexpr bool AGPR_O = D >= 256;
@@ -701,7 +476,7 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void fa_fwd_pipe_kernel(FwdA
 
   // the two score tiles (unit parity)
   f32x16 sa[2];
-  float mt = -INFINITY;        // running max of the unit being prepared
+  float mt = CAP ? INFINITY : -INFINITY;   // running max (cap: min r) of the unit being prepared
   float ps = 0.f;              // row sum of the unit being exponentiated
   bf16x8 pb[2];                // P of the current unit, bf16, per 16-key chunk
 
@@ -721,26 +496,33 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void fa_fwd_pipe_kernel(FwdA
   // visibility mask (branch-free, every unit) -- and their running max.
   // Element i of the tile is key kv0 + acc_row(i, g); it is visible iff
   // 0 <= qrow - key < span (span = W, or everything for a causal layer)
-  auto part_a = [&](auto x_c, int u, int e0, int e1) __attribute__((always_inline)) {
+  // With the cap the tile keeps r = 1 / (e^(2y) + 1) instead of tanh(y) =
+  // 1 - 2r: the "1 - 2r" folds into part B's exponent FMA, and the running
+  // max of tanh is the running min of r (masked keys: r = +inf).  Units that
+  // no row of the wave sees partially (MASK false) skip the mask.
+  auto part_a = [&](auto x_c, auto mask_c, int u, int e0, int e1) __attribute__((always_inline)) {
     constexpr int X = decltype(x_c)::value;
+    constexpr bool MASK = decltype(mask_c)::value;
     const int base = qrow - (t_lo + u) * BKV - 4 * g;   // qrow - key for acc_row(i, g) = 4g
 #pragma unroll
     for (int i = e0; i < e1; ++i) {
       float x = sa[X][i];
-      if (CAP) {
-        const float e = fast_exp2(x * a.two_scale_over_cap_log2e);
-        x = 1.f - 2.f * __builtin_amdgcn_rcpf(e + 1.f);   // tanh
+      if (CAP) x = __builtin_amdgcn_rcpf(fast_exp2(x * a.two_scale_over_cap_log2e) + 1.f);
+      if (MASK) {
+        const bool vis = (unsigned)(base - (8 * (i >> 2) + (i & 3))) < span;
+        x = vis ? x : (CAP ? INFINITY : -INFINITY);
       }
-      const bool vis = (unsigned)(base - (8 * (i >> 2) + (i & 3))) < span;
-      x = vis ? x : -INFINITY;
       sa[X][i] = x;
-      mt = fmaxf(mt, x);
+      mt = CAP ? fminf(mt, x) : fmaxf(mt, x);
     }
   };
   // the unit's max across the lane pair, then (after the O^T block that
   // precedes it) the lazy rescale of O and l
   auto a_tail = [&]() __attribute__((always_inline)) {
-    mt = xor32_max(mt) * cexp;
+    if (CAP)
+      mt = cexp - 2.f * cexp * xor32_min(mt);   // cexp * tanh at the row's min r
+    else
+      mt = xor32_max(mt) * cexp;
     if (a.max_logit) mxl = fmaxf(mxl, qrow < T ? mt : -INFINITY);
   };
   auto rescale = [&]() __attribute__((always_inline)) {
@@ -755,15 +537,17 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void fa_fwd_pipe_kernel(FwdA
 #pragma unroll
         for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
     }
-    mt = -INFINITY;
+    mt = CAP ? INFINITY : -INFINITY;
   };
   // softmax part B of the unit in tile X: p = 2^(s c - m) for elements
   // [e0, e1), row sum, bf16 packs of the 16-key chunks as they complete
   auto part_b = [&](auto x_c, int e0, int e1) __attribute__((always_inline)) {
     constexpr int X = decltype(x_c)::value;
+    // cap: c tanh - m = c (1 - 2r) - m
+    const float f_mul = CAP ? -2.f * cexp : cexp, f_add = CAP ? cexp - m : -m;
 #pragma unroll
     for (int i = e0; i < e1; ++i) {
-      const float p = fast_exp2(fmaf(sa[X][i], cexp, -m));
+      const float p = fast_exp2(fmaf(sa[X][i], f_mul, f_add));
       sa[X][i] = p;
       ps += p;
       if (i == 7 || i == 15) {
@@ -809,35 +593,46 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void fa_fwd_pipe_kernel(FwdA
   if (nu > 1) dm.load(Kp, T * D * 2, kbuf(I1{}), (t_lo + 1) * BKV, wave);
   wait_vmem();
   __syncthreads();
+  using MT = std::true_type;
+  using MF = std::false_type;
   s_block(I0{}, kbuf(I0{}), [&](int) {});
-  part_a(I0{}, 0, 0, 16);
+  part_a(I0{}, MT{}, 0, 0, 16);
   a_tail();
   rescale();
   __syncthreads();   // every wave is done with K(0) before K(2) replaces it
 
   // iteration i: tiles K(i+1) in kbuf[(i+1)&1], V(i) in vbuf[i&1]; score
   // tile of unit i in sa[i&1], of unit i+1 in sa[(i+1)&1]
-  auto step = [&](auto p_c, auto more_c, const int i) __attribute__((always_inline)) {
+  // MASK: some row of the wave sees only part of unit i + 1 (its part A
+  // evaluates the mask)
+  auto step = [&](auto p_c, auto more_c, auto mask_c, const int i) __attribute__((always_inline)) {
     constexpr int P = decltype(p_c)::value;
     constexpr bool more = decltype(more_c)::value;   // a unit i + 1 exists
     using PN = std::integral_constant<int, 1 - P>;
     lo.refresh();   // addresses formed per step, not hoisted for every buffer
-    if (i + 2 < nu) dm.load(Kp, T * D * 2, kbuf(p_c), (t_lo + i + 2) * BKV, wave);
-    if (more) dm.load(Vp, T * D * 2, vbuf(PN{}), (t_lo + i + 1) * BKV, wave);
     constexpr int EP = 16 / NC > 0 ? 16 / NC : 1;   // elements per S MFMA
     constexpr int EA = 16 / NO > 0 ? 16 / NO : 1;   // elements per O MFMA
+    constexpr int PER = TileDma<D, BKV, NW>::PER;
+    static_assert(2 * PER <= NC, "one load per S MFMA");
     if constexpr (more) {
-      // S(i+1) with P(i)'s exponentials under its MFMAs
+      // S(i+1) with P(i)'s exponentials under its MFMAs, and one load of
+      // K(i+2) or V(i+1) after each of the first 2 PER.  K(i+2) is loaded
+      // even past the last unit (rows past the end read as zeros): its
+      // buffer is then never read again.
       s_block(PN{}, kbuf(PN{}), [&](int k) __attribute__((always_inline)) {
         if (k * EP < 16) part_b(p_c, k * EP, k * EP + EP);
+        if (k < PER)
+          dm.load_piece(k, Kp, T * D * 2, kbuf(p_c), (t_lo + i + 2) * BKV, wave);
+        else if (k < 2 * PER)
+          dm.load_piece(k - PER, Vp, T * D * 2, vbuf(PN{}), (t_lo + i + 1) * BKV, wave);
       });
       if (16 / NC == 0) part_b(p_c, 0, 16);
       b_tail();
       // O^T += V(i)^T P(i)^T with S(i+1)'s cap, mask and max under its MFMAs
       o_block(vbuf(p_c), [&](int k) __attribute__((always_inline)) {
-        if (k * EA < 16) part_a(PN{}, i + 1, k * EA, k * EA + EA);
+        if (k * EA < 16) part_a(PN{}, mask_c, i + 1, k * EA, k * EA + EA);
       });
-      if (16 / NO == 0) part_a(PN{}, i + 1, 0, 16);
+      if (16 / NO == 0) part_a(PN{}, mask_c, i + 1, 0, 16);
       a_tail();
       rescale();
       wait_vmem();
@@ -850,17 +645,45 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void fa_fwd_pipe_kernel(FwdA
   };
   using T1 = std::true_type;
   using F1 = std::false_type;
+  // The units every row of the wave sees whole form one range [mlo, mhi):
+  // below it the window's first keys, above it the diagonal and the units
+  // past it.  Steps 0 .. nu-2 run in three segments -- mask, no mask, mask --
+  // so that the straight-line steps of the long middle segment carry no mask
+  // arithmetic; every wave still passes one barrier per step.
+  const int mhi = qw0 / BKV - t_lo;   // first unit holding a key past row qw0
+  // first unit whose keys are all above qw0 + 31 - W (every key counts when
+  // that bound is negative)
+  const int wlo = qw0 + 31 - W;
+  const int mlo = (W > 0 && wlo >= 0) ? max(0, wlo / BKV + 1 - t_lo) : 0;
+  const int ia = min(max(mlo - 1, 0), nu - 1);
+  const int ib = min(max(mhi - 1, ia), nu - 1);
+  // steps [i, iend) with the buffer parity of each step index
+  auto run = [&](auto mask_c, int& i, const int iend) __attribute__((always_inline)) {
+    if (i < iend && (i & 1)) {
+      step(I1{}, T1{}, mask_c, i);
+      ++i;
+    }
+    for (; i + 2 <= iend; i += 2) {
+      step(I0{}, T1{}, mask_c, i);
+      step(I1{}, T1{}, mask_c, i + 1);
+    }
+    if (i < iend) {
+      step(I0{}, T1{}, mask_c, i);
+      ++i;
+    }
+  };
   int i = 0;
-  for (; i + 2 < nu; i += 2) {
-    step(I0{}, T1{}, i);
-    step(I1{}, T1{}, i + 1);
+  for (int seg = 0; seg < 3; ++seg) {
+    const int iend = seg == 0 ? ia : seg == 1 ? ib : nu - 1;
+    if (seg == 1)
+      run(MF{}, i, iend);
+    else
+      run(MT{}, i, iend);
   }
-  if (i + 2 == nu) {
-    step(I0{}, T1{}, i);
-    step(I1{}, F1{}, i + 1);
-  } else {
-    step(I0{}, F1{}, i);
-  }
+  if ((nu - 1) & 1)
+    step(I1{}, F1{}, MT{}, nu - 1);
+  else
+    step(I0{}, F1{}, MT{}, nu - 1);
 
   if (a.max_logit) {
     float v = mxl;
@@ -886,49 +709,26 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void fa_fwd_pipe_kernel(FwdA
   }
 }
 
-// Tile shapes per head size (keys per tile, waves, query blocks per wave),
+// Tile shapes per head size (keys per tile, waves, K/V tiles in flight),
 // chosen by measurement on MI355X.
 #ifndef FWD128_CFG
-#define FWD128_CFG 64, 4, 1
+#define FWD128_CFG 64, 4
 #endif
 
 #ifndef FWD192_CFG
-#define FWD192_CFG 32, 4, 1
+#define FWD192_CFG 32, 4
 #endif
 
-template <int DK, int DV, int BKV, int NW, int QW>
+template <int DK, int DV, int BKV, int NW, int NSTG = 2, int MINWG = 0>
 static hipError_t launch_fwd_d(const FwdArgs& a, hipStream_t stream) {
-  const int nqb = (a.T + 32 * NW * QW - 1) / (32 * NW * QW);
+  const int nqb = (a.T + 32 * NW - 1) / (32 * NW);
   const dim3 grid((unsigned)nqb * a.B * a.H);
   if (a.cap_log2e > 0.f)
-    hipLaunchKernelGGL((fa_fwd_kernel<DK, DV, BKV, NW, QW, true>), grid, dim3(64 * NW), 0, stream, a);
+    hipLaunchKernelGGL((fa_fwd_kernel<DK, DV, BKV, NW, true, NSTG, MINWG>), grid, dim3(64 * NW), 0, stream,
+                       a);
   else
-    hipLaunchKernelGGL((fa_fwd_kernel<DK, DV, BKV, NW, QW, false>), grid, dim3(64 * NW), 0, stream, a);
-  stage_mark(stream);
-  return hipGetLastError();
-}
-
-#ifndef FWD256_BKV
-#define FWD256_BKV 32
-#endif
-// d = 256 forward: paired waves (two per SIMD, each holding half of d), or
-// the one-wave-per-row kernel at one wave per SIMD (FWD256_CFG shape)
-#ifndef FWD256_PAIR
-#define FWD256_PAIR 1
-#endif
-#ifndef FWD256_CFG
-#define FWD256_CFG 64, 4, 1
-#endif
-
-template <int D, int BKV>
-static hipError_t launch_fwd_pair(const FwdArgs& a, hipStream_t stream) {
-  constexpr int BQ = 128;   // 4 pairs x 32 query rows
-  const int nqb = (a.T + BQ - 1) / BQ;
-  const dim3 grid((unsigned)nqb * a.B * a.H);
-  if (a.cap_log2e > 0.f)
-    hipLaunchKernelGGL((fa_fwd_pair_kernel<D, BKV, true>), grid, dim3(512), 0, stream, a);
-  else
-    hipLaunchKernelGGL((fa_fwd_pair_kernel<D, BKV, false>), grid, dim3(512), 0, stream, a);
+    hipLaunchKernelGGL((fa_fwd_kernel<DK, DV, BKV, NW, false, NSTG, MINWG>), grid, dim3(64 * NW), 0, stream,
+                       a);
   stage_mark(stream);
   return hipGetLastError();
 }
@@ -945,15 +745,6 @@ static hipError_t launch_fwd_pipe(const FwdArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// forward kernel per head size: 0 the one-tile kernel (fa_fwd_kernel, or the
-// paired kernel at d = 256), 1 the software-pipelined kernel
-#ifndef FWD128_PIPE
-#define FWD128_PIPE 0
-#endif
-#ifndef FWD256_PIPE
-#define FWD256_PIPE 1
-#endif
-
 __global__ void fill_f32_kernel(float* p, int n, float v) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = v;
@@ -967,21 +758,12 @@ hipError_t launch_fill_f32(float* p, int n, float v, hipStream_t stream) {
 hipError_t launch_fwd_bf16(const FwdArgs& a, int d, int d_v, hipStream_t stream) {
   if (d == d_v) {
     switch (d) {
-      case 64: return launch_fwd_d<64, 64, 64, 4, 1>(a, stream);
-      case 128:
-#if FWD128_PIPE
-        return launch_fwd_pipe<128>(a, stream);
-#else
-        return launch_fwd_d<128, 128, FWD128_CFG>(a, stream);
-#endif
-      case 256:
-#if FWD256_PIPE
-        return launch_fwd_pipe<256>(a, stream);
-#elif FWD256_PAIR
-        return launch_fwd_pair<256, FWD256_BKV>(a, stream);
-#else
-        return launch_fwd_d<256, 256, FWD256_CFG>(a, stream);
-#endif
+      case 64: return launch_fwd_d<64, 64, 64, 4>(a, stream);
+      case 128: return launch_fwd_d<128, 128, FWD128_CFG>(a, stream);
+      // one wave cannot hold q, the 256-wide O accumulator and a tile of
+      // scores at two waves per SIMD: the software-pipelined kernel keeps
+      // the matrix unit busy at one
+      case 256: return launch_fwd_pipe<256>(a, stream);
     }
   } else if (d == 192 && d_v == 128) {
     return launch_fwd_d<192, 128, FWD192_CFG>(a, stream);
