@@ -368,8 +368,15 @@ __global__ __launch_bounds__(64 * NW, (MINWG > 0 ? MINWG : DK >= 256 ? 1 : 8 / N
 // double-buffered, one barrier per unit.  Head size 256 runs one wave per
 // SIMD (the 32 x 256 accumulator lives in the accumulation registers, q in
 // 64 VGPRs); head size 128 fits two.
-template <int D, bool CAP>
+//
+// With the cap every logit lies in [-cap, cap], so the softmax needs no
+// running max: the reference m = cap log2(e) - 64 keeps every p = 2^(s - m)
+// in [2^-80, 2^64], inside the normal range of fp32 and bf16 (a sink above
+// that reference becomes the reference).  The cap path therefore never
+// rescales, and tracks the max only for the max-logit output (MAXL).
+template <int D, bool CAP, bool MAXL>
 __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void fa_fwd_pipe_kernel(FwdArgs a) {
+  constexpr bool TRACK = !CAP || MAXL;   // the unit max is computed
   constexpr int NW = 4, BQ = 32 * NW, BKV = 32;
   // a tile image, rounded up to whole rounds of the loaders' 1 KB pieces
   constexpr int TILE = TileDma<D, BKV, NW>::IMG;
@@ -449,10 +456,16 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void fa_fwd_pipe_kernel(FwdA
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
-  float m = has_sink ? sink2 : kMaxInit;
-  float lsum = (has_sink && g == 0) ? 1.f : 0.f;
-  float mxl = -INFINITY;
   const float cexp = CAP ? a.cap_log2e : a.scale_log2e;
+  float m, lsum;
+  if (CAP) {
+    m = has_sink ? fmaxf(cexp - 64.f, sink2) : cexp - 64.f;
+    lsum = (has_sink && g == 0) ? fast_exp2(sink2 - m) : 0.f;
+  } else {
+    m = has_sink ? sink2 : kMaxInit;
+    lsum = (has_sink && g == 0) ? 1.f : 0.f;
+  }
+  float mxl = -INFINITY;
 
   TileDma<D, BKV, NW> dm;
   dm.init(wave, lane);
@@ -513,12 +526,13 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void fa_fwd_pipe_kernel(FwdA
         x = vis ? x : (CAP ? INFINITY : -INFINITY);
       }
       sa[X][i] = x;
-      mt = CAP ? fminf(mt, x) : fmaxf(mt, x);
+      if (TRACK) mt = CAP ? fminf(mt, x) : fmaxf(mt, x);
     }
   };
   // the unit's max across the lane pair, then (after the O^T block that
   // precedes it) the lazy rescale of O and l
   auto a_tail = [&]() __attribute__((always_inline)) {
+    if (!TRACK) return;
     if (CAP)
       mt = cexp - 2.f * cexp * xor32_min(mt);   // cexp * tanh at the row's min r
     else
@@ -526,6 +540,10 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void fa_fwd_pipe_kernel(FwdA
     if (a.max_logit) mxl = fmaxf(mxl, qrow < T ? mt : -INFINITY);
   };
   auto rescale = [&]() __attribute__((always_inline)) {
+    if (CAP) {   // fixed reference: nothing to rescale
+      mt = INFINITY;
+      return;
+    }
     if (__any(mt > m + kRescaleSlack)) {
       if constexpr (AGPR_O) agpr_acc_fence(oacc);
       const float mnew = fmaxf(m, mt);
@@ -737,10 +755,14 @@ template <int D>
 static hipError_t launch_fwd_pipe(const FwdArgs& a, hipStream_t stream) {
   const int nqb = (a.T + 127) / 128;
   const dim3 grid((unsigned)nqb * a.B * a.H);
-  if (a.cap_log2e > 0.f)
-    hipLaunchKernelGGL((fa_fwd_pipe_kernel<D, true>), grid, dim3(256), 0, stream, a);
-  else
-    hipLaunchKernelGGL((fa_fwd_pipe_kernel<D, false>), grid, dim3(256), 0, stream, a);
+  if (a.cap_log2e > 0.f) {
+    if (a.max_logit)
+      hipLaunchKernelGGL((fa_fwd_pipe_kernel<D, true, true>), grid, dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL((fa_fwd_pipe_kernel<D, true, false>), grid, dim3(256), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL((fa_fwd_pipe_kernel<D, false, true>), grid, dim3(256), 0, stream, a);
+  }
   stage_mark(stream);
   return hipGetLastError();
 }
