@@ -17,8 +17,8 @@
 //      per-lane scalars; dQ^T += K^T dS^T reads K^T through the LDS
 //      transpose read.  It also computes D_i for its rows (the backward
 //      prologue) and writes it to a [B, H, T] fp32 scratch for the dK/dV
-//      pass.  At d = 256 fa_bwd_dq_pair_kernel splits each row over two
-//      waves.
+//      pass.  At d = 256 fa_bwd_dq_pipe_kernel runs one software-pipelined
+//      wave per 32 rows.
 //   2. fa_bwd_dkdv_pair_kernel -- key-parallel: a workgroup owns 128 key
 //      rows (64 at d = 256) of one (b, kv head) and loops over the query
 //      heads of the GQA group and over the query tiles that can see its
@@ -35,27 +35,14 @@
 
 namespace fa {
 
-// LDS layout of the tile buffers per pass (0 dQ, 1 dV, 2 dK): one LDS object
-// per buffer, or one array.  With one array the compiler makes the
-// transposed LDS reads wait for every outstanding direct load; that costs
-// overlap but also bounds how far it moves work, and so its register use.
-// Chosen by measurement.
-#ifndef BWD_LDS_SEP
-#define BWD_LDS_SEP(DK, PASS) ((PASS) == 1 && (DK) != 192)
-#endif
-// loop unrolled by two (buffers chosen at compile time), or the buffer
-// picked at run time in the one array (fewer registers at d = 192)
+// dQ pass: the K and V tiles of both buffers live in one LDS array (the
+// compiler then makes the transposed LDS reads wait for every outstanding
+// direct load; that costs overlap but also bounds how far it moves work,
+// and so its register use -- chosen by measurement).  Its loop is unrolled
+// by two (buffers chosen at compile time), or at d = 192 the buffer is
+// picked at run time (fewer registers).
 #ifndef BWD_UNROLL
 #define BWD_UNROLL(DK) ((DK) != 192)
-#endif
-
-// 1: the dQ pass computes dS chunk by chunk between the MFMAs of
-// dQ^T += K^T dS^T (the VALU of chunk c + 1 under the MFMAs of chunk c);
-// 2 (32-key tiles): in addition S is computed before dP, and P under the
-// MFMAs of dP, so that only P (dP - D) is left for the product's MFMAs;
-// 0: all of dS first, then the product.
-#ifndef DQ_SPLIT
-#define DQ_SPLIT 2
 #endif
 
 #ifndef BWD_LDS_PD
@@ -86,15 +73,9 @@ __global__ __launch_bounds__(64 * NW, (DK >= 192 ? 1 : 8 / NW)) void fa_bwd_dq_k
   constexpr int TILE_V = Lay<DV>::template bytes<BKV>();
   constexpr int NDB = DK / 32;   // 32-wide blocks of dq
   constexpr int NS = BKV / 32;
-  // K, V tiles double-buffered (see BWD_LDS_SEP / BWD_UNROLL)
-  constexpr bool SEP = BWD_LDS_SEP(DK, 0);
+  // K, V tiles double-buffered in one array (see BWD_UNROLL)
   constexpr bool UNROLL = BWD_UNROLL(DK);
-  static_assert(UNROLL || !SEP, "run-time buffer choice needs the one-array layout");
-  __shared__ __attribute__((aligned(1024))) char one[SEP ? 16 : 2 * (TILE_K + TILE_V)];
-  __shared__ __attribute__((aligned(1024))) char kb0[SEP ? TILE_K : 16];
-  __shared__ __attribute__((aligned(1024))) char kb1[SEP ? TILE_K : 16];
-  __shared__ __attribute__((aligned(1024))) char vb0[SEP ? TILE_V : 16];
-  __shared__ __attribute__((aligned(1024))) char vb1[SEP ? TILE_V : 16];
+  __shared__ __attribute__((aligned(1024))) char one[2 * (TILE_K + TILE_V)];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -167,14 +148,10 @@ __global__ __launch_bounds__(64 * NW, (DK >= 192 ? 1 : 8 / NW)) void fa_bwd_dq_k
   kdm.init(wave, lane);
   vdm.init(wave, lane);
   auto kbuf = [&](auto b_c) -> LDS_AS char* {
-    constexpr int b = decltype(b_c)::value;
-    if constexpr (!SEP) return (LDS_AS char*)one + b * TILE_K;
-    return b == 0 ? (LDS_AS char*)kb0 : (LDS_AS char*)kb1;
+    return (LDS_AS char*)one + decltype(b_c)::value * TILE_K;
   };
   auto vbuf = [&](auto b_c) -> LDS_AS char* {
-    constexpr int b = decltype(b_c)::value;
-    if constexpr (!SEP) return (LDS_AS char*)one + 2 * TILE_K + b * TILE_V;
-    return b == 0 ? (LDS_AS char*)vb0 : (LDS_AS char*)vb1;
+    return (LDS_AS char*)one + 2 * TILE_K + decltype(b_c)::value * TILE_V;
   };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
@@ -198,7 +175,7 @@ __global__ __launch_bounds__(64 * NW, (DK >= 192 ? 1 : 8 / NW)) void fa_bwd_dq_k
         for (int jj = 0; jj < 8; ++jj) tmp[jj] = s[c16 >> 1][8 * (c16 & 1) + jj];
         return pack_bf16(tmp);
       };
-      if constexpr (DQ_SPLIT == 2 && NS == 1 && BWD_LDS_PD(DK) > 0 && 16 % (DV / 16) == 0) {
+      if constexpr (NS == 1 && BWD_LDS_PD(DK) > 0 && 16 % (DV / 16) == 0) {
         // S first, then dP with P = 2^(...) computed under its MFMAs; dS =
         // P (dP - D) chunk by chunk under the dQ product's MFMAs.
         if (empty) return;
@@ -268,7 +245,7 @@ __global__ __launch_bounds__(64 * NW, (DK >= 192 ? 1 : 8 / NW)) void fa_bwd_dq_k
         if (CAP) ds *= 1.f - th * th;
         s[t][i] = ds;
       };
-      if constexpr (DQ_SPLIT && BWD_LDS_PD(DK) > 0 && 8 % NDB == 0) {
+      if constexpr (BWD_LDS_PD(DK) > 0 && 8 % NDB == 0) {
         if (!empty) {
           if (!full) {
             // invisible pairs: S = -inf gives p = 0 without a cap; with one,
@@ -381,234 +358,6 @@ __global__ __launch_bounds__(64 * NW, (DK >= 192 ? 1 : 8 / NW)) void fa_bwd_dq_k
           // the negative angle
           const float4 r = *(const float4*)(a.rope_cs + (size_t)qrow * DK +
                                             2 * (16 * db + 4 * i4 + 2 * g));
-          rope_pair(r.x, -r.y, x[0], x[1]);
-          rope_pair(r.z, -r.w, x[2], x[3]);
-        }
-        bf16x4 v;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = (bf16)x[e];
-        *(bf16x4*)(Qd + 32 * db + 8 * i4 + 4 * g) = v;
-      }
-  }
-}
-
-// Head size 256, dQ pass: as the forward's paired kernel, waves work in
-// pairs on the same 32 query rows.  Wave half hf holds q and dO over columns
-// 128 hf .. +127, computes the partial S^T and dP^T over its half of d, and
-// owns dq columns 128 hf .. +127; the pair swaps its partial S^T and dP^T
-// (and once, its partial D_i) through LDS and both add them in the same
-// order, so dS is identical in both waves.  Two waves per SIMD without
-// spilling, where the single-wave kernel needs ~490 registers.
-template <int D, int BKV, bool CAP>
-__global__ __launch_bounds__(512, 1) void fa_bwd_dq_pair_kernel(BwdArgs a) {
-  constexpr int NW = 8, NT = 64 * NW;
-  constexpr int HD = D / 2;
-  constexpr int BQ = 32 * NW / 2;
-  constexpr int TILE = Lay<D>::template bytes<BKV>();
-  constexpr int NDB = HD / 32;
-  constexpr int NS = BKV / 32;
-  constexpr int NC = HD / 16;
-  constexpr int XS = 2 * NS * 16 * 64 * 4;   // one wave's partial S^T and dP^T
-  // K, V buffers as separate LDS objects (direct loads into one, reads from
-  // the other), the partial-product exchange area
-  __shared__ __attribute__((aligned(1024))) char kb0[TILE];
-  __shared__ __attribute__((aligned(1024))) char kb1[TILE];
-  __shared__ __attribute__((aligned(1024))) char vb0[TILE];
-  __shared__ __attribute__((aligned(1024))) char vb1[TILE];
-  __shared__ __attribute__((aligned(1024))) char xsm[NW * XS];
-  LDS_AS float* xsb = (LDS_AS float*)xsm;
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int pair = wave >> 1;
-  const int hf = wave & 1;
-  const int g = lane >> 5;
-  const int l32 = lane & 31;
-  const int T = a.T;
-  const int W = a.window;
-  const int G = a.H / a.Hkv;
-  const int nqb = (T + BQ - 1) / BQ;
-  const WorkItem w = decode_work(blockIdx.x, nqb, a.B, a.Hkv, G, true);
-  const int h = w.hkv * G + w.r;
-  const int q0 = w.blk * BQ;
-  const int qw0 = q0 + 32 * pair;
-  const int qrow = qw0 + l32;
-  const int qr = qrow < T ? qrow : T - 1;
-  const size_t bh = (size_t)w.b * a.H + h;
-  const size_t bkv = (size_t)w.b * a.Hkv + w.hkv;
-  const bf16* Kp = a.k + bkv * T * D;
-  const bf16* Vp = a.v + bkv * T * D;
-  LDS_AS float* const xs_mine = xsb + wave * (XS / 4);
-  const LDS_AS float* const xs_peer = xsb + (wave ^ 1) * (XS / 4);
-
-  // this wave's half of the q and dO rows; partial D_i over that half
-  bf16x8 qreg[NC], doreg[NC];
-  float Di;
-  {
-    const size_t roff = (bh * T + qr) * D + HD * hf + 8 * g;
-    const bf16x8* qs = (const bf16x8*)(a.q + roff);
-    const bf16x8* ds = (const bf16x8*)(a.dO + roff);
-    const bf16x8* os = (const bf16x8*)(a.o + roff);
-    float part = 0.f;
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      qreg[c] = qs[2 * c];
-      doreg[c] = ds[2 * c];
-      const bf16x8 ov = os[2 * c];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) part += (float)doreg[c][j] * (float)ov[j];
-    }
-    part = xor32_sum(part);
-    xs_mine[lane] = part;
-    __syncthreads();
-    const float peer = xs_peer[lane];
-    Di = hf == 0 ? part + peer : peer + part;
-    if (hf == 0 && g == 0 && qrow < T) a.Dst[bh * T + qrow] = Di;
-  }
-  const float lse2 = a.lse[bh * T + qr] * kLog2e;
-  if (a.sinks && hf == 0) {
-    float c = (g == 0 && qrow < T) ? fast_exp2(a.sinks[h] * kLog2e - lse2) * Di : 0.f;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) c += __shfl_xor(c, off);
-    if (lane == 0) atomicAdd(a.dsinks + h, -c);
-  }
-
-  int kv_lo = 0;
-  if (W > 0) kv_lo = max(0, q0 - W + 1);
-  const int t_lo = kv_lo / BKV;
-  const int kv_hi = min(T, q0 + BQ);
-  const int ntiles = (kv_hi + BKV - 1) / BKV - t_lo;
-
-  f32x16 dqacc[NDB];
-#pragma unroll
-  for (int db = 0; db < NDB; ++db)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) dqacc[db][i] = 0.f;
-
-  TileDma<D, BKV, NW> kdm, vdm;
-  kdm.init(wave, lane);
-  vdm.init(wave, lane);
-  auto kbuf = [&](auto p_c) -> LDS_AS char* {
-    return decltype(p_c)::value ? (LDS_AS char*)kb1 : (LDS_AS char*)kb0;
-  };
-  auto vbuf = [&](auto p_c) -> LDS_AS char* {
-    return decltype(p_c)::value ? (LDS_AS char*)vb1 : (LDS_AS char*)vb0;
-  };
-  using I0 = std::integral_constant<int, 0>;
-  using I1 = std::integral_constant<int, 1>;
-  kdm.load(Kp, T * D * 2, kbuf(I0{}), t_lo * BKV, wave);
-  vdm.load(Vp, T * D * 2, vbuf(I0{}), t_lo * BKV, wave);
-  wait_vmem();
-  __syncthreads();
-
-  const int qa = qw0, qb = qw0 + 31;
-  // one iteration on the tile in buffer P (unrolled by two)
-  auto step = [&](auto p_c, const int j) __attribute__((always_inline)) {
-    constexpr int P = decltype(p_c)::value;
-    using PN = std::integral_constant<int, 1 - P>;
-    const LDS_AS char* Kt = kbuf(p_c);
-    const LDS_AS char* Vt = vbuf(p_c);
-    const bool more = j + 1 < ntiles;
-    if (more) {
-      kdm.load(Kp, T * D * 2, kbuf(PN{}), (t_lo + j + 1) * BKV, wave);
-      vdm.load(Vp, T * D * 2, vbuf(PN{}), (t_lo + j + 1) * BKV, wave);
-    }
-    const int kv0 = (t_lo + j) * BKV;
-    const bool empty = qa >= T || kv0 > qb || (W > 0 && kv0 + BKV - 1 <= qa - W);
-    const bool full = kv0 + BKV - 1 <= qa && (W == 0 || kv0 > qb - W);
-    f32x16 s[NS], dp[NS];
-    if (!empty) {
-      // partial S^T = K Q^T and dP^T = V dO^T over this wave's half of d
-#pragma unroll
-      for (int t = 0; t < NS; ++t)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          s[t][i] = 0.f;
-          dp[t][i] = 0.f;
-        }
-#pragma unroll
-      for (int c = 0; c < NC; ++c)
-#pragma unroll
-        for (int t = 0; t < NS; ++t) {
-          s[t] = mfma32(lds_row_operand<D>(Kt, 32 * t, NC * hf + c, lane), qreg[c], s[t]);
-          dp[t] = mfma32(lds_row_operand<D>(Vt, 32 * t, NC * hf + c, lane), doreg[c], dp[t]);
-        }
-      // lane-major 16-byte groups: element i of array x at ((x*4 + i/4)*64 + lane)*4 + i%4
-#pragma unroll
-      for (int t = 0; t < NS; ++t)
-#pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          *(LDS_AS f32x4*)(xs_mine + (((2 * t) * 4 + i4) * 64 + lane) * 4) =
-              f32x4{s[t][4 * i4], s[t][4 * i4 + 1], s[t][4 * i4 + 2], s[t][4 * i4 + 3]};
-          *(LDS_AS f32x4*)(xs_mine + (((2 * t + 1) * 4 + i4) * 64 + lane) * 4) =
-              f32x4{dp[t][4 * i4], dp[t][4 * i4 + 1], dp[t][4 * i4 + 2], dp[t][4 * i4 + 3]};
-        }
-    }
-    __syncthreads();
-    if (!empty) {
-#pragma unroll
-      for (int t = 0; t < NS; ++t)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float ps = xs_peer[(((2 * t) * 4 + i / 4) * 64 + lane) * 4 + i % 4];
-          const float pd = xs_peer[(((2 * t + 1) * 4 + i / 4) * 64 + lane) * 4 + i % 4];
-          const float sv = hf == 0 ? s[t][i] + ps : ps + s[t][i];
-          const float dv = hf == 0 ? dp[t][i] + pd : pd + dp[t][i];
-          float th;
-          const float p = fast_exp2(p_arg<CAP>(sv, a, lse2, th));
-          float ds = p * (dv - Di);
-          if (CAP) ds *= 1.f - th * th;
-          s[t][i] = ds;
-        }
-      if (!full) {
-#pragma unroll
-        for (int t = 0; t < NS; ++t)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int kv = kv0 + 32 * t + acc_row(i, g);
-            const bool vis = (kv <= qrow) & ((W == 0) | (kv > qrow - W));
-            s[t][i] = vis ? s[t][i] : 0.f;
-          }
-      }
-      bf16x8 dsb[BKV / 16];
-#pragma unroll
-      for (int c16 = 0; c16 < BKV / 16; ++c16) {
-        float tmp[8];
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) tmp[jj] = s[c16 >> 1][8 * (c16 & 1) + jj];
-        dsb[c16] = pack_bf16(tmp);
-      }
-#pragma unroll
-      for (int c16 = 0; c16 < BKV / 16; ++c16)
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-          dqacc[db] = mfma32(lds_tr_operand<D>(Kt, 0, c16, HD * hf + 32 * db, lane), dsb[c16],
-                             dqacc[db]);
-    }
-    if (more) wait_vmem();
-    __syncthreads();
-  };
-  int j = 0;
-  for (; j + 1 < ntiles; j += 2) {
-    step(I0{}, j);
-    step(I1{}, j + 1);
-  }
-  if (j < ntiles) step(I0{}, j);
-
-  if (qrow < T) {
-    bf16* Qd = a.dq + (bh * T + qrow) * D + HD * hf;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        float x[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) x[e] = dqacc[db][4 * i4 + e] * a.scale;
-        if (a.rope_cs) {
-          // pairs 16 (NDB hf + db) + 4 i4 + 2 g + {0, 1} of the full row
-          const float4 r = *(const float4*)(a.rope_cs + (size_t)qrow * D +
-                                            2 * (16 * (NDB * hf + db) + 4 * i4 + 2 * g));
           rope_pair(r.x, -r.y, x[0], x[1]);
           rope_pair(r.z, -r.w, x[2], x[3]);
         }
@@ -877,284 +626,6 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_dq_pipe_kernel(BwdArgs a) {
 }
 
 // ----------------------------------------------------------------- dK/dV pass
-// The two-launch alternative to the fused pass below (built when
-// BWD_KV_PAIR or its per-size switches are 0, for comparison).  MODE 0
-// accumulates dK and dV together; both accumulators (2 x D/2 registers per
-// lane) beside K, V and the tiles exceed the 256 registers that two waves
-// per SIMD allow, so the pass runs as two launches instead: MODE 1
-// accumulates dV only (needs S, P), MODE 2 dK only (needs S, dP, dS) --
-// one extra S = Q K^T product buys twice the occupancy.
-template <int DK, int DV, int BQB, int NW, bool CAP, int MODE>
-__global__ __launch_bounds__(64 * NW, (DK >= 192 ? 1 : 8 / NW)) void fa_bwd_dkdv_kernel(BwdArgs a) {
-  constexpr bool DO_DV = MODE != 2;
-  constexpr bool DO_DK = MODE != 1;
-  constexpr int NT = 64 * NW;
-  constexpr int BKVB = 32 * NW;        // key rows per workgroup
-  constexpr int TILE_Q = Lay<DK>::template bytes<BQB>();  // one Q tile
-  constexpr int TILE_O = Lay<DV>::template bytes<BQB>();  // one dO tile
-  constexpr int NDBK = DK / 32;        // 32-wide blocks of dk
-  constexpr int NDBV = DV / 32;        // 32-wide blocks of dv
-  constexpr int NS = BQB / 32;         // 32-query sub-tiles
-  constexpr int STAT = BQB * 4;        // bytes of one lse or D tile
-  // Q, dO tiles double-buffered (see BWD_LDS_SEP / BWD_UNROLL), row
-  // statistics double-buffered beside them
-  constexpr bool SEP = BWD_LDS_SEP(DK, MODE);
-  constexpr bool UNROLL = BWD_UNROLL(DK);
-  static_assert(UNROLL || !SEP, "run-time buffer choice needs the one-array layout");
-  __shared__ __attribute__((aligned(1024))) char one[SEP ? 16 : 2 * (TILE_Q + TILE_O)];
-  __shared__ __attribute__((aligned(1024))) char qb0[SEP ? TILE_Q : 16];
-  __shared__ __attribute__((aligned(1024))) char qb1[SEP ? TILE_Q : 16];
-  __shared__ __attribute__((aligned(1024))) char ob0[SEP ? TILE_O : 16];
-  __shared__ __attribute__((aligned(1024))) char ob1[SEP ? TILE_O : 16];
-  __shared__ __attribute__((aligned(16))) char sbuf[4 * STAT];
-  LDS_AS char* stat = (LDS_AS char*)sbuf;  // [buf][lse2 | D][BQB] fp32
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int g = lane >> 5;
-  const int l32 = lane & 31;
-  const int T = a.T;
-  const int W = a.window;
-  const int G = a.H / a.Hkv;
-  const int nkb = (T + BKVB - 1) / BKVB;
-  const WorkItem w = decode_work(blockIdx.x, nkb, a.B, a.Hkv, 1, false);
-  const int k0 = w.blk * BKVB;
-  const int kw0 = k0 + 32 * wave;
-  const int krow = kw0 + l32;
-  const int kr = krow < T ? krow : T - 1;
-  const size_t bkv = (size_t)w.b * a.Hkv + w.hkv;
-
-  bf16x8 kreg[DK / 16], vreg[DV / 16];
-  {
-    const bf16x8* ks = (const bf16x8*)(a.k + (bkv * T + kr) * DK + 8 * g);
-    const bf16x8* vs = (const bf16x8*)(a.v + (bkv * T + kr) * DV + 8 * g);
-#pragma unroll
-    for (int c = 0; c < DK / 16; ++c) kreg[c] = ks[2 * c];
-    if (DO_DK) {
-#pragma unroll
-      for (int c = 0; c < DV / 16; ++c) vreg[c] = vs[2 * c];
-    }
-  }
-
-  // Query tiles that can see keys [k0, k0 + BKVB).
-  const int qt_lo = k0 / BQB;
-  const int q_hi = W > 0 ? min(T, k0 + BKVB - 1 + W) : T;
-  const int nqt = (q_hi + BQB - 1) / BQB - qt_lo;
-  const int niter = G * nqt;
-
-  f32x16 dkacc[DO_DK ? NDBK : 1], dvacc[DO_DV ? NDBV : 1];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-#pragma unroll
-    for (int db = 0; db < (DO_DK ? NDBK : 1); ++db) dkacc[db][i] = 0.f;
-#pragma unroll
-    for (int db = 0; db < (DO_DV ? NDBV : 1); ++db) dvacc[db][i] = 0.f;
-  }
-
-  // Iteration it visits query head (hkv*G + hi) and query tile ti, with
-  // it = hi * nqt + ti; (hi, ti) advance incrementally (no integer division
-  // in the loop).
-  auto stage_stats = [&](int hi, int ti) -> float {
-    const int hh = w.hkv * G + hi;
-    const int q0 = (qt_lo + ti) * BQB;
-    const size_t bhh = (size_t)w.b * a.H + hh;
-    float v = 0.f;
-    if (tid < 2 * BQB) {
-      // one load, raw (the lse is scaled when it is stored to LDS): a use
-      // here would make these waves wait for the load at once
-      int qq = q0 + (tid % BQB);
-      qq = qq < T ? qq : T - 1;
-      v = (tid < BQB ? a.lse : a.Dst)[bhh * T + qq];
-    }
-    return v;
-  };
-  // lse (log2 units) or D, as stored in the LDS statistics tile
-  auto stat_val = [&](float v) { return tid < BQB ? v * kLog2e : v; };
-  auto tile_src = [&](int hi, const bf16* base, int dd) {
-    return base + ((size_t)w.b * a.H + w.hkv * G + hi) * T * dd;
-  };
-  auto tile_q0 = [&](int ti) { return (qt_lo + ti) * BQB; };
-  auto advance = [&](int& hi, int& ti) {
-    if (++ti == nqt) {
-      ti = 0;
-      ++hi;
-    }
-  };
-  // Q and dO tiles go straight from HBM into the idle LDS buffer (no
-  // staging registers), the row statistics through one register: issued at
-  // the top of an iteration, waited for before its closing barrier.
-  TileDma<DK, BQB, NW> qdm;
-  TileDma<DV, BQB, NW> odm;
-  qdm.init(wave, lane);
-  odm.init(wave, lane);
-  auto qbuf = [&](auto b_c) -> LDS_AS char* {
-    constexpr int b = decltype(b_c)::value;
-    if constexpr (!SEP) return (LDS_AS char*)one + b * TILE_Q;
-    return b == 0 ? (LDS_AS char*)qb0 : (LDS_AS char*)qb1;
-  };
-  auto obuf = [&](auto b_c) -> LDS_AS char* {
-    constexpr int b = decltype(b_c)::value;
-    if constexpr (!SEP) return (LDS_AS char*)one + 2 * TILE_Q + b * TILE_O;
-    return b == 0 ? (LDS_AS char*)ob0 : (LDS_AS char*)ob1;
-  };
-  auto issue = [&](LDS_AS char* qdst, LDS_AS char* odst, int hi, int ti)
-                   __attribute__((always_inline)) -> float {
-    const float v = stage_stats(hi, ti);
-    qdm.load(tile_src(hi, a.q, DK), T * DK * 2, qdst, tile_q0(ti), wave);
-    odm.load(tile_src(hi, a.dO, DV), T * DV * 2, odst, tile_q0(ti), wave);
-    return v;
-  };
-  using I0 = std::integral_constant<int, 0>;
-  using I1 = std::integral_constant<int, 1>;
-  {
-    const float v = issue(qbuf(I0{}), obuf(I0{}), 0, 0);
-    if (tid < 2 * BQB) *(LDS_AS float*)(stat + tid * 4) = stat_val(v);
-    wait_vmem();
-  }
-  int h1 = 0, t1 = 0;
-  advance(h1, t1);   // tile 1
-  __syncthreads();
-
-  const int ka = kw0, kb = kw0 + 31;
-  int hc = 0, tc = 0;   // tile of the current iteration
-  // one query tile: S (and dP) against this workgroup's keys, P (and dS),
-  // then dV (or dK) accumulation
-  auto compute = [&](const LDS_AS char* Qt, const LDS_AS char* dOt, const LDS_AS float* lse2t,
-                     const LDS_AS float* Dt, const int q0) __attribute__((always_inline)) {
-        const bool empty = ka >= T || q0 + BQB - 1 < ka || (W > 0 && q0 - kb >= W);
-      const bool full = q0 >= kb && q0 + BQB <= T && (W == 0 || q0 + BQB - 1 - ka < W);
-      f32x16 s[NS], dp[NS];
-      // first transposed operands of the dV (dO^T) or dK (Q^T) product,
-      // issued before the softmax so their latency hides behind it
-      TrPipe<DV, NDBV, BQB / 16, BWD_LDS_PD(DK)> otp;
-      TrPipe<DK, NDBK, BQB / 16, BWD_LDS_PD(DK)> qtp;
-      if (!empty) {
-        if constexpr (DO_DK)
-          mma_rows2<DK, DV, NS, BWD_LDS_PD(DK)>(s, Qt, kreg, dp, dOt, vreg, lane);
-        else
-          mma_rows_pd<DK, NS, BWD_LDS_PD(DK)>(s, Qt, kreg, lane);
-        if constexpr (DO_DV) otp.start(dOt, 0, lane);
-        if constexpr (DO_DK) qtp.start(Qt, 0, lane);
-      }
-      if (!empty) {
-        // S, dP: lane = key row, accumulator i = query row 32t + acc_row(i, g).
-        // P into s[], dS into dp[].
-  #pragma unroll
-        for (int t = 0; t < NS; ++t)
-  #pragma unroll
-          for (int i4 = 0; i4 < 4; ++i4) {
-            const int qloc = 32 * t + 8 * i4 + 4 * g;
-            const f32x4 l4 = *(const LDS_AS f32x4*)(lse2t + qloc);
-            const f32x4 d4 = *(const LDS_AS f32x4*)(Dt + qloc);
-  #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int i = 4 * i4 + e;
-              float th;
-              const float p = fast_exp2(p_arg<CAP>(s[t][i], a, l4[e], th));
-              s[t][i] = p;
-              if (DO_DK) {
-                float ds = p * (dp[t][i] - d4[e]);
-                if (CAP) ds *= 1.f - th * th;
-                dp[t][i] = ds;
-              }
-            }
-          }
-        // Partial tiles: zero P and dS of invisible pairs in one block (every
-        // element above is computed branch-free).
-        if (!full) {
-  #pragma unroll
-          for (int t = 0; t < NS; ++t)
-  #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int q = q0 + 32 * t + acc_row(i, g);
-              const bool vis = (q < T) & (krow <= q) & ((W == 0) | (krow > q - W));
-              if (DO_DV) s[t][i] = vis ? s[t][i] : 0.f;
-              if (DO_DK) dp[t][i] = vis ? dp[t][i] : 0.f;
-            }
-        }
-        bf16x8 pb[BQB / 16], dsb[BQB / 16];
-  #pragma unroll
-        for (int c16 = 0; c16 < BQB / 16; ++c16) {
-          float tp[8], td[8];
-  #pragma unroll
-          for (int jj = 0; jj < 8; ++jj) {
-            tp[jj] = s[c16 >> 1][8 * (c16 & 1) + jj];
-            td[jj] = dp[c16 >> 1][8 * (c16 & 1) + jj];
-          }
-          if (DO_DV) pb[c16] = pack_bf16(tp);
-          if (DO_DK) dsb[c16] = pack_bf16(td);
-        }
-        if constexpr (DO_DV) otp.run(dvacc, dOt, 0, pb, lane);
-        if constexpr (DO_DK) qtp.run(dkacc, Qt, 0, dsb, lane);
-      }
-  };
-
-  // one iteration on the tile in buffer cur (qt, ot: its Q and dO tiles;
-  // qn, on: the idle buffers)
-  auto step = [&](const int it, const int cur, const LDS_AS char* qt, const LDS_AS char* ot,
-                  LDS_AS char* qn, LDS_AS char* on) __attribute__((always_inline)) {
-    const bool more = it + 1 < niter;
-    float sv = 0.f;
-    if (more) sv = issue(qn, on, h1, t1);
-    const LDS_AS float* lse2t = (const LDS_AS float*)(stat + cur * 2 * STAT);
-    compute(qt, ot, lse2t, lse2t + BQB, tile_q0(tc));
-    if (more) {
-      if (tid < 2 * BQB) *(LDS_AS float*)(stat + (cur ^ 1) * 2 * STAT + tid * 4) = stat_val(sv);
-      wait_vmem();
-    }
-    __syncthreads();
-    hc = h1;
-    tc = t1;
-    advance(h1, t1);
-  };
-  if constexpr (UNROLL) {
-    // loop unrolled by two: the buffers are compile-time choices
-    int it = 0;
-    for (; it + 1 < niter; it += 2) {
-      step(it, 0, qbuf(I0{}), obuf(I0{}), qbuf(I1{}), obuf(I1{}));
-      step(it + 1, 1, qbuf(I1{}), obuf(I1{}), qbuf(I0{}), obuf(I0{}));
-    }
-    if (it < niter) step(it, 0, qbuf(I0{}), obuf(I0{}), qbuf(I1{}), obuf(I1{}));
-  } else {
-    // the buffer picked at run time in the one array
-    for (int it = 0; it < niter; ++it) {
-      const int cur = it & 1;
-      LDS_AS char* const q0b = (LDS_AS char*)one;
-      LDS_AS char* const o0b = (LDS_AS char*)one + 2 * TILE_Q;
-      step(it, cur, q0b + cur * TILE_Q, o0b + cur * TILE_O, q0b + (cur ^ 1) * TILE_Q,
-           o0b + (cur ^ 1) * TILE_O);
-    }
-  }
-
-  if (krow < T) {
-    if (DO_DK) {
-      bf16* Kd = a.dk + (bkv * T + krow) * DK;
-#pragma unroll
-      for (int db = 0; db < NDBK; ++db)
-#pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          bf16x4 kv4;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) kv4[e] = (bf16)(dkacc[db][4 * i4 + e] * a.scale);
-          *(bf16x4*)(Kd + 32 * db + 8 * i4 + 4 * g) = kv4;
-        }
-    }
-    if (DO_DV) {
-      bf16* Vd = a.dv + (bkv * T + krow) * DV;
-#pragma unroll
-      for (int db = 0; db < NDBV; ++db)
-#pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          bf16x4 vv4;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) vv4[e] = (bf16)dvacc[db][4 * i4 + e];
-          *(bf16x4*)(Vd + 32 * db + 8 * i4 + 4 * g) = vv4;
-        }
-    }
-  }
-}
-
 // ------------------------------------------------------ fused dK/dV pass
 #ifndef PAIR_PD
 #define PAIR_PD(D) 3
@@ -1623,56 +1094,25 @@ __global__ __launch_bounds__(BQB == 32 ? 256 : 512, 1) void fa_bwd_dkdv_pair_ker
     run(std::false_type{});
 }
 
-// Tile shapes per head size: dq pass (keys per tile, waves), dV pass and
-// dK pass (queries per tile, waves); chosen by measurement on MI355X.
+// dQ pass tile shape per head size (keys per tile, waves), chosen by
+// measurement on MI355X; d = 256 runs the software-pipelined kernel.
 #ifndef BWD64_CFG
-#define BWD64_CFG 64, 4, 64, 4, 64, 4
-#endif
-#ifndef BWD256_CFG
-#define BWD256_CFG 32, 4, 64, 4, 32, 4
+#define BWD64_CFG 64, 4
 #endif
 #ifndef BWD128_CFG
-#define BWD128_CFG 32, 4, 64, 8, 32, 8
+#define BWD128_CFG 32, 4
 #endif
 #ifndef BWD192_CFG
-#define BWD192_CFG 32, 8, 64, 8, 32, 8
+#define BWD192_CFG 32, 8
 #endif
 
-// d = 256 dQ pass: the software-pipelined single-wave kernel (1) or the
-// paired-wave kernel
-#ifndef BWD_DQ_PIPE
-#define BWD_DQ_PIPE 1
-#endif
-#ifndef BWD_DQ_PAIR
-#define BWD_DQ_PAIR 1
-#endif
-// dK and dV in one launch with paired waves (every supported head size; 0
-// selects the two-launch fa_bwd_dkdv_kernel scheme)
-#ifndef BWD_KV_PAIR
-#define BWD_KV_PAIR 1
-#endif
-#ifndef BWD_KV_PAIR_192
-#define BWD_KV_PAIR_192 1
-#endif
-#ifndef BWD_KV_PAIR_256
-#define BWD_KV_PAIR_256 1
-#endif
-#define BWD_KV_PAIR_FOR(DK, DV)                                                    \
-  (BWD_KV_PAIR && (((DK) == (DV) && ((DK) == 64 || (DK) == 128)) ||              \
-                   ((DK) == 192 && (DV) == 128 && BWD_KV_PAIR_192) ||            \
-                   ((DK) == 256 && (DV) == 256 && BWD_KV_PAIR_256)))
-
-template <int DK, int DV, bool CAP, int DQ_BKV, int DQ_NW, int DV_BQB, int DV_NW, int DK_BQB,
-          int DK_NW>
+// the dQ pass, then the fused dK/dV pass
+template <int DK, int DV, bool CAP, int DQ_BKV, int DQ_NW>
 static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
-  if constexpr (DK == 256 && DV == 256 && BWD_DQ_PIPE) {
+  if constexpr (DK == 256) {
     const int nqb = (a.T + 127) / 128;
     hipLaunchKernelGGL((fa_bwd_dq_pipe_kernel<CAP>), dim3((unsigned)nqb * a.B * a.H), dim3(256), 0,
                        stream, a);
-  } else if constexpr (DK == 256 && DV == 256 && BWD_DQ_PAIR) {
-    const int nqb = (a.T + 127) / 128;
-    hipLaunchKernelGGL((fa_bwd_dq_pair_kernel<256, 32, CAP>), dim3((unsigned)nqb * a.B * a.H),
-                       dim3(512), 0, stream, a);
   } else {
     const int nqb = (a.T + 32 * DQ_NW - 1) / (32 * DQ_NW);
     hipLaunchKernelGGL((fa_bwd_dq_kernel<DK, DV, DQ_BKV, DQ_NW, CAP>), dim3((unsigned)nqb * a.B * a.H),
@@ -1681,42 +1121,24 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   stage_mark(stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if constexpr (BWD_KV_PAIR_FOR(DK, DV)) {
-    constexpr int BQB = DK == 256 ? 32 : PAIR_BQB;
-    using SH = PairShape<DK, DV, BQB>;
-    constexpr int BKVB = 32 * SH::NP;
-    const dim3 grid((unsigned)((a.T + BKVB - 1) / BKVB) * a.B * a.Hkv);
-    hipLaunchKernelGGL((fa_bwd_dkdv_pair_kernel<DK, DV, BQB, CAP>), grid, dim3(64 * SH::NW), 0,
-                       stream, a);
-    stage_mark(stream);
-    return hipGetLastError();
-  } else {
-    // the two-launch alternative (only built when selected)
-    const dim3 vgrid((unsigned)((a.T + 32 * DV_NW - 1) / (32 * DV_NW)) * a.B * a.Hkv);
-    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<DK, DV, DV_BQB, DV_NW, CAP, 1>), vgrid, dim3(64 * DV_NW),
-                       0, stream, a);
-    stage_mark(stream);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const dim3 kgrid((unsigned)((a.T + 32 * DK_NW - 1) / (32 * DK_NW)) * a.B * a.Hkv);
-    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<DK, DV, DK_BQB, DK_NW, CAP, 2>), kgrid, dim3(64 * DK_NW),
-                       0, stream, a);
-    stage_mark(stream);
-    return hipGetLastError();
-  }
+  constexpr int BQB = DK == 256 ? 32 : PAIR_BQB;
+  using SH = PairShape<DK, DV, BQB>;
+  constexpr int BKVB = 32 * SH::NP;
+  const dim3 grid((unsigned)((a.T + BKVB - 1) / BKVB) * a.B * a.Hkv);
+  hipLaunchKernelGGL((fa_bwd_dkdv_pair_kernel<DK, DV, BQB, CAP>), grid, dim3(64 * SH::NW), 0, stream,
+                     a);
+  stage_mark(stream);
+  return hipGetLastError();
 }
 
-template <int DK, int DV, int DQ_BKV, int DQ_NW, int DV_BQB, int DV_NW, int DK_BQB, int DK_NW>
+template <int DK, int DV, int DQ_BKV = 32, int DQ_NW = 4>
 static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
-  if (a.cap_log2e > 0.f)
-    return launch_bwd_t<DK, DV, true, DQ_BKV, DQ_NW, DV_BQB, DV_NW, DK_BQB, DK_NW>(a, stream);
-  return launch_bwd_t<DK, DV, false, DQ_BKV, DQ_NW, DV_BQB, DV_NW, DK_BQB, DK_NW>(a, stream);
+  if (a.cap_log2e > 0.f) return launch_bwd_t<DK, DV, true, DQ_BKV, DQ_NW>(a, stream);
+  return launch_bwd_t<DK, DV, false, DQ_BKV, DQ_NW>(a, stream);
 }
 
 const char* bwd_kernel_plan(int d, int d_v) {
-  if (d == d_v && (d == 64 || d == 128)) return BWD_KV_PAIR_FOR(64, 64) ? "dq,dkdv" : "dq,dv,dk";
-  if (d == 192 && d_v == 128) return BWD_KV_PAIR_FOR(192, 128) ? "dq,dkdv" : "dq,dv,dk";
-  if (d == d_v && d == 256) return BWD_KV_PAIR_FOR(256, 256) ? "dq,dkdv" : "dq,dv,dk";
+  if ((d == d_v && (d == 64 || d == 128 || d == 256)) || (d == 192 && d_v == 128)) return "dq,dkdv";
   return nullptr;
 }
 
@@ -1725,7 +1147,7 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, int d, int d_v, hipStream_t stream)
     switch (d) {
       case 64: return launch_bwd_d<64, 64, BWD64_CFG>(a, stream);
       case 128: return launch_bwd_d<128, 128, BWD128_CFG>(a, stream);
-      case 256: return launch_bwd_d<256, 256, BWD256_CFG>(a, stream);
+      case 256: return launch_bwd_d<256, 256>(a, stream);
     }
   } else if (d == 192 && d_v == 128) {
     return launch_bwd_d<192, 128, BWD192_CFG>(a, stream);
