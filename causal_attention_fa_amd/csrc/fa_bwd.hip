@@ -828,8 +828,7 @@ __global__ __launch_bounds__(BQB == 32 ? 256 : 512, 1) void fa_bwd_dkdv_pair_ker
   // packed per chunk as soon as its eight elements exist.
   auto p_tile = [&](const LDS_AS char* Qt, const LDS_AS char* dOt, LDS_AS char* X,
                     const LDS_AS float* lse2t, const int q0, const LaneOffs<DK>& lq,
-                    const LaneOffs<DV>& lv_) __attribute__((always_inline)) {
-    if (empty_tile(q0)) return;
+                    const LaneOffs<DV>& lv_, auto&& ld) __attribute__((always_inline)) {
     const int vb = q0 + 4 * g - krow;   // q - krow = vb + 32t + 8(i/4) + i%4
     // every pair of the tile visible to every key of the wave: no mask
     const bool full = q0 >= kb && q0 + BQB <= T && (W == 0 || q0 + BQB - 1 - ka < W);
@@ -898,6 +897,7 @@ __global__ __launch_bounds__(BQB == 32 ? 256 : 512, 1) void fa_bwd_dkdv_pair_ker
                span_of(16, NCK, k - NCK, e0, e1);
                elems(0, e0, e1);
              }
+             ld(k);
              if (k == NSQ - PD) vq.start(fV);
            });
     // the last half: with one half, its first chunk before the dV product
@@ -924,7 +924,7 @@ __global__ __launch_bounds__(BQB == 32 ? 256 : 512, 1) void fa_bwd_dkdv_pair_ker
   // chunk computed under the MFMAs of the one before, dK^T += Q^T dS;
   // tail() runs a few MFMAs before the end (it starts the next product)
   auto ds_prev = [&](f32x16 (&dp)[NS], const LDS_AS char* Qt, const LDS_AS char* X,
-                     const LDS_AS float* Dt, const LaneOffs<DK>& lq, auto&& tail)
+                     const LDS_AS float* Dt, const LaneOffs<DK>& lq, auto&& tail, auto&& ld)
                      __attribute__((always_inline)) {
     (void)Dt;
     bf16x8 xf[NC16];
@@ -957,6 +957,7 @@ __global__ __launch_bounds__(BQB == 32 ? 256 : 512, 1) void fa_bwd_dkdv_pair_ker
 #pragma unroll
                for (int jj = j0; jj < j1; ++jj) dsel(c, jj);
              }
+             ld(k);
              if (k == NKQ - PD) tail();
            });
   };
@@ -964,7 +965,7 @@ __global__ __launch_bounds__(BQB == 32 ? 256 : 512, 1) void fa_bwd_dkdv_pair_ker
   // (the statistics tile holds -D); the two halves' accumulations alternate
   // (independent MFMAs back to back)
   auto dp_cur = [&](f32x16 (&dp)[NS], MfmaSeq<NS * NCV, PD>& pq, auto&& fP, const bool started,
-                    const LDS_AS float* Dn) __attribute__((always_inline)) {
+                    const LDS_AS float* Dn, auto&& ld) __attribute__((always_inline)) {
 #pragma unroll
     for (int t = 0; t < NS; ++t)
 #pragma unroll
@@ -980,12 +981,12 @@ __global__ __launch_bounds__(BQB == 32 ? 256 : 512, 1) void fa_bwd_dkdv_pair_ker
 #pragma unroll
       for (int i = 0; i < 16; ++i) dp2[i] = 0.f;
       pq.run(fP, [&](int k) { return kv[k]; },
-             [&](int k) -> f32x16& { return (k & 1) ? dp2 : dp[0]; }, [&](int) {});
+             [&](int k) -> f32x16& { return (k & 1) ? dp2 : dp[0]; }, ld);
 #pragma unroll
       for (int i = 0; i < 16; ++i) dp[0][i] += dp2[i];
     } else {
       pq.run(fP, [&](int k) { return kv[k / NS]; }, [&](int k) -> f32x16& { return dp[k % NS]; },
-             [&](int) {});
+             ld);
     }
   };
 
@@ -1008,7 +1009,35 @@ __global__ __launch_bounds__(BQB == 32 ? 256 : 512, 1) void fa_bwd_dkdv_pair_ker
     const int xs = it & 1;   // exchange slot of tile it
     const bool more = it + 1 < niter;
     float sv = 0.f;
-    if (more) sv = issue(qbuf(qn), obuf(on), h1, t1);
+    if (more) sv = stage_stats(h1, t1);
+    // Tile it+1's Q and dO loads go out one after each MFMA of this step's
+    // first product (a burst of them stalls the wave until the memory
+    // pipeline has taken them), branch-free: with no tile it+1 they read an
+    // empty range (zeros, no memory touched) into a slot no one reads.
+    // Every wave of a side issues the same number of 1 KB pieces.
+    constexpr int W0 = PS ? 0 : NP, W1 = PS ? NP - 1 : NW - 1;   // the side's waves
+    constexpr int NQI = TileDma<DK, BQB, NW>::NI, NOI = TileDma<DV, BQB, NW>::NI;
+    constexpr int NLQ = (NQI - W0 + NW - 1) / NW, NLO = (NOI - W0 + NW - 1) / NW;
+    static_assert(NLQ == (NQI - W1 + NW - 1) / NW && NLO == (NOI - W1 + NW - 1) / NW,
+                  "every wave of a side loads as many pieces");
+    static_assert(NLQ + NLO <= 16, "one load per MFMA of a 16-MFMA product");
+    const bf16* qsrc = tile_src(h1, a.q, DK);
+    const bf16* osrc = tile_src(h1, a.dO, DV);
+    const int nq = more ? T * DK * 2 : 0, no = more ? T * DV * 2 : 0, row1 = tile_q0(t1);
+    auto ld = [&](int k) __attribute__((always_inline)) {
+      if (k < NLQ)
+        qdm.load_piece(k, qsrc, nq, qbuf(qn), row1, wave);
+      else if (k < NLQ + NLO)
+        odm.load_piece(k - NLQ, osrc, no, obuf(on), row1, wave);
+    };
+    auto ld_all = [&]() __attribute__((always_inline)) {
+#pragma unroll
+      for (int k = 0; k < NLQ + NLO; ++k) ld(k);
+    };
+    auto no_ld = [](int) {};
+    // where spreading them keeps the side spill-free (measured per shape);
+    // elsewhere all at the top of the step
+    constexpr bool SPREAD = PS ? DK <= 128 : DK != 192;
     // lane offsets refreshed per step (in place): the buffer addresses
     // derived from them are formed here (one add per buffer) instead of
     // hoisted out of the loop, where those of all the buffers would stay live
@@ -1019,24 +1048,41 @@ __global__ __launch_bounds__(BQB == 32 ? 256 : 512, 1) void fa_bwd_dkdv_pair_ker
     const LaneOffs<DV>& lv = lv0;
     const int xo = xo0;
     if constexpr (PS) {
-      if (it < niter) p_tile(qbuf(qc), obuf(oc), xbuf(xs, xo), sbufp(qc), tile_q0(tc), lq, lv);
+      const bool cur = it < niter && !empty_tile(tile_q0(tc));
+      if constexpr (SPREAD) {
+        if (cur)
+          p_tile(qbuf(qc), obuf(oc), xbuf(xs, xo), sbufp(qc), tile_q0(tc), lq, lv, ld);
+        else
+          ld_all();
+      } else {
+        ld_all();
+        if (cur) p_tile(qbuf(qc), obuf(oc), xbuf(xs, xo), sbufp(qc), tile_q0(tc), lq, lv, no_ld);
+      }
     } else {
       const bool cur = it < niter && !empty_tile(tile_q0(tc));
       auto fP = [&](int k) { return lds_row_op<DV>(obuf(oc), lv, k % NS, k / NS); };
       MfmaSeq<NS * NCV, PD> pq;   // dP of the current tile, its first reads issued early
+      // spread, the loads go under the previous tile's dK product; without
+      // one (the first step, an empty previous tile) all at once
+      if constexpr (!SPREAD) ld_all();
       bool started = false;
       if (it > 0 && !empty_tile(tile_q0(tp))) {
-        ds_prev(dp, qbuf(qp), xbuf(xs ^ 1, xo), sbufp(qp) + BQB, lq, [&]() {
-          if (cur) pq.start(fP);
-        });
+        if constexpr (SPREAD)
+          ds_prev(dp, qbuf(qp), xbuf(xs ^ 1, xo), sbufp(qp) + BQB, lq, [&]() {
+            if (cur) pq.start(fP);
+          }, ld);
+        else
+          ds_prev(dp, qbuf(qp), xbuf(xs ^ 1, xo), sbufp(qp) + BQB, lq, [&]() {
+            if (cur) pq.start(fP);
+          }, no_ld);
         started = true;
+      } else if constexpr (SPREAD) {
+        ld_all();
       }
-      if (cur) dp_cur(dp, pq, fP, started, sbufp(qc) + BQB);
+      if (cur) dp_cur(dp, pq, fP, started, sbufp(qc) + BQB, no_ld);
     }
-    if (more) {
-      if (wave < 2 * BQB / 64) sbufp(qn)[tid] = stat_val(sv);
-      wait_vmem();
-    }
+    if (more && wave < 2 * BQB / 64) sbufp(qn)[tid] = stat_val(sv);
+    wait_vmem();
     __syncthreads();
     tp = tc;
     tc = t1;
