@@ -385,7 +385,8 @@ __global__ __launch_bounds__(64 * NW, (DK >= 192 ? 1 : 8 / NW)) void fa_bwd_dq_k
 template <bool CAP>
 __global__ __launch_bounds__(256, 1) void fa_bwd_dq_pipe_kernel(BwdArgs a) {
   constexpr int D = 256, NW = 4, BQ = 32 * NW, BKV = 32;
-  constexpr int TILE = Lay<D>::template bytes<BKV>();
+  // a tile image, rounded up to whole rounds of the loaders' 1 KB pieces
+  constexpr int TILE = TileDma<D, BKV, NW>::IMG;
   constexpr int NC = D / 16;     // chunks of the S and dP contractions
   constexpr int NDB = D / 32;    // 32-wide blocks of dq
   constexpr int NQ = 2 * NDB;    // MFMAs of the dQ block
@@ -520,12 +521,14 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_dq_pipe_kernel(BwdArgs a) {
   };
   // cap and mask of unit u's scores, elements [e0, e1) (factor 1 - tanh^2
   // into tt, zero where masked; masked scores -inf so that P = 0)
-  auto part_a = [&](auto x_c, int u, int e0, int e1) __attribute__((always_inline)) {
+  // (MASK false: every row of the wave sees the whole unit)
+  auto part_a = [&](auto x_c, auto mask_c, int u, int e0, int e1) __attribute__((always_inline)) {
     constexpr int X = decltype(x_c)::value;
+    constexpr bool MASK = decltype(mask_c)::value;
     const int base = qrow - (t_lo + u) * BKV - 4 * g;
 #pragma unroll
     for (int i = e0; i < e1; ++i) {
-      const bool vis = (unsigned)(base - (8 * (i >> 2) + (i & 3))) < span;
+      const bool vis = !MASK || (unsigned)(base - (8 * (i >> 2) + (i & 3))) < span;
       float x = sx[X][i];
       if (CAP) {
         const float e = fast_exp2(x * a.two_scale_over_cap_log2e);
@@ -569,8 +572,10 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_dq_pipe_kernel(BwdArgs a) {
   }
   wait_vmem();
   __syncthreads();
+  using MT = std::true_type;
+  using MF = std::false_type;
   s_block(I0{}, kbuf(I0{}), [&](int) {});
-  part_a(I0{}, 0, 0, 16);
+  part_a(I0{}, MT{}, 0, 0, 16);
   dp_block(I0{}, vbuf(I0{}), [&](int k) __attribute__((always_inline)) { part_b(I0{}, k, k + 1); });
 
   // iteration i (buffer slots: K(i) in B0, K(i+1) and V(i+1) in B1, loads
@@ -580,25 +585,49 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_dq_pipe_kernel(BwdArgs a) {
   // buffer range reads zeros), so they are fully masked and add exact zeros;
   // every step then computes a next unit, and after each group of three the
   // next unit's tiles move back to parity 0.
-  auto step = [&](auto b0, auto b1, auto b2, auto x_c, const int i) __attribute__((always_inline)) {
+  // K(i+2) and V(i+2) load one piece after each of the S block's first
+  // MFMAs (whose hooks carry little VALU), branch-free: a wave with no piece
+  // k left loads zeros into the image's partial last round
+  constexpr int PER = TileDma<D, BKV, NW>::PER;
+  static_assert(2 * PER <= NC, "one load per S MFMA");
+  auto step = [&](auto b0, auto b1, auto b2, auto x_c, auto mask_c, const int i)
+                  __attribute__((always_inline)) {
     using XN = std::integral_constant<int, 1 - decltype(x_c)::value>;
     lo.refresh();
-    dm.load(Kp, T * D * 2, kbuf(b2), (t_lo + i + 2) * BKV, wave);
-    dm.load(Vp, T * D * 2, vbuf(b2), (t_lo + i + 2) * BKV, wave);
-    s_block(XN{}, kbuf(b1), [&](int k) __attribute__((always_inline)) { part_c(x_c, k, k + 1); });
-    q_block(kbuf(b0), [&](int k) __attribute__((always_inline)) { part_a(XN{}, i + 1, k, k + 1); });
+    s_block(XN{}, kbuf(b1), [&](int k) __attribute__((always_inline)) {
+      part_c(x_c, k, k + 1);
+      if (k < PER)
+        dm.load_piece(k, Kp, T * D * 2, kbuf(b2), (t_lo + i + 2) * BKV, wave);
+      else if (k < 2 * PER)
+        dm.load_piece(k - PER, Vp, T * D * 2, vbuf(b2), (t_lo + i + 2) * BKV, wave);
+    });
+    q_block(kbuf(b0), [&](int k) __attribute__((always_inline)) {
+      part_a(XN{}, mask_c, i + 1, k, k + 1);
+    });
     dp_block(XN{}, vbuf(b1), [&](int k) __attribute__((always_inline)) { part_b(XN{}, k, k + 1); });
     wait_vmem();
     __syncthreads();
   };
-  const int nu3 = (nu + 2) / 3 * 3;
-  for (int i = 0; i < nu3; i += 3) {
-    step(I0{}, I1{}, I2{}, I0{}, i);
-    step(I1{}, I2{}, I0{}, I1{}, i + 1);
-    step(I2{}, I0{}, I1{}, I0{}, i + 2);
+  auto group = [&](auto mask_c, const int i) __attribute__((always_inline)) {
+    step(I0{}, I1{}, I2{}, I0{}, mask_c, i);
+    step(I1{}, I2{}, I0{}, I1{}, mask_c, i + 1);
+    step(I2{}, I0{}, I1{}, I0{}, mask_c, i + 2);
     sx[0] = sx[1];
     dpx[0] = dpx[1];
-  }
+  };
+  // Groups of three steps whose units (i + 1 .. i + 3) every row of the wave
+  // sees whole form one range [ga, gb): the units in [mlo, mhi).  The groups
+  // before and after it evaluate the mask; those in it carry none.
+  const int ng = (nu + 2) / 3;
+  const int mhi = qw0 / BKV - t_lo;   // first unit holding a key past row qw0
+  const int wlo = qw0 + 31 - W;       // keys above it are in every row's window
+  const int mlo = (W > 0 && wlo >= 0) ? max(0, wlo / BKV + 1 - t_lo) : 0;
+  const int ga = min(ng, max(0, (mlo + 1) / 3));          // first group with 3 gi + 1 >= mlo
+  const int gb = min(ng, max(ga, mhi >= 4 ? (mhi - 4) / 3 + 1 : 0));   // 3 gi + 3 < mhi
+  int gi = 0;
+  for (; gi < ga; ++gi) group(MT{}, 3 * gi);
+  for (; gi < gb; ++gi) group(MF{}, 3 * gi);
+  for (; gi < ng; ++gi) group(MT{}, 3 * gi);
 
   agpr_acc_fence(dqacc);
   if (qrow < T) {
