@@ -35,13 +35,14 @@ CFLAGS = [
 ]
 
 
-# extra flags per source file.  fa_fwd.hip: the software-pipelined kernel
-# pins its O accumulator to the AGPRs; without the flag the compiler then
-# gives the score MFMAs the AGPR form too and copies every score tile back
-# to the VGPRs for the softmax.
+# extra flags per source file.  -amdgpu-mfma-vgpr-form: the d = 256 kernels
+# pin their long-lived accumulators to the AGPRs; without the flag the
+# compiler then gives the score (and dP) MFMAs the AGPR form too and copies
+# every such tile back to the VGPRs for the softmax.
 FILE_FLAGS = {
     "fa_bwd.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
     "fa_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "fa_bwd_pipe.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp", "-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 
