@@ -27,7 +27,9 @@
 //      S, P and dV, the other keeps V and computes dP, dS and dK one tile
 //      later from the factor the first leaves in LDS.  dV^T += dO^T P and
 //      dK^T += Q^T dS take dO^T and Q^T from the natural tiles through the
-//      LDS transpose read.
+//      LDS transpose read.  At d = 128 fa_bwd_kv_pipe_kernel
+//      (fa_bwd_pipe.hip) runs instead: one software-pipelined wave per 32
+//      keys does both sides' work, with no exchange through LDS.
 #include <type_traits>
 
 #include "device_common.h"
@@ -875,6 +877,12 @@ __global__ __launch_bounds__(BQB == 32 ? 256 : 512, 1) void fa_bwd_dkdv_pair_ker
 #define BWD192_CFG 32, 8
 #endif
 
+// d = 128 dK/dV pass: the software-pipelined single-wave kernel
+// (fa_bwd_pipe.hip) instead of the paired-wave one
+#ifndef BWD_KV_PIPE128
+#define BWD_KV_PIPE128 1
+#endif
+
 // the dQ pass, then the fused dK/dV pass
 template <int DK, int DV, bool CAP, int DQ_BKV, int DQ_NW>
 static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
@@ -888,6 +896,11 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   stage_mark(stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if constexpr (DK == 128 && DV == 128 && BWD_KV_PIPE128) {
+    launch_bwd_kv_pipe(a, CAP, stream);   // fa_bwd_pipe.hip
+    stage_mark(stream);
+    return hipGetLastError();
+  }
   constexpr int BQB = DK == 256 ? 32 : PAIR_BQB;
   using SH = PairShape<DK, DV, BQB>;
   constexpr int BKVB = 32 * SH::NP;

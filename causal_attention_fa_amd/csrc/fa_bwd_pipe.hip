@@ -1,10 +1,14 @@
-// d = 256 dQ pass of the causal flash-attention backward for gfx950
-// (bf16 in, fp32 accumulate): the same gradient as fa_bwd_dq_kernel in
-// fa_bwd.hip (dq = scale dS K with dS = P (dP - D) and, under a softcap, the
-// factor 1 - tanh^2), software-pipelined for one wave per SIMD.  It lives in
-// a file of its own because it is compiled with the VGPR form of the MFMA
-// (its dQ accumulator is pinned to the AGPRs, so the score and dP products
-// must not follow it there), which the dK/dV pass in fa_bwd.hip must not get.
+// Software-pipelined passes of the causal flash-attention backward for
+// gfx950 (bf16 in, fp32 accumulate), one wave per SIMD, with the same
+// gradients as the kernels in fa_bwd.hip (dS = P (dP - D) and, under a
+// softcap, the factor 1 - tanh^2):
+//   fa_bwd_dq_pipe_kernel -- the d = 256 dQ pass (dq = scale dS K);
+//   fa_bwd_kv_pipe_kernel -- the d = 128 dK/dV pass (dk = scale dS^T Q,
+//                            dv = P^T dO), in place of the paired-wave one.
+// They live in a file of their own because it is compiled with the VGPR form
+// of the MFMA (their gradient accumulators are pinned to the AGPRs, so the
+// score and dP products must not follow them there), which the paired-wave
+// dK/dV kernel in fa_bwd.hip must not get.
 #include <type_traits>
 
 #include "device_common.h"
@@ -297,6 +301,383 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_dq_pipe_kernel(BwdArgs a) {
   }
 }
 
+// Head size 128, dK/dV pass, software-pipelined: one wave per SIMD owns 32
+// key rows and does all of their work -- K and V rows in registers (the B
+// operands of S = Q K^T and dP = dO V^T), dK^T and dV^T in the accumulation
+// registers, P and dS never leaving the wave.  A workgroup (4 waves, 128
+// keys) walks the 32-query units of the GQA group's heads that can see its
+// keys; per unit i four MFMA blocks run, each carrying the VALU of a
+// neighbouring unit:
+//   S(i+1)   = Q(i+1) K^T          carrying  dS(i) = f(i) (dP(i) - D), bf16 pack,
+//                                            and the tile loads of unit i+2
+//   dK^T    += Q(i)^T dS(i)        carrying  the cap's tanh and the mask of S(i+1)
+//   dP(i+1)  = dO(i+1) V^T - D     carrying  P(i+1) (bf16 pack) and f(i+1) =
+//                                            P (1 - tanh^2) (P without a cap)
+//   dV^T    += dO(i+1)^T P(i+1)
+// (VALU under the blocks that read their operands transposed costs more
+// than under those that read rows, measured.)
+// Q and dO tiles and the row statistics (lse, -D) are triple-buffered in LDS,
+// the buffer of each unit picked at run time; one barrier per unit.  Units of
+// the workgroup's query range outside a wave's band are computed fully
+// masked (exact zeros), so every wave runs the same schedule; units every
+// row of which sees all 32 keys carry no mask.
+// MfmaSeq with the accumulators pinned to the AGPRs (mfma32_agpr): for
+// kernels whose long-lived accumulators do not fit beside their working set
+// in the VGPRs.  B operands written by the VALU must not be produced by the
+// instruction right before the MFMA that reads them (the hook of an earlier
+// MFMA, or earlier still, writes them).
+template <int N, int PD>
+struct AgprSeq {
+  static constexpr int R = PD + 1;
+  bf16x8 op[R];
+  template <class Fetch>
+  __device__ __forceinline__ void start(Fetch&& fetch) {
+#pragma unroll
+    for (int k = 0; k < PD && k < N; ++k) op[k % R] = fetch(k);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  template <class Fetch, class BOp, class Acc, class Hook>
+  __device__ __forceinline__ void run(Fetch&& fetch, BOp&& bop, Acc&& acc, Hook&& hook) {
+#pragma unroll
+    for (int k = 0; k < N; ++k) {
+      if (k + PD < N) op[(k + PD) % R] = fetch(k + PD);
+      mfma32_agpr(acc(k), op[k % R], bop(k));
+      hook(k);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+};
+
+template <bool CAP>
+__global__ __launch_bounds__(256, 1) void fa_bwd_kv_pipe_kernel(BwdArgs a) {
+  constexpr int D = 128, NW = 4, BQ = 32, BKVB = 32 * NW;
+  using Dma = TileDma<D, BQ, NW>;
+  constexpr int TILE = Dma::IMG;   // a tile image, whole rounds of 1 KB pieces
+  constexpr int PER = Dma::PER;
+  constexpr int NC = D / 16;       // k steps of S and dP
+  constexpr int NDB = D / 32;      // 32-wide blocks of dK and dV
+  constexpr int NQ = 2 * NDB;      // MFMAs of the dK and dV blocks
+  constexpr int PD = 2;   // operand reads run two MFMAs ahead (3: slower)
+  constexpr int NSL = 3;   // buffers per tile kind
+  static_assert(2 * PER <= NC, "one tile load per S MFMA");
+  // one LDS object per buffer (the compiler then sees that a tile load
+  // into one does not touch the tiles being read, and keeps it in flight)
+  __shared__ __attribute__((aligned(1024))) char qs0[TILE];
+  __shared__ __attribute__((aligned(1024))) char qs1[TILE];
+  __shared__ __attribute__((aligned(1024))) char qs2[TILE];
+  __shared__ __attribute__((aligned(1024))) char os0[TILE];
+  __shared__ __attribute__((aligned(1024))) char os1[TILE];
+  __shared__ __attribute__((aligned(1024))) char os2[TILE];
+  __shared__ __attribute__((aligned(16))) float stat[NSL * 2 * BQ];   // [slot][lse2 | -D]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5;
+  const int l32 = lane & 31;
+  const int T = a.T;
+  const int W = a.window;
+  const int G = a.H / a.Hkv;
+  const int nkb = (T + BKVB - 1) / BKVB;
+  const WorkItem w = decode_work(blockIdx.x, nkb, a.B, a.Hkv, 1, false);
+  const int k0 = w.blk * BKVB;
+  const int ka = k0 + 32 * wave;
+  const int krow = ka + l32;
+  const int kr = krow < T ? krow : T - 1;
+  const size_t bkv = (size_t)w.b * a.Hkv + w.hkv;
+
+  bf16x8 kreg[NC], vreg[NC];
+  {
+    const bf16x8* ks = (const bf16x8*)(a.k + (bkv * T + kr) * D + 8 * g);
+    const bf16x8* vs = (const bf16x8*)(a.v + (bkv * T + kr) * D + 8 * g);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      kreg[c] = ks[2 * c];
+      vreg[c] = vs[2 * c];
+    }
+  }
+  f32x16 dkacc[NDB], dvacc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      dkacc[db][i] = 0.f;
+      dvacc[db][i] = 0.f;
+    }
+
+  // query tiles that can see keys [k0, k0 + BKVB), for every head of the group
+  const int qt_lo = k0 / BQ;
+  const int q_hi = W > 0 ? min(T, k0 + BKVB - 1 + W) : T;
+  const int nqt = (q_hi + BQ - 1) / BQ - qt_lo;
+  const int niter = G * nqt;   // unit u: head u / nqt, tile u % nqt
+  // query q sees this lane's key iff (unsigned)(q - krow) < span
+  const unsigned span = W > 0 ? (unsigned)W : 0x7fffffffu;
+  const float cexp = CAP ? a.cap_log2e : a.scale_log2e;
+
+  Dma dm;
+  dm.init(wave, lane);
+  LaneOffs<D> lo;
+  lo.init(lane);
+  auto head_base = [&](int hi, const bf16* base) {
+    const int hh = w.hkv * G + (hi < G ? hi : G - 1);
+    return base + ((size_t)w.b * a.H + hh) * T * D;
+  };
+  // the statistics of a unit (lane < 32: lse, else D of row q0 + lane % 32),
+  // fetched into a register and stored to LDS by wave 0 once the step's
+  // loads are waited for.  Rows past T and units past the range get lse =
+  // +inf and D = 0, so that their P is exactly 0 whatever the (zero) tiles
+  // hold: no mask is needed for them.
+  auto stat_load = [&](int hi, int ti) -> float {
+    const int hh = w.hkv * G + (hi < G ? hi : G - 1);
+    const int q = (qt_lo + ti) * BQ + l32;
+    const float v = (g == 0 ? a.lse : a.Dst)[((size_t)w.b * a.H + hh) * T + (q < T ? q : T - 1)];
+    return hi < G && q < T ? v : (g == 0 ? INFINITY : 0.f);
+  };
+  auto stat_store = [&](LDS_AS float* st, float v) {
+    if (wave == 0) st[lane] = g == 0 ? v * kLog2e : -v;
+  };
+
+  f32x16 sacc;   // S of the unit being prepared, then its capped, masked score
+  f32x16 fx;     // f of the unit whose dS is due: P (1 - tanh^2), or P
+  f32x16 dp;     // dP - D of that unit
+  f32x16 tt;     // cap: 1 - tanh^2 of the unit being prepared (0 where masked)
+  bf16x8 pb[2], dsb[2];
+  f32x4 lsev[4];
+
+  // operands of the four products read from the LDS tiles: rows of Q or dO
+  // (S, dP), or the tile read transposed (dK, dV)
+  auto rows = [&](const LDS_AS char* X) {
+    return [=, &lo](int k) { return lds_row_op<D>(X, lo, 0, k); };
+  };
+  auto cols = [&](const LDS_AS char* X) {
+    return [=, &lo](int k) { return lds_tr_op<D>(X, lo, k / NDB, k % NDB); };
+  };
+  // cap and mask of the prepared unit's scores (tile at query q0), elements
+  // [e0, e1); masked scores become -inf so that P = 0 (MASK false: every row
+  // sees all of the wave's keys)
+  auto part_a = [&](auto mask_c, int q0, int e0, int e1) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_c)::value;
+    const int base = q0 + 4 * g - krow;
+#pragma unroll
+    for (int i = e0; i < e1; ++i) {
+      const bool vis = !MASK || (unsigned)(base + 8 * (i >> 2) + (i & 3)) < span;
+      float x = sacc[i];
+      if (CAP) {
+        const float e = fast_exp2(x * a.two_scale_over_cap_log2e);
+        x = 1.f - 2.f * __builtin_amdgcn_rcpf(e + 1.f);   // tanh
+        tt[i] = vis ? fmaf(-x, x, 1.f) : 0.f;
+      }
+      sacc[i] = vis ? x : -INFINITY;
+    }
+  };
+  // P = 2^(S' c - lse) of the prepared unit, elements [e0, e1): bf16 packs of
+  // P per 16-query chunk, f into fx
+  auto part_b = [&](int e0, int e1) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = e0; i < e1; ++i) {
+      const float p = fast_exp2(fmaf(sacc[i], cexp, -lsev[i >> 2][i & 3]));
+      sacc[i] = p;
+      fx[i] = CAP ? p * tt[i] : p;
+      if (i == 7 || i == 15) {
+        float tmp[8];
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) tmp[jj] = sacc[i - 7 + jj];
+        pb[i >> 3] = pack_bf16(tmp);
+      }
+    }
+  };
+  // dS = f (dP - D), elements [e0, e1), bf16 packs per chunk
+  auto part_c = [&](int e0, int e1) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = e0; i < e1; ++i) {
+      fx[i] *= dp[i];
+      if (i == 7 || i == 15) {
+        float tmp[8];
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) tmp[jj] = fx[i - 7 + jj];
+        dsb[i >> 3] = pack_bf16(tmp);
+      }
+    }
+  };
+  // statistics of the prepared unit: lse (log2) of the lane's rows, and -D
+  // as the dP accumulator's start
+  auto read_lse = [&](const LDS_AS float* st, int i4) __attribute__((always_inline)) {
+    lsev[i4] = *(const LDS_AS f32x4*)(st + 8 * i4 + 4 * g);
+  };
+  auto read_negd = [&](const LDS_AS float* st, int i4) __attribute__((always_inline)) {
+    const f32x4 d4 = *(const LDS_AS f32x4*)(st + BQ + 8 * i4 + 4 * g);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) dp[4 * i4 + e] = d4[e];
+  };
+  using MT = std::true_type;
+  using MF = std::false_type;
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  auto qbuf = [&](auto b_c) -> LDS_AS char* {
+    constexpr int b = decltype(b_c)::value;
+    return b == 0 ? (LDS_AS char*)qs0 : b == 1 ? (LDS_AS char*)qs1 : (LDS_AS char*)qs2;
+  };
+  auto obuf = [&](auto b_c) -> LDS_AS char* {
+    constexpr int b = decltype(b_c)::value;
+    return b == 0 ? (LDS_AS char*)os0 : b == 1 ? (LDS_AS char*)os1 : (LDS_AS char*)os2;
+  };
+  auto sbuf = [&](auto b_c) -> LDS_AS float* {
+    return (LDS_AS float*)stat + decltype(b_c)::value * 2 * BQ;
+  };
+
+  // prologue: units 0 and 1 resident; S(0), its mask, dP(0) with P(0), dV(0)
+  int h1 = 0, t1 = 0, h2 = 0, t2 = 0;   // units i+1 and i+2 of iteration i
+  auto advance = [&](int& hi, int& ti) {
+    if (++ti == nqt) {
+      ti = 0;
+      ++hi;
+    }
+  };
+  {
+    dm.load(head_base(0, a.q), T * D * 2, qbuf(I0{}), qt_lo * BQ, wave);
+    dm.load(head_base(0, a.dO), T * D * 2, obuf(I0{}), qt_lo * BQ, wave);
+    const float v0 = stat_load(0, 0);
+    advance(h1, t1);   // unit 1
+    const int nb = niter > 1 ? T * D * 2 : 0;
+    dm.load(head_base(h1, a.q), nb, qbuf(I1{}), (qt_lo + t1) * BQ, wave);
+    dm.load(head_base(h1, a.dO), nb, obuf(I1{}), (qt_lo + t1) * BQ, wave);
+    const float v1 = stat_load(h1, t1);
+    wait_vmem();
+    stat_store(sbuf(I0{}), v0);
+    stat_store(sbuf(I1{}), v1);
+    __syncthreads();
+    h2 = h1;
+    t2 = t1;
+    advance(h2, t2);   // unit 2
+  }
+  {
+    MfmaSeq<NC, PD> sq, pq;
+    AgprSeq<NQ, PD> vq;
+    const auto fS = rows(qbuf(I0{})), fP = rows(obuf(I0{}));
+    const auto fV = cols(obuf(I0{}));
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
+    sq.start(fS);
+    sq.run(fS, [&](int k) { return kreg[k]; }, [&](int) -> f32x16& { return sacc; }, [](int) {});
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      read_lse(sbuf(I0{}), i4);
+      read_negd(sbuf(I0{}), i4);
+    }
+    part_a(MT{}, qt_lo * BQ, 0, 16);
+    pq.start(fP);
+    pq.run(fP, [&](int k) { return vreg[k]; }, [&](int) -> f32x16& { return dp; },
+           [&](int k) __attribute__((always_inline)) { part_b(2 * k, 2 * k + 2); });
+    vq.start(fV);
+    vq.run(fV, [&](int k) { return pb[k / NDB]; }, [&](int k) -> f32x16& { return dvacc[k % NDB]; },
+           [](int) {});
+  }
+
+  // iteration i: dK of unit i and units i+1 (prepared) and i+2 (loading) in
+  // buffers b0, b1, b2 (compile-time: the loop is unrolled by three)
+  auto step = [&](auto b0, auto b1, auto b2, auto mask_c) __attribute__((always_inline)) {
+    lo.refresh();
+    const bool more = h2 < G;   // unit i+2 exists
+    const float sv = stat_load(h2, t2);
+    const bf16* qsrc = head_base(h2, a.q);
+    const bf16* osrc = head_base(h2, a.dO);
+    const int nb = more ? T * D * 2 : 0;
+    const int row2 = (qt_lo + t2) * BQ;
+    const int q01 = (qt_lo + t1) * BQ;
+    // S(i+1), carrying dS(i) and unit i+2's tile loads (one per MFMA,
+    // branch-free: a wave with no piece k left loads zeros into the image's
+    // partial last round).  Every block issues the next one's first operand
+    // reads PD MFMAs before its end.  (Measured and not kept: the loads split
+    // between the S and dP blocks, dS moved under the dV block, P split
+    // between the dK and dP blocks.)
+    MfmaSeq<NC, PD> sq, pq;
+    AgprSeq<NQ, PD> kq, vq;
+    const auto fS = rows(qbuf(b1)), fP = rows(obuf(b1));
+    const auto fK = cols(qbuf(b0)), fV = cols(obuf(b1));
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
+    sq.start(fS);
+    sq.run(fS, [&](int k) { return kreg[k]; }, [&](int) -> f32x16& { return sacc; },
+           [&](int k) __attribute__((always_inline)) {
+             part_c(2 * k, 2 * k + 2);
+             if (k < PER)
+               dm.load_piece(k, qsrc, nb, qbuf(b2), row2, wave);
+             else if (k < 2 * PER)
+               dm.load_piece(k - PER, osrc, nb, obuf(b2), row2, wave);
+             if (k == NC - PD) kq.start(fK);
+           });
+    // dK(i), carrying the mask (and cap) of S(i+1) and its statistics (-D
+    // as the start of dP(i+1))
+    kq.run(fK, [&](int k) { return dsb[k / NDB]; }, [&](int k) -> f32x16& { return dkacc[k % NDB]; },
+           [&](int k) __attribute__((always_inline)) {
+             part_a(mask_c, q01, 2 * k, 2 * k + 2);
+             if (k < 4)
+               read_lse(sbuf(b1), k);
+             else
+               read_negd(sbuf(b1), k - 4);
+             if (k == NQ - PD) pq.start(fP);
+           });
+    // dP(i+1), carrying P(i+1) and f(i+1)
+    pq.run(fP, [&](int k) { return vreg[k]; }, [&](int) -> f32x16& { return dp; },
+           [&](int k) __attribute__((always_inline)) {
+             part_b(2 * k, 2 * k + 2);
+             if (k == NC - PD) vq.start(fV);
+           });
+    // dV(i+1)
+    vq.run(fV, [&](int k) { return pb[k / NDB]; }, [&](int k) -> f32x16& { return dvacc[k % NDB]; },
+           [](int) {});
+    stat_store(sbuf(b2), sv);
+    wait_vmem();
+    lds_barrier();
+    h1 = h2;
+    t1 = t2;
+    advance(h2, t2);
+  };
+  auto group = [&](auto mask_c) __attribute__((always_inline)) {
+    step(I0{}, I1{}, I2{}, mask_c);
+    step(I1{}, I2{}, I0{}, mask_c);
+    step(I2{}, I0{}, I1{}, mask_c);
+  };
+  // niter iterations (the last finishes unit niter-1's dK), padded to whole
+  // groups of three: the extra ones see units past the range (zero tiles,
+  // P = 0) and add exact zeros.  Iteration i prepares unit i + 1; a group is
+  // mask-free when all three of its units lie in a head's tiles [fl, fh),
+  // those whose 32 x 32 blocks the wave sees whole.
+  const int ng = (niter + 2) / 3;
+  const int fl = min(nqt, wave + 1);
+  const int fh = W > 0 ? (W >= 32 ? min(nqt, max(fl, wave + (W - 32) / 32 + 1)) : fl) : nqt;
+  int gi = 0;
+  for (int hi = 0; hi < G; ++hi) {
+    const int u0 = hi * nqt + fl, u1 = hi * nqt + fh;   // its mask-free units [u0, u1)
+    const int ga = min(ng, max(gi, (u0 + 1) / 3));      // first group with 3 g + 1 >= u0
+    const int gb = min(ng, max(ga, u1 >= 4 ? (u1 - 4) / 3 + 1 : 0));   // 3 g + 3 < u1
+    for (; gi < ga; ++gi) group(MT{});
+    for (; gi < gb; ++gi) group(MF{});
+  }
+  for (; gi < ng; ++gi) group(MT{});
+
+  agpr_acc_fence(dkacc);
+  agpr_acc_fence(dvacc);
+  if (krow < T) {
+    bf16* dkp = a.dk + (bkv * T + krow) * D;
+    bf16* dvp = a.dv + (bkv * T + krow) * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        bf16x4 vk, vv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          vk[e] = (bf16)(dkacc[db][4 * i4 + e] * a.scale);
+          vv[e] = (bf16)dvacc[db][4 * i4 + e];
+        }
+        *(bf16x4*)(dkp + 32 * db + 8 * i4 + 4 * g) = vk;
+        *(bf16x4*)(dvp + 32 * db + 8 * i4 + 4 * g) = vv;
+      }
+  }
+}
+
 hipError_t launch_bwd_dq_pipe(const BwdArgs& a, bool cap, hipStream_t stream) {
   const int nqb = (a.T + 127) / 128;
   const dim3 grid((unsigned)nqb * a.B * a.H);
@@ -304,6 +685,16 @@ hipError_t launch_bwd_dq_pipe(const BwdArgs& a, bool cap, hipStream_t stream) {
     hipLaunchKernelGGL(fa_bwd_dq_pipe_kernel<true>, grid, dim3(256), 0, stream, a);
   else
     hipLaunchKernelGGL(fa_bwd_dq_pipe_kernel<false>, grid, dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_kv_pipe(const BwdArgs& a, bool cap, hipStream_t stream) {
+  const int nkb = (a.T + 127) / 128;
+  const dim3 grid((unsigned)nkb * a.B * a.Hkv);
+  if (cap)
+    hipLaunchKernelGGL(fa_bwd_kv_pipe_kernel<true>, grid, dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(fa_bwd_kv_pipe_kernel<false>, grid, dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -114,6 +114,8 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, int d, int d_v, hipStream_t stream)
 hipError_t launch_bwd_bf16(const BwdArgs& a, int d, int d_v, hipStream_t stream);
 // the d = 256 dQ pass (fa_bwd_pipe.hip), launched by launch_bwd_bf16
 hipError_t launch_bwd_dq_pipe(const BwdArgs& a, bool cap, hipStream_t stream);
+// the d = 128 dK/dV pass (fa_bwd_pipe.hip), launched by launch_bwd_bf16
+hipError_t launch_bwd_kv_pipe(const BwdArgs& a, bool cap, hipStream_t stream);
 // kernels launch_bwd_bf16 runs for (d, d_v), in order ("dq,dkdv"); null for
 // unsupported sizes
 const char* bwd_kernel_plan(int d, int d_v);
