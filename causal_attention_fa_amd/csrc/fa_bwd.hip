@@ -17,8 +17,8 @@
 //      per-lane scalars; dQ^T += K^T dS^T reads K^T through the LDS
 //      transpose read.  It also computes D_i for its rows (the backward
 //      prologue) and writes it to a [B, H, T] fp32 scratch for the dK/dV
-//      pass.  At d = 256 fa_bwd_dq_pipe_kernel (fa_bwd_pipe.hip) runs one
-//      software-pipelined wave per 32 rows.
+//      pass.  At d = 128 and 256 fa_bwd_dq_pipe_kernel (fa_bwd_pipe.hip)
+//      runs one software-pipelined wave per 32 rows.
 //   2. fa_bwd_dkdv_pair_kernel -- key-parallel: a workgroup owns 128 key
 //      rows (64 at d = 256) of one (b, kv head) and loops over the query
 //      heads of the GQA group and over the query tiles that can see its
@@ -866,7 +866,7 @@ __global__ __launch_bounds__(BQB == 32 ? 256 : 512, 1) void fa_bwd_dkdv_pair_ker
 }
 
 // dQ pass tile shape per head size (keys per tile, waves), chosen by
-// measurement on MI355X; d = 256 runs the software-pipelined kernel.
+// measurement on MI355X; d = 128 and 256 run the software-pipelined kernel.
 #ifndef BWD64_CFG
 #define BWD64_CFG 64, 4
 #endif
@@ -877,17 +877,22 @@ __global__ __launch_bounds__(BQB == 32 ? 256 : 512, 1) void fa_bwd_dkdv_pair_ker
 #define BWD192_CFG 32, 8
 #endif
 
-// d = 128 dK/dV pass: the software-pipelined single-wave kernel
-// (fa_bwd_pipe.hip) instead of the paired-wave one
+// d = 128: the software-pipelined kernels of fa_bwd_pipe.hip for the dK/dV
+// pass (one wave per SIMD, instead of the paired-wave kernel: mistral
+// 3.24 -> 3.05 ms) and for the dQ pass (two waves per SIMD, instead of
+// fa_bwd_dq_kernel: mistral 2.15 -> 2.08 ms; one wave per SIMD: 2.31)
 #ifndef BWD_KV_PIPE128
 #define BWD_KV_PIPE128 1
+#endif
+#ifndef BWD_DQ_PIPE128
+#define BWD_DQ_PIPE128 1
 #endif
 
 // the dQ pass, then the fused dK/dV pass
 template <int DK, int DV, bool CAP, int DQ_BKV, int DQ_NW>
 static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
-  if constexpr (DK == 256) {
-    launch_bwd_dq_pipe(a, CAP, stream);   // fa_bwd_pipe.hip
+  if constexpr (DK == 256 || (DK == 128 && DV == 128 && BWD_DQ_PIPE128)) {
+    launch_bwd_dq_pipe(a, DK, CAP, stream);   // fa_bwd_pipe.hip
   } else {
     const int nqb = (a.T + 32 * DQ_NW - 1) / (32 * DQ_NW);
     hipLaunchKernelGGL((fa_bwd_dq_kernel<DK, DV, DQ_BKV, DQ_NW, CAP>), dim3((unsigned)nqb * a.B * a.H),

@@ -2,7 +2,8 @@
 // gfx950 (bf16 in, fp32 accumulate), one wave per SIMD, with the same
 // gradients as the kernels in fa_bwd.hip (dS = P (dP - D) and, under a
 // softcap, the factor 1 - tanh^2):
-//   fa_bwd_dq_pipe_kernel -- the d = 256 dQ pass (dq = scale dS K);
+//   fa_bwd_dq_pipe_kernel -- the dQ pass (dq = scale dS K) at d = 256 (one
+//                            wave per SIMD) and d = 128 (two);
 //   fa_bwd_kv_pipe_kernel -- the d = 128 dK/dV pass (dk = scale dS^T Q,
 //                            dv = P^T dO), in place of the paired-wave one.
 // They live in a file of their own because it is compiled with the VGPR form
@@ -16,10 +17,11 @@
 
 namespace fa {
 
-// Head size 256, dQ pass, software-pipelined like the d = 256 forward: one
-// wave per 32 query rows holds the whole q and dO rows (128 VGPRs), dQ lives
-// in the accumulation registers, and per 32-key unit i three MFMA blocks run,
-// each carrying the VALU of another unit:
+// dQ pass (head size 128 or 256), software-pipelined like the d = 256
+// forward: one wave per 32 query rows holds the whole q and dO rows (D / 2
+// VGPRs), dQ lives in the accumulation registers, and per 32-key unit i three
+// MFMA blocks run, each carrying the VALU of another unit (a unit's 16 score
+// elements spread over a block's MFMAs):
 //   S(i+1)  = K(i+1) Q^T        carrying  dS(i) = f(i) (dP(i) - D), bf16 pack
 //   dQ^T   += K(i)^T dS(i)^T    carrying  the cap's tanh and the mask of S(i+1)
 //   dP(i+1) = V(i+1) dO^T - D   carrying  f(i+1) = P (1 - tanh^2) (P without a cap)
@@ -29,15 +31,25 @@ namespace fa {
 // barrier per unit.  Units of the workgroup's key range outside a wave's band
 // are computed fully masked (exact zeros), so every wave runs the same
 // straight-line schedule.  Also writes D_i for the dK/dV pass.
-template <bool CAP>
-__global__ __launch_bounds__(256, 1) void fa_bwd_dq_pipe_kernel(BwdArgs a) {
-  constexpr int D = 256, NW = 4, BQ = 32 * NW, BKV = 32;
+//
+// Waves per SIMD of the d = 128 dQ pass (its working set fits two; one is
+// slower, measured)
+#ifndef DQP128_OCC
+#define DQP128_OCC 2
+#endif
+template <int D, bool CAP>
+__global__ __launch_bounds__(256, D >= 256 ? 1 : DQP128_OCC) void fa_bwd_dq_pipe_kernel(BwdArgs a) {
+  constexpr int NW = 4, BQ = 32 * NW, BKV = 32;
   // a tile image, rounded up to whole rounds of the loaders' 1 KB pieces
   constexpr int TILE = TileDma<D, BKV, NW>::IMG;
   constexpr int NC = D / 16;     // chunks of the S and dP contractions
   constexpr int NDB = D / 32;    // 32-wide blocks of dq
   constexpr int NQ = 2 * NDB;    // MFMAs of the dQ block
   constexpr int PD = 2;
+  // each block has NC = NQ MFMAs; the hooks of a block cover a unit's 16
+  // score elements, EPB after each MFMA
+  constexpr int EPB = 16 / NC;
+  static_assert(NC == NQ && EPB * NC == 16, "16 elements over the MFMAs of a block");
   __shared__ __attribute__((aligned(1024))) char kt0[TILE];
   __shared__ __attribute__((aligned(1024))) char kt1[TILE];
   __shared__ __attribute__((aligned(1024))) char kt2[TILE];
@@ -223,7 +235,9 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_dq_pipe_kernel(BwdArgs a) {
   using MF = std::false_type;
   s_block(I0{}, kbuf(I0{}), [&](int) {});
   part_a(I0{}, MT{}, 0, 0, 16);
-  dp_block(I0{}, vbuf(I0{}), [&](int k) __attribute__((always_inline)) { part_b(I0{}, k, k + 1); });
+  dp_block(I0{}, vbuf(I0{}), [&](int k) __attribute__((always_inline)) {
+    part_b(I0{}, EPB * k, EPB * k + EPB);
+  });
 
   // iteration i (buffer slots: K(i) in B0, K(i+1) and V(i+1) in B1, loads
   // into B2; unit parities X for unit i, 1 - X for unit i + 1).  The unit
@@ -242,16 +256,18 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_dq_pipe_kernel(BwdArgs a) {
     using XN = std::integral_constant<int, 1 - decltype(x_c)::value>;
     lo.refresh();
     s_block(XN{}, kbuf(b1), [&](int k) __attribute__((always_inline)) {
-      part_c(x_c, k, k + 1);
+      part_c(x_c, EPB * k, EPB * k + EPB);
       if (k < PER)
         dm.load_piece(k, Kp, T * D * 2, kbuf(b2), (t_lo + i + 2) * BKV, wave);
       else if (k < 2 * PER)
         dm.load_piece(k - PER, Vp, T * D * 2, vbuf(b2), (t_lo + i + 2) * BKV, wave);
     });
     q_block(kbuf(b0), [&](int k) __attribute__((always_inline)) {
-      part_a(XN{}, mask_c, i + 1, k, k + 1);
+      part_a(XN{}, mask_c, i + 1, EPB * k, EPB * k + EPB);
     });
-    dp_block(XN{}, vbuf(b1), [&](int k) __attribute__((always_inline)) { part_b(XN{}, k, k + 1); });
+    dp_block(XN{}, vbuf(b1), [&](int k) __attribute__((always_inline)) {
+      part_b(XN{}, EPB * k, EPB * k + EPB);
+    });
     wait_vmem();
     __syncthreads();
   };
@@ -678,14 +694,21 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_kv_pipe_kernel(BwdArgs a) {
   }
 }
 
-hipError_t launch_bwd_dq_pipe(const BwdArgs& a, bool cap, hipStream_t stream) {
+template <int D>
+static hipError_t launch_dq_pipe_d(const BwdArgs& a, bool cap, hipStream_t stream) {
   const int nqb = (a.T + 127) / 128;
   const dim3 grid((unsigned)nqb * a.B * a.H);
   if (cap)
-    hipLaunchKernelGGL(fa_bwd_dq_pipe_kernel<true>, grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((fa_bwd_dq_pipe_kernel<D, true>), grid, dim3(256), 0, stream, a);
   else
-    hipLaunchKernelGGL(fa_bwd_dq_pipe_kernel<false>, grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((fa_bwd_dq_pipe_kernel<D, false>), grid, dim3(256), 0, stream, a);
   return hipGetLastError();
+}
+
+hipError_t launch_bwd_dq_pipe(const BwdArgs& a, int d, bool cap, hipStream_t stream) {
+  if (d == 128) return launch_dq_pipe_d<128>(a, cap, stream);
+  if (d == 256) return launch_dq_pipe_d<256>(a, cap, stream);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_bwd_kv_pipe(const BwdArgs& a, bool cap, hipStream_t stream) {

@@ -112,8 +112,9 @@ hipError_t launch_fill_f32(float* p, int n, float v, hipStream_t stream);
 // x in {64, 128, 256} and (192, 128)).
 hipError_t launch_fwd_bf16(const FwdArgs& a, int d, int d_v, hipStream_t stream);
 hipError_t launch_bwd_bf16(const BwdArgs& a, int d, int d_v, hipStream_t stream);
-// the d = 256 dQ pass (fa_bwd_pipe.hip), launched by launch_bwd_bf16
-hipError_t launch_bwd_dq_pipe(const BwdArgs& a, bool cap, hipStream_t stream);
+// the software-pipelined dQ pass (fa_bwd_pipe.hip) for d = d_v = 128 or 256,
+// launched by launch_bwd_bf16
+hipError_t launch_bwd_dq_pipe(const BwdArgs& a, int d, bool cap, hipStream_t stream);
 // the d = 128 dK/dV pass (fa_bwd_pipe.hip), launched by launch_bwd_bf16
 hipError_t launch_bwd_kv_pipe(const BwdArgs& a, bool cap, hipStream_t stream);
 // kernels launch_bwd_bf16 runs for (d, d_v), in order ("dq,dkdv"); null for
