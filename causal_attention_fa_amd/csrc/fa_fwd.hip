@@ -21,6 +21,9 @@
 //   * tiles entirely outside a wave's causal/window band are skipped, tiles
 //     entirely inside are not masked; only diagonal and window-edge tiles
 //     evaluate the mask.
+// Head size 128 runs fa_fwd_sp_kernel, the same structure software-pipelined
+// across tiles (the next tile's scores computed under this tile's softmax);
+// head size 256 runs fa_fwd_pipe_kernel.
 #include <type_traits>
 
 #include "device_common.h"
@@ -36,6 +39,15 @@ namespace fa {
 #endif
 #ifndef FWD_PIPE_PD
 #define FWD_PIPE_PD 2
+#endif
+// fa_fwd_sp_kernel: operand reads this many MFMAs ahead (3: no faster), and
+// the first O-block MFMA whose hook starts the next tile's exponentials
+// (the hooks before it take the next tile's cap, mask and max)
+#ifndef FWD_SP_PD
+#define FWD_SP_PD 2
+#endif
+#ifndef SP_KE0
+#define SP_KE0 8
 #endif
 
 // One wave owns 32 query rows.  DK is the head size of q and k, DV that of
@@ -341,6 +353,364 @@ __global__ __launch_bounds__(64 * NW, (MINWG > 0 ? MINWG : DK >= 256 ? 1 : 8 / N
   if (qrow < T) {
     const float inv = 1.f / ltot;
     bf16* Op = a.o + (bh * T + qrow) * DV;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        bf16x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = (bf16)(oacc[db][4 * i4 + e] * inv);
+        *(bf16x4*)(Op + 32 * db + 8 * i4 + 4 * g) = v;
+      }
+    if (g == 0) a.lse[bh * T + qrow] = (m + __log2f(ltot)) * kLn2;
+  }
+}
+
+// Head size 128, software-pipelined across 64-key tiles at two waves per
+// SIMD.  Each wave owns 32 query rows as in fa_fwd_kernel; per tile j it
+// issues the score block of the next tile before the O block of this one,
+// and puts under each the softmax VALU that does not wait for it:
+//   S(j+1) = K(j+1) Q^T (16 MFMAs)    carrying  exp2, row sum and bf16 packs of
+//                                              P(j)'s keys 32..63, and the tile
+//                                              loads of K(j+2) and V(j+1)
+//   O^T += V(j)^T P(j)^T (16 MFMAs)   carrying  cap, mask and row max of S(j+1),
+//                                              the rescale decision, and P(j+1)
+//                                              of its keys 0..31
+// The O rescale that tile j+1's max may need waits until the O block is done
+// (rare: the running max moves only past the slack).  K(j+1) and V(j) are read
+// in step j while K(j+2) and V(j+1) load, so both tiles are double-buffered,
+// one barrier per step.  Every wave walks the workgroup's whole key range:
+// tiles outside a wave's band are computed fully masked (exact zeros).
+// Tiles every row of the wave sees whole run in a mask-free segment.
+template <bool CAP>
+__global__ __launch_bounds__(256, 2) void fa_fwd_sp_kernel(FwdArgs a) {
+  constexpr int D = 128, NW = 4, BQ = 32 * NW, BKV = 64;
+  using Dma = TileDma<D, BKV, NW>;
+  constexpr int TILE = Dma::IMG;
+  constexpr int PER = Dma::PER;
+  constexpr int NC = D / 16;       // 16-wide chunks of the q.k contraction
+  constexpr int NDB = D / 32;      // 32-wide blocks of the output
+  constexpr int NSQ = 2 * NC;      // MFMAs of the score block (two 32-key halves)
+  constexpr int NPV = 4 * NDB;     // MFMAs of the O block (four 16-key chunks)
+  constexpr int PD = FWD_SP_PD;
+  static_assert(2 * PER <= NSQ, "one tile load per score MFMA");
+  __shared__ __attribute__((aligned(1024))) char kb0[TILE];
+  __shared__ __attribute__((aligned(1024))) char kb1[TILE];
+  __shared__ __attribute__((aligned(1024))) char vb0[TILE];
+  __shared__ __attribute__((aligned(1024))) char vb1[TILE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5;
+  const int T = a.T;
+  const int W = a.window;
+  const int G = a.H / a.Hkv;
+  const int nqb = (T + BQ - 1) / BQ;
+  const WorkItem w = decode_work(blockIdx.x, nqb, a.B, a.Hkv, G, true);
+  const int h = w.hkv * G + w.r;
+  const int q0 = w.blk * BQ;
+  const int qw0 = q0 + 32 * wave;
+  const int qrow = qw0 + (lane & 31);
+  const size_t bh = (size_t)w.b * a.H + h;
+  const size_t bkv = (size_t)w.b * a.Hkv + w.hkv;
+  const bf16* Kp = a.k + bkv * T * D;
+  const bf16* Vp = a.v + bkv * T * D;
+
+  // q as the B operand of S^T = K Q^T (RoPE fused into the load as in
+  // fa_fwd_kernel)
+  bf16x8 qreg[NC];
+  {
+    const int qr = min(qrow, T - 1);
+    const bf16x8* src = (const bf16x8*)(a.q + (bh * T + qr) * D + 8 * g);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) qreg[c] = src[2 * c];
+    if (a.rope_cs) {
+      const float4* cs4 = (const float4*)(a.rope_cs + (size_t)qr * D);
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        bf16x8 x = qreg[c];
+        const float4 r0 = cs4[(8 * c + 4 * g) / 2], r1 = cs4[(8 * c + 4 * g) / 2 + 1];
+        const float cv[4] = {r0.x, r0.z, r1.x, r1.z}, sv[4] = {r0.y, r0.w, r1.y, r1.w};
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          float xe = (float)x[2 * p], xo = (float)x[2 * p + 1];
+          rope_pair(cv[p], sv[p], xe, xo);
+          x[2 * p] = (bf16)xe;
+          x[2 * p + 1] = (bf16)xo;
+        }
+        qreg[c] = x;
+      }
+      if (a.q_rot && qrow < T) {
+        bf16x8* dst = (bf16x8*)(a.q_rot + (bh * T + qrow) * D + 8 * g);
+#pragma unroll
+        for (int c = 0; c < NC; ++c) dst[2 * c] = qreg[c];
+      }
+    }
+  }
+
+  int kv_lo = 0;
+  if (W > 0) kv_lo = max(0, q0 - W + 1);
+  const int t_lo = kv_lo / BKV;
+  const int kv_hi = min(T, q0 + BQ);
+  const int ntiles = (kv_hi + BKV - 1) / BKV - t_lo;
+
+  const bool has_sink = a.sinks != nullptr;
+  const float sink2 = has_sink ? a.sinks[h] * kLog2e : 0.f;
+  f32x16 oacc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
+  float m = has_sink ? sink2 : kMaxInit;
+  float lsum = (has_sink && g == 0) ? 1.f : 0.f;
+  float mxl = -INFINITY;
+  const float cexp = CAP ? a.cap_log2e : a.scale_log2e;
+  const bool want_max = a.max_logit != nullptr;
+
+  Dma dm;
+  dm.init(wave, lane);
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  auto kbuf = [&](auto p_c) -> LDS_AS char* {
+    return decltype(p_c)::value == 0 ? (LDS_AS char*)kb0 : (LDS_AS char*)kb1;
+  };
+  auto vbuf = [&](auto p_c) -> LDS_AS char* {
+    return decltype(p_c)::value == 0 ? (LDS_AS char*)vb0 : (LDS_AS char*)vb1;
+  };
+
+  f32x16 sn[2];   // S of the tile being prepared (two 32-key halves)
+  float mt;       // its row max (log2 units), mnew the running max it leads to
+  auto zero_s = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sn[t][i] = 0.f;
+  };
+  LaneOffs<D> lo;
+  lo.init(lane);
+  auto fK = [&](auto p_c) {
+    const LDS_AS char* kt = kbuf(p_c);
+    return [=, &lo](int k) { return lds_row_op<D>(kt, lo, k & 1, k >> 1); };
+  };
+  // cap and mask of the prepared tile's elements [e0, e1) of 32 (e = 16 t
+  // + i: half t, accumulator i), folded into its running max mt
+  // (key kv is visible to row qrow iff 0 <= qrow - kv < span)
+  const unsigned span = W > 0 ? (unsigned)W : 0x7fffffffu;
+  auto prep = [&](auto mask_c, int kv0, int e0, int e1) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_c)::value;
+    const int base = qrow - kv0 - 4 * g;   // qrow - kv = base - (32 t + 8 (i / 4) + i % 4)
+#pragma unroll
+    for (int e = e0; e < e1; ++e) {
+      const int t = e >> 4, i = e & 15;
+      float x = sn[t][i];
+      if (CAP) {
+        const float ex = fast_exp2(x * a.two_scale_over_cap_log2e);
+        x = 1.f - 2.f * __builtin_amdgcn_rcpf(ex + 1.f);
+      }
+      if (MASK) {
+        const bool vis = (unsigned)(base - (32 * t + 8 * (i >> 2) + (i & 3))) < span;
+        x = vis ? x : -INFINITY;
+      }
+      sn[t][i] = x;
+      mt = fmaxf(mt, x);
+    }
+  };
+  // the rescale decision for the prepared tile: the running max moves only
+  // when some row's tile max passes it by more than the slack
+  float mnew, alpha;
+  bool resc;
+  auto decide = [&]() __attribute__((always_inline)) {
+    mt = xor32_max(mt) * cexp;
+    if (want_max) mxl = fmaxf(mxl, qrow < T ? mt : -INFINITY);
+    resc = __any(mt > m + kRescaleSlack);
+    mnew = resc ? fmaxf(m, mt) : m;
+    alpha = fast_exp2(m - mnew);
+  };
+  // P = 2^(x c - mref) of one element, summed into ps
+  auto pexp = [&](float x, float mref, float& ps) __attribute__((always_inline)) {
+    const float p = fast_exp2(fmaf(x, cexp, -mref));
+    ps += p;
+    return p;
+  };
+  // element e (0 .. 15) of a 16-key chunk pair, packed to bf16 as each pair
+  // of elements completes (two bf16 per register: no eight-float staging);
+  // the chunk's operand is out[e / 8] once element 8 k + 7 is in
+  struct Packer {
+    float prev;
+    uint32_t wd[4];
+    __device__ __forceinline__ void put(int e, float p, bf16x8 (&out)[2]) {
+      if ((e & 1) == 0) {
+        prev = p;
+        return;
+      }
+      typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+      const bf16x2 v = {(bf16)prev, (bf16)p};
+      wd[(e & 7) >> 1] = __builtin_bit_cast(uint32_t, v);
+      if ((e & 7) == 7) {
+        const u32x4 u = {wd[0], wd[1], wd[2], wd[3]};
+        out[e >> 3] = __builtin_bit_cast(bf16x8, u);
+      }
+    }
+  };
+
+  // prologue: K(0), V(0), K(1) resident; tile 0's scores, max and the P of
+  // its keys 0..31
+  dm.load(Kp, T * D * 2, kbuf(I0{}), t_lo * BKV, wave);
+  dm.load(Vp, T * D * 2, vbuf(I0{}), t_lo * BKV, wave);
+  dm.load(Kp, ntiles > 1 ? T * D * 2 : 0, kbuf(I1{}), (t_lo + 1) * BKV, wave);
+  wait_vmem();
+  __syncthreads();
+  bf16x8 pa[2];          // P of the current tile's keys 0..31 (chunks 0, 1)
+  f32x16 sc;             // raw scores of its keys 32..63
+  float ps = 0.f;        // row sum of its P so far
+  {
+    zero_s();
+    auto f = fK(I0{});
+    MfmaSeq<NSQ, PD> sq;
+    sq.start(f);
+    sq.run(f, [&](int k) { return qreg[k >> 1]; }, [&](int k) -> f32x16& { return sn[k & 1]; },
+           [](int) {});
+    mt = -INFINITY;
+    prep(std::true_type{}, t_lo * BKV, 0, 32);
+    decide();
+    if (resc) lsum *= alpha;   // O is still zero
+    m = mnew;
+    Packer pk;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) pk.put(e, pexp(sn[0][e], m, ps), pa);
+    sc = sn[1];
+  }
+  lds_barrier();   // every wave is done with K(0) before K(2) loads into its buffer
+
+  // step j (buffers by parity P = j % 2: K(j+1) in kbuf(1-P), V(j) in
+  // vbuf(P); K(j+2) loads into kbuf(P), V(j+1) into vbuf(1-P)).  LAST: the
+  // final tile (no next tile: its keys 32..63 go under the O block's first
+  // half instead).
+  auto step = [&](auto p_c, auto mask_c, auto last_c, const int j) __attribute__((always_inline)) {
+    constexpr int P = decltype(p_c)::value;
+    constexpr bool LAST = decltype(last_c)::value;
+    using PN = std::integral_constant<int, 1 - P>;
+    lo.refresh();
+    bf16x8 pb2[2];   // P of keys 32..63
+    Packer pk2;
+    auto pchunk_hi = [&](int e) __attribute__((always_inline)) {   // element e of 16
+      pk2.put(e, pexp(sc[e], m, ps), pb2);
+    };
+    auto fV = [&](int k) { return lds_tr_op<D>(vbuf(p_c), lo, k / NDB, k % NDB); };
+    MfmaSeq<NPV, PD> vq;
+    if constexpr (!LAST) {
+      const int n2 = j + 2 < ntiles ? T * D * 2 : 0;
+      const int row2 = (t_lo + j + 2) * BKV, row1 = (t_lo + j + 1) * BKV;
+      zero_s();
+      auto f = fK(PN{});
+      MfmaSeq<NSQ, PD> sq;
+      sq.start(f);
+      sq.run(f, [&](int k) { return qreg[k >> 1]; }, [&](int k) -> f32x16& { return sn[k & 1]; },
+             [&](int k) __attribute__((always_inline)) {
+               pchunk_hi(k);
+               if (k < PER)
+                 dm.load_piece(k, Kp, n2, kbuf(p_c), row2, wave);
+               else if (k < 2 * PER)
+                 dm.load_piece(k - PER, Vp, T * D * 2, vbuf(PN{}), row1, wave);
+               if (k == NSQ - PD) vq.start(fV);
+             });
+    } else {
+      vq.start(fV);
+    }
+    // O^T += V(j)^T P(j)^T; under it, tile j+1's cap, mask, max and the P of
+    // its keys 0..31 (or, on the last tile, this tile's keys 32..63)
+    const int kv1 = (t_lo + j + 1) * BKV;
+    bf16x8 pn[2];
+    float psn = 0.f;
+    Packer pkn;
+    mt = -INFINITY;
+    vq.run(fV,
+           [&](int k) { return k < 8 ? pa[k >> 2] : pb2[(k >> 2) - 2]; },
+           [&](int k) -> f32x16& { return oacc[k % NDB]; },
+           [&](int k) __attribute__((always_inline)) {
+             if constexpr (LAST) {
+               if (k < 8) {
+                 pchunk_hi(2 * k);
+                 pchunk_hi(2 * k + 1);
+               }
+             } else {
+               if (k >= 1 && k <= 4) prep(mask_c, kv1, 8 * (k - 1), 8 * k);
+               if (k == 5) decide();
+               if (k >= SP_KE0) {
+                 // keys 0..31 (half 0), elements spread over hooks SP_KE0 .. 15
+                 constexpr int NH = 16 - SP_KE0;
+#pragma unroll
+                 for (int e = 16 * (k - SP_KE0) / NH; e < 16 * (k - SP_KE0 + 1) / NH; ++e)
+                   pkn.put(e, pexp(sn[0][e], mnew, psn), pn);
+               }
+             }
+           });
+    lsum += ps;
+    if constexpr (!LAST) {
+      if (resc) {
+        lsum *= alpha;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+      }
+      m = mnew;
+      ps = psn;
+      pa[0] = pn[0];
+      pa[1] = pn[1];
+      sc = sn[1];
+      wait_vmem();
+      lds_barrier();
+    }
+  };
+  // per-wave range of tiles every row sees whole: [tb, ta]
+  const int qa = qw0, qb = qw0 + 31;
+  const int ta = qa >= BKV - 1 ? (qa - (BKV - 1)) / BKV - t_lo : -1;
+  const int tb = (W > 0 && qb - W >= 0) ? (qb - W) / BKV + 1 - t_lo : 0;
+  // step j prepares tile j + 1: steps [ja, jb) carry no mask
+  const int jl = ntiles - 1;
+  const int ja = min(jl, max(0, tb - 1));
+  const int jb = min(jl, max(ja, ta));
+  using MT = std::true_type;
+  using MF = std::false_type;
+  int j = 0;
+  // a segment of steps [j, jend): unrolled by two so that every buffer is a
+  // compile-time choice (a run-time parity branch around the steps makes the
+  // compiler hold two copies of the state, and it spills), an odd first step
+  // peeled
+  auto run = [&](auto mask_c, const int jend) __attribute__((always_inline)) {
+    if ((j & 1) && j < jend) {
+      step(I1{}, mask_c, MF{}, j);
+      ++j;
+    }
+    for (; j + 1 < jend; j += 2) {
+      step(I0{}, mask_c, MF{}, j);
+      step(I1{}, mask_c, MF{}, j + 1);
+    }
+    if (j < jend) {
+      step(I0{}, mask_c, MF{}, j);
+      ++j;
+    }
+  };
+  run(MT{}, ja);
+  run(MF{}, jb);
+  run(MT{}, jl);
+  if (jl & 1)
+    step(I1{}, MT{}, MT{}, jl);
+  else
+    step(I0{}, MT{}, MT{}, jl);
+
+  if (want_max) {
+    float v = mxl;
+#pragma unroll
+    for (int off = 1; off < 32; off <<= 1) v = fmaxf(v, __shfl_xor(v, off));
+    if (lane == 0 && v > -INFINITY) atomic_max_f32(a.max_logit + bh, v * kLn2);
+  }
+  const float ltot = xor32_sum(lsum);
+  if (qrow < T) {
+    const float inv = 1.f / ltot;
+    bf16* Op = a.o + (bh * T + qrow) * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -777,11 +1147,30 @@ hipError_t launch_fill_f32(float* p, int n, float v, hipStream_t stream) {
   return hipGetLastError();
 }
 
+static hipError_t launch_fwd_sp(const FwdArgs& a, hipStream_t stream) {
+  const int nqb = (a.T + 127) / 128;
+  const dim3 grid((unsigned)nqb * a.B * a.H);
+  if (a.cap_log2e > 0.f)
+    hipLaunchKernelGGL(fa_fwd_sp_kernel<true>, grid, dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(fa_fwd_sp_kernel<false>, grid, dim3(256), 0, stream, a);
+  stage_mark(stream);
+  return hipGetLastError();
+}
+
+// d = 128 runs the software-pipelined two-wave kernel (mistral forward
+// 1.64 -> 1.59 ms, qwen25 0.329 -> 0.314 ms against fa_fwd_kernel)
+#ifndef FWD_SP128
+#define FWD_SP128 1
+#endif
+
 hipError_t launch_fwd_bf16(const FwdArgs& a, int d, int d_v, hipStream_t stream) {
   if (d == d_v) {
     switch (d) {
       case 64: return launch_fwd_d<64, 64, 64, 4>(a, stream);
-      case 128: return launch_fwd_d<128, 128, FWD128_CFG>(a, stream);
+      case 128:
+        if (FWD_SP128) return launch_fwd_sp(a, stream);
+        return launch_fwd_d<128, 128, FWD128_CFG>(a, stream);
       // one wave cannot hold q, the 256-wide O accumulator and a tile of
       // scores at two waves per SIMD: the software-pipelined kernel keeps
       // the matrix unit busy at one
