@@ -223,12 +223,13 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : DQP128_OCC) void fa_bwd_dq_pipe
 
   // prologue: K(0), V(0), K(1), V(1) resident; S(0), its cap and mask, dP(0)
   // with f(0)
+  // K(1) and V(1) load even past the last unit: the first step computes
+  // S(1) and dP(1) whatever nu is, and a masked P of 0 times stale LDS
+  // contents (possibly NaN) would not be 0; past T the range reads zeros
   dm.load(Kp, T * D * 2, kbuf(I0{}), t_lo * BKV, wave);
   dm.load(Vp, T * D * 2, vbuf(I0{}), t_lo * BKV, wave);
-  if (nu > 1) {
-    dm.load(Kp, T * D * 2, kbuf(I1{}), (t_lo + 1) * BKV, wave);
-    dm.load(Vp, T * D * 2, vbuf(I1{}), (t_lo + 1) * BKV, wave);
-  }
+  dm.load(Kp, T * D * 2, kbuf(I1{}), (t_lo + 1) * BKV, wave);
+  dm.load(Vp, T * D * 2, vbuf(I1{}), (t_lo + 1) * BKV, wave);
   wait_vmem();
   __syncthreads();
   using MT = std::true_type;
