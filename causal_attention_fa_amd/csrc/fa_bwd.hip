@@ -379,12 +379,13 @@ __global__ __launch_bounds__(64 * NW, (DK >= 192 ? 1 : 8 / NW)) void fa_bwd_dq_k
 #ifndef PAIR_BQB
 #define PAIR_BQB 64
 #endif
-// mask every tile (1) or only the tiles that cross the band's edges (0).
-// With one wave per SIMD (d = 256) nothing hides the per-tile branch and
-// the branch-free mask is faster (gemma dK/dV 1.20 -> 1.13 ms); with two,
-// skipping the mask on full tiles is (mistral dK/dV -3.5 %).
-#ifndef PAIR_MASK_FULL
-#define PAIR_MASK_FULL(DK) ((DK) == 256)
+// How the P side skips the mask on tiles that every pair of which its keys
+// see: with one wave per SIMD (d = 256) nothing hides a per-tile branch, so
+// the loop runs in segments of mask-free and masked groups of tiles
+// (PAIR_SEGMENTS); with two, a per-tile branch costs little (mistral dK/dV
+// -3.5 % against masking every tile).
+#ifndef PAIR_SEGMENTS
+#define PAIR_SEGMENTS(DK) ((DK) == 256)
 #endif
 // One launch for dK and dV, with paired waves: waves p and p + NP own the
 // same 32 key rows (NP = 4 pairs, 128 keys per workgroup; at d = 256 NP = 2
@@ -572,9 +573,12 @@ __global__ __launch_bounds__(BQB == 32 ? 256 : 512, 1) void fa_bwd_dkdv_pair_ker
   // the MFMAs of half 1), then dV^T += dO^T P over the 16-query chunks (exp of
   // half 1 under the MFMAs of chunks 0-1); P and the exchange factor are
   // packed per chunk as soon as its eight elements exist.
+  // mask_c: 1 evaluate the mask, 0 none (a tile every pair of which the
+  // wave's keys see), 2 decide per tile
   auto p_tile = [&](const LDS_AS char* Qt, const LDS_AS char* dOt, LDS_AS char* X,
                     const LDS_AS float* lse2t, const int q0, const LaneOffs<DK>& lq,
-                    const LaneOffs<DV>& lv_, auto&& ld) __attribute__((always_inline)) {
+                    const LaneOffs<DV>& lv_, auto mask_c, auto&& ld) __attribute__((always_inline)) {
+    constexpr int MSK = decltype(mask_c)::value;
     const int vb = q0 + 4 * g - krow;   // q - krow = vb + 32t + 8(i/4) + i%4
     // every pair of the tile visible to every key of the wave: no mask
     const bool full = q0 >= kb && q0 + BQB <= T && (W == 0 || q0 + BQB - 1 - ka < W);
@@ -597,7 +601,7 @@ __global__ __launch_bounds__(BQB == 32 ? 256 : 512, 1) void fa_bwd_dkdv_pair_ker
     auto elem = [&](int t, int i) __attribute__((always_inline)) {
       float th;
       float p = fast_exp2(p_arg<CAP>(s[t][i], a, lv[t][i >> 2][i & 3], th));
-      if (PAIR_MASK_FULL(DK) || !full) {
+      if (MSK == 1 || (MSK == 2 && !full)) {
         const bool vis = (unsigned)(vb + 32 * t + 8 * (i >> 2) + (i & 3)) < span;
         p = vis ? p : 0.f;
       }
@@ -728,7 +732,7 @@ __global__ __launch_bounds__(BQB == 32 ? 256 : 512, 1) void fa_bwd_dkdv_pair_ker
   f32x16 dp[NS];        // dS side: dP of the previous tile
   // qc, qn, qp: Q / statistics slots of tiles it, it+1, it-1; oc, on: dO
   // slots of tiles it, it+1
-  auto step = [&](auto side_c, const int it, auto qc, auto qn, auto qp, auto oc, auto on)
+  auto step = [&](auto side_c, auto mask_c, const int it, auto qc, auto qn, auto qp, auto oc, auto on)
                   __attribute__((always_inline)) {
     constexpr bool PS = decltype(side_c)::value;
     const int xs = it & 1;   // exchange slot of tile it
@@ -776,12 +780,13 @@ __global__ __launch_bounds__(BQB == 32 ? 256 : 512, 1) void fa_bwd_dkdv_pair_ker
       const bool cur = it < niter && !empty_tile(tile_q0(tc));
       if constexpr (SPREAD) {
         if (cur)
-          p_tile(qbuf(qc), obuf(oc), xbuf(xs, xo), sbufp(qc), tile_q0(tc), lq, lv, ld);
+          p_tile(qbuf(qc), obuf(oc), xbuf(xs, xo), sbufp(qc), tile_q0(tc), lq, lv, mask_c, ld);
         else
           ld_all();
       } else {
         ld_all();
-        if (cur) p_tile(qbuf(qc), obuf(oc), xbuf(xs, xo), sbufp(qc), tile_q0(tc), lq, lv, no_ld);
+        if (cur)
+          p_tile(qbuf(qc), obuf(oc), xbuf(xs, xo), sbufp(qc), tile_q0(tc), lq, lv, mask_c, no_ld);
       }
     } else {
       const bool cur = it < niter && !empty_tile(tile_q0(tc));
@@ -820,26 +825,54 @@ __global__ __launch_bounds__(BQB == 32 ? 256 : 512, 1) void fa_bwd_dkdv_pair_ker
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
     if constexpr (OSL == 3) {
-      for (int it = 0; it <= niter; it += 3) {
-        step(side_c, it, I0{}, I1{}, I2{}, I0{}, I1{});
-        if (it + 1 > niter) break;
-        step(side_c, it + 1, I1{}, I2{}, I0{}, I1{}, I2{});
-        if (it + 2 > niter) break;
-        step(side_c, it + 2, I2{}, I0{}, I1{}, I2{}, I0{});
+      // iterations it .. it+2 (false: the last one, niter, was among them)
+      auto group = [&](auto mask_c, const int it) __attribute__((always_inline)) -> bool {
+        step(side_c, mask_c, it, I0{}, I1{}, I2{}, I0{}, I1{});
+        if (it + 1 > niter) return false;
+        step(side_c, mask_c, it + 1, I1{}, I2{}, I0{}, I1{}, I2{});
+        if (it + 2 > niter) return false;
+        step(side_c, mask_c, it + 2, I2{}, I0{}, I1{}, I2{}, I0{});
+        return it + 2 < niter;
+      };
+      using M0 = std::integral_constant<int, 0>;
+      using M1 = std::integral_constant<int, 1>;
+      using M2 = std::integral_constant<int, 2>;
+      if constexpr (decltype(side_c)::value && PAIR_SEGMENTS(DK)) {
+        // P side: groups of three tiles that every key of the wave sees whole
+        // (tiles [fl, fh) of each head) carry no mask; the rest evaluate it
+        const int fl = min(nqt, pr + 1);
+        const int t_end = T >= BQB ? (T - BQB) / BQB + 1 - qt_lo : 0;   // q0 + BQB <= T
+        const int fw = W > 0 ? (W >= BQB ? pr + (W - BQB) / BQB + 1 : fl) : nqt;
+        const int fh = max(fl, min(nqt, min(t_end, fw)));
+        const int ng = niter / 3 + 1;   // groups covering iterations 0 .. niter
+        int gi = 0;
+        bool go = true;
+        for (int hi = 0; hi < G && go; ++hi) {
+          const int u0 = hi * nqt + fl, u1 = hi * nqt + fh;   // mask-free tiles [u0, u1)
+          const int ga = min(ng, max(gi, (u0 + 2) / 3));        // 3 g >= u0
+          const int gb = min(ng, max(ga, u1 >= 3 ? (u1 - 3) / 3 + 1 : 0));   // 3 g + 2 < u1
+          for (; go && gi < ga; ++gi) go = group(M1{}, 3 * gi);
+          for (; go && gi < gb; ++gi) go = group(M0{}, 3 * gi);
+        }
+        for (; go && gi < ng; ++gi) go = group(M1{}, 3 * gi);
+      } else {
+        for (int it = 0; it <= niter; it += 3)
+          if (!group(M2{}, it)) break;
       }
     } else {
+      using M2 = std::integral_constant<int, 2>;
       for (int it = 0; it <= niter; it += 6) {
-        step(side_c, it, I0{}, I1{}, I2{}, I0{}, I1{});
+        step(side_c, M2{}, it, I0{}, I1{}, I2{}, I0{}, I1{});
         if (it + 1 > niter) break;
-        step(side_c, it + 1, I1{}, I2{}, I0{}, I1{}, I0{});
+        step(side_c, M2{}, it + 1, I1{}, I2{}, I0{}, I1{}, I0{});
         if (it + 2 > niter) break;
-        step(side_c, it + 2, I2{}, I0{}, I1{}, I0{}, I1{});
+        step(side_c, M2{}, it + 2, I2{}, I0{}, I1{}, I0{}, I1{});
         if (it + 3 > niter) break;
-        step(side_c, it + 3, I0{}, I1{}, I2{}, I1{}, I0{});
+        step(side_c, M2{}, it + 3, I0{}, I1{}, I2{}, I1{}, I0{});
         if (it + 4 > niter) break;
-        step(side_c, it + 4, I1{}, I2{}, I0{}, I0{}, I1{});
+        step(side_c, M2{}, it + 4, I1{}, I2{}, I0{}, I0{}, I1{});
         if (it + 5 > niter) break;
-        step(side_c, it + 5, I2{}, I0{}, I1{}, I1{}, I0{});
+        step(side_c, M2{}, it + 5, I2{}, I0{}, I1{}, I1{}, I0{});
       }
     }
     // this side's gradient rows: dV (P side) or scale * dK (dS side)
@@ -891,29 +924,30 @@ __global__ __launch_bounds__(BQB == 32 ? 256 : 512, 1) void fa_bwd_dkdv_pair_ker
 // the dQ pass, then the fused dK/dV pass
 template <int DK, int DV, bool CAP, int DQ_BKV, int DQ_NW>
 static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
+  hipError_t e;
   if constexpr (DK == 256 || (DK == 128 && DV == 128 && BWD_DQ_PIPE128)) {
-    launch_bwd_dq_pipe(a, DK, CAP, stream);   // fa_bwd_pipe.hip
+    e = launch_bwd_dq_pipe(a, DK, CAP, stream);   // fa_bwd_pipe.hip
   } else {
     const int nqb = (a.T + 32 * DQ_NW - 1) / (32 * DQ_NW);
     hipLaunchKernelGGL((fa_bwd_dq_kernel<DK, DV, DQ_BKV, DQ_NW, CAP>), dim3((unsigned)nqb * a.B * a.H),
                        dim3(64 * DQ_NW), 0, stream, a);
+    e = hipGetLastError();
   }
   stage_mark(stream);
-  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if constexpr (DK == 128 && DV == 128 && BWD_KV_PIPE128) {
-    launch_bwd_kv_pipe(a, CAP, stream);   // fa_bwd_pipe.hip
-    stage_mark(stream);
-    return hipGetLastError();
+    e = launch_bwd_kv_pipe(a, CAP, stream);   // fa_bwd_pipe.hip
+  } else {
+    constexpr int BQB = DK == 256 ? 32 : PAIR_BQB;
+    using SH = PairShape<DK, DV, BQB>;
+    constexpr int BKVB = 32 * SH::NP;
+    const dim3 grid((unsigned)((a.T + BKVB - 1) / BKVB) * a.B * a.Hkv);
+    hipLaunchKernelGGL((fa_bwd_dkdv_pair_kernel<DK, DV, BQB, CAP>), grid, dim3(64 * SH::NW), 0, stream,
+                       a);
+    e = hipGetLastError();
   }
-  constexpr int BQB = DK == 256 ? 32 : PAIR_BQB;
-  using SH = PairShape<DK, DV, BQB>;
-  constexpr int BKVB = 32 * SH::NP;
-  const dim3 grid((unsigned)((a.T + BKVB - 1) / BKVB) * a.B * a.Hkv);
-  hipLaunchKernelGGL((fa_bwd_dkdv_pair_kernel<DK, DV, BQB, CAP>), grid, dim3(64 * SH::NW), 0, stream,
-                     a);
   stage_mark(stream);
-  return hipGetLastError();
+  return e;
 }
 
 template <int DK, int DV, int DQ_BKV = 32, int DQ_NW = 4>

@@ -1169,8 +1169,11 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, int d, int d_v, hipStream_t stream)
     switch (d) {
       case 64: return launch_fwd_d<64, 64, 64, 4>(a, stream);
       case 128:
-        if (FWD_SP128) return launch_fwd_sp(a, stream);
+#if FWD_SP128
+        return launch_fwd_sp(a, stream);
+#else
         return launch_fwd_d<128, 128, FWD128_CFG>(a, stream);
+#endif
       // one wave cannot hold q, the 256-wide O accumulator and a tile of
       // scores at two waves per SIMD: the software-pipelined kernel keeps
       // the matrix unit busy at one
