@@ -84,6 +84,30 @@ def test_window_at_least_T_matches_causal_on_gpu():
         assert np.array_equal(a[n], b[n]) and np.array_equal(a[n], c[n]), n
 
 
+def test_single_unit_after_nan_lds():
+    """Workgroups whose key (or query) range is one unit still compute their
+    first step's next tiles; those must come from zero-filling loads, never
+    from stale LDS (a masked P of 0 times a NaN left there is NaN).  Each
+    one-unit shape runs before and after a pass over NaN K and V on every CU
+    (which leaves NaN tiles in LDS): the outputs must be finite and bitwise
+    identical (the kernels are deterministic; their accuracy on these shapes
+    is the parity cases' business)."""
+    for d in (128, 256):
+        shapes = [(T, _inputs(1, 2, 1, T, d, 1.0, "bf16", seed=12 + T)) for T in (2, 31)]
+        before = [run_gpu(*x, d ** -0.5, 0, 0.0) for _, x in shapes]
+        q, k, v, do = _inputs(1, 32, 8, 1024, d, 1.0, "bf16", seed=11)
+        k[:] = float("nan")
+        v[:] = float("nan")
+        say(f"[stale-lds] NaN pass d{d}")
+        run_gpu(q, k, v, do, d ** -0.5, 0, 0.0)
+        for (T, x), a in zip(shapes, before):
+            say(f"[stale-lds] T{T} d{d}")
+            b = run_gpu(*x, d ** -0.5, 0, 0.0)
+            for n in ("o", "lse", "dq", "dk", "dv"):
+                assert np.isfinite(b[n]).all(), f"{n} not finite (T={T}, d={d})"
+                assert np.array_equal(a[n], b[n]), f"{n} depends on LDS contents (T={T}, d={d})"
+
+
 def test_nan_input_propagates_not_hangs():
     q, k, v, do = _inputs(1, 2, 2, 130, 64, 1.0, "bf16", seed=6)
     q[0, 0, 100, 3] = float("nan")
