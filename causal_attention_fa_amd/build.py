@@ -40,7 +40,7 @@ CFLAGS = [
 # compiler then gives the score (and dP) MFMAs the AGPR form too and copies
 # every such tile back to the VGPRs for the softmax.
 FILE_FLAGS = {
-    "fa_bwd.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
+    "fa_bwd.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp", "-mllvm", "-amdgpu-mfma-vgpr-form"],
     "fa_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "fa_bwd_pipe.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp", "-mllvm", "-amdgpu-mfma-vgpr-form"],
 }

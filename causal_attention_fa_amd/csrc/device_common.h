@@ -374,6 +374,33 @@ struct MfmaSeq {
   }
 };
 
+// MfmaSeq with the accumulators pinned to the AGPRs (mfma32_agpr): for
+// kernels whose long-lived accumulators do not fit beside their working set
+// in the VGPRs.  B operands written by the VALU must not be produced by the
+// instruction right before the MFMA that reads them (the hook of an earlier
+// MFMA, or earlier still, writes them).
+template <int N, int PD>
+struct AgprSeq {
+  static constexpr int R = PD + 1;
+  bf16x8 op[R];
+  template <class Fetch>
+  __device__ __forceinline__ void start(Fetch&& fetch) {
+#pragma unroll
+    for (int k = 0; k < PD && k < N; ++k) op[k % R] = fetch(k);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  template <class Fetch, class BOp, class Acc, class Hook>
+  __device__ __forceinline__ void run(Fetch&& fetch, BOp&& bop, Acc&& acc, Hook&& hook) {
+#pragma unroll
+    for (int k = 0; k < N; ++k) {
+      if (k + PD < N) op[(k + PD) % R] = fetch(k + PD);
+      mfma32_agpr(acc(k), op[k % R], bop(k));
+      hook(k);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+};
+
 // acc[t] = sum_c A_t(c) B(c) over the D/16 chunks of d, where A_t(c) is
 // the row operand of rows 32t.. of `tile` (read from LDS) and B(c) = breg[c]
 // lives in registers: NS independent 32x32 accumulators.  The LDS operands

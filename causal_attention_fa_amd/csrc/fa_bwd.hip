@@ -387,6 +387,10 @@ __global__ __launch_bounds__(64 * NW, (DK >= 192 ? 1 : 8 / NW)) void fa_bwd_dq_k
 #ifndef PAIR_SEGMENTS
 #define PAIR_SEGMENTS(DK) ((DK) == 256)
 #endif
+// gradient accumulators in the AGPRs (one wave per SIMD, d = 256)
+#ifndef PAIR_AGPR
+#define PAIR_AGPR(DK) ((DK) == 256)
+#endif
 // One launch for dK and dV, with paired waves: waves p and p + NP own the
 // same 32 key rows (NP = 4 pairs, 128 keys per workgroup; at d = 256 NP = 2
 // and one wave per SIMD, see PairShape).  Wave p (the P side) keeps K in
@@ -439,6 +443,10 @@ __global__ __launch_bounds__(BQB == 32 ? 256 : 512, 1) void fa_bwd_dkdv_pair_ker
   constexpr int NKV = NCK > NCV ? NCK : NCV;
   constexpr int NACC = NDBK > NDBV ? NDBK : NDBV;
   static_assert(NS == 1 || NS == 2, "32 or 64 queries per tile");
+  // the gradient accumulator pinned to the AGPRs (the score and dP products
+  // then stay in the VGPRs, where the VALU reads them while the matrix unit
+  // works on the accumulator)
+  constexpr bool AG = PAIR_AGPR(DK);
   __shared__ __attribute__((aligned(1024))) char qs0[TILE_Q];
   __shared__ __attribute__((aligned(1024))) char qs1[TILE_Q];
   __shared__ __attribute__((aligned(1024))) char qs2[TILE_Q];
@@ -594,7 +602,7 @@ __global__ __launch_bounds__(BQB == 32 ? 256 : 512, 1) void fa_bwd_dkdv_pair_ker
     auto fV = [&](int k) { return lds_tr_op<DV>(dOt, lv_, k / NDBV, k % NDBV); };
     constexpr int NSQ = NS * NCK, NVQ = NC16 * NDBV;
     MfmaSeq<NSQ, PD> sq;
-    MfmaSeq<NVQ, PD> vq;
+    std::conditional_t<AG, AgprSeq<NVQ, PD>, MfmaSeq<NVQ, PD>> vq;
     sq.start(fS);
 #pragma unroll
     for (int i4 = 0; i4 < 4; ++i4) lv[0][i4] = *(const LDS_AS f32x4*)(lse2t + 8 * i4 + 4 * g);
@@ -647,10 +655,18 @@ __global__ __launch_bounds__(BQB == 32 ? 256 : 512, 1) void fa_bwd_dkdv_pair_ker
            });
     // the last half: with one half, its first chunk before the dV product
     // and the second under the MFMAs of the first
+    // (with the accumulator in the AGPRs the compiler does not separate a
+    // VALU write from the MFMA that reads it: the last chunk is packed two
+    // MFMAs before its first use, and a wait follows the first pack)
     constexpr int TL = NS - 1;
-    constexpr int NH = NS == 2 ? 2 * NDBV : NDBV;   // dV MFMAs that carry exp work
+    constexpr int NH = (NS == 2 ? 2 * NDBV : NDBV) - (AG ? 2 : 0);   // dV MFMAs that carry exp work
     constexpr int EH = NS == 2 ? 16 : 8;            // elements placed in them
     if constexpr (NS == 1) elems(0, 0, 8);
+    if constexpr (AG) {
+      // the packs stay above this point, two wait states before the MFMA
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("s_nop 1");
+    }
     vq.run(fV, [&](int k) { return pb[k / NDBV]; }, [&](int k) -> f32x16& { return acc[k % NDBV]; },
            [&](int k) __attribute__((always_inline)) {
              if (k < NH) {
@@ -677,7 +693,7 @@ __global__ __launch_bounds__(BQB == 32 ? 256 : 512, 1) void fa_bwd_dkdv_pair_ker
     load_chunk(1);
     auto fK = [&](int k) { return lds_tr_op<DK>(Qt, lq, k / NDBK, k % NDBK); };
     constexpr int NKQ = NC16 * NDBK;
-    MfmaSeq<NKQ, PD> kq;
+    std::conditional_t<AG, AgprSeq<NKQ, PD>, MfmaSeq<NKQ, PD>> kq;
     kq.start(fK);
     float td[NC16][8];
     bf16x8 dsb[NC16];
@@ -688,13 +704,20 @@ __global__ __launch_bounds__(BQB == 32 ? 256 : 512, 1) void fa_bwd_dkdv_pair_ker
     };
 #pragma unroll
     for (int jj = 0; jj < 8; ++jj) dsel(0, jj);
+    if constexpr (AG) {
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("s_nop 1");
+    }
+    // chunk c + 1 under chunk c's MFMAs (with AGPR accumulators, finished two
+    // MFMAs before its first use)
+    constexpr int NDS = NDBK - (AG ? 2 : 0);
     kq.run(fK, [&](int k) { return dsb[k / NDBK]; }, [&](int k) -> f32x16& { return acc[k % NDBK]; },
            [&](int k) __attribute__((always_inline)) {
              const int c = k / NDBK + 1;   // the chunk after this MFMA's
              if (k % NDBK == 0 && c + 1 < NC16) load_chunk(c + 1);
-             if (c < NC16) {
+             if (c < NC16 && k % NDBK < NDS) {
                int j0, j1;
-               span_of(8, NDBK, k % NDBK, j0, j1);
+               span_of(8, NDS, k % NDBK, j0, j1);
 #pragma unroll
                for (int jj = j0; jj < j1; ++jj) dsel(c, jj);
              }
@@ -732,13 +755,19 @@ __global__ __launch_bounds__(BQB == 32 ? 256 : 512, 1) void fa_bwd_dkdv_pair_ker
   f32x16 dp[NS];        // dS side: dP of the previous tile
   // qc, qn, qp: Q / statistics slots of tiles it, it+1, it-1; oc, on: dO
   // slots of tiles it, it+1
-  auto step = [&](auto side_c, auto mask_c, const int it, auto qc, auto qn, auto qp, auto oc, auto on)
-                  __attribute__((always_inline)) {
+  // first_c: the first step (it = 0; the dS side has no previous tile)
+  auto step = [&](auto side_c, auto mask_c, auto first_c, const int it, auto qc, auto qn, auto qp,
+                  auto oc, auto on) __attribute__((always_inline)) {
     constexpr bool PS = decltype(side_c)::value;
+    constexpr bool FIRST = decltype(first_c)::value;
     const int xs = it & 1;   // exchange slot of tile it
     const bool more = it + 1 < niter;
     float sv = 0.f;
     if (more) sv = stage_stats(h1, t1);
+    // with AGPR accumulators every step runs both products (a branch around
+    // them makes the compiler copy the accumulator at the join): the tile
+    // past the range (zero Q and dO) gets lse = +inf and D = 0, so its P is 0
+    if (AG && !more) sv = tid < BQB ? INFINITY : 0.f;
     // Tile it+1's Q and dO loads go out one after each MFMA of this step's
     // first product (a burst of them stalls the wave until the memory
     // pipeline has taken them), branch-free: with no tile it+1 they read an
@@ -776,7 +805,25 @@ __global__ __launch_bounds__(BQB == 32 ? 256 : 512, 1) void fa_bwd_dkdv_pair_ker
     const LaneOffs<DK>& lq = lq0;
     const LaneOffs<DV>& lv = lv0;
     const int xo = xo0;
-    if constexpr (PS) {
+    if constexpr (PS && AG) {
+      // tiles outside the band are computed fully masked (they are in the
+      // masked segments): exact zeros
+      ld_all();
+      p_tile(qbuf(qc), obuf(oc), xbuf(xs, xo), sbufp(qc), tile_q0(tc), lq, lv, mask_c, no_ld);
+    } else if constexpr (!PS && AG) {
+      auto fP = [&](int k) { return lds_row_op<DV>(obuf(oc), lv, k % NS, k / NS); };
+      MfmaSeq<NS * NCV, PD> pq;
+      if constexpr (!SPREAD) ld_all();
+      if constexpr (!FIRST) {
+        if constexpr (SPREAD)
+          ds_prev(dp, qbuf(qp), xbuf(xs ^ 1, xo), sbufp(qp) + BQB, lq, [&]() { pq.start(fP); }, ld);
+        else
+          ds_prev(dp, qbuf(qp), xbuf(xs ^ 1, xo), sbufp(qp) + BQB, lq, [&]() { pq.start(fP); }, no_ld);
+      } else if constexpr (SPREAD) {
+        ld_all();
+      }
+      dp_cur(dp, pq, fP, !FIRST, sbufp(qc) + BQB, no_ld);
+    } else if constexpr (PS) {
       const bool cur = it < niter && !empty_tile(tile_q0(tc));
       if constexpr (SPREAD) {
         if (cur)
@@ -811,7 +858,7 @@ __global__ __launch_bounds__(BQB == 32 ? 256 : 512, 1) void fa_bwd_dkdv_pair_ker
       }
       if (cur) dp_cur(dp, pq, fP, started, sbufp(qc) + BQB, no_ld);
     }
-    if (more && wave < 2 * BQB / 64) sbufp(qn)[tid] = stat_val(sv);
+    if ((AG || more) && wave < 2 * BQB / 64) sbufp(qn)[tid] = stat_val(sv);
     wait_vmem();
     __syncthreads();
     tp = tc;
@@ -825,57 +872,90 @@ __global__ __launch_bounds__(BQB == 32 ? 256 : 512, 1) void fa_bwd_dkdv_pair_ker
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
     if constexpr (OSL == 3) {
-      // iterations it .. it+2 (false: the last one, niter, was among them)
-      auto group = [&](auto mask_c, const int it) __attribute__((always_inline)) -> bool {
-        step(side_c, mask_c, it, I0{}, I1{}, I2{}, I0{}, I1{});
+      // iterations it .. it+2 (false: the last one, niter, was among them);
+      // first_c marks the group of iteration 0
+      using TF = std::true_type;
+      using FF = std::false_type;
+      auto group = [&](auto mask_c, auto first_c, const int it) __attribute__((always_inline)) -> bool {
+        step(side_c, mask_c, first_c, it, I0{}, I1{}, I2{}, I0{}, I1{});
         if (it + 1 > niter) return false;
-        step(side_c, mask_c, it + 1, I1{}, I2{}, I0{}, I1{}, I2{});
+        step(side_c, mask_c, FF{}, it + 1, I1{}, I2{}, I0{}, I1{}, I2{});
         if (it + 2 > niter) return false;
-        step(side_c, mask_c, it + 2, I2{}, I0{}, I1{}, I2{}, I0{});
+        step(side_c, mask_c, FF{}, it + 2, I2{}, I0{}, I1{}, I2{}, I0{});
         return it + 2 < niter;
       };
       using M0 = std::integral_constant<int, 0>;
       using M1 = std::integral_constant<int, 1>;
       using M2 = std::integral_constant<int, 2>;
-      if constexpr (decltype(side_c)::value && PAIR_SEGMENTS(DK)) {
+      if constexpr (AG) {
+        // whole groups of three, no exit inside one (each exit is a point
+        // where the accumulator would have to sit in its final registers):
+        // the iterations past niter see tiles past the range, zero tiles
+        // with P = 0, and add exact zeros
+        auto group3 = [&](auto mask_c, auto first_c, const int it) __attribute__((always_inline)) {
+          step(side_c, mask_c, first_c, it, I0{}, I1{}, I2{}, I0{}, I1{});
+          step(side_c, mask_c, FF{}, it + 1, I1{}, I2{}, I0{}, I1{}, I2{});
+          step(side_c, mask_c, FF{}, it + 2, I2{}, I0{}, I1{}, I2{}, I0{});
+        };
+        const int ng = niter / 3 + 1;   // groups covering iterations 0 .. niter
+        group3(M1{}, TF{}, 0);          // holds the wave's diagonal tile: masked
+        int gi = 1;
+        if constexpr (decltype(side_c)::value && PAIR_SEGMENTS(DK)) {
+          const int fl = min(nqt, pr + 1);
+          const int t_end = T >= BQB ? (T - BQB) / BQB + 1 - qt_lo : 0;   // q0 + BQB <= T
+          const int fw = W > 0 ? (W >= BQB ? pr + (W - BQB) / BQB + 1 : fl) : nqt;
+          const int fh = max(fl, min(nqt, min(t_end, fw)));
+          for (int hi = 0; hi < G; ++hi) {
+            const int u0 = hi * nqt + fl, u1 = hi * nqt + fh;   // mask-free tiles [u0, u1)
+            const int ga = min(ng, max(gi, (u0 + 2) / 3));        // 3 g >= u0
+            const int gb = min(ng, max(ga, u1 >= 3 ? (u1 - 3) / 3 + 1 : 0));   // 3 g + 2 < u1
+            for (; gi < ga; ++gi) group3(M1{}, FF{}, 3 * gi);
+            for (; gi < gb; ++gi) group3(M0{}, FF{}, 3 * gi);
+          }
+        }
+        for (; gi < ng; ++gi) group3(M1{}, FF{}, 3 * gi);
+      } else if constexpr (decltype(side_c)::value && PAIR_SEGMENTS(DK)) {
         // P side: groups of three tiles that every key of the wave sees whole
-        // (tiles [fl, fh) of each head) carry no mask; the rest evaluate it
+        // (tiles [fl, fh) of each head) carry no mask; the rest evaluate it.
+        // Group 0 holds the wave's diagonal tile (fl >= 1): always masked.
         const int fl = min(nqt, pr + 1);
         const int t_end = T >= BQB ? (T - BQB) / BQB + 1 - qt_lo : 0;   // q0 + BQB <= T
         const int fw = W > 0 ? (W >= BQB ? pr + (W - BQB) / BQB + 1 : fl) : nqt;
         const int fh = max(fl, min(nqt, min(t_end, fw)));
         const int ng = niter / 3 + 1;   // groups covering iterations 0 .. niter
-        int gi = 0;
-        bool go = true;
+        int gi = 1;
+        bool go = group(M1{}, TF{}, 0);
         for (int hi = 0; hi < G && go; ++hi) {
           const int u0 = hi * nqt + fl, u1 = hi * nqt + fh;   // mask-free tiles [u0, u1)
           const int ga = min(ng, max(gi, (u0 + 2) / 3));        // 3 g >= u0
           const int gb = min(ng, max(ga, u1 >= 3 ? (u1 - 3) / 3 + 1 : 0));   // 3 g + 2 < u1
-          for (; go && gi < ga; ++gi) go = group(M1{}, 3 * gi);
-          for (; go && gi < gb; ++gi) go = group(M0{}, 3 * gi);
+          for (; go && gi < ga; ++gi) go = group(M1{}, FF{}, 3 * gi);
+          for (; go && gi < gb; ++gi) go = group(M0{}, FF{}, 3 * gi);
         }
-        for (; go && gi < ng; ++gi) go = group(M1{}, 3 * gi);
+        for (; go && gi < ng; ++gi) go = group(M1{}, FF{}, 3 * gi);
       } else {
-        for (int it = 0; it <= niter; it += 3)
-          if (!group(M2{}, it)) break;
+        if (group(M2{}, TF{}, 0))
+          for (int it = 3; it <= niter; it += 3)
+            if (!group(M2{}, FF{}, it)) break;
       }
     } else {
       using M2 = std::integral_constant<int, 2>;
       for (int it = 0; it <= niter; it += 6) {
-        step(side_c, M2{}, it, I0{}, I1{}, I2{}, I0{}, I1{});
+        step(side_c, M2{}, std::false_type{}, it, I0{}, I1{}, I2{}, I0{}, I1{});
         if (it + 1 > niter) break;
-        step(side_c, M2{}, it + 1, I1{}, I2{}, I0{}, I1{}, I0{});
+        step(side_c, M2{}, std::false_type{}, it + 1, I1{}, I2{}, I0{}, I1{}, I0{});
         if (it + 2 > niter) break;
-        step(side_c, M2{}, it + 2, I2{}, I0{}, I1{}, I0{}, I1{});
+        step(side_c, M2{}, std::false_type{}, it + 2, I2{}, I0{}, I1{}, I0{}, I1{});
         if (it + 3 > niter) break;
-        step(side_c, M2{}, it + 3, I0{}, I1{}, I2{}, I1{}, I0{});
+        step(side_c, M2{}, std::false_type{}, it + 3, I0{}, I1{}, I2{}, I1{}, I0{});
         if (it + 4 > niter) break;
-        step(side_c, M2{}, it + 4, I1{}, I2{}, I0{}, I0{}, I1{});
+        step(side_c, M2{}, std::false_type{}, it + 4, I1{}, I2{}, I0{}, I0{}, I1{});
         if (it + 5 > niter) break;
-        step(side_c, M2{}, it + 5, I2{}, I0{}, I1{}, I1{}, I0{});
+        step(side_c, M2{}, std::false_type{}, it + 5, I2{}, I0{}, I1{}, I1{}, I0{});
       }
     }
     // this side's gradient rows: dV (P side) or scale * dK (dS side)
+    if constexpr (AG) agpr_acc_fence(acc);
     if (krow < T) {
       constexpr bool PS = decltype(side_c)::value;
       constexpr int DD = PS ? DV : DK;

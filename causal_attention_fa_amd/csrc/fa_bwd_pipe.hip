@@ -338,33 +338,6 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : DQP128_OCC) void fa_bwd_dq_pipe
 // the workgroup's query range outside a wave's band are computed fully
 // masked (exact zeros), so every wave runs the same schedule; units every
 // row of which sees all 32 keys carry no mask.
-// MfmaSeq with the accumulators pinned to the AGPRs (mfma32_agpr): for
-// kernels whose long-lived accumulators do not fit beside their working set
-// in the VGPRs.  B operands written by the VALU must not be produced by the
-// instruction right before the MFMA that reads them (the hook of an earlier
-// MFMA, or earlier still, writes them).
-template <int N, int PD>
-struct AgprSeq {
-  static constexpr int R = PD + 1;
-  bf16x8 op[R];
-  template <class Fetch>
-  __device__ __forceinline__ void start(Fetch&& fetch) {
-#pragma unroll
-    for (int k = 0; k < PD && k < N; ++k) op[k % R] = fetch(k);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  template <class Fetch, class BOp, class Acc, class Hook>
-  __device__ __forceinline__ void run(Fetch&& fetch, BOp&& bop, Acc&& acc, Hook&& hook) {
-#pragma unroll
-    for (int k = 0; k < N; ++k) {
-      if (k + PD < N) op[(k + PD) % R] = fetch(k + PD);
-      mfma32_agpr(acc(k), op[k % R], bop(k));
-      hook(k);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  }
-};
-
 template <bool CAP>
 __global__ __launch_bounds__(256, 1) void fa_bwd_kv_pipe_kernel(BwdArgs a) {
   constexpr int D = 128, NW = 4, BQ = 32, BKVB = 32 * NW;
