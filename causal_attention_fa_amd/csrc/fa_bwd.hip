@@ -391,6 +391,10 @@ __global__ __launch_bounds__(64 * NW, (DK >= 192 ? 1 : 8 / NW)) void fa_bwd_dq_k
 #ifndef PAIR_AGPR
 #define PAIR_AGPR(DK) ((DK) == 256)
 #endif
+// with them, the P side's tile loads spread over its score MFMAs
+#ifndef PAIR_SPREAD_AG
+#define PAIR_SPREAD_AG 1
+#endif
 // One launch for dK and dV, with paired waves: waves p and p + NP own the
 // same 32 key rows (NP = 4 pairs, 128 keys per workgroup; at d = 256 NP = 2
 // and one wave per SIMD, see PairShape).  Wave p (the P side) keeps K in
@@ -795,7 +799,7 @@ __global__ __launch_bounds__(BQB == 32 ? 256 : 512, 1) void fa_bwd_dkdv_pair_ker
     auto no_ld = [](int) {};
     // where spreading them keeps the side spill-free (measured per shape);
     // elsewhere all at the top of the step
-    constexpr bool SPREAD = PS ? DK <= 128 : DK != 192;
+    constexpr bool SPREAD = PS ? (DK <= 128 || (AG && PAIR_SPREAD_AG)) : DK != 192;
     // lane offsets refreshed per step (in place): the buffer addresses
     // derived from them are formed here (one add per buffer) instead of
     // hoisted out of the loop, where those of all the buffers would stay live
@@ -808,8 +812,12 @@ __global__ __launch_bounds__(BQB == 32 ? 256 : 512, 1) void fa_bwd_dkdv_pair_ker
     if constexpr (PS && AG) {
       // tiles outside the band are computed fully masked (they are in the
       // masked segments): exact zeros
-      ld_all();
-      p_tile(qbuf(qc), obuf(oc), xbuf(xs, xo), sbufp(qc), tile_q0(tc), lq, lv, mask_c, no_ld);
+      if constexpr (SPREAD) {
+        p_tile(qbuf(qc), obuf(oc), xbuf(xs, xo), sbufp(qc), tile_q0(tc), lq, lv, mask_c, ld);
+      } else {
+        ld_all();
+        p_tile(qbuf(qc), obuf(oc), xbuf(xs, xo), sbufp(qc), tile_q0(tc), lq, lv, mask_c, no_ld);
+      }
     } else if constexpr (!PS && AG) {
       auto fP = [&](int k) { return lds_row_op<DV>(obuf(oc), lv, k % NS, k / NS); };
       MfmaSeq<NS * NCV, PD> pq;
