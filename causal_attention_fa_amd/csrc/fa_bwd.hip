@@ -379,22 +379,6 @@ __global__ __launch_bounds__(64 * NW, (DK >= 192 ? 1 : 8 / NW)) void fa_bwd_dq_k
 #ifndef PAIR_BQB
 #define PAIR_BQB 64
 #endif
-// How the P side skips the mask on tiles that every pair of which its keys
-// see: with one wave per SIMD (d = 256) nothing hides a per-tile branch, so
-// the loop runs in segments of mask-free and masked groups of tiles
-// (PAIR_SEGMENTS); with two, a per-tile branch costs little (mistral dK/dV
-// -3.5 % against masking every tile).
-#ifndef PAIR_SEGMENTS
-#define PAIR_SEGMENTS(DK) ((DK) == 256)
-#endif
-// gradient accumulators in the AGPRs (one wave per SIMD, d = 256)
-#ifndef PAIR_AGPR
-#define PAIR_AGPR(DK) ((DK) == 256)
-#endif
-// with them, the P side's tile loads spread over its score MFMAs
-#ifndef PAIR_SPREAD_AG
-#define PAIR_SPREAD_AG 1
-#endif
 // One launch for dK and dV, with paired waves: waves p and p + NP own the
 // same 32 key rows (NP = 4 pairs, 128 keys per workgroup; at d = 256 NP = 2
 // and one wave per SIMD, see PairShape).  Wave p (the P side) keeps K in
@@ -447,10 +431,16 @@ __global__ __launch_bounds__(BQB == 32 ? 256 : 512, 1) void fa_bwd_dkdv_pair_ker
   constexpr int NKV = NCK > NCV ? NCK : NCV;
   constexpr int NACC = NDBK > NDBV ? NDBK : NDBV;
   static_assert(NS == 1 || NS == 2, "32 or 64 queries per tile");
-  // the gradient accumulator pinned to the AGPRs (the score and dP products
-  // then stay in the VGPRs, where the VALU reads them while the matrix unit
-  // works on the accumulator)
-  constexpr bool AG = PAIR_AGPR(DK);
+  // At d = 256 (one wave per SIMD) the gradient accumulator is pinned to the
+  // AGPRs: the score and dP products then stay in the VGPRs, where the VALU
+  // reads them while the matrix unit works on the accumulator (with them in
+  // the AGPRs VALU and MFMA co-executed 3 % of the time; gemma-global dK/dV
+  // 1.37 -> 1.24 ms).  Its P side also skips the mask on tiles every pair of
+  // which its keys see by running segments of mask-free and masked tile
+  // groups (nothing hides a per-tile branch at one wave per SIMD; with two
+  // waves per SIMD a per-tile branch costs little: mistral -3.5 % against
+  // masking every tile).
+  constexpr bool AG = DK == 256;
   __shared__ __attribute__((aligned(1024))) char qs0[TILE_Q];
   __shared__ __attribute__((aligned(1024))) char qs1[TILE_Q];
   __shared__ __attribute__((aligned(1024))) char qs2[TILE_Q];
@@ -799,7 +789,7 @@ __global__ __launch_bounds__(BQB == 32 ? 256 : 512, 1) void fa_bwd_dkdv_pair_ker
     auto no_ld = [](int) {};
     // where spreading them keeps the side spill-free (measured per shape);
     // elsewhere all at the top of the step
-    constexpr bool SPREAD = PS ? (DK <= 128 || (AG && PAIR_SPREAD_AG)) : DK != 192;
+    constexpr bool SPREAD = PS ? (DK <= 128 || AG) : DK != 192;
     // lane offsets refreshed per step (in place): the buffer addresses
     // derived from them are formed here (one add per buffer) instead of
     // hoisted out of the loop, where those of all the buffers would stay live
@@ -908,7 +898,10 @@ __global__ __launch_bounds__(BQB == 32 ? 256 : 512, 1) void fa_bwd_dkdv_pair_ker
         const int ng = niter / 3 + 1;   // groups covering iterations 0 .. niter
         group3(M1{}, TF{}, 0);          // holds the wave's diagonal tile: masked
         int gi = 1;
-        if constexpr (decltype(side_c)::value && PAIR_SEGMENTS(DK)) {
+        if constexpr (decltype(side_c)::value) {
+          // P side: groups of three tiles that every key of the wave sees
+          // whole (tiles [fl, fh) of each head) carry no mask; the rest
+          // evaluate it
           const int fl = min(nqt, pr + 1);
           const int t_end = T >= BQB ? (T - BQB) / BQB + 1 - qt_lo : 0;   // q0 + BQB <= T
           const int fw = W > 0 ? (W >= BQB ? pr + (W - BQB) / BQB + 1 : fl) : nqt;
@@ -922,25 +915,6 @@ __global__ __launch_bounds__(BQB == 32 ? 256 : 512, 1) void fa_bwd_dkdv_pair_ker
           }
         }
         for (; gi < ng; ++gi) group3(M1{}, FF{}, 3 * gi);
-      } else if constexpr (decltype(side_c)::value && PAIR_SEGMENTS(DK)) {
-        // P side: groups of three tiles that every key of the wave sees whole
-        // (tiles [fl, fh) of each head) carry no mask; the rest evaluate it.
-        // Group 0 holds the wave's diagonal tile (fl >= 1): always masked.
-        const int fl = min(nqt, pr + 1);
-        const int t_end = T >= BQB ? (T - BQB) / BQB + 1 - qt_lo : 0;   // q0 + BQB <= T
-        const int fw = W > 0 ? (W >= BQB ? pr + (W - BQB) / BQB + 1 : fl) : nqt;
-        const int fh = max(fl, min(nqt, min(t_end, fw)));
-        const int ng = niter / 3 + 1;   // groups covering iterations 0 .. niter
-        int gi = 1;
-        bool go = group(M1{}, TF{}, 0);
-        for (int hi = 0; hi < G && go; ++hi) {
-          const int u0 = hi * nqt + fl, u1 = hi * nqt + fh;   // mask-free tiles [u0, u1)
-          const int ga = min(ng, max(gi, (u0 + 2) / 3));        // 3 g >= u0
-          const int gb = min(ng, max(ga, u1 >= 3 ? (u1 - 3) / 3 + 1 : 0));   // 3 g + 2 < u1
-          for (; go && gi < ga; ++gi) go = group(M1{}, FF{}, 3 * gi);
-          for (; go && gi < gb; ++gi) go = group(M0{}, FF{}, 3 * gi);
-        }
-        for (; go && gi < ng; ++gi) go = group(M1{}, FF{}, 3 * gi);
       } else {
         if (group(M2{}, TF{}, 0))
           for (int it = 3; it <= niter; it += 3)
@@ -991,29 +965,22 @@ __global__ __launch_bounds__(BQB == 32 ? 256 : 512, 1) void fa_bwd_dkdv_pair_ker
 #ifndef BWD64_CFG
 #define BWD64_CFG 64, 4
 #endif
-#ifndef BWD128_CFG
-#define BWD128_CFG 32, 4
-#endif
 #ifndef BWD192_CFG
 #define BWD192_CFG 32, 8
 #endif
 
-// d = 128: the software-pipelined kernels of fa_bwd_pipe.hip for the dK/dV
-// pass (one wave per SIMD, instead of the paired-wave kernel: mistral
-// 3.24 -> 3.05 ms) and for the dQ pass (two waves per SIMD, instead of
-// fa_bwd_dq_kernel: mistral 2.15 -> 2.08 ms; one wave per SIMD: 2.31)
-#ifndef BWD_KV_PIPE128
-#define BWD_KV_PIPE128 1
-#endif
-#ifndef BWD_DQ_PIPE128
-#define BWD_DQ_PIPE128 1
-#endif
+// d = 128 runs the software-pipelined kernels of fa_bwd_pipe.hip: the dK/dV
+// pass at one wave per SIMD (against the paired-wave kernel: mistral 3.24 ->
+// 3.05 ms) and the dQ pass at two (against fa_bwd_dq_kernel: 2.15 -> 2.08 ms;
+// at one wave per SIMD 2.31); d = 256 its dQ pass.
+constexpr bool pipe_dq(int dk, int dv) { return dk == dv && (dk == 128 || dk == 256); }
+constexpr bool pipe_kv(int dk, int dv) { return dk == 128 && dv == 128; }
 
 // the dQ pass, then the fused dK/dV pass
 template <int DK, int DV, bool CAP, int DQ_BKV, int DQ_NW>
 static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   hipError_t e;
-  if constexpr (DK == 256 || (DK == 128 && DV == 128 && BWD_DQ_PIPE128)) {
+  if constexpr (pipe_dq(DK, DV)) {
     e = launch_bwd_dq_pipe(a, DK, CAP, stream);   // fa_bwd_pipe.hip
   } else {
     const int nqb = (a.T + 32 * DQ_NW - 1) / (32 * DQ_NW);
@@ -1023,7 +990,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   }
   stage_mark(stream);
   if (e != hipSuccess) return e;
-  if constexpr (DK == 128 && DV == 128 && BWD_KV_PIPE128) {
+  if constexpr (pipe_kv(DK, DV)) {
     e = launch_bwd_kv_pipe(a, CAP, stream);   // fa_bwd_pipe.hip
   } else {
     constexpr int BQB = DK == 256 ? 32 : PAIR_BQB;
@@ -1053,7 +1020,7 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, int d, int d_v, hipStream_t stream)
   if (d == d_v) {
     switch (d) {
       case 64: return launch_bwd_d<64, 64, BWD64_CFG>(a, stream);
-      case 128: return launch_bwd_d<128, 128, BWD128_CFG>(a, stream);
+      case 128: return launch_bwd_d<128, 128>(a, stream);
       case 256: return launch_bwd_d<256, 256>(a, stream);
     }
   } else if (d == 192 && d_v == 128) {

@@ -31,14 +31,10 @@ namespace fa {
 // barrier per unit.  Units of the workgroup's key range outside a wave's band
 // are computed fully masked (exact zeros), so every wave runs the same
 // straight-line schedule.  Also writes D_i for the dK/dV pass.
-//
-// Waves per SIMD of the d = 128 dQ pass (its working set fits two; one is
-// slower, measured)
-#ifndef DQP128_OCC
-#define DQP128_OCC 2
-#endif
+// At d = 128 the working set fits two waves per SIMD (one is slower,
+// measured).
 template <int D, bool CAP>
-__global__ __launch_bounds__(256, D >= 256 ? 1 : DQP128_OCC) void fa_bwd_dq_pipe_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void fa_bwd_dq_pipe_kernel(BwdArgs a) {
   constexpr int NW = 4, BQ = 32 * NW, BKV = 32;
   // a tile image, rounded up to whole rounds of the loaders' 1 KB pieces
   constexpr int TILE = TileDma<D, BKV, NW>::IMG;

@@ -40,15 +40,6 @@ namespace fa {
 #ifndef FWD_PIPE_PD
 #define FWD_PIPE_PD 2
 #endif
-// fa_fwd_sp_kernel: operand reads this many MFMAs ahead (3: no faster), and
-// the first O-block MFMA whose hook starts the next tile's exponentials
-// (the hooks before it take the next tile's cap, mask and max)
-#ifndef FWD_SP_PD
-#define FWD_SP_PD 2
-#endif
-#ifndef SP_KE0
-#define SP_KE0 8
-#endif
 
 // One wave owns 32 query rows.  DK is the head size of q and k, DV that of
 // v and o (equal except for MLA-style heads).  NSTG (2..4) K/V tiles are in
@@ -392,7 +383,10 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_sp_kernel(FwdArgs a) {
   constexpr int NDB = D / 32;      // 32-wide blocks of the output
   constexpr int NSQ = 2 * NC;      // MFMAs of the score block (two 32-key halves)
   constexpr int NPV = 4 * NDB;     // MFMAs of the O block (four 16-key chunks)
-  constexpr int PD = FWD_SP_PD;
+  constexpr int PD = 2;      // operand reads this many MFMAs ahead (3: no faster)
+  // the first O-block MFMA whose hook starts the next tile's exponentials
+  // (the hooks before it take the next tile's cap, mask and max; 6: no faster)
+  constexpr int KE0 = 8;
   static_assert(2 * PER <= NSQ, "one tile load per score MFMA");
   __shared__ __attribute__((aligned(1024))) char kb0[TILE];
   __shared__ __attribute__((aligned(1024))) char kb1[TILE];
@@ -637,11 +631,11 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_sp_kernel(FwdArgs a) {
              } else {
                if (k >= 1 && k <= 4) prep(mask_c, kv1, 8 * (k - 1), 8 * k);
                if (k == 5) decide();
-               if (k >= SP_KE0) {
-                 // keys 0..31 (half 0), elements spread over hooks SP_KE0 .. 15
-                 constexpr int NH = 16 - SP_KE0;
+               if (k >= KE0) {
+                 // keys 0..31 (half 0), elements spread over hooks KE0 .. 15
+                 constexpr int NH = 16 - KE0;
 #pragma unroll
-                 for (int e = 16 * (k - SP_KE0) / NH; e < 16 * (k - SP_KE0 + 1) / NH; ++e)
+                 for (int e = 16 * (k - KE0) / NH; e < 16 * (k - KE0 + 1) / NH; ++e)
                    pkn.put(e, pexp(sn[0][e], mnew, psn), pn);
                }
              }
@@ -1097,12 +1091,8 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void fa_fwd_pipe_kernel(FwdA
   }
 }
 
-// Tile shapes per head size (keys per tile, waves, K/V tiles in flight),
+// Tile shape of the one-tile kernel at d = 192/128 (keys per tile, waves),
 // chosen by measurement on MI355X.
-#ifndef FWD128_CFG
-#define FWD128_CFG 64, 4
-#endif
-
 #ifndef FWD192_CFG
 #define FWD192_CFG 32, 4
 #endif
@@ -1158,22 +1148,14 @@ static hipError_t launch_fwd_sp(const FwdArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// d = 128 runs the software-pipelined two-wave kernel (mistral forward
-// 1.64 -> 1.59 ms, qwen25 0.329 -> 0.314 ms against fa_fwd_kernel)
-#ifndef FWD_SP128
-#define FWD_SP128 1
-#endif
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, int d, int d_v, hipStream_t stream) {
   if (d == d_v) {
     switch (d) {
       case 64: return launch_fwd_d<64, 64, 64, 4>(a, stream);
-      case 128:
-#if FWD_SP128
-        return launch_fwd_sp(a, stream);
-#else
-        return launch_fwd_d<128, 128, FWD128_CFG>(a, stream);
-#endif
+      // the software-pipelined two-wave kernel (mistral forward 1.64 -> 1.59
+      // ms, qwen25 0.329 -> 0.314 ms against fa_fwd_kernel at 64-key tiles)
+      case 128: return launch_fwd_sp(a, stream);
       // one wave cannot hold q, the 256-wide O accumulator and a tile of
       // scores at two waves per SIMD: the software-pipelined kernel keeps
       // the matrix unit busy at one
