@@ -1023,6 +1023,11 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void fa_fwd_pipe_kernel(FwdA
       part_b(p_c, 0, 16);
       b_tail();
       o_block(vbuf(p_c), [&](int) {});
+      // The last step runs in one of two parity branches, and their join
+      // may copy the accumulator between AGPRs: copies the compiler places
+      // right after the last MFMA, whose latency it does not see.  The wait
+      // comes first, inside the branch.
+      if constexpr (AGPR_O) agpr_acc_fence(oacc);
     }
   };
   using T1 = std::true_type;
@@ -1074,7 +1079,7 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void fa_fwd_pipe_kernel(FwdA
     if (lane == 0 && v > -INFINITY) atomic_max_f32(a.max_logit + bh, v * kLn2);
   }
   const float ltot = xor32_sum(lsum);
-  if constexpr (AGPR_O) agpr_acc_fence(oacc);
+  // (the last step has waited for the accumulator's last MFMAs)
   if (qrow < T) {
     const float inv = 1.f / ltot;
     bf16* Op = a.o + (bh * T + qrow) * D;

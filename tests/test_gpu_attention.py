@@ -38,6 +38,10 @@ BF16_CASES = [
     (1, 4, 2, 640, 256, 257, 0.0, 1.0),
     (1, 16, 1, 700, 64, 0, 0.0, 1.0),
     (1, 32, 2, 333, 128, 100, 20.0, 2.0),
+    # d = 256 workgroups with an odd number of key units (ragged last block,
+    # short windows): the last step's parity branch joins after the O MFMAs
+    (1, 7, 1, 600, 256, 1, 0.0, 1.0),
+    (2, 4, 1, 191, 256, 10, 30.0, 2.0),
 ]
 
 F32_CASES = [
