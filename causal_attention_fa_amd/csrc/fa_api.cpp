@@ -333,13 +333,7 @@ int attn_bwd(bool f32, const void* q, const void* k, const void* v, const void* 
 // most kDecMaxSplits chunks.  max_keys bounds the visible keys of any
 // sequence.
 void decode_split(int units, int max_keys, int* nsplit, int* chunk) {
-#ifndef DEC_TARGET_UNITS
-#define DEC_TARGET_UNITS 4096
-#endif
-#ifndef DEC_MIN_CHUNK
-#define DEC_MIN_CHUNK 1024
-#endif
-  constexpr int kTargetUnits = DEC_TARGET_UNITS, kMinChunk = DEC_MIN_CHUNK, kTile = 32;
+  constexpr int kTargetUnits = 4096, kMinChunk = 1024, kTile = 32;
   int ns = (kTargetUnits + units - 1) / units;
   ns = std::min(ns, (max_keys + kMinChunk - 1) / kMinChunk);
   ns = std::max(1, std::min(ns, fa::kDecMaxSplits));

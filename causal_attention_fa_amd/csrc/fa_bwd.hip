@@ -43,13 +43,11 @@ namespace fa {
 // and so its register use -- chosen by measurement).  Its loop is unrolled
 // by two (buffers chosen at compile time), or at d = 192 the buffer is
 // picked at run time (fewer registers).
-#ifndef BWD_UNROLL
-#define BWD_UNROLL(DK) ((DK) != 192)
-#endif
-
-#ifndef BWD_LDS_PD
-#define BWD_LDS_PD(DK) ((DK) == 192 ? 0 : 2)
-#endif
+// per head size: K, V tiles double-buffered in one array with the loop
+// unrolled by two (not at 192: spills), and how many MFMAs ahead the LDS
+// operands are read (192: as needed)
+constexpr bool bwd_unroll(int dk) { return dk != 192; }
+constexpr int bwd_lds_pd(int dk) { return dk == 192 ? 0 : 2; }
 
 // exp2 argument of P: capped score in the log2 domain minus the row's lse
 // (log2), with the constant folded into one FMA -- cap*log2(e)*tanh(scale*x/
@@ -75,8 +73,8 @@ __global__ __launch_bounds__(64 * NW, (DK >= 192 ? 1 : 8 / NW)) void fa_bwd_dq_k
   constexpr int TILE_V = Lay<DV>::template bytes<BKV>();
   constexpr int NDB = DK / 32;   // 32-wide blocks of dq
   constexpr int NS = BKV / 32;
-  // K, V tiles double-buffered in one array (see BWD_UNROLL)
-  constexpr bool UNROLL = BWD_UNROLL(DK);
+  // K, V tiles double-buffered in one array (see bwd_unroll)
+  constexpr bool UNROLL = bwd_unroll(DK);
   __shared__ __attribute__((aligned(1024))) char one[2 * (TILE_K + TILE_V)];
 
   const int tid = threadIdx.x;
@@ -169,7 +167,7 @@ __global__ __launch_bounds__(64 * NW, (DK >= 192 ? 1 : 8 / NW)) void fa_bwd_dq_k
       const bool empty = qa >= T || kv0 > qb || (W > 0 && kv0 + BKV - 1 <= qa - W);
       const bool full = kv0 + BKV - 1 <= qa && (W == 0 || kv0 > qb - W);
       f32x16 s[NS], dp[NS];
-      TrPipe<DK, NDB, BKV / 16, BWD_LDS_PD(DK)> ktp;
+      TrPipe<DK, NDB, BKV / 16, bwd_lds_pd(DK)> ktp;
       constexpr int NC16 = BKV / 16;
       auto pack_chunk = [&](int c16) __attribute__((always_inline)) {
         float tmp[8];
@@ -177,11 +175,11 @@ __global__ __launch_bounds__(64 * NW, (DK >= 192 ? 1 : 8 / NW)) void fa_bwd_dq_k
         for (int jj = 0; jj < 8; ++jj) tmp[jj] = s[c16 >> 1][8 * (c16 & 1) + jj];
         return pack_bf16(tmp);
       };
-      if constexpr (NS == 1 && BWD_LDS_PD(DK) > 0 && 16 % (DV / 16) == 0) {
+      if constexpr (NS == 1 && bwd_lds_pd(DK) > 0 && 16 % (DV / 16) == 0) {
         // S first, then dP with P = 2^(...) computed under its MFMAs; dS =
         // P (dP - D) chunk by chunk under the dQ product's MFMAs.
         if (empty) return;
-        constexpr int PD = BWD_LDS_PD(DK), NK = DK / 16, NV = DV / 16, EP = 16 / NV;
+        constexpr int PD = bwd_lds_pd(DK), NK = DK / 16, NV = DV / 16, EP = 16 / NV;
   #pragma unroll
         for (int i = 0; i < 16; ++i) {
           s[0][i] = 0.f;
@@ -237,7 +235,7 @@ __global__ __launch_bounds__(64 * NW, (DK >= 192 ? 1 : 8 / NW)) void fa_bwd_dq_k
         return;
       }
       if (!empty) {
-        mma_rows2<DK, DV, NS, BWD_LDS_PD(DK)>(s, Kt, qreg, dp, Vt, doreg, lane);
+        mma_rows2<DK, DV, NS, bwd_lds_pd(DK)>(s, Kt, qreg, dp, Vt, doreg, lane);
         ktp.start(Kt, 0, lane);   // first K^T operands of dQ, read during the softmax
       }
       auto elem = [&](int t, int i) __attribute__((always_inline)) {
@@ -247,7 +245,7 @@ __global__ __launch_bounds__(64 * NW, (DK >= 192 ? 1 : 8 / NW)) void fa_bwd_dq_k
         if (CAP) ds *= 1.f - th * th;
         s[t][i] = ds;
       };
-      if constexpr (BWD_LDS_PD(DK) > 0 && 8 % NDB == 0) {
+      if constexpr (bwd_lds_pd(DK) > 0 && 8 % NDB == 0) {
         if (!empty) {
           if (!full) {
             // invisible pairs: S = -inf gives p = 0 without a cap; with one,
@@ -373,12 +371,8 @@ __global__ __launch_bounds__(64 * NW, (DK >= 192 ? 1 : 8 / NW)) void fa_bwd_dq_k
 
 // ----------------------------------------------------------------- dK/dV pass
 // ------------------------------------------------------ fused dK/dV pass
-#ifndef PAIR_PD
-#define PAIR_PD(D) 3
-#endif
-#ifndef PAIR_BQB
-#define PAIR_BQB 64
-#endif
+constexpr int kPairPD = 3;     // LDS operands read this many MFMAs ahead
+constexpr int kPairBQB = 64;   // query tile of the paired pass (d = 256: 32)
 // One launch for dK and dV, with paired waves: waves p and p + NP own the
 // same 32 key rows (NP = 4 pairs, 128 keys per workgroup; at d = 256 NP = 2
 // and one wave per SIMD, see PairShape).  Wave p (the P side) keeps K in
@@ -427,7 +421,7 @@ __global__ __launch_bounds__(BQB == 32 ? 256 : 512, 1) void fa_bwd_dkdv_pair_ker
   constexpr int NC16 = BQB / 16;            // 16-query chunks (k steps of dV, dK)
   constexpr int STAT = SH::STAT;            // bytes of one lse or D tile
   constexpr int XB = SH::XB;
-  constexpr int PD = PAIR_PD(DK);
+  constexpr int PD = kPairPD;
   constexpr int NKV = NCK > NCV ? NCK : NCV;
   constexpr int NACC = NDBK > NDBV ? NDBK : NDBV;
   static_assert(NS == 1 || NS == 2, "32 or 64 queries per tile");
@@ -962,12 +956,6 @@ __global__ __launch_bounds__(BQB == 32 ? 256 : 512, 1) void fa_bwd_dkdv_pair_ker
 
 // dQ pass tile shape per head size (keys per tile, waves), chosen by
 // measurement on MI355X; d = 128 and 256 run the software-pipelined kernel.
-#ifndef BWD64_CFG
-#define BWD64_CFG 64, 4
-#endif
-#ifndef BWD192_CFG
-#define BWD192_CFG 32, 8
-#endif
 
 // d = 128 runs the software-pipelined kernels of fa_bwd_pipe.hip: the dK/dV
 // pass at one wave per SIMD (against the paired-wave kernel: mistral 3.24 ->
@@ -993,7 +981,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   if constexpr (pipe_kv(DK, DV)) {
     e = launch_bwd_kv_pipe(a, CAP, stream);   // fa_bwd_pipe.hip
   } else {
-    constexpr int BQB = DK == 256 ? 32 : PAIR_BQB;
+    constexpr int BQB = DK == 256 ? 32 : kPairBQB;
     using SH = PairShape<DK, DV, BQB>;
     constexpr int BKVB = 32 * SH::NP;
     const dim3 grid((unsigned)((a.T + BKVB - 1) / BKVB) * a.B * a.Hkv);
@@ -1019,12 +1007,12 @@ const char* bwd_kernel_plan(int d, int d_v) {
 hipError_t launch_bwd_bf16(const BwdArgs& a, int d, int d_v, hipStream_t stream) {
   if (d == d_v) {
     switch (d) {
-      case 64: return launch_bwd_d<64, 64, BWD64_CFG>(a, stream);
+      case 64: return launch_bwd_d<64, 64, 64, 4>(a, stream);
       case 128: return launch_bwd_d<128, 128>(a, stream);
       case 256: return launch_bwd_d<256, 256>(a, stream);
     }
   } else if (d == 192 && d_v == 128) {
-    return launch_bwd_d<192, 128, BWD192_CFG>(a, stream);
+    return launch_bwd_d<192, 128, 32, 8>(a, stream);
   }
   return hipErrorInvalidValue;
 }

@@ -29,9 +29,7 @@
 namespace fa {
 
 // the cache is streamed once per call: non-temporal loads (cache policy 2)
-#ifndef DEC_AUX
-#define DEC_AUX 2
-#endif
+constexpr int kDecAux = 2;   // cache policy bits of the direct tile loads (non-temporal)
 
 constexpr int kDecBKV = 32;  // keys per tile
 
@@ -117,8 +115,8 @@ __global__ __launch_bounds__(64 * NW, 2) void fa_decode_split_kernel(DecodeArgs 
   };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
-  kdm.template load<DEC_AUX>(Kp, end * D * 2, kbuf(I0{}), start, wave);
-  vdm.template load<DEC_AUX>(Vp, end * D * 2, vbuf(I0{}), start, wave);
+  kdm.template load<kDecAux>(Kp, end * D * 2, kbuf(I0{}), start, wave);
+  vdm.template load<kDecAux>(Vp, end * D * 2, vbuf(I0{}), start, wave);
   wait_vmem();
   __syncthreads();
   auto step = [&](auto p_c, const int j) __attribute__((always_inline)) {
@@ -127,8 +125,8 @@ __global__ __launch_bounds__(64 * NW, 2) void fa_decode_split_kernel(DecodeArgs 
     const LDS_AS char* Vt = vbuf(p_c);
     const int kv0 = start + j * kDecBKV;
     if (j + 1 < ntiles) {
-      kdm.template load<DEC_AUX>(Kp, end * D * 2, kbuf(PN{}), kv0 + kDecBKV, wave);
-      vdm.template load<DEC_AUX>(Vp, end * D * 2, vbuf(PN{}), kv0 + kDecBKV, wave);
+      kdm.template load<kDecAux>(Kp, end * D * 2, kbuf(PN{}), kv0 + kDecBKV, wave);
+      vdm.template load<kDecAux>(Vp, end * D * 2, vbuf(PN{}), kv0 + kDecBKV, wave);
     }
     f32x16 sacc[1];
     mma_rows<D, 1>(sacc, Kt, qreg, lane);
@@ -282,33 +280,20 @@ __global__ __launch_bounds__(64) void fa_decode_combine_kernel(DecodeArgs a) {
   if (lane == 0 && a.lse) a.lse[bh] = (M + __log2f(L)) * kLn2;
 }
 
-// Waves per split workgroup, by head size.
-#ifndef DEC_NW64
-#define DEC_NW64 1
-#endif
-#ifndef DEC_NW128
-#define DEC_NW128 2
-#endif
-#ifndef DEC_NW256
-#define DEC_NW256 2
-#endif
-
-// At d = 128 with at least this many (b, KV head, chunk) units, one wave per
-// workgroup: enough workgroups to keep the loads in flight, and no score
+// Waves per split workgroup: one at d = 64, two at 128 and 256 (each wave
+// owning half of the output columns).  At d = 128 with at least 2048
+// (b, KV head, chunk) units, one wave per workgroup: enough workgroups to keep the loads in flight, and no score
 // recomputation per wave (qwen25-decode 5.56 -> 5.76 TB/s); with fewer
 // units the two-wave split keeps more waves per CU (mistral-decode, 1024
 // units, is 3 % faster with two).
-#ifndef DEC_NW128_ONE_UNITS
-#define DEC_NW128_ONE_UNITS 2048
-#endif
 
 template <int D, bool CAP>
 static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
-  constexpr int NW = D == 64 ? DEC_NW64 : D == 128 ? DEC_NW128 : DEC_NW256;
+  constexpr int NW = D == 64 ? 1 : 2;
   const unsigned units = (unsigned)a.B * a.Hkv * a.nsplit;
   bool one = false;
   if constexpr (D == 128 && NW != 1) {
-    one = units >= DEC_NW128_ONE_UNITS;
+    one = units >= 2048;
     if (one) fa_decode_split_kernel<D, 1, CAP><<<units, 64, 0, stream>>>(a);
   }
   if (!one) fa_decode_split_kernel<D, NW, CAP><<<units, 64 * NW, 0, stream>>>(a);

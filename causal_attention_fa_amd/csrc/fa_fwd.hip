@@ -34,12 +34,8 @@ namespace fa {
 
 // LDS operand reads run this many MFMAs ahead of their use (the one-tile
 // kernel, the software-pipelined kernel).
-#ifndef FWD_PD
-#define FWD_PD 3
-#endif
-#ifndef FWD_PIPE_PD
-#define FWD_PIPE_PD 2
-#endif
+constexpr int kFwdPD = 3;       // one-tile kernel: LDS operands this many MFMAs ahead
+constexpr int kFwdPipePD = 2;   // pipelined d = 256 kernel: the same
 
 // One wave owns 32 query rows.  DK is the head size of q and k, DV that of
 // v and o (equal except for MLA-style heads).  NSTG (2..4) K/V tiles are in
@@ -221,7 +217,7 @@ __global__ __launch_bounds__(64 * NW, (MINWG > 0 ? MINWG : DK >= 256 ? 1 : 8 / N
     const bool full = kv0 + BKV - 1 <= qa && (W == 0 || kv0 > qb - W);
     if (!empty) {
       // S^T = K Q^T as a pinned MFMA sequence whose K operands are read
-      // FWD_PD MFMAs ahead: left to itself the compiler sinks each read down
+      // kFwdPD MFMAs ahead: left to itself the compiler sinks each read down
       // to its MFMA, and the LDS latency stalls the matrix unit.
       f32x16 s[NS];
 #pragma unroll
@@ -229,7 +225,7 @@ __global__ __launch_bounds__(64 * NW, (MINWG > 0 ? MINWG : DK >= 256 ? 1 : 8 / N
 #pragma unroll
         for (int i = 0; i < 16; ++i) s[t][i] = 0.f;
       {
-        MfmaSeq<NC * NS, FWD_PD> sq;
+        MfmaSeq<NC * NS, kFwdPD> sq;
         auto fK = [&](int k) __attribute__((always_inline)) {
           return lds_row_operand<DK>(Kt, 32 * (k % NS), k / NS, lane);
         };
@@ -240,7 +236,7 @@ __global__ __launch_bounds__(64 * NW, (MINWG > 0 ? MINWG : DK >= 256 ? 1 : 8 / N
       }
       // the transposed V operands of O^T += V^T P^T are requested now, their
       // latency hidden behind the softmax
-      MfmaSeq<NP * NDB, FWD_PD> vq;
+      MfmaSeq<NP * NDB, kFwdPD> vq;
       auto fV = [&](int k) __attribute__((always_inline)) {
         return lds_tr_operand<DV>(Vt, 0, k / NDB, 32 * (k % NDB), lane);
       };
@@ -747,7 +743,7 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void fa_fwd_pipe_kernel(FwdA
   constexpr int NC = D / 16;     // 16-wide chunks of the q.k contraction
   constexpr int NDB = D / 32;    // 32-wide blocks of the output
   constexpr int NO = 2 * NDB;    // MFMAs of the O^T block
-  constexpr int PD = FWD_PIPE_PD; // LDS operands issued this many MFMAs ahead
+  constexpr int PD = kFwdPipePD; // LDS operands issued this many MFMAs ahead
   // head size 256: O (32 x 256 fp32 = 128 registers per lane) stays in the
   // AGPRs, beside q (64 VGPRs) and the working set in the VGPRs
   constexpr bool AGPR_O = D >= 256;
@@ -1098,9 +1094,6 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void fa_fwd_pipe_kernel(FwdA
 
 // Tile shape of the one-tile kernel at d = 192/128 (keys per tile, waves),
 // chosen by measurement on MI355X.
-#ifndef FWD192_CFG
-#define FWD192_CFG 32, 4
-#endif
 
 template <int DK, int DV, int BKV, int NW, int NSTG = 2, int MINWG = 0>
 static hipError_t launch_fwd_d(const FwdArgs& a, hipStream_t stream) {
@@ -1167,7 +1160,7 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, int d, int d_v, hipStream_t stream)
       case 256: return launch_fwd_pipe<256>(a, stream);
     }
   } else if (d == 192 && d_v == 128) {
-    return launch_fwd_d<192, 128, FWD192_CFG>(a, stream);
+    return launch_fwd_d<192, 128, 32, 4>(a, stream);
   }
   return hipErrorInvalidValue;
 }

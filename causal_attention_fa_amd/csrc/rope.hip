@@ -108,14 +108,10 @@ void launch_vec(const RopeArgs& a, unsigned gx, hipStream_t stream) {
   hipLaunchKernelGGL((rope_vec_kernel<T, BWD, BH_PER>), grid, dim3(kThreads), 0, stream, a);
 }
 
-#ifndef ROPE_MIN_WG_PER_CU
-#define ROPE_MIN_WG_PER_CU 2
-#endif
 template <typename T, bool BWD>
 void launch_vec_bh(const RopeArgs& a, unsigned gx, hipStream_t stream) {
-  // largest slices-per-thread count that keeps >= ROPE_MIN_WG_PER_CU
-  // workgroups per CU
-  constexpr long kMinGroups = ROPE_MIN_WG_PER_CU * 256;
+  // largest slices-per-thread count that keeps at least 2 workgroups per CU
+  constexpr long kMinGroups = 2 * 256;
   const long per1 = (long)gx * a.BH;               // workgroups at one slice per thread
   if (per1 >= 8 * kMinGroups)
     launch_vec<T, BWD, 8>(a, gx, stream);
