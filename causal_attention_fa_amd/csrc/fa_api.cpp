@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <cstdlib>
@@ -119,6 +120,52 @@ int check_ptrs(const char* fn, const Range* rs, int n, int first_out) {
 // looked up on the first call that runs on the device and kept.
 constexpr size_t kNoAllocRows = size_t(1) << 22;   // B * H * T at most (16 MiB of float)
 constexpr int kMaxDevices = 64;
+
+// dQ strategy of the bf16 backward (fa_set_dq_mode): 0 = the measured choice
+// (fa::ds_mode_applies), 1 = the dQ pass recomputes S and dP, 2 = dQ from
+// stored dS wherever supported.
+std::atomic<int> g_dq_mode{0};
+
+// The dS workspace comes from a stream-ordered pool of the library's own per
+// device, whose release threshold keeps freed memory for the next call (a
+// backward's workspace is GBs: mapping it anew on every call would cost
+// more than the pass it serves).  Calls on one device share the pool; the
+// stream order keeps their workspaces apart.  A workspace larger than a
+// quarter of the device's memory is not taken (the recomputing dQ pass runs
+// instead).
+std::mutex g_pool_mu;
+hipMemPool_t g_pool[kMaxDevices] = {};
+size_t g_pool_cap[kMaxDevices] = {};
+
+// the pool of the current device (created on first use) and its cap; null
+// when the device has none (then no workspace is taken)
+hipMemPool_t ws_pool(size_t* cap) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lk(g_pool_mu);
+  if (!g_pool[dev]) {
+    size_t free_b = 0, total_b = 0;
+    if (hipMemGetInfo(&free_b, &total_b) != hipSuccess) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    hipMemPoolProps props{};
+    props.allocType = hipMemAllocationTypePinned;
+    props.location.type = hipMemLocationTypeDevice;
+    props.location.id = dev;
+    hipMemPool_t p = nullptr;
+    if (hipMemPoolCreate(&p, &props) != hipSuccess) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    uint64_t keep = UINT64_MAX;
+    (void)hipMemPoolSetAttribute(p, hipMemPoolAttrReleaseThreshold, &keep);
+    g_pool[dev] = p;
+    g_pool_cap[dev] = total_b / 4;
+  }
+  *cap = g_pool_cap[dev];
+  return g_pool[dev];
+}
 std::mutex g_scratch_mu;
 float* g_scratch_dev[kMaxDevices] = {};
 
@@ -293,6 +340,22 @@ int attn_bwd(bool f32, const void* q, const void* k, const void* v, const void* 
       return finish(e, stream, fn);
     }
   }
+  // dS workspace: [B, H, ceil(T/32), band] tiles of 2 KB, where band = the
+  // key tiles one query tile sees (ceil((W - 1) / 32) + 1 under a window)
+  fa::bf16* dsw = nullptr;
+  const int nqt = (T + 31) / 32;
+  const int nkt = W > 0 ? std::min(nqt, (W - 1 + 31) / 32 + 1) : nqt;
+  if (!f32 && !static_rows && !dsinks && fa::ds_mode_applies(g_dq_mode.load(), d, d_v)) {
+    const size_t tiles = (size_t)B * H * nqt * nkt;
+    size_t cap = 0;
+    hipMemPool_t pool = ws_pool(&cap);
+    if (pool && tiles < (size_t(1) << 31) && tiles * 2048 <= cap) {
+      if (hipMallocFromPoolAsync((void**)&dsw, tiles * 2048, pool, stream) != hipSuccess) {
+        (void)hipGetLastError();   // out of memory: the recomputing pass instead
+        dsw = nullptr;
+      }
+    }
+  }
   stage_begin(stream);
   if (f32) {
     fa::F32Args a{};
@@ -316,7 +379,14 @@ int attn_bwd(bool f32, const void* q, const void* k, const void* v, const void* 
     a.sinks = sinks;
     a.dsinks = dsinks;
     a.rope_cs = rope_cs;
+    a.dsw = dsw;
+    a.nqt_ws = nqt;
+    a.nkt_ws = nkt;
     e = fa::launch_bwd_bf16(a, d, d_v, stream);
+  }
+  if (dsw) {
+    const hipError_t e3 = hipFreeAsync(dsw, stream);
+    if (e == hipSuccess) e = e3;
   }
   hipError_t e2 = static_rows ? hipSuccess : hipFreeAsync(Dst, stream);
   if (e == hipSuccess) e = e2;
@@ -480,7 +550,14 @@ int fa_decode(const void* q, const void* k_cache, const void* v_cache, const int
   return finish(e, stream, fn);
 }
 
-const char* fa_bwd_kernels(int d, int d_v) { return fa::bwd_kernel_plan(d, d_v); }
+const char* fa_bwd_kernels(int d, int d_v) {
+  return fa::bwd_kernel_plan(d, d_v, g_dq_mode.load());
+}
+
+int fa_set_dq_mode(int mode) {
+  if (mode < 0 || mode > 2) return fail(FA_ERR_INVALID_ARG, "fa_set_dq_mode: mode must be 0, 1 or 2");
+  return g_dq_mode.exchange(mode);
+}
 
 int fa_measure_dq_atomics(int B, int H, int Hkv, int T, int d, int window, float* ms) {
   const char* fn = "fa_measure_dq_atomics";

@@ -408,7 +408,14 @@ struct PairShape {
   static_assert(fixed + OSL * TILE_O <= LDS_MAX, "tiles exceed the LDS");
 };
 
-template <int DK, int DV, int BQB, bool CAP>
+// DS (d = 256): the dS side also writes each tile's dS (bf16, as packed for
+// the dK product) to the workspace a.dsw for the dQ pass that reads it
+// (fa_bwd_ds.hip): its 32 keys x 32 queries tile at slot (b, query head,
+// query tile, key tile - query tile + nkt_ws - 1), lane L's two packs at
+// byte 64 (L % 32) + 32 (L / 32) -- the layout of fa_bwd_kv_pipe_kernel's
+// stores.  Tiles outside the band (or past the range) are sent past the
+// store's buffer range, which drops them: no branch.
+template <int DK, int DV, int BQB, bool CAP, bool DS = false>
 __global__ __launch_bounds__(BQB == 32 ? 256 : 512, 1) void fa_bwd_dkdv_pair_kernel(BwdArgs a) {
   using SH = PairShape<DK, DV, BQB>;
   constexpr int NW = SH::NW;
@@ -435,6 +442,7 @@ __global__ __launch_bounds__(BQB == 32 ? 256 : 512, 1) void fa_bwd_dkdv_pair_ker
   // waves per SIMD a per-tile branch costs little: mistral -3.5 % against
   // masking every tile).
   constexpr bool AG = DK == 256;
+  static_assert(!DS || (AG && BQB == 32), "dS stores: d = 256, 32-query tiles");
   __shared__ __attribute__((aligned(1024))) char qs0[TILE_Q];
   __shared__ __attribute__((aligned(1024))) char qs1[TILE_Q];
   __shared__ __attribute__((aligned(1024))) char qs2[TILE_Q];
@@ -669,8 +677,8 @@ __global__ __launch_bounds__(BQB == 32 ? 256 : 512, 1) void fa_bwd_dkdv_pair_ker
   // chunk computed under the MFMAs of the one before, dK^T += Q^T dS;
   // tail() runs a few MFMAs before the end (it starts the next product)
   auto ds_prev = [&](f32x16 (&dp)[NS], const LDS_AS char* Qt, const LDS_AS char* X,
-                     const LDS_AS float* Dt, const LaneOffs<DK>& lq, auto&& tail, auto&& ld)
-                     __attribute__((always_inline)) {
+                     const LDS_AS float* Dt, const LaneOffs<DK>& lq, auto&& tail, auto&& ld,
+                     auto&& sto) __attribute__((always_inline)) {
     (void)Dt;
     bf16x8 xf[NC16];
     // the exchange factor of chunk c16, read a chunk before its use
@@ -710,6 +718,7 @@ __global__ __launch_bounds__(BQB == 32 ? 256 : 512, 1) void fa_bwd_dkdv_pair_ker
                for (int jj = j0; jj < j1; ++jj) dsel(c, jj);
              }
              ld(k);
+             sto(k, dsb);
              if (k == NKQ - PD) tail();
            });
   };
@@ -735,6 +744,7 @@ __global__ __launch_bounds__(BQB == 32 ? 256 : 512, 1) void fa_bwd_dkdv_pair_ker
   // The two sides run separate copies of the loop (the same loads and
   // barriers), so that neither holds the other's registers.
   int tc = 0, tp = 0;   // tile index (within the head) of tiles it and it-1
+  int hc = 0, hp = 0;   // their query heads (within the group)
   LaneOffs<DK> lq0;
   LaneOffs<DV> lv0;
   lq0.init(lane);
@@ -781,6 +791,35 @@ __global__ __launch_bounds__(BQB == 32 ? 256 : 512, 1) void fa_bwd_dkdv_pair_ker
       for (int k = 0; k < NLQ + NLO; ++k) ld(k);
     };
     auto no_ld = [](int) {};
+    // dS of tile it-1 to the workspace (DS): both packs after the step's
+    // last tile load (and after the second pack exists), so that the wait at
+    // the step's end can leave them in flight
+    auto no_sto = [](int, const bf16x8*) {};
+    auto sto = [&](int k, const bf16x8* dsb) __attribute__((always_inline)) {
+      if constexpr (DS) {
+        constexpr int KS = NLQ + NLO > NDBK - 2 ? NLQ + NLO : NDBK - 2;
+        static_assert(KS < NC16 * NDBK, "stores inside the dK product");
+        if (k == KS) {
+          const int qt = qt_lo + tp;
+          const int hh = w.hkv * G + (hp < G ? hp : G - 1);
+          const int row = __builtin_amdgcn_readfirstlane(
+              ((w.b * a.H + hh) * a.nqt_ws + (qt < a.nqt_ws ? qt : 0)) * a.nkt_ws);
+          const int nrec = hp < G && qt < a.nqt_ws ? a.nkt_ws * 2048 : 0;
+          const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+              a.dsw + (size_t)row * 1024, 0, __builtin_amdgcn_readfirstlane(nrec), 0x00020000);
+          // slot of the key tile in the query tile's row; outside the band a
+          // slot far past any row's range (the lane offset cannot wrap it)
+          const unsigned j0 = (unsigned)(kw0 / 32 - qt + a.nkt_ws - 1);
+          const unsigned j = j0 < (unsigned)a.nkt_ws ? j0 : 0x40000u;
+          const unsigned vo = j * 2048u + 64u * l32 + 32u * g;
+#if defined(__HIP_DEVICE_COMPILE__)
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, dsb[0]), rs, vo, 0, 2);
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, dsb[1]), rs, vo + 16, 0,
+                                                 2);
+#endif
+        }
+      }
+    };
     // where spreading them keeps the side spill-free (measured per shape);
     // elsewhere all at the top of the step
     constexpr bool SPREAD = PS ? (DK <= 128 || AG) : DK != 192;
@@ -808,9 +847,11 @@ __global__ __launch_bounds__(BQB == 32 ? 256 : 512, 1) void fa_bwd_dkdv_pair_ker
       if constexpr (!SPREAD) ld_all();
       if constexpr (!FIRST) {
         if constexpr (SPREAD)
-          ds_prev(dp, qbuf(qp), xbuf(xs ^ 1, xo), sbufp(qp) + BQB, lq, [&]() { pq.start(fP); }, ld);
+          ds_prev(dp, qbuf(qp), xbuf(xs ^ 1, xo), sbufp(qp) + BQB, lq, [&]() { pq.start(fP); }, ld,
+                  sto);
         else
-          ds_prev(dp, qbuf(qp), xbuf(xs ^ 1, xo), sbufp(qp) + BQB, lq, [&]() { pq.start(fP); }, no_ld);
+          ds_prev(dp, qbuf(qp), xbuf(xs ^ 1, xo), sbufp(qp) + BQB, lq, [&]() { pq.start(fP); }, no_ld,
+                  sto);
       } else if constexpr (SPREAD) {
         ld_all();
       }
@@ -839,11 +880,11 @@ __global__ __launch_bounds__(BQB == 32 ? 256 : 512, 1) void fa_bwd_dkdv_pair_ker
         if constexpr (SPREAD)
           ds_prev(dp, qbuf(qp), xbuf(xs ^ 1, xo), sbufp(qp) + BQB, lq, [&]() {
             if (cur) pq.start(fP);
-          }, ld);
+          }, ld, no_sto);
         else
           ds_prev(dp, qbuf(qp), xbuf(xs ^ 1, xo), sbufp(qp) + BQB, lq, [&]() {
             if (cur) pq.start(fP);
-          }, no_ld);
+          }, no_ld, no_sto);
         started = true;
       } else if constexpr (SPREAD) {
         ld_all();
@@ -851,10 +892,21 @@ __global__ __launch_bounds__(BQB == 32 ? 256 : 512, 1) void fa_bwd_dkdv_pair_ker
       if (cur) dp_cur(dp, pq, fP, started, sbufp(qc) + BQB, no_ld);
     }
     if ((AG || more) && wave < 2 * BQB / 64) sbufp(qn)[tid] = stat_val(sv);
-    wait_vmem();
-    __syncthreads();
+    if constexpr (DS) {
+      // this step's tile loads (and everything older: vector-memory
+      // operations report completion in issue order) are done; the dS
+      // side's two stores, issued last, may stay in flight until the next
+      // step's wait.  An LDS-only barrier: __syncthreads would wait for them.
+      wait_vmem<(!PS && !FIRST) ? 2 : 0>();
+      lds_barrier();
+    } else {
+      wait_vmem();
+      __syncthreads();
+    }
     tp = tc;
     tc = t1;
+    hp = hc;
+    hc = h1;
     advance(h1, t1);
   };
   auto run = [&](auto side_c) __attribute__((always_inline)) {
@@ -964,10 +1016,32 @@ __global__ __launch_bounds__(BQB == 32 ? 256 : 512, 1) void fa_bwd_dkdv_pair_ker
 constexpr bool pipe_dq(int dk, int dv) { return dk == dv && (dk == 128 || dk == 256); }
 constexpr bool pipe_kv(int dk, int dv) { return dk == 128 && dv == 128; }
 
-// the dQ pass, then the fused dK/dV pass
+// the dQ pass, then the fused dK/dV pass; with a dS workspace (a.dsw) the
+// row statistics D, the dK/dV pass storing dS, then dQ from the stored dS
 template <int DK, int DV, bool CAP, int DQ_BKV, int DQ_NW>
 static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   hipError_t e;
+  if constexpr (ds_workspace_sizes(DK, DV)) {
+    if (a.dsw) {
+      e = launch_bwd_rowdot(a, DK, stream);   // fa_bwd_ds.hip
+      stage_mark(stream);
+      if (e != hipSuccess) return e;
+      if constexpr (pipe_kv(DK, DV)) {
+        e = launch_bwd_kv_pipe(a, CAP, stream);
+      } else {
+        using SH = PairShape<DK, DV, 32>;
+        const dim3 grid((unsigned)((a.T + 32 * SH::NP - 1) / (32 * SH::NP)) * a.B * a.Hkv);
+        hipLaunchKernelGGL((fa_bwd_dkdv_pair_kernel<DK, DV, 32, CAP, true>), grid,
+                           dim3(64 * SH::NW), 0, stream, a);
+        e = hipGetLastError();
+      }
+      stage_mark(stream);
+      if (e != hipSuccess) return e;
+      e = launch_bwd_dq_ds(a, DK, stream);
+      stage_mark(stream);
+      return e;
+    }
+  }
   if constexpr (pipe_dq(DK, DV)) {
     e = launch_bwd_dq_pipe(a, DK, CAP, stream);   // fa_bwd_pipe.hip
   } else {
@@ -999,7 +1073,8 @@ static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
   return launch_bwd_t<DK, DV, false, DQ_BKV, DQ_NW>(a, stream);
 }
 
-const char* bwd_kernel_plan(int d, int d_v) {
+const char* bwd_kernel_plan(int d, int d_v, int mode) {
+  if (ds_mode_applies(mode, d, d_v)) return "rowdot,dkdv,dq_ds";
   if ((d == d_v && (d == 64 || d == 128 || d == 256)) || (d == 192 && d_v == 128)) return "dq,dkdv";
   return nullptr;
 }

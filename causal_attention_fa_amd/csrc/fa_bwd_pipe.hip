@@ -81,16 +81,25 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void fa_bwd_dq_pipe_kernel(B
     const bf16x8* qs = (const bf16x8*)(a.q + roff);
     const bf16x8* ds = (const bf16x8*)(a.dO + roff);
     const bf16x8* os = (const bf16x8*)(a.o + roff);
-    float part = 0.f;
+    // D's fixed summation order (the stored-dS path's prologue computes the
+    // same bits): an 8-term chain per 8-column chunk t = 2 c + g, then a
+    // balanced tree over t with the pairs (t, t ^ 1) at its leaves
+    float u[NC];
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       qreg[c] = qs[2 * c];
       doreg[c] = ds[2 * c];
       const bf16x8 ov = os[2 * c];
+      float part = 0.f;
 #pragma unroll
       for (int j = 0; j < 8; ++j) part += (float)doreg[c][j] * (float)ov[j];
+      u[c] = xor32_sum(part);
     }
-    Di = xor32_sum(part);
+#pragma unroll
+    for (int st = 1; st < NC; st <<= 1)
+#pragma unroll
+      for (int c = 0; c < NC; c += 2 * st) u[c] = u[c] + u[c + st];
+    Di = u[0];
     if (g == 0 && qrow < T) a.Dst[bh * T + qrow] = Di;
   }
   const float lse2 = a.lse[bh * T + qr] * kLog2e;
@@ -334,7 +343,14 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void fa_bwd_dq_pipe_kernel(B
 // the workgroup's query range outside a wave's band are computed fully
 // masked (exact zeros), so every wave runs the same schedule; units every
 // row of which sees all 32 keys carry no mask.
-template <bool CAP>
+// DS: each unit's dS (bf16, as packed for the dK product) is also written to
+// the workspace a.dsw for the dQ pass that reads it (fa_bwd_ds.hip): the
+// wave's 32 keys x 32 queries tile at slot (b, query head, query tile,
+// key tile - query tile + nkt_ws - 1), lane L's 32 bytes at byte
+// 64 (L % 32) + 32 (L / 32): row r of the tile is key r.  Units outside the
+// band the workspace holds (fully masked ones, padding) are sent past the
+// store's buffer range, which drops them: no branch.
+template <bool CAP, bool DS>
 __global__ __launch_bounds__(256, 1) void fa_bwd_kv_pipe_kernel(BwdArgs a) {
   constexpr int D = 128, NW = 4, BQ = 32, BKVB = 32 * NW;
   using Dma = TileDma<D, BQ, NW>;
@@ -421,6 +437,30 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_kv_pipe_kernel(BwdArgs a) {
   };
   auto stat_store = [&](LDS_AS float* st, float v) {
     if (wave == 0) st[lane] = g == 0 ? v * kLog2e : -v;
+  };
+  // the dS store of unit (hi, ti): its workspace row (query tile) as a
+  // buffer of nkt_ws slots, empty for units past the range
+  const int kt_w = ka / 32;
+  auto ds_rsrc = [&](int hi, int ti) {
+    const int qt = qt_lo + ti;
+    const int hh = w.hkv * G + (hi < G ? hi : G - 1);
+    const int row = __builtin_amdgcn_readfirstlane(
+        ((w.b * a.H + hh) * a.nqt_ws + (qt < a.nqt_ws ? qt : 0)) * a.nkt_ws);
+    const int nrec = hi < G && qt < a.nqt_ws ? a.nkt_ws * 2048 : 0;
+    return __builtin_amdgcn_make_buffer_rsrc(a.dsw + (size_t)row * 1024, 0,
+                                             __builtin_amdgcn_readfirstlane(nrec), 0x00020000);
+  };
+  // slot of the unit's key tile in its query tile's row; outside the band a
+  // slot far past any row's range (adding the lane offset cannot wrap it)
+  auto ds_voff = [&](int ti) -> unsigned {
+    const unsigned j0 = (unsigned)(kt_w - (qt_lo + ti) + a.nkt_ws - 1);
+    const unsigned j = j0 < (unsigned)a.nkt_ws ? j0 : 0x40000u;
+    return j * 2048u + 64u * l32 + 32u * g;
+  };
+  auto ds_store = [&](const __amdgpu_buffer_rsrc_t& rs, unsigned voff, int c, bf16x8 v) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs, voff + 16 * c, 0, 2);
+#endif
   };
 
   f32x16 sacc;   // S of the unit being prepared, then its capped, masked score
@@ -513,7 +553,7 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_kv_pipe_kernel(BwdArgs a) {
   };
 
   // prologue: units 0 and 1 resident; S(0), its mask, dP(0) with P(0), dV(0)
-  int h1 = 0, t1 = 0, h2 = 0, t2 = 0;   // units i+1 and i+2 of iteration i
+  int h0 = 0, t0 = 0, h1 = 0, t1 = 0, h2 = 0, t2 = 0;   // units i, i+1, i+2 of iteration i
   auto advance = [&](int& hi, int& ti) {
     if (++ti == nqt) {
       ti = 0;
@@ -571,6 +611,12 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_kv_pipe_kernel(BwdArgs a) {
     const int nb = more ? T * D * 2 : 0;
     const int row2 = (qt_lo + t2) * BQ;
     const int q01 = (qt_lo + t1) * BQ;
+    __amdgpu_buffer_rsrc_t drs;
+    unsigned dvo = 0;
+    if constexpr (DS) {
+      drs = ds_rsrc(h0, t0);
+      dvo = ds_voff(t0);
+    }
     // S(i+1), carrying dS(i) and unit i+2's tile loads (one per MFMA,
     // branch-free: a wave with no piece k left loads zeros into the image's
     // partial last round).  Every block issues the next one's first operand
@@ -591,6 +637,14 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_kv_pipe_kernel(BwdArgs a) {
                dm.load_piece(k, qsrc, nb, qbuf(b2), row2, wave);
              else if (k < 2 * PER)
                dm.load_piece(k - PER, osrc, nb, obuf(b2), row2, wave);
+             // the step's two dS stores come after all of its loads, so
+             // that the wait at its end can leave them in flight
+             if constexpr (DS) {
+               if (k == NC - 1) {
+                 ds_store(drs, dvo, 0, dsb[0]);
+                 ds_store(drs, dvo, 1, dsb[1]);
+               }
+             }
              if (k == NC - PD) kq.start(fK);
            });
     // dK(i), carrying the mask (and cap) of S(i+1) and its statistics (-D
@@ -614,8 +668,13 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_kv_pipe_kernel(BwdArgs a) {
     vq.run(fV, [&](int k) { return pb[k / NDB]; }, [&](int k) -> f32x16& { return dvacc[k % NDB]; },
            [](int) {});
     stat_store(sbuf(b2), sv);
-    wait_vmem();
+    // this step's loads (and everything older: vector-memory operations
+    // report completion in issue order) are done; its dS stores, issued
+    // last, may still be in flight until the next step's wait
+    wait_vmem<DS ? 2 : 0>();
     lds_barrier();
+    h0 = h1;
+    t0 = t1;
     h1 = h2;
     t1 = t2;
     advance(h2, t2);
@@ -684,10 +743,15 @@ hipError_t launch_bwd_dq_pipe(const BwdArgs& a, int d, bool cap, hipStream_t str
 hipError_t launch_bwd_kv_pipe(const BwdArgs& a, bool cap, hipStream_t stream) {
   const int nkb = (a.T + 127) / 128;
   const dim3 grid((unsigned)nkb * a.B * a.Hkv);
-  if (cap)
-    hipLaunchKernelGGL(fa_bwd_kv_pipe_kernel<true>, grid, dim3(256), 0, stream, a);
+  const bool ds = a.dsw != nullptr;
+  if (cap && ds)
+    hipLaunchKernelGGL((fa_bwd_kv_pipe_kernel<true, true>), grid, dim3(256), 0, stream, a);
+  else if (cap)
+    hipLaunchKernelGGL((fa_bwd_kv_pipe_kernel<true, false>), grid, dim3(256), 0, stream, a);
+  else if (ds)
+    hipLaunchKernelGGL((fa_bwd_kv_pipe_kernel<false, true>), grid, dim3(256), 0, stream, a);
   else
-    hipLaunchKernelGGL(fa_bwd_kv_pipe_kernel<false>, grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((fa_bwd_kv_pipe_kernel<false, false>), grid, dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

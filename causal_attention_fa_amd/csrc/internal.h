@@ -53,6 +53,13 @@ struct BwdArgs {
   float* dsinks;                   // [H] gradient of the sinks (accumulated), or null
   const float* rope_cs;            // [T, d/2, 2] RoPE (cos, sin): dq is rotated back
                                    // (gradient w.r.t. the un-rotated q), or null
+  // dQ from stored dS: the dK/dV pass writes every visible 32 x 32 tile of
+  // bf16 dS to dsw and the dQ pass reads it back (null: the dQ pass
+  // recomputes S and dP).  Layout: [B, H, nqt_ws, nkt_ws] tiles of 2 KB;
+  // slot j of query tile qt holds key tile qt - nkt_ws + 1 + j.
+  bf16* dsw;
+  int nqt_ws;                      // query tiles per head, ceil(T / 32)
+  int nkt_ws;                      // key tiles a query tile can see
 };
 
 // float32 twins (plain pointers, same semantics).
@@ -117,9 +124,23 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, int d, int d_v, hipStream_t stream)
 hipError_t launch_bwd_dq_pipe(const BwdArgs& a, int d, bool cap, hipStream_t stream);
 // the d = 128 dK/dV pass (fa_bwd_pipe.hip), launched by launch_bwd_bf16
 hipError_t launch_bwd_kv_pipe(const BwdArgs& a, bool cap, hipStream_t stream);
-// kernels launch_bwd_bf16 runs for (d, d_v), in order ("dq,dkdv"); null for
-// unsupported sizes
-const char* bwd_kernel_plan(int d, int d_v);
+// head sizes whose backward can take dQ from stored dS (fa_bwd_ds.hip)
+constexpr bool ds_workspace_sizes(int d, int d_v) { return d == d_v && (d == 128 || d == 256); }
+// dQ mode (fa_set_dq_mode): 0 stored dS where it measured faster than the
+// recomputing dQ pass (d = 256: gemma-global 0.80 ms of dQ pass against the
+// stored tiles' cost; at d = 128 the dK/dV pass's 2 bytes of stores per
+// visible pair cost more than the recomputation saves: mistral 5.04 against
+// 5.6 ms of backward), 1 recompute everywhere, 2 stored dS wherever supported
+constexpr bool ds_mode_applies(int mode, int d, int d_v) {
+  return ds_workspace_sizes(d, d_v) && (mode == 2 || (mode == 0 && d == 256));
+}
+// D prologue and dQ-from-stored-dS pass (fa_bwd_ds.hip), launched by
+// launch_bwd_bf16 when a.dsw is set
+hipError_t launch_bwd_rowdot(const BwdArgs& a, int d, hipStream_t stream);
+hipError_t launch_bwd_dq_ds(const BwdArgs& a, int d, hipStream_t stream);
+// kernels launch_bwd_bf16 runs for (d, d_v), in order ("dq,dkdv", or
+// "rowdot,dkdv,dq_ds" with a dS workspace); null for unsupported sizes
+const char* bwd_kernel_plan(int d, int d_v, int mode);
 hipError_t launch_fwd_f32(const F32Args& a, hipStream_t stream);
 hipError_t launch_bwd_f32(const F32Args& a, hipStream_t stream);
 hipError_t launch_decode_bf16(const DecodeArgs& a, int d, bool cap, hipStream_t stream);

@@ -83,6 +83,8 @@ _lib.fa_set_stage_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), _I]
 _lib.fa_set_stage_events.restype = _I
 _lib.fa_bwd_kernels.argtypes = [_I, _I]
 _lib.fa_bwd_kernels.restype = ctypes.c_char_p
+_lib.fa_set_dq_mode.argtypes = [_I]
+_lib.fa_set_dq_mode.restype = _I
 _lib.fa_measure_dq_atomics.argtypes = [_I, _I, _I, _I, _I, _I, ctypes.POINTER(ctypes.c_float)]
 _lib.fa_measure_dq_atomics.restype = _I
 _lib.fa_last_error.argtypes = []
@@ -93,7 +95,7 @@ EXPORTS = ("fa_fwd", "fa_bwd", "fa_bwd_noalloc", "fa_fwd_sink", "fa_bwd_sink", "
            "fa_decode", "fa_decode_splits", "rope_apply", "rope_apply_bwd", "fa_fwd_f32",
            "fa_bwd_f32", "rope_apply_f32", "rope_apply_bwd_f32", "fa_layer_window", "fa_rope_inv_freq",
            "fa_rope_inv_freq_llama3", "fa_layer_rope_theta", "fa_set_stage_events",
-           "fa_bwd_kernels", "fa_measure_dq_atomics", "fa_last_error")
+           "fa_bwd_kernels", "fa_set_dq_mode", "fa_measure_dq_atomics", "fa_last_error")
 
 
 class FAError(RuntimeError):
@@ -233,6 +235,15 @@ def fa_bwd_kernels(d, d_v=None):
     if r is None:
         raise FAError(FA_ERR_UNSUPPORTED, f"fa_bwd_kernels: unsupported head sizes ({d}, {d_v})")
     return r.decode().split(",")
+
+
+def fa_set_dq_mode(mode):
+    """Process-wide dQ strategy of the bf16 backward (0: dQ from stored dS
+    where it applies, 1: the recomputing dQ pass); returns the previous one."""
+    r = _lib.fa_set_dq_mode(int(mode))
+    if r < 0:
+        _check(r)
+    return r
 
 
 def fa_measure_dq_atomics(B, H, Hkv, T, d, window=0):

@@ -50,8 +50,12 @@
  * (hipMallocAsync/hipFreeAsync on `stream`): fa_bwd and its _sink, _vdim
  * and _rope variants (the [B, H, T] float32 row statistics), fa_fwd_rope
  * and fa_bwd_rope (a [T, d/2] float32 (cos, sin) table), fa_decode (the
- * per-chunk partial results).  fa_bwd_noalloc allocates nothing.  No state
- * persists between calls.
+ * per-chunk partial results).  The bf16 fa_bwd and fa_bwd_rope at
+ * d = 128 also take a dS workspace (see fa_bwd_kernels) from a
+ * stream-ordered memory pool the library keeps per device: freed at the end
+ * of the call, its memory stays in the pool for the next one until the
+ * process ends.  fa_bwd_noalloc allocates nothing.  No other state persists
+ * between calls.
  *
  * Errors: 0 on success, else a negative FA_ERR_* code; fa_last_error()
  * returns a thread-local message describing the most recent failure.
@@ -89,8 +93,10 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o,
 
 /* fa_bwd without any allocation, for callers that cannot allocate (code
  * under HIP graph capture, allocation-free serving loops, harnesses that
- * forbid hipMalloc): same parameters, semantics and results as fa_bwd
- * (bit for bit), with the [B, H, T] float32 row statistics in a fixed array
+ * forbid hipMalloc): same parameters and semantics as fa_bwd, and its
+ * results bit for bit under dQ mode 1 (fa_set_dq_mode; in the default mode
+ * dk and dv are the same bits and dq agrees within the parity bound), with
+ * the kernels "dq,dkdv" and the [B, H, T] float32 row statistics in a fixed array
  * in device memory that the library holds for the life of the process on
  * each GPU it runs on (16 MiB).  B * H * T must not exceed 4,194,304
  * (FA_ERR_INVALID_ARG otherwise, before any device work); `stream` must
@@ -269,12 +275,32 @@ int fa_layer_rope_theta(int layer, double theta, double theta_global,
  * null handle.  Thread-local state; no device work. */
 int fa_set_stage_events(void* const* events, int count);
 
-/* The kernels the bf16 fa_bwd (and its _rope, _vdim, _sink variants)
- * launches for head sizes (d, d_v), in launch order, comma-separated:
- * "dq,dkdv" (dK and dV in one pass) or "dq,dv,dk"; null for sizes the
- * backward does not support.  Static string owned by the library; host
- * only, no device work. */
+/* The kernels the bf16 fa_bwd (and its _rope and _vdim variants) launches
+ * for head sizes (d, d_v), in launch order, comma-separated, under the
+ * current dQ mode (fa_set_dq_mode):
+ *   "rowdot,dkdv,dq_ds" -- dQ from stored dS: the prologue D = rowsum(dO o)
+ *                          alone, the key-parallel dK/dV pass writing every
+ *                          visible dS tile (bf16) to a workspace, then the
+ *                          query-parallel dQ pass dq = scale dS K reading it
+ *                          (d = d_v = 128; taken when the workspace, 2 bytes
+ *                          per (query, key tile of 32) pair of the band, fits
+ *                          a quarter of the device's memory);
+ *   "dq,dkdv"           -- the query-parallel dQ pass recomputing S and dP
+ *                          (it also writes D), then the dK/dV pass;
+ * null for sizes the backward does not support.  fa_bwd_sink and
+ * fa_bwd_noalloc always run "dq,dkdv".  Static string owned by the library;
+ * host only, no device work.  (ARCHITECTURES.md, prioritised plan: the
+ * backward's dQ either by a separate query-parallel pass or accumulated by
+ * the key-parallel pass, chosen by measurement.) */
 const char* fa_bwd_kernels(int d, int d_v);
+
+/* Process-wide dQ strategy of the bf16 backward, for measurement and tests:
+ * 0 (the default) takes dQ from stored dS where fa_bwd_kernels says so, 1
+ * always runs the recomputing dQ pass.  Both give dq within the parity
+ * bound of the oracle; dk and dv are bit for bit the same in both.  Returns
+ * the previous mode, or FA_ERR_INVALID_ARG for another value.  Calls
+ * already enqueued keep the mode they were enqueued with. */
+int fa_set_dq_mode(int mode);
 
 /* Measurement behind the choice of the dQ strategy (host call, synchronous;
  * allocates and frees its own buffer): the time in ms (best of three) of

@@ -155,12 +155,27 @@ def test_layer_rope_theta_matches_oracle():
 
 
 def test_bwd_kernel_plan():
-    """Every supported head-size pair names the dq pass first and covers dK
-    and dV exactly once; unsupported sizes raise."""
-    for d, dv in ((64, 64), (128, 128), (256, 256), (192, 128)):
-        plan = fa.fa_bwd_kernels(d, dv)
-        assert plan[0] == "dq"
-        assert plan[1:] in (["dkdv"], ["dv", "dk"]), plan
+    """Every supported head-size pair covers dK and dV in one pass and dQ
+    once: by the recomputing dQ pass first, or from the dS the dK/dV pass
+    stores, after the D prologue.  Mode 0 (default) stores dS at d = 256
+    only, mode 1 never, mode 2 wherever supported (d = 128, 256); other
+    modes and unsupported sizes raise."""
+    sizes = ((64, 64), (128, 128), (256, 256), (192, 128))
+    stored = {0: {(256, 256)}, 1: set(), 2: {(128, 128), (256, 256)}}
+    prev = fa.fa_set_dq_mode(0)
+    try:
+        for mode in (0, 1, 2, 0):
+            fa.fa_set_dq_mode(mode)
+            for d, dv in sizes:
+                plan = fa.fa_bwd_kernels(d, dv)
+                want = ["rowdot", "dkdv", "dq_ds"] if (d, dv) in stored[mode] else ["dq", "dkdv"]
+                assert plan == want, (mode, d, dv, plan)
+        for bad in (-1, 3):
+            with pytest.raises(fa.FAError):
+                fa.fa_set_dq_mode(bad)
+        assert fa.fa_set_dq_mode(2) == 0 and fa.fa_set_dq_mode(0) == 2
+    finally:
+        fa.fa_set_dq_mode(prev)
     for d, dv in ((96, 96), (128, 64), (0, 0)):
         with pytest.raises(fa.FAError):
             fa.fa_bwd_kernels(d, dv)

@@ -1,8 +1,10 @@
 """fa_bwd_noalloc (the backward with its row statistics in a fixed device
 array, for callers that cannot allocate) against fa_bwd through the C ABI:
 two calls in a row, the second on a smaller input, each bit for bit equal to
-fa_bwd on the same inputs (the same kernels run; only where D lives
-differs), and within the oracle's bf16 envelope."""
+fa_bwd under dQ mode 1 on the same inputs (the same kernels run; only where
+D lives differs); against fa_bwd in the default mode (dQ from stored dS at
+d = 128) dk and dv bit for bit, and all three within the oracle's bf16
+envelope."""
 import math
 
 import numpy as np
@@ -35,10 +37,18 @@ def test_noalloc_matches_fa_bwd_twice():
         o = poison(q.shape, q.dtype)
         lse = poison((w.B, w.H, w.T), torch.float32)
         fa.fa_fwd(qd, kd, vd, o, lse, w.B, w.H, w.Hkv, w.T, w.d, w.scale, w.window, 0, w.softcap)
-        ref = _bwd(fa.fa_bwd, qd, kd, vd, o, lse, dod, w)
+        dflt = _bwd(fa.fa_bwd, qd, kd, vd, o, lse, dod, w)
+        prev = fa.fa_set_dq_mode(1)
+        try:
+            ref = _bwd(fa.fa_bwd, qd, kd, vd, o, lse, dod, w)
+        finally:
+            fa.fa_set_dq_mode(prev)
         got = _bwd(fa.fa_bwd_noalloc, qd, kd, vd, o, lse, dod, w)
         for n in got:
             assert np.array_equal(got[n], ref[n]), f"{n}: fa_bwd_noalloc differs from fa_bwd"
+        for n in ("dk", "dv"):
+            assert np.array_equal(got[n], dflt[n]), f"{n}: differs from the default-mode fa_bwd"
         orc = oracle_full(q, k, v, do, w.scale, w.window, w.softcap)
+        check("dq(default mode)", dflt["dq"], orc["dq"], env=orc["E_dq"])
         errs = {n: check(n, got[n], orc[n], env=orc["E_" + n]) for n in got}
         say(f"  equal to fa_bwd; oracle rms-relative {errs}")
