@@ -426,7 +426,8 @@ def main():
     ap.add_argument("--rope-workloads", default="forge-default,qwen25",
                     help="workloads whose standalone RoPE is timed in GB/s ('none' to skip)")
     ap.add_argument("--dq-strategy", type=int, default=1,
-                    help="1: time the dQ-atomics traffic beside the separate dQ pass")
+                    help="1: time the backward under each dQ strategy (recomputing pass, "
+                         "stored dS) beside the dQ-atomics traffic alone")
     ap.add_argument("--decode-workload", default="qwen25-decode",
                     help="decode workload timed after the main step ('none' to skip)")
     ap.add_argument("--decode-iters", type=int, default=20)
@@ -529,21 +530,45 @@ def main():
     if configs:
         out["configs"] = configs
 
-    # the dQ strategy, chosen by measurement: the separate query-parallel
-    # pass's time against only the float atomics that accumulating dQ in the
-    # dK/dV pass would issue (a lower bound on that variant's extra cost)
+    # the dQ strategy, chosen by measurement: per workload the whole
+    # backward with dQ recomputed by its own query-parallel pass (mode 1)
+    # and with dQ from the dS tiles the dK/dV pass stores (mode 2, where the
+    # head size allows), beside only the float atomics that accumulating dQ
+    # in the dK/dV pass would issue (a lower bound on that variant's extra
+    # cost over the dK/dV pass); the library's default (mode 0) is reported
+    # beside the measured choice
     if args.dq_strategy:
         dqs = {}
-        timed = {args.workload: out.get("kernel_ms", {})}
-        timed.update({n: c.get("kernel_ms", {}) for n, c in configs.items()})
-        for name, km in timed.items():
+        for name in [args.workload] + list(configs):
             w = synth.WORKLOADS.get(name)
-            if w is None or "bwd_dq" not in km or w.dv != w.d:
+            if w is None or w.dv != w.d:
                 continue
+            r = {}
+            for mode, key in ((1, "recompute"), (2, "stored_ds")):
+                fa.fa_set_dq_mode(mode)
+                try:
+                    names = fa.fa_bwd_kernels(w.d)
+                    if key == "stored_ds" and "dq_ds" not in names:
+                        continue
+                    torch.cuda.empty_cache()
+                    ls, _ = build_layers(name, dev, args.rope)
+                    _, _, km = time_layers(ls, 10, 3)
+                    del ls
+                finally:
+                    fa.fa_set_dq_mode(0)
+                r[key + "_bwd_ms"] = round(sum(km["bwd_" + n] for n in names), 4)
+                r[key + "_kernel_ms"] = {n: round(km["bwd_" + n], 4) for n in names}
             torch.cuda.empty_cache()
-            ms = fa.fa_measure_dq_atomics(w.B, w.H, w.Hkv, w.T, w.d, w.window)
-            dqs[name] = {"dq_pass_ms": km["bwd_dq"], "atomics_only_ms": round(ms, 4),
-                         "choice": "separate pass" if km["bwd_dq"] < ms else "atomics"}
+            r["atomics_only_ms"] = round(
+                fa.fa_measure_dq_atomics(w.B, w.H, w.Hkv, w.T, w.d, w.window), 4)
+            dk = r["recompute_kernel_ms"]["dkdv"]
+            cand = {"recompute": r["recompute_bwd_ms"],
+                    "atomics (lower bound)": round(dk + r["atomics_only_ms"], 4)}
+            if "stored_ds_bwd_ms" in r:
+                cand["stored_ds"] = r["stored_ds_bwd_ms"]
+            r["choice"] = min(cand, key=cand.get)
+            r["library_default"] = "stored_ds" if "dq_ds" in fa.fa_bwd_kernels(w.d) else "recompute"
+            dqs[name] = r
         out["dq_strategy"] = dqs
 
     rope = {}
