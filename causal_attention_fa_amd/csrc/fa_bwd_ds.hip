@@ -73,38 +73,60 @@ __device__ __forceinline__ bf16x8 ds_tile_tr(const LDS_AS char* tile, int c16, i
   return __builtin_bit_cast(bf16x8, v);
 }
 
-// dQ pass from stored dS.  A workgroup (4 waves) owns 128 query rows of one
-// (b, h); wave w the 32 rows of query tile qt_w.  It walks the key tiles
-// that any of its rows can see; per tile the waves share the K tile (loaded
-// into LDS together, padded Lay<D> image) and each loads its own 2 KB dS
-// tile (two direct 1 KB loads, no padding); a key tile outside a wave's band
-// has no slot, its loads fall outside the buffer range and read zeros.
-// dQ^T (D x 32 queries, accumulator column = slot s) += K^T dS^T: 2 D / 32
-// MFMAs per tile, K read transposed (lds_tr_op), dS read transposed
-// (ds_tile_tr).  The dS tiles stream from HBM (read once) and run NSD - 1
-// tiles ahead through a ring of NSD; the K tiles, which the G heads of a
-// group and neighbouring query blocks share through L2, NK - 1 ahead through
-// a ring of NK (NK <= NSD).  One barrier per tile.  The store writes slot s's
-// row to query 32 qt_w + pi(s), scaled (and rotated back, with fused RoPE).
-template <int D, int NK, int NSD>
+// dQ pass from stored dS.  A workgroup (4 waves) owns 128 query rows (query
+// tiles qt_0 .. qt_0 + 3) of one (b, h) and walks the key tiles that any of
+// its rows can see.  Per key tile the waves share the K tile (padded Lay<D>
+// image) and the four 2 KB dS tiles (unpadded images); a key tile outside a
+// query tile's band has no slot, its loads fall outside the buffer range and
+// read zeros.  Wave w computes dQ^T (accumulator column = slot s) += K^T dS^T
+// for query tiles 2 (w / 2) and 2 (w / 2) + 1 and the half w % 2 of d: each
+// transposed K operand it reads (lds_tr_op) feeds two MFMAs, one per query
+// tile; dS read transposed (ds_tile_tr).
+// Loads: waves 0 and 1 load the K tiles (mostly L2 hits), waves 2 and 3 the
+// dS tiles of all four query tiles (streamed from HBM, read once), each
+// tile's loads spread one per MFMA of the tile before it (a burst stalls
+// the issuing wave) and branch-free (past the last tile they read an empty
+// range).  Two LDS slots, each an object of its own, and the loop unrolled
+// by two, so every slot is a compile-time choice: the compiler then sees
+// that the loads in flight do not write the slot being read (with one
+// array, or with loads left in flight across the barrier, it waited for all
+// of them before the reads: no prefetch at all).  Each step waits for its
+// own loads before the barrier.  The loop is padded to whole pairs of
+// tiles; a tile past the last reads zeros and adds exact zeros.  The store
+// writes slot s's row to query 32 qt + pi(s), scaled (and rotated back,
+// with fused RoPE).
+template <int D>
 __global__ __launch_bounds__(256, 2) void fa_bwd_dq_ds_kernel(BwdArgs a) {
   constexpr int NW = 4, BQ = 32 * NW, BKV = 32;
-  using Dma = TileDma<D, BKV, NW>;
+  using Dma = TileDma<D, BKV, 2>;   // the K tiles: waves 0 and 1
   constexpr int KIMG = Dma::IMG;
-  constexpr int PER = Dma::PER;
-  constexpr int NDB = D / 32;   // 32-wide blocks of dq
-  constexpr int NQ = 2 * NDB;   // MFMAs per key tile
-  constexpr int PD = 2;         // K operands read this many MFMAs ahead
+  constexpr int KPER = Dma::PER;    // loads per tile of a K wave
+  constexpr int SPER = 4;           // loads per tile of a dS wave (2 tiles x 2 KB)
+  constexpr int NDB = D / 32;       // 32-wide blocks of dq
+  constexpr int NDH = NDB / 2;      // the blocks of one half of d
+  constexpr int NKO = 2 * NDH;      // K operands per tile (each feeds 2 MFMAs)
+  constexpr int PD = 2;             // K operands read this many ahead
   constexpr int R = PD + 1;
-  constexpr int AS = NSD - 1;   // dS tiles in flight ahead of the one in use
-  constexpr int AK = NK - 1;    // K tiles in flight ahead of the one in use
-  static_assert(AK >= 1 && AK <= AS, "rings");
-  __shared__ __attribute__((aligned(1024))) char kt[NK * KIMG];
-  __shared__ __attribute__((aligned(1024))) char st[NSD * NW * 2048];
+  static_assert(KPER <= 2 * NKO && SPER <= 2 * NKO, "one load per MFMA");
+  __shared__ __attribute__((aligned(1024))) char kt0[KIMG];
+  __shared__ __attribute__((aligned(1024))) char kt1[KIMG];
+  __shared__ __attribute__((aligned(1024))) char st0[NW * 2048];
+  __shared__ __attribute__((aligned(1024))) char st1[NW * 2048];
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  auto kbuf = [&](auto c) -> LDS_AS char* {
+    constexpr int b = decltype(c)::value;
+    return b == 0 ? (LDS_AS char*)kt0 : (LDS_AS char*)kt1;
+  };
+  auto sbuf = [&](auto c) -> LDS_AS char* {
+    constexpr int b = decltype(c)::value;
+    return b == 0 ? (LDS_AS char*)st0 : (LDS_AS char*)st1;
+  };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool kwave = wave < 2;
   const int g = lane >> 5;
   const int T = a.T;
   const int W = a.window;
@@ -113,7 +135,8 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq_ds_kernel(BwdArgs a) {
   const WorkItem w = decode_work(blockIdx.x, nqb, a.B, a.Hkv, G, true);
   const int h = w.hkv * G + w.r;
   const int q0 = w.blk * BQ;
-  const int qtw = q0 / BKV + wave;
+  const int qp = wave >> 1;   // its query tiles 2 qp, 2 qp + 1 (of the four)
+  const int dh = wave & 1;    // its half of d
   const size_t bh = (size_t)w.b * a.H + h;
   const size_t bkv = (size_t)w.b * a.Hkv + w.hkv;
   const bf16* Kp = a.k + bkv * T * D;
@@ -124,115 +147,133 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq_ds_kernel(BwdArgs a) {
   const int t_hi = min(T, q0 + BQ) - 1;
   const int nu = t_hi / BKV - t_lo + 1;
 
-  // this wave's workspace row (query tile qtw): nkt slots of 2 KB, empty
-  // past the last query tile
-  const int wrow = __builtin_amdgcn_readfirstlane((int)(bh * a.nqt_ws) +
-                                                  (qtw < a.nqt_ws ? qtw : 0));
-  const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
-      a.dsw + (size_t)wrow * nkt * 1024, 0,
-      __builtin_amdgcn_readfirstlane(qtw < a.nqt_ws ? nkt * 2048 : 0), 0x00020000);
+  // a dS wave loads the tiles of query tiles qt_0 + cw0 + i, i = 0, 1: each
+  // one's workspace row as a buffer of nkt slots of 2 KB, empty past the
+  // last query tile
+  const int cw0 = kwave ? 0 : 2 * (wave - 2);
+  __amdgpu_buffer_rsrc_t srs[2];
+  int sq[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    sq[i] = q0 / BKV + cw0 + i;
+    const int row = __builtin_amdgcn_readfirstlane((int)(bh * a.nqt_ws) +
+                                                   (sq[i] < a.nqt_ws ? sq[i] : 0));
+    srs[i] = __builtin_amdgcn_make_buffer_rsrc(
+        a.dsw + (size_t)row * nkt * 1024, 0,
+        __builtin_amdgcn_readfirstlane(sq[i] < a.nqt_ws ? nkt * 2048 : 0), 0x00020000);
+  }
 
   Dma dm;
-  dm.init(wave, lane);
+  dm.init(wave & 1, lane);
   LaneOffs<D> lo;
   lo.init(lane);
 
-  // K tile t_lo + u into buffer u % NK: every wave issues PER loads
-  // (branch-free, as TileDma::load_piece does them)
-  auto load_k = [&](int u) __attribute__((always_inline)) {
-    LDS_AS char* kd = (LDS_AS char*)kt + (u % NK) * KIMG;
-#pragma unroll
-    for (int k = 0; k < PER; ++k) dm.load_piece(k, Kp, T * D * 2, kd, (t_lo + u) * BKV, wave);
-  };
-  // this wave's dS tile for key tile t_lo + u into ring slot u % NSD: two
-  // loads; a slot outside the band is moved to kNoSlot, far past any row's
-  // range, so that adding the lane offset cannot wrap it back into range
+  // load p of this wave's share of tile v (t_lo + v) into ring slot c:
+  // a K wave's piece p of the K tile, a dS wave's piece p & 1 of query tile
+  // cw0 + (p >> 1)'s dS tile.  Past the last tile the K range is empty and
+  // the dS slot is kNoSlot (far past any row's range, so that adding the
+  // lane offset cannot wrap it back into range): zero reads, no traffic.
   constexpr unsigned kNoSlot = 0x40000u;
-  auto load_s = [&](int u) __attribute__((always_inline)) {
-    const unsigned j0 = (unsigned)(t_lo + u - qtw + nkt - 1);
-    const unsigned j = j0 < (unsigned)nkt ? j0 : kNoSlot;
-    LDS_AS char* sd = (LDS_AS char*)st + ((u % NSD) * NW + wave) * 2048;
+  auto load = [&](int p, int v, auto c) __attribute__((always_inline)) {
+    if (kwave) {
+      dm.load_piece(p, Kp, v < nu ? T * D * 2 : 0, kbuf(c), (t_lo + v) * BKV, wave & 1);
+    } else {
+      const int i = p >> 1;
+      const unsigned j0 = (unsigned)(t_lo + v - sq[i] + nkt - 1);
+      const unsigned j = v < nu && j0 < (unsigned)nkt ? j0 : kNoSlot;
+      LDS_AS char* sd = sbuf(c) + (cw0 + i) * 2048 + (p & 1) * 1024;
 #if defined(__HIP_DEVICE_COMPILE__)
-#pragma unroll
-    for (int p = 0; p < 2; ++p)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(srs, (LDS_AS void*)(sd + p * 1024), 16,
-                                               j * 2048u + p * 1024 + 16 * lane, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(srs[i], (LDS_AS void*)sd, 16,
+                                               j * 2048u + (p & 1) * 1024 + 16 * lane, 0, 0, 0);
 #endif
+    }
   };
 
-  f32x16 acc[NDB];
+  f32x16 acc[2][NDH];
 #pragma unroll
-  for (int db = 0; db < NDB; ++db)
+  for (int qi = 0; qi < 2; ++qi)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
+    for (int db = 0; db < NDH; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[qi][db][i] = 0.f;
 
-  // Issue order: dS(0 .. AS - AK - 1), then K(v), dS(v + AS - AK) for
-  // v < AK; iteration u then issues K(u + AK), dS(u + AS).  Vector-memory
-  // operations complete in issue order, so at the top of iteration u it is
-  // enough that at most NWAIT operations are outstanding -- those issued
-  // after the later of K(u) and dS(u): with AK < AS, dS(u + AS - AK) and
-  // the AK - 1 iterations after K(u)'s; with AK = AS (dS(u) right after
-  // K(u)) the AK - 1 iterations after.  Near the end fewer were issued: wait
-  // for all.
-  constexpr int NWAIT = (AK < AS ? 2 : 0) + (AK - 1) * (PER + 2);
-  static_assert(NWAIT < 64, "vmcnt");
+  // tile 0 up front, into slot 0
+  auto load_all = [&](int v, auto c) __attribute__((always_inline)) {
+    if (kwave) {
 #pragma unroll
-  for (int u = 0; u < AS - AK; ++u)
-    if (u < nu) load_s(u);
+      for (int p = 0; p < KPER; ++p) load(p, v, c);
+    } else {
 #pragma unroll
-  for (int v = 0; v < AK; ++v) {
-    if (v < nu) load_k(v);
-    if (v + AS - AK < nu) load_s(v + AS - AK);
-  }
+      for (int p = 0; p < SPER; ++p) load(p, v, c);
+    }
+  };
+  load_all(0, I0{});
 
-  for (int u = 0; u < nu; ++u) {
-    if (u + AS - 1 < nu) wait_vmem<NWAIT>();
-    else wait_vmem();
+  // tile u from slot c, tile u + 1 loading into slot n (the one tile u - 1
+  // used)
+  auto step = [&](const int u, auto c, auto n) __attribute__((always_inline)) {
+    wait_vmem();
     lds_barrier();
-    // the buffers unit u - 1 used are free once every wave has passed the
-    // barrier
-    if (u + AK < nu) load_k(u + AK);
-    if (u + AS < nu) load_s(u + AS);
-    const LDS_AS char* kb = (const LDS_AS char*)kt + (u % NK) * KIMG;
-    const LDS_AS char* sb = (const LDS_AS char*)st + ((u % NSD) * NW + wave) * 2048;
-    bf16x8 dsop[2];
-    dsop[0] = ds_tile_tr(sb, 0, lane);
-    dsop[1] = ds_tile_tr(sb, 1, lane);
-    auto f = [&](int k) { return lds_tr_op<D>(kb, lo, k / NDB, k % NDB); };
+    // the slot tile u - 1 used is free once every wave has passed the
+    // barrier: tile u + 1 goes there, one load after each MFMA below
+    const LDS_AS char* kb = kbuf(c);
+    const LDS_AS char* sb = sbuf(c) + 2 * qp * 2048;
+    bf16x8 dsop[2][2];   // [query tile][key chunk]
+#pragma unroll
+    for (int qi = 0; qi < 2; ++qi)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) dsop[qi][c] = ds_tile_tr(sb + qi * 2048, c, lane);
+    // K operand k: key chunk k / NDH, block dh NDH + k % NDH of d
+    auto f = [&](int k) { return lds_tr_op<D>(kb, lo, k / NDH, dh * NDH + k % NDH); };
     bf16x8 op[R];
 #pragma unroll
     for (int k = 0; k < PD; ++k) op[k] = f(k);
 #pragma unroll
-    for (int k = 0; k < NQ; ++k) {
-      if (k + PD < NQ) op[(k + PD) % R] = f(k + PD);
-      acc[k % NDB] = mfma32(op[k % R], dsop[k / NDB], acc[k % NDB]);
+    for (int k = 0; k < NKO; ++k) {
+      if (k + PD < NKO) op[(k + PD) % R] = f(k + PD);
+#pragma unroll
+      for (int qi = 0; qi < 2; ++qi) {
+        acc[qi][k % NDH] = mfma32(op[k % R], dsop[qi][k / NDH], acc[qi][k % NDH]);
+        const int m = 2 * k + qi;
+        if (kwave ? m < KPER : m < SPER) load(m, u + 1, n);
+      }
     }
+  };
+  for (int u = 0; u < nu; u += 2) {
+    step(u, I0{}, I1{});
+    step(u + 1, I1{}, I0{});
   }
 
-  // slot s = lane % 32 of the accumulator holds query 32 qtw + pi(s)
+  // slot s = lane % 32 of query tile qi's accumulator holds query
+  // 32 (qt_0 + 2 qp + qi) + pi(s); its blocks are dh NDH .. of d
   const int s = lane & 31;
-  const int qrow = qtw * BKV + 16 * ((s >> 3) & 1) + 8 * ((s & 7) >> 2) + 4 * (s >> 4) + (s & 3);
-  if (qrow < T) {
-    bf16* Qd = a.dq + (bh * T + qrow) * D;
+  const int ps = 16 * ((s >> 3) & 1) + 8 * ((s & 7) >> 2) + 4 * (s >> 4) + (s & 3);
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+  for (int qi = 0; qi < 2; ++qi) {
+    const int qrow = (q0 / BKV + 2 * qp + qi) * BKV + ps;
+    if (qrow < T) {
+      bf16* Qd = a.dq + (bh * T + qrow) * D;
 #pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        float x[4];
+      for (int j = 0; j < NDH; ++j)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) x[e] = acc[db][4 * i4 + e] * a.scale;
-        if (a.rope_cs) {
-          // RoPE backward fused into the store (pairs 16 db + 4 i4 + 2 g + {0, 1})
-          const float4 r = *(const float4*)(a.rope_cs + (size_t)qrow * D +
-                                            2 * (16 * db + 4 * i4 + 2 * g));
-          rope_pair(r.x, -r.y, x[0], x[1]);
-          rope_pair(r.z, -r.w, x[2], x[3]);
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const int db = dh * NDH + j;
+          float x[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[e] = acc[qi][j][4 * i4 + e] * a.scale;
+          if (a.rope_cs) {
+            // RoPE backward fused into the store (pairs 16 db + 4 i4 + 2 g + {0, 1})
+            const float4 r = *(const float4*)(a.rope_cs + (size_t)qrow * D +
+                                              2 * (16 * db + 4 * i4 + 2 * g));
+            rope_pair(r.x, -r.y, x[0], x[1]);
+            rope_pair(r.z, -r.w, x[2], x[3]);
+          }
+          bf16x4 v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = (bf16)x[e];
+          *(bf16x4*)(Qd + 32 * db + 8 * i4 + 4 * g) = v;
         }
-        bf16x4 v;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = (bf16)x[e];
-        *(bf16x4*)(Qd + 32 * db + 8 * i4 + 4 * g) = v;
-      }
+    }
   }
 }
 
@@ -253,9 +294,9 @@ hipError_t launch_bwd_dq_ds(const BwdArgs& a, int d, hipStream_t stream) {
   const int nqb = (a.T + 127) / 128;
   const dim3 grid((unsigned)nqb * a.B * a.H);
   if (d == 128)
-    hipLaunchKernelGGL((fa_bwd_dq_ds_kernel<128, 4, 4>), grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(fa_bwd_dq_ds_kernel<128>, grid, dim3(256), 0, stream, a);
   else if (d == 256)
-    hipLaunchKernelGGL((fa_bwd_dq_ds_kernel<256, 2, 4>), grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(fa_bwd_dq_ds_kernel<256>, grid, dim3(256), 0, stream, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
