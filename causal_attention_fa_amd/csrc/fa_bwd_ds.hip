@@ -82,19 +82,28 @@ __device__ __forceinline__ bf16x8 ds_tile_tr(const LDS_AS char* tile, int c16, i
 // for query tiles 2 (w / 2) and 2 (w / 2) + 1 and the half w % 2 of d: each
 // transposed K operand it reads (lds_tr_op) feeds two MFMAs, one per query
 // tile; dS read transposed (ds_tile_tr).
-// Loads: waves 0 and 1 load the K tiles (mostly L2 hits), waves 2 and 3 the
-// dS tiles of all four query tiles (streamed from HBM, read once), each
-// tile's loads spread one per MFMA of the tile before it (a burst stalls
-// the issuing wave) and branch-free (past the last tile they read an empty
-// range).  Two LDS slots, each an object of its own, and the loop unrolled
-// by two, so every slot is a compile-time choice: the compiler then sees
-// that the loads in flight do not write the slot being read (with one
-// array, or with loads left in flight across the barrier, it waited for all
-// of them before the reads: no prefetch at all).  Each step waits for its
-// own loads before the barrier.  The loop is padded to whole pairs of
-// tiles; a tile past the last reads zeros and adds exact zeros.  The store
-// writes slot s's row to query 32 qt + pi(s), scaled (and rotated back,
-// with fused RoPE).
+// Loads go through registers, split by kind between the waves: waves 0 and
+// 1 load the K tiles (mostly L2 hits) AK = 2 tiles ahead, waves 2 and 3 the
+// dS tiles of all four query tiles (streamed from HBM, read once) AH = 4
+// tiles ahead, each from a ring of register sets; at its tile's step a wave
+// writes its registers into the LDS slot (where a direct load of the tile
+// image would have put them) just before the barrier that publishes it.  A
+// wave's vector-memory operations complete in issue order, so it waits for
+// its oldest tile alone, and with one kind per wave neither kind waits
+// behind the other.  (Direct HBM -> LDS loads kept in flight across a
+// barrier made the compiler wait for all of them before any LDS read: the
+// tiles then got one step of latency, too little for HBM; d = 256 dQ from
+// dS 0.37 -> 0.34 ms at gemma-global, 0.32 -> 0.27 at gemma-local.)  The two
+// kinds run separate copies of the loop (the same steps and barriers), so
+// that the compiler's wait tracking of one kind never merges with the
+// other's.  The loads of a tile are spread one per MFMA of the step that
+// issues them and are branch-free (past the last tile they read an empty
+// range, so every wave issues the same count per step and the waits are
+// exact).  Two LDS slots, each an object of its own, and the loop unrolled by
+// four, so slots and register sets are compile-time choices; the loop is
+// padded to whole groups, and a tile past the last reads zeros and adds exact
+// zeros.  The store writes slot s's row to query 32 qt + pi(s), scaled (and
+// rotated back, with fused RoPE).
 template <int D>
 __global__ __launch_bounds__(256, 2) void fa_bwd_dq_ds_kernel(BwdArgs a) {
   constexpr int NW = 4, BQ = 32 * NW, BKV = 32;
@@ -168,25 +177,50 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq_ds_kernel(BwdArgs a) {
   LaneOffs<D> lo;
   lo.init(lane);
 
-  // load p of this wave's share of tile v (t_lo + v) into ring slot c:
-  // a K wave's piece p of the K tile, a dS wave's piece p & 1 of query tile
-  // cw0 + (p >> 1)'s dS tile.  Past the last tile the K range is empty and
-  // the dS slot is kNoSlot (far past any row's range, so that adding the
-  // lane offset cannot wrap it back into range): zero reads, no traffic.
-  constexpr unsigned kNoSlot = 0x40000u;
-  auto load = [&](int p, int v, auto c) __attribute__((always_inline)) {
-    if (kwave) {
-      dm.load_piece(p, Kp, v < nu ? T * D * 2 : 0, kbuf(c), (t_lo + v) * BKV, wave & 1);
-    } else {
-      const int i = p >> 1;
-      const unsigned j0 = (unsigned)(t_lo + v - sq[i] + nkt - 1);
-      const unsigned j = v < nu && j0 < (unsigned)nkt ? j0 : kNoSlot;
-      LDS_AS char* sd = sbuf(c) + (cw0 + i) * 2048 + (p & 1) * 1024;
+  // K wave: piece p of K tile v (t_lo + v) -- the 16 bytes a direct load of
+  // the padded tile image would put at this lane's place in piece
+  // (wave & 1) + 2 p -- into registers, AK tiles ahead; past the last tile
+  // the range is empty (zeros, no traffic)
+  constexpr int AK = 2;
+  u32x4 stk[AK][KPER];
+  auto load_kr = [&](int p, int v) __attribute__((always_inline)) -> u32x4 {
 #if defined(__HIP_DEVICE_COMPILE__)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(srs[i], (LDS_AS void*)sd, 16,
-                                               j * 2048u + (p & 1) * 1024 + 16 * lane, 0, 0, 0);
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                         Dma::rsrc(Kp, v < nu ? T * D * 2 : 0, (t_lo + v) * BKV),
+                                         dm.voff[p], 0, 0));
+#else
+    return u32x4{};
 #endif
-    }
+  };
+  auto put_k = [&](const u32x4 (&r)[KPER], auto c) __attribute__((always_inline)) {
+#pragma unroll
+    for (int p = 0; p < KPER; ++p)
+      *(LDS_AS u32x4*)(kbuf(c) + ((wave & 1) + 2 * p) * 1024 + 16 * lane) = r[p];
+  };
+  // dS wave: piece p (query tile cw0 + (p >> 1), half p & 1) of dS tile v
+  // into registers; a slot outside the band or past the last tile is moved to
+  // kNoSlot, far past any row's range, so that adding the lane offset cannot
+  // wrap it back into range: zeros, no traffic
+  constexpr unsigned kNoSlot = 0x40000u;
+  constexpr int AH = 4;
+  u32x4 stg[AH][SPER];
+  auto load_s = [&](int p, int v) __attribute__((always_inline)) -> u32x4 {
+    const int i = p >> 1;
+    const unsigned j0 = (unsigned)(t_lo + v - sq[i] + nkt - 1);
+    const unsigned j = v < nu && j0 < (unsigned)nkt ? j0 : kNoSlot;
+#if defined(__HIP_DEVICE_COMPILE__)
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                         srs[i], j * 2048u + (p & 1) * 1024 + 16 * lane, 0, 0));
+#else
+    return u32x4{};
+#endif
+  };
+  // ... and its registers into LDS slot c at the places a direct load would
+  // have written them (lane l at + 16 l of each 1 KB half)
+  auto put_s = [&](const u32x4 (&r)[SPER], auto c) __attribute__((always_inline)) {
+#pragma unroll
+    for (int p = 0; p < SPER; ++p)
+      *(LDS_AS u32x4*)(sbuf(c) + (cw0 + (p >> 1)) * 2048 + (p & 1) * 1024 + 16 * lane) = r[p];
   };
 
   f32x16 acc[2][NDH];
@@ -197,32 +231,30 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq_ds_kernel(BwdArgs a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[qi][db][i] = 0.f;
 
-  // tile 0 up front, into slot 0
-  auto load_all = [&](int v, auto c) __attribute__((always_inline)) {
-    if (kwave) {
-#pragma unroll
-      for (int p = 0; p < KPER; ++p) load(p, v, c);
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  // tile u: LDS slot c (K tile u + 1 loading into slot n, the one tile u - 1
+  // used), dS registers x (refilled with tile u + AH once in LDS)
+  auto step = [&](auto kind, const int u, auto c, auto n, auto x) __attribute__((always_inline)) {
+    constexpr bool KW = decltype(kind)::value;
+    constexpr int X = decltype(x)::value;
+    if constexpr (KW) {
+      // tile u's registers are this wave's oldest outstanding loads
+      wait_vmem<(AK - 1) * KPER>();
+      put_k(stk[X % AK], c);
     } else {
-#pragma unroll
-      for (int p = 0; p < SPER; ++p) load(p, v, c);
+      // tile u's registers are this wave's oldest outstanding loads
+      wait_vmem<(AH - 1) * SPER>();
+      put_s(stg[X], c);
     }
-  };
-  load_all(0, I0{});
-
-  // tile u from slot c, tile u + 1 loading into slot n (the one tile u - 1
-  // used)
-  auto step = [&](const int u, auto c, auto n) __attribute__((always_inline)) {
-    wait_vmem();
     lds_barrier();
-    // the slot tile u - 1 used is free once every wave has passed the
-    // barrier: tile u + 1 goes there, one load after each MFMA below
     const LDS_AS char* kb = kbuf(c);
     const LDS_AS char* sb = sbuf(c) + 2 * qp * 2048;
     bf16x8 dsop[2][2];   // [query tile][key chunk]
 #pragma unroll
     for (int qi = 0; qi < 2; ++qi)
 #pragma unroll
-      for (int c = 0; c < 2; ++c) dsop[qi][c] = ds_tile_tr(sb + qi * 2048, c, lane);
+      for (int cc = 0; cc < 2; ++cc) dsop[qi][cc] = ds_tile_tr(sb + qi * 2048, cc, lane);
     // K operand k: key chunk k / NDH, block dh NDH + k % NDH of d
     auto f = [&](int k) { return lds_tr_op<D>(kb, lo, k / NDH, dh * NDH + k % NDH); };
     bf16x8 op[R];
@@ -235,14 +267,38 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq_ds_kernel(BwdArgs a) {
       for (int qi = 0; qi < 2; ++qi) {
         acc[qi][k % NDH] = mfma32(op[k % R], dsop[qi][k / NDH], acc[qi][k % NDH]);
         const int m = 2 * k + qi;
-        if (kwave ? m < KPER : m < SPER) load(m, u + 1, n);
+        if constexpr (KW) {
+          if (m < KPER) stk[X % AK][m] = load_kr(m, u + AK);
+        } else {
+          if (m < SPER) stg[X][m] = load_s(m, u + AH);
+        }
       }
     }
   };
-  for (int u = 0; u < nu; u += 2) {
-    step(u, I0{}, I1{});
-    step(u + 1, I1{}, I0{});
-  }
+  auto run = [&](auto kind) __attribute__((always_inline)) {
+    // up front: K tile 0 into slot 0; dS tiles 0 .. AH - 1 into the registers
+    if constexpr (decltype(kind)::value) {
+#pragma unroll
+      for (int v = 0; v < AK; ++v)
+#pragma unroll
+        for (int p = 0; p < KPER; ++p) stk[v][p] = load_kr(p, v);
+    } else {
+#pragma unroll
+      for (int v = 0; v < AH; ++v)
+#pragma unroll
+        for (int p = 0; p < SPER; ++p) stg[v][p] = load_s(p, v);
+    }
+    for (int u = 0; u < nu; u += AH) {
+      step(kind, u, I0{}, I1{}, I0{});
+      step(kind, u + 1, I1{}, I0{}, I1{});
+      step(kind, u + 2, I0{}, I1{}, I2{});
+      step(kind, u + 3, I1{}, I0{}, I3{});
+    }
+  };
+  if (kwave)
+    run(std::true_type{});
+  else
+    run(std::false_type{});
 
   // slot s = lane % 32 of query tile qi's accumulator holds query
   // 32 (qt_0 + 2 qp + qi) + pi(s); its blocks are dh NDH .. of d
