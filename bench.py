@@ -568,6 +568,9 @@ def main():
                 cand["stored_ds"] = r["stored_ds_bwd_ms"]
             r["choice"] = min(cand, key=cand.get)
             r["library_default"] = "stored_ds" if "dq_ds" in fa.fa_bwd_kernels(w.d) else "recompute"
+            # how far the default is from the fastest (run-to-run spread: ~2 %)
+            r["default_vs_choice_pct"] = round(
+                100 * (cand[r["library_default"]] / cand[r["choice"]] - 1), 2)
             dqs[name] = r
         out["dq_strategy"] = dqs
 
