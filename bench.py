@@ -543,6 +543,7 @@ def main():
             w = synth.WORKLOADS.get(name)
             if w is None or w.dv != w.d:
                 continue
+            log(f"[bench] dq strategy {name}")
             r = {}
             for mode, key in ((1, "recompute"), (2, "stored_ds")):
                 fa.fa_set_dq_mode(mode)
