@@ -9,9 +9,12 @@
 // writing it out as bf16 -- the precision the dQ product consumes it in --
 // turns the dQ pass from S, dP and dQ products (6d flops per visible pair)
 // into the dQ product alone (2d), at the price of 2 bytes per visible pair
-// written and read once.  At d = 128, 256 that traffic is far cheaper than
-// the recomputation; the workspace ([B, H, T/32, band] tiles of 2 KB)
-// is O(T x window), which one GPU's HBM holds at the sizes of interest.
+// written and read once.  At d = 256 that traffic costs far less than the
+// 4d of recomputation it replaces; at d = 128 the two are close and the
+// recomputing pass measured faster where the dS volume is large (the dK/dV
+// pass's stores cost more per byte there).  The workspace ([B, H, T/32,
+// band] tiles of 2 KB) is O(T x window), which one GPU's HBM holds at the
+// sizes of interest.
 //
 // Workspace layout: tile (b, h, qt, j) holds dS for query tile qt (queries
 // 32 qt ..) and key tile kt = qt - nkt + 1 + j, as the dK/dV pass's wave

@@ -282,21 +282,24 @@ int fa_set_stage_events(void* const* events, int count);
  *                          alone, the key-parallel dK/dV pass writing every
  *                          visible dS tile (bf16) to a workspace, then the
  *                          query-parallel dQ pass dq = scale dS K reading it
- *                          (d = d_v = 128; taken when the workspace, 2 bytes
- *                          per (query, key tile of 32) pair of the band, fits
- *                          a quarter of the device's memory);
+ *                          (d = d_v = 256 in mode 0, 128 and 256 in mode 2;
+ *                          taken when the workspace, 2 KB per (query tile,
+ *                          key tile) of the band, fits a quarter of the
+ *                          device's memory);
  *   "dq,dkdv"           -- the query-parallel dQ pass recomputing S and dP
  *                          (it also writes D), then the dK/dV pass;
  * null for sizes the backward does not support.  fa_bwd_sink and
  * fa_bwd_noalloc always run "dq,dkdv".  Static string owned by the library;
- * host only, no device work.  (ARCHITECTURES.md, prioritised plan: the
- * backward's dQ either by a separate query-parallel pass or accumulated by
- * the key-parallel pass, chosen by measurement.) */
+ * host only, no device work.  (Forge attention.h commit log, "Measured
+ * findings": register pressure, not bandwidth, dominates the attention
+ * backward -- storing dS trades the recomputation's registers and flops
+ * for HBM traffic, which pays at d = 256.) */
 const char* fa_bwd_kernels(int d, int d_v);
 
 /* Process-wide dQ strategy of the bf16 backward, for measurement and tests:
- * 0 (the default) takes dQ from stored dS where fa_bwd_kernels says so, 1
- * always runs the recomputing dQ pass.  Both give dq within the parity
+ * 0 (the default) takes dQ from stored dS at d = 256, where it measured
+ * faster, 1 always runs the recomputing dQ pass, 2 takes dQ from stored dS
+ * at d = 128 and 256.  Both give dq within the parity
  * bound of the oracle; dk and dv are bit for bit the same in both.  Returns
  * the previous mode, or FA_ERR_INVALID_ARG for another value.  Calls
  * already enqueued keep the mode they were enqueued with. */
