@@ -203,6 +203,19 @@ int scratch_on_stream_device(hipStream_t stream, const char* fn, float** out) {
 
 int resolve_window(int window, int T) { return window >= T ? 0 : window; }
 
+// Shape of the dS workspace for a resolved window W: ceil(T/32) query tiles
+// per head, and the key tiles one query tile can see -- its band:
+// keys 32 qt - W + 1 .. 32 qt + 31, i.e. ceil((W - 1) / 32) + 1 tiles under a
+// window (each holding a visible pair of the query tile), every earlier tile
+// without one (at most ceil(T/32)).
+struct DsShape {
+  int nqt, nkt;
+};
+DsShape ds_shape(int T, int W) {
+  const int nqt = (T + 31) / 32;
+  return {nqt, W > 0 ? std::min(nqt, (W - 1 + 31) / 32 + 1) : nqt};
+}
+
 constexpr float kLog2e = 1.4426950408889634f;
 
 int attn_fwd(bool f32, const void* q, const void* k, const void* v, void* o, float* lse, int B,
@@ -343,8 +356,8 @@ int attn_bwd(bool f32, const void* q, const void* k, const void* v, const void* 
   // dS workspace: [B, H, ceil(T/32), band] tiles of 2 KB, where band = the
   // key tiles one query tile sees (ceil((W - 1) / 32) + 1 under a window)
   fa::bf16* dsw = nullptr;
-  const int nqt = (T + 31) / 32;
-  const int nkt = W > 0 ? std::min(nqt, (W - 1 + 31) / 32 + 1) : nqt;
+  const DsShape dsh = ds_shape(T, W);
+  const int nqt = dsh.nqt, nkt = dsh.nkt;
   if (!f32 && !static_rows && !dsinks && fa::ds_mode_applies(g_dq_mode.load(), d, d_v)) {
     const size_t tiles = (size_t)B * H * nqt * nkt;
     size_t cap = 0;
@@ -552,6 +565,19 @@ int fa_decode(const void* q, const void* k_cache, const void* v_cache, const int
 
 const char* fa_bwd_kernels(int d, int d_v) {
   return fa::bwd_kernel_plan(d, d_v, g_dq_mode.load());
+}
+
+int fa_bwd_workspace(int B, int H, int T, int d, int d_v, int window, size_t* bytes,
+                     int* query_tiles, int* band_tiles) {
+  int rc = check_attn("fa_bwd_workspace", B, H, H, T, d, 1.f, window, 0, 0.f, d_v);
+  if (rc) return rc;
+  if (!bytes || !query_tiles || !band_tiles)
+    return fail(FA_ERR_INVALID_ARG, "fa_bwd_workspace: null output pointer");
+  const DsShape s = ds_shape(T, resolve_window(window, T));
+  *query_tiles = s.nqt;
+  *band_tiles = s.nkt;
+  *bytes = fa::ds_mode_applies(g_dq_mode.load(), d, d_v) ? (size_t)B * H * s.nqt * s.nkt * 2048 : 0;
+  return FA_OK;
 }
 
 int fa_set_dq_mode(int mode) {

@@ -83,6 +83,9 @@ _lib.fa_set_stage_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), _I]
 _lib.fa_set_stage_events.restype = _I
 _lib.fa_bwd_kernels.argtypes = [_I, _I]
 _lib.fa_bwd_kernels.restype = ctypes.c_char_p
+_lib.fa_bwd_workspace.argtypes = [_I, _I, _I, _I, _I, _I, ctypes.POINTER(ctypes.c_size_t),
+                                  ctypes.POINTER(_I), ctypes.POINTER(_I)]
+_lib.fa_bwd_workspace.restype = _I
 _lib.fa_set_dq_mode.argtypes = [_I]
 _lib.fa_set_dq_mode.restype = _I
 _lib.fa_measure_dq_atomics.argtypes = [_I, _I, _I, _I, _I, _I, ctypes.POINTER(ctypes.c_float)]
@@ -95,7 +98,7 @@ EXPORTS = ("fa_fwd", "fa_bwd", "fa_bwd_noalloc", "fa_fwd_sink", "fa_bwd_sink", "
            "fa_decode", "fa_decode_splits", "rope_apply", "rope_apply_bwd", "fa_fwd_f32",
            "fa_bwd_f32", "rope_apply_f32", "rope_apply_bwd_f32", "fa_layer_window", "fa_rope_inv_freq",
            "fa_rope_inv_freq_llama3", "fa_layer_rope_theta", "fa_set_stage_events",
-           "fa_bwd_kernels", "fa_set_dq_mode", "fa_measure_dq_atomics", "fa_last_error")
+           "fa_bwd_kernels", "fa_bwd_workspace", "fa_set_dq_mode", "fa_measure_dq_atomics", "fa_last_error")
 
 
 class FAError(RuntimeError):
@@ -235,6 +238,16 @@ def fa_bwd_kernels(d, d_v=None):
     if r is None:
         raise FAError(FA_ERR_UNSUPPORTED, f"fa_bwd_kernels: unsupported head sizes ({d}, {d_v})")
     return r.decode().split(",")
+
+
+def fa_bwd_workspace(B, H, T, d, d_v=None, window=0):
+    """(bytes, query tiles per head, band slots per query tile) of the dS
+    workspace the bf16 backward takes for these sizes under the current dQ
+    mode (bytes 0: the recomputing dQ pass runs)."""
+    nb, nq, nk = ctypes.c_size_t(), _I(), _I()
+    _check(_lib.fa_bwd_workspace(B, H, T, d, d if d_v is None else d_v, window,
+                                 ctypes.byref(nb), ctypes.byref(nq), ctypes.byref(nk)))
+    return nb.value, nq.value, nk.value
 
 
 def fa_set_dq_mode(mode):

@@ -65,6 +65,8 @@
 #ifndef CAUSAL_FA_H
 #define CAUSAL_FA_H
 
+#include <stddef.h>
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -295,6 +297,19 @@ int fa_set_stage_events(void* const* events, int count);
  * backward -- storing dS trades the recomputation's registers and flops
  * for HBM traffic, which pays at d = 256.) */
 const char* fa_bwd_kernels(int d, int d_v);
+
+/* The dS workspace the bf16 fa_bwd (and fa_bwd_rope) takes for these sizes
+ * under the current dQ mode, for callers that plan device memory: *bytes
+ * (0 when the recomputing dQ pass runs), and its shape -- *query_tiles =
+ * ceil(T/32) query tiles per (b, h), each with *band_tiles 2 KB slots, one
+ * per key tile of 32 that holds a visible key of the query tile (under a
+ * window W: ceil((W - 1)/32) + 1, else ceil(T/32); ARCHITECTURES.md,
+ * prioritised plan, wave 2, item 8: the mask q - W < k <= q).  The backward
+ * takes it from the library's pool when it fits a quarter of the device's
+ * memory.  Host only, no device work.  Returns 0, or FA_ERR_INVALID_ARG /
+ * FA_ERR_UNSUPPORTED as fa_bwd's size checks (H stands for Hkv). */
+int fa_bwd_workspace(int B, int H, int T, int d, int d_v, int window,
+                     size_t* bytes, int* query_tiles, int* band_tiles);
 
 /* Process-wide dQ strategy of the bf16 backward, for measurement and tests:
  * 0 (the default) takes dQ from stored dS at d = 256, where it measured

@@ -194,3 +194,42 @@ def test_bwd_noalloc_rejects_oversize_before_device_work():
     bad[6] = bad[0]  # dq aliases q: the shared validation still applies
     assert lib.fa_bwd_noalloc(*bad, 1, 2, 2, 8, 64, 0.125, 0, 0, 0.0, None) == -1
     assert "overlaps" in fa.fa_last_error()
+
+
+@pytest.mark.parametrize("T,W", [(1, 0), (31, 0), (33, 1), (100, 31), (100, 32), (100, 33),
+                                 (257, 64), (300, 97), (640, 257), (1000, 999), (1000, 1000),
+                                 (130, 5000)])
+def test_bwd_workspace_band_covers_exactly_the_visible_tiles(T, W):
+    """The dS workspace shape against the oracle's mask (q - W < k <= q),
+    brute force over every (query, key) pair: each visible pair's key tile
+    lands in a slot of its query tile's band (slot kt - qt + band - 1 in
+    [0, band)), and each slot of a query tile's band that names a real key
+    tile holds at least one visible pair of it (no slot is wasted on a tile
+    the query tile cannot see).  Bytes: 2 KB per slot for B*H heads at
+    d = 256 in the default mode and at d = 128 only in mode 2."""
+    from oracle import attention as OA
+    _, nqt, band = fa.fa_bwd_workspace(1, 1, T, 256, 256, W)
+    assert nqt == (T + 31) // 32
+    vis = OA.visibility(np.arange(T), np.arange(T), W if W < T else 0)
+    qi, kj = np.nonzero(vis)
+    slot = kj // 32 - qi // 32 + band - 1
+    assert slot.min() >= 0 and slot.max() < band
+    seen = np.zeros((nqt, band), dtype=bool)
+    seen[qi // 32, slot] = True
+    for qt in range(nqt):
+        for j in range(band):
+            kt = qt - band + 1 + j
+            assert seen[qt, j] == (kt >= 0), (qt, j, kt)
+    prev = fa.fa_set_dq_mode(0)
+    try:
+        assert fa.fa_bwd_workspace(2, 3, T, 256, 256, W)[0] == 2 * 3 * nqt * band * 2048
+        assert fa.fa_bwd_workspace(2, 3, T, 128, 128, W)[0] == 0
+        fa.fa_set_dq_mode(2)
+        assert fa.fa_bwd_workspace(2, 3, T, 128, 128, W)[0] == 2 * 3 * nqt * band * 2048
+        assert fa.fa_bwd_workspace(2, 3, T, 64, 64, W)[0] == 0
+        fa.fa_set_dq_mode(1)
+        assert fa.fa_bwd_workspace(2, 3, T, 256, 256, W)[0] == 0
+    finally:
+        fa.fa_set_dq_mode(prev)
+    with pytest.raises(fa.FAError):
+        fa.fa_bwd_workspace(1, 1, T, 96, 96, W)
