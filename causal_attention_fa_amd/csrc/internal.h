@@ -127,10 +127,10 @@ hipError_t launch_bwd_kv_pipe(const BwdArgs& a, bool cap, hipStream_t stream);
 // head sizes whose backward can take dQ from stored dS (fa_bwd_ds.hip)
 constexpr bool ds_workspace_sizes(int d, int d_v) { return d == d_v && (d == 128 || d == 256); }
 // dQ mode (fa_set_dq_mode): 0 stored dS where it measured faster than the
-// recomputing dQ pass (d = 256: gemma-global 0.80 ms of dQ pass against the
-// stored tiles' cost; at d = 128 the dK/dV pass's 2 bytes of stores per
-// visible pair cost more than the recomputation saves: mistral 5.04 against
-// 5.6 ms of backward), 1 recompute everywhere, 2 stored dS wherever supported
+// recomputing dQ pass (d = 256: gemma-global backward 1.73 against 2.11 ms;
+// at d = 128 the dK/dV pass's 2 bytes of stores per visible pair cost about
+// what the recomputation saves: mistral 5.19 against 5.01 ms, qwen25 within
+// 2 %), 1 recompute everywhere, 2 stored dS wherever supported
 constexpr bool ds_mode_applies(int mode, int d, int d_v) {
   return ds_workspace_sizes(d, d_v) && (mode == 2 || (mode == 0 && d == 256));
 }
